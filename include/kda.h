@@ -1,0 +1,146 @@
+/*
+ * libkda — Kimi Delta Attention (KDA) forward pass on AMD Instinct MI355X (gfx950).
+ *
+ * The method (sources cited by page title and section):
+ *   [K3-notes]  "NLP——技术报告解读-Kimi-K3" (joezjh.github.io),
+ *               Model Architecture / Kimi Delta Attention (KDA):
+ *                 S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T,
+ *                 o_t = S_t^T q_t,   alpha_t = exp(g_t) in (0, 1]^{d_k},
+ *                 g_t^h = g_min * Sigmoid(exp(A_h) * z_t^h),  g_min = -5.
+ *               Infrastructure / KDA algorithm-system co-design: chunkwise
+ *               kernels for prefill, intra-device context parallelism
+ *               (segments of one sequence composed exactly), and the KCP
+ *               identity S = S~ + M S_in.
+ *   [K3-plain]  "Kimi K3 技术报告 · 大白话版" (aicoding.csdn.net), §2.1.1
+ *               (decay, then delta correction, then read; at most 99.33%
+ *               forgotten per step) and §5.4 (the decode state is updated in
+ *               place token by token).
+ *   [LateTalk]  "详解Kimi K3：强到冲击Anthropic估值的模型什么样？"
+ *               (latetalk.qiaomu.ai), section on the hybrid 3:1 layout: the
+ *               recurrent state has a fixed size and is overwritten by every
+ *               token.
+ *
+ * Conventions for every call:
+ *   - All tensor arguments are DEVICE pointers (memory of the current HIP
+ *     device), row-major, densely packed, owned by the caller.  The library
+ *     allocates nothing and keeps no state between calls.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Calls only enqueue work and return; completion and asynchronous HIP
+ *     faults are observed by the caller synchronising the stream.
+ *   - Arguments are validated on the host before anything is launched; a
+ *     failed check returns an error status and enqueues nothing.
+ *     kda_last_error() then describes the failure (thread-local string).
+ *   - dtype selects the storage type of the token tensors (q, k, v, g, z,
+ *     beta, o).  States are always fp32.  Arithmetic is fp32 with fp32
+ *     accumulation; bf16 tensors feed the matrix cores as bf16.
+ *   - The library does not normalise q or k, does not scale q, and applies
+ *     no output gate: it returns o_t exactly as defined above.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARGUMENT = 1,    /* null pointer, negative size, bad cu_seqlens ... */
+    KDA_ERR_UNSUPPORTED = 2,         /* a dimension / dtype / chunk outside the built set */
+    KDA_ERR_WORKSPACE_TOO_SMALL = 3, /* prefill workspace smaller than the queried size */
+    KDA_ERR_HIP = 4                  /* a HIP runtime call or launch failed */
+} kda_status_t;
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype_t;
+
+/* Human-readable name of a status code (static string). */
+const char* kda_status_string(kda_status_t s);
+
+/* Description of the most recent failure on the calling thread ("" if none). */
+const char* kda_last_error(void);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int kda_version(void);
+
+/*
+ * kda_gate — the lower-bounded log-decay gate ([K3-notes], KDA, lower-bounded
+ * decay; [K3-plain] §2.1.1):
+ *     g[t,h,c] = g_min * sigmoid(exp(A[h]) * z[t,h,c])
+ * z, g : [n_tokens, H, d_k] in `dtype` (g may alias z: in-place is allowed).
+ * A    : [H] fp32 device pointer.
+ * g_min: the lower bound (the pages use -5); must be finite and < 0.
+ * Computed in fp32 and rounded once to dtype.  n_tokens == 0 is a no-op.
+ * Errors: KDA_ERR_INVALID_ARGUMENT for null pointers / negative sizes / bad
+ * g_min, KDA_ERR_UNSUPPORTED for an unknown dtype, KDA_ERR_HIP on launch failure.
+ */
+kda_status_t kda_gate(const void* z, const float* A, void* g, int64_t n_tokens, int H,
+                      int d_k, kda_dtype_t dtype, float g_min, void* stream);
+
+/*
+ * Workspace bytes kda_prefill needs for this problem shape (0 on invalid
+ * arguments).  The value depends only on the arguments listed.
+ */
+size_t kda_prefill_workspace_size(int64_t T_total, int N, int H, int d_k, int d_v, int chunk,
+                                  kda_dtype_t dtype);
+
+/*
+ * kda_prefill — chunkwise KDA forward over packed sequences ([K3-notes], KDA
+ * recurrence; Infrastructure: chunkwise kernel, intra-device CP, KCP).
+ *   q, k, g : [T_total, H, d_k]   (g = log-decay, as produced by kda_gate)
+ *   v, o    : [T_total, H, d_v]
+ *   beta    : [T_total, H]
+ *   all in `dtype`.
+ *   cu_seqlens : int32 [N + 1] DEVICE array of token offsets, cu[0] = 0,
+ *                non-decreasing, cu[N] = T_total.  NULL means one sequence
+ *                (then N must be 1).  Sequences of length 0 are allowed.
+ *                The device copy cannot be checked on the host: the kernels
+ *                clamp every offset into [0, T_total] so malformed offsets
+ *                cannot cause out-of-bounds access, but the results are then
+ *                unspecified.
+ *   initial_state : fp32 [N, H, d_k, d_v] or NULL (zero initial states).
+ *   final_state   : fp32 [N, H, d_k, d_v] or NULL (not written).  May alias
+ *                   initial_state exactly (in-place hand-off); no other
+ *                   aliasing is allowed between any two buffers.
+ *   chunk   : tokens per chunk; 64 is the supported value.
+ *   d_k, d_v: each one of 32, 64, 128 for bf16; 32 or 64 for fp32 (the fp32
+ *             operand tiles of a 128-wide head do not fit one CU's LDS).
+ *   workspace : device buffer of at least kda_prefill_workspace_size(...) bytes
+ *               (may be NULL when that size is 0); its contents on entry do
+ *               not matter and are clobbered.
+ * Chunks restart at every sequence start; the last chunk of a sequence may be
+ * short.  Long sequences are split into segments that run in parallel and are
+ * composed exactly through S_end = S~ + M S_in.
+ * Errors: KDA_ERR_INVALID_ARGUMENT (null required pointer, N < 1, T_total < 0,
+ * N != 1 without cu_seqlens, forbidden aliasing), KDA_ERR_UNSUPPORTED (d_k,
+ * d_v, chunk or dtype outside the supported set),
+ * KDA_ERR_WORKSPACE_TOO_SMALL, KDA_ERR_HIP.
+ */
+kda_status_t kda_prefill(const void* q, const void* k, const void* v, const void* g,
+                         const void* beta, const int32_t* cu_seqlens, int N, int64_t T_total,
+                         int H, int d_k, int d_v, int chunk, const float* initial_state,
+                         float* final_state, void* o, kda_dtype_t dtype, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/*
+ * kda_decode_step — one token per sequence against a resident fp32 state,
+ * updated IN PLACE ([K3-notes] KDA recurrence; [K3-plain] §5.4; [LateTalk]
+ * fixed-size state overwritten by every token):
+ *     S <- (I - beta k k^T) Diag(exp(g)) S + beta k v^T ;   o = S^T q
+ *   q, k, g : [B, H, d_k]   v, o : [B, H, d_v]   beta : [B, H]   (dtype)
+ *   state   : fp32 [B, H, d_k, d_v], read and overwritten.
+ *   d_k, d_v: each one of 32, 64, 128.  B == 0 is a no-op.
+ * `o` must not alias any input or the state.
+ * Errors: KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED, KDA_ERR_HIP.
+ */
+kda_status_t kda_decode_step(const void* q, const void* k, const void* v, const void* g,
+                             const void* beta, float* state, void* o, int B, int H, int d_k,
+                             int d_v, kda_dtype_t dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

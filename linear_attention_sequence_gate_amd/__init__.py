@@ -1,0 +1,147 @@
+"""Python binding of libkda (the KDA forward pass for MI355X / gfx950).
+
+Argument marshalling only: every entry point takes torch tensors that live on
+the current HIP device, passes their device pointers and sizes to the C ABI in
+include/kda.h, and raises on a non-OK status.  torch is used for device memory
+and streams; all arithmetic happens in libkda's kernels.  If libkda.so has not
+been built, importing the binding functions raises: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libkda.so")
+
+KDA_F32, KDA_BF16 = 0, 1
+_STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARGUMENT", 2: "KDA_ERR_UNSUPPORTED",
+           3: "KDA_ERR_WORKSPACE_TOO_SMALL", 4: "KDA_ERR_HIP"}
+EXPORTED = ("kda_status_string", "kda_last_error", "kda_version", "kda_gate",
+            "kda_prefill_workspace_size", "kda_prefill", "kda_decode_step")
+
+_lib = None
+
+
+class KDAError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libkda (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"libkda.so not found at {LIB_PATH}; build it with "
+                              "`python -m linear_attention_sequence_gate_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, I64, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+        L.kda_status_string.argtypes = [I]
+        L.kda_status_string.restype = ctypes.c_char_p
+        L.kda_last_error.argtypes = []
+        L.kda_last_error.restype = ctypes.c_char_p
+        L.kda_version.argtypes = []
+        L.kda_version.restype = I
+        L.kda_gate.argtypes = [P, P, P, I64, I, I, I, F, P]
+        L.kda_gate.restype = I
+        L.kda_prefill_workspace_size.argtypes = [I64, I, I, I, I, I, I]
+        L.kda_prefill_workspace_size.restype = SZ
+        L.kda_prefill.argtypes = [P, P, P, P, P, P, I, I64, I, I, I, I, P, P, P, I, P, SZ, P]
+        L.kda_prefill.restype = I
+        L.kda_decode_step.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, P]
+        L.kda_decode_step.restype = I
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise KDAError(status, lib().kda_last_error().decode())
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    if t.dtype == torch.float32:
+        return KDA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _dense(*ts):
+    for t in ts:
+        if t is not None and not t.is_contiguous():
+            raise ValueError("libkda takes dense row-major tensors")
+
+
+def version() -> int:
+    return lib().kda_version()
+
+
+def kda_gate(z, A, g=None, g_min: float = -5.0, stream=None):
+    """g = g_min * sigmoid(exp(A[h]) * z) for z [T, H, d_k]; A fp32 [H]."""
+    import torch
+    _dense(z, A, g)
+    if g is None:
+        g = torch.empty_like(z)
+    T, H, dk = z.shape
+    _check(lib().kda_gate(_ptr(z), _ptr(A), _ptr(g), T, H, dk, _dtype_code(z), float(g_min),
+                          _stream(stream)))
+    return g
+
+
+def kda_prefill_workspace_size(T_total: int, N: int, H: int, d_k: int, d_v: int, chunk: int = 64,
+                               dtype: int = KDA_BF16) -> int:
+    return int(lib().kda_prefill_workspace_size(T_total, N, H, d_k, d_v, chunk, dtype))
+
+
+def kda_prefill(q, k, v, g, beta, cu_seqlens=None, initial_state=None, final_state=None, o=None,
+                workspace=None, chunk: int = 64, want_final_state: bool = True, stream=None):
+    """Chunkwise KDA prefill over packed sequences.
+
+    q, k, g: [T, H, d_k]; v: [T, H, d_v]; beta: [T, H]; cu_seqlens: int32 [N+1]
+    device tensor or None (one sequence); initial_state: fp32 [N, H, d_k, d_v]
+    or None.  Returns (o, final_state)."""
+    import torch
+    _dense(q, k, v, g, beta, cu_seqlens, initial_state, final_state, o)
+    T, H, dk = k.shape
+    dv = v.shape[2]
+    N = 1 if cu_seqlens is None else cu_seqlens.shape[0] - 1
+    code = _dtype_code(k)
+    if o is None:
+        o = torch.empty((T, H, dv), dtype=v.dtype, device=v.device)
+    if final_state is None and want_final_state:
+        final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=k.device)
+    need = kda_prefill_workspace_size(T, N, H, dk, dv, chunk, code)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=k.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().kda_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N, T,
+                             H, dk, dv, chunk, _ptr(initial_state), _ptr(final_state), _ptr(o), code,
+                             _ptr(workspace), wbytes, _stream(stream)))
+    return o, final_state
+
+
+def kda_decode_step(q, k, v, g, beta, state, o=None, stream=None):
+    """One token per sequence; state fp32 [B, H, d_k, d_v] is updated in place. Returns o."""
+    import torch
+    _dense(q, k, v, g, beta, state, o)
+    B, H, dk = k.shape
+    dv = v.shape[2]
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=v.dtype, device=v.device)
+    _check(lib().kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(o),
+                                 B, H, dk, dv, _dtype_code(k), _stream(stream)))
+    return o

@@ -1,0 +1,197 @@
+// libkda C ABI: argument validation, planning and kernel launches.
+// Every check runs on the host before anything is enqueued; see include/kda.h
+// for the contract of each entry point.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+
+#include "kda.h"
+#include "kda_decode.hpp"
+#include "kda_gate.hpp"
+#include "kda_prefill.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+kda_status_t fail(kda_status_t s, const char* fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+kda_status_t ok()
+{
+    g_err[0] = '\0';
+    return KDA_OK;
+}
+
+kda_status_t from_hip(hipError_t e, const char* what)
+{
+    if (e == hipSuccess) return ok();
+    return fail(KDA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool dim_ok(int d) { return d == 32 || d == 64 || d == 128; }
+bool dtype_ok(kda_dtype_t t) { return t == KDA_F32 || t == KDA_BF16; }
+size_t dsize(kda_dtype_t t) { return t == KDA_BF16 ? 2 : 4; }
+
+// true when [a, a+na) and [b, b+nb) overlap (byte ranges)
+bool overlap(const void* a, size_t na, const void* b, size_t nb)
+{
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kda_status_string(kda_status_t s)
+{
+    switch (s) {
+    case KDA_OK: return "KDA_OK";
+    case KDA_ERR_INVALID_ARGUMENT: return "KDA_ERR_INVALID_ARGUMENT";
+    case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
+    case KDA_ERR_WORKSPACE_TOO_SMALL: return "KDA_ERR_WORKSPACE_TOO_SMALL";
+    case KDA_ERR_HIP: return "KDA_ERR_HIP";
+    }
+    return "KDA_ERR_UNKNOWN";
+}
+
+const char* kda_last_error(void) { return g_err; }
+
+int kda_version(void) { return 100; }
+
+kda_status_t kda_gate(const void* z, const float* A, void* g, int64_t n_tokens, int H, int d_k,
+                      kda_dtype_t dtype, float g_min, void* stream)
+{
+    if (n_tokens < 0 || H < 1 || d_k < 1)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_gate: bad sizes n_tokens=%lld H=%d d_k=%d",
+                    (long long)n_tokens, H, d_k);
+    if (!dtype_ok(dtype)) return fail(KDA_ERR_UNSUPPORTED, "kda_gate: unknown dtype %d", (int)dtype);
+    if (!std::isfinite(g_min) || !(g_min < 0.f))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_gate: g_min must be finite and negative");
+    if (n_tokens == 0) return ok();
+    if (!z || !A || !g) return fail(KDA_ERR_INVALID_ARGUMENT, "kda_gate: null pointer");
+    const size_t bytes = size_t(n_tokens) * H * d_k * dsize(dtype);
+    if (z != g && overlap(z, bytes, g, bytes))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_gate: g partially overlaps z");
+    if (overlap(A, sizeof(float) * H, g, bytes))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_gate: g overlaps A");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = dtype == KDA_BF16 ? kda::launch_gate<kda::BF16>(z, A, g, n_tokens, H, d_k, g_min, s)
+                                     : kda::launch_gate<kda::F32>(z, A, g, n_tokens, H, d_k, g_min, s);
+    return from_hip(e, "kda_gate launch");
+}
+
+kda_status_t kda_decode_step(const void* q, const void* k, const void* v, const void* g,
+                             const void* beta, float* state, void* o, int B, int H, int d_k,
+                             int d_v, kda_dtype_t dtype, void* stream)
+{
+    if (B < 0 || H < 1)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_decode_step: bad sizes B=%d H=%d", B, H);
+    if (!dtype_ok(dtype))
+        return fail(KDA_ERR_UNSUPPORTED, "kda_decode_step: unknown dtype %d", (int)dtype);
+    if (!dim_ok(d_k) || !dim_ok(d_v))
+        return fail(KDA_ERR_UNSUPPORTED, "kda_decode_step: d_k=%d d_v=%d not in {32,64,128}", d_k, d_v);
+    if (B == 0) return ok();
+    if (!q || !k || !v || !g || !beta || !state || !o)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_decode_step: null pointer");
+    if ((reinterpret_cast<uintptr_t>(state) & 15) != 0)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_decode_step: state must be 16-byte aligned");
+    if (int64_t(B) * H > 0x7fffffff)
+        return fail(KDA_ERR_UNSUPPORTED, "kda_decode_step: B*H too large");
+    const size_t es = dsize(dtype);
+    const size_t nk = size_t(B) * H * d_k * es, nv = size_t(B) * H * d_v * es;
+    const size_t nb = size_t(B) * H * es, ns = size_t(B) * H * d_k * d_v * sizeof(float);
+    const void* ins[5] = {q, k, v, g, beta};
+    const size_t insz[5] = {nk, nk, nv, nk, nb};
+    for (int i = 0; i < 5; ++i) {
+        if (overlap(o, nv, ins[i], insz[i]))
+            return fail(KDA_ERR_INVALID_ARGUMENT, "kda_decode_step: o aliases an input");
+        if (overlap(state, ns, ins[i], insz[i]))
+            return fail(KDA_ERR_INVALID_ARGUMENT, "kda_decode_step: state aliases an input");
+    }
+    if (overlap(o, nv, state, ns))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_decode_step: o aliases the state");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = dtype == KDA_BF16
+                       ? kda::launch_decode<kda::BF16>(q, k, v, g, beta, state, o, B * H, d_k, d_v, s)
+                       : kda::launch_decode<kda::F32>(q, k, v, g, beta, state, o, B * H, d_k, d_v, s);
+    return from_hip(e, "kda_decode_step launch");
+}
+
+size_t kda_prefill_workspace_size(int64_t T_total, int N, int H, int d_k, int d_v, int chunk,
+                                  kda_dtype_t dtype)
+{
+    if (T_total < 0 || N < 1 || H < 1 || !dim_ok(d_k) || !dim_ok(d_v) || chunk != 64 ||
+        !dtype_ok(dtype) || (dtype == KDA_F32 && (d_k > 64 || d_v > 64)))
+        return 0;
+    return kda::prefill_plan(T_total, N, H, d_k, d_v).workspace_bytes;
+}
+
+kda_status_t kda_prefill(const void* q, const void* k, const void* v, const void* g,
+                         const void* beta, const int32_t* cu_seqlens, int N, int64_t T_total,
+                         int H, int d_k, int d_v, int chunk, const float* initial_state,
+                         float* final_state, void* o, kda_dtype_t dtype, void* workspace,
+                         size_t workspace_bytes, void* stream)
+{
+    if (N < 1 || T_total < 0 || H < 1)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_prefill: bad sizes N=%d T_total=%lld H=%d", N,
+                    (long long)T_total, H);
+    if (!cu_seqlens && N != 1)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_prefill: cu_seqlens is NULL but N=%d", N);
+    if (!dtype_ok(dtype))
+        return fail(KDA_ERR_UNSUPPORTED, "kda_prefill: unknown dtype %d", (int)dtype);
+    if (!dim_ok(d_k) || !dim_ok(d_v))
+        return fail(KDA_ERR_UNSUPPORTED, "kda_prefill: d_k=%d d_v=%d not in {32,64,128}", d_k, d_v);
+    if (chunk != 64) return fail(KDA_ERR_UNSUPPORTED, "kda_prefill: chunk=%d (only 64)", chunk);
+    if (dtype == KDA_F32 && (d_k > 64 || d_v > 64))
+        return fail(KDA_ERR_UNSUPPORTED, "kda_prefill: fp32 tensors need d_k, d_v <= 64");
+    if (T_total > (int64_t(1) << 40))
+        return fail(KDA_ERR_UNSUPPORTED, "kda_prefill: T_total too large");
+    if (T_total > 0 && (!q || !k || !v || !g || !beta || !o))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_prefill: null token tensor");
+    const kda::PrefillPlan plan = kda::prefill_plan(T_total, N, H, d_k, d_v);
+    if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
+        return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "kda_prefill: workspace %zu bytes < %zu needed",
+                    workspace_bytes, plan.workspace_bytes);
+    const size_t es = dsize(dtype);
+    const size_t nk = size_t(T_total) * H * d_k * es, nv = size_t(T_total) * H * d_v * es;
+    const size_t nb = size_t(T_total) * H * es;
+    const size_t ns = size_t(N) * H * d_k * d_v * sizeof(float);
+    const void* ins[6] = {q, k, v, g, beta, initial_state};
+    const size_t insz[6] = {nk, nk, nv, nk, nb, initial_state ? ns : 0};
+    for (int i = 0; i < 6; ++i) {
+        if (overlap(o, nv, ins[i], insz[i]))
+            return fail(KDA_ERR_INVALID_ARGUMENT, "kda_prefill: o aliases an input");
+        if (i < 5 && overlap(final_state, final_state ? ns : 0, ins[i], insz[i]))
+            return fail(KDA_ERR_INVALID_ARGUMENT, "kda_prefill: final_state aliases a token input");
+        if (overlap(workspace, plan.workspace_bytes, ins[i], insz[i]))
+            return fail(KDA_ERR_INVALID_ARGUMENT, "kda_prefill: workspace aliases an input");
+    }
+    if (final_state && initial_state && final_state != initial_state &&
+        overlap(final_state, ns, initial_state, ns))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_prefill: final_state partially overlaps initial_state");
+    if (overlap(o, nv, final_state, final_state ? ns : 0) ||
+        overlap(workspace, plan.workspace_bytes, o, nv) ||
+        overlap(workspace, plan.workspace_bytes, final_state, final_state ? ns : 0))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_prefill: output buffers overlap");
+    if (!final_state && T_total == 0) return ok();
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    kda::PrefillArgs a{q, k, v, g, beta, cu_seqlens, N, T_total, H, d_k, d_v,
+                       initial_state, final_state, o, workspace};
+    hipError_t e = dtype == KDA_BF16 ? kda::launch_prefill<kda::BF16>(a, plan, s)
+                                     : kda::launch_prefill<kda::F32>(a, plan, s);
+    return from_hip(e, "kda_prefill launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,91 @@
+// Shared device helpers for the libkda kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+// ---- bf16 <-> fp32 (bit exact; fp32 -> bf16 rounds to nearest even in hardware)
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
+{
+    f32x2 v = {a, b};
+    bf16x2 r = __builtin_convertvector(v, bf16x2);
+    return __builtin_bit_cast(uint32_t, r);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float a)
+{
+    return __builtin_bit_cast(uint16_t, (__bf16)a);
+}
+
+// Token-tensor element type tags.
+struct F32 {
+    using storage = float;
+    static constexpr bool is_bf16 = false;
+};
+struct BF16 {
+    using storage = uint16_t;
+    static constexpr bool is_bf16 = true;
+};
+
+template <typename DT>
+__device__ __forceinline__ float load_elem(const typename DT::storage* p, int64_t i)
+{
+    if constexpr (DT::is_bf16) return bf16_to_f32(p[i]);
+    else return p[i];
+}
+template <typename DT>
+__device__ __forceinline__ void store_elem(typename DT::storage* p, int64_t i, float x)
+{
+    if constexpr (DT::is_bf16) p[i] = f32_to_bf16(x);
+    else p[i] = x;
+}
+
+// Eight consecutive elements (16-byte aligned for bf16, 32-byte pair of float4 for f32).
+template <typename DT>
+__device__ __forceinline__ void load8(const typename DT::storage* p, float (&x)[8])
+{
+    if constexpr (DT::is_bf16) {
+        u32x4 w = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = bf16_lo(w[i]);
+            x[2 * i + 1] = bf16_hi(w[i]);
+        }
+    } else {
+        f32x4 a = *reinterpret_cast<const f32x4*>(p);
+        f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[i] = a[i];
+            x[4 + i] = b[i];
+        }
+    }
+}
+template <typename DT>
+__device__ __forceinline__ void store8(typename DT::storage* p, const float (&x)[8])
+{
+    if constexpr (DT::is_bf16) {
+        u32x4 w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
+        *reinterpret_cast<u32x4*>(p) = w;
+    } else {
+        f32x4 a = {x[0], x[1], x[2], x[3]};
+        f32x4 b = {x[4], x[5], x[6], x[7]};
+        *reinterpret_cast<f32x4*>(p) = a;
+        *reinterpret_cast<f32x4*>(p + 4) = b;
+    }
+}
+
+}  // namespace kda

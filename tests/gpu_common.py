@@ -1,0 +1,38 @@
+"""Helpers shared by the GPU parity tests: device copies of the seeded inputs
+and the error measure (normwise max relative error, max|x - y| / max|y|)."""
+from __future__ import annotations
+
+import numpy as np
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def torch_dtype(name):
+    import torch
+    return torch.bfloat16 if name == "bf16" else torch.float32
+
+
+def dev(x: np.ndarray, dtype: str = "f32"):
+    """float32 numpy array (exact in `dtype`) -> device tensor of that dtype."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to("cuda")
+    return t.to(torch_dtype(dtype)) if dtype == "bf16" else t
+
+
+def host(t) -> np.ndarray:
+    import torch
+    return t.detach().to(torch.float64).cpu().numpy()
+
+
+def relerr(got, want) -> float:
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    if want.size == 0:
+        return 0.0
+    assert np.all(np.isfinite(got)), "non-finite values from the GPU"
+    scale = np.max(np.abs(want))
+    return float(np.max(np.abs(got - want)) / max(scale, 1e-300))
+
+
+def announce(msg: str):
+    print(f"[case] {msg}", flush=True)

@@ -1,0 +1,130 @@
+"""libkda's C ABI on the CPU: the library loads, exports every symbol the header
+declares, and rejects bad arguments on the host before anything is launched.
+No call here reaches a kernel launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import linear_attention_sequence_gate_amd as kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+FAKE = 0x10000  # a non-null address; validation rejects the call before any use
+BF16, F32 = kda.KDA_BF16, kda.KDA_F32
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return kda.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert set(names) == set(kda.EXPORTED), names
+    for n in names:
+        assert hasattr(L, n), f"libkda does not export {n}"
+
+
+def test_version_and_status_strings(L):
+    assert kda.version() == 100
+    for code, name in kda._STATUS.items():
+        assert L.kda_status_string(code).decode() == name
+    assert L.kda_status_string(99).decode() == "KDA_ERR_UNKNOWN"
+
+
+def status(call):
+    return call
+
+
+def test_gate_validation(L):
+    assert L.kda_gate(FAKE, FAKE, FAKE, -1, 2, 32, BF16, -5.0, None) == 1
+    assert L.kda_gate(FAKE, FAKE, FAKE, 4, 0, 32, BF16, -5.0, None) == 1
+    assert L.kda_gate(FAKE, FAKE, FAKE, 4, 2, 32, 7, -5.0, None) == 2
+    assert L.kda_gate(FAKE, FAKE, FAKE, 4, 2, 32, BF16, 1.0, None) == 1
+    assert L.kda_gate(FAKE, FAKE, FAKE, 4, 2, 32, BF16, float("nan"), None) == 1
+    assert L.kda_gate(None, FAKE, FAKE, 4, 2, 32, BF16, -5.0, None) == 1
+    assert b"null" in L.kda_last_error()
+    # partial overlap of g with z (exact aliasing is allowed)
+    assert L.kda_gate(FAKE, FAKE + 1 << 20, FAKE + 64, 4, 2, 32, BF16, -5.0, None) == 1
+    # n_tokens == 0 is a no-op that succeeds without touching the device
+    assert L.kda_gate(None, None, None, 0, 2, 32, BF16, -5.0, None) == 0
+
+
+def test_decode_validation(L):
+    base = dict(q=FAKE, k=FAKE + (1 << 20), v=FAKE + (2 << 20), g=FAKE + (3 << 20),
+                beta=FAKE + (4 << 20), state=FAKE + (8 << 20), o=FAKE + (64 << 20))
+
+    def call(**kw):
+        a = dict(base, B=4, H=2, dk=128, dv=128, dt=BF16)
+        a.update(kw)
+        return L.kda_decode_step(a["q"], a["k"], a["v"], a["g"], a["beta"], a["state"], a["o"],
+                                 a["B"], a["H"], a["dk"], a["dv"], a["dt"], None)
+
+    assert call(B=-1) == 1
+    assert call(H=0) == 1
+    assert call(dk=48) == 2
+    assert call(dv=256) == 2
+    assert call(dt=5) == 2
+    assert call(q=None) == 1
+    assert call(state=FAKE + (8 << 20) + 4) == 1          # misaligned state
+    assert call(o=FAKE + 16) == 1                          # o aliases q
+    assert call(o=FAKE + (8 << 20)) == 1                   # o aliases the state
+    assert call(state=FAKE + (3 << 20)) == 1               # state aliases g
+    assert call(B=0, q=None, o=None) == 0                  # empty batch: no-op
+
+
+def test_prefill_workspace_size(L):
+    ws = kda.kda_prefill_workspace_size
+    assert ws(8192, 1, 32, 128, 128) > 0
+    assert ws(0, 1, 32, 128, 128) > 0
+    assert ws(8192, 1, 32, 96, 128) == 0
+    assert ws(8192, 1, 32, 128, 128, chunk=32) == 0
+    assert ws(8192, 1, 32, 128, 128, dtype=F32) == 0      # fp32 needs d <= 64
+    assert ws(256, 1, 2, 32, 32, dtype=F32) > 0
+    # a sequence too short to split needs no segment buffers
+    small = ws(64 * 16, 1, 32, 128, 128)
+    assert small < 4096
+    # a long one does (transition + incoming state per segment)
+    big = ws(1 << 20, 1, 8, 128, 128)
+    assert big > 8 * 128 * 256 * 4
+
+
+def test_prefill_validation(L):
+    T, N, H, dk, dv = 256, 1, 2, 64, 64
+    need = kda.kda_prefill_workspace_size(T, N, H, dk, dv)
+
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE + (1 << 20), v=FAKE + (2 << 20), g=FAKE + (3 << 20),
+                 beta=FAKE + (4 << 20), cu=None, N=N, T=T, H=H, dk=dk, dv=dv, chunk=64,
+                 init=None, fin=FAKE + (8 << 20), o=FAKE + (16 << 20), dt=BF16,
+                 ws=FAKE + (32 << 20), wsb=need)
+        a.update(kw)
+        return L.kda_prefill(a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu"], a["N"], a["T"],
+                             a["H"], a["dk"], a["dv"], a["chunk"], a["init"], a["fin"], a["o"],
+                             a["dt"], a["ws"], a["wsb"], None)
+
+    assert call(N=0) == 1
+    assert call(T=-5) == 1
+    assert call(N=3) == 1                                   # N > 1 needs cu_seqlens
+    assert call(dk=96) == 2
+    assert call(chunk=32) == 2
+    assert call(dt=F32, dk=128, dv=128) == 2
+    assert call(dt=9) == 2
+    assert call(q=None) == 1
+    assert call(o=None) == 1
+    if need > 0:
+        assert call(wsb=need - 1) == 3
+        assert call(ws=None) == 3
+    assert call(o=FAKE + 8) == 1                             # o aliases q
+    assert call(fin=FAKE + (2 << 20)) == 1                   # final state aliases v
+    assert call(init=FAKE + (8 << 20) + 4) == 1              # partial init/final overlap
+    assert call(ws=FAKE + (16 << 20)) == 1                   # workspace aliases o
+    assert call(ws=FAKE + (4 << 20)) == 1                    # workspace aliases beta

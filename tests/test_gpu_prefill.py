@@ -1,0 +1,109 @@
+"""GPU parity: kda_gate + kda_prefill against the fp64 oracle (token-serial
+recurrence).  The GPU path applies its own gate to z and A; the oracle applies
+its gate and rounds g to the storage dtype, as the gate's output contract says."""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_common import TOL, announce, dev, host, relerr
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def kda():
+    import torch
+    import linear_attention_sequence_gate_amd as m
+    assert torch.cuda.is_available()
+    m.lib()
+    return m
+
+
+class SegEnv:
+    """Force a segment length (chunks) for the library's planner."""
+
+    def __init__(self, chunks):
+        self.chunks = chunks
+
+    def __enter__(self):
+        self.old = os.environ.get("KDA_SEG_CHUNKS")
+        if self.chunks is not None:
+            os.environ["KDA_SEG_CHUNKS"] = str(self.chunks)
+
+    def __exit__(self, *a):
+        if self.old is None:
+            os.environ.pop("KDA_SEG_CHUNKS", None)
+        else:
+            os.environ["KDA_SEG_CHUNKS"] = self.old
+
+
+def run_gpu(kda, wl, x, S0, seg=None):
+    import torch
+    dt = wl.dtype
+    cu = torch.from_numpy(wl.cu_seqlens).to("cuda") if wl.N > 1 else None
+    g = kda.kda_gate(dev(x["z"], dt), dev(x["A"]))
+    with SegEnv(seg):
+        o, S = kda.kda_prefill(dev(x["q"], dt), dev(x["k"], dt), dev(x["v"], dt), g,
+                               dev(x["beta"], dt), cu_seqlens=cu,
+                               initial_state=None if S0 is None else dev(S0))
+    torch.cuda.synchronize()
+    return host(o), host(S)
+
+
+def run_oracle(wl, x, S0):
+    g = oracle.gate(x["z"], x["A"], round_bf16=(wl.dtype == "bf16"))
+    return oracle.prefill(x["q"], x["k"], x["v"], g, x["beta"], cu=wl.cu_seqlens, S0=S0)
+
+
+def check(kda, wl, seg=None, tag=""):
+    announce(f"prefill {wl.name} {tag} H={wl.H} dk={wl.dk} dv={wl.dv} {wl.dtype} "
+             f"lens={list(wl.seqlens)[:8]} seg={seg}")
+    x = synth.prefill_inputs(wl)
+    S0 = synth.initial_state(wl) if wl.state_std > 0 else None
+    o, S = run_gpu(kda, wl, x, S0, seg)
+    o_ref, S_ref = run_oracle(wl, x, S0)
+    e_o, e_s = relerr(o, o_ref), relerr(S, S_ref)
+    print(f"  o err {e_o:.3e}  state err {e_s:.3e}")
+    tol = TOL[wl.dtype]
+    assert e_o < tol, f"output error {e_o:.3e}"
+    assert e_s < tol, f"final state error {e_s:.3e}"
+    return o, S
+
+
+def test_prefill_tiny_f32(kda):
+    check(kda, synth.TINY_F32)
+
+
+def test_prefill_8k_bf16(kda):
+    check(kda, synth.PREFILL_8K)
+
+
+LENS = (0, 1, 63, 64, 65, 130, 300, 17)
+
+
+@pytest.mark.parametrize("dk,dv,dtype", [(128, 128, "bf16"), (64, 64, "bf16"), (32, 32, "bf16"),
+                                         (128, 32, "bf16"), (32, 128, "bf16"), (64, 128, "bf16"),
+                                         (32, 32, "f32"), (64, 64, "f32"), (64, 32, "f32")])
+def test_prefill_varlen_dims(kda, dk, dv, dtype):
+    wl = synth.VARLEN_64.with_(H=3, dk=dk, dv=dv, dtype=dtype, seqlens=LENS, state_std=0.1)
+    check(kda, wl)
+
+
+@pytest.mark.parametrize("seg", [1, 2, 3])
+@pytest.mark.parametrize("zshift", [0.0, -3.0])
+def test_prefill_segmented(kda, seg, zshift):
+    """Segments of `seg` chunks: transition/zero-state summary, scan, rerun."""
+    wl = synth.VARLEN_64.with_(H=4, seqlens=(700, 0, 64, 129, 1000, 5), state_std=0.1,
+                               z_shift=zshift)
+    check(kda, wl, seg=seg, tag=f"zshift={zshift}")
+
+
+def test_prefill_weak_decay_long(kda):
+    """z shifted by -3 (alpha ~ 0.7): the incoming state and early tokens still
+    matter thousands of tokens later."""
+    wl = synth.PREFILL_8K.with_(H=4, seqlens=(4096,), z_shift=-3.0, state_std=0.1)
+    check(kda, wl)
+    check(kda, wl, seg=4, tag="seg4")
