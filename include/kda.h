@@ -105,8 +105,9 @@ size_t kda_prefill_workspace_size(int64_t T_total, int N, int H, int d_k, int d_
  *                   initial_state exactly (in-place hand-off); no other
  *                   aliasing is allowed between any two buffers.
  *   chunk   : tokens per chunk; 64 is the supported value.
- *   d_k, d_v: each one of 32, 64, 128 for bf16; 32 or 64 for fp32 (the fp32
- *             operand tiles of a 128-wide head do not fit one CU's LDS).
+ *   d_k, d_v: each one of 32, 64, 128 for bf16; for fp32 d_k = 32 and d_v is
+ *             32 or 64 (the fp32 operand tiles of wider heads do not fit one
+ *             CU's LDS).
  *   workspace : device buffer of at least kda_prefill_workspace_size(...) bytes
  *               (may be NULL when that size is 0); its contents on entry do
  *               not matter and are clobbered.

@@ -133,7 +133,7 @@ size_t kda_prefill_workspace_size(int64_t T_total, int N, int H, int d_k, int d_
                                   kda_dtype_t dtype)
 {
     if (T_total < 0 || N < 1 || H < 1 || !dim_ok(d_k) || !dim_ok(d_v) || chunk != 64 ||
-        !dtype_ok(dtype) || (dtype == KDA_F32 && (d_k > 64 || d_v > 64)))
+        !dtype_ok(dtype) || (dtype == KDA_F32 && (d_k != 32 || d_v > 64)))
         return 0;
     return kda::prefill_plan(T_total, N, H, d_k, d_v).workspace_bytes;
 }
@@ -154,8 +154,8 @@ kda_status_t kda_prefill(const void* q, const void* k, const void* v, const void
     if (!dim_ok(d_k) || !dim_ok(d_v))
         return fail(KDA_ERR_UNSUPPORTED, "kda_prefill: d_k=%d d_v=%d not in {32,64,128}", d_k, d_v);
     if (chunk != 64) return fail(KDA_ERR_UNSUPPORTED, "kda_prefill: chunk=%d (only 64)", chunk);
-    if (dtype == KDA_F32 && (d_k > 64 || d_v > 64))
-        return fail(KDA_ERR_UNSUPPORTED, "kda_prefill: fp32 tensors need d_k, d_v <= 64");
+    if (dtype == KDA_F32 && (d_k != 32 || d_v > 64))
+        return fail(KDA_ERR_UNSUPPORTED, "kda_prefill: fp32 tensors need d_k = 32, d_v <= 64");
     if (T_total > (int64_t(1) << 40))
         return fail(KDA_ERR_UNSUPPORTED, "kda_prefill: T_total too large");
     if (T_total > 0 && (!q || !k || !v || !g || !beta || !o))
@@ -195,3 +195,12 @@ kda_status_t kda_prefill(const void* q, const void* k, const void* v, const void
 }
 
 }  // extern "C"
+
+#ifdef KDA_PHASE_TIMING
+// Copy the per-workgroup phase cycle counters of the last chunk-kernel launch.
+extern "C" int kda_phase_cycles_read(unsigned long long* host, int n)
+{
+    return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(kda::kda_phase_cycles),
+                                    sizeof(unsigned long long) * size_t(n), 0, hipMemcpyDeviceToHost);
+}
+#endif

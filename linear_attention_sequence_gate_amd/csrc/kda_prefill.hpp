@@ -48,6 +48,27 @@
 
 namespace kda {
 
+// Optional per-phase cycle counters of the chunk kernel (built only with
+// -DKDA_PHASE_TIMING; the default build compiles the markers away).
+#ifdef KDA_PHASE_TIMING
+#ifndef KDA_PHASE_TID
+#define KDA_PHASE_TID 0
+#endif
+__device__ unsigned long long kda_phase_cycles[16384 * 16];
+#define KDA_PHASE(i)                                    \
+    do {                                                \
+        if (tid == KDA_PHASE_TID) {                     \
+            const long long t_ = clock64();             \
+            phase_acc[i] += t_ - phase_last;            \
+            phase_last = t_;                            \
+        }                                               \
+    } while (0)
+#else
+#define KDA_PHASE(i) \
+    do {             \
+    } while (0)
+#endif
+
 constexpr int CH = 64;  // tokens per chunk
 constexpr int NCU_TARGET = 256;
 
@@ -210,12 +231,32 @@ __device__ __forceinline__ int find_seq(const int32_t* off, int N, int item)
 }
 
 // ------------------------------------------------------- operand plumbing
+// MFMA operand tiles in LDS keep each 32-column block in a permuted order:
+// logical column c = 16h + 4q + j (h in {0,1}, q, j in 0..3) is stored at
+// position 8q + 4h + j.  Lane group q of a 16x16x32 MFMA then reads its eight
+// K-values k(q, e) = 16*(e/4) + 4q + e%4 (e = 0..7) as one contiguous 16-byte
+// (bf16) load.  The same k(q, e) order lets a pair of 16x16 accumulator tiles
+// (rows 4q..4q+3 of rows 0-15 and of rows 16-31) serve directly as the other
+// operand, so the state, X and U never leave registers.
+__host__ __device__ constexpr int pcol(int c)
+{
+    return (c & ~31) | (((c >> 2) & 3) << 3) | (((c >> 4) & 1) << 2) | (c & 3);
+}
+__device__ __forceinline__ int kperm(int q, int e) { return ((e >> 2) << 4) + (q << 2) + (e & 3); }
+
+// 2^x with the hardware instruction (about 1 ulp; results below the fp32
+// range flush to zero, which the decay factoring above tolerates: every
+// flushed factor multiplies terms bounded by 1)
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 template <typename DT>
 struct Op;
+typedef __attribute__((ext_vector_type(4))) short s16x4;
 template <>
 struct Op<BF16> {
     using T = uint16_t;  // LDS operand element
-    using Frag = bf16x8;
+    using Frag = bf16x8;  // 16x16x32 operand
+    using Frag4 = s16x4;  // 16x16x16 operand
     static __device__ __forceinline__ Frag make(const float (&x)[8])
     {
         u32x4 w;
@@ -225,20 +266,48 @@ struct Op<BF16> {
         w[3] = pack_bf16x2(x[6], x[7]);
         return __builtin_bit_cast(Frag, w);
     }
+    static __device__ __forceinline__ Frag load(const T* p)  // 8 consecutive elements
+    {
+        return __builtin_bit_cast(Frag, *reinterpret_cast<const u32x4*>(p));
+    }
+    static __device__ __forceinline__ void unpack(const Frag& f, float (&x)[8])
+    {
+        const u32x4 w = __builtin_bit_cast(u32x4, f);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = bf16_lo(w[i]);
+            x[2 * i + 1] = bf16_hi(w[i]);
+        }
+    }
+    static __device__ __forceinline__ Frag4 load4(const T* p)
+    {
+        return __builtin_bit_cast(Frag4, *reinterpret_cast<const u32x2*>(p));
+    }
+    static __device__ __forceinline__ Frag4 make4(const f32x4& v)
+    {
+        u32x2 w;
+        w[0] = pack_bf16x2(v[0], v[1]);
+        w[1] = pack_bf16x2(v[2], v[3]);
+        return __builtin_bit_cast(Frag4, w);
+    }
     static __device__ __forceinline__ void mma(f32x4& acc, const Frag& a, const Frag& b)
     {
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
     }
+    static __device__ __forceinline__ void mma4(f32x4& acc, const Frag4& a, const Frag4& b)
+    {
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, acc, 0, 0, 0);
+    }
     static __device__ __forceinline__ T to_op(float x) { return f32_to_bf16(x); }
     static __device__ __forceinline__ float from_op(T x) { return bf16_to_f32(x); }
-    // 4 consecutive LDS elements -> 4 floats
-    static __device__ __forceinline__ void ld4(const T* p, float* x)
+    // two adjacent elements (channels 2m, 2m+1)
+    using Pair = uint32_t;
+    static __device__ __forceinline__ Pair ldp(const T* p) { return *reinterpret_cast<const uint32_t*>(p); }
+    static __device__ __forceinline__ float p0(Pair w) { return bf16_lo(w); }
+    static __device__ __forceinline__ float p1(Pair w) { return bf16_hi(w); }
+    static __device__ __forceinline__ void stp(T* p, float a, float b)
     {
-        const u32x2 w = *reinterpret_cast<const u32x2*>(p);
-        x[0] = bf16_lo(w[0]);
-        x[1] = bf16_hi(w[0]);
-        x[2] = bf16_lo(w[1]);
-        x[3] = bf16_hi(w[1]);
+        *reinterpret_cast<uint32_t*>(p) = pack_bf16x2(a, b);
     }
     static __device__ __forceinline__ void st4(T* p, const f32x4& v)
     {
@@ -255,6 +324,7 @@ template <>
 struct Op<F32> {
     using T = float;
     using Frag = f32x8;
+    using Frag4 = f32x4;
     static __device__ __forceinline__ Frag make(const float (&x)[8])
     {
         Frag f;
@@ -262,42 +332,48 @@ struct Op<F32> {
         for (int i = 0; i < 8; ++i) f.v[i] = x[i];
         return f;
     }
+    static __device__ __forceinline__ Frag load(const T* p)
+    {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+        Frag f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f.v[i] = a[i];
+            f.v[4 + i] = b[i];
+        }
+        return f;
+    }
+    static __device__ __forceinline__ void unpack(const Frag& f, float (&x)[8])
+    {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = f.v[i];
+    }
+    static __device__ __forceinline__ Frag4 load4(const T* p) { return *reinterpret_cast<const f32x4*>(p); }
+    static __device__ __forceinline__ Frag4 make4(const f32x4& v) { return v; }
     static __device__ __forceinline__ void mma(f32x4& acc, const Frag& a, const Frag& b)
     {
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[e], b.v[e], acc, 0, 0, 0);
     }
+    // K = 16 with lane group q holding k = 4q..4q+3: MFMA s takes element s (k = 4q + s)
+    static __device__ __forceinline__ void mma4(f32x4& acc, const Frag4& a, const Frag4& b)
+    {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], acc, 0, 0, 0);
+    }
     static __device__ __forceinline__ T to_op(float x) { return x; }
     static __device__ __forceinline__ float from_op(T x) { return x; }
-    static __device__ __forceinline__ void ld4(const T* p, float* x)
+    using Pair = f32x2;
+    static __device__ __forceinline__ Pair ldp(const T* p) { return *reinterpret_cast<const f32x2*>(p); }
+    static __device__ __forceinline__ float p0(Pair w) { return w[0]; }
+    static __device__ __forceinline__ float p1(Pair w) { return w[1]; }
+    static __device__ __forceinline__ void stp(T* p, float a, float b)
     {
-        const f32x4 w = *reinterpret_cast<const f32x4*>(p);
-        x[0] = w[0];
-        x[1] = w[1];
-        x[2] = w[2];
-        x[3] = w[3];
+        *reinterpret_cast<f32x2*>(p) = f32x2{a, b};
     }
-    static __device__ __forceinline__ void st4(T* p, const f32x4& v)
-    {
-        *reinterpret_cast<f32x4*>(p) = v;
-    }
+    static __device__ __forceinline__ void st4(T* p, const f32x4& v) { *reinterpret_cast<f32x4*>(p) = v; }
 };
-
-// K-block of 32 with the permuted index k(q, e) = 16*(e/4) + 4q + (e%4): lane
-// group q supplies elements e = 0..7.  The same permutation is used for both
-// operands of every product, so the sum over k is unchanged; it lets a pair of
-// 16x16 accumulator tiles (rows 4q..4q+3 of each) serve directly as an operand.
-__device__ __forceinline__ int kperm(int q, int e) { return ((e >> 2) << 4) + (q << 2) + (e & 3); }
-
-// fragment of a row-major LDS tile: row `row`, K-block starting at column kc
-template <typename DT>
-__device__ __forceinline__ void lds_row_frag(const typename Op<DT>::T* tile, int stride, int row,
-                                             int kc, int q, float (&x)[8])
-{
-    const typename Op<DT>::T* p = tile + row * stride + kc + 4 * q;
-    Op<DT>::ld4(p, x);
-    Op<DT>::ld4(p + 16, x + 4);
-}
 
 // operand fragment from two accumulator tiles (rows 0-15 and 16-31 of a K-block)
 template <typename DT>
@@ -311,48 +387,212 @@ __device__ __forceinline__ typename Op<DT>::Frag acc_frag(const f32x4& lo, const
 template <typename DT, int DK, int DV, bool SUMMARY>
 struct ChunkCfg {
     static constexpr int NCOL = SUMMARY ? DV + DK : DV;  // extended state columns
-    static constexpr int NCW = NCOL / 32;                 // chain waves
+    // state columns per chain wave: 16 for the output pass (two waves per SIMD
+    // hide LDS latency), 32 for the summary pass (twice the columns, no outputs)
+    static constexpr int CW = (SUMMARY || NCOL <= 32) ? 32 : 16;
+    static constexpr int NCT = CW / 16;                   // 16-wide column tiles per wave
+    static constexpr int NCW = NCOL / CW;                 // chain waves
     static constexpr int NW0 = NCW > DK / 64 ? NCW : DK / 64;
     static constexpr int NW = NW0 <= 1 ? 1 : NW0 <= 2 ? 2 : NW0 <= 4 ? 4 : 8;
     static constexpr int NT = NW * 64;
-    static constexpr int PARTS = NT / DK;     // threads per key channel (elementwise phase)
-    static constexpr int TPT = CH / PARTS;    // tokens per thread
+    static constexpr int CP = DK / 2;          // channel pairs
+    static constexpr int PARTS = NT / CP;      // threads per channel pair (elementwise phases)
+    static constexpr int TPT = CH / PARTS;     // tokens per thread
     static constexpr int SL = TPT < 16 ? TPT : 16;
     static constexpr int NSLOT = CH / SL;
     using OT = typename Op<DT>::T;
     static constexpr int ES = sizeof(OT);
-    static constexpr int SK = DK + 8;  // row strides (elements) of the padded tiles
-    static constexpr int SV = DV + 8;
-    static constexpr int ST = CH + 8;
-    static constexpr int SA = CH + 4;  // fp32 solve tiles
+    static constexpr int SK = DK + 16 / ES;  // padded row strides (elements)
+    static constexpr int SV = DV + 16 / ES;
+    static constexpr int ST = CH + 16 / ES;
+    static constexpr int SD = 16 + 16 / ES;
+    static constexpr int TILE_K = CH * SK * ES;
     // LDS layout (bytes)
-    static constexpr int O_Q = 0;                      // q -> QE
-    static constexpr int O_K = O_Q + CH * SK * ES;     // k -> KE
-    static constexpr int O_G = O_K + CH * SK * ES;     // g -> KF
-    static constexpr int O_V = O_G + CH * SK * ES;     // v
-    static constexpr int O_T = O_V + CH * SV * ES;     // T
-    static constexpr int O_P = O_T + CH * ST * ES;     // P
-    static constexpr int O_A = O_P + CH * ST * ES;     // A (fp32)
-    static constexpr int O_X = O_A + CH * SA * 4;      // (I+A)^-1 (fp32)
-    static constexpr int O_Y = O_X + CH * SA * 4;      // solve scratch, 3 x 16x16 fp32
-    static constexpr int O_VEC = O_Y + 3 * 256 * 4;    // 16 x DK fp32 channel vectors
-    static constexpr int O_SIG = O_VEC + 16 * DK * 4;  // NSLOT x DK fp32
-    static constexpr int O_B = O_SIG + NSLOT * DK * 4; // beta[64]
+    static constexpr int O_Q = 0;                       // raw q -> q.e^{G-R_a}
+    static constexpr int O_K = O_Q + TILE_K;            // raw k -> k.e^{G-R_a}
+    static constexpr int O_G = O_K + TILE_K;            // raw g -> k.e^{R_a-G}
+    static constexpr int O_V = O_G + TILE_K;            // raw v
+    static constexpr int O_QG = O_V + CH * SV * ES;     // q.e^{G}
+    static constexpr int O_KG = O_QG + TILE_K;          // -k.e^{G}
+    static constexpr int O_KH = O_KG + TILE_K;          // (k.e^{G_last-G})^T  [DK][ST]
+    static constexpr int O_A = O_KH + DK * ST * ES;     // -A (x beta_r), natural columns
+    static constexpr int O_P = O_A + CH * ST * ES;      // P, permuted columns
+    static constexpr int O_D = O_P + CH * ST * ES;      // (I + A_aa)^{-1}, 4 blocks
+    static constexpr int O_DS = O_D + 4 * 16 * SD * ES;  // N^2, N^4 per diagonal block (inverse scratch)
+    static constexpr int O_VEC = O_DS + 8 * 16 * SD * ES;  // 16 x DK fp32 channel vectors
+    static constexpr int O_SIG = O_VEC + 16 * DK * 4;   // NSLOT x DK fp32
+    static constexpr int O_B = O_SIG + NSLOT * DK * 4;  // beta[64]
     static constexpr int LDS = O_B + CH * 4;
+    // output staging in the -k.e^G tile: rows of DV storage elements (stride SO)
+    static constexpr int SO = DV + 8;
+    static constexpr bool STAGE_O = !SUMMARY && CH * SO * int(sizeof(typename DT::storage)) <= TILE_K;
     // raw tile loading: 16-byte units
-    static constexpr int UPR_K = DK * ES / 16;  // units per row
-    static constexpr int UPR_V = DV * ES / 16;
-    static constexpr int U_K = CH * UPR_K;      // units per q/k/g tile
+    static constexpr int EPU = 16 / ES;           // elements per unit
+    static constexpr int UPR_K = DK / EPU;        // units per row
+    static constexpr int UPR_V = DV / EPU;
+    static constexpr int U_K = CH * UPR_K;        // units per q/k/g tile
     static constexpr int U_V = CH * UPR_V;
-    static constexpr int U_ALL = 3 * U_K + U_V;
-    static constexpr int UPT = (U_ALL + NT - 1) / NT;  // units per thread
+    static constexpr int NTILE_K = SUMMARY ? 2 : 3;  // pass 1 needs no q
+    static constexpr int UPT_K = (U_K + NT - 1) / NT;  // units per thread, per q/k/g tile
+    static constexpr int UPT_V = (U_V + NT - 1) / NT;
+    static constexpr int UPT = NTILE_K * UPT_K + UPT_V;
     static_assert(LDS <= 160 * 1024, "LDS budget exceeded");
     static_assert(PARTS >= 1 && CH % PARTS == 0, "bad elementwise split");
     static_assert((TPT % 16 == 0) || (16 % TPT == 0), "sub-tile alignment");
 };
 
-// channel-vector slots
+// channel-vector slots (each DK fp32, permuted channel order)
 enum { V_ER = 0, V_FY = 4, V_FX = 8, V_EL = 11, V_GC = 15 };
+
+// Raw tile prefetch into registers: per tensor a uniform base pointer for the
+// chunk and a fixed per-lane offset, so each 16-byte unit is one load.  Rows
+// past the sequence end are re-read from its last row (only needed when the
+// chunk ends past the tensor) and zeroed at commit.
+template <typename C, typename DT>
+__device__ __forceinline__ void raw_prefetch(u32x4 (&pre)[C::UPT], const typename DT::storage* gq,
+                                             const typename DT::storage* gk,
+                                             const typename DT::storage* gv,
+                                             const typename DT::storage* gg, int64_t c0, int len,
+                                             int64_t T_total, int H, int h, int tid, int dk, int dv)
+{
+    using ST = typename DT::storage;
+    const bool clamp = c0 + CH > T_total;
+    const int hdk = H * dk, hdv = H * dv;
+    const ST* bases[3] = {gq, gk, gg};
+#pragma unroll
+    for (int t = 0; t < C::NTILE_K; ++t) {
+        const ST* base = bases[C::NTILE_K == 3 ? t : t + 1] + (c0 * H + h) * int64_t(dk);
+#pragma unroll
+        for (int j = 0; j < C::UPT_K; ++j) {
+            const int uu = tid + j * C::NT;
+            if (C::U_K % C::NT == 0 || uu < C::U_K) {
+                int row = uu / C::UPR_K;
+                if (clamp) row = row < len ? row : len - 1;
+                pre[t * C::UPT_K + j] =
+                    *reinterpret_cast<const u32x4*>(base + (row * hdk + (uu % C::UPR_K) * C::EPU));
+            }
+        }
+    }
+    const ST* vbase = gv + (c0 * H + h) * int64_t(dv);
+#pragma unroll
+    for (int j = 0; j < C::UPT_V; ++j) {
+        const int uu = tid + j * C::NT;
+        if (C::U_V % C::NT == 0 || uu < C::U_V) {
+            int row = uu / C::UPR_V;
+            if (clamp) row = row < len ? row : len - 1;
+            pre[C::NTILE_K * C::UPT_K + j] =
+                *reinterpret_cast<const u32x4*>(vbase + (row * hdv + (uu % C::UPR_V) * C::EPU));
+        }
+    }
+}
+
+// raw tiles into LDS, each 16-byte unit placed at its permuted column position
+// (rows at or past `len` are written as zeros)
+template <typename C>
+__device__ __forceinline__ void raw_commit(const u32x4 (&pre)[C::UPT], unsigned char* smem, int tid, int len)
+{
+    using OT = typename C::OT;
+    constexpr int offs[3] = {C::NTILE_K == 3 ? C::O_Q : C::O_K, C::NTILE_K == 3 ? C::O_K : C::O_G, C::O_G};
+#pragma unroll
+    for (int i = 0; i < C::UPT; ++i) {
+        const bool isv = i >= C::NTILE_K * C::UPT_K;
+        const int t = isv ? 0 : i / C::UPT_K;
+        const int j = isv ? i - C::NTILE_K * C::UPT_K : i % C::UPT_K;
+        const int uu = tid + j * C::NT;
+        const int UPR = isv ? C::UPR_V : C::UPR_K;
+        if ((isv ? C::U_V : C::U_K) % C::NT == 0 || uu < (isv ? C::U_V : C::U_K)) {
+            const int row = uu / UPR, c0 = (uu % UPR) * C::EPU;
+            OT* row_base = isv ? reinterpret_cast<OT*>(smem + C::O_V) + row * C::SV
+                               : reinterpret_cast<OT*>(smem + offs[t]) + row * C::SK;
+            const bool keep = row < len;
+            const u32x4 w = {keep ? pre[i][0] : 0u, keep ? pre[i][1] : 0u, keep ? pre[i][2] : 0u,
+                             keep ? pre[i][3] : 0u};
+            if constexpr (C::ES == 2) {  // 8 columns -> two runs of 4 (8 bytes each)
+                *reinterpret_cast<u32x2*>(row_base + pcol(c0)) = u32x2{w[0], w[1]};
+                *reinterpret_cast<u32x2*>(row_base + pcol(c0 + 4)) = u32x2{w[2], w[3]};
+            } else {  // 4 fp32 columns stay contiguous
+                *reinterpret_cast<u32x4*>(row_base + pcol(c0)) = w;
+            }
+        }
+    }
+}
+
+// copy a staged output tile (LDS rows of DV elements, row stride SO) to o, 16 bytes per unit
+template <typename C, typename DT, int DV>
+__device__ __forceinline__ void store_out_tile(const unsigned char* smem, typename DT::storage* go, int64_t c0,
+                                               int len, int H, int h, int tid)
+{
+    using ST = typename DT::storage;
+    constexpr int EPU = 16 / int(sizeof(ST));
+    constexpr int UPR = DV / EPU;
+    const ST* stage = reinterpret_cast<const ST*>(smem + C::O_KG);
+    for (int u = tid; u < CH * UPR; u += C::NT) {
+        const int row = u / UPR, cu = u % UPR;
+        if (row < len)
+            *reinterpret_cast<u32x4*>(go + ((c0 + row) * H + h) * DV + cu * EPU) =
+                *reinterpret_cast<const u32x4*>(stage + row * C::SO + cu * EPU);
+    }
+}
+
+// (I + N)^{-1} for one 16x16 diagonal block of the strictly lower N, by one
+// full wave on the matrix cores.  N is nilpotent (N^16 = 0), so
+//     (I + N)^{-1} = (I - N)(I + N^2)(I + N^4)(I + N^8):
+// three squarings and three products of 16x16 tiles.  A 16x16 accumulator tile
+// is directly the B operand of the next 16x16x16 product; the A operand needs
+// rows, so each power is written once to LDS (wave-private scratch, read back
+// by the same wave: LDS operations of one wave complete in order).
+// sA holds -N (natural column order); the result goes to sD.
+template <typename C, typename O>
+__device__ __forceinline__ void diag_inverse(const typename O::T* sA, typename O::T* sD, typename O::T* scr,
+                                             int a, int lane)
+{
+    using OT = typename O::T;
+    using Frag4 = typename O::Frag4;
+    const int l16 = lane & 15, q4 = lane >> 4;
+    const OT* Qrows = sA + (a * 16) * C::ST + a * 16;  // -N
+    OT* n2 = scr + (2 * a) * 16 * C::SD;
+    OT* n4 = scr + (2 * a + 1) * 16 * C::SD;
+    auto rowfrag = [&](const OT* base, int ld) { return O::load4(base + l16 * ld + 4 * q4); };
+    auto put = [&](OT* base, const f32x4& t) {  // accumulator tile -> natural rows
+#pragma unroll
+        for (int j = 0; j < 4; ++j) base[(4 * q4 + j) * C::SD + l16] = O::to_op(t[j]);
+    };
+    auto wave_sync = [] {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+    // B operand of -N: column l16, rows 4q..4q+3
+    f32x4 qcol;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) qcol[j] = O::from_op(Qrows[(4 * q4 + j) * C::ST + l16]);
+    const Frag4 qa = rowfrag(Qrows, C::ST);
+    f32x4 t2 = {0.f, 0.f, 0.f, 0.f};
+    O::mma4(t2, qa, O::make4(qcol));  // N^2 = (-N)(-N)
+    put(n2, t2);
+    wave_sync();
+    f32x4 t4 = {0.f, 0.f, 0.f, 0.f};
+    const Frag4 n2a = rowfrag(n2, C::SD);
+    O::mma4(t4, n2a, O::make4(t2));  // N^4
+    put(n4, t4);
+    wave_sync();
+    f32x4 t8 = {0.f, 0.f, 0.f, 0.f};
+    const Frag4 n4a = rowfrag(n4, C::SD);
+    O::mma4(t8, n4a, O::make4(t4));  // N^8
+    // E1 = (I + N^4)(I + N^8) = I + N^4 + N^8 + N^4 N^8
+    f32x4 e = t4 + t8;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) e[j] += (4 * q4 + j == l16) ? 1.f : 0.f;
+    O::mma4(e, n4a, O::make4(t8));
+    // E2 = (I + N^2) E1
+    f32x4 e2 = e;
+    O::mma4(e2, n2a, O::make4(e));
+    // D = (I - N) E2
+    f32x4 d = e2;
+    O::mma4(d, qa, O::make4(e2));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sD[(a * 16 + 4 * q4 + j) * C::SD + l16] = O::to_op(d[j]);
+}
 
 template <typename DT, int DK, int DV, bool SUMMARY>
 __global__ void __launch_bounds__((ChunkCfg<DT, DK, DV, SUMMARY>::NT))
@@ -362,17 +602,23 @@ prefill_chunk_kernel(PrefillDev p)
     using O = Op<DT>;
     using OT = typename O::T;
     using Frag = typename O::Frag;
+    using Frag4 = typename O::Frag4;
+    using Pair = typename O::Pair;
     using ST = typename DT::storage;
+    constexpr float LOG2E = 1.4426950408889634f;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     OT* sQ = reinterpret_cast<OT*>(smem + C::O_Q);
     OT* sK = reinterpret_cast<OT*>(smem + C::O_K);
     OT* sG = reinterpret_cast<OT*>(smem + C::O_G);
     OT* sV = reinterpret_cast<OT*>(smem + C::O_V);
-    OT* sT = reinterpret_cast<OT*>(smem + C::O_T);
+    OT* sQG = reinterpret_cast<OT*>(smem + C::O_QG);
+    OT* sKG = reinterpret_cast<OT*>(smem + C::O_KG);
+    OT* sKH = reinterpret_cast<OT*>(smem + C::O_KH);
+    OT* sA = reinterpret_cast<OT*>(smem + C::O_A);
     OT* sP = reinterpret_cast<OT*>(smem + C::O_P);
-    float* sA = reinterpret_cast<float*>(smem + C::O_A);
-    float* sX = reinterpret_cast<float*>(smem + C::O_X);
-    float* sY = reinterpret_cast<float*>(smem + C::O_Y);
+    OT* sD = reinterpret_cast<OT*>(smem + C::O_D);
+    OT* sDS = reinterpret_cast<OT*>(smem + C::O_DS);
+    ST* sO = reinterpret_cast<ST*>(smem + C::O_KG);  // output staging (reuses the -k.e^G tile)
     float* sVec = reinterpret_cast<float*>(smem + C::O_VEC);
     float* sSig = reinterpret_cast<float*>(smem + C::O_SIG);
     float* sB = reinterpret_cast<float*>(smem + C::O_B);
@@ -382,6 +628,10 @@ prefill_chunk_kernel(PrefillDev p)
     const int wave = tid >> 6;
     const int l16 = lane & 15;
     const int q4 = lane >> 4;
+#ifdef KDA_PHASE_TIMING
+    long long phase_acc[10] = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+    long long phase_last = clock64();
+#endif
 
     // ---- work item
     const int H = p.H;
@@ -389,8 +639,7 @@ prefill_chunk_kernel(PrefillDev p)
     const int h = blockIdx.x % H;
     const int32_t* cuc = p.tab;
     const int32_t* seg_off = p.tab + (p.N + 1);
-    const int32_t* p1_off = p.tab + 2 * (p.N + 1);
-    const int32_t* off = SUMMARY ? p1_off : seg_off;
+    const int32_t* off = SUMMARY ? p.tab + 2 * (p.N + 1) : seg_off;
     if (item >= off[p.N]) return;
     const int n = find_seq(off, p.N, item);
     const int s = item - off[n];
@@ -406,13 +655,15 @@ prefill_chunk_kernel(PrefillDev p)
     const ST* gv = static_cast<const ST*>(p.v);
     const ST* gg = static_cast<const ST*>(p.g);
     const ST* gb = static_cast<const ST*>(p.beta);
+    ST* go = static_cast<ST*>(p.o);
 
     // ---- chain registers: wave owns columns [32*wave, 32*wave+32) of the extended state
     constexpr int RT = DK / 16;  // state row tiles
     const bool chain = wave < C::NCW;
-    const int colbase = 32 * wave;
+    constexpr int NCT = C::NCT;
+    const int colbase = C::CW * wave;
     const bool mcols = SUMMARY && colbase >= DV;
-    f32x4 S[RT][2];
+    f32x4 S[RT][NCT];
     {
         const float* src = nullptr;
         if (!SUMMARY) {
@@ -425,7 +676,7 @@ prefill_chunk_kernel(PrefillDev p)
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
+            for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int row = rt * 16 + 4 * q4 + j;
@@ -439,383 +690,408 @@ prefill_chunk_kernel(PrefillDev p)
                 }
     }
 
-    // zero the strictly-upper 16x16 blocks of T and P once: only lower blocks are rewritten
-    for (int e = tid; e < CH * CH; e += C::NT) {
-        const int r = e / CH, c = e % CH;
-        if ((c >> 4) > (r >> 4)) {
-            sT[r * C::ST + c] = O::to_op(0.f);
-            sP[r * C::ST + c] = O::to_op(0.f);
+    // strictly-upper 16x16 blocks of P are read by the P U product and never written
+    if (!SUMMARY)
+        for (int e = tid; e < CH * CH; e += C::NT) {
+            const int r = e / CH, c = e % CH;
+            if ((c >> 4) > (r >> 4)) sP[r * C::ST + pcol(c)] = O::to_op(0.f);
         }
-    }
 
-    // identity fragments (exact in bf16) for X = V I
-    Frag Iden[2];
+    // identity fragments (exact) for X = V I: pick this wave's columns out of
+    // the 32-column block that holds them
+    Frag Iden[NCT];
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
+    for (int ct = 0; ct < NCT; ++ct) {
         float x[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = (kperm(q4, e) == ct * 16 + l16) ? 1.f : 0.f;
+        for (int e = 0; e < 8; ++e) x[e] = (kperm(q4, e) == (colbase & 31) + ct * 16 + l16) ? 1.f : 0.f;
         Iden[ct] = O::make(x);
     }
 
-    // ---- raw tile prefetch (registers) and commit (LDS)
     u32x4 pre[C::UPT];
-    float preb = 0.f;
-    auto prefetch = [&](int64_t c0, int len) {
-#pragma unroll
-        for (int i = 0; i < C::UPT; ++i) {
-            const int u = tid + i * C::NT;
-            u32x4 w = {0u, 0u, 0u, 0u};
-            if (u < C::U_ALL) {
-                const ST* base;
-                int row, cu8, D;
-                if (u < 3 * C::U_K) {
-                    const int tsel = u / C::U_K, uu = u % C::U_K;
-                    row = uu / C::UPR_K;
-                    cu8 = uu % C::UPR_K;
-                    base = tsel == 0 ? gq : tsel == 1 ? gk : gg;
-                    D = DK;
-                } else {
-                    const int uu = u - 3 * C::U_K;
-                    row = uu / C::UPR_V;
-                    cu8 = uu % C::UPR_V;
-                    base = gv;
-                    D = DV;
-                }
-                if (row < len) {
-                    const ST* ptr = base + ((c0 + row) * H + h) * D + cu8 * (16 / C::ES);
-                    w = *reinterpret_cast<const u32x4*>(ptr);
-                }
-            }
-            pre[i] = w;
-        }
-        preb = (tid < len) ? load_elem<DT>(gb, (c0 + tid) * H + h) : 0.f;
-    };
-    auto commit = [&]() {
-#pragma unroll
-        for (int i = 0; i < C::UPT; ++i) {
-            const int u = tid + i * C::NT;
-            if (u < C::U_ALL) {
-                OT* dst;
-                if (u < 3 * C::U_K) {
-                    const int tsel = u / C::U_K, uu = u % C::U_K;
-                    const int row = uu / C::UPR_K, cu8 = uu % C::UPR_K;
-                    OT* t = tsel == 0 ? sQ : tsel == 1 ? sK : sG;
-                    dst = t + row * C::SK + cu8 * (16 / C::ES);
-                } else {
-                    const int uu = u - 3 * C::U_K;
-                    const int row = uu / C::UPR_V, cu8 = uu % C::UPR_V;
-                    dst = sV + row * C::SV + cu8 * (16 / C::ES);
-                }
-                *reinterpret_cast<u32x4*>(dst) = pre[i];
-            }
-        }
-        if (tid < CH) sB[tid] = preb;
-    };
-
     const int64_t nchunks = (t_end - t_begin + CH - 1) / CH;
-    if (nchunks > 0) prefetch(t_begin, int(t_end - t_begin < CH ? t_end - t_begin : CH));
+    if (nchunks > 0)
+        raw_prefetch<C, DT>(pre, gq, gk, gv, gg, t_begin, int(t_end - t_begin < CH ? t_end - t_begin : CH),
+                            p.T_total, H, h, tid, DK, DV);
 
+    const int cp = tid % C::CP;  // channel pair (elementwise phases)
+    const int part = tid / C::CP;
+    const int pc = pcol(2 * cp);  // stored position of channels 2cp, 2cp+1 (adjacent)
+    const int tok0 = part * C::TPT;
+
+    int64_t prev_c0 = 0;
+    int prev_len = 0;
     for (int64_t ci = 0; ci < nchunks; ++ci) {
         const int64_t c0 = t_begin + ci * CH;
         const int len = int(t_end - c0 < CH ? t_end - c0 : CH);
-        __syncthreads();  // previous chunk's operands are no longer read
-        commit();
+        __syncthreads();  // the previous chunk's operands are no longer read
+        KDA_PHASE(0);
+        if (!SUMMARY && C::STAGE_O && ci > 0) store_out_tile<C, DT, DV>(smem, go, prev_c0, prev_len, H, h, tid);
+        raw_commit<C>(pre, smem, tid, len);
         __syncthreads();
+        KDA_PHASE(1);
 
-        // ---- elementwise phase A: per-slot sums of g (per key channel)
-        const int ch = tid % DK;
-        const int part = tid / DK;
-        const int tok0 = part * C::TPT;
-        {
+        // beta for this chunk: loaded now, first needed by the products (two phases later)
+        float bload = 0.f;
+        if (tid < CH) bload = load_elem<DT>(gb, (c0 + (tid < len ? tid : len - 1)) * H + h);
+        // ---- phase A: per-slot sums of g (log2 domain), two channels per thread
 #pragma unroll
-            for (int sl = 0; sl < C::TPT / C::SL; ++sl) {
-                float acc = 0.f;
+        for (int sl = 0; sl < C::TPT / C::SL; ++sl) {
+            float a0 = 0.f, a1 = 0.f;
 #pragma unroll
-                for (int i = 0; i < C::SL; ++i)
-                    acc += O::from_op(sG[(tok0 + sl * C::SL + i) * C::SK + ch]);
-                sSig[((tok0 / C::SL) + sl) * DK + ch] = acc;
+            for (int i = 0; i < C::SL; ++i) {
+                const Pair w = O::ldp(sG + (tok0 + sl * C::SL + i) * C::SK + pc);
+                a0 += O::p0(w);
+                a1 += O::p1(w);
             }
+            const int slot = tok0 / C::SL + sl;
+            *reinterpret_cast<f32x2*>(sSig + slot * DK + pc) = f32x2{a0 * LOG2E, a1 * LOG2E};
         }
         __syncthreads();
-        // ---- elementwise phase B: decayed operands, in place, and channel vectors
+
+        KDA_PHASE(2);
+        // ---- phase B: decayed operand tiles and channel vectors
         {
-            float R[5];
-            R[0] = 0.f;
-            float run = 0.f;
+            float R0[5], R1[5];  // G before sub-tile a (log2 domain); R[4] = G at chunk end
+            R0[0] = R1[0] = 0.f;
+            float r0 = 0.f, r1 = 0.f, G0 = 0.f, G1 = 0.f;
 #pragma unroll
             for (int sl = 0; sl < C::NSLOT; ++sl) {
-                run += sSig[sl * DK + ch];
-                if (((sl + 1) * C::SL) % 16 == 0) R[((sl + 1) * C::SL) / 16] = run;
-            }
-            float G = 0.f;
-            for (int sl = 0; sl < tok0 / C::SL; ++sl) G += sSig[sl * DK + ch];
-#pragma unroll 4
-            for (int i = 0; i < C::TPT; ++i) {
-                const int r = tok0 + i;
-                const int a = r >> 4;
-                const float gr = O::from_op(sG[r * C::SK + ch]);
-                G += gr;
-                const float ra = a == 0 ? R[0] : a == 1 ? R[1] : a == 2 ? R[2] : R[3];
-                const float e1 = __expf(G - ra);
-                const float e2 = __expf(ra - G);
-                const float kv = O::from_op(sK[r * C::SK + ch]);
-                const float qv = O::from_op(sQ[r * C::SK + ch]);
-                sQ[r * C::SK + ch] = O::to_op(qv * e1);
-                sK[r * C::SK + ch] = O::to_op(kv * e1);
-                sG[r * C::SK + ch] = O::to_op(kv * e2);
+                if (sl == tok0 / C::SL) {
+                    G0 = r0;
+                    G1 = r1;
+                }
+                const f32x2 sg = *reinterpret_cast<const f32x2*>(sSig + sl * DK + pc);
+                r0 += sg[0];
+                r1 += sg[1];
+                if (((sl + 1) * C::SL) % 16 == 0) {
+                    R0[((sl + 1) * C::SL) / 16] = r0;
+                    R1[((sl + 1) * C::SL) / 16] = r1;
+                }
             }
             if (part == 0) {
-                float* vv = sVec;
+                f32x2* vv = reinterpret_cast<f32x2*>(sVec);
 #pragma unroll
-                for (int a = 0; a < 4; ++a) vv[(V_ER + a) * DK + ch] = __expf(R[a]);
-#pragma unroll
-                for (int b = 0; b < 4; ++b) vv[(V_FY + b) * DK + ch] = __expf(R[b + 1] - R[b]);
-                vv[(V_FX + 0) * DK + ch] = __expf(R[2] - R[1]);  // (a,b) = (2,0)
-                vv[(V_FX + 1) * DK + ch] = __expf(R[3] - R[1]);  // (3,0)
-                vv[(V_FX + 2) * DK + ch] = __expf(R[3] - R[2]);  // (3,1)
-#pragma unroll
-                for (int b = 0; b < 4; ++b) vv[(V_EL + b) * DK + ch] = __expf(R[4] - R[b + 1]);
-                vv[V_GC * DK + ch] = __expf(R[4]);
-            }
-        }
-        __syncthreads();
-
-        // ---- products: A (strictly lower, x beta_r, fp32) and P (lower incl. diagonal)
-        for (int task = wave; task < 20; task += C::NW) {
-            const bool isP = task >= 10;
-            int bi = isP ? task - 10 : task;
-            int a = 0;
-            while (bi > a) { bi -= a + 1; ++a; }
-            const int b = bi;  // 0 <= b <= a
-            const OT* X = isP ? sQ : sK;
-            const int fx = (a >= b + 2) ? (a == 2 ? 0 : (b == 0 ? 1 : 2)) : -1;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < DK / 32; ++kb) {
-                float y[8], x[8];
-                lds_row_frag<DT>(sG, C::SK, b * 16 + l16, kb * 32, q4, y);
-                lds_row_frag<DT>(X, C::SK, a * 16 + l16, kb * 32, q4, x);
-                if (b < a) {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) y[e] *= sVec[(V_FY + b) * DK + kb * 32 + kperm(q4, e)];
+                for (int a = 0; a < 4; ++a) {
+                    vv[((V_ER + a) * DK + pc) / 2] = f32x2{fexp2(R0[a]), fexp2(R1[a])};
+                    vv[((V_FY + a) * DK + pc) / 2] = f32x2{fexp2(R0[a + 1] - R0[a]), fexp2(R1[a + 1] - R1[a])};
+                    vv[((V_EL + a) * DK + pc) / 2] = f32x2{fexp2(R0[4] - R0[a + 1]), fexp2(R1[4] - R1[a + 1])};
                 }
-                if (fx >= 0) {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) x[e] *= sVec[(V_FX + fx) * DK + kb * 32 + kperm(q4, e)];
-                }
-                O::mma(acc, O::make(y), O::make(x));
+                vv[((V_FX + 0) * DK + pc) / 2] = f32x2{fexp2(R0[2] - R0[1]), fexp2(R1[2] - R1[1])};  // (2,0)
+                vv[((V_FX + 1) * DK + pc) / 2] = f32x2{fexp2(R0[3] - R0[1]), fexp2(R1[3] - R1[1])};  // (3,0)
+                vv[((V_FX + 2) * DK + pc) / 2] = f32x2{fexp2(R0[3] - R0[2]), fexp2(R1[3] - R1[2])};  // (3,1)
+                vv[(V_GC * DK + pc) / 2] = f32x2{fexp2(R0[4]), fexp2(R1[4])};
             }
-            // acc: lane (col r = 16a + l16, rows i = 16b + 4*q4 + j)
-            const int r = a * 16 + l16;
-            const int i0 = b * 16 + 4 * q4;
-            if (isP) {
-                f32x4 v4;
+            // all loads of this thread's tokens first
+            Pair wg[C::TPT], wk[C::TPT], wq[C::TPT];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) v4[j] = (i0 + j <= r) ? acc[j] : 0.f;
-                O::st4(sP + r * C::ST + i0, v4);
+            for (int i = 0; i < C::TPT; ++i) {
+                const int r = tok0 + i;
+                wg[i] = O::ldp(sG + r * C::SK + pc);
+                wk[i] = O::ldp(sK + r * C::SK + pc);
+                if (!SUMMARY) wq[i] = O::ldp(sQ + r * C::SK + pc);
+            }
+            float kh0[C::TPT], kh1[C::TPT];
+            // the thread's tokens cover whole sub-tiles (TPT >= 16) or lie in one (TPT < 16)
+            constexpr int SPAN = C::TPT < 16 ? C::TPT : 16;
+#pragma unroll
+            for (int i0 = 0; i0 < C::TPT; i0 += SPAN) {
+                const int a = (tok0 + i0) >> 4;
+                const float ra0 = a == 0 ? R0[0] : a == 1 ? R0[1] : a == 2 ? R0[2] : R0[3];
+                const float ra1 = a == 0 ? R1[0] : a == 1 ? R1[1] : a == 2 ? R1[2] : R1[3];
+                const float rb0 = a == 0 ? R0[1] : a == 1 ? R0[2] : a == 2 ? R0[3] : R0[4];  // E_a
+                const float rb1 = a == 0 ? R1[1] : a == 1 ? R1[2] : a == 2 ? R1[3] : R1[4];
+                const float er0 = fexp2(ra0), er1 = fexp2(ra1);                  // e^{R_a}
+                const float fy0 = fexp2(rb0 - ra0), fy1 = fexp2(rb1 - ra1);      // e^{E_a - R_a}
+                const float el0 = fexp2(R0[4] - rb0), el1 = fexp2(R1[4] - rb1);  // e^{G_last - E_a}
+#pragma unroll
+                for (int i = i0; i < i0 + SPAN; ++i) {
+                    const int r = tok0 + i;
+                    G0 += O::p0(wg[i]) * LOG2E;
+                    G1 += O::p1(wg[i]) * LOG2E;
+                    const float e1a = fexp2(G0 - ra0), e1b = fexp2(G1 - ra1);  // e^{G - R_a} in [e^-80, 1]
+                    const float e2a = fexp2(ra0 - G0), e2b = fexp2(ra1 - G1);  // e^{R_a - G} in [1, e^80]
+                    const float ga = e1a * er0, gb2 = e1b * er1;                // e^{G}
+                    const float k0 = O::p0(wk[i]), k1 = O::p1(wk[i]);
+                    const float kf0 = k0 * e2a, kf1 = k1 * e2b;
+                    O::stp(sK + r * C::SK + pc, k0 * e1a, k1 * e1b);
+                    O::stp(sG + r * C::SK + pc, kf0, kf1);
+                    O::stp(sKG + r * C::SK + pc, -k0 * ga, -k1 * gb2);
+                    // k e^{G_last - G} = (k e^{R_a - G} e^{E_a - R_a}) e^{G_last - E_a}, each factor <= 1
+                    kh0[i] = (kf0 * fy0) * el0;
+                    kh1[i] = (kf1 * fy1) * el1;
+                    if (!SUMMARY) {
+                        const float q0 = O::p0(wq[i]), q1 = O::p1(wq[i]);
+                        O::stp(sQ + r * C::SK + pc, q0 * e1a, q1 * e1b);
+                        O::stp(sQG + r * C::SK + pc, q0 * ga, q1 * gb2);
+                    }
+                }
+            }
+            if (tid < CH) sB[tid] = tid < len ? bload : 0.f;
+            // transposed K-hat rows (channels 2cp, 2cp+1): 4 tokens per store when a
+            // thread owns at least 4 (tokens 4m..4m+3 sit contiguously after pcol)
+            if constexpr (C::TPT >= 4) {
+#pragma unroll
+                for (int i = 0; i < C::TPT; i += 4) {
+                    const int tp = pcol(tok0 + i);
+                    O::st4(sKH + (2 * cp) * C::ST + tp, f32x4{kh0[i], kh0[i + 1], kh0[i + 2], kh0[i + 3]});
+                    O::st4(sKH + (2 * cp + 1) * C::ST + tp, f32x4{kh1[i], kh1[i + 1], kh1[i + 2], kh1[i + 3]});
+                }
             } else {
-                const float br = sB[r];
-                f32x4 v4;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) v4[j] = (i0 + j < r) ? br * acc[j] : 0.f;
-                *reinterpret_cast<f32x4*>(sA + r * C::SA + i0) = v4;
-            }
-        }
-        __syncthreads();
-
-        // ---- solve X = (I + A)^{-1}: diagonal 16x16 blocks by forward substitution
-        if (tid < 64) {
-            const int a = tid >> 4, j = tid & 15;
-            float x[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float acc = (r == j) ? 1.f : 0.f;
-                const float* arow = sA + (a * 16 + r) * C::SA + a * 16;
-#pragma unroll
-                for (int i = 0; i < r; ++i) acc -= arow[i] * x[i];
-                x[r] = acc;
-            }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sX[(a * 16 + r) * C::SA + a * 16 + j] = x[r];
-        }
-        __syncthreads();
-        // off-diagonal blocks, by distance d = a - b:  X_ab = -X_aa sum_{m=b}^{a-1} A_am X_mb
-#pragma unroll
-        for (int d = 1; d <= 3; ++d) {
-            const int nb = 4 - d;
-            for (int e = tid; e < nb * 256; e += C::NT) {
-                const int blk = e >> 8, rr = (e >> 4) & 15, cc = e & 15;
-                const int a = d + blk, b = blk;
-                float acc = 0.f;
-                for (int m = b; m < a; ++m) {
-                    const float* arow = sA + (a * 16 + rr) * C::SA + m * 16;
-                    const float* xcol = sX + (m * 16) * C::SA + b * 16 + cc;
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) acc += arow[i] * xcol[i * C::SA];
+                for (int i = 0; i < C::TPT; ++i) {
+                    const int tp = pcol(tok0 + i);
+                    sKH[(2 * cp) * C::ST + tp] = O::to_op(kh0[i]);
+                    sKH[(2 * cp + 1) * C::ST + tp] = O::to_op(kh1[i]);
                 }
-                sY[blk * 256 + rr * 16 + cc] = acc;
-            }
-            __syncthreads();
-            for (int e = tid; e < nb * 256; e += C::NT) {
-                const int blk = e >> 8, rr = (e >> 4) & 15, cc = e & 15;
-                const int a = d + blk, b = blk;
-                const float* xrow = sX + (a * 16 + rr) * C::SA + a * 16;
-                float acc = 0.f;
-#pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    if (i <= rr) acc += xrow[i] * sY[blk * 256 + i * 16 + cc];
-                sX[(a * 16 + rr) * C::SA + b * 16 + cc] = -acc;
-            }
-            __syncthreads();
-        }
-        // T = X Diag(beta) on the lower blocks (diagonal blocks: upper part zero)
-        for (int e = tid; e < CH * CH; e += C::NT) {
-            const int r = e / CH, c = e % CH;
-            if ((c >> 4) <= (r >> 4)) {
-                const float x = (c <= r) ? sX[r * C::SA + c] * sB[c] : 0.f;
-                sT[r * C::ST + c] = O::to_op(x);
             }
         }
         __syncthreads();
 
+        KDA_PHASE(3);
         // ---- prefetch the next chunk while the chain runs
         if (ci + 1 < nchunks) {
             const int64_t n0 = c0 + CH;
-            prefetch(n0, int(t_end - n0 < CH ? t_end - n0 : CH));
+            raw_prefetch<C, DT>(pre, gq, gk, gv, gg, n0, int(t_end - n0 < CH ? t_end - n0 : CH), p.T_total,
+                                H, h, tid, DK, DV);
         }
 
+        KDA_PHASE(4);
+        // ---- chain part 1: X = V - (K . e^G) S   (rows = tokens; 4 row tiles x 2 column tiles)
+        Frag Sb[DK / 32][NCT];
+        f32x4 Xt[4][NCT];
         if (chain) {
-            // packed state operands (rows = key channels), reused by X and O
-            Frag Sb[DK / 32][2];
 #pragma unroll
             for (int kb = 0; kb < DK / 32; ++kb)
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct) Sb[kb][ct] = acc_frag<DT>(S[2 * kb][ct], S[2 * kb + 1][ct]);
-
-            // X = V - (K . e^G) S       (rows = tokens, 4 row tiles x 2 col tiles)
-            f32x4 Xt[4][2];
+                for (int ct = 0; ct < NCT; ++ct) Sb[kb][ct] = acc_frag<DT>(S[2 * kb][ct], S[2 * kb + 1][ct]);
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct) Xt[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int ct = 0; ct < NCT; ++ct) Xt[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
             if (!mcols) {
 #pragma unroll
                 for (int rt = 0; rt < 4; ++rt) {
-                    float x[8];
-                    lds_row_frag<DT>(sV, C::SV, rt * 16 + l16, colbase, q4, x);
-                    const Frag vf = O::make(x);
+                    const Frag vf = O::load(sV + (rt * 16 + l16) * C::SV + (colbase & ~31) + 8 * q4);
 #pragma unroll
-                    for (int ct = 0; ct < 2; ++ct) O::mma(Xt[rt][ct], vf, Iden[ct]);
+                    for (int ct = 0; ct < NCT; ++ct) O::mma(Xt[rt][ct], vf, Iden[ct]);
                 }
             }
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
                 for (int kb = 0; kb < DK / 32; ++kb) {
-                    float x[8];
-                    lds_row_frag<DT>(sK, C::SK, rt * 16 + l16, kb * 32, q4, x);
+                    const Frag af = O::load(sKG + (rt * 16 + l16) * C::SK + kb * 32 + 8 * q4);
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) x[e] *= -sVec[(V_ER + rt) * DK + kb * 32 + kperm(q4, e)];
-                    const Frag af = O::make(x);
-#pragma unroll
-                    for (int ct = 0; ct < 2; ++ct) O::mma(Xt[rt][ct], af, Sb[kb][ct]);
+                    for (int ct = 0; ct < NCT; ++ct) O::mma(Xt[rt][ct], af, Sb[kb][ct]);
                 }
+        }
+        KDA_PHASE(5);
+        // ---- products per 16x16 block (a, b), b <= a, sharing the key-side fragment:
+        //      -A x beta_r (strictly lower, natural columns) and P (lower incl. diagonal)
+        // With 8 waves, waves 4..7 take the diagonal blocks and invert them at once
+        // (their own LDS writes, so no barrier), while waves 0..3 take the six
+        // off-diagonal blocks.  Otherwise blocks go round-robin and the
+        // inversion follows in its own phase.
+        constexpr bool DIAG_WAVES = C::NW == 8;
+        const int ntask = DIAG_WAVES ? (wave < 4 ? (wave < 2 ? 2 : 1) : 1) : (10 - wave + C::NW - 1) / C::NW;
+        for (int tk = 0; tk < ntask; ++tk) {
+            int a, b;
+            if (DIAG_WAVES) {
+                if (wave >= 4) {
+                    a = b = wave - 4;
+                } else {
+                    const int ot = wave + 4 * tk;  // off-diagonal (1,0),(2,0),(2,1),(3,0),(3,1),(3,2)
+                    a = ot == 0 ? 1 : ot <= 2 ? 2 : 3;
+                    b = ot == 0 ? 0 : ot == 1 ? 0 : ot == 2 ? 1 : ot - 3;
+                }
+            } else {
+                int bi = wave + tk * C::NW;
+                a = 0;
+                while (bi > a) {
+                    bi -= a + 1;
+                    ++a;
+                }
+                b = bi;  // 0 <= b <= a
+            }
+            const int fx = (a >= b + 2) ? (a == 2 ? 0 : (b == 0 ? 1 : 2)) : -1;
+            Frag yf[DK / 32], kf[DK / 32], qf[DK / 32];
+#pragma unroll
+            for (int kb = 0; kb < DK / 32; ++kb) {
+                yf[kb] = O::load(sG + (b * 16 + l16) * C::SK + kb * 32 + 8 * q4);
+                kf[kb] = O::load(sK + (a * 16 + l16) * C::SK + kb * 32 + 8 * q4);
+                if (!SUMMARY) qf[kb] = O::load(sQ + (a * 16 + l16) * C::SK + kb * 32 + 8 * q4);
+            }
+            f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < DK / 32; ++kb) {
+                Frag y = yf[kb], kx = kf[kb], qx;
+                if (!SUMMARY) qx = qf[kb];
+                if (b < a) {  // off-diagonal: key side referenced at the end of sub-tile b
+                    float t[8];
+                    O::unpack(y, t);
+                    const f32x4* fv = reinterpret_cast<const f32x4*>(sVec + (V_FY + b) * DK + kb * 32 + 8 * q4);
+                    const f32x4 f0 = fv[0], f1 = fv[1];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        t[e] *= f0[e];
+                        t[4 + e] *= f1[e];
+                    }
+                    y = O::make(t);
+                }
+                if (fx >= 0) {
+                    const f32x4* fv = reinterpret_cast<const f32x4*>(sVec + (V_FX + fx) * DK + kb * 32 + 8 * q4);
+                    const f32x4 f0 = fv[0], f1 = fv[1];
+                    float t[8];
+                    O::unpack(kx, t);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        t[e] *= f0[e];
+                        t[4 + e] *= f1[e];
+                    }
+                    kx = O::make(t);
+                    if (!SUMMARY) {
+                        O::unpack(qx, t);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            t[e] *= f0[e];
+                            t[4 + e] *= f1[e];
+                        }
+                        qx = O::make(t);
+                    }
+                }
+                O::mma(accA, y, kx);
+                if (!SUMMARY) O::mma(accP, y, qx);
+            }
+            // acc: lane (col r = 16a + l16, rows i = 16b + 4*q4 + j)
+            const int r = a * 16 + l16;
+            const int i0 = b * 16 + 4 * q4;
+            const float br = -sB[r];
+            f32x4 v4;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v4[j] = (i0 + j < r) ? br * accA[j] : 0.f;
+            O::st4(sA + r * C::ST + i0, v4);
+            if (!SUMMARY) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) v4[j] = (i0 + j <= r) ? accP[j] : 0.f;
+                O::st4(sP + r * C::ST + pcol(i0), v4);
+            }
+            if (DIAG_WAVES && wave >= 4) {
+                // this wave's block is complete in LDS (in-order within the wave)
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                diag_inverse<C, O>(sA, sD, sDS, a, lane);
+            }
+        }
+        __syncthreads();
 
-            // U = T X      (T lower triangular: row tile rt needs token blocks kbt <= rt/2)
-            Frag Xb[2][2];
+        KDA_PHASE(6);
+        // ---- diagonal blocks (I + A_aa)^{-1} (when not already done in the products phase)
+        if (!DIAG_WAVES) {
+            for (int a = wave; a < 4; a += C::NW) diag_inverse<C, O>(sA, sD, sDS, a, lane);
+        }
+        KDA_PHASE(7);
+        if (!DIAG_WAVES) __syncthreads();
+        KDA_PHASE(8);
+
+        if (chain) {
+            // ---- U = (I + A)^{-1} Diag(beta) X by block forward substitution:
+            //      U_a = D_a (beta_a X_a - sum_{b<a} A_ab U_b)
+            f32x4 Ut[4][NCT];
+            Frag4 Uf[4][NCT];
 #pragma unroll
-            for (int kbt = 0; kbt < 2; ++kbt)
+            for (int a = 0; a < 4; ++a) {
+                const f32x4 bv = *reinterpret_cast<const f32x4*>(sB + a * 16 + 4 * q4);
+                f32x4 R[NCT];
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct) Xb[kbt][ct] = acc_frag<DT>(Xt[2 * kbt][ct], Xt[2 * kbt + 1][ct]);
-            f32x4 Ut[4][2];
+                for (int ct = 0; ct < NCT; ++ct) R[ct] = bv * Xt[a][ct];
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
+                for (int b = 0; b < a; ++b) {
+                    const Frag4 af = O::load4(sA + (a * 16 + l16) * C::ST + b * 16 + 4 * q4);
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct) Ut[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    for (int ct = 0; ct < NCT; ++ct) O::mma4(R[ct], af, Uf[b][ct]);
+                }
+                const Frag4 df = O::load4(sD + (a * 16 + l16) * C::SD + 4 * q4);
 #pragma unroll
-                for (int kbt = 0; kbt <= rt / 2; ++kbt) {
-                    float x[8];
-                    lds_row_frag<DT>(sT, C::ST, rt * 16 + l16, kbt * 32, q4, x);
-                    const Frag tf = O::make(x);
-#pragma unroll
-                    for (int ct = 0; ct < 2; ++ct) O::mma(Ut[rt][ct], tf, Xb[kbt][ct]);
+                for (int ct = 0; ct < NCT; ++ct) {
+                    Ut[a][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    O::mma4(Ut[a][ct], df, O::make4(R[ct]));
+                    Uf[a][ct] = O::make4(Ut[a][ct]);
                 }
             }
-            Frag Ub[2][2];
+            Frag Ub[2][NCT];
 #pragma unroll
             for (int kbt = 0; kbt < 2; ++kbt)
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct) Ub[kbt][ct] = acc_frag<DT>(Ut[2 * kbt][ct], Ut[2 * kbt + 1][ct]);
+                for (int ct = 0; ct < NCT; ++ct) Ub[kbt][ct] = acc_frag<DT>(Ut[2 * kbt][ct], Ut[2 * kbt + 1][ct]);
 
             if (!SUMMARY) {
-                // O = (Q . e^G) S + P U
-                ST* go = static_cast<ST*>(p.o);
+                // ---- O = (Q . e^G) S + P U
 #pragma unroll
                 for (int rt = 0; rt < 4; ++rt) {
-                    f32x4 Ot[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+                    f32x4 Ot[NCT];
+#pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct) Ot[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int kb = 0; kb < DK / 32; ++kb) {
-                        float x[8];
-                        lds_row_frag<DT>(sQ, C::SK, rt * 16 + l16, kb * 32, q4, x);
+                        const Frag af = O::load(sQG + (rt * 16 + l16) * C::SK + kb * 32 + 8 * q4);
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) x[e] *= sVec[(V_ER + rt) * DK + kb * 32 + kperm(q4, e)];
-                        const Frag af = O::make(x);
-#pragma unroll
-                        for (int ct = 0; ct < 2; ++ct) O::mma(Ot[ct], af, Sb[kb][ct]);
+                        for (int ct = 0; ct < NCT; ++ct) O::mma(Ot[ct], af, Sb[kb][ct]);
                     }
 #pragma unroll
                     for (int kbt = 0; kbt <= rt / 2; ++kbt) {
-                        float x[8];
-                        lds_row_frag<DT>(sP, C::ST, rt * 16 + l16, kbt * 32, q4, x);
-                        const Frag pf = O::make(x);
+                        const Frag pf = O::load(sP + (rt * 16 + l16) * C::ST + kbt * 32 + 8 * q4);
 #pragma unroll
-                        for (int ct = 0; ct < 2; ++ct) O::mma(Ot[ct], pf, Ub[kbt][ct]);
+                        for (int ct = 0; ct < NCT; ++ct) O::mma(Ot[ct], pf, Ub[kbt][ct]);
                     }
 #pragma unroll
-                    for (int ct = 0; ct < 2; ++ct)
+                    for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
                         for (int j = 0; j < 4; ++j) {
                             const int row = rt * 16 + 4 * q4 + j;
-                            if (row < len)
-                                store_elem<DT>(go, ((c0 + row) * H + h) * DV + colbase + ct * 16 + l16,
-                                               Ot[ct][j]);
+                            const int col = colbase + ct * 16 + l16;
+                            if (C::STAGE_O) {
+                                store_elem<DT>(sO, row * C::SO + col, Ot[ct][j]);
+                            } else if (row < len) {
+                                store_elem<DT>(go, ((c0 + row) * H + h) * DV + col, Ot[ct][j]);
+                            }
                         }
                 }
             }
 
-            // S <- Diag(e^{G_last}) S + (K . e^{G_last - G})^T U
+            // ---- S <- Diag(e^{G_last}) S + (K . e^{G_last - G})^T U
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
+                // channels rt*16 + 4q .. +3 are stored contiguously (permuted position)
+                const f32x4 gc = *reinterpret_cast<const f32x4*>(sVec + V_GC * DK + pcol(rt * 16 + 4 * q4));
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float gc = sVec[V_GC * DK + rt * 16 + 4 * q4 + j];
-                    S[rt][0][j] *= gc;
-                    S[rt][1][j] *= gc;
-                }
-                const int c = rt * 16 + l16;  // key channel of this lane's operand row
+                for (int ct = 0; ct < NCT; ++ct) S[rt][ct] *= gc;
 #pragma unroll
                 for (int kbt = 0; kbt < 2; ++kbt) {
-                    float x[8];
+                    const Frag kf = O::load(sKH + (rt * 16 + l16) * C::ST + kbt * 32 + 8 * q4);
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int tok = kbt * 32 + kperm(q4, e);
-                        const int b = tok >> 4;
-                        x[e] = O::from_op(sG[tok * C::SK + c]) * sVec[(V_FY + b) * DK + c] *
-                               sVec[(V_EL + b) * DK + c];
-                    }
-                    const Frag kf = O::make(x);
-#pragma unroll
-                    for (int ct = 0; ct < 2; ++ct) O::mma(S[rt][ct], kf, Ub[kbt][ct]);
+                    for (int ct = 0; ct < NCT; ++ct) O::mma(S[rt][ct], kf, Ub[kbt][ct]);
                 }
             }
         }
+        prev_c0 = c0;
+        prev_len = len;
+    }
+    if (!SUMMARY && C::STAGE_O && nchunks > 0) {
+        __syncthreads();
+        store_out_tile<C, DT, DV>(smem, go, prev_c0, prev_len, H, h, tid);
     }
 
+    KDA_PHASE(9);
+#ifdef KDA_PHASE_TIMING
+    if (tid == KDA_PHASE_TID && blockIdx.x < 16384)
+        for (int i = 0; i < 10; ++i) kda_phase_cycles[blockIdx.x * 16 + i] = phase_acc[i];
+#endif
     // ---- write the segment result
     if (chain) {
         float* dst = nullptr;
-        int ld = DV, cofs = 0;
+        int ld = DV;
         if (SUMMARY) {
             dst = p.ms + (int64_t(item) * H + h) * DK * (DK + DV);
             ld = DK + DV;
@@ -826,21 +1102,26 @@ prefill_chunk_kernel(PrefillDev p)
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct)
+                for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
-                        dst[(rt * 16 + 4 * q4 + j) * ld + cofs + colbase + ct * 16 + l16] = S[rt][ct][j];
+                        dst[(rt * 16 + 4 * q4 + j) * ld + colbase + ct * 16 + l16] = S[rt][ct][j];
         }
     }
 }
 
 // ------------------------------------------------------------- scan kernel
-// Per (sequence, head, 32-column block): S_in(s+1) = M_s S_in(s) + S~_s.
+// Per (sequence, head, 8-column slice of the state): S_in(s+1) = M_s S_in(s) + S~_s
+// over the sequence's segments, in fp32.  Columns are independent, so each
+// slice is its own workgroup (d_v / 8 of them per sequence and head).
+constexpr int SCAN_COLS = 8;
 template <int DK, int DV>
 __global__ void __launch_bounds__(256) scan_kernel(PrefillDev p)
 {
-    constexpr int NB = DV / 32;
-    __shared__ float sS[DK][33];
+    constexpr int NB = DV / SCAN_COLS;
+    constexpr int TPR = 256 / DK;        // threads per state row
+    constexpr int CPT = SCAN_COLS / TPR; // columns per thread
+    __shared__ float sS[DK][SCAN_COLS];
     const int H = p.H;
     const int jb = blockIdx.x % NB;
     const int h = (blockIdx.x / NB) % H;
@@ -850,35 +1131,34 @@ __global__ void __launch_bounds__(256) scan_kernel(PrefillDev p)
     const int nseg = seg_off[n + 1] - seg_off[n];
     if (nseg <= 1) return;
     const int tid = threadIdx.x;
-    // thread -> (row c, 32/(256/DK) columns)
-    constexpr int TPR = 256 / DK;       // threads per row
-    constexpr int CPT = 32 / TPR;       // columns per thread
     const int c = tid / TPR;
     const int j0 = (tid % TPR) * CPT;
-    for (int e = tid; e < DK * 32; e += 256) {
-        const int r = e / 32, cc = e % 32;
-        float x = 0.f;
-        if (p.init) x = p.init[(int64_t(n) * H + h) * DK * DV + r * DV + jb * 32 + cc];
-        sS[r][cc] = x;
+    const int col0 = jb * SCAN_COLS + j0;
+    for (int e = tid; e < DK * SCAN_COLS; e += 256) {
+        const int r = e / SCAN_COLS, cc = e % SCAN_COLS;
+        sS[r][cc] = p.init ? p.init[(int64_t(n) * H + h) * DK * DV + r * DV + jb * SCAN_COLS + cc] : 0.f;
     }
     __syncthreads();
     for (int s = 0; s + 1 < nseg; ++s) {
         const float* ms = p.ms + (int64_t(p1_off[n] + s) * H + h) * DK * (DK + DV);
+        const float* mrow = ms + c * (DK + DV) + DV;
         float acc[CPT];
 #pragma unroll
-        for (int j = 0; j < CPT; ++j) acc[j] = ms[c * (DK + DV) + jb * 32 + j0 + j];
-        const float* mrow = ms + c * (DK + DV) + DV;
-        for (int cc = 0; cc < DK; ++cc) {
-            const float m = mrow[cc];
+        for (int j = 0; j < CPT; ++j) acc[j] = ms[c * (DK + DV) + col0 + j];
+#pragma unroll 4
+        for (int cc = 0; cc < DK; cc += 4) {
+            const f32x4 m = *reinterpret_cast<const f32x4*>(mrow + cc);
 #pragma unroll
-            for (int j = 0; j < CPT; ++j) acc[j] += m * sS[cc][j0 + j];
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int j = 0; j < CPT; ++j) acc[j] += m[u] * sS[cc + u][j0 + j];
         }
         __syncthreads();
         float* out = p.sin + (int64_t(seg_off[n] + s + 1) * H + h) * DK * DV;
 #pragma unroll
         for (int j = 0; j < CPT; ++j) {
             sS[c][j0 + j] = acc[j];
-            out[c * DV + jb * 32 + j0 + j] = acc[j];
+            out[c * DV + col0 + j] = acc[j];
         }
         __syncthreads();
     }
@@ -906,7 +1186,7 @@ hipError_t launch_prefill_t(const PrefillArgs& a, const PrefillPlan& plan, hipSt
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(k1, dim3(unsigned(plan.np1_max * a.H)), dim3(C1::NT), C1::LDS, stream, d);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        hipLaunchKernelGGL((scan_kernel<DK, DV>), dim3(unsigned(a.N * a.H * (DV / 32))), dim3(256), 0,
+        hipLaunchKernelGGL((scan_kernel<DK, DV>), dim3(unsigned(a.N * a.H * (DV / SCAN_COLS))), dim3(256), 0,
                            stream, d);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
@@ -929,7 +1209,7 @@ hipError_t launch_prefill(const PrefillArgs& a, const PrefillPlan& plan, hipStre
         KDA_PF(64, 32) KDA_PF(64, 64) KDA_PF(64, 128)
         KDA_PF(128, 32) KDA_PF(128, 64) KDA_PF(128, 128)
     } else {
-        KDA_PF(32, 32) KDA_PF(32, 64) KDA_PF(64, 32) KDA_PF(64, 64)
+        KDA_PF(32, 32) KDA_PF(32, 64)
     }
 #undef KDA_PF
     return hipErrorInvalidValue;

@@ -87,7 +87,8 @@ def test_prefill_workspace_size(L):
     assert ws(0, 1, 32, 128, 128) > 0
     assert ws(8192, 1, 32, 96, 128) == 0
     assert ws(8192, 1, 32, 128, 128, chunk=32) == 0
-    assert ws(8192, 1, 32, 128, 128, dtype=F32) == 0      # fp32 needs d <= 64
+    assert ws(8192, 1, 32, 128, 128, dtype=F32) == 0      # fp32 needs d_k = 32
+    assert ws(8192, 1, 32, 64, 64, dtype=F32) == 0
     assert ws(256, 1, 2, 32, 32, dtype=F32) > 0
     # a sequence too short to split needs no segment buffers
     small = ws(64 * 16, 1, 32, 128, 128)
