@@ -94,8 +94,10 @@ PREFILL_1M = Workload("prefill_1m", H=8, dk=128, dv=128, seqlens=(1 << 20,), dty
                       z_shift=3.0, seed=1002)
 DECODE_B256 = Workload("decode_b256", H=32, dk=128, dv=128, seqlens=(1,) * 256, dtype="bf16",
                        state_std=0.1, seed=1003)
+# lengths drawn with seed 1015: the first seed from 1004 up whose 64 lengths sum
+# to within 3% of the ~1M tokens the workload describes (1,026,790 tokens)
 VARLEN_64 = Workload("varlen_64", H=32, dk=128, dv=128,
-                     seqlens=varlen_lengths(64, 1024, 65536, 1004), dtype="bf16",
+                     seqlens=varlen_lengths(64, 1024, 65536, 1015), dtype="bf16",
                      state_std=0.1, seed=1004)
 
 WORKLOADS = {w.name: w for w in (TINY_F32, PREFILL_8K, PREFILL_1M, DECODE_B256, VARLEN_64)}
