@@ -441,8 +441,13 @@ struct ChunkCfg {
     static_assert((TPT % 16 == 0) || (16 % TPT == 0), "sub-tile alignment");
 };
 
-// channel-vector slots (each DK fp32, permuted channel order)
-enum { V_ER = 0, V_FY = 4, V_FX = 8, V_EL = 11, V_GC = 15 };
+// channel-vector slots (each DK fp32, permuted channel order):
+//   V_ER + a : e^{R_a}                              (q, k decayed to the chunk start)
+//   V_YS + t : e^{R_a - R_b} for off-diagonal block t = (a, b), key side
+//   V_GC     : e^{G_last}
+enum { V_ER = 0, V_YS = 4, V_GC = 10 };
+// off-diagonal blocks in task order (1,0),(2,0),(2,1),(3,0),(3,1),(3,2) -> slot
+__host__ __device__ constexpr int ys_slot(int a, int b) { return (a * (a - 1)) / 2 + b; }
 
 // Raw tile prefetch into registers: per tensor a uniform base pointer for the
 // chunk and a fixed per-lane offset, so each 16-byte unit is one load.  Rows
@@ -514,6 +519,17 @@ __device__ __forceinline__ void raw_commit(const u32x4 (&pre)[C::UPT], unsigned 
                 *reinterpret_cast<u32x4*>(row_base + pcol(c0)) = w;
             }
         }
+    }
+}
+
+// four consecutive elements of a token tensor from fp32
+template <typename DT>
+__device__ __forceinline__ void store4(typename DT::storage* p, const f32x4& v)
+{
+    if constexpr (DT::is_bf16) {
+        *reinterpret_cast<u32x2*>(p) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    } else {
+        *reinterpret_cast<f32x4*>(p) = v;
     }
 }
 
@@ -629,7 +645,7 @@ prefill_chunk_kernel(PrefillDev p)
     const int l16 = lane & 15;
     const int q4 = lane >> 4;
 #ifdef KDA_PHASE_TIMING
-    long long phase_acc[10] = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+    long long phase_acc[12] = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
     long long phase_last = clock64();
 #endif
 
@@ -772,14 +788,17 @@ prefill_chunk_kernel(PrefillDev p)
             if (part == 0) {
                 f32x2* vv = reinterpret_cast<f32x2*>(sVec);
 #pragma unroll
-                for (int a = 0; a < 4; ++a) {
-                    vv[((V_ER + a) * DK + pc) / 2] = f32x2{fexp2(R0[a]), fexp2(R1[a])};
-                    vv[((V_FY + a) * DK + pc) / 2] = f32x2{fexp2(R0[a + 1] - R0[a]), fexp2(R1[a + 1] - R1[a])};
-                    vv[((V_EL + a) * DK + pc) / 2] = f32x2{fexp2(R0[4] - R0[a + 1]), fexp2(R1[4] - R1[a + 1])};
-                }
-                vv[((V_FX + 0) * DK + pc) / 2] = f32x2{fexp2(R0[2] - R0[1]), fexp2(R1[2] - R1[1])};  // (2,0)
-                vv[((V_FX + 1) * DK + pc) / 2] = f32x2{fexp2(R0[3] - R0[1]), fexp2(R1[3] - R1[1])};  // (3,0)
-                vv[((V_FX + 2) * DK + pc) / 2] = f32x2{fexp2(R0[3] - R0[2]), fexp2(R1[3] - R1[2])};  // (3,1)
+                for (int a = 0; a < 4; ++a) vv[((V_ER + a) * DK + pc) / 2] = f32x2{fexp2(R0[a]), fexp2(R1[a])};
+                // key side of block (a, b): e^{R_a - R_b} = e^{E_b - R_b} e^{R_a - E_b}; the
+                // first factor is >= e^-80 (one sub-tile), the second may underflow only
+                // when the true value is negligible; the multiply keeps denormals
+#pragma unroll
+                for (int a = 1; a < 4; ++a)
+#pragma unroll
+                    for (int b = 0; b < a; ++b)
+                        vv[((V_YS + ys_slot(a, b)) * DK + pc) / 2] =
+                            f32x2{fexp2(R0[b + 1] - R0[b]) * fexp2(R0[a] - R0[b + 1]),
+                                  fexp2(R1[b + 1] - R1[b]) * fexp2(R1[a] - R1[b + 1])};
                 vv[(V_GC * DK + pc) / 2] = f32x2{fexp2(R0[4]), fexp2(R1[4])};
             }
             // all loads of this thread's tokens first
@@ -801,25 +820,28 @@ prefill_chunk_kernel(PrefillDev p)
                 const float ra1 = a == 0 ? R1[0] : a == 1 ? R1[1] : a == 2 ? R1[2] : R1[3];
                 const float rb0 = a == 0 ? R0[1] : a == 1 ? R0[2] : a == 2 ? R0[3] : R0[4];  // E_a
                 const float rb1 = a == 0 ? R1[1] : a == 1 ? R1[2] : a == 2 ? R1[3] : R1[4];
-                const float er0 = fexp2(ra0), er1 = fexp2(ra1);                  // e^{R_a}
-                const float fy0 = fexp2(rb0 - ra0), fy1 = fexp2(rb1 - ra1);      // e^{E_a - R_a}
-                const float el0 = fexp2(R0[4] - rb0), el1 = fexp2(R1[4] - rb1);  // e^{G_last - E_a}
+                const float er0 = fexp2(ra0), er1 = fexp2(ra1);  // e^{R_a}
+                // e^{G_last - R_a} as e^{E_a - R_a} (>= e^-80) times e^{G_last - E_a}; the
+                // product may be denormal, which fp32 multiplies keep
+                const float fe0 = fexp2(rb0 - ra0) * fexp2(R0[4] - rb0);
+                const float fe1 = fexp2(rb1 - ra1) * fexp2(R1[4] - rb1);
 #pragma unroll
                 for (int i = i0; i < i0 + SPAN; ++i) {
                     const int r = tok0 + i;
                     G0 += O::p0(wg[i]) * LOG2E;
                     G1 += O::p1(wg[i]) * LOG2E;
-                    const float e1a = fexp2(G0 - ra0), e1b = fexp2(G1 - ra1);  // e^{G - R_a} in [e^-80, 1]
-                    const float e2a = fexp2(ra0 - G0), e2b = fexp2(ra1 - G1);  // e^{R_a - G} in [1, e^80]
+                    const float d0 = G0 - ra0, d1 = G1 - ra1;
+                    const float e1a = fexp2(d0), e1b = fexp2(d1);    // e^{G - R_a} in [e^-80, 1]
+                    const float e2a = fexp2(-d0), e2b = fexp2(-d1);  // e^{R_a - G} in [1, e^80]
                     const float ga = e1a * er0, gb2 = e1b * er1;                // e^{G}
                     const float k0 = O::p0(wk[i]), k1 = O::p1(wk[i]);
                     const float kf0 = k0 * e2a, kf1 = k1 * e2b;
                     O::stp(sK + r * C::SK + pc, k0 * e1a, k1 * e1b);
                     O::stp(sG + r * C::SK + pc, kf0, kf1);
                     O::stp(sKG + r * C::SK + pc, -k0 * ga, -k1 * gb2);
-                    // k e^{G_last - G} = (k e^{R_a - G} e^{E_a - R_a}) e^{G_last - E_a}, each factor <= 1
-                    kh0[i] = (kf0 * fy0) * el0;
-                    kh1[i] = (kf1 * fy1) * el1;
+                    // k e^{G_last - G} = (k e^{R_a - G}) e^{G_last - R_a}
+                    kh0[i] = kf0 * fe0;
+                    kh1[i] = kf1 * fe1;
                     if (!SUMMARY) {
                         const float q0 = O::p0(wq[i]), q1 = O::p1(wq[i]);
                         O::stp(sQ + r * C::SK + pc, q0 * e1a, q1 * e1b);
@@ -914,7 +936,6 @@ prefill_chunk_kernel(PrefillDev p)
                 }
                 b = bi;  // 0 <= b <= a
             }
-            const int fx = (a >= b + 2) ? (a == 2 ? 0 : (b == 0 ? 1 : 2)) : -1;
             Frag yf[DK / 32], kf[DK / 32], qf[DK / 32];
 #pragma unroll
             for (int kb = 0; kb < DK / 32; ++kb) {
@@ -925,12 +946,11 @@ prefill_chunk_kernel(PrefillDev p)
             f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < DK / 32; ++kb) {
-                Frag y = yf[kb], kx = kf[kb], qx;
-                if (!SUMMARY) qx = qf[kb];
-                if (b < a) {  // off-diagonal: key side referenced at the end of sub-tile b
+                Frag y = yf[kb];
+                if (b < a) {  // off-diagonal: key side moved from R_b to R_a
                     float t[8];
                     O::unpack(y, t);
-                    const f32x4* fv = reinterpret_cast<const f32x4*>(sVec + (V_FY + b) * DK + kb * 32 + 8 * q4);
+                    const f32x4* fv = reinterpret_cast<const f32x4*>(sVec + (V_YS + ys_slot(a, b)) * DK + kb * 32 + 8 * q4);
                     const f32x4 f0 = fv[0], f1 = fv[1];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
@@ -939,29 +959,8 @@ prefill_chunk_kernel(PrefillDev p)
                     }
                     y = O::make(t);
                 }
-                if (fx >= 0) {
-                    const f32x4* fv = reinterpret_cast<const f32x4*>(sVec + (V_FX + fx) * DK + kb * 32 + 8 * q4);
-                    const f32x4 f0 = fv[0], f1 = fv[1];
-                    float t[8];
-                    O::unpack(kx, t);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        t[e] *= f0[e];
-                        t[4 + e] *= f1[e];
-                    }
-                    kx = O::make(t);
-                    if (!SUMMARY) {
-                        O::unpack(qx, t);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            t[e] *= f0[e];
-                            t[4 + e] *= f1[e];
-                        }
-                        qx = O::make(t);
-                    }
-                }
-                O::mma(accA, y, kx);
-                if (!SUMMARY) O::mma(accP, y, qx);
+                O::mma(accA, y, kf[kb]);
+                if (!SUMMARY) O::mma(accP, y, qf[kb]);
             }
             // acc: lane (col r = 16a + l16, rows i = 16b + 4*q4 + j)
             const int r = a * 16 + l16;
@@ -1020,6 +1019,7 @@ prefill_chunk_kernel(PrefillDev p)
                     Uf[a][ct] = O::make4(Ut[a][ct]);
                 }
             }
+            KDA_PHASE(10);
             Frag Ub[2][NCT];
 #pragma unroll
             for (int kbt = 0; kbt < 2; ++kbt)
@@ -1027,7 +1027,9 @@ prefill_chunk_kernel(PrefillDev p)
                 for (int ct = 0; ct < NCT; ++ct) Ub[kbt][ct] = acc_frag<DT>(Ut[2 * kbt][ct], Ut[2 * kbt + 1][ct]);
 
             if (!SUMMARY) {
-                // ---- O = (Q . e^G) S + P U
+                // ---- O^T = S^T (Q . e^G)^T + U^T P^T: the register fragments of S and U
+                //      serve as the left operand, so each lane ends up holding four
+                //      consecutive value columns of one token (one 8-byte store)
 #pragma unroll
                 for (int rt = 0; rt < 4; ++rt) {
                     f32x4 Ot[NCT];
@@ -1035,31 +1037,27 @@ prefill_chunk_kernel(PrefillDev p)
                     for (int ct = 0; ct < NCT; ++ct) Ot[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int kb = 0; kb < DK / 32; ++kb) {
-                        const Frag af = O::load(sQG + (rt * 16 + l16) * C::SK + kb * 32 + 8 * q4);
+                        const Frag bf = O::load(sQG + (rt * 16 + l16) * C::SK + kb * 32 + 8 * q4);
 #pragma unroll
-                        for (int ct = 0; ct < NCT; ++ct) O::mma(Ot[ct], af, Sb[kb][ct]);
+                        for (int ct = 0; ct < NCT; ++ct) O::mma(Ot[ct], Sb[kb][ct], bf);
                     }
 #pragma unroll
                     for (int kbt = 0; kbt <= rt / 2; ++kbt) {
                         const Frag pf = O::load(sP + (rt * 16 + l16) * C::ST + kbt * 32 + 8 * q4);
 #pragma unroll
-                        for (int ct = 0; ct < NCT; ++ct) O::mma(Ot[ct], pf, Ub[kbt][ct]);
+                        for (int ct = 0; ct < NCT; ++ct) O::mma(Ot[ct], Ub[kbt][ct], pf);
                     }
+                    const int row = rt * 16 + l16;  // token
 #pragma unroll
-                    for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const int row = rt * 16 + 4 * q4 + j;
-                            const int col = colbase + ct * 16 + l16;
-                            if (C::STAGE_O) {
-                                store_elem<DT>(sO, row * C::SO + col, Ot[ct][j]);
-                            } else if (row < len) {
-                                store_elem<DT>(go, ((c0 + row) * H + h) * DV + col, Ot[ct][j]);
-                            }
-                        }
+                    for (int ct = 0; ct < NCT; ++ct) {
+                        const int col = colbase + ct * 16 + 4 * q4;
+                        if (C::STAGE_O) store4<DT>(sO + row * C::SO + col, Ot[ct]);
+                        else if (row < len) store4<DT>(go + ((c0 + row) * H + h) * DV + col, Ot[ct]);
+                    }
                 }
             }
 
+            KDA_PHASE(11);
             // ---- S <- Diag(e^{G_last}) S + (K . e^{G_last - G})^T U
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
@@ -1086,14 +1084,14 @@ prefill_chunk_kernel(PrefillDev p)
     KDA_PHASE(9);
 #ifdef KDA_PHASE_TIMING
     if (tid == KDA_PHASE_TID && blockIdx.x < 16384)
-        for (int i = 0; i < 10; ++i) kda_phase_cycles[blockIdx.x * 16 + i] = phase_acc[i];
+        for (int i = 0; i < 12; ++i) kda_phase_cycles[blockIdx.x * 16 + i] = phase_acc[i];
 #endif
     // ---- write the segment result
     if (chain) {
         float* dst = nullptr;
         int ld = DV;
         if (SUMMARY) {
-            dst = p.ms + (int64_t(item) * H + h) * DK * (DK + DV);
+            dst = p.ms + (int64_t(item) * H + h) * DK * (DK + DV);  // [S~ | M], rows of DK + DV
             ld = DK + DV;
         } else if (last_seg && p.fin) {
             dst = p.fin + (int64_t(n) * H + h) * DK * DV;
@@ -1111,17 +1109,42 @@ prefill_chunk_kernel(PrefillDev p)
 }
 
 // ------------------------------------------------------------- scan kernel
-// Per (sequence, head, 8-column slice of the state): S_in(s+1) = M_s S_in(s) + S~_s
-// over the sequence's segments, in fp32.  Columns are independent, so each
-// slice is its own workgroup (d_v / 8 of them per sequence and head).
-constexpr int SCAN_COLS = 8;
+// Per (sequence, head, 32-column slice of the state):
+//     S_in(s+1) = M_s S_in(s) + S~_s
+// over the sequence's segments, on the matrix cores with fp32-level accuracy:
+// each fp32 operand x is split as hi = bf16(x), lo = bf16(x - hi) and the
+// product accumulates hi*hi + hi*lo + lo*hi in fp32.  Per step the workgroup
+// stages M_s in LDS (next step's M prefetched into registers during this
+// step's products) and keeps its S_in slice in LDS, transposed, as the other
+// operand.  Wave w owns state row tiles w, w+4, ... and both column tiles.
+constexpr int SCAN_COLS = 32;
+template <int DK, int DV>
+struct ScanCfg {
+    static constexpr int SM = DK + 4;                 // fp32 row stride of M and S_in^T in LDS
+    static constexpr int UNITS = DK * (DK / 4);       // 16-byte units of M
+    static constexpr int UPT = (UNITS + 255) / 256;
+    static constexpr int RTW = (DK / 16 + 3) / 4;     // row tiles per wave
+    static constexpr int LDS = (DK + SCAN_COLS) * SM * 4;
+};
+
+__device__ __forceinline__ void split_bf16(const float (&x)[8], bf16x8& hi, bf16x8& lo)
+{
+    float h[8], l[8];
+    hi = Op<BF16>::make(x);
+    Op<BF16>::unpack(hi, h);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) l[e] = x[e] - h[e];
+    lo = Op<BF16>::make(l);
+}
+
 template <int DK, int DV>
 __global__ void __launch_bounds__(256) scan_kernel(PrefillDev p)
 {
+    using SC = ScanCfg<DK, DV>;
     constexpr int NB = DV / SCAN_COLS;
-    constexpr int TPR = 256 / DK;        // threads per state row
-    constexpr int CPT = SCAN_COLS / TPR; // columns per thread
-    __shared__ float sS[DK][SCAN_COLS];
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    float* sM = reinterpret_cast<float*>(smem);  // [DK][SM]: M_s rows
+    float* sT = sM + DK * SC::SM;                // [32][SM]: S_in slice, transposed (column j, row k)
     const int H = p.H;
     const int jb = blockIdx.x % NB;
     const int h = (blockIdx.x / NB) % H;
@@ -1130,37 +1153,96 @@ __global__ void __launch_bounds__(256) scan_kernel(PrefillDev p)
     const int32_t* p1_off = p.tab + 2 * (p.N + 1);
     const int nseg = seg_off[n + 1] - seg_off[n];
     if (nseg <= 1) return;
-    const int tid = threadIdx.x;
-    const int c = tid / TPR;
-    const int j0 = (tid % TPR) * CPT;
-    const int col0 = jb * SCAN_COLS + j0;
-    for (int e = tid; e < DK * SCAN_COLS; e += 256) {
-        const int r = e / SCAN_COLS, cc = e % SCAN_COLS;
-        sS[r][cc] = p.init ? p.init[(int64_t(n) * H + h) * DK * DV + r * DV + jb * SCAN_COLS + cc] : 0.f;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, q4 = lane >> 4;
+    const int col0 = jb * SCAN_COLS;
+    auto ms_of = [&](int st) { return p.ms + (int64_t(p1_off[n] + st) * H + h) * DK * (DK + DV); };
+
+    for (int e = tid; e < SCAN_COLS * DK; e += 256) {
+        const int j = e / DK, k = e % DK;
+        sT[j * SC::SM + k] = p.init ? p.init[(int64_t(n) * H + h) * DK * DV + k * DV + col0 + j] : 0.f;
     }
-    __syncthreads();
-    for (int s = 0; s + 1 < nseg; ++s) {
-        const float* ms = p.ms + (int64_t(p1_off[n] + s) * H + h) * DK * (DK + DV);
-        const float* mrow = ms + c * (DK + DV) + DV;
-        float acc[CPT];
+    f32x4 pre[SC::UPT];
+    f32x4 nxt[SC::RTW][2];
+    // M_st (columns DV .. DV+DK-1 of each row) and this wave's S~_st tiles
+    // (columns 0 .. DV-1) into registers; consumed one step later.
+    auto load_step = [&](int st) {
+        const float* base = ms_of(st);
 #pragma unroll
-        for (int j = 0; j < CPT; ++j) acc[j] = ms[c * (DK + DV) + col0 + j];
-#pragma unroll 4
-        for (int cc = 0; cc < DK; cc += 4) {
-            const f32x4 m = *reinterpret_cast<const f32x4*>(mrow + cc);
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-#pragma unroll
-                for (int j = 0; j < CPT; ++j) acc[j] += m[u] * sS[cc + u][j0 + j];
+        for (int i = 0; i < SC::UPT; ++i) {
+            const int u = tid + i * 256;
+            if (SC::UNITS % 256 == 0 || u < SC::UNITS)
+                pre[i] = *reinterpret_cast<const f32x4*>(base + DV + (u / (DK / 4)) * (DK + DV) + (u % (DK / 4)) * 4);
         }
+#pragma unroll
+        for (int i = 0; i < SC::RTW; ++i) {
+            const int rt = wave + 4 * i;
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    nxt[i][ct][j] = rt < DK / 16 ? base[(rt * 16 + 4 * q4 + j) * (DK + DV) + col0 + ct * 16 + l16] : 0.f;
+        }
+    };
+    load_step(0);
+    for (int s = 0; s + 1 < nseg; ++s) {
+        __syncthreads();  // sM free
+#pragma unroll
+        for (int i = 0; i < SC::UPT; ++i) {
+            const int u = tid + i * 256;
+            if (SC::UNITS % 256 == 0 || u < SC::UNITS)
+                *reinterpret_cast<f32x4*>(sM + (u / (DK / 4)) * SC::SM + (u % (DK / 4)) * 4) = pre[i];
+        }
+        f32x4 acc[SC::RTW][2];
+#pragma unroll
+        for (int i = 0; i < SC::RTW; ++i)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) acc[i][ct] = nxt[i][ct];
         __syncthreads();
+        if (s + 2 < nseg) load_step(s + 1);  // in flight during the products
+#pragma unroll
+        for (int kb = 0; kb < DK / 32; ++kb) {
+            bf16x8 bh[2], bl[2];
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                const float* b = sT + (ct * 16 + l16) * SC::SM + kb * 32 + 4 * q4;
+                const f32x4 b0 = *reinterpret_cast<const f32x4*>(b), b1 = *reinterpret_cast<const f32x4*>(b + 16);
+                const float x[8] = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+                split_bf16(x, bh[ct], bl[ct]);
+            }
+#pragma unroll
+            for (int i = 0; i < SC::RTW; ++i) {
+                const int rt = wave + 4 * i;
+                if (rt < DK / 16) {
+                    const float* a = sM + (rt * 16 + l16) * SC::SM + kb * 32 + 4 * q4;
+                    const f32x4 a0 = *reinterpret_cast<const f32x4*>(a), a1 = *reinterpret_cast<const f32x4*>(a + 16);
+                    const float x[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+                    bf16x8 ah, al;
+                    split_bf16(x, ah, al);
+#pragma unroll
+                    for (int ct = 0; ct < 2; ++ct) {
+                        Op<BF16>::mma(acc[i][ct], ah, bh[ct]);
+                        Op<BF16>::mma(acc[i][ct], ah, bl[ct]);
+                        Op<BF16>::mma(acc[i][ct], al, bh[ct]);
+                    }
+                }
+            }
+        }
+        __syncthreads();  // every wave is done reading sT
         float* out = p.sin + (int64_t(seg_off[n] + s + 1) * H + h) * DK * DV;
 #pragma unroll
-        for (int j = 0; j < CPT; ++j) {
-            sS[c][j0 + j] = acc[j];
-            out[c * DV + col0 + j] = acc[j];
+        for (int i = 0; i < SC::RTW; ++i) {
+            const int rt = wave + 4 * i;
+            if (rt < DK / 16) {
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct) {
+                    const int j = ct * 16 + l16;
+                    *reinterpret_cast<f32x4*>(sT + j * SC::SM + rt * 16 + 4 * q4) = acc[i][ct];
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) out[(rt * 16 + 4 * q4 + jj) * DV + col0 + j] = acc[i][ct][jj];
+                }
+            }
         }
-        __syncthreads();
     }
 }
 
@@ -1186,8 +1268,12 @@ hipError_t launch_prefill_t(const PrefillArgs& a, const PrefillPlan& plan, hipSt
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(k1, dim3(unsigned(plan.np1_max * a.H)), dim3(C1::NT), C1::LDS, stream, d);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        hipLaunchKernelGGL((scan_kernel<DK, DV>), dim3(unsigned(a.N * a.H * (DV / SCAN_COLS))), dim3(256), 0,
-                           stream, d);
+        auto ks = scan_kernel<DK, DV>;
+        constexpr int scan_lds = ScanCfg<DK, DV>::LDS;
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(ks), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                scan_lds);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(ks, dim3(unsigned(a.N * a.H * (DV / SCAN_COLS))), dim3(256), scan_lds, stream, d);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     using C3 = ChunkCfg<DT, DK, DV, false>;

@@ -101,6 +101,13 @@ def test_prefill_segmented(kda, seg, zshift):
     check(kda, wl, seg=seg, tag=f"zshift={zshift}")
 
 
+@pytest.mark.parametrize("dv", [32, 64])
+def test_prefill_segmented_f32(kda, dv):
+    """fp32 storage through the segment summary and scan (fp32 tolerance)."""
+    wl = synth.TINY_F32.with_(H=3, dv=dv, seqlens=(700, 3, 450), state_std=0.1, z_shift=-2.0)
+    check(kda, wl, seg=2)
+
+
 def test_prefill_weak_decay_long(kda):
     """z shifted by -3 (alpha ~ 0.7): the incoming state and early tokens still
     matter thousands of tokens later."""
