@@ -56,6 +56,9 @@ typedef enum {
 
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype_t;
 
+/* Largest head count kda_prefill accepts (token rows stay below 2^24 bytes). */
+#define KDA_MAX_HEADS 16384
+
 /* Human-readable name of a status code (static string). */
 const char* kda_status_string(kda_status_t s);
 
@@ -104,7 +107,13 @@ size_t kda_prefill_workspace_size(int64_t T_total, int N, int H, int d_k, int d_
  *   final_state   : fp32 [N, H, d_k, d_v] or NULL (not written).  May alias
  *                   initial_state exactly (in-place hand-off); no other
  *                   aliasing is allowed between any two buffers.
- *   chunk   : tokens per chunk; 64 is the supported value.
+ *   chunk   : 64, the granularity (in tokens) at which long sequences are
+ *             cut into segments; inside a segment the recurrence advances
+ *             in blocks of 32 tokens.
+ *   H       : 1 .. KDA_MAX_HEADS.
+ *   g       : every value in [-5, 0] (the range kda_gate produces); the
+ *             kernels factor decay ratios per 16-token sub-tile and rely on
+ *             this bound to keep every factor inside the fp32 range.
  *   d_k, d_v: each one of 32, 64, 128 for bf16; for fp32 d_k = 32 and d_v is
  *             32 or 64 (the fp32 operand tiles of wider heads do not fit one
  *             CU's LDS).
@@ -116,7 +125,7 @@ size_t kda_prefill_workspace_size(int64_t T_total, int N, int H, int d_k, int d_
  * composed exactly through S_end = S~ + M S_in.
  * Errors: KDA_ERR_INVALID_ARGUMENT (null required pointer, N < 1, T_total < 0,
  * N != 1 without cu_seqlens, forbidden aliasing), KDA_ERR_UNSUPPORTED (d_k,
- * d_v, chunk or dtype outside the supported set),
+ * d_v, chunk, H or dtype outside the supported set),
  * KDA_ERR_WORKSPACE_TOO_SMALL, KDA_ERR_HIP.
  */
 kda_status_t kda_prefill(const void* q, const void* k, const void* v, const void* g,

@@ -132,7 +132,7 @@ kda_status_t kda_decode_step(const void* q, const void* k, const void* v, const 
 size_t kda_prefill_workspace_size(int64_t T_total, int N, int H, int d_k, int d_v, int chunk,
                                   kda_dtype_t dtype)
 {
-    if (T_total < 0 || N < 1 || H < 1 || !dim_ok(d_k) || !dim_ok(d_v) || chunk != 64 ||
+    if (T_total < 0 || N < 1 || H < 1 || H > KDA_MAX_HEADS || !dim_ok(d_k) || !dim_ok(d_v) || chunk != 64 ||
         !dtype_ok(dtype) || (dtype == KDA_F32 && (d_k != 32 || d_v > 64)))
         return 0;
     return kda::prefill_plan(T_total, N, H, d_k, d_v).workspace_bytes;
@@ -147,6 +147,7 @@ kda_status_t kda_prefill(const void* q, const void* k, const void* v, const void
     if (N < 1 || T_total < 0 || H < 1)
         return fail(KDA_ERR_INVALID_ARGUMENT, "kda_prefill: bad sizes N=%d T_total=%lld H=%d", N,
                     (long long)T_total, H);
+    if (H > KDA_MAX_HEADS) return fail(KDA_ERR_UNSUPPORTED, "kda_prefill: H=%d > %d", H, KDA_MAX_HEADS);
     if (!cu_seqlens && N != 1)
         return fail(KDA_ERR_INVALID_ARGUMENT, "kda_prefill: cu_seqlens is NULL but N=%d", N);
     if (!dtype_ok(dtype))

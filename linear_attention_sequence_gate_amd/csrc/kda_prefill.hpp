@@ -55,19 +55,31 @@ namespace kda {
 #define KDA_PHASE_TID 0
 #endif
 __device__ unsigned long long kda_phase_cycles[16384 * 16];
-#define KDA_PHASE(i)                                    \
-    do {                                                \
-        if (tid == KDA_PHASE_TID) {                     \
-            const long long t_ = clock64();             \
-            phase_acc[i] += t_ - phase_last;            \
-            phase_last = t_;                            \
-        }                                               \
-    } while (0)
+struct PhaseClock {
+    long long acc[12] = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+    long long last = 0;
+    bool on = false;
+    __device__ void mark(int i)
+    {
+        if (on) {
+            const long long t = clock64();
+            acc[i] += t - last;
+            last = t;
+        }
+    }
+    __device__ void save()
+    {
+        if (on && blockIdx.x < 16384)
+            for (int i = 0; i < 12; ++i) kda_phase_cycles[blockIdx.x * 16 + i] = acc[i];
+    }
+};
 #else
-#define KDA_PHASE(i) \
-    do {             \
-    } while (0)
+struct PhaseClock {
+    __device__ void mark(int) {}
+    __device__ void save() {}
+};
 #endif
+#define KDA_PHASE(i) pclk.mark(i)
 
 constexpr int CH = 64;  // tokens per chunk
 constexpr int NCU_TARGET = 256;
@@ -383,144 +395,80 @@ __device__ __forceinline__ typename Op<DT>::Frag acc_frag(const f32x4& lo, const
     return Op<DT>::make(x);
 }
 
-// ------------------------------------------------------------ chunk kernel
-template <typename DT, int DK, int DV, bool SUMMARY>
-struct ChunkCfg {
+// ------------------------------------------------------------ block kernel
+// The recurrence advances in blocks of BC = 32 tokens (two 16-token sub-tiles).
+// Waves have two roles inside a workgroup:
+//   chain waves (NCW, 32 state columns each) hold their columns of the state
+//   in registers for the whole segment and run X, U, O and the state update;
+//   prep waves (4) build every state-independent operand of the NEXT block:
+//   the decayed q/k tiles, the channel vectors, the products A and P and the
+//   inverses of the diagonal blocks of (I + A).
+// Two stages per block, one barrier each:
+//   alpha:  chain X_b = V_b - (K.e^G)_b S        | prep: A_b, P_b, (I + A_aa)^{-1}
+//   beta:   chain U_b, O_b, S <- ...             | prep: tiles of block b+1 from
+//                                                   registers; loads of block b+2
+// so the vector work of one block runs beside the matrix work of the other.
+// Only the tiles that the two roles touch in the same stage are double
+// buffered (q.e^G, K-hat^T, e^{G_last}, beta).
+constexpr int BC = 32;
+
+template <typename DT, int DKV, int DVV, bool SUMMARY>
+struct BlockCfg {
+    static constexpr int DK = DKV, DV = DVV;
     static constexpr int NCOL = SUMMARY ? DV + DK : DV;  // extended state columns
-    // state columns per chain wave: 16 for the output pass (two waves per SIMD
-    // hide LDS latency), 32 for the summary pass (twice the columns, no outputs)
-    static constexpr int CW = (SUMMARY || NCOL <= 32) ? 32 : 16;
-    static constexpr int NCT = CW / 16;                   // 16-wide column tiles per wave
-    static constexpr int NCW = NCOL / CW;                 // chain waves
-    static constexpr int NW0 = NCW > DK / 64 ? NCW : DK / 64;
-    static constexpr int NW = NW0 <= 1 ? 1 : NW0 <= 2 ? 2 : NW0 <= 4 ? 4 : 8;
-    static constexpr int NT = NW * 64;
+    static constexpr int NCW = NCOL / 32;                 // chain waves
+    // prep waves: two per SIMD for the output pass of wide heads (their
+    // vector work is the longer side of the pipeline), one otherwise
+    static constexpr int NPW = (!SUMMARY && DKV >= 64) ? 8 : 4;
+    static constexpr int NW = NCW + NPW;
+    static constexpr int NT = 64 * NW;
+    static constexpr int NPT = 64 * NPW;       // prep threads
     static constexpr int CP = DK / 2;          // channel pairs
-    static constexpr int PARTS = NT / CP;      // threads per channel pair (elementwise phases)
-    static constexpr int TPT = CH / PARTS;     // tokens per thread
-    static constexpr int SL = TPT < 16 ? TPT : 16;
-    static constexpr int NSLOT = CH / SL;
+    static constexpr int PARTS = NPT / CP;     // token runs per channel pair
+    static constexpr int TPT = BC / PARTS;     // tokens per prep thread (one run)
+    static constexpr int CPW = 64 / PARTS;     // channel pairs per prep wave
     using OT = typename Op<DT>::T;
     static constexpr int ES = sizeof(OT);
     static constexpr int SK = DK + 16 / ES;  // padded row strides (elements)
     static constexpr int SV = DV + 16 / ES;
-    static constexpr int ST = CH + 16 / ES;
+    static constexpr int ST = BC + 16 / ES;
     static constexpr int SD = 16 + 16 / ES;
-    static constexpr int TILE_K = CH * SK * ES;
+    static constexpr int TILE_K = BC * SK * ES;
+    static constexpr int TILE_H = DK * ST * ES;
+    static constexpr int TILE_S = BC * ST * ES;
+    static constexpr int TILE_D = 16 * SD * ES;
     // LDS layout (bytes)
-    static constexpr int O_Q = 0;                       // raw q -> q.e^{G-R_a}
-    static constexpr int O_K = O_Q + TILE_K;            // raw k -> k.e^{G-R_a}
-    static constexpr int O_G = O_K + TILE_K;            // raw g -> k.e^{R_a-G}
-    static constexpr int O_V = O_G + TILE_K;            // raw v
-    static constexpr int O_QG = O_V + CH * SV * ES;     // q.e^{G}
-    static constexpr int O_KG = O_QG + TILE_K;          // -k.e^{G}
-    static constexpr int O_KH = O_KG + TILE_K;          // (k.e^{G_last-G})^T  [DK][ST]
-    static constexpr int O_A = O_KH + DK * ST * ES;     // -A (x beta_r), natural columns
-    static constexpr int O_P = O_A + CH * ST * ES;      // P, permuted columns
-    static constexpr int O_D = O_P + CH * ST * ES;      // (I + A_aa)^{-1}, 4 blocks
-    static constexpr int O_DS = O_D + 4 * 16 * SD * ES;  // N^2, N^4 per diagonal block (inverse scratch)
-    static constexpr int O_VEC = O_DS + 8 * 16 * SD * ES;  // 16 x DK fp32 channel vectors
-    static constexpr int O_SIG = O_VEC + 16 * DK * 4;   // NSLOT x DK fp32
-    static constexpr int O_B = O_SIG + NSLOT * DK * 4;  // beta[64]
-    static constexpr int LDS = O_B + CH * 4;
-    // output staging in the -k.e^G tile: rows of DV storage elements (stride SO)
-    static constexpr int SO = DV + 8;
-    static constexpr bool STAGE_O = !SUMMARY && CH * SO * int(sizeof(typename DT::storage)) <= TILE_K;
-    // raw tile loading: 16-byte units
-    static constexpr int EPU = 16 / ES;           // elements per unit
-    static constexpr int UPR_K = DK / EPU;        // units per row
+    static constexpr int O_KE = 0;                                  // k.e^{G-R_a}
+    static constexpr int O_KF = O_KE + TILE_K;                      // k.e^{R_a-G}
+    static constexpr int O_QE = O_KF + TILE_K;                      // q.e^{G-R_a}
+    static constexpr int O_KG = O_QE + (SUMMARY ? 0 : TILE_K);      // -k.e^{G}
+    static constexpr int O_V = O_KG + TILE_K;                       // v
+    static constexpr int O_QG = O_V + BC * SV * ES;                 // q.e^{G}, 2 buffers
+    static constexpr int O_KH = O_QG + (SUMMARY ? 0 : 2 * TILE_K);  // (k.e^{G_last-G})^T [DK][ST], 2 buffers
+    static constexpr int O_A = O_KH + 2 * TILE_H;                   // -beta_r A, natural columns
+    static constexpr int O_P = O_A + TILE_S;                        // P, permuted columns
+    static constexpr int O_D = O_P + (SUMMARY ? 0 : TILE_S);        // (I + A_aa)^{-1}, 2 blocks
+    static constexpr int O_DS = O_D + 2 * TILE_D;                   // inverse scratch, 4 blocks
+    static constexpr int O_VEC = O_DS + 4 * TILE_D;                 // fp32 channel vectors
+    static constexpr int O_B = O_VEC + 3 * DK * 4;                  // beta, 2 buffers
+    static constexpr int O_RUN = O_B + 2 * BC * 4;                  // run sums of g, wave-private
+    static constexpr int LDS = O_RUN + NPT * 8;
+    // v tile: 16-byte units
+    static constexpr int EPU = 16 / ES;
     static constexpr int UPR_V = DV / EPU;
-    static constexpr int U_K = CH * UPR_K;        // units per q/k/g tile
-    static constexpr int U_V = CH * UPR_V;
-    static constexpr int NTILE_K = SUMMARY ? 2 : 3;  // pass 1 needs no q
-    static constexpr int UPT_K = (U_K + NT - 1) / NT;  // units per thread, per q/k/g tile
-    static constexpr int UPT_V = (U_V + NT - 1) / NT;
-    static constexpr int UPT = NTILE_K * UPT_K + UPT_V;
+    static constexpr int U_V = BC * UPR_V;
+    static constexpr int UPT_V = (U_V + NPT - 1) / NPT;
+    static_assert(NCOL % 32 == 0 && NCW >= 1, "state columns come in blocks of 32");
     static_assert(LDS <= 160 * 1024, "LDS budget exceeded");
-    static_assert(PARTS >= 1 && CH % PARTS == 0, "bad elementwise split");
-    static_assert((TPT % 16 == 0) || (16 % TPT == 0), "sub-tile alignment");
+    static_assert(PARTS >= 2 && BC % PARTS == 0 && CP * PARTS == NPT, "bad elementwise split");
+    static_assert(16 % TPT == 0, "a token run stays inside one sub-tile");
+    static_assert(NT <= 1024, "workgroup too large");
 };
 
-// channel-vector slots (each DK fp32, permuted channel order):
-//   V_ER + a : e^{R_a}                              (q, k decayed to the chunk start)
-//   V_YS + t : e^{R_a - R_b} for off-diagonal block t = (a, b), key side
-//   V_GC     : e^{G_last}
-enum { V_ER = 0, V_YS = 4, V_GC = 10 };
-// off-diagonal blocks in task order (1,0),(2,0),(2,1),(3,0),(3,1),(3,2) -> slot
-__host__ __device__ constexpr int ys_slot(int a, int b) { return (a * (a - 1)) / 2 + b; }
-
-// Raw tile prefetch into registers: per tensor a uniform base pointer for the
-// chunk and a fixed per-lane offset, so each 16-byte unit is one load.  Rows
-// past the sequence end are re-read from its last row (only needed when the
-// chunk ends past the tensor) and zeroed at commit.
-template <typename C, typename DT>
-__device__ __forceinline__ void raw_prefetch(u32x4 (&pre)[C::UPT], const typename DT::storage* gq,
-                                             const typename DT::storage* gk,
-                                             const typename DT::storage* gv,
-                                             const typename DT::storage* gg, int64_t c0, int len,
-                                             int64_t T_total, int H, int h, int tid, int dk, int dv)
-{
-    using ST = typename DT::storage;
-    const bool clamp = c0 + CH > T_total;
-    const int hdk = H * dk, hdv = H * dv;
-    const ST* bases[3] = {gq, gk, gg};
-#pragma unroll
-    for (int t = 0; t < C::NTILE_K; ++t) {
-        const ST* base = bases[C::NTILE_K == 3 ? t : t + 1] + (c0 * H + h) * int64_t(dk);
-#pragma unroll
-        for (int j = 0; j < C::UPT_K; ++j) {
-            const int uu = tid + j * C::NT;
-            if (C::U_K % C::NT == 0 || uu < C::U_K) {
-                int row = uu / C::UPR_K;
-                if (clamp) row = row < len ? row : len - 1;
-                pre[t * C::UPT_K + j] =
-                    *reinterpret_cast<const u32x4*>(base + (row * hdk + (uu % C::UPR_K) * C::EPU));
-            }
-        }
-    }
-    const ST* vbase = gv + (c0 * H + h) * int64_t(dv);
-#pragma unroll
-    for (int j = 0; j < C::UPT_V; ++j) {
-        const int uu = tid + j * C::NT;
-        if (C::U_V % C::NT == 0 || uu < C::U_V) {
-            int row = uu / C::UPR_V;
-            if (clamp) row = row < len ? row : len - 1;
-            pre[C::NTILE_K * C::UPT_K + j] =
-                *reinterpret_cast<const u32x4*>(vbase + (row * hdv + (uu % C::UPR_V) * C::EPU));
-        }
-    }
-}
-
-// raw tiles into LDS, each 16-byte unit placed at its permuted column position
-// (rows at or past `len` are written as zeros)
-template <typename C>
-__device__ __forceinline__ void raw_commit(const u32x4 (&pre)[C::UPT], unsigned char* smem, int tid, int len)
-{
-    using OT = typename C::OT;
-    constexpr int offs[3] = {C::NTILE_K == 3 ? C::O_Q : C::O_K, C::NTILE_K == 3 ? C::O_K : C::O_G, C::O_G};
-#pragma unroll
-    for (int i = 0; i < C::UPT; ++i) {
-        const bool isv = i >= C::NTILE_K * C::UPT_K;
-        const int t = isv ? 0 : i / C::UPT_K;
-        const int j = isv ? i - C::NTILE_K * C::UPT_K : i % C::UPT_K;
-        const int uu = tid + j * C::NT;
-        const int UPR = isv ? C::UPR_V : C::UPR_K;
-        if ((isv ? C::U_V : C::U_K) % C::NT == 0 || uu < (isv ? C::U_V : C::U_K)) {
-            const int row = uu / UPR, c0 = (uu % UPR) * C::EPU;
-            OT* row_base = isv ? reinterpret_cast<OT*>(smem + C::O_V) + row * C::SV
-                               : reinterpret_cast<OT*>(smem + offs[t]) + row * C::SK;
-            const bool keep = row < len;
-            const u32x4 w = {keep ? pre[i][0] : 0u, keep ? pre[i][1] : 0u, keep ? pre[i][2] : 0u,
-                             keep ? pre[i][3] : 0u};
-            if constexpr (C::ES == 2) {  // 8 columns -> two runs of 4 (8 bytes each)
-                *reinterpret_cast<u32x2*>(row_base + pcol(c0)) = u32x2{w[0], w[1]};
-                *reinterpret_cast<u32x2*>(row_base + pcol(c0 + 4)) = u32x2{w[2], w[3]};
-            } else {  // 4 fp32 columns stay contiguous
-                *reinterpret_cast<u32x4*>(row_base + pcol(c0)) = w;
-            }
-        }
-    }
-}
+// channel vectors (DK fp32 each, permuted channel order):
+//   V_YS       : e^{R_1 - R_0}, key side of the off-diagonal block (1, 0)
+//   V_GC + buf : e^{G_last}
+enum { V_YS = 0, V_GC = 1 };
 
 // four consecutive elements of a token tensor from fp32
 template <typename DT>
@@ -530,23 +478,6 @@ __device__ __forceinline__ void store4(typename DT::storage* p, const f32x4& v)
         *reinterpret_cast<u32x2*>(p) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
     } else {
         *reinterpret_cast<f32x4*>(p) = v;
-    }
-}
-
-// copy a staged output tile (LDS rows of DV elements, row stride SO) to o, 16 bytes per unit
-template <typename C, typename DT, int DV>
-__device__ __forceinline__ void store_out_tile(const unsigned char* smem, typename DT::storage* go, int64_t c0,
-                                               int len, int H, int h, int tid)
-{
-    using ST = typename DT::storage;
-    constexpr int EPU = 16 / int(sizeof(ST));
-    constexpr int UPR = DV / EPU;
-    const ST* stage = reinterpret_cast<const ST*>(smem + C::O_KG);
-    for (int u = tid; u < CH * UPR; u += C::NT) {
-        const int row = u / UPR, cu = u % UPR;
-        if (row < len)
-            *reinterpret_cast<u32x4*>(go + ((c0 + row) * H + h) * DV + cu * EPU) =
-                *reinterpret_cast<const u32x4*>(stage + row * C::SO + cu * EPU);
     }
 }
 
@@ -610,43 +541,310 @@ __device__ __forceinline__ void diag_inverse(const typename O::T* sA, typename O
     for (int j = 0; j < 4; ++j) sD[(a * 16 + 4 * q4 + j) * C::SD + l16] = O::to_op(d[j]);
 }
 
-template <typename DT, int DK, int DV, bool SUMMARY>
-__global__ void __launch_bounds__((ChunkCfg<DT, DK, DV, SUMMARY>::NT))
-prefill_chunk_kernel(PrefillDev p)
+
+// One block's raw inputs in a prep thread's registers: q, k, g of its token
+// run (two adjacent channels per token), its 16-byte units of v and, for the
+// first BC threads, one beta.  Rows at or past the block's valid length
+// re-read the last valid row, so no load leaves the sequence.  Only their g
+// (no decay past the end) and beta are zeroed: with beta = 0 a padded row's U
+// row is 0, so its q, k and v reach no valid output or state.
+template <typename C, typename DT>
+struct PrepRegs {
+    typename Op<DT>::Pair q[C::TPT], k[C::TPT], g[C::TPT];
+    u32x4 v[C::UPT_V];
+    typename DT::storage b;  // raw bits: converted where used, so the load is not waited on here
+};
+
+template <typename C, typename DT, bool SUMMARY>
+__device__ __forceinline__ void prep_load(PrepRegs<C, DT>& r, const PrefillDev& p, int64_t b0, int len, int h,
+                                          int ptid, int cpair, int tok0)
 {
-    using C = ChunkCfg<DT, DK, DV, SUMMARY>;
+    using ST = typename DT::storage;
+    using Pair = typename Op<DT>::Pair;
+    const int64_t H = p.H;
+    // uniform per-block byte bases + 32-bit lane byte offsets (a block spans 32
+    // token rows, and the host caps H so that a row is below 2^24 bytes)
+    const int64_t rk0 = (b0 * H + h) * C::DK * int64_t(sizeof(ST)), rv0 = (b0 * H + h) * C::DV * int64_t(sizeof(ST));
+    const char* gq = static_cast<const char*>(p.q) + rk0;
+    const char* gk = static_cast<const char*>(p.k) + rk0;
+    const char* gg = static_cast<const char*>(p.g) + rk0;
+    const char* gv = static_cast<const char*>(p.v) + rv0;
+    const uint32_t rsk = uint32_t(H) * uint32_t(C::DK * sizeof(ST)), rsv = uint32_t(H) * uint32_t(C::DV * sizeof(ST));
+    const uint32_t cb = uint32_t(2 * cpair * sizeof(ST));
+#pragma unroll
+    for (int i = 0; i < C::TPT; ++i) {
+        const int row = tok0 + i < len ? tok0 + i : len - 1;
+        const uint32_t off = __umul24(uint32_t(row), rsk) + cb;
+        if (!SUMMARY) r.q[i] = *reinterpret_cast<const Pair*>(gq + off);
+        r.k[i] = *reinterpret_cast<const Pair*>(gk + off);
+        r.g[i] = *reinterpret_cast<const Pair*>(gg + off);
+    }
+#pragma unroll
+    for (int j = 0; j < C::UPT_V; ++j) {
+        const int u = ptid + j * C::NPT;
+        if (C::U_V % C::NPT == 0 || u < C::U_V) {
+            int row = u / C::UPR_V;
+            row = row < len ? row : len - 1;
+            const uint32_t off = __umul24(uint32_t(row), rsv) + uint32_t((u % C::UPR_V) * 16);
+            r.v[j] = *reinterpret_cast<const u32x4*>(gv + off);
+        }
+    }
+    const char* gb = static_cast<const char*>(p.beta) + (b0 * H + h) * int64_t(sizeof(ST));
+    r.b = *reinterpret_cast<const ST*>(gb + __umul24(uint32_t(ptid < len ? ptid : len - 1), uint32_t(H * sizeof(ST))));
+}
+
+// Prep stage of the beta step: every state-independent tile of one block from
+// the registers.  A thread owns channels 2c, 2c+1 over a run of TPT tokens;
+// the runs of one channel pair sit in one wave (lanes cpl + CPW * part), so the
+// running sum of g across runs is a lane scan.  Log-decays are kept in the
+// log2 domain; R_a is G before sub-tile a (R_0 = 0) and E_a = G at its end.
+template <typename C, typename DT, bool SUMMARY>
+__device__ __forceinline__ void prep_tiles(const PrepRegs<C, DT>& r, unsigned char* smem, int buf, int len,
+                                           int lane, int ptid, int cpair, int part, int tok0, PhaseClock& pclk)
+{
+    using O = Op<DT>;
+    using OT = typename O::T;
+    constexpr int DK = C::DK;
+    constexpr float LOG2E = 1.4426950408889634f;
+    OT* sKE = reinterpret_cast<OT*>(smem + C::O_KE);
+    OT* sKF = reinterpret_cast<OT*>(smem + C::O_KF);
+    OT* sQE = reinterpret_cast<OT*>(smem + C::O_QE);
+    OT* sKG = reinterpret_cast<OT*>(smem + C::O_KG);
+    OT* sV = reinterpret_cast<OT*>(smem + C::O_V);
+    OT* sQG = reinterpret_cast<OT*>(smem + C::O_QG + buf * C::TILE_K);
+    OT* sKH = reinterpret_cast<OT*>(smem + C::O_KH + buf * C::TILE_H);
+    float* sVec = reinterpret_cast<float*>(smem + C::O_VEC);
+    float* sB = reinterpret_cast<float*>(smem + C::O_B) + buf * BC;
+    const int pc = pcol(2 * cpair);
+
+    float g0[C::TPT], g1[C::TPT];
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < C::TPT; ++i) {
+        const bool ok = tok0 + i < len;
+        g0[i] = ok ? O::p0(r.g[i]) * LOG2E : 0.f;
+        g1[i] = ok ? O::p1(r.g[i]) * LOG2E : 0.f;
+        s0 += g0[i];
+        s1 += g1[i];
+    }
+    pclk.mark(7);
+    // running sum across the runs of this channel pair: each lane publishes its
+    // run sums, then reads all runs of its pair (wave-private LDS, in order)
+    {
+        f32x2* run = reinterpret_cast<f32x2*>(smem + C::O_RUN);
+        run[cpair * C::PARTS + part] = f32x2{s0, s1};
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    float G0 = 0.f, G1 = 0.f, R10 = 0.f, R11 = 0.f, GL0 = 0.f, GL1 = 0.f;  // G before the run, at token 15, at the end
+    {
+        constexpr int P15 = 16 / C::TPT - 1;  // run holding token 15
+        const f32x4* run4 = reinterpret_cast<const f32x4*>(smem + C::O_RUN) + cpair * (C::PARTS / 2);
+#pragma unroll
+        for (int m = 0; m < C::PARTS / 2; ++m) {
+            const f32x4 w = run4[m];
+#pragma unroll
+            for (int hlf = 0; hlf < 2; ++hlf) {
+                const int pp = 2 * m + hlf;
+                const float x0 = w[2 * hlf], x1 = w[2 * hlf + 1];
+                if (pp < part) {
+                    G0 += x0;
+                    G1 += x1;
+                }
+                if (pp <= P15) {
+                    R10 += x0;
+                    R11 += x1;
+                }
+                GL0 += x0;
+                GL1 += x1;
+            }
+        }
+    }
+    const bool hi = tok0 >= 16;  // sub-tile of the run
+    const float ra0 = hi ? R10 : 0.f, ra1 = hi ? R11 : 0.f;
+    const float ea0 = hi ? GL0 : R10, ea1 = hi ? GL1 : R11;
+    const float er0 = fexp2(ra0), er1 = fexp2(ra1);  // e^{R_a}
+    // e^{G_last - R_a} = e^{E_a - R_a} (>= e^-80) e^{G_last - E_a} (<= 1); the
+    // product may be denormal, which fp32 multiplies keep
+    const float fe0 = fexp2(ea0 - ra0) * fexp2(GL0 - ea0);
+    const float fe1 = fexp2(ea1 - ra1) * fexp2(GL1 - ea1);
+    pclk.mark(8);
+    float kh0[C::TPT], kh1[C::TPT];
+#pragma unroll
+    for (int i = 0; i < C::TPT; ++i) {
+        const int t = tok0 + i;
+        G0 += g0[i];
+        G1 += g1[i];
+        const float d0 = G0 - ra0, d1 = G1 - ra1;
+        const float e1a = fexp2(d0), e1b = fexp2(d1);    // e^{G - R_a} in [e^-80, 1]
+        const float e2a = fexp2(-d0), e2b = fexp2(-d1);  // e^{R_a - G} in [1, e^80]
+        const float ga = e1a * er0, gb = e1b * er1;      // e^{G}
+        const float k0 = O::p0(r.k[i]), k1 = O::p1(r.k[i]);
+        const float kf0 = k0 * e2a, kf1 = k1 * e2b;
+        O::stp(sKE + t * C::SK + pc, k0 * e1a, k1 * e1b);
+        O::stp(sKF + t * C::SK + pc, kf0, kf1);
+        O::stp(sKG + t * C::SK + pc, -k0 * ga, -k1 * gb);
+        kh0[i] = kf0 * fe0;  // k e^{G_last - G}
+        kh1[i] = kf1 * fe1;
+        if (!SUMMARY) {
+            const float q0 = O::p0(r.q[i]), q1 = O::p1(r.q[i]);
+            O::stp(sQE + t * C::SK + pc, q0 * e1a, q1 * e1b);
+            O::stp(sQG + t * C::SK + pc, q0 * ga, q1 * gb);
+        }
+    }
+    pclk.mark(9);
+    // K-hat^T rows 2c, 2c+1 (tokens 4m..4m+3 stay contiguous under pcol)
+    if constexpr (C::TPT >= 4) {
+#pragma unroll
+        for (int i = 0; i < C::TPT; i += 4) {
+            const int tp = pcol(tok0 + i);
+            O::st4(sKH + (2 * cpair) * C::ST + tp, f32x4{kh0[i], kh0[i + 1], kh0[i + 2], kh0[i + 3]});
+            O::st4(sKH + (2 * cpair + 1) * C::ST + tp, f32x4{kh1[i], kh1[i + 1], kh1[i + 2], kh1[i + 3]});
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < C::TPT; ++i) {
+            const int tp = pcol(tok0 + i);
+            sKH[(2 * cpair) * C::ST + tp] = O::to_op(kh0[i]);
+            sKH[(2 * cpair + 1) * C::ST + tp] = O::to_op(kh1[i]);
+        }
+    }
+    if (part == 0) {
+        f32x2* vv = reinterpret_cast<f32x2*>(sVec);
+        vv[(V_YS * DK + pc) / 2] = f32x2{fexp2(R10), fexp2(R11)};
+        vv[((V_GC + buf) * DK + pc) / 2] = f32x2{fexp2(GL0), fexp2(GL1)};
+    }
+    if (ptid < BC) {
+        float bv;
+        if constexpr (DT::is_bf16) bv = bf16_to_f32(r.b);
+        else bv = r.b;
+        sB[ptid] = ptid < len ? bv : 0.f;
+    }
+    // v rows at their permuted column positions
+#pragma unroll
+    for (int j = 0; j < C::UPT_V; ++j) {
+        const int u = ptid + j * C::NPT;
+        if (C::U_V % C::NPT == 0 || u < C::U_V) {
+            const int row = u / C::UPR_V, cc = (u % C::UPR_V) * C::EPU;
+            const u32x4 w = r.v[j];
+            OT* rb = sV + row * C::SV;
+            if constexpr (C::ES == 2) {  // 8 columns -> two runs of 4
+                *reinterpret_cast<u32x2*>(rb + pcol(cc)) = u32x2{w[0], w[1]};
+                *reinterpret_cast<u32x2*>(rb + pcol(cc + 4)) = u32x2{w[2], w[3]};
+            } else {
+                *reinterpret_cast<u32x4*>(rb + pcol(cc)) = w;
+            }
+        }
+    }
+}
+
+// Prep stage of the alpha step: per 16x16 block (a, b), b <= a, of the block
+// the products -beta_r A (strictly lower, natural columns) and P (lower with
+// the diagonal, permuted columns), sharing the key-side fragment.  Task t:
+// blocks (0,0), (1,1), (1,0) for t = 0, 1, 2; with eight prep waves the P
+// products move to their own waves (t = 3, 4, 5).  The waves holding a
+// diagonal A block then invert their block of (I + A) in place
+// (wave-private, no barrier).
+template <typename C, typename DT, bool SUMMARY>
+__device__ __forceinline__ void prep_products(unsigned char* smem, int buf, int pw, int lane)
+{
     using O = Op<DT>;
     using OT = typename O::T;
     using Frag = typename O::Frag;
-    using Frag4 = typename O::Frag4;
-    using Pair = typename O::Pair;
-    using ST = typename DT::storage;
-    constexpr float LOG2E = 1.4426950408889634f;
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    OT* sQ = reinterpret_cast<OT*>(smem + C::O_Q);
-    OT* sK = reinterpret_cast<OT*>(smem + C::O_K);
-    OT* sG = reinterpret_cast<OT*>(smem + C::O_G);
-    OT* sV = reinterpret_cast<OT*>(smem + C::O_V);
-    OT* sQG = reinterpret_cast<OT*>(smem + C::O_QG);
-    OT* sKG = reinterpret_cast<OT*>(smem + C::O_KG);
-    OT* sKH = reinterpret_cast<OT*>(smem + C::O_KH);
+    constexpr int DK = C::DK;
+    constexpr bool SPLIT = !SUMMARY && C::NPW >= 6;
+    if (pw >= (SPLIT ? 6 : 3)) return;
+    const bool doA = !SPLIT || pw < 3, doP = !SUMMARY && (!SPLIT || pw >= 3);
+    const int t = SPLIT && pw >= 3 ? pw - 3 : pw;
+    const OT* sKE = reinterpret_cast<const OT*>(smem + C::O_KE);
+    const OT* sKF = reinterpret_cast<const OT*>(smem + C::O_KF);
+    const OT* sQE = reinterpret_cast<const OT*>(smem + C::O_QE);
     OT* sA = reinterpret_cast<OT*>(smem + C::O_A);
     OT* sP = reinterpret_cast<OT*>(smem + C::O_P);
     OT* sD = reinterpret_cast<OT*>(smem + C::O_D);
     OT* sDS = reinterpret_cast<OT*>(smem + C::O_DS);
-    ST* sO = reinterpret_cast<ST*>(smem + C::O_KG);  // output staging (reuses the -k.e^G tile)
-    float* sVec = reinterpret_cast<float*>(smem + C::O_VEC);
-    float* sSig = reinterpret_cast<float*>(smem + C::O_SIG);
-    float* sB = reinterpret_cast<float*>(smem + C::O_B);
+    const float* sVec = reinterpret_cast<const float*>(smem + C::O_VEC);
+    const float* sB = reinterpret_cast<const float*>(smem + C::O_B) + buf * BC;
+    const int l16 = lane & 15, q4 = lane >> 4;
+    const int a = t == 0 ? 0 : 1, b = t == 1 ? 1 : 0;
+    Frag yf[DK / 32], kf[DK / 32], qf[DK / 32];
+#pragma unroll
+    for (int kb = 0; kb < DK / 32; ++kb) {
+        yf[kb] = O::load(sKF + (b * 16 + l16) * C::SK + kb * 32 + 8 * q4);
+        if (doA) kf[kb] = O::load(sKE + (a * 16 + l16) * C::SK + kb * 32 + 8 * q4);
+        if (doP) qf[kb] = O::load(sQE + (a * 16 + l16) * C::SK + kb * 32 + 8 * q4);
+    }
+    f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < DK / 32; ++kb) {
+        Frag y = yf[kb];
+        if (b < a) {  // off-diagonal: key side moved from R_0 to R_1
+            float tt[8];
+            O::unpack(y, tt);
+            const f32x4* fv = reinterpret_cast<const f32x4*>(sVec + V_YS * DK + kb * 32 + 8 * q4);
+            const f32x4 f0 = fv[0], f1 = fv[1];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                tt[e] *= f0[e];
+                tt[4 + e] *= f1[e];
+            }
+            y = O::make(tt);
+        }
+        if (doA) O::mma(accA, y, kf[kb]);
+        if (doP) O::mma(accP, y, qf[kb]);
+    }
+    // acc: lane (column r = 16a + l16, rows i = 16b + 4*q4 + j)
+    const int rr = a * 16 + l16;
+    const int i0 = b * 16 + 4 * q4;
+    f32x4 v4;
+    if (doA) {
+        const float br = -sB[rr];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v4[j] = (i0 + j < rr) ? br * accA[j] : 0.f;
+        O::st4(sA + rr * C::ST + i0, v4);
+    }
+    if (doP) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v4[j] = (i0 + j <= rr) ? accP[j] : 0.f;
+        O::st4(sP + rr * C::ST + pcol(i0), v4);
+    }
+    if (doA && a == b) {
+        // this wave's block is complete in LDS (in-order within the wave)
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        diag_inverse<C, O>(sA, sD, sDS, a, lane);
+    }
+}
+
+template <typename DT, int DK, int DV, bool SUMMARY>
+__global__ void __launch_bounds__((BlockCfg<DT, DK, DV, SUMMARY>::NT))
+prefill_block_kernel(PrefillDev p)
+{
+    using C = BlockCfg<DT, DK, DV, SUMMARY>;
+    using O = Op<DT>;
+    using OT = typename O::T;
+    using Frag = typename O::Frag;
+    using Frag4 = typename O::Frag4;
+    using ST = typename DT::storage;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    const OT* sKG = reinterpret_cast<const OT*>(smem + C::O_KG);
+    const OT* sV = reinterpret_cast<const OT*>(smem + C::O_V);
+    const OT* sA = reinterpret_cast<const OT*>(smem + C::O_A);
+    OT* sP = reinterpret_cast<OT*>(smem + C::O_P);
+    const OT* sD = reinterpret_cast<const OT*>(smem + C::O_D);
+    const float* sVec = reinterpret_cast<const float*>(smem + C::O_VEC);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int l16 = lane & 15;
     const int q4 = lane >> 4;
+    PhaseClock pclk;
 #ifdef KDA_PHASE_TIMING
-    long long phase_acc[12] = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-    long long phase_last = clock64();
+    pclk.on = tid == KDA_PHASE_TID;
+    pclk.last = clock64();
 #endif
 
     // ---- work item
@@ -665,21 +863,62 @@ prefill_chunk_kernel(PrefillDev p)
     int64_t t_end = t_begin + int64_t(p.L) * CH;
     if (t_end > seq1) t_end = seq1;
     const bool last_seg = (s == nseg - 1);
-
-    const ST* gq = static_cast<const ST*>(p.q);
-    const ST* gk = static_cast<const ST*>(p.k);
-    const ST* gv = static_cast<const ST*>(p.v);
-    const ST* gg = static_cast<const ST*>(p.g);
-    const ST* gb = static_cast<const ST*>(p.beta);
+    const int64_t nblk = (t_end - t_begin + BC - 1) / BC;
     ST* go = static_cast<ST*>(p.o);
 
-    // ---- chain registers: wave owns columns [32*wave, 32*wave+32) of the extended state
+    // strictly-upper 16x16 block of P: read by the P U product, never written
+    if (!SUMMARY)
+        for (int e = tid; e < BC * BC; e += C::NT) {
+            const int r = e / BC, c = e % BC;
+            if ((c >> 4) > (r >> 4)) sP[r * C::ST + pcol(c)] = O::to_op(0.f);
+        }
+    auto blen = [&](int64_t bi) {
+        const int64_t b0 = t_begin + bi * BC;
+        return int(t_end - b0 < BC ? t_end - b0 : BC);
+    };
+
+    // The two roles run separate loops with the same barrier sequence (one
+    // after the prologue, two per block), so their registers never overlap.
+    if (wave >= C::NCW) {
+        // ================= prep waves
+        const int pw = wave - C::NCW;
+        const int ptid = tid - 64 * C::NCW;
+        const int part = lane / C::CPW;
+        const int cpair = pw * C::CPW + lane % C::CPW;
+        const int tok0 = part * C::TPT;
+        PrepRegs<C, DT> pr;
+        if (nblk > 0) {
+            prep_load<C, DT, SUMMARY>(pr, p, t_begin, blen(0), h, ptid, cpair, tok0);
+            prep_tiles<C, DT, SUMMARY>(pr, smem, 0, blen(0), lane, ptid, cpair, part, tok0, pclk);
+            if (nblk > 1) prep_load<C, DT, SUMMARY>(pr, p, t_begin + BC, blen(1), h, ptid, cpair, tok0);
+        }
+        __syncthreads();
+        KDA_PHASE(4);
+        for (int64_t bi = 0; bi < nblk; ++bi) {
+            const int buf = int(bi & 1);
+            prep_products<C, DT, SUMMARY>(smem, buf, pw, lane);  // alpha: block bi
+            KDA_PHASE(0);
+            __syncthreads();
+            KDA_PHASE(1);
+            if (bi + 1 < nblk) {  // beta: tiles of block bi+1, loads of block bi+2
+                prep_tiles<C, DT, SUMMARY>(pr, smem, buf ^ 1, blen(bi + 1), lane, ptid, cpair, part, tok0, pclk);
+                KDA_PHASE(10);
+                if (bi + 2 < nblk)
+                    prep_load<C, DT, SUMMARY>(pr, p, t_begin + (bi + 2) * BC, blen(bi + 2), h, ptid, cpair, tok0);
+            }
+            KDA_PHASE(2);
+            __syncthreads();
+            KDA_PHASE(3);
+        }
+        pclk.save();
+        return;
+    }
+
+    // ================= chain waves: 32 columns of the extended state each, in registers
     constexpr int RT = DK / 16;  // state row tiles
-    const bool chain = wave < C::NCW;
-    constexpr int NCT = C::NCT;
-    const int colbase = C::CW * wave;
+    const int colbase = 32 * wave;
     const bool mcols = SUMMARY && colbase >= DV;
-    f32x4 S[RT][NCT];
+    f32x4 S[RT][2];
     {
         const float* src = nullptr;
         if (!SUMMARY) {
@@ -692,419 +931,146 @@ prefill_chunk_kernel(PrefillDev p)
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct)
+            for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int row = rt * 16 + 4 * q4 + j;
                     const int col = colbase + ct * 16 + l16;
                     float x = 0.f;
-                    if (chain) {
-                        if (mcols) x = (row == col - DV) ? 1.f : 0.f;
-                        else if (src) x = src[row * DV + col];
-                    }
+                    if (mcols) x = (row == col - DV) ? 1.f : 0.f;
+                    else if (src) x = src[row * DV + col];
                     S[rt][ct][j] = x;
                 }
     }
-
-    // strictly-upper 16x16 blocks of P are read by the P U product and never written
-    if (!SUMMARY)
-        for (int e = tid; e < CH * CH; e += C::NT) {
-            const int r = e / CH, c = e % CH;
-            if ((c >> 4) > (r >> 4)) sP[r * C::ST + pcol(c)] = O::to_op(0.f);
-        }
-
-    // identity fragments (exact) for X = V I: pick this wave's columns out of
-    // the 32-column block that holds them
-    Frag Iden[NCT];
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-        float x[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = (kperm(q4, e) == (colbase & 31) + ct * 16 + l16) ? 1.f : 0.f;
-        Iden[ct] = O::make(x);
-    }
-
-    u32x4 pre[C::UPT];
-    const int64_t nchunks = (t_end - t_begin + CH - 1) / CH;
-    if (nchunks > 0)
-        raw_prefetch<C, DT>(pre, gq, gk, gv, gg, t_begin, int(t_end - t_begin < CH ? t_end - t_begin : CH),
-                            p.T_total, H, h, tid, DK, DV);
-
-    const int cp = tid % C::CP;  // channel pair (elementwise phases)
-    const int part = tid / C::CP;
-    const int pc = pcol(2 * cp);  // stored position of channels 2cp, 2cp+1 (adjacent)
-    const int tok0 = part * C::TPT;
-
-    int64_t prev_c0 = 0;
-    int prev_len = 0;
-    for (int64_t ci = 0; ci < nchunks; ++ci) {
-        const int64_t c0 = t_begin + ci * CH;
-        const int len = int(t_end - c0 < CH ? t_end - c0 : CH);
-        __syncthreads();  // the previous chunk's operands are no longer read
-        KDA_PHASE(0);
-        if (!SUMMARY && C::STAGE_O && ci > 0) store_out_tile<C, DT, DV>(smem, go, prev_c0, prev_len, H, h, tid);
-        raw_commit<C>(pre, smem, tid, len);
-        __syncthreads();
-        KDA_PHASE(1);
-
-        // beta for this chunk: loaded now, first needed by the products (two phases later)
-        float bload = 0.f;
-        if (tid < CH) bload = load_elem<DT>(gb, (c0 + (tid < len ? tid : len - 1)) * H + h);
-        // ---- phase A: per-slot sums of g (log2 domain), two channels per thread
-#pragma unroll
-        for (int sl = 0; sl < C::TPT / C::SL; ++sl) {
-            float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-            for (int i = 0; i < C::SL; ++i) {
-                const Pair w = O::ldp(sG + (tok0 + sl * C::SL + i) * C::SK + pc);
-                a0 += O::p0(w);
-                a1 += O::p1(w);
-            }
-            const int slot = tok0 / C::SL + sl;
-            *reinterpret_cast<f32x2*>(sSig + slot * DK + pc) = f32x2{a0 * LOG2E, a1 * LOG2E};
-        }
-        __syncthreads();
-
-        KDA_PHASE(2);
-        // ---- phase B: decayed operand tiles and channel vectors
+    __syncthreads();
+    KDA_PHASE(4);
+    for (int64_t bi = 0; bi < nblk; ++bi) {
+        const int64_t b0 = t_begin + bi * BC;
+        const int len = blen(bi);
+        const int buf = int(bi & 1);
+        // ---- alpha: X = V - (K . e^G) S, rows = the block's 32 tokens
+        f32x4 Xt[2][2];
         {
-            float R0[5], R1[5];  // G before sub-tile a (log2 domain); R[4] = G at chunk end
-            R0[0] = R1[0] = 0.f;
-            float r0 = 0.f, r1 = 0.f, G0 = 0.f, G1 = 0.f;
-#pragma unroll
-            for (int sl = 0; sl < C::NSLOT; ++sl) {
-                if (sl == tok0 / C::SL) {
-                    G0 = r0;
-                    G1 = r1;
-                }
-                const f32x2 sg = *reinterpret_cast<const f32x2*>(sSig + sl * DK + pc);
-                r0 += sg[0];
-                r1 += sg[1];
-                if (((sl + 1) * C::SL) % 16 == 0) {
-                    R0[((sl + 1) * C::SL) / 16] = r0;
-                    R1[((sl + 1) * C::SL) / 16] = r1;
-                }
-            }
-            if (part == 0) {
-                f32x2* vv = reinterpret_cast<f32x2*>(sVec);
-#pragma unroll
-                for (int a = 0; a < 4; ++a) vv[((V_ER + a) * DK + pc) / 2] = f32x2{fexp2(R0[a]), fexp2(R1[a])};
-                // key side of block (a, b): e^{R_a - R_b} = e^{E_b - R_b} e^{R_a - E_b}; the
-                // first factor is >= e^-80 (one sub-tile), the second may underflow only
-                // when the true value is negligible; the multiply keeps denormals
-#pragma unroll
-                for (int a = 1; a < 4; ++a)
-#pragma unroll
-                    for (int b = 0; b < a; ++b)
-                        vv[((V_YS + ys_slot(a, b)) * DK + pc) / 2] =
-                            f32x2{fexp2(R0[b + 1] - R0[b]) * fexp2(R0[a] - R0[b + 1]),
-                                  fexp2(R1[b + 1] - R1[b]) * fexp2(R1[a] - R1[b + 1])};
-                vv[(V_GC * DK + pc) / 2] = f32x2{fexp2(R0[4]), fexp2(R1[4])};
-            }
-            // all loads of this thread's tokens first
-            Pair wg[C::TPT], wk[C::TPT], wq[C::TPT];
-#pragma unroll
-            for (int i = 0; i < C::TPT; ++i) {
-                const int r = tok0 + i;
-                wg[i] = O::ldp(sG + r * C::SK + pc);
-                wk[i] = O::ldp(sK + r * C::SK + pc);
-                if (!SUMMARY) wq[i] = O::ldp(sQ + r * C::SK + pc);
-            }
-            float kh0[C::TPT], kh1[C::TPT];
-            // the thread's tokens cover whole sub-tiles (TPT >= 16) or lie in one (TPT < 16)
-            constexpr int SPAN = C::TPT < 16 ? C::TPT : 16;
-#pragma unroll
-            for (int i0 = 0; i0 < C::TPT; i0 += SPAN) {
-                const int a = (tok0 + i0) >> 4;
-                const float ra0 = a == 0 ? R0[0] : a == 1 ? R0[1] : a == 2 ? R0[2] : R0[3];
-                const float ra1 = a == 0 ? R1[0] : a == 1 ? R1[1] : a == 2 ? R1[2] : R1[3];
-                const float rb0 = a == 0 ? R0[1] : a == 1 ? R0[2] : a == 2 ? R0[3] : R0[4];  // E_a
-                const float rb1 = a == 0 ? R1[1] : a == 1 ? R1[2] : a == 2 ? R1[3] : R1[4];
-                const float er0 = fexp2(ra0), er1 = fexp2(ra1);  // e^{R_a}
-                // e^{G_last - R_a} as e^{E_a - R_a} (>= e^-80) times e^{G_last - E_a}; the
-                // product may be denormal, which fp32 multiplies keep
-                const float fe0 = fexp2(rb0 - ra0) * fexp2(R0[4] - rb0);
-                const float fe1 = fexp2(rb1 - ra1) * fexp2(R1[4] - rb1);
-#pragma unroll
-                for (int i = i0; i < i0 + SPAN; ++i) {
-                    const int r = tok0 + i;
-                    G0 += O::p0(wg[i]) * LOG2E;
-                    G1 += O::p1(wg[i]) * LOG2E;
-                    const float d0 = G0 - ra0, d1 = G1 - ra1;
-                    const float e1a = fexp2(d0), e1b = fexp2(d1);    // e^{G - R_a} in [e^-80, 1]
-                    const float e2a = fexp2(-d0), e2b = fexp2(-d1);  // e^{R_a - G} in [1, e^80]
-                    const float ga = e1a * er0, gb2 = e1b * er1;                // e^{G}
-                    const float k0 = O::p0(wk[i]), k1 = O::p1(wk[i]);
-                    const float kf0 = k0 * e2a, kf1 = k1 * e2b;
-                    O::stp(sK + r * C::SK + pc, k0 * e1a, k1 * e1b);
-                    O::stp(sG + r * C::SK + pc, kf0, kf1);
-                    O::stp(sKG + r * C::SK + pc, -k0 * ga, -k1 * gb2);
-                    // k e^{G_last - G} = (k e^{R_a - G}) e^{G_last - R_a}
-                    kh0[i] = kf0 * fe0;
-                    kh1[i] = kf1 * fe1;
-                    if (!SUMMARY) {
-                        const float q0 = O::p0(wq[i]), q1 = O::p1(wq[i]);
-                        O::stp(sQ + r * C::SK + pc, q0 * e1a, q1 * e1b);
-                        O::stp(sQG + r * C::SK + pc, q0 * ga, q1 * gb2);
-                    }
-                }
-            }
-            if (tid < CH) sB[tid] = tid < len ? bload : 0.f;
-            // transposed K-hat rows (channels 2cp, 2cp+1): 4 tokens per store when a
-            // thread owns at least 4 (tokens 4m..4m+3 sit contiguously after pcol)
-            if constexpr (C::TPT >= 4) {
-#pragma unroll
-                for (int i = 0; i < C::TPT; i += 4) {
-                    const int tp = pcol(tok0 + i);
-                    O::st4(sKH + (2 * cp) * C::ST + tp, f32x4{kh0[i], kh0[i + 1], kh0[i + 2], kh0[i + 3]});
-                    O::st4(sKH + (2 * cp + 1) * C::ST + tp, f32x4{kh1[i], kh1[i + 1], kh1[i + 2], kh1[i + 3]});
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < C::TPT; ++i) {
-                    const int tp = pcol(tok0 + i);
-                    sKH[(2 * cp) * C::ST + tp] = O::to_op(kh0[i]);
-                    sKH[(2 * cp + 1) * C::ST + tp] = O::to_op(kh1[i]);
-                }
-            }
-        }
-        __syncthreads();
-
-        KDA_PHASE(3);
-        // ---- prefetch the next chunk while the chain runs
-        if (ci + 1 < nchunks) {
-            const int64_t n0 = c0 + CH;
-            raw_prefetch<C, DT>(pre, gq, gk, gv, gg, n0, int(t_end - n0 < CH ? t_end - n0 : CH), p.T_total,
-                                H, h, tid, DK, DV);
-        }
-
-        KDA_PHASE(4);
-        // ---- chain part 1: X = V - (K . e^G) S   (rows = tokens; 4 row tiles x 2 column tiles)
-        Frag Sb[DK / 32][NCT];
-        f32x4 Xt[4][NCT];
-        if (chain) {
+            Frag Sb[DK / 32][2];
 #pragma unroll
             for (int kb = 0; kb < DK / 32; ++kb)
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) Sb[kb][ct] = acc_frag<DT>(S[2 * kb][ct], S[2 * kb + 1][ct]);
+                for (int ct = 0; ct < 2; ++ct) Sb[kb][ct] = acc_frag<DT>(S[2 * kb][ct], S[2 * kb + 1][ct]);
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt)
+            for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) Xt[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int ct = 0; ct < 2; ++ct) Xt[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
             if (!mcols) {
+                // V I with exact identity fragments picking column ct*16 + l16 of the wave's 32
 #pragma unroll
-                for (int rt = 0; rt < 4; ++rt) {
-                    const Frag vf = O::load(sV + (rt * 16 + l16) * C::SV + (colbase & ~31) + 8 * q4);
+                for (int ct = 0; ct < 2; ++ct) {
+                    float x[8];
 #pragma unroll
-                    for (int ct = 0; ct < NCT; ++ct) O::mma(Xt[rt][ct], vf, Iden[ct]);
+                    for (int e = 0; e < 8; ++e) x[e] = (kperm(q4, e) == ct * 16 + l16) ? 1.f : 0.f;
+                    const Frag iden = O::make(x);
+#pragma unroll
+                    for (int rt = 0; rt < 2; ++rt)
+                        O::mma(Xt[rt][ct], O::load(sV + (rt * 16 + l16) * C::SV + colbase + 8 * q4), iden);
                 }
             }
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt)
+            for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
                 for (int kb = 0; kb < DK / 32; ++kb) {
                     const Frag af = O::load(sKG + (rt * 16 + l16) * C::SK + kb * 32 + 8 * q4);
 #pragma unroll
-                    for (int ct = 0; ct < NCT; ++ct) O::mma(Xt[rt][ct], af, Sb[kb][ct]);
+                    for (int ct = 0; ct < 2; ++ct) O::mma(Xt[rt][ct], af, Sb[kb][ct]);
                 }
         }
+        KDA_PHASE(0);
+        __syncthreads();
+        KDA_PHASE(1);
+        // ---- beta: U = (I + A)^{-1} Diag(beta) X by block substitution:
+        //   U_0 = D_0 beta_0 X_0,  U_1 = D_1 (beta_1 X_1 - A_10 U_0)
+        const float* sBb = reinterpret_cast<const float*>(smem + C::O_B) + buf * BC;
+        f32x4 U0[2], U1[2];
+        {
+            const f32x4 bv0 = *reinterpret_cast<const f32x4*>(sBb + 4 * q4);
+            const f32x4 bv1 = *reinterpret_cast<const f32x4*>(sBb + 16 + 4 * q4);
+            const Frag4 d0 = O::load4(sD + l16 * C::SD + 4 * q4);
+            const Frag4 d1 = O::load4(sD + (16 + l16) * C::SD + 4 * q4);
+            const Frag4 a10 = O::load4(sA + (16 + l16) * C::ST + 4 * q4);
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                U0[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+                O::mma4(U0[ct], d0, O::make4(bv0 * Xt[0][ct]));
+                f32x4 R = bv1 * Xt[1][ct];
+                O::mma4(R, a10, O::make4(U0[ct]));
+                U1[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+                O::mma4(U1[ct], d1, O::make4(R));
+            }
+        }
+        Frag Ub[2];
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) Ub[ct] = acc_frag<DT>(U0[ct], U1[ct]);
         KDA_PHASE(5);
-        // ---- products per 16x16 block (a, b), b <= a, sharing the key-side fragment:
-        //      -A x beta_r (strictly lower, natural columns) and P (lower incl. diagonal)
-        // With 8 waves, waves 4..7 take the diagonal blocks and invert them at once
-        // (their own LDS writes, so no barrier), while waves 0..3 take the six
-        // off-diagonal blocks.  Otherwise blocks go round-robin and the
-        // inversion follows in its own phase.
-        constexpr bool DIAG_WAVES = C::NW == 8;
-        const int ntask = DIAG_WAVES ? (wave < 4 ? (wave < 2 ? 2 : 1) : 1) : (10 - wave + C::NW - 1) / C::NW;
-        for (int tk = 0; tk < ntask; ++tk) {
-            int a, b;
-            if (DIAG_WAVES) {
-                if (wave >= 4) {
-                    a = b = wave - 4;
-                } else {
-                    const int ot = wave + 4 * tk;  // off-diagonal (1,0),(2,0),(2,1),(3,0),(3,1),(3,2)
-                    a = ot == 0 ? 1 : ot <= 2 ? 2 : 3;
-                    b = ot == 0 ? 0 : ot == 1 ? 0 : ot == 2 ? 1 : ot - 3;
+        if (!SUMMARY) {
+            // O^T = S^T (Q . e^G)^T + U^T P^T: each lane ends up with four
+            // consecutive value columns of one token
+            const OT* sQG = reinterpret_cast<const OT*>(smem + C::O_QG + buf * C::TILE_K);
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+                f32x4 Ot[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+                for (int kb = 0; kb < DK / 32; ++kb) {
+                    const Frag bf = O::load(sQG + (rt * 16 + l16) * C::SK + kb * 32 + 8 * q4);
+#pragma unroll
+                    for (int ct = 0; ct < 2; ++ct)
+                        O::mma(Ot[ct], acc_frag<DT>(S[2 * kb][ct], S[2 * kb + 1][ct]), bf);
                 }
-            } else {
-                int bi = wave + tk * C::NW;
-                a = 0;
-                while (bi > a) {
-                    bi -= a + 1;
-                    ++a;
+                const Frag pf = O::load(sP + (rt * 16 + l16) * C::ST + 8 * q4);
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct) O::mma(Ot[ct], Ub[ct], pf);
+                const int row = rt * 16 + l16;
+                if (row < len) {
+#pragma unroll
+                    for (int ct = 0; ct < 2; ++ct)
+                        store4<DT>(go + ((b0 + row) * H + h) * DV + colbase + ct * 16 + 4 * q4, Ot[ct]);
                 }
-                b = bi;  // 0 <= b <= a
-            }
-            Frag yf[DK / 32], kf[DK / 32], qf[DK / 32];
-#pragma unroll
-            for (int kb = 0; kb < DK / 32; ++kb) {
-                yf[kb] = O::load(sG + (b * 16 + l16) * C::SK + kb * 32 + 8 * q4);
-                kf[kb] = O::load(sK + (a * 16 + l16) * C::SK + kb * 32 + 8 * q4);
-                if (!SUMMARY) qf[kb] = O::load(sQ + (a * 16 + l16) * C::SK + kb * 32 + 8 * q4);
-            }
-            f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < DK / 32; ++kb) {
-                Frag y = yf[kb];
-                if (b < a) {  // off-diagonal: key side moved from R_b to R_a
-                    float t[8];
-                    O::unpack(y, t);
-                    const f32x4* fv = reinterpret_cast<const f32x4*>(sVec + (V_YS + ys_slot(a, b)) * DK + kb * 32 + 8 * q4);
-                    const f32x4 f0 = fv[0], f1 = fv[1];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        t[e] *= f0[e];
-                        t[4 + e] *= f1[e];
-                    }
-                    y = O::make(t);
-                }
-                O::mma(accA, y, kf[kb]);
-                if (!SUMMARY) O::mma(accP, y, qf[kb]);
-            }
-            // acc: lane (col r = 16a + l16, rows i = 16b + 4*q4 + j)
-            const int r = a * 16 + l16;
-            const int i0 = b * 16 + 4 * q4;
-            const float br = -sB[r];
-            f32x4 v4;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) v4[j] = (i0 + j < r) ? br * accA[j] : 0.f;
-            O::st4(sA + r * C::ST + i0, v4);
-            if (!SUMMARY) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) v4[j] = (i0 + j <= r) ? accP[j] : 0.f;
-                O::st4(sP + r * C::ST + pcol(i0), v4);
-            }
-            if (DIAG_WAVES && wave >= 4) {
-                // this wave's block is complete in LDS (in-order within the wave)
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                __builtin_amdgcn_wave_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-                diag_inverse<C, O>(sA, sD, sDS, a, lane);
             }
         }
-        __syncthreads();
-
         KDA_PHASE(6);
-        // ---- diagonal blocks (I + A_aa)^{-1} (when not already done in the products phase)
-        if (!DIAG_WAVES) {
-            for (int a = wave; a < 4; a += C::NW) diag_inverse<C, O>(sA, sD, sDS, a, lane);
-        }
-        KDA_PHASE(7);
-        if (!DIAG_WAVES) __syncthreads();
-        KDA_PHASE(8);
-
-        if (chain) {
-            // ---- U = (I + A)^{-1} Diag(beta) X by block forward substitution:
-            //      U_a = D_a (beta_a X_a - sum_{b<a} A_ab U_b)
-            f32x4 Ut[4][NCT];
-            Frag4 Uf[4][NCT];
+        // S <- Diag(e^{G_last}) S + (K . e^{G_last - G})^T U
+        const OT* sKH = reinterpret_cast<const OT*>(smem + C::O_KH + buf * C::TILE_H);
+        const float* gcv = sVec + (V_GC + buf) * DK;
 #pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                const f32x4 bv = *reinterpret_cast<const f32x4*>(sB + a * 16 + 4 * q4);
-                f32x4 R[NCT];
+        for (int rt = 0; rt < RT; ++rt) {
+            const f32x4 gc = *reinterpret_cast<const f32x4*>(gcv + pcol(rt * 16 + 4 * q4));
+            const Frag kf = O::load(sKH + (rt * 16 + l16) * C::ST + 8 * q4);
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) R[ct] = bv * Xt[a][ct];
-#pragma unroll
-                for (int b = 0; b < a; ++b) {
-                    const Frag4 af = O::load4(sA + (a * 16 + l16) * C::ST + b * 16 + 4 * q4);
-#pragma unroll
-                    for (int ct = 0; ct < NCT; ++ct) O::mma4(R[ct], af, Uf[b][ct]);
-                }
-                const Frag4 df = O::load4(sD + (a * 16 + l16) * C::SD + 4 * q4);
-#pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) {
-                    Ut[a][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    O::mma4(Ut[a][ct], df, O::make4(R[ct]));
-                    Uf[a][ct] = O::make4(Ut[a][ct]);
-                }
-            }
-            KDA_PHASE(10);
-            Frag Ub[2][NCT];
-#pragma unroll
-            for (int kbt = 0; kbt < 2; ++kbt)
-#pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) Ub[kbt][ct] = acc_frag<DT>(Ut[2 * kbt][ct], Ut[2 * kbt + 1][ct]);
-
-            if (!SUMMARY) {
-                // ---- O^T = S^T (Q . e^G)^T + U^T P^T: the register fragments of S and U
-                //      serve as the left operand, so each lane ends up holding four
-                //      consecutive value columns of one token (one 8-byte store)
-#pragma unroll
-                for (int rt = 0; rt < 4; ++rt) {
-                    f32x4 Ot[NCT];
-#pragma unroll
-                    for (int ct = 0; ct < NCT; ++ct) Ot[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int kb = 0; kb < DK / 32; ++kb) {
-                        const Frag bf = O::load(sQG + (rt * 16 + l16) * C::SK + kb * 32 + 8 * q4);
-#pragma unroll
-                        for (int ct = 0; ct < NCT; ++ct) O::mma(Ot[ct], Sb[kb][ct], bf);
-                    }
-#pragma unroll
-                    for (int kbt = 0; kbt <= rt / 2; ++kbt) {
-                        const Frag pf = O::load(sP + (rt * 16 + l16) * C::ST + kbt * 32 + 8 * q4);
-#pragma unroll
-                        for (int ct = 0; ct < NCT; ++ct) O::mma(Ot[ct], Ub[kbt][ct], pf);
-                    }
-                    const int row = rt * 16 + l16;  // token
-#pragma unroll
-                    for (int ct = 0; ct < NCT; ++ct) {
-                        const int col = colbase + ct * 16 + 4 * q4;
-                        if (C::STAGE_O) store4<DT>(sO + row * C::SO + col, Ot[ct]);
-                        else if (row < len) store4<DT>(go + ((c0 + row) * H + h) * DV + col, Ot[ct]);
-                    }
-                }
-            }
-
-            KDA_PHASE(11);
-            // ---- S <- Diag(e^{G_last}) S + (K . e^{G_last - G})^T U
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-                // channels rt*16 + 4q .. +3 are stored contiguously (permuted position)
-                const f32x4 gc = *reinterpret_cast<const f32x4*>(sVec + V_GC * DK + pcol(rt * 16 + 4 * q4));
-#pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) S[rt][ct] *= gc;
-#pragma unroll
-                for (int kbt = 0; kbt < 2; ++kbt) {
-                    const Frag kf = O::load(sKH + (rt * 16 + l16) * C::ST + kbt * 32 + 8 * q4);
-#pragma unroll
-                    for (int ct = 0; ct < NCT; ++ct) O::mma(S[rt][ct], kf, Ub[kbt][ct]);
-                }
+            for (int ct = 0; ct < 2; ++ct) {
+                S[rt][ct] *= gc;
+                O::mma(S[rt][ct], kf, Ub[ct]);
             }
         }
-        prev_c0 = c0;
-        prev_len = len;
-    }
-    if (!SUMMARY && C::STAGE_O && nchunks > 0) {
+        KDA_PHASE(2);
         __syncthreads();
-        store_out_tile<C, DT, DV>(smem, go, prev_c0, prev_len, H, h, tid);
+        KDA_PHASE(3);
     }
 
-    KDA_PHASE(9);
-#ifdef KDA_PHASE_TIMING
-    if (tid == KDA_PHASE_TID && blockIdx.x < 16384)
-        for (int i = 0; i < 12; ++i) kda_phase_cycles[blockIdx.x * 16 + i] = phase_acc[i];
-#endif
+    pclk.save();
     // ---- write the segment result
-    if (chain) {
-        float* dst = nullptr;
-        int ld = DV;
-        if (SUMMARY) {
-            dst = p.ms + (int64_t(item) * H + h) * DK * (DK + DV);  // [S~ | M], rows of DK + DV
-            ld = DK + DV;
-        } else if (last_seg && p.fin) {
-            dst = p.fin + (int64_t(n) * H + h) * DK * DV;
-        }
-        if (dst) {
+    float* dst = nullptr;
+    int ld = DV;
+    if (SUMMARY) {
+        dst = p.ms + (int64_t(item) * H + h) * DK * (DK + DV);  // [S~ | M], rows of DK + DV
+        ld = DK + DV;
+    } else if (last_seg && p.fin) {
+        dst = p.fin + (int64_t(n) * H + h) * DK * DV;
+    }
+    if (dst) {
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
+        for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct)
+            for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        dst[(rt * 16 + 4 * q4 + j) * ld + colbase + ct * 16 + l16] = S[rt][ct][j];
-        }
+                for (int j = 0; j < 4; ++j)
+                    dst[(rt * 16 + 4 * q4 + j) * ld + colbase + ct * 16 + l16] = S[rt][ct][j];
     }
 }
 
@@ -1261,8 +1227,8 @@ hipError_t launch_prefill_t(const PrefillArgs& a, const PrefillPlan& plan, hipSt
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (plan.np1_max > 0) {
-        using C1 = ChunkCfg<DT, DK, DV, true>;
-        auto k1 = prefill_chunk_kernel<DT, DK, DV, true>;
+        using C1 = BlockCfg<DT, DK, DV, true>;
+        auto k1 = prefill_block_kernel<DT, DK, DV, true>;
         e = hipFuncSetAttribute(reinterpret_cast<const void*>(k1),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, C1::LDS);
         if (e != hipSuccess) return e;
@@ -1276,8 +1242,8 @@ hipError_t launch_prefill_t(const PrefillArgs& a, const PrefillPlan& plan, hipSt
         hipLaunchKernelGGL(ks, dim3(unsigned(a.N * a.H * (DV / SCAN_COLS))), dim3(256), scan_lds, stream, d);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    using C3 = ChunkCfg<DT, DK, DV, false>;
-    auto k3 = prefill_chunk_kernel<DT, DK, DV, false>;
+    using C3 = BlockCfg<DT, DK, DV, false>;
+    auto k3 = prefill_block_kernel<DT, DK, DV, false>;
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(k3),
                             hipFuncAttributeMaxDynamicSharedMemorySize, C3::LDS);
     if (e != hipSuccess) return e;

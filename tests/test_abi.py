@@ -90,6 +90,8 @@ def test_prefill_workspace_size(L):
     assert ws(8192, 1, 32, 128, 128, dtype=F32) == 0      # fp32 needs d_k = 32
     assert ws(8192, 1, 32, 64, 64, dtype=F32) == 0
     assert ws(256, 1, 2, 32, 32, dtype=F32) > 0
+    assert ws(256, 1, 16384, 32, 32) > 0
+    assert ws(256, 1, 16385, 32, 32) == 0                 # H above KDA_MAX_HEADS
     # a sequence too short to split needs no segment buffers
     small = ws(64 * 16, 1, 32, 128, 128)
     assert small < 4096
@@ -119,6 +121,7 @@ def test_prefill_validation(L):
     assert call(chunk=32) == 2
     assert call(dt=F32, dk=128, dv=128) == 2
     assert call(dt=9) == 2
+    assert call(H=16385) == 2                               # H above KDA_MAX_HEADS
     assert call(q=None) == 1
     assert call(o=None) == 1
     if need > 0:
