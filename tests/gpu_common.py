@@ -36,3 +36,19 @@ def relerr(got, want) -> float:
 
 def announce(msg: str):
     print(f"[case] {msg}", flush=True)
+
+
+def dev_stream(wl, name: str, set_index: int = 0, rows: int = 1 << 16):
+    """A token tensor of a (possibly very long) workload, generated in windows of
+    `rows` tokens straight into a device tensor of the workload's dtype, so the
+    host never holds the whole fp32 copy."""
+    import torch
+    import synth
+    T = wl.T_total
+    shape = (T,) + synth._shape(wl, name, 1)[1:]
+    out = torch.empty(shape, dtype=torch_dtype(wl.dtype), device="cuda")
+    for t0 in range(0, T, rows):
+        t1 = min(T, t0 + rows)
+        x = torch.from_numpy(synth.token_rows(wl, name, t0, t1, set_index))
+        out[t0:t1].copy_(x.to(torch_dtype(wl.dtype)))
+    return out
