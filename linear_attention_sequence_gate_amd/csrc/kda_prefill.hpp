@@ -67,16 +67,16 @@ struct PhaseClock {
             last = t;
         }
     }
-    __device__ void save()
+    __device__ void save(int base = 0)
     {
-        if (on && blockIdx.x < 16384)
-            for (int i = 0; i < 12; ++i) kda_phase_cycles[blockIdx.x * 16 + i] = acc[i];
+        if (on && base + blockIdx.x < 16384)
+            for (int i = 0; i < 12; ++i) kda_phase_cycles[(base + blockIdx.x) * 16 + i] = acc[i];
     }
 };
 #else
 struct PhaseClock {
     __device__ void mark(int) {}
-    __device__ void save() {}
+    __device__ void save(int = 0) {}
 };
 #endif
 #define KDA_PHASE(i) pclk.mark(i)
@@ -448,11 +448,9 @@ struct BlockCfg {
     static constexpr int O_A = O_KH + 2 * TILE_H;                   // -beta_r A, natural columns
     static constexpr int O_P = O_A + TILE_S;                        // P, permuted columns
     static constexpr int O_D = O_P + (SUMMARY ? 0 : TILE_S);        // (I + A_aa)^{-1}, 2 blocks
-    static constexpr int O_DS = O_D + 2 * TILE_D;                   // inverse scratch, 4 blocks
-    static constexpr int O_VEC = O_DS + 4 * TILE_D;                 // fp32 channel vectors
+    static constexpr int O_VEC = O_D + 2 * TILE_D;                  // fp32 channel vectors
     static constexpr int O_B = O_VEC + 3 * DK * 4;                  // beta, 2 buffers
-    static constexpr int O_RUN = O_B + 2 * BC * 4;                  // run sums of g, wave-private
-    static constexpr int LDS = O_RUN + NPT * 8;
+    static constexpr int LDS = O_B + 2 * BC * 4;
     // v tile: 16-byte units
     static constexpr int EPU = 16 / ES;
     static constexpr int UPR_V = DV / EPU;
@@ -482,65 +480,68 @@ __device__ __forceinline__ void store4(typename DT::storage* p, const f32x4& v)
 }
 
 // (I + N)^{-1} for one 16x16 diagonal block of the strictly lower N, by one
-// full wave on the matrix cores.  N is nilpotent (N^16 = 0), so
-//     (I + N)^{-1} = (I - N)(I + N^2)(I + N^4)(I + N^8):
-// three squarings and three products of 16x16 tiles.  A 16x16 accumulator tile
-// is directly the B operand of the next 16x16x16 product; the A operand needs
-// rows, so each power is written once to LDS (wave-private scratch, read back
-// by the same wave: LDS operations of one wave complete in order).
-// sA holds -N (natural column order); the result goes to sD.
+// wave on the matrix cores, entirely in registers.  N is nilpotent (N^16 = 0):
+// with Q = -N,  (I + N)^{-1} = (I + Q)(I + Q^2)(I + Q^4)(I + Q^8).
+// A 16x16 accumulator tile of P serves directly as the B operand of P and as
+// the A operand of P^T; a row read and a column read of Q give both operands
+// of Q and of Q^T.  Each power needed later as a left operand is therefore
+// formed together with its transpose (Q^2 and (Q^2)^T, Q^4 and (Q^4)^T), and
+// nothing goes back through LDS.  sA holds Q = -N (natural column order); the
+// result goes to rows 16a.. of sD.
 template <typename C, typename O>
-__device__ __forceinline__ void diag_inverse(const typename O::T* sA, typename O::T* sD, typename O::T* scr,
-                                             int a, int lane)
+__device__ __forceinline__ void diag_inverse(const typename O::T* sA, typename O::T* sD, int a, int lane)
 {
     using OT = typename O::T;
     using Frag4 = typename O::Frag4;
     const int l16 = lane & 15, q4 = lane >> 4;
-    const OT* Qrows = sA + (a * 16) * C::ST + a * 16;  // -N
-    OT* n2 = scr + (2 * a) * 16 * C::SD;
-    OT* n4 = scr + (2 * a + 1) * 16 * C::SD;
-    auto rowfrag = [&](const OT* base, int ld) { return O::load4(base + l16 * ld + 4 * q4); };
-    auto put = [&](OT* base, const f32x4& t) {  // accumulator tile -> natural rows
+    const OT* Qb = sA + (a * 16) * C::ST + a * 16;
+    const Frag4 rQ = O::load4(Qb + l16 * C::ST + 4 * q4);  // A(Q) = B(Q^T)
+    f32x4 c;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) base[(4 * q4 + j) * C::SD + l16] = O::to_op(t[j]);
-    };
-    auto wave_sync = [] {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    };
-    // B operand of -N: column l16, rows 4q..4q+3
-    f32x4 qcol;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) qcol[j] = O::from_op(Qrows[(4 * q4 + j) * C::ST + l16]);
-    const Frag4 qa = rowfrag(Qrows, C::ST);
-    f32x4 t2 = {0.f, 0.f, 0.f, 0.f};
-    O::mma4(t2, qa, O::make4(qcol));  // N^2 = (-N)(-N)
-    put(n2, t2);
-    wave_sync();
-    f32x4 t4 = {0.f, 0.f, 0.f, 0.f};
-    const Frag4 n2a = rowfrag(n2, C::SD);
-    O::mma4(t4, n2a, O::make4(t2));  // N^4
-    put(n4, t4);
-    wave_sync();
-    f32x4 t8 = {0.f, 0.f, 0.f, 0.f};
-    const Frag4 n4a = rowfrag(n4, C::SD);
-    O::mma4(t8, n4a, O::make4(t4));  // N^8
-    // E1 = (I + N^4)(I + N^8) = I + N^4 + N^8 + N^4 N^8
-    f32x4 e = t4 + t8;
+    for (int j = 0; j < 4; ++j) c[j] = O::from_op(Qb[(4 * q4 + j) * C::ST + l16]);
+    const Frag4 cQ = O::make4(c);  // B(Q) = A(Q^T)
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    f32x4 q2 = z, q2t = z;
+    O::mma4(q2, rQ, cQ);   // Q^2       -> B(Q^2), A((Q^2)^T)
+    O::mma4(q2t, cQ, rQ);  // (Q^2)^T   -> B((Q^2)^T), A(Q^2)
+    const Frag4 f2 = O::make4(q2), f2t = O::make4(q2t);
+    f32x4 p4 = z, p4t = z;
+    O::mma4(p4, f2t, f2);   // Q^4
+    O::mma4(p4t, f2, f2t);  // (Q^4)^T
+    const Frag4 f4 = O::make4(p4), f4t = O::make4(p4t);
+    f32x4 q8 = z;
+    O::mma4(q8, f4t, f4);  // Q^8
+    // E1 = (I + Q^4)(I + Q^8) = I + Q^4 + Q^8 + Q^4 Q^8
+    f32x4 e = p4 + q8;
 #pragma unroll
     for (int j = 0; j < 4; ++j) e[j] += (4 * q4 + j == l16) ? 1.f : 0.f;
-    O::mma4(e, n4a, O::make4(t8));
-    // E2 = (I + N^2) E1
+    O::mma4(e, f4t, O::make4(q8));
+    // E2 = (I + Q^2) E1, D = (I + Q) E2
     f32x4 e2 = e;
-    O::mma4(e2, n2a, O::make4(e));
-    // D = (I - N) E2
+    O::mma4(e2, f2t, O::make4(e));
     f32x4 d = e2;
-    O::mma4(d, qa, O::make4(e2));
+    O::mma4(d, rQ, O::make4(e2));
 #pragma unroll
     for (int j = 0; j < 4; ++j) sD[(a * 16 + 4 * q4 + j) * C::SD + l16] = O::to_op(d[j]);
 }
 
+// The value held by lane `lane ^ dist` (dist a power of two): rows of 16 lanes
+// swap with v_permlane16_swap / v_permlane32_swap, half rows with a DPP
+// rotate, and smaller distances go through ds_bpermute.
+__device__ __forceinline__ float xor_lanes(float x, int dist, int lane)
+{
+    const unsigned u = __float_as_uint(x);
+    if (dist == 32) {
+        const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        return __uint_as_float(lane >= 32 ? r[0] : r[1]);
+    }
+    if (dist == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        return __uint_as_float((lane & 16) ? r[0] : r[1]);
+    }
+    if (dist == 8) return __int_as_float(__builtin_amdgcn_update_dpp(0, int(u), 0x128, 0xf, 0xf, false));  // row_ror:8
+    return __shfl_xor(x, dist);
+}
 
 // One block's raw inputs in a prep thread's registers: q, k, g of its token
 // run (two adjacent channels per token), its 16-byte units of v and, for the
@@ -628,38 +629,25 @@ __device__ __forceinline__ void prep_tiles(const PrepRegs<C, DT>& r, unsigned ch
         s1 += g1[i];
     }
     pclk.mark(7);
-    // running sum across the runs of this channel pair: each lane publishes its
-    // run sums, then reads all runs of its pair (wave-private LDS, in order)
-    {
-        f32x2* run = reinterpret_cast<f32x2*>(smem + C::O_RUN);
-        run[cpair * C::PARTS + part] = f32x2{s0, s1};
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    float G0 = 0.f, G1 = 0.f, R10 = 0.f, R11 = 0.f, GL0 = 0.f, GL1 = 0.f;  // G before the run, at token 15, at the end
-    {
-        constexpr int P15 = 16 / C::TPT - 1;  // run holding token 15
-        const f32x4* run4 = reinterpret_cast<const f32x4*>(smem + C::O_RUN) + cpair * (C::PARTS / 2);
+    // running sums across the runs of this channel pair (lanes cpl + CPW * part):
+    // an exchange butterfly over the part index.  At level d every lane adds its
+    // partner's block total; lanes in the upper half also add it to their
+    // prefix.  Partners add the same two numbers, so every lane of a pair ends
+    // with bit-identical totals.
+    float G0 = 0.f, G1 = 0.f, R10 = 0.f, R11 = 0.f, GL0 = s0, GL1 = s1;  // G before the run, at token 15, at the end
 #pragma unroll
-        for (int m = 0; m < C::PARTS / 2; ++m) {
-            const f32x4 w = run4[m];
-#pragma unroll
-            for (int hlf = 0; hlf < 2; ++hlf) {
-                const int pp = 2 * m + hlf;
-                const float x0 = w[2 * hlf], x1 = w[2 * hlf + 1];
-                if (pp < part) {
-                    G0 += x0;
-                    G1 += x1;
-                }
-                if (pp <= P15) {
-                    R10 += x0;
-                    R11 += x1;
-                }
-                GL0 += x0;
-                GL1 += x1;
-            }
+    for (int d = 1; d < C::PARTS; d <<= 1) {
+        const float p0 = xor_lanes(GL0, d * C::CPW, lane), p1 = xor_lanes(GL1, d * C::CPW, lane);
+        if (d == 16 / C::TPT) {  // parts 0 .. 16/TPT - 1 hold sub-tile 0
+            R10 = (part & d) ? p0 : GL0;
+            R11 = (part & d) ? p1 : GL1;
         }
+        if (part & d) {
+            G0 += p0;
+            G1 += p1;
+        }
+        GL0 += p0;
+        GL1 += p1;
     }
     const bool hi = tok0 >= 16;  // sub-tile of the run
     const float ra0 = hi ? R10 : 0.f, ra1 = hi ? R11 : 0.f;
@@ -763,7 +751,6 @@ __device__ __forceinline__ void prep_products(unsigned char* smem, int buf, int 
     OT* sA = reinterpret_cast<OT*>(smem + C::O_A);
     OT* sP = reinterpret_cast<OT*>(smem + C::O_P);
     OT* sD = reinterpret_cast<OT*>(smem + C::O_D);
-    OT* sDS = reinterpret_cast<OT*>(smem + C::O_DS);
     const float* sVec = reinterpret_cast<const float*>(smem + C::O_VEC);
     const float* sB = reinterpret_cast<const float*>(smem + C::O_B) + buf * BC;
     const int l16 = lane & 15, q4 = lane >> 4;
@@ -814,7 +801,7 @@ __device__ __forceinline__ void prep_products(unsigned char* smem, int buf, int 
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        diag_inverse<C, O>(sA, sD, sDS, a, lane);
+        diag_inverse<C, O>(sA, sD, a, lane);
     }
 }
 
@@ -910,7 +897,7 @@ prefill_block_kernel(PrefillDev p)
             __syncthreads();
             KDA_PHASE(3);
         }
-        pclk.save();
+        pclk.save(SUMMARY ? 8192 : 0);
         return;
     }
 
@@ -1053,7 +1040,7 @@ prefill_block_kernel(PrefillDev p)
         KDA_PHASE(3);
     }
 
-    pclk.save();
+    pclk.save(SUMMARY ? 8192 : 0);
     // ---- write the segment result
     float* dst = nullptr;
     int ld = DV;
@@ -1112,9 +1099,21 @@ __global__ void __launch_bounds__(256) scan_kernel(PrefillDev p)
     float* sM = reinterpret_cast<float*>(smem);  // [DK][SM]: M_s rows
     float* sT = sM + DK * SC::SM;                // [32][SM]: S_in slice, transposed (column j, row k)
     const int H = p.H;
-    const int jb = blockIdx.x % NB;
-    const int h = (blockIdx.x / NB) % H;
-    const int n = blockIdx.x / (NB * H);
+    // Workgroups go to the 8 XCDs round-robin by index; the NB column slices of
+    // one (sequence, head) read the same M_s, so they are given indices that
+    // share an XCD (and its L2): slices of unit u sit at u%8 + 8*(NB*(u/8) + jb).
+    const int nunits = p.N * H;
+    const int bx = blockIdx.x;
+    int unit, jb;
+    if ((nunits & 7) == 0) {
+        jb = (bx >> 3) % NB;
+        unit = (bx & 7) + 8 * ((bx >> 3) / NB);
+    } else {
+        jb = bx % NB;
+        unit = bx / NB;
+    }
+    const int h = unit % H;
+    const int n = unit / H;
     const int32_t* seg_off = p.tab + (p.N + 1);
     const int32_t* p1_off = p.tab + 2 * (p.N + 1);
     const int nseg = seg_off[n + 1] - seg_off[n];
@@ -1122,6 +1121,11 @@ __global__ void __launch_bounds__(256) scan_kernel(PrefillDev p)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, q4 = lane >> 4;
     const int col0 = jb * SCAN_COLS;
+    PhaseClock pclk;
+#ifdef KDA_PHASE_TIMING
+    pclk.on = tid == 0;
+    pclk.last = clock64();
+#endif
     auto ms_of = [&](int st) { return p.ms + (int64_t(p1_off[n] + st) * H + h) * DK * (DK + DV); };
 
     for (int e = tid; e < SCAN_COLS * DK; e += 256) {
@@ -1151,8 +1155,10 @@ __global__ void __launch_bounds__(256) scan_kernel(PrefillDev p)
         }
     };
     load_step(0);
+    KDA_PHASE(0);
     for (int s = 0; s + 1 < nseg; ++s) {
         __syncthreads();  // sM free
+        KDA_PHASE(1);
 #pragma unroll
         for (int i = 0; i < SC::UPT; ++i) {
             const int u = tid + i * 256;
@@ -1165,7 +1171,9 @@ __global__ void __launch_bounds__(256) scan_kernel(PrefillDev p)
 #pragma unroll
             for (int ct = 0; ct < 2; ++ct) acc[i][ct] = nxt[i][ct];
         __syncthreads();
+        KDA_PHASE(2);
         if (s + 2 < nseg) load_step(s + 1);  // in flight during the products
+        KDA_PHASE(3);
 #pragma unroll
         for (int kb = 0; kb < DK / 32; ++kb) {
             bf16x8 bh[2], bl[2];
@@ -1194,7 +1202,9 @@ __global__ void __launch_bounds__(256) scan_kernel(PrefillDev p)
                 }
             }
         }
+        KDA_PHASE(4);
         __syncthreads();  // every wave is done reading sT
+        KDA_PHASE(5);
         float* out = p.sin + (int64_t(seg_off[n] + s + 1) * H + h) * DK * DV;
 #pragma unroll
         for (int i = 0; i < SC::RTW; ++i) {
@@ -1209,7 +1219,9 @@ __global__ void __launch_bounds__(256) scan_kernel(PrefillDev p)
                 }
             }
         }
+        KDA_PHASE(6);
     }
+    pclk.save(12288);
 }
 
 // ------------------------------------------------------------------ launch
