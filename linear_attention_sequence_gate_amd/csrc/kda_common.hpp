@@ -72,19 +72,27 @@ __device__ __forceinline__ void load8(const typename DT::storage* p, float (&x)[
         }
     }
 }
-template <typename DT>
+// Stores are streaming (non-temporal) when NT: the data is not kept in the
+// caches on its way to HBM.
+template <typename T, bool NT>
+__device__ __forceinline__ void store_vec(T* p, const T& v)
+{
+    if constexpr (NT) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
+template <typename DT, bool NT = false>
 __device__ __forceinline__ void store8(typename DT::storage* p, const float (&x)[8])
 {
     if constexpr (DT::is_bf16) {
         u32x4 w;
 #pragma unroll
         for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
-        *reinterpret_cast<u32x4*>(p) = w;
+        store_vec<u32x4, NT>(reinterpret_cast<u32x4*>(p), w);
     } else {
         f32x4 a = {x[0], x[1], x[2], x[3]};
         f32x4 b = {x[4], x[5], x[6], x[7]};
-        *reinterpret_cast<f32x4*>(p) = a;
-        *reinterpret_cast<f32x4*>(p + 4) = b;
+        store_vec<f32x4, NT>(reinterpret_cast<f32x4*>(p), a);
+        store_vec<f32x4, NT>(reinterpret_cast<f32x4*>(p + 4), b);
     }
 }
 

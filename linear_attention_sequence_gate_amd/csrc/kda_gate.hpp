@@ -8,7 +8,8 @@
 // g may alias z (in place); each element is read before it is written by the
 // same thread.  HBM-bound streaming kernel: 8 elements per thread per iteration with 16-byte
 // (bf16) or 2x16-byte (fp32) accesses, grid-stride so one launch of a few
-// thousand workgroups covers any size.  Computed in fp32, rounded once.
+// thousand workgroups covers any size.  Computed in fp32, rounded once; g is
+// written with streaming (non-temporal) stores.
 #pragma once
 
 #include "kda_common.hpp"
@@ -39,7 +40,7 @@ __global__ void __launch_bounds__(256) gate_kernel_vec8(const typename DT::stora
         const float s = __expf(A[h]);
 #pragma unroll
         for (int i = 0; i < 8; ++i) x[i] = gate_value(x[i], s, g_min);
-        store8<DT>(g + e0, x);
+        store8<DT, true>(g + e0, x);
     }
 }
 
