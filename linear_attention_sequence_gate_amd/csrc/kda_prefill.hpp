@@ -450,7 +450,12 @@ struct BlockCfg {
     static constexpr int O_D = O_P + (SUMMARY ? 0 : TILE_S);        // (I + A_aa)^{-1}, 2 blocks
     static constexpr int O_VEC = O_D + 2 * TILE_D;                  // fp32 channel vectors
     static constexpr int O_B = O_VEC + 3 * DK * 4;                  // beta, 2 buffers
-    static constexpr int LDS = O_B + 2 * BC * 4;
+    static constexpr int LDS_TILES = O_B + 2 * BC * 4;
+    // summary pass, after the last block: each M-column wave stages its 32
+    // columns (fp32, rows padded to 36) to write M split and permuted
+    static constexpr int MSTAGE = 36;
+    static constexpr int LDS_MSTAGE = SUMMARY ? (DK / 32) * DK * MSTAGE * 4 : 0;
+    static constexpr int LDS = LDS_TILES > LDS_MSTAGE ? LDS_TILES : LDS_MSTAGE;
     // v tile: 16-byte units
     static constexpr int EPU = 16 / ES;
     static constexpr int UPR_V = DV / EPU;
@@ -1041,23 +1046,70 @@ prefill_block_kernel(PrefillDev p)
     }
 
     pclk.save(SUMMARY ? 8192 : 0);
-    // ---- write the segment result
-    float* dst = nullptr;
-    int ld = DV;
+    // ---- write the segment result.  Summary pass: S~ as fp32 rows [d_k][d_v],
+    // then M as two bf16 tiles (hi = bf16(M), lo = bf16(M - hi)) [d_k][d_k] with
+    // the permuted column order of the operand tiles, ready as A operands of the
+    // scan's split-precision products.
     if (SUMMARY) {
-        dst = p.ms + (int64_t(item) * H + h) * DK * (DK + DV);  // [S~ | M], rows of DK + DV
-        ld = DK + DV;
+        float* base = p.ms + (int64_t(item) * H + h) * DK * (DK + DV);
+        if (!mcols) {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        base[(rt * 16 + 4 * q4 + j) * DV + colbase + ct * 16 + l16] = S[rt][ct][j];
+        } else {
+            // every other wave is past its last LDS access (final barrier above)
+            const int mw = (colbase - DV) / 32;  // this wave's 32-column block of M
+            float* stg = reinterpret_cast<float*>(smem) + mw * DK * C::MSTAGE;
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) stg[(rt * 16 + 4 * q4 + j) * C::MSTAGE + ct * 16 + l16] = S[rt][ct][j];
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            uint16_t* mhi = reinterpret_cast<uint16_t*>(base + DK * DV);
+            uint16_t* mlo = mhi + DK * DK;
+            for (int r = lane; r < DK; r += 64) {
+                float x[32];
+#pragma unroll
+                for (int m = 0; m < 8; ++m) {
+                    const f32x4 w = *reinterpret_cast<const f32x4*>(stg + r * C::MSTAGE + 4 * m);
+                    x[4 * m] = w[0];
+                    x[4 * m + 1] = w[1];
+                    x[4 * m + 2] = w[2];
+                    x[4 * m + 3] = w[3];
+                }
+                // position p of the block holds column 16*((p>>2)&1) + 4*(p>>3) + (p&3)
+                u32x4 hv[4], lv[4];
+#pragma unroll
+                for (int pp = 0; pp < 32; pp += 2) {
+                    const int c0 = 16 * ((pp >> 2) & 1) + 4 * (pp >> 3) + (pp & 3);
+                    const uint32_t hw = pack_bf16x2(x[c0], x[c0 + 1]);
+                    hv[pp / 8][(pp / 2) % 4] = hw;
+                    lv[pp / 8][(pp / 2) % 4] = pack_bf16x2(x[c0] - bf16_lo(hw), x[c0 + 1] - bf16_hi(hw));
+                }
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    *reinterpret_cast<u32x4*>(mhi + r * DK + mw * 32 + 8 * m) = hv[m];
+                    *reinterpret_cast<u32x4*>(mlo + r * DK + mw * 32 + 8 * m) = lv[m];
+                }
+            }
+        }
     } else if (last_seg && p.fin) {
-        dst = p.fin + (int64_t(n) * H + h) * DK * DV;
-    }
-    if (dst) {
+        float* dst = p.fin + (int64_t(n) * H + h) * DK * DV;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    dst[(rt * 16 + 4 * q4 + j) * ld + colbase + ct * 16 + l16] = S[rt][ct][j];
+                    dst[(rt * 16 + 4 * q4 + j) * DV + colbase + ct * 16 + l16] = S[rt][ct][j];
     }
 }
 
@@ -1066,28 +1118,26 @@ prefill_block_kernel(PrefillDev p)
 //     S_in(s+1) = M_s S_in(s) + S~_s
 // over the sequence's segments, on the matrix cores with fp32-level accuracy:
 // each fp32 operand x is split as hi = bf16(x), lo = bf16(x - hi) and the
-// product accumulates hi*hi + hi*lo + lo*hi in fp32.  Per step the workgroup
-// stages M_s in LDS (next step's M prefetched into registers during this
-// step's products) and keeps its S_in slice in LDS, transposed, as the other
-// operand.  Wave w owns state row tiles w, w+4, ... and both column tiles.
+// product accumulates hi*hi + hi*lo + lo*hi in fp32.  The summary pass stores
+// M_s already split (hi and lo bf16 tiles, permuted columns).  Wave w owns
+// state row tiles w, w+4, ...: it needs only those rows of M_s, so it loads
+// their fragments straight from global memory into registers, one step ahead.
+// The S_in slice, which every wave reads whole, sits in LDS transposed and
+// split the same way, written once by the wave that computed it.
 constexpr int SCAN_COLS = 32;
 template <int DK, int DV>
 struct ScanCfg {
-    static constexpr int SM = DK + 4;                 // fp32 row stride of M and S_in^T in LDS
-    static constexpr int UNITS = DK * (DK / 4);       // 16-byte units of M
-    static constexpr int UPT = (UNITS + 255) / 256;
-    static constexpr int RTW = (DK / 16 + 3) / 4;     // row tiles per wave
-    static constexpr int LDS = (DK + SCAN_COLS) * SM * 4;
+    static constexpr int SB = DK + 8;              // bf16 row stride of the S_in^T tiles in LDS
+    static constexpr int RTW = (DK / 16 + 3) / 4;  // row tiles per wave
+    static constexpr int LDS = 2 * SCAN_COLS * SB * 2;
 };
 
-__device__ __forceinline__ void split_bf16(const float (&x)[8], bf16x8& hi, bf16x8& lo)
+// four consecutive fp32 values -> bf16 hi and lo parts (8 bytes each)
+__device__ __forceinline__ void split4(const f32x4& x, u32x2& hi, u32x2& lo)
 {
-    float h[8], l[8];
-    hi = Op<BF16>::make(x);
-    Op<BF16>::unpack(hi, h);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) l[e] = x[e] - h[e];
-    lo = Op<BF16>::make(l);
+    hi = u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+    lo = u32x2{pack_bf16x2(x[0] - bf16_lo(hi[0]), x[1] - bf16_hi(hi[0])),
+               pack_bf16x2(x[2] - bf16_lo(hi[1]), x[3] - bf16_hi(hi[1]))};
 }
 
 template <int DK, int DV>
@@ -1095,9 +1145,11 @@ __global__ void __launch_bounds__(256) scan_kernel(PrefillDev p)
 {
     using SC = ScanCfg<DK, DV>;
     constexpr int NB = DV / SCAN_COLS;
+    constexpr int KB = DK / 32;
+    constexpr int RTW = SC::RTW;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    float* sM = reinterpret_cast<float*>(smem);  // [DK][SM]: M_s rows
-    float* sT = sM + DK * SC::SM;                // [32][SM]: S_in slice, transposed (column j, row k)
+    uint16_t* sTh = reinterpret_cast<uint16_t*>(smem);  // [32][SB]: S_in slice^T, hi part, permuted rows
+    uint16_t* sTl = sTh + SCAN_COLS * SC::SB;           // lo part
     const int H = p.H;
     // Workgroups go to the 8 XCDs round-robin by index; the NB column slices of
     // one (sequence, head) read the same M_s, so they are given indices that
@@ -1128,98 +1180,106 @@ __global__ void __launch_bounds__(256) scan_kernel(PrefillDev p)
 #endif
     auto ms_of = [&](int st) { return p.ms + (int64_t(p1_off[n] + st) * H + h) * DK * (DK + DV); };
 
-    for (int e = tid; e < SCAN_COLS * DK; e += 256) {
-        const int j = e / DK, k = e % DK;
-        sT[j * SC::SM + k] = p.init ? p.init[(int64_t(n) * H + h) * DK * DV + k * DV + col0 + j] : 0.f;
+    // S_in(0) slice: column j of the slice is row j of the tiles; state row k sits at pcol(k)
+    for (int e = tid; e < SCAN_COLS * DK / 4; e += 256) {
+        const int j = e / (DK / 4), k = (e % (DK / 4)) * 4;
+        f32x4 x = {0.f, 0.f, 0.f, 0.f};
+        if (p.init) {
+            const float* src = p.init + (int64_t(n) * H + h) * DK * DV + col0 + j;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) x[m] = src[(k + m) * DV];
+        }
+        u32x2 hi, lo;
+        split4(x, hi, lo);
+        *reinterpret_cast<u32x2*>(sTh + j * SC::SB + pcol(k)) = hi;
+        *reinterpret_cast<u32x2*>(sTl + j * SC::SB + pcol(k)) = lo;
     }
-    f32x4 pre[SC::UPT];
-    f32x4 nxt[SC::RTW][2];
-    // M_st (columns DV .. DV+DK-1 of each row) and this wave's S~_st tiles
-    // (columns 0 .. DV-1) into registers; consumed one step later.
+    // this wave's rows of M_st (A operands: hi and lo fragments) and of S~_st
+    // (accumulator layout)
+    bf16x8 mh[RTW][KB], ml[RTW][KB];
+    f32x4 stl[RTW][2];
     auto load_step = [&](int st) {
         const float* base = ms_of(st);
+        const uint16_t* mhi = reinterpret_cast<const uint16_t*>(base + DK * DV);
+        const uint16_t* mlo = mhi + DK * DK;
 #pragma unroll
-        for (int i = 0; i < SC::UPT; ++i) {
-            const int u = tid + i * 256;
-            if (SC::UNITS % 256 == 0 || u < SC::UNITS)
-                pre[i] = *reinterpret_cast<const f32x4*>(base + DV + (u / (DK / 4)) * (DK + DV) + (u % (DK / 4)) * 4);
-        }
-#pragma unroll
-        for (int i = 0; i < SC::RTW; ++i) {
+        for (int i = 0; i < RTW; ++i) {
             const int rt = wave + 4 * i;
+            if (rt < DK / 16) {
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
+                for (int kb = 0; kb < KB; ++kb) {
+                    mh[i][kb] = Op<BF16>::load(mhi + (rt * 16 + l16) * DK + kb * 32 + 8 * q4);
+                    ml[i][kb] = Op<BF16>::load(mlo + (rt * 16 + l16) * DK + kb * 32 + 8 * q4);
+                }
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    nxt[i][ct][j] = rt < DK / 16 ? base[(rt * 16 + 4 * q4 + j) * (DK + DV) + col0 + ct * 16 + l16] : 0.f;
+                for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        stl[i][ct][j] = base[(rt * 16 + 4 * q4 + j) * DV + col0 + ct * 16 + l16];
+            }
         }
     };
     load_step(0);
+    __syncthreads();
     KDA_PHASE(0);
     for (int s = 0; s + 1 < nseg; ++s) {
-        __syncthreads();  // sM free
+        // take this step's fragments, then start loading the next step's into the same registers
+        bf16x8 ah[RTW][KB], al[RTW][KB];
+        f32x4 acc[RTW][2];
+#pragma unroll
+        for (int i = 0; i < RTW; ++i) {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                ah[i][kb] = mh[i][kb];
+                al[i][kb] = ml[i][kb];
+            }
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) acc[i][ct] = stl[i][ct];
+        }
+        if (s + 2 < nseg) load_step(s + 1);  // in flight during the products
         KDA_PHASE(1);
 #pragma unroll
-        for (int i = 0; i < SC::UPT; ++i) {
-            const int u = tid + i * 256;
-            if (SC::UNITS % 256 == 0 || u < SC::UNITS)
-                *reinterpret_cast<f32x4*>(sM + (u / (DK / 4)) * SC::SM + (u % (DK / 4)) * 4) = pre[i];
-        }
-        f32x4 acc[SC::RTW][2];
-#pragma unroll
-        for (int i = 0; i < SC::RTW; ++i)
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct) acc[i][ct] = nxt[i][ct];
-        __syncthreads();
-        KDA_PHASE(2);
-        if (s + 2 < nseg) load_step(s + 1);  // in flight during the products
-        KDA_PHASE(3);
-#pragma unroll
-        for (int kb = 0; kb < DK / 32; ++kb) {
+        for (int kb = 0; kb < KB; ++kb) {
             bf16x8 bh[2], bl[2];
 #pragma unroll
             for (int ct = 0; ct < 2; ++ct) {
-                const float* b = sT + (ct * 16 + l16) * SC::SM + kb * 32 + 4 * q4;
-                const f32x4 b0 = *reinterpret_cast<const f32x4*>(b), b1 = *reinterpret_cast<const f32x4*>(b + 16);
-                const float x[8] = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
-                split_bf16(x, bh[ct], bl[ct]);
+                bh[ct] = Op<BF16>::load(sTh + (ct * 16 + l16) * SC::SB + kb * 32 + 8 * q4);
+                bl[ct] = Op<BF16>::load(sTl + (ct * 16 + l16) * SC::SB + kb * 32 + 8 * q4);
             }
 #pragma unroll
-            for (int i = 0; i < SC::RTW; ++i) {
-                const int rt = wave + 4 * i;
-                if (rt < DK / 16) {
-                    const float* a = sM + (rt * 16 + l16) * SC::SM + kb * 32 + 4 * q4;
-                    const f32x4 a0 = *reinterpret_cast<const f32x4*>(a), a1 = *reinterpret_cast<const f32x4*>(a + 16);
-                    const float x[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-                    bf16x8 ah, al;
-                    split_bf16(x, ah, al);
+            for (int i = 0; i < RTW; ++i) {
+                if (wave + 4 * i < DK / 16) {
 #pragma unroll
                     for (int ct = 0; ct < 2; ++ct) {
-                        Op<BF16>::mma(acc[i][ct], ah, bh[ct]);
-                        Op<BF16>::mma(acc[i][ct], ah, bl[ct]);
-                        Op<BF16>::mma(acc[i][ct], al, bh[ct]);
+                        Op<BF16>::mma(acc[i][ct], ah[i][kb], bh[ct]);
+                        Op<BF16>::mma(acc[i][ct], ah[i][kb], bl[ct]);
+                        Op<BF16>::mma(acc[i][ct], al[i][kb], bh[ct]);
                     }
                 }
             }
         }
-        KDA_PHASE(4);
-        __syncthreads();  // every wave is done reading sT
-        KDA_PHASE(5);
+        KDA_PHASE(2);
+        __syncthreads();  // every wave is done reading the S_in tiles
+        KDA_PHASE(3);
         float* out = p.sin + (int64_t(seg_off[n] + s + 1) * H + h) * DK * DV;
 #pragma unroll
-        for (int i = 0; i < SC::RTW; ++i) {
+        for (int i = 0; i < RTW; ++i) {
             const int rt = wave + 4 * i;
             if (rt < DK / 16) {
 #pragma unroll
                 for (int ct = 0; ct < 2; ++ct) {
                     const int j = ct * 16 + l16;
-                    *reinterpret_cast<f32x4*>(sT + j * SC::SM + rt * 16 + 4 * q4) = acc[i][ct];
+                    u32x2 hi, lo;
+                    split4(acc[i][ct], hi, lo);  // state rows rt*16 + 4q .. +3: contiguous under pcol
+                    *reinterpret_cast<u32x2*>(sTh + j * SC::SB + pcol(rt * 16 + 4 * q4)) = hi;
+                    *reinterpret_cast<u32x2*>(sTl + j * SC::SB + pcol(rt * 16 + 4 * q4)) = lo;
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj) out[(rt * 16 + 4 * q4 + jj) * DV + col0 + j] = acc[i][ct][jj];
                 }
             }
         }
-        KDA_PHASE(6);
+        __syncthreads();  // the new S_in slice is complete
+        KDA_PHASE(4);
     }
     pclk.save(12288);
 }
