@@ -398,7 +398,7 @@ __device__ __forceinline__ typename Op<DT>::Frag acc_frag(const f32x4& lo, const
 // ------------------------------------------------------------ block kernel
 // The recurrence advances in blocks of BC = 32 tokens (two 16-token sub-tiles).
 // Waves have two roles inside a workgroup:
-//   chain waves (NCW, 32 state columns each) hold their columns of the state
+//   chain waves (NCW, 32 or 64 state columns each) hold their columns of the state
 //   in registers for the whole segment and run X, U, O and the state update;
 //   prep waves (4) build every state-independent operand of the NEXT block:
 //   the decayed q/k tiles, the channel vectors, the products A and P and the
@@ -416,7 +416,11 @@ template <typename DT, int DKV, int DVV, bool SUMMARY>
 struct BlockCfg {
     static constexpr int DK = DKV, DV = DVV;
     static constexpr int NCOL = SUMMARY ? DV + DK : DV;  // extended state columns
-    static constexpr int NCW = NCOL / 32;                 // chain waves
+    // state columns per chain wave (64 was measured slower for the summary
+    // pass: the chain's vector work, not its LDS reads, competes with the prep)
+    static constexpr int CW = 32;
+    static constexpr int NCT = CW / 16;                   // 16-wide column tiles per chain wave
+    static constexpr int NCW = NCOL / CW;                 // chain waves
     // prep waves: two per SIMD for the output pass of wide heads (their
     // vector work is the longer side of the pipeline), one otherwise
     static constexpr int NPW = (!SUMMARY && DKV >= 64) ? 8 : 4;
@@ -906,11 +910,12 @@ prefill_block_kernel(PrefillDev p)
         return;
     }
 
-    // ================= chain waves: 32 columns of the extended state each, in registers
+    // ================= chain waves: CW columns of the extended state each, in registers
     constexpr int RT = DK / 16;  // state row tiles
-    const int colbase = 32 * wave;
+    constexpr int NCT = C::NCT;
+    const int colbase = C::CW * wave;
     const bool mcols = SUMMARY && colbase >= DV;
-    f32x4 S[RT][2];
+    f32x4 S[RT][NCT];
     {
         const float* src = nullptr;
         if (!SUMMARY) {
@@ -923,7 +928,7 @@ prefill_block_kernel(PrefillDev p)
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
+            for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int row = rt * 16 + 4 * q4 + j;
@@ -941,38 +946,38 @@ prefill_block_kernel(PrefillDev p)
         const int len = blen(bi);
         const int buf = int(bi & 1);
         // ---- alpha: X = V - (K . e^G) S, rows = the block's 32 tokens
-        f32x4 Xt[2][2];
+        f32x4 Xt[2][NCT];
         {
-            Frag Sb[DK / 32][2];
-#pragma unroll
-            for (int kb = 0; kb < DK / 32; ++kb)
-#pragma unroll
-                for (int ct = 0; ct < 2; ++ct) Sb[kb][ct] = acc_frag<DT>(S[2 * kb][ct], S[2 * kb + 1][ct]);
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct) Xt[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int ct = 0; ct < NCT; ++ct) Xt[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
             if (!mcols) {
-                // V I with exact identity fragments picking column ct*16 + l16 of the wave's 32
+                // V I with exact identity fragments picking column (ct%2)*16 + l16 of
+                // the 32-column block ct/2
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct) {
+                for (int ct = 0; ct < NCT; ++ct) {
                     float x[8];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) x[e] = (kperm(q4, e) == ct * 16 + l16) ? 1.f : 0.f;
+                    for (int e = 0; e < 8; ++e) x[e] = (kperm(q4, e) == (ct % 2) * 16 + l16) ? 1.f : 0.f;
                     const Frag iden = O::make(x);
 #pragma unroll
                     for (int rt = 0; rt < 2; ++rt)
-                        O::mma(Xt[rt][ct], O::load(sV + (rt * 16 + l16) * C::SV + colbase + 8 * q4), iden);
+                        O::mma(Xt[rt][ct], O::load(sV + (rt * 16 + l16) * C::SV + colbase + 32 * (ct / 2) + 8 * q4),
+                               iden);
                 }
             }
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
+            for (int kb = 0; kb < DK / 32; ++kb) {
+                const Frag a0 = O::load(sKG + l16 * C::SK + kb * 32 + 8 * q4);
+                const Frag a1 = O::load(sKG + (16 + l16) * C::SK + kb * 32 + 8 * q4);
 #pragma unroll
-                for (int kb = 0; kb < DK / 32; ++kb) {
-                    const Frag af = O::load(sKG + (rt * 16 + l16) * C::SK + kb * 32 + 8 * q4);
-#pragma unroll
-                    for (int ct = 0; ct < 2; ++ct) O::mma(Xt[rt][ct], af, Sb[kb][ct]);
+                for (int ct = 0; ct < NCT; ++ct) {
+                    const Frag sb = acc_frag<DT>(S[2 * kb][ct], S[2 * kb + 1][ct]);
+                    O::mma(Xt[0][ct], a0, sb);
+                    O::mma(Xt[1][ct], a1, sb);
                 }
+            }
         }
         KDA_PHASE(0);
         __syncthreads();
@@ -980,7 +985,7 @@ prefill_block_kernel(PrefillDev p)
         // ---- beta: U = (I + A)^{-1} Diag(beta) X by block substitution:
         //   U_0 = D_0 beta_0 X_0,  U_1 = D_1 (beta_1 X_1 - A_10 U_0)
         const float* sBb = reinterpret_cast<const float*>(smem + C::O_B) + buf * BC;
-        f32x4 U0[2], U1[2];
+        f32x4 U0[NCT], U1[NCT];
         {
             const f32x4 bv0 = *reinterpret_cast<const f32x4*>(sBb + 4 * q4);
             const f32x4 bv1 = *reinterpret_cast<const f32x4*>(sBb + 16 + 4 * q4);
@@ -988,7 +993,7 @@ prefill_block_kernel(PrefillDev p)
             const Frag4 d1 = O::load4(sD + (16 + l16) * C::SD + 4 * q4);
             const Frag4 a10 = O::load4(sA + (16 + l16) * C::ST + 4 * q4);
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
+            for (int ct = 0; ct < NCT; ++ct) {
                 U0[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
                 O::mma4(U0[ct], d0, O::make4(bv0 * Xt[0][ct]));
                 f32x4 R = bv1 * Xt[1][ct];
@@ -997,9 +1002,9 @@ prefill_block_kernel(PrefillDev p)
                 O::mma4(U1[ct], d1, O::make4(R));
             }
         }
-        Frag Ub[2];
+        Frag Ub[NCT];
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) Ub[ct] = acc_frag<DT>(U0[ct], U1[ct]);
+        for (int ct = 0; ct < NCT; ++ct) Ub[ct] = acc_frag<DT>(U0[ct], U1[ct]);
         KDA_PHASE(5);
         if (!SUMMARY) {
             // O^T = S^T (Q . e^G)^T + U^T P^T: each lane ends up with four
@@ -1007,21 +1012,23 @@ prefill_block_kernel(PrefillDev p)
             const OT* sQG = reinterpret_cast<const OT*>(smem + C::O_QG + buf * C::TILE_K);
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt) {
-                f32x4 Ot[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+                f32x4 Ot[NCT];
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) Ot[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kb = 0; kb < DK / 32; ++kb) {
                     const Frag bf = O::load(sQG + (rt * 16 + l16) * C::SK + kb * 32 + 8 * q4);
 #pragma unroll
-                    for (int ct = 0; ct < 2; ++ct)
+                    for (int ct = 0; ct < NCT; ++ct)
                         O::mma(Ot[ct], acc_frag<DT>(S[2 * kb][ct], S[2 * kb + 1][ct]), bf);
                 }
                 const Frag pf = O::load(sP + (rt * 16 + l16) * C::ST + 8 * q4);
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct) O::mma(Ot[ct], Ub[ct], pf);
+                for (int ct = 0; ct < NCT; ++ct) O::mma(Ot[ct], Ub[ct], pf);
                 const int row = rt * 16 + l16;
                 if (row < len) {
 #pragma unroll
-                    for (int ct = 0; ct < 2; ++ct)
+                    for (int ct = 0; ct < NCT; ++ct)
                         store4<DT>(go + ((b0 + row) * H + h) * DV + colbase + ct * 16 + 4 * q4, Ot[ct]);
                 }
             }
@@ -1035,7 +1042,7 @@ prefill_block_kernel(PrefillDev p)
             const f32x4 gc = *reinterpret_cast<const f32x4*>(gcv + pcol(rt * 16 + 4 * q4));
             const Frag kf = O::load(sKH + (rt * 16 + l16) * C::ST + 8 * q4);
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
+            for (int ct = 0; ct < NCT; ++ct) {
                 S[rt][ct] *= gc;
                 O::mma(S[rt][ct], kf, Ub[ct]);
             }
@@ -1056,48 +1063,52 @@ prefill_block_kernel(PrefillDev p)
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct)
+                for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
                         base[(rt * 16 + 4 * q4 + j) * DV + colbase + ct * 16 + l16] = S[rt][ct][j];
         } else {
             // every other wave is past its last LDS access (final barrier above)
-            const int mw = (colbase - DV) / 32;  // this wave's 32-column block of M
-            float* stg = reinterpret_cast<float*>(smem) + mw * DK * C::MSTAGE;
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-                for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) stg[(rt * 16 + 4 * q4 + j) * C::MSTAGE + ct * 16 + l16] = S[rt][ct][j];
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             uint16_t* mhi = reinterpret_cast<uint16_t*>(base + DK * DV);
             uint16_t* mlo = mhi + DK * DK;
-            for (int r = lane; r < DK; r += 64) {
-                float x[32];
 #pragma unroll
-                for (int m = 0; m < 8; ++m) {
-                    const f32x4 w = *reinterpret_cast<const f32x4*>(stg + r * C::MSTAGE + 4 * m);
-                    x[4 * m] = w[0];
-                    x[4 * m + 1] = w[1];
-                    x[4 * m + 2] = w[2];
-                    x[4 * m + 3] = w[3];
-                }
-                // position p of the block holds column 16*((p>>2)&1) + 4*(p>>3) + (p&3)
-                u32x4 hv[4], lv[4];
+            for (int cb = 0; cb < NCT / 2; ++cb) {
+                const int mw = (colbase - DV) / 32 + cb;  // a 32-column block of M
+                float* stg = reinterpret_cast<float*>(smem) + mw * DK * C::MSTAGE;
 #pragma unroll
-                for (int pp = 0; pp < 32; pp += 2) {
-                    const int c0 = 16 * ((pp >> 2) & 1) + 4 * (pp >> 3) + (pp & 3);
-                    const uint32_t hw = pack_bf16x2(x[c0], x[c0 + 1]);
-                    hv[pp / 8][(pp / 2) % 4] = hw;
-                    lv[pp / 8][(pp / 2) % 4] = pack_bf16x2(x[c0] - bf16_lo(hw), x[c0 + 1] - bf16_hi(hw));
-                }
+                for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    *reinterpret_cast<u32x4*>(mhi + r * DK + mw * 32 + 8 * m) = hv[m];
-                    *reinterpret_cast<u32x4*>(mlo + r * DK + mw * 32 + 8 * m) = lv[m];
+                    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            stg[(rt * 16 + 4 * q4 + j) * C::MSTAGE + ct * 16 + l16] = S[rt][2 * cb + ct][j];
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                for (int r = lane; r < DK; r += 64) {
+                    float x[32];
+#pragma unroll
+                    for (int m = 0; m < 8; ++m) {
+                        const f32x4 w = *reinterpret_cast<const f32x4*>(stg + r * C::MSTAGE + 4 * m);
+                        x[4 * m] = w[0];
+                        x[4 * m + 1] = w[1];
+                        x[4 * m + 2] = w[2];
+                        x[4 * m + 3] = w[3];
+                    }
+                    // position p of the block holds column 16*((p>>2)&1) + 4*(p>>3) + (p&3)
+                    u32x4 hv[4], lv[4];
+#pragma unroll
+                    for (int pp = 0; pp < 32; pp += 2) {
+                        const int c0 = 16 * ((pp >> 2) & 1) + 4 * (pp >> 3) + (pp & 3);
+                        const uint32_t hw = pack_bf16x2(x[c0], x[c0 + 1]);
+                        hv[pp / 8][(pp / 2) % 4] = hw;
+                        lv[pp / 8][(pp / 2) % 4] = pack_bf16x2(x[c0] - bf16_lo(hw), x[c0 + 1] - bf16_hi(hw));
+                    }
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        *reinterpret_cast<u32x4*>(mhi + r * DK + mw * 32 + 8 * m) = hv[m];
+                        *reinterpret_cast<u32x4*>(mlo + r * DK + mw * 32 + 8 * m) = lv[m];
+                    }
                 }
             }
         }
@@ -1106,7 +1117,7 @@ prefill_block_kernel(PrefillDev p)
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
+            for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     dst[(rt * 16 + 4 * q4 + j) * DV + colbase + ct * 16 + l16] = S[rt][ct][j];
