@@ -72,6 +72,15 @@ def decode_algo(B: int, H: int, dk: int, dv: int):
     return nbytes, flops
 
 
+def spec_algo(B: int, K: int, H: int, dk: int, dv: int, commit: bool):
+    """verify: state read once, K draft tokens in, K outputs out; commit (all K
+    accepted): state read and written once, K tokens in (no q, no output)."""
+    bh = B * H
+    state = bh * dk * dv * 4 * (2 if commit else 1)
+    tok = bh * K * ((2 * dk + dv + 1) * 2 if commit else (3 * dk + dv + 1) * 2 + dv * 2)
+    return state + tok
+
+
 def cpu_baseline(wl, seconds: float = 12.0):
     """The fp64 oracle on this host over the whole 8K workload (every head,
     every token), repeated until at least `seconds` of CPU time have passed;
@@ -226,6 +235,57 @@ def main():
                            "algorithmic_bytes_per_call": d_bytes,
                            "ms_per_call": round(d_kernel_ms, 4)}}
 
+    # ------------------------------------------- speculative decode leg (K = 4)
+    swl = synth.VERIFY_B256_K4
+    K = swl.seqlens[0]
+    SB = swl.N
+    sA = torch.from_numpy(synth.gate_A(swl)).to(dev)
+    ssets = []
+    for si in range(4):
+        x = {n: synth.token_rows(swl, n, 0, SB * K, set_index=si) for n in ("q", "k", "v", "z", "beta")}
+        d = {n: torch.from_numpy(x[n]).to(dev).to(torch.bfloat16) for n in x}
+        d["g"] = kda.kda_gate(d["z"], sA)
+        d = {n: t.reshape((SB, K) + tuple(t.shape[1:])) for n, t in d.items()}
+        ssets.append(d)
+    sstate = torch.from_numpy(synth.initial_state(swl.with_(seqlens=(1,) * SB))).to(dev)
+    sout = torch.empty((SB, K, swl.H, swl.dv), dtype=torch.bfloat16, device=dev)
+    n_all = torch.full((SB,), K, dtype=torch.int32, device=dev)
+    spec_iters = 200
+    for i in range(5):
+        d = ssets[i % 4]
+        kda.kda_verify(d["q"], d["k"], d["v"], d["g"], d["beta"], sstate, o=sout)
+        kda.kda_commit(d["k"], d["v"], d["g"], d["beta"], n_all, sstate)
+    torch.cuda.synchronize()
+    vev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+            torch.cuda.Event(enable_timing=True)) for _ in range(spec_iters)]
+    for i in range(spec_iters):
+        d = ssets[i % 4]
+        vev[i][0].record(stream)
+        kda.kda_verify(d["q"], d["k"], d["v"], d["g"], d["beta"], sstate, o=sout)
+        vev[i][1].record(stream)
+        kda.kda_commit(d["k"], d["v"], d["g"], d["beta"], n_all, sstate)
+        vev[i][2].record(stream)
+    torch.cuda.synchronize()
+    v_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in vev]))
+    c_ms = float(np.mean([b.elapsed_time(c) for _, b, c in vev]))
+    vb = spec_algo(SB, K, swl.H, swl.dk, swl.dv, False)
+    cb = spec_algo(SB, K, swl.H, swl.dk, swl.dv, True)
+    spec = {"value": round(SB * K / ((v_ms + c_ms) * 1e-3), 1), "unit": "draft tokens/s (verify + commit)",
+            "config": {"workload": "verify_b256_k4", "B": SB, "K": K, "H": swl.H, "d_k": swl.dk,
+                       "d_v": swl.dv, "n_accept": K, "input_sets": 4},
+            "verify": {"ms_per_call": round(v_ms, 4),
+                       "roofline": {"bound": "hbm", "achieved": round(vb / (v_ms * 1e-3) / 1e9, 1),
+                                    "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                    "frac": round(vb / (v_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                    "traffic": None, "kernel": "spec_kernel (verify)",
+                                    "algorithmic_bytes_per_call": vb}},
+            "commit": {"ms_per_call": round(c_ms, 4),
+                       "roofline": {"bound": "hbm", "achieved": round(cb / (c_ms * 1e-3) / 1e9, 1),
+                                    "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                    "frac": round(cb / (c_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                    "traffic": None, "kernel": "spec_kernel (commit)",
+                                    "algorithmic_bytes_per_call": cb}}}
+
     if args.copy_calib:  # plain copy of known size, for the HBM counter calibration
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -242,7 +302,7 @@ def main():
            "config": {"workload": "prefill_8k: gate + chunked prefill, B=1 H=32 T=8192 "
                                   "d_k=d_v=128 chunk=64, zero initial state",
                       "B": 1, "H": H, "T": T, "d_k": dk, "d_v": dv, "chunk": 64, "input_sets": 3},
-           "roofline": roofline, "cpu_baseline": cpu, "decode": decode,
+           "roofline": roofline, "cpu_baseline": cpu, "decode": decode, "speculative": spec,
            "wall_s": round(wall, 3), "source_hash": kernel_source_hash()}
     print(json.dumps(out), flush=True)
 

@@ -149,6 +149,46 @@ kda_status_t kda_decode_step(const void* q, const void* k, const void* v, const 
                              const void* beta, float* state, void* o, int B, int H, int d_k,
                              int d_v, kda_dtype_t dtype, void* stream);
 
+/* Largest number of draft tokens per sequence kda_verify / kda_commit accept. */
+#define KDA_MAX_DRAFT 64
+
+/*
+ * kda_verify — speculative multi-token decode: K draft tokens per sequence run
+ * through the recurrence from the resident state, which is NOT modified
+ * ([K3-notes] Infrastructure / 推理与在线服务, KDA decoding under MTP
+ * speculative decoding: cache the projected inputs, not states; [K3-plain]
+ * §5.4: a wrong guess cannot be undone on an in-place state, so inputs are
+ * kept and replayed; [LateTalk] section 先分后合，和一条没有开源的流水线).
+ *   q, k, g : [B, K, H, d_k]   v, o : [B, K, H, d_v]   beta : [B, K, H]  (dtype)
+ *   state   : fp32 [B, H, d_k, d_v], read only.
+ *   o[b, i] is what kda_decode_step would return for draft token i after the
+ *   tokens 0..i-1 of the same sequence.
+ *   1 <= K <= KDA_MAX_DRAFT; d_k, d_v each one of 32, 64, 128; B == 0 is a no-op.
+ *   The caller keeps q, k, v, g, beta (the projected inputs) for kda_commit.
+ * `o` must not alias any input or the state.
+ * Errors: KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED, KDA_ERR_HIP.
+ */
+kda_status_t kda_verify(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                        const float* state, void* o, int B, int K, int H, int d_k, int d_v,
+                        kda_dtype_t dtype, void* stream);
+
+/*
+ * kda_commit — roll forward by replay: the first n_accept[b] of the K cached
+ * draft tokens of sequence b (the tensors passed to kda_verify) are applied to
+ * the state IN PLACE; the rejected rest leave no trace.  Same sources as
+ * kda_verify.
+ *   k, g : [B, K, H, d_k]   v : [B, K, H, d_v]   beta : [B, K, H]  (dtype)
+ *   n_accept : int32 [B] DEVICE array; each value is clamped to [0, K]
+ *              (0 leaves that sequence's state untouched).
+ *   state    : fp32 [B, H, d_k, d_v], read and overwritten.
+ *   No output is written (the outputs of accepted tokens are those kda_verify
+ *   returned).  Sizes as for kda_verify.
+ * Errors: KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED, KDA_ERR_HIP.
+ */
+kda_status_t kda_commit(const void* k, const void* v, const void* g, const void* beta,
+                        const int32_t* n_accept, float* state, int B, int K, int H, int d_k, int d_v,
+                        kda_dtype_t dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

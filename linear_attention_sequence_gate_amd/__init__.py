@@ -18,7 +18,7 @@ KDA_F32, KDA_BF16 = 0, 1
 _STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARGUMENT", 2: "KDA_ERR_UNSUPPORTED",
            3: "KDA_ERR_WORKSPACE_TOO_SMALL", 4: "KDA_ERR_HIP"}
 EXPORTED = ("kda_status_string", "kda_last_error", "kda_version", "kda_gate",
-            "kda_prefill_workspace_size", "kda_prefill", "kda_decode_step")
+            "kda_prefill_workspace_size", "kda_prefill", "kda_decode_step", "kda_verify", "kda_commit")
 
 _lib = None
 
@@ -52,6 +52,10 @@ def lib() -> ctypes.CDLL:
         L.kda_prefill.restype = I
         L.kda_decode_step.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, P]
         L.kda_decode_step.restype = I
+        L.kda_verify.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, P]
+        L.kda_verify.restype = I
+        L.kda_commit.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, P]
+        L.kda_commit.restype = I
         _lib = L
     return _lib
 
@@ -145,3 +149,30 @@ def kda_decode_step(q, k, v, g, beta, state, o=None, stream=None):
     _check(lib().kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(o),
                                  B, H, dk, dv, _dtype_code(k), _stream(stream)))
     return o
+
+
+def kda_verify(q, k, v, g, beta, state, o=None, stream=None):
+    """K draft tokens per sequence from the resident state (not modified).
+
+    q, k, g: [B, K, H, d_k]; v: [B, K, H, d_v]; beta: [B, K, H]; state fp32
+    [B, H, d_k, d_v].  Returns o [B, K, H, d_v]."""
+    import torch
+    _dense(q, k, v, g, beta, state, o)
+    B, K, H, dk = k.shape
+    dv = v.shape[3]
+    if o is None:
+        o = torch.empty((B, K, H, dv), dtype=v.dtype, device=v.device)
+    _check(lib().kda_verify(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(o),
+                            B, K, H, dk, dv, _dtype_code(k), _stream(stream)))
+    return o
+
+
+def kda_commit(k, v, g, beta, n_accept, state, stream=None):
+    """Replay the first n_accept[b] (int32 device [B]) cached draft tokens onto
+    the state in place."""
+    _dense(k, v, g, beta, n_accept, state)
+    B, K, H, dk = k.shape
+    dv = v.shape[3]
+    _check(lib().kda_commit(_ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(n_accept), _ptr(state),
+                            B, K, H, dk, dv, _dtype_code(k), _stream(stream)))
+    return state

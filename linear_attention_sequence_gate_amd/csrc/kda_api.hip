@@ -12,6 +12,7 @@
 #include "kda_decode.hpp"
 #include "kda_gate.hpp"
 #include "kda_prefill.hpp"
+#include "kda_spec.hpp"
 
 namespace {
 
@@ -127,6 +128,79 @@ kda_status_t kda_decode_step(const void* q, const void* k, const void* v, const 
                        ? kda::launch_decode<kda::BF16>(q, k, v, g, beta, state, o, B * H, d_k, d_v, s)
                        : kda::launch_decode<kda::F32>(q, k, v, g, beta, state, o, B * H, d_k, d_v, s);
     return from_hip(e, "kda_decode_step launch");
+}
+
+// shared checks of kda_verify / kda_commit; returns KDA_OK with *noop set for B == 0
+static kda_status_t spec_check(const char* who, bool commit, const void* q, const void* k, const void* v,
+                               const void* g, const void* beta, const void* n_accept, const float* state,
+                               const void* o, int B, int K, int H, int d_k, int d_v, kda_dtype_t dtype,
+                               bool* noop)
+{
+    *noop = false;
+    if (B < 0 || H < 1 || K < 1)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: bad sizes B=%d K=%d H=%d", who, B, K, H);
+    if (K > KDA_MAX_DRAFT) return fail(KDA_ERR_UNSUPPORTED, "%s: K=%d > %d", who, K, KDA_MAX_DRAFT);
+    if (!dtype_ok(dtype)) return fail(KDA_ERR_UNSUPPORTED, "%s: unknown dtype %d", who, (int)dtype);
+    if (!dim_ok(d_k) || !dim_ok(d_v))
+        return fail(KDA_ERR_UNSUPPORTED, "%s: d_k=%d d_v=%d not in {32,64,128}", who, d_k, d_v);
+    if (B == 0) {
+        *noop = true;
+        return ok();
+    }
+    if ((!commit && (!q || !o)) || !k || !v || !g || !beta || !state || (commit && !n_accept))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: null pointer", who);
+    if ((reinterpret_cast<uintptr_t>(state) & 15) != 0)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: state must be 16-byte aligned", who);
+    if (int64_t(B) * H > 0x7fffffff || int64_t(B) * K * H * 128 > (int64_t(1) << 40))
+        return fail(KDA_ERR_UNSUPPORTED, "%s: B*K*H too large", who);
+    const size_t es = dsize(dtype);
+    const size_t nt = size_t(B) * K * H;
+    const size_t nk = nt * d_k * es, nv = nt * d_v * es, nb = nt * es;
+    const size_t ns = size_t(B) * H * d_k * d_v * sizeof(float);
+    const void* ins[6] = {q, k, v, g, beta, n_accept};
+    const size_t insz[6] = {commit ? 0 : nk, nk, nv, nk, nb, commit ? size_t(B) * sizeof(int32_t) : 0};
+    for (int i = 0; i < 6; ++i) {
+        if (!commit && overlap(o, nv, ins[i], insz[i]))
+            return fail(KDA_ERR_INVALID_ARGUMENT, "%s: o aliases an input", who);
+        if (overlap(state, ns, ins[i], insz[i]))
+            return fail(KDA_ERR_INVALID_ARGUMENT, "%s: state aliases an input", who);
+    }
+    if (!commit && overlap(o, nv, state, ns))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: o aliases the state", who);
+    return ok();
+}
+
+kda_status_t kda_verify(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                        const float* state, void* o, int B, int K, int H, int d_k, int d_v,
+                        kda_dtype_t dtype, void* stream)
+{
+    bool noop;
+    kda_status_t st = spec_check("kda_verify", false, q, k, v, g, beta, nullptr, state, o, B, K, H, d_k, d_v,
+                                 dtype, &noop);
+    if (st != KDA_OK || noop) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    float* S = const_cast<float*>(state);  // read only in verify mode
+    hipError_t e = dtype == KDA_BF16
+                       ? kda::launch_spec<kda::BF16>(q, k, v, g, beta, nullptr, S, o, B, K, H, d_k, d_v, false, s)
+                       : kda::launch_spec<kda::F32>(q, k, v, g, beta, nullptr, S, o, B, K, H, d_k, d_v, false, s);
+    return from_hip(e, "kda_verify launch");
+}
+
+kda_status_t kda_commit(const void* k, const void* v, const void* g, const void* beta,
+                        const int32_t* n_accept, float* state, int B, int K, int H, int d_k, int d_v,
+                        kda_dtype_t dtype, void* stream)
+{
+    bool noop;
+    kda_status_t st = spec_check("kda_commit", true, nullptr, k, v, g, beta, n_accept, state, nullptr, B, K, H,
+                                 d_k, d_v, dtype, &noop);
+    if (st != KDA_OK || noop) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = dtype == KDA_BF16
+                       ? kda::launch_spec<kda::BF16>(nullptr, k, v, g, beta, n_accept, state, nullptr, B, K, H,
+                                                     d_k, d_v, true, s)
+                       : kda::launch_spec<kda::F32>(nullptr, k, v, g, beta, n_accept, state, nullptr, B, K, H,
+                                                    d_k, d_v, true, s);
+    return from_hip(e, "kda_commit launch");
 }
 
 size_t kda_prefill_workspace_size(int64_t T_total, int N, int H, int d_k, int d_v, int chunk,

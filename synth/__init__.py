@@ -100,7 +100,12 @@ VARLEN_64 = Workload("varlen_64", H=32, dk=128, dv=128,
                      seqlens=varlen_lengths(64, 1024, 65536, 1015), dtype="bf16",
                      state_std=0.1, seed=1004)
 
-WORKLOADS = {w.name: w for w in (TINY_F32, PREFILL_8K, PREFILL_1M, DECODE_B256, VARLEN_64)}
+# speculative decode: K = 4 draft tokens for each of the 256 sequences of the
+# decode workload (token tensors [B, K, H, d] are the packed [B*K, H, d] rows)
+VERIFY_B256_K4 = Workload("verify_b256_k4", H=32, dk=128, dv=128, seqlens=(4,) * 256, dtype="bf16",
+                          state_std=0.1, seed=1005)
+
+WORKLOADS = {w.name: w for w in (TINY_F32, PREFILL_8K, PREFILL_1M, DECODE_B256, VARLEN_64, VERIFY_B256_K4)}
 
 
 def _gen(wl: Workload, name: str, set_index: int, block: int) -> np.random.Generator:

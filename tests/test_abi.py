@@ -132,3 +132,37 @@ def test_prefill_validation(L):
     assert call(init=FAKE + (8 << 20) + 4) == 1              # partial init/final overlap
     assert call(ws=FAKE + (16 << 20)) == 1                   # workspace aliases o
     assert call(ws=FAKE + (4 << 20)) == 1                    # workspace aliases beta
+
+
+def test_verify_commit_validation(L):
+    base = dict(q=FAKE, k=FAKE + (1 << 20), v=FAKE + (2 << 20), g=FAKE + (3 << 20),
+                beta=FAKE + (4 << 20), state=FAKE + (8 << 20), o=FAKE + (64 << 20), n=FAKE + (96 << 20))
+
+    def verify(**kw):
+        a = dict(base, B=4, K=3, H=2, dk=64, dv=64, dt=BF16)
+        a.update(kw)
+        return L.kda_verify(a["q"], a["k"], a["v"], a["g"], a["beta"], a["state"], a["o"],
+                            a["B"], a["K"], a["H"], a["dk"], a["dv"], a["dt"], None)
+
+    def commit(**kw):
+        a = dict(base, B=4, K=3, H=2, dk=64, dv=64, dt=BF16)
+        a.update(kw)
+        return L.kda_commit(a["k"], a["v"], a["g"], a["beta"], a["n"], a["state"],
+                            a["B"], a["K"], a["H"], a["dk"], a["dv"], a["dt"], None)
+
+    for call in (verify, commit):
+        assert call(B=-1) == 1
+        assert call(K=0) == 1
+        assert call(H=0) == 1
+        assert call(K=65) == 2                                # above KDA_MAX_DRAFT
+        assert call(dk=48) == 2
+        assert call(dt=7) == 2
+        assert call(k=None) == 1
+        assert call(state=FAKE + (8 << 20) + 4) == 1          # misaligned state
+        assert call(state=FAKE + (3 << 20)) == 1              # state aliases g
+        assert call(B=0, k=None, state=None) == 0             # empty batch: no-op
+    assert verify(q=None) == 1
+    assert verify(o=None) == 1
+    assert verify(o=FAKE + 16) == 1                           # o aliases q
+    assert verify(o=FAKE + (8 << 20)) == 1                    # o aliases the state
+    assert commit(n=None) == 1
