@@ -186,6 +186,25 @@ def main():
                 "mfma_tflops": round(p_flops / (prefill_ms * 1e-3) / 1e12, 1),
                 "mfma_frac": round(p_flops / (prefill_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)}
 
+    # prefill with state checkpoints every 512 tokens (prefix-cache emission)
+    n_ck = kda.kda_checkpoint_count(None, T, 512)
+    ck = torch.empty((n_ck, H, dk, dv), dtype=torch.float32, device=dev)
+    cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for i in range(args.warmup + args.steps):
+        d = sets[i % 3]
+        if i >= args.warmup:
+            cev[i - args.warmup][0].record(stream)
+        kda.kda_prefill_ckpt(d["q"], d["k"], d["v"], d["g"], d["beta"], 512, ckpt=ck, final_state=d["S"],
+                             o=d["o"], workspace=ws)
+        if i >= args.warmup:
+            cev[i - args.warmup][1].record(stream)
+    torch.cuda.synchronize()
+    ck_ms = float(np.mean([a.elapsed_time(b) for a, b in cev]))
+    ckpt_leg = {"interval": 512, "checkpoints_per_call": n_ck * H, "ms_per_call": round(ck_ms, 4),
+                "overhead_vs_plain": round(ck_ms / prefill_ms - 1.0, 4),
+                "checkpoint_bytes_per_call": n_ck * H * dk * dv * 4}
+
     # ------------------------------------------------------------- decode leg
     dwl = synth.DECODE_B256
     B = dwl.N
@@ -302,7 +321,8 @@ def main():
            "config": {"workload": "prefill_8k: gate + chunked prefill, B=1 H=32 T=8192 "
                                   "d_k=d_v=128 chunk=64, zero initial state",
                       "B": 1, "H": H, "T": T, "d_k": dk, "d_v": dv, "chunk": 64, "input_sets": 3},
-           "roofline": roofline, "cpu_baseline": cpu, "decode": decode, "speculative": spec,
+           "roofline": roofline, "cpu_baseline": cpu, "checkpoints": ckpt_leg, "decode": decode,
+           "speculative": spec,
            "wall_s": round(wall, 3), "source_hash": kernel_source_hash()}
     print(json.dumps(out), flush=True)
 

@@ -135,6 +135,39 @@ kda_status_t kda_prefill(const void* q, const void* k, const void* v, const void
                          size_t workspace_bytes, void* stream);
 
 /*
+ * kda_prefill_ckpt — kda_prefill that also emits state checkpoints for a
+ * prefix cache ([K3-notes] Infrastructure / 推理与在线服务, KDA-aware prefix
+ * cache: hashes over 512-token blocks; KDA states kept only at sparse
+ * boundaries, so a hit can sit at any multiple of the block size).
+ * Every argument of kda_prefill, plus:
+ *   ckpt_interval : tokens between checkpoints, a positive multiple of 64
+ *                   (512 matches the pages' block).
+ *   ckpt_states   : fp32 [ckpt_capacity, H, d_k, d_v] DEVICE buffer.  For
+ *                   sequence n of length len_n the state after its first
+ *                   j * ckpt_interval tokens (j = 1 .. len_n / ckpt_interval)
+ *                   goes to row ckpt_off[n] + j - 1, with ckpt_off the running
+ *                   sum of len_m / ckpt_interval over the sequences m < n
+ *                   (lengths as clamped by the planner; see kda_prefill).
+ *   ckpt_capacity : rows the buffer holds; checkpoints past it are skipped.
+ *                   kda_checkpoint_count gives the number needed.
+ * Errors: as kda_prefill, plus KDA_ERR_INVALID_ARGUMENT for a bad interval,
+ * a null buffer with a positive capacity, or a buffer overlapping another.
+ */
+kda_status_t kda_prefill_ckpt(const void* q, const void* k, const void* v, const void* g,
+                              const void* beta, const int32_t* cu_seqlens, int N, int64_t T_total,
+                              int H, int d_k, int d_v, int chunk, const float* initial_state,
+                              float* final_state, void* o, kda_dtype_t dtype, void* workspace,
+                              size_t workspace_bytes, int ckpt_interval, float* ckpt_states,
+                              int64_t ckpt_capacity, void* stream);
+
+/*
+ * Number of checkpoints kda_prefill_ckpt writes for these HOST cu_seqlens
+ * (NULL: one sequence of T_total tokens), with the planner's clamping; -1 on
+ * invalid arguments (N < 1, T_total < 0, ckpt_interval <= 0).  Host only.
+ */
+int64_t kda_checkpoint_count(const int32_t* cu_seqlens_host, int N, int64_t T_total, int ckpt_interval);
+
+/*
  * kda_decode_step — one token per sequence against a resident fp32 state,
  * updated IN PLACE ([K3-notes] KDA recurrence; [K3-plain] §5.4; [LateTalk]
  * fixed-size state overwritten by every token):

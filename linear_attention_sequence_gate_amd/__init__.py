@@ -18,7 +18,8 @@ KDA_F32, KDA_BF16 = 0, 1
 _STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARGUMENT", 2: "KDA_ERR_UNSUPPORTED",
            3: "KDA_ERR_WORKSPACE_TOO_SMALL", 4: "KDA_ERR_HIP"}
 EXPORTED = ("kda_status_string", "kda_last_error", "kda_version", "kda_gate",
-            "kda_prefill_workspace_size", "kda_prefill", "kda_decode_step", "kda_verify", "kda_commit")
+            "kda_prefill_workspace_size", "kda_prefill", "kda_decode_step", "kda_verify", "kda_commit",
+            "kda_prefill_ckpt", "kda_checkpoint_count")
 
 _lib = None
 
@@ -56,6 +57,10 @@ def lib() -> ctypes.CDLL:
         L.kda_verify.restype = I
         L.kda_commit.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, P]
         L.kda_commit.restype = I
+        L.kda_prefill_ckpt.argtypes = [P, P, P, P, P, P, I, I64, I, I, I, I, P, P, P, I, P, SZ, I, P, I64, P]
+        L.kda_prefill_ckpt.restype = I
+        L.kda_checkpoint_count.argtypes = [P, I, I64, I]
+        L.kda_checkpoint_count.restype = I64
         _lib = L
     return _lib
 
@@ -176,3 +181,43 @@ def kda_commit(k, v, g, beta, n_accept, state, stream=None):
     _check(lib().kda_commit(_ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(n_accept), _ptr(state),
                             B, K, H, dk, dv, _dtype_code(k), _stream(stream)))
     return state
+
+
+def kda_checkpoint_count(cu_seqlens_host, T_total: int, interval: int) -> int:
+    """Checkpoints kda_prefill_ckpt writes; cu_seqlens_host: int32 numpy [N+1] or None."""
+    import numpy as np
+    if cu_seqlens_host is None:
+        return int(lib().kda_checkpoint_count(None, 1, T_total, interval))
+    cu = np.ascontiguousarray(cu_seqlens_host, dtype=np.int32)
+    return int(lib().kda_checkpoint_count(cu.ctypes.data, cu.shape[0] - 1, T_total, interval))
+
+
+def kda_prefill_ckpt(q, k, v, g, beta, interval: int, ckpt=None, cu_seqlens=None, cu_seqlens_host=None,
+                     initial_state=None, final_state=None, o=None, workspace=None, chunk: int = 64,
+                     stream=None):
+    """kda_prefill plus state checkpoints every `interval` tokens of each sequence.
+    Returns (o, final_state, ckpt) with ckpt fp32 [n_ckpt, H, d_k, d_v]."""
+    import torch
+    _dense(q, k, v, g, beta, cu_seqlens, initial_state, final_state, o, ckpt)
+    T, H, dk = k.shape
+    dv = v.shape[2]
+    N = 1 if cu_seqlens is None else cu_seqlens.shape[0] - 1
+    code = _dtype_code(k)
+    if o is None:
+        o = torch.empty((T, H, dv), dtype=v.dtype, device=v.device)
+    if final_state is None:
+        final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=k.device)
+    if ckpt is None:
+        if cu_seqlens is not None and cu_seqlens_host is None:
+            cu_seqlens_host = cu_seqlens.cpu().numpy()
+        n = kda_checkpoint_count(cu_seqlens_host, T, interval)
+        ckpt = torch.empty((max(n, 0), H, dk, dv), dtype=torch.float32, device=k.device)
+    need = kda_prefill_workspace_size(T, N, H, dk, dv, chunk, code)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=k.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().kda_prefill_ckpt(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N, T,
+                                  H, dk, dv, chunk, _ptr(initial_state), _ptr(final_state), _ptr(o), code,
+                                  _ptr(workspace), wbytes, int(interval), _ptr(ckpt) if ckpt.numel() else None,
+                                  ckpt.shape[0], _stream(stream)))
+    return o, final_state, ckpt

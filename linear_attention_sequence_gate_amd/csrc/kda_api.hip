@@ -212,32 +212,32 @@ size_t kda_prefill_workspace_size(int64_t T_total, int N, int H, int d_k, int d_
     return kda::prefill_plan(T_total, N, H, d_k, d_v).workspace_bytes;
 }
 
-kda_status_t kda_prefill(const void* q, const void* k, const void* v, const void* g,
-                         const void* beta, const int32_t* cu_seqlens, int N, int64_t T_total,
-                         int H, int d_k, int d_v, int chunk, const float* initial_state,
-                         float* final_state, void* o, kda_dtype_t dtype, void* workspace,
-                         size_t workspace_bytes, void* stream)
+static kda_status_t prefill_impl(const char* who, const void* q, const void* k, const void* v, const void* g,
+                                 const void* beta, const int32_t* cu_seqlens, int N, int64_t T_total, int H,
+                                 int d_k, int d_v, int chunk, const float* initial_state, float* final_state,
+                                 void* o, kda_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                                 int ckpt_interval, float* ckpt_states, int64_t ckpt_capacity, void* stream)
 {
     if (N < 1 || T_total < 0 || H < 1)
-        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_prefill: bad sizes N=%d T_total=%lld H=%d", N,
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: bad sizes N=%d T_total=%lld H=%d", who, N,
                     (long long)T_total, H);
-    if (H > KDA_MAX_HEADS) return fail(KDA_ERR_UNSUPPORTED, "kda_prefill: H=%d > %d", H, KDA_MAX_HEADS);
+    if (H > KDA_MAX_HEADS) return fail(KDA_ERR_UNSUPPORTED, "%s: H=%d > %d", who, H, KDA_MAX_HEADS);
     if (!cu_seqlens && N != 1)
-        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_prefill: cu_seqlens is NULL but N=%d", N);
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: cu_seqlens is NULL but N=%d", who, N);
     if (!dtype_ok(dtype))
-        return fail(KDA_ERR_UNSUPPORTED, "kda_prefill: unknown dtype %d", (int)dtype);
+        return fail(KDA_ERR_UNSUPPORTED, "%s: unknown dtype %d", who, (int)dtype);
     if (!dim_ok(d_k) || !dim_ok(d_v))
-        return fail(KDA_ERR_UNSUPPORTED, "kda_prefill: d_k=%d d_v=%d not in {32,64,128}", d_k, d_v);
-    if (chunk != 64) return fail(KDA_ERR_UNSUPPORTED, "kda_prefill: chunk=%d (only 64)", chunk);
+        return fail(KDA_ERR_UNSUPPORTED, "%s: d_k=%d d_v=%d not in {32,64,128}", who, d_k, d_v);
+    if (chunk != 64) return fail(KDA_ERR_UNSUPPORTED, "%s: chunk=%d (only 64)", who, chunk);
     if (dtype == KDA_F32 && (d_k != 32 || d_v > 64))
-        return fail(KDA_ERR_UNSUPPORTED, "kda_prefill: fp32 tensors need d_k = 32, d_v <= 64");
+        return fail(KDA_ERR_UNSUPPORTED, "%s: fp32 tensors need d_k = 32, d_v <= 64", who);
     if (T_total > (int64_t(1) << 40))
-        return fail(KDA_ERR_UNSUPPORTED, "kda_prefill: T_total too large");
+        return fail(KDA_ERR_UNSUPPORTED, "%s: T_total too large", who);
     if (T_total > 0 && (!q || !k || !v || !g || !beta || !o))
-        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_prefill: null token tensor");
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: null token tensor", who);
     const kda::PrefillPlan plan = kda::prefill_plan(T_total, N, H, d_k, d_v);
     if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
-        return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "kda_prefill: workspace %zu bytes < %zu needed",
+        return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes < %zu needed", who,
                     workspace_bytes, plan.workspace_bytes);
     const size_t es = dsize(dtype);
     const size_t nk = size_t(T_total) * H * d_k * es, nv = size_t(T_total) * H * d_v * es;
@@ -247,26 +247,92 @@ kda_status_t kda_prefill(const void* q, const void* k, const void* v, const void
     const size_t insz[6] = {nk, nk, nv, nk, nb, initial_state ? ns : 0};
     for (int i = 0; i < 6; ++i) {
         if (overlap(o, nv, ins[i], insz[i]))
-            return fail(KDA_ERR_INVALID_ARGUMENT, "kda_prefill: o aliases an input");
+            return fail(KDA_ERR_INVALID_ARGUMENT, "%s: o aliases an input", who);
         if (i < 5 && overlap(final_state, final_state ? ns : 0, ins[i], insz[i]))
-            return fail(KDA_ERR_INVALID_ARGUMENT, "kda_prefill: final_state aliases a token input");
+            return fail(KDA_ERR_INVALID_ARGUMENT, "%s: final_state aliases a token input", who);
         if (overlap(workspace, plan.workspace_bytes, ins[i], insz[i]))
-            return fail(KDA_ERR_INVALID_ARGUMENT, "kda_prefill: workspace aliases an input");
+            return fail(KDA_ERR_INVALID_ARGUMENT, "%s: workspace aliases an input", who);
     }
     if (final_state && initial_state && final_state != initial_state &&
         overlap(final_state, ns, initial_state, ns))
-        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_prefill: final_state partially overlaps initial_state");
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: final_state partially overlaps initial_state", who);
     if (overlap(o, nv, final_state, final_state ? ns : 0) ||
         overlap(workspace, plan.workspace_bytes, o, nv) ||
         overlap(workspace, plan.workspace_bytes, final_state, final_state ? ns : 0))
-        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_prefill: output buffers overlap");
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: output buffers overlap", who);
+    if (ckpt_interval < 0 || (ckpt_interval > 0 && ckpt_interval % kda::CH != 0))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: checkpoint interval %d is not a positive multiple of %d", who,
+                    ckpt_interval, kda::CH);
+    if (ckpt_interval > 0 && T_total / ckpt_interval > 0x7fffffff)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: too many checkpoints", who);
+    if (ckpt_interval > 0 && ckpt_capacity > 0) {
+        if (!ckpt_states) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: null checkpoint buffer", who);
+        if ((reinterpret_cast<uintptr_t>(ckpt_states) & 3) != 0)
+            return fail(KDA_ERR_INVALID_ARGUMENT, "%s: checkpoint buffer not 4-byte aligned", who);
+        const size_t nc = size_t(ckpt_capacity) * H * d_k * d_v * sizeof(float);
+        const void* all[9] = {q, k, v, g, beta, initial_state, final_state, o, workspace};
+        const size_t allsz[9] = {size_t(T_total) * H * d_k * dsize(dtype), size_t(T_total) * H * d_k * dsize(dtype),
+                                 size_t(T_total) * H * d_v * dsize(dtype), size_t(T_total) * H * d_k * dsize(dtype),
+                                 size_t(T_total) * H * dsize(dtype),
+                                 initial_state ? size_t(N) * H * d_k * d_v * sizeof(float) : 0,
+                                 final_state ? size_t(N) * H * d_k * d_v * sizeof(float) : 0,
+                                 size_t(T_total) * H * d_v * dsize(dtype), plan.workspace_bytes};
+        for (int i = 0; i < 9; ++i)
+            if (overlap(ckpt_states, nc, all[i], allsz[i]))
+                return fail(KDA_ERR_INVALID_ARGUMENT, "%s: checkpoint buffer overlaps another buffer", who);
+    }
     if (!final_state && T_total == 0) return ok();
     hipStream_t s = static_cast<hipStream_t>(stream);
     kda::PrefillArgs a{q, k, v, g, beta, cu_seqlens, N, T_total, H, d_k, d_v,
                        initial_state, final_state, o, workspace};
+    if (ckpt_interval > 0 && ckpt_capacity > 0) {
+        a.ckpt = ckpt_states;
+        a.ckpt_interval = ckpt_interval;
+        a.ckpt_cap = ckpt_capacity;
+    }
     hipError_t e = dtype == KDA_BF16 ? kda::launch_prefill<kda::BF16>(a, plan, s)
                                      : kda::launch_prefill<kda::F32>(a, plan, s);
     return from_hip(e, "kda_prefill launch");
+}
+
+kda_status_t kda_prefill(const void* q, const void* k, const void* v, const void* g,
+                         const void* beta, const int32_t* cu_seqlens, int N, int64_t T_total,
+                         int H, int d_k, int d_v, int chunk, const float* initial_state,
+                         float* final_state, void* o, kda_dtype_t dtype, void* workspace,
+                         size_t workspace_bytes, void* stream)
+{
+    return prefill_impl("kda_prefill", q, k, v, g, beta, cu_seqlens, N, T_total, H, d_k, d_v, chunk,
+                        initial_state, final_state, o, dtype, workspace, workspace_bytes, 0, nullptr, 0, stream);
+}
+
+kda_status_t kda_prefill_ckpt(const void* q, const void* k, const void* v, const void* g,
+                              const void* beta, const int32_t* cu_seqlens, int N, int64_t T_total,
+                              int H, int d_k, int d_v, int chunk, const float* initial_state,
+                              float* final_state, void* o, kda_dtype_t dtype, void* workspace,
+                              size_t workspace_bytes, int ckpt_interval, float* ckpt_states,
+                              int64_t ckpt_capacity, void* stream)
+{
+    if (ckpt_interval <= 0)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_prefill_ckpt: checkpoint interval %d", ckpt_interval);
+    if (ckpt_capacity < 0)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_prefill_ckpt: negative checkpoint capacity");
+    return prefill_impl("kda_prefill_ckpt", q, k, v, g, beta, cu_seqlens, N, T_total, H, d_k, d_v, chunk,
+                        initial_state, final_state, o, dtype, workspace, workspace_bytes, ckpt_interval,
+                        ckpt_states, ckpt_capacity, stream);
+}
+
+int64_t kda_checkpoint_count(const int32_t* cu_seqlens_host, int N, int64_t T_total, int ckpt_interval)
+{
+    if (N < 1 || T_total < 0 || ckpt_interval <= 0) return -1;
+    int64_t total = 0, prev = 0;
+    for (int n = 0; n < N; ++n) {
+        int64_t x = cu_seqlens_host ? int64_t(cu_seqlens_host[n + 1]) : T_total;
+        x = x < 0 ? 0 : (x > T_total ? T_total : x);
+        if (x < prev) x = prev;  // the same clamping the device planner applies
+        total += (x - prev) / ckpt_interval;
+        prev = x;
+    }
+    return total;
 }
 
 }  // extern "C"

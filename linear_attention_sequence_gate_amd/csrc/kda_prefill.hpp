@@ -113,7 +113,7 @@ inline PrefillPlan prefill_plan(int64_t T_total, int N, int H, int dk, int dv)
     p.np1_max = (max_seq_chunks > L) ? chunks_bound / L + 1 : 0;
     size_t off = 0;
     p.off_table = off;
-    off = align256(off + sizeof(int32_t) * 3 * size_t(N + 1));
+    off = align256(off + sizeof(int32_t) * 4 * size_t(N + 1));
     if (p.np1_max > 0) {
         p.off_ms = off;
         off = align256(off + sizeof(float) * size_t(p.np1_max) * H * dk * (dk + dv));
@@ -134,12 +134,15 @@ struct PrefillArgs {
     float* fin;
     void* o;
     void* ws;
+    float* ckpt = nullptr;  // state checkpoints (or null)
+    int ckpt_interval = 0;  // tokens between checkpoints (multiple of CH), 0 = none
+    int64_t ckpt_cap = 0;   // checkpoints the buffer holds
 };
 
 // Device-side view shared by the prefill kernels.
 struct PrefillDev {
     const void *q, *k, *v, *g, *beta;
-    const int32_t* tab;  // cuc[N+1] | seg_off[N+1] | p1_off[N+1]
+    const int32_t* tab;  // cuc[N+1] | seg_off[N+1] | p1_off[N+1] | ckpt_off[N+1]
     int N;
     int64_t T_total;
     int H;
@@ -149,27 +152,35 @@ struct PrefillDev {
     void* o;
     float* ms;   // [np1][H][dk][dk+dv]
     float* sin;  // [nseg][H][dk][dv]
+    float* ckpt;  // [ckpt_cap][H][dk][dv] or null
+    int ckpt_interval;
+    int64_t ckpt_cap;
 };
 
 // ------------------------------------------------------------- plan kernel
 // One workgroup: clamps cu_seqlens into a non-decreasing sequence inside
-// [0, T_total] and writes the per-sequence segment / pass-1 offsets.
+// [0, T_total] and writes the per-sequence segment, pass-1 and checkpoint
+// offsets (a sequence of length len holds len / ckpt_interval checkpoints).
 __global__ void __launch_bounds__(256) plan_kernel(const int32_t* __restrict__ cu, int N,
-                                                   int64_t T_total, int L, int32_t* __restrict__ tab)
+                                                   int64_t T_total, int L, int ckpt_interval,
+                                                   int32_t* __restrict__ tab)
 {
-    __shared__ int32_t s_seg[256], s_p1[256], s_cu[256];
-    __shared__ int32_t carry_seg, carry_p1, carry_cu;
+    __shared__ int32_t s_seg[256], s_p1[256], s_cu[256], s_ck[256];
+    __shared__ int32_t carry_seg, carry_p1, carry_cu, carry_ck;
     int32_t* cuc = tab;
     int32_t* seg_off = tab + (N + 1);
     int32_t* p1_off = tab + 2 * (N + 1);
+    int32_t* ck_off = tab + 3 * (N + 1);
     const int t = threadIdx.x;
     if (t == 0) {
         carry_seg = 0;
         carry_p1 = 0;
         carry_cu = 0;
+        carry_ck = 0;
         cuc[0] = 0;
         seg_off[0] = 0;
         p1_off[0] = 0;
+        ck_off[0] = 0;
     }
     __syncthreads();
     for (int base = 0; base < N; base += 256) {
@@ -195,7 +206,7 @@ __global__ void __launch_bounds__(256) plan_kernel(const int32_t* __restrict__ c
         s_cu[t] = c1m;
         __syncthreads();
         const int32_t c0m = (t == 0) ? carry_cu : s_cu[t - 1];
-        int32_t nseg = 0, np1 = 0;
+        int32_t nseg = 0, np1 = 0, nck = 0;
         if (n < N) {
             const int64_t len = int64_t(c1m) - c0m;
             const int64_t ch = (len + CH - 1) / CH;
@@ -203,28 +214,34 @@ __global__ void __launch_bounds__(256) plan_kernel(const int32_t* __restrict__ c
             if (ns < 1) ns = 1;
             nseg = int32_t(ns);
             np1 = int32_t(ns - 1);
+            nck = ckpt_interval > 0 ? int32_t(len / ckpt_interval) : 0;
         }
         s_seg[t] = nseg;
         s_p1[t] = np1;
+        s_ck[t] = nck;
         __syncthreads();
         for (int d = 1; d < 256; d <<= 1) {  // inclusive sum-scans
             const int32_t a = (t >= d) ? s_seg[t - d] : 0;
             const int32_t b = (t >= d) ? s_p1[t - d] : 0;
+            const int32_t c = (t >= d) ? s_ck[t - d] : 0;
             __syncthreads();
             s_seg[t] += a;
             s_p1[t] += b;
+            s_ck[t] += c;
             __syncthreads();
         }
         if (n < N) {
             cuc[n + 1] = c1m;
             seg_off[n + 1] = carry_seg + s_seg[t];
             p1_off[n + 1] = carry_p1 + s_p1[t];
+            ck_off[n + 1] = carry_ck + s_ck[t];
         }
         __syncthreads();
         if (t == 255) {
             carry_seg += s_seg[255];
             carry_p1 += s_p1[255];
             carry_cu = s_cu[255];
+            carry_ck += s_ck[255];
         }
         __syncthreads();
     }
@@ -1047,6 +1064,25 @@ prefill_block_kernel(PrefillDev p)
                 O::mma(S[rt][ct], kf, Ub[ct]);
             }
         }
+        // state checkpoint when this block ends on a multiple of the interval
+        // (intervals are multiples of 64, so checkpoints fall on block ends)
+        if (!SUMMARY && p.ckpt) {
+            const int64_t pos = b0 + len - seq0;  // tokens of the sequence consumed
+            if (pos % p.ckpt_interval == 0) {
+                const int64_t idx = int64_t(p.tab[3 * (p.N + 1) + n]) + pos / p.ckpt_interval - 1;
+                if (idx < p.ckpt_cap) {
+                    float* dst = p.ckpt + (idx * H + h) * DK * DV;
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                            for (int j = 0; j < 4; ++j)
+                                __builtin_nontemporal_store(S[rt][ct][j],
+                                                            dst + (rt * 16 + 4 * q4 + j) * DV + colbase + ct * 16 + l16);
+                }
+            }
+        }
         KDA_PHASE(2);
         __syncthreads();
         KDA_PHASE(3);
@@ -1304,9 +1340,10 @@ hipError_t launch_prefill_t(const PrefillArgs& a, const PrefillPlan& plan, hipSt
     PrefillDev d{a.q, a.k, a.v, a.g, a.beta, tab, a.N, a.T_total, a.H, plan.seg_chunks,
                  a.init, a.fin, a.o,
                  plan.np1_max > 0 ? reinterpret_cast<float*>(ws + plan.off_ms) : nullptr,
-                 plan.np1_max > 0 ? reinterpret_cast<float*>(ws + plan.off_sin) : nullptr};
+                 plan.np1_max > 0 ? reinterpret_cast<float*>(ws + plan.off_sin) : nullptr,
+                 a.ckpt, a.ckpt_interval, a.ckpt_cap};
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, stream, a.cu, a.N, a.T_total,
-                       plan.seg_chunks, tab);
+                       plan.seg_chunks, a.ckpt ? a.ckpt_interval : 0, tab);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (plan.np1_max > 0) {

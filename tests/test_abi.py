@@ -166,3 +166,49 @@ def test_verify_commit_validation(L):
     assert verify(o=FAKE + 16) == 1                           # o aliases q
     assert verify(o=FAKE + (8 << 20)) == 1                    # o aliases the state
     assert commit(n=None) == 1
+
+
+def test_checkpoint_count_host(L):
+    """kda_checkpoint_count applies the planner's clamping (non-decreasing
+    offsets inside [0, T_total]) and counts len // interval per sequence."""
+    import numpy as np
+    rng = np.random.default_rng(3)
+    for _ in range(50):
+        N = int(rng.integers(1, 20))
+        T = int(rng.integers(0, 5000))
+        cu = np.concatenate([[0], rng.integers(-100, T + 200, size=N)]).astype(np.int32)
+        interval = int(rng.choice([64, 128, 512]))
+        want, prev = 0, 0
+        for n in range(N):
+            x = min(max(int(cu[n + 1]), 0), T)
+            x = max(x, prev)
+            want += (x - prev) // interval
+            prev = x
+        assert kda.kda_checkpoint_count(cu, T, interval) == want
+    assert kda.kda_checkpoint_count(None, 8192, 512) == 16
+    assert L.kda_checkpoint_count(None, 0, 10, 64) == -1
+    assert L.kda_checkpoint_count(None, 1, 10, 0) == -1
+
+
+def test_prefill_ckpt_validation(L):
+    T, N, H, dk, dv = 256, 1, 2, 64, 64
+    need = kda.kda_prefill_workspace_size(T, N, H, dk, dv)
+
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE + (1 << 20), v=FAKE + (2 << 20), g=FAKE + (3 << 20),
+                 beta=FAKE + (4 << 20), cu=None, N=N, T=T, H=H, dk=dk, dv=dv, chunk=64,
+                 init=None, fin=FAKE + (8 << 20), o=FAKE + (16 << 20), dt=BF16,
+                 ws=FAKE + (32 << 20), wsb=need, iv=64, ck=FAKE + (64 << 20), cap=4)
+        a.update(kw)
+        return L.kda_prefill_ckpt(a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu"], a["N"], a["T"],
+                                  a["H"], a["dk"], a["dv"], a["chunk"], a["init"], a["fin"], a["o"],
+                                  a["dt"], a["ws"], a["wsb"], a["iv"], a["ck"], a["cap"], None)
+
+    assert call(iv=0) == 1
+    assert call(iv=100) == 1                                  # not a multiple of 64
+    assert call(cap=-1) == 1
+    assert call(ck=None) == 1                                 # capacity without a buffer
+    assert call(ck=FAKE + (16 << 20)) == 1                    # overlaps o
+    assert call(ck=FAKE + (2 << 20)) == 1                     # overlaps v
+    assert call(ck=FAKE + (64 << 20) + 2) == 1                # misaligned
+    assert call(dk=96) == 2                                   # prefill checks still apply
