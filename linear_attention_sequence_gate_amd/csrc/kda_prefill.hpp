@@ -623,8 +623,9 @@ __device__ __forceinline__ void prep_load(PrepRegs<C, DT>& r, const PrefillDev& 
 // Prep stage of the beta step: every state-independent tile of one block from
 // the registers.  A thread owns channels 2c, 2c+1 over a run of TPT tokens;
 // the runs of one channel pair sit in one wave (lanes cpl + CPW * part), so the
-// running sum of g across runs is a lane scan.  Log-decays are kept in the
-// log2 domain; R_a is G before sub-tile a (R_0 = 0) and E_a = G at its end.
+// running sum of g across runs is a lane scan.  Sums are kept in natural-log
+// units and scaled to log2 once, inside the exponent's FMA; R_a is G before
+// sub-tile a (R_0 = 0).
 template <typename C, typename DT, bool SUMMARY>
 __device__ __forceinline__ void prep_tiles(const PrepRegs<C, DT>& r, unsigned char* smem, int buf, int len,
                                            int lane, int ptid, int cpair, int part, int tok0, PhaseClock& pclk)
@@ -644,15 +645,17 @@ __device__ __forceinline__ void prep_tiles(const PrepRegs<C, DT>& r, unsigned ch
     float* sB = reinterpret_cast<float*>(smem + C::O_B) + buf * BC;
     const int pc = pcol(2 * cpair);
 
-    float g0[C::TPT], g1[C::TPT];
+    // inclusive running sums of g inside the run (natural log units; rows at
+    // or past the valid length add nothing)
+    float c0[C::TPT], c1[C::TPT];
     float s0 = 0.f, s1 = 0.f;
 #pragma unroll
     for (int i = 0; i < C::TPT; ++i) {
         const bool ok = tok0 + i < len;
-        g0[i] = ok ? O::p0(r.g[i]) * LOG2E : 0.f;
-        g1[i] = ok ? O::p1(r.g[i]) * LOG2E : 0.f;
-        s0 += g0[i];
-        s1 += g1[i];
+        s0 += ok ? O::p0(r.g[i]) : 0.f;
+        s1 += ok ? O::p1(r.g[i]) : 0.f;
+        c0[i] = s0;
+        c1[i] = s1;
     }
     pclk.mark(7);
     // running sums across the runs of this channel pair (lanes cpl + CPW * part):
@@ -676,21 +679,24 @@ __device__ __forceinline__ void prep_tiles(const PrepRegs<C, DT>& r, unsigned ch
         GL1 += p1;
     }
     const bool hi = tok0 >= 16;  // sub-tile of the run
-    const float ra0 = hi ? R10 : 0.f, ra1 = hi ? R11 : 0.f;
-    const float ea0 = hi ? GL0 : R10, ea1 = hi ? GL1 : R11;
-    const float er0 = fexp2(ra0), er1 = fexp2(ra1);  // e^{R_a}
-    // e^{G_last - R_a} = e^{E_a - R_a} (>= e^-80) e^{G_last - E_a} (<= 1); the
-    // product may be denormal, which fp32 multiplies keep
-    const float fe0 = fexp2(ea0 - ra0) * fexp2(GL0 - ea0);
-    const float fe1 = fexp2(ea1 - ra1) * fexp2(GL1 - ea1);
+    // e^{R_1} and e^{G_last - R_1}, each in [e^-80, 1]; every other factor is
+    // one of them or their product:  e^{R_a} = 1 or e^{R_1},  e^{G_last} =
+    // e^{R_1} e^{G_last - R_1},  e^{G_last - R_a} = e^{G_last} or e^{G_last - R_1}.
+    // A product may be denormal or flush to zero, which only ever scales terms
+    // bounded by 1.
+    const float ya0 = fexp2(R10 * LOG2E), ya1 = fexp2(R11 * LOG2E);
+    const float za0 = fexp2((GL0 - R10) * LOG2E), za1 = fexp2((GL1 - R11) * LOG2E);
+    const float er0 = hi ? ya0 : 1.f, er1 = hi ? ya1 : 1.f;  // e^{R_a}
+    const float gc0 = ya0 * za0, gc1 = ya1 * za1;            // e^{G_last}
+    const float fe0 = hi ? za0 : gc0, fe1 = hi ? za1 : gc1;  // e^{G_last - R_a}
+    // log2 of e^{G - R_a} = (G before the run - R_a + running sum) log2(e)
+    const float off0 = (G0 - (hi ? R10 : 0.f)) * LOG2E, off1 = (G1 - (hi ? R11 : 0.f)) * LOG2E;
     pclk.mark(8);
     float kh0[C::TPT], kh1[C::TPT];
 #pragma unroll
     for (int i = 0; i < C::TPT; ++i) {
         const int t = tok0 + i;
-        G0 += g0[i];
-        G1 += g1[i];
-        const float d0 = G0 - ra0, d1 = G1 - ra1;
+        const float d0 = __builtin_fmaf(c0[i], LOG2E, off0), d1 = __builtin_fmaf(c1[i], LOG2E, off1);
         const float e1a = fexp2(d0), e1b = fexp2(d1);    // e^{G - R_a} in [e^-80, 1]
         const float e2a = fexp2(-d0), e2b = fexp2(-d1);  // e^{R_a - G} in [1, e^80]
         const float ga = e1a * er0, gb = e1b * er1;      // e^{G}
@@ -726,8 +732,8 @@ __device__ __forceinline__ void prep_tiles(const PrepRegs<C, DT>& r, unsigned ch
     }
     if (part == 0) {
         f32x2* vv = reinterpret_cast<f32x2*>(sVec);
-        vv[(V_YS * DK + pc) / 2] = f32x2{fexp2(R10), fexp2(R11)};
-        vv[((V_GC + buf) * DK + pc) / 2] = f32x2{fexp2(GL0), fexp2(GL1)};
+        vv[(V_YS * DK + pc) / 2] = f32x2{ya0, ya1};
+        vv[((V_GC + buf) * DK + pc) / 2] = f32x2{gc0, gc1};
     }
     if (ptid < BC) {
         float bv;
