@@ -1077,15 +1077,19 @@ prefill_block_kernel(PrefillDev p)
             if (pos % p.ckpt_interval == 0) {
                 const int64_t idx = int64_t(p.tab[3 * (p.N + 1) + n]) + pos / p.ckpt_interval - 1;
                 if (idx < p.ckpt_cap) {
-                    float* dst = p.ckpt + (idx * H + h) * DK * DV;
+                    // one lane pointer, formed here: hoisted out of the block
+                    // loop, the 64 element addresses would live in (spilled)
+                    // registers for the whole segment
+                    uint32_t eo = uint32_t(4 * q4 * DV + colbase + l16);
+                    asm volatile("" : "+v"(eo));
+                    float* dst = p.ckpt + (idx * H + h) * DK * DV + eo;
 #pragma unroll
                     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
                         for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
                             for (int j = 0; j < 4; ++j)
-                                __builtin_nontemporal_store(S[rt][ct][j],
-                                                            dst + (rt * 16 + 4 * q4 + j) * DV + colbase + ct * 16 + l16);
+                                __builtin_nontemporal_store(S[rt][ct][j], dst + (rt * 16 + j) * DV + ct * 16);
                 }
             }
         }
