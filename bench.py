@@ -6,8 +6,9 @@ Prints ONE JSON line.  `value` is prefill throughput on the 8K-token workload
 over one batch of seeded synthetic inputs already resident in HBM (three input
 sets are rotated so the 256 MB last-level cache cannot hold a step's working
 set).  The decode leg (B=256, H=32, 1000 consecutive in-place steps) is
-reported under "decode".  `roofline` covers the prefill call (HIP-event
-duration of each kda_prefill on its stream, algorithmic bytes per call);
+reported under "decode".  `roofline` covers the prefill call (mean duration
+of back-to-back kda_prefill calls bracketed by two HIP events on the stream the
+library launches on; algorithmic bytes per call);
 `cpu_baseline` is the fp64 oracle timed on this host on a bounded sample.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps D]
@@ -148,15 +149,27 @@ def main():
     wbytes = kda.kda_prefill_workspace_size(T, 1, H, dk, dv)
     ws = torch.empty(max(wbytes, 1), dtype=torch.uint8, device=dev)
 
-    def step(i, ev=None):
+    def prefill(i):
         d = sets[i % 3]
-        kda.kda_gate(d["z"], A, g=d["g"])
-        if ev is not None:
-            ev[0].record(stream)
         kda.kda_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], final_state=d["S"], o=d["o"],
                         workspace=ws)
-        if ev is not None:
-            ev[1].record(stream)
+
+    def step(i):
+        d = sets[i % 3]
+        kda.kda_gate(d["z"], A, g=d["g"])
+        prefill(i)
+
+    def timed_loop(fn, n):
+        """Mean ms per call of n back-to-back calls fn(i), bracketed by two events
+        on the stream the library launches on (no event between calls)."""
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
 
     # bring the GPU to its steady clocks first (untimed): a fresh device runs
     # the first few hundred microsecond-scale launches at ramping clocks
@@ -171,25 +184,16 @@ def main():
         step(i)
     torch.cuda.synchronize()
     ref_sum = float(sets[0]["o"].float().abs().sum())
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for i in range(args.steps):
-        step(i, evs[i])
-    end.record(stream)
-    torch.cuda.synchronize()
+    ms_step = timed_loop(step, args.steps)  # the timed region: K whole steps
     wall = time.perf_counter() - t0
-    total_ms = start.elapsed_time(end)
-    ms_step = total_ms / args.steps
-    prefill_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    total_ms = ms_step * args.steps
     # the timed runs produce the verified run's result (no caching, same inputs)
     step(0)
     torch.cuda.synchronize()
     assert abs(float(sets[0]["o"].float().abs().sum()) - ref_sum) <= 1e-6 * max(ref_sum, 1.0)
+    # duration of one kda_prefill call (the roofline's unit), same inputs, no gate between
+    prefill_ms = timed_loop(prefill, args.steps)
 
     p_bytes, p_flops = prefill_algo(T, H, dk, dv)
     achieved = p_bytes / (prefill_ms * 1e-3) / 1e9
@@ -204,18 +208,14 @@ def main():
     # prefill with state checkpoints every 512 tokens (prefix-cache emission)
     n_ck = kda.kda_checkpoint_count(None, T, 512)
     ck = torch.empty((n_ck, H, dk, dv), dtype=torch.float32, device=dev)
-    cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    for i in range(args.warmup + args.steps):
+    def prefill_ckpt(i):
         d = sets[i % 3]
-        if i >= args.warmup:
-            cev[i - args.warmup][0].record(stream)
         kda.kda_prefill_ckpt(d["q"], d["k"], d["v"], d["g"], d["beta"], 512, ckpt=ck, final_state=d["S"],
                              o=d["o"], workspace=ws)
-        if i >= args.warmup:
-            cev[i - args.warmup][1].record(stream)
-    torch.cuda.synchronize()
-    ck_ms = float(np.mean([a.elapsed_time(b) for a, b in cev]))
+
+    for i in range(args.warmup):
+        prefill_ckpt(i)
+    ck_ms = timed_loop(prefill_ckpt, args.steps)
     ckpt_leg = {"interval": 512, "checkpoints_per_call": n_ck * H, "ms_per_call": round(ck_ms, 4),
                 "overhead_vs_plain": round(ck_ms / prefill_ms - 1.0, 4),
                 "checkpoint_bytes_per_call": n_ck * H * dk * dv * 4}

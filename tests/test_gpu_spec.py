@@ -51,10 +51,11 @@ CASES = [(32, 32, "bf16"), (64, 128, "bf16"), (128, 64, "bf16"), (128, 128, "bf1
          (32, 64, "f32")]
 
 
+@pytest.mark.parametrize("K", [3, 5, 12])
 @pytest.mark.parametrize("dk,dv,dtype", CASES)
-def test_verify_and_commit_small(kda, dk, dv, dtype):
+def test_verify_and_commit_small(kda, dk, dv, dtype, K):
     import torch
-    B, K = 6, 5
+    B = 6
     wl = synth.VERIFY_B256_K4.with_(H=3, dk=dk, dv=dv, dtype=dtype)
     announce(f"verify/commit B={B} K={K} H=3 dk={dk} dv={dv} {dtype}")
     x, g, S0 = inputs(wl, B, K)
