@@ -13,6 +13,7 @@
 #include "kda_gate.hpp"
 #include "kda_prefill.hpp"
 #include "kda_spec.hpp"
+#include "kda_step.hpp"
 
 namespace {
 
@@ -93,6 +94,15 @@ kda_status_t kda_gate(const void* z, const float* A, void* g, int64_t n_tokens, 
     return from_hip(e, "kda_gate launch");
 }
 
+// the one-wave step kernels take 16-byte aligned token tensors and one
+// workgroup per 32-column slice of each (b, h) state; otherwise the
+// workgroup-per-state kernels run (scalar token loads)
+static bool step_wave_ok(const void* q, const void* k, const void* v, const void* g, const void* o, int B, int H,
+                         int d_v)
+{
+    return kda::step_wave_aligned(q, k, v, g, o) && int64_t(B) * H * (d_v / 32) <= 0x7fffffff;
+}
+
 kda_status_t kda_decode_step(const void* q, const void* k, const void* v, const void* g,
                              const void* beta, float* state, void* o, int B, int H, int d_k,
                              int d_v, kda_dtype_t dtype, void* stream)
@@ -124,9 +134,15 @@ kda_status_t kda_decode_step(const void* q, const void* k, const void* v, const 
     if (overlap(o, nv, state, ns))
         return fail(KDA_ERR_INVALID_ARGUMENT, "kda_decode_step: o aliases the state");
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = dtype == KDA_BF16
-                       ? kda::launch_decode<kda::BF16>(q, k, v, g, beta, state, o, B * H, d_k, d_v, s)
-                       : kda::launch_decode<kda::F32>(q, k, v, g, beta, state, o, B * H, d_k, d_v, s);
+    hipError_t e;
+    if (step_wave_ok(q, k, v, g, o, B, H, d_v))
+        e = dtype == KDA_BF16
+                ? kda::launch_step_wave<kda::BF16>(0, q, k, v, g, beta, nullptr, state, o, B, 1, H, d_k, d_v, s)
+                : kda::launch_step_wave<kda::F32>(0, q, k, v, g, beta, nullptr, state, o, B, 1, H, d_k, d_v, s);
+    else
+        e = dtype == KDA_BF16
+                ? kda::launch_decode<kda::BF16>(q, k, v, g, beta, state, o, B * H, d_k, d_v, s)
+                : kda::launch_decode<kda::F32>(q, k, v, g, beta, state, o, B * H, d_k, d_v, s);
     return from_hip(e, "kda_decode_step launch");
 }
 
@@ -180,9 +196,15 @@ kda_status_t kda_verify(const void* q, const void* k, const void* v, const void*
     if (st != KDA_OK || noop) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     float* S = const_cast<float*>(state);  // read only in verify mode
-    hipError_t e = dtype == KDA_BF16
-                       ? kda::launch_spec<kda::BF16>(q, k, v, g, beta, nullptr, S, o, B, K, H, d_k, d_v, false, s)
-                       : kda::launch_spec<kda::F32>(q, k, v, g, beta, nullptr, S, o, B, K, H, d_k, d_v, false, s);
+    hipError_t e;
+    if (step_wave_ok(q, k, v, g, o, B, H, d_v))
+        e = dtype == KDA_BF16
+                ? kda::launch_step_wave<kda::BF16>(1, q, k, v, g, beta, nullptr, S, o, B, K, H, d_k, d_v, s)
+                : kda::launch_step_wave<kda::F32>(1, q, k, v, g, beta, nullptr, S, o, B, K, H, d_k, d_v, s);
+    else
+        e = dtype == KDA_BF16
+                ? kda::launch_spec<kda::BF16>(q, k, v, g, beta, nullptr, S, o, B, K, H, d_k, d_v, false, s)
+                : kda::launch_spec<kda::F32>(q, k, v, g, beta, nullptr, S, o, B, K, H, d_k, d_v, false, s);
     return from_hip(e, "kda_verify launch");
 }
 
@@ -195,11 +217,17 @@ kda_status_t kda_commit(const void* k, const void* v, const void* g, const void*
                                  d_k, d_v, dtype, &noop);
     if (st != KDA_OK || noop) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = dtype == KDA_BF16
-                       ? kda::launch_spec<kda::BF16>(nullptr, k, v, g, beta, n_accept, state, nullptr, B, K, H,
-                                                     d_k, d_v, true, s)
-                       : kda::launch_spec<kda::F32>(nullptr, k, v, g, beta, n_accept, state, nullptr, B, K, H,
-                                                    d_k, d_v, true, s);
+    hipError_t e;
+    if (step_wave_ok(nullptr, k, v, g, nullptr, B, H, d_v))
+        e = dtype == KDA_BF16 ? kda::launch_step_wave<kda::BF16>(2, nullptr, k, v, g, beta, n_accept, state,
+                                                                 nullptr, B, K, H, d_k, d_v, s)
+                              : kda::launch_step_wave<kda::F32>(2, nullptr, k, v, g, beta, n_accept, state,
+                                                                nullptr, B, K, H, d_k, d_v, s);
+    else
+        e = dtype == KDA_BF16 ? kda::launch_spec<kda::BF16>(nullptr, k, v, g, beta, n_accept, state, nullptr, B,
+                                                            K, H, d_k, d_v, true, s)
+                              : kda::launch_spec<kda::F32>(nullptr, k, v, g, beta, n_accept, state, nullptr, B, K,
+                                                           H, d_k, d_v, true, s);
     return from_hip(e, "kda_commit launch");
 }
 

@@ -19,6 +19,18 @@ def dev(x: np.ndarray, dtype: str = "f32"):
     return t.to(torch_dtype(dtype)) if dtype == "bf16" else t
 
 
+def dev_unaligned(t):
+    """The same values in a contiguous device tensor whose data starts one
+    element past a 16-byte boundary (exercises the kernels for unaligned
+    token tensors)."""
+    import torch
+    flat = torch.empty(t.numel() + 8, dtype=t.dtype, device=t.device)
+    out = flat[1:1 + t.numel()].view(t.shape)
+    out.copy_(t)
+    assert out.data_ptr() % 16 != 0
+    return out
+
+
 def host(t) -> np.ndarray:
     import torch
     return t.detach().to(torch.float64).cpu().numpy()

@@ -4,7 +4,7 @@ import pytest
 
 import oracle
 import synth
-from tests.gpu_common import TOL, announce, dev, host, relerr
+from tests.gpu_common import TOL, announce, dev, dev_unaligned, host, relerr
 
 pytestmark = pytest.mark.gpu
 
@@ -68,20 +68,23 @@ def _decode_inputs(wl, set_index, B):
     return d
 
 
+@pytest.mark.parametrize("unaligned", [False, True])  # one-wave slice kernel / workgroup-per-state kernel
 @pytest.mark.parametrize("dk,dv,dtype", [(128, 128, "bf16"), (64, 32, "bf16"), (32, 128, "bf16"),
                                          (32, 32, "f32"), (128, 64, "f32")])
-def test_decode_small(kda, dk, dv, dtype):
+def test_decode_small(kda, dk, dv, dtype, unaligned):
     import torch
     wl = synth.DECODE_B256.with_(H=3, dk=dk, dv=dv, dtype=dtype, seqlens=(1,) * 5)
-    announce(f"decode small dk={dk} dv={dv} {dtype}")
+    announce(f"decode small dk={dk} dv={dv} {dtype} unaligned={unaligned}")
     B = 5
     x = _decode_inputs(wl, 0, B)
     A = synth.gate_A(wl)
     S0 = synth.initial_state(wl)
     St = dev(S0)
     g = kda.kda_gate(dev(x["z"], dtype), dev(A))
-    o = kda.kda_decode_step(dev(x["q"], dtype), dev(x["k"], dtype), dev(x["v"], dtype), g,
-                            dev(x["beta"], dtype), St)
+    q = dev(x["q"], dtype)
+    if unaligned:
+        q = dev_unaligned(q)
+    o = kda.kda_decode_step(q, dev(x["k"], dtype), dev(x["v"], dtype), g, dev(x["beta"], dtype), St)
     gr = oracle.gate(x["z"], A, round_bf16=(dtype == "bf16"))
     o_ref, S_ref = oracle.decode_step(x["q"], x["k"], x["v"], gr, x["beta"], S0)
     tol = TOL[dtype]

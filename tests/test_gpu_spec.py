@@ -7,7 +7,7 @@ import pytest
 
 import oracle
 import synth
-from tests.gpu_common import TOL, announce, dev, host, relerr
+from tests.gpu_common import TOL, announce, dev, dev_unaligned, host, relerr
 
 pytestmark = pytest.mark.gpu
 
@@ -51,15 +51,19 @@ CASES = [(32, 32, "bf16"), (64, 128, "bf16"), (128, 64, "bf16"), (128, 128, "bf1
          (32, 64, "f32")]
 
 
-@pytest.mark.parametrize("K", [3, 5, 12])
+@pytest.mark.parametrize("K,unaligned", [(3, False), (5, False), (12, False), (5, True)])
 @pytest.mark.parametrize("dk,dv,dtype", CASES)
-def test_verify_and_commit_small(kda, dk, dv, dtype, K):
+def test_verify_and_commit_small(kda, dk, dv, dtype, K, unaligned):
+    """unaligned: token tensors off a 16-byte boundary, which the
+    workgroup-per-state kernels take instead of the one-wave slice kernels."""
     import torch
     B = 6
     wl = synth.VERIFY_B256_K4.with_(H=3, dk=dk, dv=dv, dtype=dtype)
-    announce(f"verify/commit B={B} K={K} H=3 dk={dk} dv={dv} {dtype}")
+    announce(f"verify/commit B={B} K={K} H=3 dk={dk} dv={dv} {dtype} unaligned={unaligned}")
     x, g, S0 = inputs(wl, B, K)
     t = to_dev(kda, wl, x, B, K)
+    if unaligned:
+        t = {n: dev_unaligned(a) for n, a in t.items()}
     state = dev(S0)
     before = state.clone()
     o = kda.kda_verify(t["q"], t["k"], t["v"], t["g"], t["beta"], state)
