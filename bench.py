@@ -6,9 +6,10 @@ Prints ONE JSON line.  `value` is prefill throughput on the 8K-token workload
 over one batch of seeded synthetic inputs already resident in HBM (three input
 sets are rotated so the 256 MB last-level cache cannot hold a step's working
 set).  The decode leg (B=256, H=32, 1000 consecutive in-place steps) is
-reported under "decode".  `roofline` covers the prefill call (mean duration
-of back-to-back kda_prefill calls bracketed by two HIP events on the stream the
-library launches on; algorithmic bytes per call);
+reported under "decode", and verify/commit (B=256, K=4) under "spec".  Every
+duration is the mean over back-to-back calls bracketed by two HIP events on
+the stream the library launches on (an event between calls would serialise
+them).  `roofline` covers the prefill call (algorithmic bytes per call);
 `cpu_baseline` is the fp64 oracle timed on this host on a bounded sample.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps D]
@@ -233,30 +234,19 @@ def main():
     state = torch.from_numpy(synth.initial_state(dwl)).to(dev)
     dout = torch.empty((B, dwl.H, dwl.dv), dtype=torch.bfloat16, device=dev)
 
-    def dstep(i, ev=None):
+    def dstep(i):
         d = dsets[i % 8]
         kda.kda_gate(d["z"], dA, g=d["g"])
-        if ev is not None:
-            ev[0].record(stream)
         kda.kda_decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], state, o=dout)
-        if ev is not None:
-            ev[1].record(stream)
 
-    for i in range(10):
+    def dcall(i):  # the decode kernel alone (g of every set is current after the warmup)
+        d = dsets[i % 8]
+        kda.kda_decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], state, o=dout)
+
+    for i in range(16):
         dstep(i)
-    torch.cuda.synchronize()
-    devs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in range(args.decode_steps)]
-    dstart = torch.cuda.Event(enable_timing=True)
-    dend = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    dstart.record(stream)
-    for i in range(args.decode_steps):
-        dstep(i, devs[i])
-    dend.record(stream)
-    torch.cuda.synchronize()
-    d_total_ms = dstart.elapsed_time(dend)
-    d_kernel_ms = float(np.mean([a.elapsed_time(b) for a, b in devs]))
+    d_total_ms = timed_loop(dstep, args.decode_steps) * args.decode_steps
+    d_kernel_ms = timed_loop(dcall, args.decode_steps)
     d_bytes, d_flops = decode_algo(B, dwl.H, dwl.dk, dwl.dv)
     d_ach = d_bytes / (d_kernel_ms * 1e-3) / 1e9
     decode = {"value": round(B * args.decode_steps / (d_total_ms * 1e-3), 1), "unit": "tokens/s",
@@ -265,7 +255,7 @@ def main():
                          "d_v": dwl.dv, "input_sets": 8},
               "roofline": {"bound": "hbm", "achieved": round(d_ach, 1), "peak": HBM_PEAK_GBS,
                            "unit": "GB/s", "frac": round(d_ach / HBM_PEAK_GBS, 4),
-                           "traffic": load_traffic("decode_b256"), "kernel": "decode_kernel",
+                           "traffic": load_traffic("decode_b256"), "kernel": "step_wave_kernel (decode)",
                            "algorithmic_bytes_per_call": d_bytes,
                            "ms_per_call": round(d_kernel_ms, 4)}}
 
@@ -290,18 +280,17 @@ def main():
         kda.kda_verify(d["q"], d["k"], d["v"], d["g"], d["beta"], sstate, o=sout)
         kda.kda_commit(d["k"], d["v"], d["g"], d["beta"], n_all, sstate)
     torch.cuda.synchronize()
-    vev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-            torch.cuda.Event(enable_timing=True)) for _ in range(spec_iters)]
-    for i in range(spec_iters):
+
+    def vcall(i):
         d = ssets[i % 4]
-        vev[i][0].record(stream)
         kda.kda_verify(d["q"], d["k"], d["v"], d["g"], d["beta"], sstate, o=sout)
-        vev[i][1].record(stream)
+
+    def ccall(i):
+        d = ssets[i % 4]
         kda.kda_commit(d["k"], d["v"], d["g"], d["beta"], n_all, sstate)
-        vev[i][2].record(stream)
-    torch.cuda.synchronize()
-    v_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in vev]))
-    c_ms = float(np.mean([b.elapsed_time(c) for _, b, c in vev]))
+
+    v_ms = timed_loop(vcall, spec_iters)
+    c_ms = timed_loop(ccall, spec_iters)
     vb = spec_algo(SB, K, swl.H, swl.dk, swl.dv, False)
     cb = spec_algo(SB, K, swl.H, swl.dk, swl.dv, True)
     spec = {"value": round(SB * K / ((v_ms + c_ms) * 1e-3), 1), "unit": "draft tokens/s (verify + commit)",
@@ -311,13 +300,13 @@ def main():
                        "roofline": {"bound": "hbm", "achieved": round(vb / (v_ms * 1e-3) / 1e9, 1),
                                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                     "frac": round(vb / (v_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                                    "traffic": load_traffic("verify_b256_k4"), "kernel": "spec_kernel (verify)",
+                                    "traffic": load_traffic("verify_b256_k4"), "kernel": "step_wave_kernel (verify)",
                                     "algorithmic_bytes_per_call": vb}},
             "commit": {"ms_per_call": round(c_ms, 4),
                        "roofline": {"bound": "hbm", "achieved": round(cb / (c_ms * 1e-3) / 1e9, 1),
                                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                     "frac": round(cb / (c_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                                    "traffic": load_traffic("commit_b256_k4"), "kernel": "spec_kernel (commit)",
+                                    "traffic": load_traffic("commit_b256_k4"), "kernel": "step_wave_kernel (commit)",
                                     "algorithmic_bytes_per_call": cb}}}
 
     if args.copy_calib:  # plain copy of known size, for the HBM counter calibration

@@ -271,6 +271,18 @@ __host__ __device__ constexpr int pcol(int c)
 {
     return (c & ~31) | (((c >> 2) & 3) << 3) | (((c >> 4) & 1) << 2) | (c & 3);
 }
+
+// Offset of 16x16 tile (rt, ct) of a [d_k][DV] fp32 state held in the
+// matrix-core accumulator layout: 64 lanes x 4 consecutive floats, lane
+// l16 + 16 q holding column 16 ct + l16, rows 16 rt + 4 q .. +3.  The
+// workspace keeps S~ and S_in this way, so each lane moves one 16-byte vector
+// per tile.
+template <int DV>
+__host__ __device__ constexpr int acc_tile_off(int rt, int ct, int lane)
+{
+    return ((rt * (DV / 16) + ct) * 64 + lane) * 4;
+}
+
 __device__ __forceinline__ int kperm(int q, int e) { return ((e >> 2) << 4) + (q << 2) + (e & 3); }
 
 // 2^x with the hardware instruction (about 1 ulp; results below the fp32
@@ -941,26 +953,30 @@ prefill_block_kernel(PrefillDev p)
     f32x4 S[RT][NCT];
     {
         const float* src = nullptr;
-        if (!SUMMARY) {
-            if (s == 0) {
-                if (p.init) src = p.init + (int64_t(n) * H + h) * DK * DV;
-            } else {
-                src = p.sin + (int64_t(seg_off[n] + s) * H + h) * DK * DV;
-            }
+        if (!SUMMARY && s == 0 && p.init) src = p.init + (int64_t(n) * H + h) * DK * DV;
+        if (!SUMMARY && s > 0) {
+            // S_in from the scan, in accumulator tiles
+            const float* tin = p.sin + (int64_t(seg_off[n] + s) * H + h) * DK * DV;
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct)
+                    S[rt][ct] = *reinterpret_cast<const f32x4*>(tin + acc_tile_off<DV>(rt, colbase / 16 + ct, lane));
+        } else {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int row = rt * 16 + 4 * q4 + j;
+                        const int col = colbase + ct * 16 + l16;
+                        float x = 0.f;
+                        if (mcols) x = (row == col - DV) ? 1.f : 0.f;
+                        else if (src) x = src[row * DV + col];
+                        S[rt][ct][j] = x;
+                    }
         }
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int row = rt * 16 + 4 * q4 + j;
-                    const int col = colbase + ct * 16 + l16;
-                    float x = 0.f;
-                    if (mcols) x = (row == col - DV) ? 1.f : 0.f;
-                    else if (src) x = src[row * DV + col];
-                    S[rt][ct][j] = x;
-                }
     }
     __syncthreads();
     KDA_PHASE(4);
@@ -1099,7 +1115,7 @@ prefill_block_kernel(PrefillDev p)
     }
 
     pclk.save(SUMMARY ? 8192 : 0);
-    // ---- write the segment result.  Summary pass: S~ as fp32 rows [d_k][d_v],
+    // ---- write the segment result.  Summary pass: S~ in fp32 accumulator tiles,
     // then M as two bf16 tiles (hi = bf16(M), lo = bf16(M - hi)) [d_k][d_k] with
     // the permuted column order of the operand tiles, ready as A operands of the
     // scan's split-precision products.
@@ -1110,9 +1126,7 @@ prefill_block_kernel(PrefillDev p)
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        base[(rt * 16 + 4 * q4 + j) * DV + colbase + ct * 16 + l16] = S[rt][ct][j];
+                    *reinterpret_cast<f32x4*>(base + acc_tile_off<DV>(rt, colbase / 16 + ct, lane)) = S[rt][ct];
         } else {
             // every other wave is past its last LDS access (final barrier above)
             uint16_t* mhi = reinterpret_cast<uint16_t*>(base + DK * DV);
@@ -1171,17 +1185,22 @@ prefill_block_kernel(PrefillDev p)
 }
 
 // ------------------------------------------------------------- scan kernel
-// Per (sequence, head, 32-column slice of the state):
+// Per (sequence, head, 16-column slice of the state):
 //     S_in(s+1) = M_s S_in(s) + S~_s
 // over the sequence's segments, on the matrix cores with fp32-level accuracy:
 // each fp32 operand x is split as hi = bf16(x), lo = bf16(x - hi) and the
 // product accumulates hi*hi + hi*lo + lo*hi in fp32.  The summary pass stores
-// M_s already split (hi and lo bf16 tiles, permuted columns).  Wave w owns
-// state row tiles w, w+4, ...: it needs only those rows of M_s, so it loads
-// their fragments straight from global memory into registers, one step ahead.
-// The S_in slice, which every wave reads whole, sits in LDS transposed and
-// split the same way, written once by the wave that computed it.
-constexpr int SCAN_COLS = 32;
+// M_s already split (hi and lo bf16 tiles, permuted columns) and S~_s in
+// accumulator tiles.  Wave w owns state row tiles w, w+4, ...: it needs only
+// those rows of M_s, so it loads their fragments straight from global memory
+// into registers, two steps ahead.  The S_in slice, which every wave reads
+// whole, sits in LDS transposed and split the same way, written once by the
+// wave that computed it.
+// The steps are bound by how fast one compute unit streams M_s in (all of it
+// per workgroup and step; about 40 GB/s per unit here), not by the products:
+// 16-column slices spread the sequence-head pairs over twice as many units as
+// 32-column ones, at the price of reading M_s eight times instead of four.
+constexpr int SCAN_COLS = 16;
 template <int DK, int DV>
 struct ScanCfg {
     static constexpr int SB = DK + 8;              // bf16 row stride of the S_in^T tiles in LDS
@@ -1202,6 +1221,8 @@ __global__ void __launch_bounds__(256) scan_kernel(PrefillDev p)
 {
     using SC = ScanCfg<DK, DV>;
     constexpr int NB = DV / SCAN_COLS;
+    constexpr int SCT = SCAN_COLS / 16;  // 16-wide column tiles of the slice
+    constexpr bool ALL_ROWS = (DK / 16) % 4 == 0;  // every wave owns RTW row tiles
     constexpr int KB = DK / 32;
     constexpr int RTW = SC::RTW;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -1235,7 +1256,11 @@ __global__ void __launch_bounds__(256) scan_kernel(PrefillDev p)
     pclk.on = tid == 0;
     pclk.last = clock64();
 #endif
-    auto ms_of = [&](int st) { return p.ms + (int64_t(p1_off[n] + st) * H + h) * DK * (DK + DV); };
+    // Table entries are read once, into registers: a re-read after the state
+    // stores below would wait for every load in flight, the prefetch included.
+    const float* const ms0 = p.ms + (int64_t(p1_off[n]) * H + h) * DK * (DK + DV);
+    float* const sin0 = p.sin + (int64_t(seg_off[n]) * H + h) * DK * DV;
+    auto ms_of = [&](int st) { return ms0 + int64_t(st) * H * DK * (DK + DV); };
 
     // S_in(0) slice: column j of the slice is row j of the tiles; state row k sits at pcol(k)
     for (int e = tid; e < SCAN_COLS * DK / 4; e += 256) {
@@ -1252,91 +1277,91 @@ __global__ void __launch_bounds__(256) scan_kernel(PrefillDev p)
         *reinterpret_cast<u32x2*>(sTl + j * SC::SB + pcol(k)) = lo;
     }
     // this wave's rows of M_st (A operands: hi and lo fragments) and of S~_st
-    // (accumulator layout)
-    bf16x8 mh[RTW][KB], ml[RTW][KB];
-    f32x4 stl[RTW][2];
-    auto load_step = [&](int st) {
+    // (accumulator layout), in two register sets: set st & 1 is loaded two
+    // steps before it is used, so the loads have two steps to land.
+    bf16x8 mh[2][RTW][KB], ml[2][RTW][KB];
+    f32x4 stl[2][RTW][SCT];
+    auto load_step = [&](const int set, int st) {
         const float* base = ms_of(st);
         const uint16_t* mhi = reinterpret_cast<const uint16_t*>(base + DK * DV);
         const uint16_t* mlo = mhi + DK * DK;
 #pragma unroll
         for (int i = 0; i < RTW; ++i) {
             const int rt = wave + 4 * i;
-            if (rt < DK / 16) {
+            if (ALL_ROWS || rt < DK / 16) {
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb) {
-                    mh[i][kb] = Op<BF16>::load(mhi + (rt * 16 + l16) * DK + kb * 32 + 8 * q4);
-                    ml[i][kb] = Op<BF16>::load(mlo + (rt * 16 + l16) * DK + kb * 32 + 8 * q4);
+                    mh[set][i][kb] = Op<BF16>::load(mhi + (rt * 16 + l16) * DK + kb * 32 + 8 * q4);
+                    ml[set][i][kb] = Op<BF16>::load(mlo + (rt * 16 + l16) * DK + kb * 32 + 8 * q4);
                 }
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        stl[i][ct][j] = base[(rt * 16 + 4 * q4 + j) * DV + col0 + ct * 16 + l16];
+                for (int ct = 0; ct < SCT; ++ct)
+                    stl[set][i][ct] = *reinterpret_cast<const f32x4*>(base + acc_tile_off<DV>(rt, col0 / 16 + ct, lane));
             }
         }
     };
-    load_step(0);
-    __syncthreads();
-    KDA_PHASE(0);
-    for (int s = 0; s + 1 < nseg; ++s) {
-        // take this step's fragments, then start loading the next step's into the same registers
-        bf16x8 ah[RTW][KB], al[RTW][KB];
-        f32x4 acc[RTW][2];
+    const int nsteps = nseg - 1;
+    // S_in(s + 1) = M_s S_in(s) + S~_s from register set `set`, which is then
+    // refilled with step s + 2
+    auto run_step = [&](const int set, int s) {
+        f32x4 acc[RTW][SCT];
 #pragma unroll
-        for (int i = 0; i < RTW; ++i) {
+        for (int i = 0; i < RTW; ++i)
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                ah[i][kb] = mh[i][kb];
-                al[i][kb] = ml[i][kb];
-            }
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct) acc[i][ct] = stl[i][ct];
-        }
-        if (s + 2 < nseg) load_step(s + 1);  // in flight during the products
+            for (int ct = 0; ct < SCT; ++ct) acc[i][ct] = stl[set][i][ct];
         KDA_PHASE(1);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-            bf16x8 bh[2], bl[2];
+            bf16x8 bh[SCT], bl[SCT];
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
+            for (int ct = 0; ct < SCT; ++ct) {
                 bh[ct] = Op<BF16>::load(sTh + (ct * 16 + l16) * SC::SB + kb * 32 + 8 * q4);
                 bl[ct] = Op<BF16>::load(sTl + (ct * 16 + l16) * SC::SB + kb * 32 + 8 * q4);
             }
 #pragma unroll
             for (int i = 0; i < RTW; ++i) {
-                if (wave + 4 * i < DK / 16) {
+                if (ALL_ROWS || wave + 4 * i < DK / 16) {
 #pragma unroll
-                    for (int ct = 0; ct < 2; ++ct) {
-                        Op<BF16>::mma(acc[i][ct], ah[i][kb], bh[ct]);
-                        Op<BF16>::mma(acc[i][ct], ah[i][kb], bl[ct]);
-                        Op<BF16>::mma(acc[i][ct], al[i][kb], bh[ct]);
+                    for (int ct = 0; ct < SCT; ++ct) {
+                        Op<BF16>::mma(acc[i][ct], mh[set][i][kb], bh[ct]);
+                        Op<BF16>::mma(acc[i][ct], mh[set][i][kb], bl[ct]);
+                        Op<BF16>::mma(acc[i][ct], ml[set][i][kb], bh[ct]);
                     }
                 }
             }
         }
+        // unconditional (the last steps re-read step nsteps - 1), so the two
+        // register sets never merge with their old values at the loop head
+        load_step(set, s + 2 < nsteps ? s + 2 : nsteps - 1);
         KDA_PHASE(2);
         __syncthreads();  // every wave is done reading the S_in tiles
         KDA_PHASE(3);
-        float* out = p.sin + (int64_t(seg_off[n] + s + 1) * H + h) * DK * DV;
+        float* out = sin0 + int64_t(s + 1) * H * DK * DV;
 #pragma unroll
         for (int i = 0; i < RTW; ++i) {
             const int rt = wave + 4 * i;
-            if (rt < DK / 16) {
+            if (ALL_ROWS || rt < DK / 16) {
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct) {
+                for (int ct = 0; ct < SCT; ++ct) {
                     const int j = ct * 16 + l16;
                     u32x2 hi, lo;
                     split4(acc[i][ct], hi, lo);  // state rows rt*16 + 4q .. +3: contiguous under pcol
                     *reinterpret_cast<u32x2*>(sTh + j * SC::SB + pcol(rt * 16 + 4 * q4)) = hi;
                     *reinterpret_cast<u32x2*>(sTl + j * SC::SB + pcol(rt * 16 + 4 * q4)) = lo;
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) out[(rt * 16 + 4 * q4 + jj) * DV + col0 + j] = acc[i][ct][jj];
+                    *reinterpret_cast<f32x4*>(out + acc_tile_off<DV>(rt, col0 / 16 + ct, lane)) = acc[i][ct];
                 }
             }
         }
         __syncthreads();  // the new S_in slice is complete
         KDA_PHASE(4);
+    };
+    load_step(0, 0);
+    load_step(1, nsteps > 1 ? 1 : 0);
+    __syncthreads();
+    KDA_PHASE(0);
+    for (int s = 0; s < nsteps; s += 2) {
+        run_step(0, s);
+        if (s + 1 < nsteps) run_step(1, s + 1);
     }
     pclk.save(12288);
 }
