@@ -6,11 +6,14 @@ Prints ONE JSON line.  `value` is prefill throughput on the 8K-token workload
 over one batch of seeded synthetic inputs already resident in HBM (three input
 sets are rotated so the 256 MB last-level cache cannot hold a step's working
 set).  The decode leg (B=256, H=32, 1000 consecutive in-place steps) is
-reported under "decode", and verify/commit (B=256, K=4) under "spec".  Every
+reported under "decode", and verify/commit (B=256, K=4) under "speculative".  Every
 duration is the mean over back-to-back calls bracketed by two HIP events on
 the stream the library launches on (an event between calls would serialise
 them).  `roofline` covers the prefill call (algorithmic bytes per call);
-`cpu_baseline` is the fp64 oracle timed on this host on a bounded sample.
+each roofline also carries the fraction of a plain 1 GiB device copy measured
+on the same device.  `cpu_baseline` is the fp64 oracle timed on this host on a
+bounded sample; `verified` compares the timed run's output with that oracle
+pass (whole workload, normwise max relative error).
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps D]
                   [--no-cpu] [--copy-calib] [--spin-up SECONDS]
@@ -90,23 +93,36 @@ def spec_algo(B: int, K: int, H: int, dk: int, dv: int, commit: bool):
 def cpu_baseline(wl, seconds: float = 12.0):
     """The fp64 oracle on this host over the whole 8K workload (every head,
     every token), repeated until at least `seconds` of CPU time have passed;
-    tokens/s of the full problem."""
+    tokens/s of the full problem.  Also returns the first pass's (o, S): the
+    oracle's result for input set 0 (bf16-rounded inputs, as the GPU holds
+    them), against which the timed run's output is checked."""
     import oracle
     import synth
     threads = oracle.default_threads()
     x = synth.prefill_inputs(wl)
+    for n in ("q", "k", "v", "z", "beta"):
+        x[n] = oracle.round_bf16(x[n])
     g = oracle.gate(x["z"], x["A"], round_bf16=True)
-    reps, t0 = 0, time.perf_counter()
+    reps, first, t0 = 0, None, time.perf_counter()
     while True:
-        oracle.prefill(x["q"], x["k"], x["v"], g, x["beta"], threads=threads)
+        res = oracle.prefill(x["q"], x["k"], x["v"], g, x["beta"], threads=threads)
+        first = first or res
         reps += 1
         dt = time.perf_counter() - t0
         if dt >= seconds:
             break
-    return {"value": round(reps * wl.T_total / dt, 1), "unit": "tokens/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"fp64 token-serial oracle on the whole 8K workload ({wl.H} heads x "
-                      f"{wl.T_total} tokens), {reps} passes in {dt:.1f} s"}
+    return ({"value": round(reps * wl.T_total / dt, 1), "unit": "tokens/s", "cores": threads,
+             "kind": "oracle",
+             "sample": f"fp64 token-serial oracle on the whole 8K workload ({wl.H} heads x "
+                       f"{wl.T_total} tokens), {reps} passes in {dt:.1f} s"}, first)
+
+
+def max_rel_err(got, want) -> float:
+    """Normwise max relative error, max|got - want| / max|want|."""
+    import numpy as np
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    return float(np.max(np.abs(got - want)) / max(float(np.max(np.abs(want))), 1e-300))
 
 
 def main():
@@ -193,6 +209,8 @@ def main():
     step(0)
     torch.cuda.synchronize()
     assert abs(float(sets[0]["o"].float().abs().sum()) - ref_sum) <= 1e-6 * max(ref_sum, 1.0)
+    o_timed = sets[0]["o"].float().cpu().numpy()
+    S_timed = sets[0]["S"].cpu().numpy()
     # duration of one kda_prefill call (the roofline's unit), same inputs, no gate between
     prefill_ms = timed_loop(prefill, args.steps)
 
@@ -309,6 +327,19 @@ def main():
                                     "traffic": load_traffic("commit_b256_k4"), "kernel": "step_wave_kernel (commit)",
                                     "algorithmic_bytes_per_call": cb}}}
 
+    # achievable HBM bandwidth on this device: a plain 1 GiB device-to-device
+    # copy (2 GiB moved per copy), for fractions against a measured roof too
+    csrc = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    cdst = torch.empty_like(csrc)
+    for _ in range(3):
+        cdst.copy_(csrc)
+    copy_ms = timed_loop(lambda i: cdst.copy_(csrc), 10)
+    copy_gbs = 2.0 * (1 << 30) / (copy_ms * 1e-3) / 1e9
+    del csrc, cdst
+    for r in (roofline, decode["roofline"], spec["verify"]["roofline"], spec["commit"]["roofline"]):
+        r["measured_copy_gbs"] = round(copy_gbs, 1)
+        r["frac_of_measured_copy"] = round(r["achieved"] / copy_gbs, 4)
+
     if args.copy_calib:  # plain copy of known size, for the HBM counter calibration
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -316,7 +347,12 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
 
-    cpu = None if args.no_cpu else cpu_baseline(wl)
+    cpu, verified = None, None
+    if not args.no_cpu:
+        cpu, (o_ref, S_ref) = cpu_baseline(wl)
+        verified = {"against": "fp64 oracle on input set 0 (bf16-rounded inputs), whole workload",
+                    "o_max_rel_err": max_rel_err(o_timed, o_ref),
+                    "final_state_max_rel_err": max_rel_err(S_timed, S_ref), "tolerance": 2e-2}
     tok_s = T * args.steps / (total_ms * 1e-3)
     out = {"metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
@@ -325,7 +361,8 @@ def main():
            "config": {"workload": "prefill_8k: gate + chunked prefill, B=1 H=32 T=8192 "
                                   "d_k=d_v=128 chunk=64, zero initial state",
                       "B": 1, "H": H, "T": T, "d_k": dk, "d_v": dv, "chunk": 64, "input_sets": 3},
-           "roofline": roofline, "cpu_baseline": cpu, "checkpoints": ckpt_leg, "decode": decode,
+           "roofline": roofline, "cpu_baseline": cpu, "verified": verified, "checkpoints": ckpt_leg,
+           "decode": decode,
            "speculative": spec,
            "wall_s": round(wall, 3), "source_hash": kernel_source_hash()}
     print(json.dumps(out), flush=True)
