@@ -155,7 +155,31 @@ struct PrefillDev {
     float* ckpt;  // [ckpt_cap][H][dk][dv] or null
     int ckpt_interval;
     int64_t ckpt_cap;
+    // One sequence without cu_seqlens: the table is [0, T] | [0, nseg] |
+    // [0, nseg - 1] | [0, nck], known on the host and carried here, so no
+    // plan launch is needed.
+    int single;
+    int single_nseg;
+    int single_nck;
 };
+
+// Table entries (cu_seqlens clamped, segment, pass-1 and checkpoint offsets)
+__device__ __forceinline__ int32_t tab_cu(const PrefillDev& p, int n)
+{
+    return p.single ? (n ? int32_t(p.T_total) : 0) : p.tab[n];
+}
+__device__ __forceinline__ int32_t tab_seg(const PrefillDev& p, int n)
+{
+    return p.single ? (n ? p.single_nseg : 0) : p.tab[(p.N + 1) + n];
+}
+__device__ __forceinline__ int32_t tab_p1(const PrefillDev& p, int n)
+{
+    return p.single ? (n ? p.single_nseg - 1 : 0) : p.tab[2 * (p.N + 1) + n];
+}
+__device__ __forceinline__ int32_t tab_ck(const PrefillDev& p, int n)
+{
+    return p.single ? (n ? p.single_nck : 0) : p.tab[3 * (p.N + 1) + n];
+}
 
 // ------------------------------------------------------------- plan kernel
 // One workgroup: clamps cu_seqlens into a non-decreasing sequence inside
@@ -882,20 +906,22 @@ prefill_block_kernel(PrefillDev p)
     const int H = p.H;
     const int item = blockIdx.x / H;
     const int h = blockIdx.x % H;
-    const int32_t* cuc = p.tab;
-    const int32_t* seg_off = p.tab + (p.N + 1);
-    const int32_t* off = SUMMARY ? p.tab + 2 * (p.N + 1) : seg_off;
-    if (item >= off[p.N]) return;
-    const int n = find_seq(off, p.N, item);
-    const int s = item - off[n];
-    const int nseg = seg_off[n + 1] - seg_off[n];
-    const int64_t seq0 = cuc[n], seq1 = cuc[n + 1];
+    auto off = [&](int i) { return SUMMARY ? tab_p1(p, i) : tab_seg(p, i); };
+    if (item >= off(p.N)) return;
+    const int n = p.single ? 0 : find_seq(p.tab + (SUMMARY ? 2 : 1) * (p.N + 1), p.N, item);
+    const int s = item - off(n);
+    const int seg0 = tab_seg(p, n);
+    const int nseg = tab_seg(p, n + 1) - seg0;
+    const int64_t seq0 = tab_cu(p, n), seq1 = tab_cu(p, n + 1);
     const int64_t t_begin = seq0 + int64_t(s) * p.L * CH;
     int64_t t_end = t_begin + int64_t(p.L) * CH;
     if (t_end > seq1) t_end = seq1;
     const bool last_seg = (s == nseg - 1);
     const int64_t nblk = (t_end - t_begin + BC - 1) / BC;
     ST* go = static_cast<ST*>(p.o);
+    // first checkpoint slot of this sequence, read before the block loop (a
+    // table read inside it would wait for every store in flight)
+    const int64_t ck_first = (!SUMMARY && p.ckpt) ? int64_t(tab_ck(p, n)) : 0;
 
     // strictly-upper 16x16 block of P: read by the P U product, never written
     if (!SUMMARY)
@@ -956,7 +982,7 @@ prefill_block_kernel(PrefillDev p)
         if (!SUMMARY && s == 0 && p.init) src = p.init + (int64_t(n) * H + h) * DK * DV;
         if (!SUMMARY && s > 0) {
             // S_in from the scan, in accumulator tiles
-            const float* tin = p.sin + (int64_t(seg_off[n] + s) * H + h) * DK * DV;
+            const float* tin = p.sin + (int64_t(seg0 + s) * H + h) * DK * DV;
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -1091,7 +1117,7 @@ prefill_block_kernel(PrefillDev p)
         if (!SUMMARY && p.ckpt) {
             const int64_t pos = b0 + len - seq0;  // tokens of the sequence consumed
             if (pos % p.ckpt_interval == 0) {
-                const int64_t idx = int64_t(p.tab[3 * (p.N + 1) + n]) + pos / p.ckpt_interval - 1;
+                const int64_t idx = ck_first + pos / p.ckpt_interval - 1;
                 if (idx < p.ckpt_cap) {
                     // one lane pointer, formed here: hoisted out of the block
                     // loop, the 64 element addresses would live in (spilled)
@@ -1244,9 +1270,7 @@ __global__ void __launch_bounds__(256) scan_kernel(PrefillDev p)
     }
     const int h = unit % H;
     const int n = unit / H;
-    const int32_t* seg_off = p.tab + (p.N + 1);
-    const int32_t* p1_off = p.tab + 2 * (p.N + 1);
-    const int nseg = seg_off[n + 1] - seg_off[n];
+    const int nseg = tab_seg(p, n + 1) - tab_seg(p, n);
     if (nseg <= 1) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, q4 = lane >> 4;
@@ -1258,8 +1282,8 @@ __global__ void __launch_bounds__(256) scan_kernel(PrefillDev p)
 #endif
     // Table entries are read once, into registers: a re-read after the state
     // stores below would wait for every load in flight, the prefetch included.
-    const float* const ms0 = p.ms + (int64_t(p1_off[n]) * H + h) * DK * (DK + DV);
-    float* const sin0 = p.sin + (int64_t(seg_off[n]) * H + h) * DK * DV;
+    const float* const ms0 = p.ms + (int64_t(tab_p1(p, n)) * H + h) * DK * (DK + DV);
+    float* const sin0 = p.sin + (int64_t(tab_seg(p, n)) * H + h) * DK * DV;
     auto ms_of = [&](int st) { return ms0 + int64_t(st) * H * DK * (DK + DV); };
 
     // S_in(0) slice: column j of the slice is row j of the tiles; state row k sits at pcol(k)
@@ -1372,15 +1396,26 @@ hipError_t launch_prefill_t(const PrefillArgs& a, const PrefillPlan& plan, hipSt
 {
     unsigned char* ws = static_cast<unsigned char*>(a.ws);
     int32_t* tab = reinterpret_cast<int32_t*>(ws + plan.off_table);
+    const bool single = a.cu == nullptr && a.N == 1;
+    int single_nseg = 1, single_nck = 0;
+    if (single) {  // the plan kernel's arithmetic for the one sequence [0, T_total)
+        const int64_t len = a.T_total > 0 ? a.T_total : 0;
+        const int64_t ch = (len + CH - 1) / CH;
+        const int64_t ns = (ch + plan.seg_chunks - 1) / plan.seg_chunks;
+        single_nseg = int(ns < 1 ? 1 : ns);
+        single_nck = (a.ckpt && a.ckpt_interval > 0) ? int(len / a.ckpt_interval) : 0;
+    }
     PrefillDev d{a.q, a.k, a.v, a.g, a.beta, tab, a.N, a.T_total, a.H, plan.seg_chunks,
                  a.init, a.fin, a.o,
                  plan.np1_max > 0 ? reinterpret_cast<float*>(ws + plan.off_ms) : nullptr,
                  plan.np1_max > 0 ? reinterpret_cast<float*>(ws + plan.off_sin) : nullptr,
-                 a.ckpt, a.ckpt_interval, a.ckpt_cap};
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, stream, a.cu, a.N, a.T_total,
-                       plan.seg_chunks, a.ckpt ? a.ckpt_interval : 0, tab);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+                 a.ckpt, a.ckpt_interval, a.ckpt_cap, single ? 1 : 0, single_nseg, single_nck};
+    hipError_t e = hipSuccess;
+    if (!single) {
+        hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, stream, a.cu, a.N, a.T_total,
+                           plan.seg_chunks, a.ckpt ? a.ckpt_interval : 0, tab);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     if (plan.np1_max > 0) {
         using C1 = BlockCfg<DT, DK, DV, true>;
         auto k1 = prefill_block_kernel<DT, DK, DV, true>;
