@@ -2,10 +2,11 @@
 """Benchmark of the KDA forward hot path on one MI355X.
 
 Prints ONE JSON line.  `value` is prefill throughput on the 8K-token workload
-(H=32, T=8192, d_k=d_v=128, chunk 64, bf16): one step = kda_gate + kda_prefill
-over one batch of seeded synthetic inputs already resident in HBM (three input
-sets are rotated so the 256 MB last-level cache cannot hold a step's working
-set).  The decode leg (B=256, H=32, 1000 consecutive in-place steps) is
+(H=32, T=8192, d_k=d_v=128, chunk 64, bf16): one step = the gate and the
+prefill over one batch of seeded synthetic inputs already resident in HBM, as
+one kda_prefill_gated call (the gate computed in the prefill's decay stage;
+three input sets are rotated so the 256 MB last-level cache cannot hold a
+step's working set).  `unfused` times the same work as kda_gate + kda_prefill.  The decode leg (B=256, H=32, 1000 consecutive in-place steps) is
 reported under "decode", and verify/commit (B=256, K=4) under "speculative".  Every
 duration is the mean over back-to-back calls bracketed by two HIP events on
 the stream the library launches on (an event between calls would serialise
@@ -19,7 +20,7 @@ pass (whole workload, normwise max relative error).
                   [--no-cpu] [--copy-calib] [--spin-up SECONDS]
 
 Before the W warmup steps the prefill step runs untimed for --spin-up seconds
-(0.3 by default) so that the timed steps see the GPU's steady clocks.
+(0.5 by default) so that the timed steps see the GPU's steady clocks.
 """
 from __future__ import annotations
 
@@ -36,7 +37,7 @@ sys.path.insert(0, ROOT)
 METRIC = "KDA prefill tokens/s (H=32,d=128,T=8K) + decode tok/s (B=256); % of roofline"
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
-SPIN_UP_S = 0.3  # untimed full steps before the warmup steps
+SPIN_UP_S = 0.5  # untimed full steps before the warmup steps
 
 
 def kernel_source_hash() -> str:
@@ -95,14 +96,15 @@ def cpu_baseline(wl, seconds: float = 12.0):
     every token), repeated until at least `seconds` of CPU time have passed;
     tokens/s of the full problem.  Also returns the first pass's (o, S): the
     oracle's result for input set 0 (bf16-rounded inputs, as the GPU holds
-    them), against which the timed run's output is checked."""
+    them; g from the gate in fp64, unrounded, as the fused gate keeps it),
+    against which the timed run's output is checked."""
     import oracle
     import synth
     threads = oracle.default_threads()
     x = synth.prefill_inputs(wl)
     for n in ("q", "k", "v", "z", "beta"):
         x[n] = oracle.round_bf16(x[n])
-    g = oracle.gate(x["z"], x["A"], round_bf16=True)
+    g = oracle.gate(x["z"], x["A"])  # the fused gate keeps g in fp32
     reps, first, t0 = 0, None, time.perf_counter()
     while True:
         res = oracle.prefill(x["q"], x["k"], x["v"], g, x["beta"], threads=threads)
@@ -166,12 +168,17 @@ def main():
     wbytes = kda.kda_prefill_workspace_size(T, 1, H, dk, dv)
     ws = torch.empty(max(wbytes, 1), dtype=torch.uint8, device=dev)
 
-    def prefill(i):
+    def step(i):  # one call: the gate fused into the prefill's decay stage
+        d = sets[i % 3]
+        kda.kda_prefill_gated(d["q"], d["k"], d["v"], d["z"], A, d["beta"], final_state=d["S"], o=d["o"],
+                              workspace=ws)
+
+    def prefill(i):  # the unfused prefill, on g from a separate kda_gate
         d = sets[i % 3]
         kda.kda_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], final_state=d["S"], o=d["o"],
                         workspace=ws)
 
-    def step(i):
+    def step_unfused(i):
         d = sets[i % 3]
         kda.kda_gate(d["z"], A, g=d["g"])
         prefill(i)
@@ -189,7 +196,14 @@ def main():
         return e0.elapsed_time(e1) / n
 
     # bring the GPU to its steady clocks first (untimed): a fresh device runs
-    # the first few hundred microsecond-scale launches at ramping clocks
+    # the first few hundred microsecond-scale launches at ramping clocks.  The
+    # clock starts after a first call has finished, which also loads the
+    # library's kernels (that can take longer than the whole spin-up).
+    step(0)
+    torch.cuda.synchronize()
+    # the checksum every later run must reproduce, taken on the host: a device-side
+    # reduction here allocates and slowed the next hundred or so calls
+    ref_sum = float(sets[0]["o"].cpu().float().abs().sum())
     spin_end = time.perf_counter() + args.spin_up
     i = 0
     while time.perf_counter() < spin_end:
@@ -200,7 +214,6 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    ref_sum = float(sets[0]["o"].float().abs().sum())
     t0 = time.perf_counter()
     ms_step = timed_loop(step, args.steps)  # the timed region: K whole steps
     wall = time.perf_counter() - t0
@@ -208,35 +221,42 @@ def main():
     # the timed runs produce the verified run's result (no caching, same inputs)
     step(0)
     torch.cuda.synchronize()
-    assert abs(float(sets[0]["o"].float().abs().sum()) - ref_sum) <= 1e-6 * max(ref_sum, 1.0)
-    o_timed = sets[0]["o"].float().cpu().numpy()
+    o_host = sets[0]["o"].cpu().float()
+    assert abs(float(o_host.abs().sum()) - ref_sum) <= 1e-6 * max(ref_sum, 1.0)
+    o_timed = o_host.numpy()
     S_timed = sets[0]["S"].cpu().numpy()
-    # duration of one kda_prefill call (the roofline's unit), same inputs, no gate between
+    # the same work as separate launches: kda_gate (g through HBM) then kda_prefill
+    for i in range(args.warmup):
+        step_unfused(i)
+    unfused_ms = timed_loop(step_unfused, args.steps)
     prefill_ms = timed_loop(prefill, args.steps)
+    unfused = {"ms_per_step": round(unfused_ms, 4), "kda_prefill_ms_per_call": round(prefill_ms, 4),
+               "value": round(T / (unfused_ms * 1e-3), 1)}
 
+    # the roofline's unit is the step's one call, kda_prefill_gated
     p_bytes, p_flops = prefill_algo(T, H, dk, dv)
-    achieved = p_bytes / (prefill_ms * 1e-3) / 1e9
+    achieved = p_bytes / (ms_step * 1e-3) / 1e9
     traffic = load_traffic("prefill_8k")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "kda_prefill (plan + segment summary + scan + chunk kernels)",
-                "algorithmic_bytes_per_call": p_bytes, "ms_per_call": round(prefill_ms, 4),
-                "mfma_tflops": round(p_flops / (prefill_ms * 1e-3) / 1e12, 1),
-                "mfma_frac": round(p_flops / (prefill_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)}
+                "kernel": "kda_prefill_gated (segment summary + scan + chunk kernels, gate in the decay stage)",
+                "algorithmic_bytes_per_call": p_bytes, "ms_per_call": round(ms_step, 4),
+                "mfma_tflops": round(p_flops / (ms_step * 1e-3) / 1e12, 1),
+                "mfma_frac": round(p_flops / (ms_step * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)}
 
     # prefill with state checkpoints every 512 tokens (prefix-cache emission)
     n_ck = kda.kda_checkpoint_count(None, T, 512)
     ck = torch.empty((n_ck, H, dk, dv), dtype=torch.float32, device=dev)
     def prefill_ckpt(i):
         d = sets[i % 3]
-        kda.kda_prefill_ckpt(d["q"], d["k"], d["v"], d["g"], d["beta"], 512, ckpt=ck, final_state=d["S"],
-                             o=d["o"], workspace=ws)
+        kda.kda_prefill_gated(d["q"], d["k"], d["v"], d["z"], A, d["beta"], final_state=d["S"], o=d["o"],
+                              workspace=ws, interval=512, ckpt=ck)
 
     for i in range(args.warmup):
         prefill_ckpt(i)
     ck_ms = timed_loop(prefill_ckpt, args.steps)
     ckpt_leg = {"interval": 512, "checkpoints_per_call": n_ck * H, "ms_per_call": round(ck_ms, 4),
-                "overhead_vs_plain": round(ck_ms / prefill_ms - 1.0, 4),
+                "overhead_vs_plain": round(ck_ms / ms_step - 1.0, 4),
                 "checkpoint_bytes_per_call": n_ck * H * dk * dv * 4}
 
     # ------------------------------------------------------------- decode leg
@@ -358,10 +378,11 @@ def main():
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic",
-           "config": {"workload": "prefill_8k: gate + chunked prefill, B=1 H=32 T=8192 "
-                                  "d_k=d_v=128 chunk=64, zero initial state",
+           "config": {"workload": "prefill_8k: gate + chunked prefill in one kda_prefill_gated call, "
+                                  "B=1 H=32 T=8192 d_k=d_v=128 chunk=64, zero initial state",
                       "B": 1, "H": H, "T": T, "d_k": dk, "d_v": dv, "chunk": 64, "input_sets": 3},
-           "roofline": roofline, "cpu_baseline": cpu, "verified": verified, "checkpoints": ckpt_leg,
+           "roofline": roofline, "cpu_baseline": cpu, "verified": verified, "unfused": unfused,
+           "checkpoints": ckpt_leg,
            "decode": decode,
            "speculative": spec,
            "wall_s": round(wall, 3), "source_hash": kernel_source_hash()}

@@ -161,6 +161,29 @@ kda_status_t kda_prefill_ckpt(const void* q, const void* k, const void* v, const
                               int64_t ckpt_capacity, void* stream);
 
 /*
+ * kda_prefill_gated — kda_prefill whose decay comes straight from the gate's
+ * input: g = g_min * sigmoid(exp(A[h]) * z) ("NLP——技术报告解读-Kimi-K3",
+ * Model Architecture / Kimi Delta Attention (KDA), lower-bounded decay; the
+ * same map as kda_gate) is computed in fp32 inside the prefill's decay stage
+ * and never written out, so one call covers the gate and the prefill.
+ * Arguments as kda_prefill and kda_prefill_ckpt, except:
+ *   z      : [T_total, H, d_k] DEVICE, the input dtype (in place of g).
+ *   A      : fp32 [H] DEVICE, read only (may be NULL when T_total = 0).
+ *   g_min  : in [-5, 0) (-5 on the pages); the block kernels bound every decay
+ *            factor through g >= -5.
+ *   ckpt_interval : 0 for no checkpoints, else as in kda_prefill_ckpt.
+ * Results equal kda_gate followed by kda_prefill up to the rounding of g to
+ * the input dtype, which this path skips.
+ * Errors: as kda_prefill_ckpt, plus KDA_ERR_INVALID_ARGUMENT for a null A, a
+ * g_min outside [-5, 0), or A overlapping an output buffer.
+ */
+kda_status_t kda_prefill_gated(const void* q, const void* k, const void* v, const void* z, const float* A,
+                               float g_min, const void* beta, const int32_t* cu_seqlens, int N, int64_t T_total,
+                               int H, int d_k, int d_v, int chunk, const float* initial_state, float* final_state,
+                               void* o, kda_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                               int ckpt_interval, float* ckpt_states, int64_t ckpt_capacity, void* stream);
+
+/*
  * Number of checkpoints kda_prefill_ckpt writes for these HOST cu_seqlens
  * (NULL: one sequence of T_total tokens), with the planner's clamping; -1 on
  * invalid arguments (N < 1, T_total < 0, ckpt_interval <= 0).  Host only.

@@ -19,7 +19,7 @@ _STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARGUMENT", 2: "KDA_ERR_UNSUPPORTED",
            3: "KDA_ERR_WORKSPACE_TOO_SMALL", 4: "KDA_ERR_HIP"}
 EXPORTED = ("kda_status_string", "kda_last_error", "kda_version", "kda_gate",
             "kda_prefill_workspace_size", "kda_prefill", "kda_decode_step", "kda_verify", "kda_commit",
-            "kda_prefill_ckpt", "kda_checkpoint_count")
+            "kda_prefill_ckpt", "kda_checkpoint_count", "kda_prefill_gated")
 
 _lib = None
 
@@ -59,6 +59,9 @@ def lib() -> ctypes.CDLL:
         L.kda_commit.restype = I
         L.kda_prefill_ckpt.argtypes = [P, P, P, P, P, P, I, I64, I, I, I, I, P, P, P, I, P, SZ, I, P, I64, P]
         L.kda_prefill_ckpt.restype = I
+        L.kda_prefill_gated.argtypes = [P, P, P, P, P, F, P, P, I, I64, I, I, I, I, P, P, P, I, P, SZ, I, P, I64,
+                                        P]
+        L.kda_prefill_gated.restype = I
         L.kda_checkpoint_count.argtypes = [P, I, I64, I]
         L.kda_checkpoint_count.restype = I64
         _lib = L
@@ -221,3 +224,39 @@ def kda_prefill_ckpt(q, k, v, g, beta, interval: int, ckpt=None, cu_seqlens=None
                                   _ptr(workspace), wbytes, int(interval), _ptr(ckpt) if ckpt.numel() else None,
                                   ckpt.shape[0], _stream(stream)))
     return o, final_state, ckpt
+
+
+def kda_prefill_gated(q, k, v, z, A, beta, g_min: float = -5.0, cu_seqlens=None, initial_state=None,
+                      final_state=None, o=None, workspace=None, interval: int = 0, ckpt=None,
+                      cu_seqlens_host=None, chunk: int = 64, want_final_state: bool = True, stream=None):
+    """kda_prefill with the gate fused: the decay is g = g_min * sigmoid(exp(A[h]) * z),
+    computed inside the prefill from z [T, H, d_k] and A fp32 [H].  With interval > 0
+    it also writes state checkpoints as kda_prefill_ckpt does.
+    Returns (o, final_state) or, with interval > 0, (o, final_state, ckpt)."""
+    import torch
+    _dense(q, k, v, z, A, beta, cu_seqlens, initial_state, final_state, o, ckpt)
+    T, H, dk = k.shape
+    dv = v.shape[2]
+    N = 1 if cu_seqlens is None else cu_seqlens.shape[0] - 1
+    code = _dtype_code(k)
+    if o is None:
+        o = torch.empty((T, H, dv), dtype=v.dtype, device=v.device)
+    if final_state is None and (want_final_state or interval > 0):
+        final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=k.device)
+    if interval > 0 and ckpt is None:
+        if cu_seqlens is not None and cu_seqlens_host is None:
+            cu_seqlens_host = cu_seqlens.cpu().numpy()
+        n = kda_checkpoint_count(cu_seqlens_host, T, interval)
+        ckpt = torch.empty((max(n, 0), H, dk, dv), dtype=torch.float32, device=k.device)
+    need = kda_prefill_workspace_size(T, N, H, dk, dv, chunk, code)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=k.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    cap = 0 if ckpt is None else ckpt.shape[0]
+    _check(lib().kda_prefill_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(A), float(g_min), _ptr(beta),
+                                   _ptr(cu_seqlens), N, T, H, dk, dv, chunk, _ptr(initial_state),
+                                   _ptr(final_state), _ptr(o), code, _ptr(workspace), wbytes, int(interval),
+                                   _ptr(ckpt) if cap else None, cap, _stream(stream)))
+    if interval > 0:
+        return o, final_state, ckpt
+    return o, final_state

@@ -244,7 +244,8 @@ static kda_status_t prefill_impl(const char* who, const void* q, const void* k, 
                                  const void* beta, const int32_t* cu_seqlens, int N, int64_t T_total, int H,
                                  int d_k, int d_v, int chunk, const float* initial_state, float* final_state,
                                  void* o, kda_dtype_t dtype, void* workspace, size_t workspace_bytes,
-                                 int ckpt_interval, float* ckpt_states, int64_t ckpt_capacity, void* stream)
+                                 int ckpt_interval, float* ckpt_states, int64_t ckpt_capacity, void* stream,
+                                 const float* gate_A = nullptr, float g_min = -5.f)
 {
     if (N < 1 || T_total < 0 || H < 1)
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: bad sizes N=%d T_total=%lld H=%d", who, N,
@@ -263,6 +264,16 @@ static kda_status_t prefill_impl(const char* who, const void* q, const void* k, 
         return fail(KDA_ERR_UNSUPPORTED, "%s: T_total too large", who);
     if (T_total > 0 && (!q || !k || !v || !g || !beta || !o))
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: null token tensor", who);
+    if (gate_A) {
+        // the block kernels bound every decay factor through g >= -5 per token
+        if (!std::isfinite(g_min) || !(g_min < 0.f) || g_min < -5.f)
+            return fail(KDA_ERR_INVALID_ARGUMENT, "%s: g_min must lie in [-5, 0)", who);
+        const size_t na = size_t(H) * sizeof(float);
+        if (overlap(o, size_t(T_total) * H * d_v * dsize(dtype), gate_A, na) ||
+            overlap(final_state, final_state ? size_t(N) * H * d_k * d_v * sizeof(float) : 0, gate_A, na) ||
+            overlap(workspace, kda::prefill_plan(T_total, N, H, d_k, d_v).workspace_bytes, gate_A, na))
+            return fail(KDA_ERR_INVALID_ARGUMENT, "%s: A overlaps an output buffer", who);
+    }
     const kda::PrefillPlan plan = kda::prefill_plan(T_total, N, H, d_k, d_v);
     if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
         return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes < %zu needed", who,
@@ -318,6 +329,8 @@ static kda_status_t prefill_impl(const char* who, const void* q, const void* k, 
         a.ckpt_interval = ckpt_interval;
         a.ckpt_cap = ckpt_capacity;
     }
+    a.gate_A = gate_A;
+    a.g_min = g_min;
     hipError_t e = dtype == KDA_BF16 ? kda::launch_prefill<kda::BF16>(a, plan, s)
                                      : kda::launch_prefill<kda::F32>(a, plan, s);
     return from_hip(e, "kda_prefill launch");
@@ -347,6 +360,23 @@ kda_status_t kda_prefill_ckpt(const void* q, const void* k, const void* v, const
     return prefill_impl("kda_prefill_ckpt", q, k, v, g, beta, cu_seqlens, N, T_total, H, d_k, d_v, chunk,
                         initial_state, final_state, o, dtype, workspace, workspace_bytes, ckpt_interval,
                         ckpt_states, ckpt_capacity, stream);
+}
+
+kda_status_t kda_prefill_gated(const void* q, const void* k, const void* v, const void* z, const float* A,
+                               float g_min, const void* beta, const int32_t* cu_seqlens, int N, int64_t T_total,
+                               int H, int d_k, int d_v, int chunk, const float* initial_state, float* final_state,
+                               void* o, kda_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                               int ckpt_interval, float* ckpt_states, int64_t ckpt_capacity, void* stream)
+{
+    if (!std::isfinite(g_min) || !(g_min < 0.f) || g_min < -5.f)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_prefill_gated: g_min must lie in [-5, 0)");
+    if (T_total > 0 && !A) return fail(KDA_ERR_INVALID_ARGUMENT, "kda_prefill_gated: null A");
+    if (ckpt_interval < 0 || ckpt_capacity < 0)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_prefill_gated: negative checkpoint interval or capacity");
+    // with no tokens nothing reads A (the state is only copied through)
+    return prefill_impl("kda_prefill_gated", q, k, v, z, beta, cu_seqlens, N, T_total, H, d_k, d_v, chunk,
+                        initial_state, final_state, o, dtype, workspace, workspace_bytes, ckpt_interval,
+                        ckpt_states, ckpt_capacity, stream, T_total > 0 ? A : nullptr, g_min);
 }
 
 int64_t kda_checkpoint_count(const int32_t* cu_seqlens_host, int N, int64_t T_total, int ckpt_interval)

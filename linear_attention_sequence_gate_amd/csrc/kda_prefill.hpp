@@ -137,6 +137,8 @@ struct PrefillArgs {
     float* ckpt = nullptr;  // state checkpoints (or null)
     int ckpt_interval = 0;  // tokens between checkpoints (multiple of CH), 0 = none
     int64_t ckpt_cap = 0;   // checkpoints the buffer holds
+    const float* gate_A = nullptr;  // non-null: g holds the gate's input z, and g = g_min sigmoid(e^{A_h} z)
+    float g_min = -5.f;
 };
 
 // Device-side view shared by the prefill kernels.
@@ -161,6 +163,22 @@ struct PrefillDev {
     int single;
     int single_nseg;
     int single_nck;
+    const float* gate_A;  // non-null: the gate is applied to g (which holds z) in the decay stage
+    float g_min;
+};
+
+// The gate fused into the decay stage ("NLP——技术报告解读-Kimi-K3", Model
+// Architecture / Kimi Delta Attention (KDA), lower-bounded decay):
+// g = g_min sigmoid(e^{A_h} z) = g_min / (1 + 2^{s2 z}) with
+// s2 = -e^{A_h} log2(e), in fp32, so the decay input never goes through HBM
+// as g.  Both passes over a segment apply it to the same z and get the same g.
+struct GateZ {
+    bool on;
+    float s2, g_min;
+    __device__ __forceinline__ float operator()(float z) const
+    {
+        return on ? g_min * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(s2 * z)) : z;
+    }
 };
 
 // Table entries (cu_seqlens clamped, segment, pass-1 and checkpoint offsets)
@@ -664,7 +682,8 @@ __device__ __forceinline__ void prep_load(PrepRegs<C, DT>& r, const PrefillDev& 
 // sub-tile a (R_0 = 0).
 template <typename C, typename DT, bool SUMMARY>
 __device__ __forceinline__ void prep_tiles(const PrepRegs<C, DT>& r, unsigned char* smem, int buf, int len,
-                                           int lane, int ptid, int cpair, int part, int tok0, PhaseClock& pclk)
+                                           int lane, int ptid, int cpair, int part, int tok0, const GateZ& gz,
+                                           PhaseClock& pclk)
 {
     using O = Op<DT>;
     using OT = typename O::T;
@@ -688,8 +707,8 @@ __device__ __forceinline__ void prep_tiles(const PrepRegs<C, DT>& r, unsigned ch
 #pragma unroll
     for (int i = 0; i < C::TPT; ++i) {
         const bool ok = tok0 + i < len;
-        s0 += ok ? O::p0(r.g[i]) : 0.f;
-        s1 += ok ? O::p1(r.g[i]) : 0.f;
+        s0 += ok ? gz(O::p0(r.g[i])) : 0.f;
+        s1 += ok ? gz(O::p1(r.g[i])) : 0.f;
         c0[i] = s0;
         c1[i] = s1;
     }
@@ -943,10 +962,12 @@ prefill_block_kernel(PrefillDev p)
         const int part = lane / C::CPW;
         const int cpair = pw * C::CPW + lane % C::CPW;
         const int tok0 = part * C::TPT;
+        GateZ gz{p.gate_A != nullptr, 0.f, p.g_min};
+        if (gz.on) gz.s2 = -__expf(p.gate_A[h]) * 1.4426950408889634f;
         PrepRegs<C, DT> pr;
         if (nblk > 0) {
             prep_load<C, DT, SUMMARY>(pr, p, t_begin, blen(0), h, ptid, cpair, tok0);
-            prep_tiles<C, DT, SUMMARY>(pr, smem, 0, blen(0), lane, ptid, cpair, part, tok0, pclk);
+            prep_tiles<C, DT, SUMMARY>(pr, smem, 0, blen(0), lane, ptid, cpair, part, tok0, gz, pclk);
             if (nblk > 1) prep_load<C, DT, SUMMARY>(pr, p, t_begin + BC, blen(1), h, ptid, cpair, tok0);
         }
         __syncthreads();
@@ -958,7 +979,8 @@ prefill_block_kernel(PrefillDev p)
             __syncthreads();
             KDA_PHASE(1);
             if (bi + 1 < nblk) {  // beta: tiles of block bi+1, loads of block bi+2
-                prep_tiles<C, DT, SUMMARY>(pr, smem, buf ^ 1, blen(bi + 1), lane, ptid, cpair, part, tok0, pclk);
+                prep_tiles<C, DT, SUMMARY>(pr, smem, buf ^ 1, blen(bi + 1), lane, ptid, cpair, part, tok0, gz,
+                                           pclk);
                 KDA_PHASE(10);
                 if (bi + 2 < nblk)
                     prep_load<C, DT, SUMMARY>(pr, p, t_begin + (bi + 2) * BC, blen(bi + 2), h, ptid, cpair, tok0);
@@ -1409,7 +1431,8 @@ hipError_t launch_prefill_t(const PrefillArgs& a, const PrefillPlan& plan, hipSt
                  a.init, a.fin, a.o,
                  plan.np1_max > 0 ? reinterpret_cast<float*>(ws + plan.off_ms) : nullptr,
                  plan.np1_max > 0 ? reinterpret_cast<float*>(ws + plan.off_sin) : nullptr,
-                 a.ckpt, a.ckpt_interval, a.ckpt_cap, single ? 1 : 0, single_nseg, single_nck};
+                 a.ckpt, a.ckpt_interval, a.ckpt_cap, single ? 1 : 0, single_nseg, single_nck,
+                 a.gate_A, a.g_min};
     hipError_t e = hipSuccess;
     if (!single) {
         hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, stream, a.cu, a.N, a.T_total,

@@ -212,3 +212,33 @@ def test_prefill_ckpt_validation(L):
     assert call(ck=FAKE + (2 << 20)) == 1                     # overlaps v
     assert call(ck=FAKE + (64 << 20) + 2) == 1                # misaligned
     assert call(dk=96) == 2                                   # prefill checks still apply
+
+
+def test_prefill_gated_validation(L):
+    T, N, H, dk, dv = 256, 1, 2, 64, 64
+    need = kda.kda_prefill_workspace_size(T, N, H, dk, dv)
+
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE + (1 << 20), v=FAKE + (2 << 20), z=FAKE + (3 << 20), A=FAKE + (5 << 20),
+                 gmin=-5.0, beta=FAKE + (4 << 20), cu=None, N=N, T=T, H=H, dk=dk, dv=dv, chunk=64,
+                 init=None, fin=FAKE + (8 << 20), o=FAKE + (16 << 20), dt=BF16,
+                 ws=FAKE + (32 << 20), wsb=need, iv=0, ck=None, cap=0)
+        a.update(kw)
+        return L.kda_prefill_gated(a["q"], a["k"], a["v"], a["z"], a["A"], a["gmin"], a["beta"], a["cu"],
+                                   a["N"], a["T"], a["H"], a["dk"], a["dv"], a["chunk"], a["init"], a["fin"],
+                                   a["o"], a["dt"], a["ws"], a["wsb"], a["iv"], a["ck"], a["cap"], None)
+
+    assert call(A=None) == 1                                  # A is required when there are tokens
+    assert call(gmin=-6.0) == 1                               # below the bound the kernels rely on
+    assert call(gmin=0.0) == 1
+    assert call(gmin=float("nan")) == 1
+    assert call(A=FAKE + (16 << 20) + 64) == 1                # A inside o
+    assert call(A=FAKE + (32 << 20) + 64) == 1                # A inside the workspace
+    assert call(z=None) == 1
+    assert call(iv=-64) == 1
+    assert call(iv=100, ck=FAKE + (64 << 20), cap=4) == 1     # checkpoint rules of kda_prefill_ckpt
+    assert call(dk=96) == 2                                   # prefill checks still apply
+    assert call(wsb=need - 1) == 3
+    assert b"kda_prefill_gated" in L.kda_last_error()
+    # no tokens and no final state: nothing to do, A may be NULL
+    assert call(T=0, A=None, fin=None, q=None, k=None, v=None, z=None, beta=None, o=None) == 0

@@ -1,0 +1,104 @@
+"""GPU parity: kda_prefill_gated (the gate fused into the prefill's decay stage)
+against the fp64 oracle.  The fused path never rounds g to the storage dtype,
+so the oracle's gate is not rounded either; everything else is as in the
+kda_gate + kda_prefill tests."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_common import TOL, announce, dev, host, relerr
+from tests.test_gpu_prefill import SegEnv
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def kda():
+    import torch
+    import linear_attention_sequence_gate_amd as m
+    assert torch.cuda.is_available()
+    m.lib()
+    return m
+
+
+def run_gated(kda, wl, x, S0, seg=None, g_min=-5.0, interval=0):
+    import torch
+    dt = wl.dtype
+    cu = torch.from_numpy(wl.cu_seqlens).to("cuda") if wl.N > 1 else None
+    with SegEnv(seg):
+        res = kda.kda_prefill_gated(dev(x["q"], dt), dev(x["k"], dt), dev(x["v"], dt), dev(x["z"], dt),
+                                    dev(x["A"]), dev(x["beta"], dt), g_min=g_min, cu_seqlens=cu,
+                                    initial_state=None if S0 is None else dev(S0), interval=interval,
+                                    cu_seqlens_host=wl.cu_seqlens if wl.N > 1 else None)
+    torch.cuda.synchronize()
+    return tuple(host(t) for t in res)
+
+
+def check(kda, wl, seg=None, g_min=-5.0, tag=""):
+    announce(f"prefill_gated {wl.name} {tag} H={wl.H} dk={wl.dk} dv={wl.dv} {wl.dtype} "
+             f"lens={list(wl.seqlens)[:8]} seg={seg} g_min={g_min}")
+    x = synth.prefill_inputs(wl)
+    S0 = synth.initial_state(wl) if wl.state_std > 0 else None
+    o, S = run_gated(kda, wl, x, S0, seg, g_min)
+    g = oracle.gate(x["z"], x["A"], g_min=g_min)
+    o_ref, S_ref = oracle.prefill(x["q"], x["k"], x["v"], g, x["beta"], cu=wl.cu_seqlens, S0=S0)
+    e_o, e_s = relerr(o, o_ref), relerr(S, S_ref)
+    print(f"  o err {e_o:.3e}  state err {e_s:.3e}")
+    tol = TOL[wl.dtype]
+    assert e_o < tol, f"output error {e_o:.3e}"
+    assert e_s < tol, f"final state error {e_s:.3e}"
+
+
+def test_gated_tiny_f32(kda):
+    check(kda, synth.TINY_F32)
+
+
+def test_gated_8k_bf16(kda):
+    check(kda, synth.PREFILL_8K)
+
+
+@pytest.mark.parametrize("dk,dv,dtype", [(128, 128, "bf16"), (64, 64, "bf16"), (32, 32, "bf16"),
+                                         (32, 32, "f32"), (32, 64, "f32")])
+def test_gated_varlen_dims(kda, dk, dv, dtype):
+    wl = synth.VARLEN_64.with_(H=3, dk=dk, dv=dv, dtype=dtype, seqlens=(0, 1, 63, 64, 65, 130, 300, 17),
+                               state_std=0.1)
+    check(kda, wl)
+
+
+@pytest.mark.parametrize("zshift", [0.0, -3.0])
+def test_gated_segmented(kda, zshift):
+    """Summary pass, scan and output pass each apply the gate to the same z."""
+    wl = synth.VARLEN_64.with_(H=4, seqlens=(700, 0, 64, 129, 1000, 5), state_std=0.1, z_shift=zshift)
+    check(kda, wl, seg=2, tag=f"zshift={zshift}")
+
+
+@pytest.mark.parametrize("g_min", [-5.0, -2.0, -0.25])
+def test_gated_g_min(kda, g_min):
+    wl = synth.TINY_F32.with_(H=2, seqlens=(300,), state_std=0.1)
+    check(kda, wl, seg=2, g_min=g_min)
+    check(kda, wl.with_(dtype="bf16", dk=64, dv=64), g_min=g_min)
+
+
+def test_gated_checkpoints(kda):
+    """Checkpoints from the fused path against oracle states at those tokens."""
+    wl = synth.VARLEN_64.with_(H=2, dk=64, dv=64, seqlens=(300, 520), state_std=0.1)
+    announce(f"prefill_gated checkpoints lens={wl.seqlens} interval=128")
+    x = synth.prefill_inputs(wl)
+    S0 = synth.initial_state(wl)
+    o, S, ck = run_gated(kda, wl, x, S0, seg=2, interval=128)
+    g = oracle.gate(x["z"], x["A"])
+    cu = wl.cu_seqlens
+    row = 0
+    for n in range(wl.N):
+        L = int(cu[n + 1] - cu[n])
+        for j in range(1, L // 128 + 1):
+            t0, t1 = int(cu[n]), int(cu[n]) + 128 * j
+            _, Sj = oracle.prefill(x["q"][t0:t1], x["k"][t0:t1], x["v"][t0:t1], g[t0:t1], x["beta"][t0:t1],
+                                   S0=S0[n:n + 1])
+            e = relerr(ck[row], Sj[0])
+            assert e < TOL["bf16"], f"checkpoint {row} (sequence {n}, token {128 * j}): {e:.3e}"
+            row += 1
+    assert row == ck.shape[0]
+    o_ref, S_ref = oracle.prefill(x["q"], x["k"], x["v"], g, x["beta"], cu=cu, S0=S0)
+    assert relerr(o, o_ref) < TOL["bf16"] and relerr(S, S_ref) < TOL["bf16"]
