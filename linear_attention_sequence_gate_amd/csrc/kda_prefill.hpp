@@ -492,9 +492,11 @@ struct BlockCfg {
     static constexpr int CW = 32;
     static constexpr int NCT = CW / 16;                   // 16-wide column tiles per chain wave
     static constexpr int NCW = NCOL / CW;                 // chain waves
-    // prep waves: two per SIMD for the output pass of wide heads (their
-    // vector work is the longer side of the pipeline), one otherwise
-    static constexpr int NPW = (!SUMMARY && DKV >= 64) ? 8 : 4;
+    // prep waves: two per SIMD for heads with d_k >= 64 (their vector work,
+    // the gate's included when it is fused, is the longer side of the
+    // pipeline in both passes: the summary pass then runs 16 waves at 118
+    // VGPRs), one otherwise
+    static constexpr int NPW = (DKV >= 64) ? 8 : 4;
     static constexpr int NW = NCW + NPW;
     static constexpr int NT = 64 * NW;
     static constexpr int NPT = 64 * NPW;       // prep threads
