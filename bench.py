@@ -6,15 +6,17 @@ Prints ONE JSON line.  `value` is prefill throughput on the 8K-token workload
 prefill over one batch of seeded synthetic inputs already resident in HBM, as
 one kda_prefill_gated call (the gate computed in the prefill's decay stage;
 three input sets are rotated so the 256 MB last-level cache cannot hold a
-step's working set).  `unfused` times the same work as kda_gate + kda_prefill.  The decode leg (B=256, H=32, 1000 consecutive in-place steps) is
-reported under "decode", and verify/commit (B=256, K=4) under "speculative".  Every
-duration is the mean over back-to-back calls bracketed by two HIP events on
-the stream the library launches on (an event between calls would serialise
-them).  `roofline` covers the prefill call (algorithmic bytes per call);
-each roofline also carries the fraction of a plain 1 GiB device copy measured
-on the same device.  `cpu_baseline` is the fp64 oracle timed on this host on a
-bounded sample; `verified` compares the timed run's output with that oracle
-pass (whole workload, normwise max relative error).
+step's working set).  `unfused` times the same work as kda_gate + kda_prefill.
+The decode leg (B=256, H=32, 1000 consecutive in-place steps) is reported
+under "decode" (one kda_decode_step_gated call per step; `unfused` times
+kda_gate + kda_decode_step), and verify/commit (B=256, K=4) under
+"speculative".  Every duration is the mean over back-to-back calls bracketed
+by two HIP events on the stream the library launches on (an event between
+calls would serialise them).  `roofline` covers the prefill call (algorithmic
+bytes per call); each roofline also carries the fraction of a plain 1 GiB
+device copy measured on the same device.  `cpu_baseline` is the fp64 oracle
+timed on this host on a bounded sample; `verified` compares the timed run's
+output with that oracle pass (whole workload, normwise max relative error).
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps D]
                   [--no-cpu] [--copy-calib] [--spin-up SECONDS]
@@ -272,19 +274,22 @@ def main():
     state = torch.from_numpy(synth.initial_state(dwl)).to(dev)
     dout = torch.empty((B, dwl.H, dwl.dv), dtype=torch.bfloat16, device=dev)
 
-    def dstep(i):
+    def dstep(i):  # one call: the gate fused into the decode step
+        d = dsets[i % 8]
+        kda.kda_decode_step_gated(d["q"], d["k"], d["v"], d["z"], dA, d["beta"], state, o=dout)
+
+    def dstep_unfused(i):
         d = dsets[i % 8]
         kda.kda_gate(d["z"], dA, g=d["g"])
-        kda.kda_decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], state, o=dout)
-
-    def dcall(i):  # the decode kernel alone (g of every set is current after the warmup)
-        d = dsets[i % 8]
         kda.kda_decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], state, o=dout)
 
     for i in range(16):
         dstep(i)
     d_total_ms = timed_loop(dstep, args.decode_steps) * args.decode_steps
-    d_kernel_ms = timed_loop(dcall, args.decode_steps)
+    d_kernel_ms = d_total_ms / args.decode_steps  # the step is the one launch
+    for i in range(16):
+        dstep_unfused(i)
+    d_unfused_ms = timed_loop(dstep_unfused, args.decode_steps)
     d_bytes, d_flops = decode_algo(B, dwl.H, dwl.dk, dwl.dv)
     d_ach = d_bytes / (d_kernel_ms * 1e-3) / 1e9
     decode = {"value": round(B * args.decode_steps / (d_total_ms * 1e-3), 1), "unit": "tokens/s",
@@ -293,9 +298,12 @@ def main():
                          "d_v": dwl.dv, "input_sets": 8},
               "roofline": {"bound": "hbm", "achieved": round(d_ach, 1), "peak": HBM_PEAK_GBS,
                            "unit": "GB/s", "frac": round(d_ach / HBM_PEAK_GBS, 4),
-                           "traffic": load_traffic("decode_b256"), "kernel": "step_wave_kernel (decode)",
+                           "traffic": load_traffic("decode_b256"),
+                           "kernel": "step_wave_kernel (kda_decode_step_gated)",
                            "algorithmic_bytes_per_call": d_bytes,
-                           "ms_per_call": round(d_kernel_ms, 4)}}
+                           "ms_per_call": round(d_kernel_ms, 4)},
+              "unfused": {"ms_per_step": round(d_unfused_ms, 4),
+                          "value": round(B / (d_unfused_ms * 1e-3), 1)}}
 
     # ------------------------------------------- speculative decode leg (K = 4)
     swl = synth.VERIFY_B256_K4

@@ -205,6 +205,24 @@ kda_status_t kda_decode_step(const void* q, const void* k, const void* v, const 
                              const void* beta, float* state, void* o, int B, int H, int d_k,
                              int d_v, kda_dtype_t dtype, void* stream);
 
+/*
+ * kda_decode_step_gated — kda_decode_step taking the gate's input: the decay
+ * is g = g_min * sigmoid(exp(A[h]) * z) ([K3-notes] KDA, lower-bounded decay;
+ * the map kda_gate computes), evaluated in fp32 inside the step, so one call
+ * covers the gate and the decode step.
+ *   z     : [B, H, d_k] (dtype), in place of g.
+ *   A     : fp32 [H] DEVICE, read only (may be NULL when B == 0).
+ *   g_min : finite and negative (-5 on the pages).
+ * Other arguments as kda_decode_step.  Results equal kda_gate followed by
+ * kda_decode_step up to the rounding of g to the input dtype, which this path
+ * skips.
+ * Errors: as kda_decode_step, plus KDA_ERR_INVALID_ARGUMENT for a null A, a
+ * bad g_min, or A overlapping o or the state.
+ */
+kda_status_t kda_decode_step_gated(const void* q, const void* k, const void* v, const void* z, const float* A,
+                                   float g_min, const void* beta, float* state, void* o, int B, int H, int d_k,
+                                   int d_v, kda_dtype_t dtype, void* stream);
+
 /* Largest number of draft tokens per sequence kda_verify / kda_commit accept. */
 #define KDA_MAX_DRAFT 64
 

@@ -19,7 +19,7 @@ _STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARGUMENT", 2: "KDA_ERR_UNSUPPORTED",
            3: "KDA_ERR_WORKSPACE_TOO_SMALL", 4: "KDA_ERR_HIP"}
 EXPORTED = ("kda_status_string", "kda_last_error", "kda_version", "kda_gate",
             "kda_prefill_workspace_size", "kda_prefill", "kda_decode_step", "kda_verify", "kda_commit",
-            "kda_prefill_ckpt", "kda_checkpoint_count", "kda_prefill_gated")
+            "kda_prefill_ckpt", "kda_checkpoint_count", "kda_prefill_gated", "kda_decode_step_gated")
 
 _lib = None
 
@@ -62,6 +62,8 @@ def lib() -> ctypes.CDLL:
         L.kda_prefill_gated.argtypes = [P, P, P, P, P, F, P, P, I, I64, I, I, I, I, P, P, P, I, P, SZ, I, P, I64,
                                         P]
         L.kda_prefill_gated.restype = I
+        L.kda_decode_step_gated.argtypes = [P, P, P, P, P, F, P, P, P, I, I, I, I, I, P]
+        L.kda_decode_step_gated.restype = I
         L.kda_checkpoint_count.argtypes = [P, I, I64, I]
         L.kda_checkpoint_count.restype = I64
         _lib = L
@@ -260,3 +262,18 @@ def kda_prefill_gated(q, k, v, z, A, beta, g_min: float = -5.0, cu_seqlens=None,
     if interval > 0:
         return o, final_state, ckpt
     return o, final_state
+
+
+def kda_decode_step_gated(q, k, v, z, A, beta, state, o=None, g_min: float = -5.0, stream=None):
+    """kda_decode_step with the gate fused: the decay is g = g_min * sigmoid(exp(A[h]) * z),
+    computed inside the step from z [B, H, d_k] and A fp32 [H].  Returns o; state is
+    updated in place."""
+    import torch
+    _dense(q, k, v, z, A, beta, state, o)
+    B, H, dk = k.shape
+    dv = v.shape[2]
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=v.dtype, device=v.device)
+    _check(lib().kda_decode_step_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(A), float(g_min), _ptr(beta),
+                                       _ptr(state), _ptr(o), B, H, dk, dv, _dtype_code(k), _stream(stream)))
+    return o

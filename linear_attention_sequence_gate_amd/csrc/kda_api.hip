@@ -103,47 +103,66 @@ static bool step_wave_ok(const void* q, const void* k, const void* v, const void
     return kda::step_wave_aligned(q, k, v, g, o) && int64_t(B) * H * (d_v / 32) <= 0x7fffffff;
 }
 
+static kda_status_t decode_impl(const char* who, const void* q, const void* k, const void* v, const void* g,
+                               const void* beta, float* state, void* o, int B, int H, int d_k, int d_v,
+                               kda_dtype_t dtype, void* stream, const float* gate_A = nullptr, float g_min = -5.f)
+{
+    if (B < 0 || H < 1)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: bad sizes B=%d H=%d", who, B, H);
+    if (!dtype_ok(dtype))
+        return fail(KDA_ERR_UNSUPPORTED, "%s: unknown dtype %d", who, (int)dtype);
+    if (!dim_ok(d_k) || !dim_ok(d_v))
+        return fail(KDA_ERR_UNSUPPORTED, "%s: d_k=%d d_v=%d not in {32,64,128}", who, d_k, d_v);
+    if (B == 0) return ok();
+    if (!q || !k || !v || !g || !beta || !state || !o)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: null pointer", who);
+    if ((reinterpret_cast<uintptr_t>(state) & 15) != 0)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: state must be 16-byte aligned", who);
+    if (int64_t(B) * H > 0x7fffffff)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: B*H too large", who);
+    const size_t es = dsize(dtype);
+    const size_t nk = size_t(B) * H * d_k * es, nv = size_t(B) * H * d_v * es;
+    const size_t nb = size_t(B) * H * es, ns = size_t(B) * H * d_k * d_v * sizeof(float);
+    const void* ins[6] = {q, k, v, g, beta, gate_A};
+    const size_t insz[6] = {nk, nk, nv, nk, nb, gate_A ? size_t(H) * sizeof(float) : 0};
+    for (int i = 0; i < 6; ++i) {
+        if (overlap(o, nv, ins[i], insz[i]))
+            return fail(KDA_ERR_INVALID_ARGUMENT, "%s: o aliases an input", who);
+        if (overlap(state, ns, ins[i], insz[i]))
+            return fail(KDA_ERR_INVALID_ARGUMENT, "%s: state aliases an input", who);
+    }
+    if (overlap(o, nv, state, ns))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: o aliases the state", who);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (step_wave_ok(q, k, v, g, o, B, H, d_v))
+        e = dtype == KDA_BF16 ? kda::launch_step_wave<kda::BF16>(0, q, k, v, g, beta, nullptr, state, o, B, 1, H,
+                                                                 d_k, d_v, s, gate_A, g_min)
+                              : kda::launch_step_wave<kda::F32>(0, q, k, v, g, beta, nullptr, state, o, B, 1, H,
+                                                                d_k, d_v, s, gate_A, g_min);
+    else
+        e = dtype == KDA_BF16
+                ? kda::launch_decode<kda::BF16>(q, k, v, g, beta, state, o, B * H, d_k, d_v, s, H, gate_A, g_min)
+                : kda::launch_decode<kda::F32>(q, k, v, g, beta, state, o, B * H, d_k, d_v, s, H, gate_A, g_min);
+    return from_hip(e, "decode launch");
+}
+
 kda_status_t kda_decode_step(const void* q, const void* k, const void* v, const void* g,
                              const void* beta, float* state, void* o, int B, int H, int d_k,
                              int d_v, kda_dtype_t dtype, void* stream)
 {
-    if (B < 0 || H < 1)
-        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_decode_step: bad sizes B=%d H=%d", B, H);
-    if (!dtype_ok(dtype))
-        return fail(KDA_ERR_UNSUPPORTED, "kda_decode_step: unknown dtype %d", (int)dtype);
-    if (!dim_ok(d_k) || !dim_ok(d_v))
-        return fail(KDA_ERR_UNSUPPORTED, "kda_decode_step: d_k=%d d_v=%d not in {32,64,128}", d_k, d_v);
-    if (B == 0) return ok();
-    if (!q || !k || !v || !g || !beta || !state || !o)
-        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_decode_step: null pointer");
-    if ((reinterpret_cast<uintptr_t>(state) & 15) != 0)
-        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_decode_step: state must be 16-byte aligned");
-    if (int64_t(B) * H > 0x7fffffff)
-        return fail(KDA_ERR_UNSUPPORTED, "kda_decode_step: B*H too large");
-    const size_t es = dsize(dtype);
-    const size_t nk = size_t(B) * H * d_k * es, nv = size_t(B) * H * d_v * es;
-    const size_t nb = size_t(B) * H * es, ns = size_t(B) * H * d_k * d_v * sizeof(float);
-    const void* ins[5] = {q, k, v, g, beta};
-    const size_t insz[5] = {nk, nk, nv, nk, nb};
-    for (int i = 0; i < 5; ++i) {
-        if (overlap(o, nv, ins[i], insz[i]))
-            return fail(KDA_ERR_INVALID_ARGUMENT, "kda_decode_step: o aliases an input");
-        if (overlap(state, ns, ins[i], insz[i]))
-            return fail(KDA_ERR_INVALID_ARGUMENT, "kda_decode_step: state aliases an input");
-    }
-    if (overlap(o, nv, state, ns))
-        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_decode_step: o aliases the state");
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e;
-    if (step_wave_ok(q, k, v, g, o, B, H, d_v))
-        e = dtype == KDA_BF16
-                ? kda::launch_step_wave<kda::BF16>(0, q, k, v, g, beta, nullptr, state, o, B, 1, H, d_k, d_v, s)
-                : kda::launch_step_wave<kda::F32>(0, q, k, v, g, beta, nullptr, state, o, B, 1, H, d_k, d_v, s);
-    else
-        e = dtype == KDA_BF16
-                ? kda::launch_decode<kda::BF16>(q, k, v, g, beta, state, o, B * H, d_k, d_v, s)
-                : kda::launch_decode<kda::F32>(q, k, v, g, beta, state, o, B * H, d_k, d_v, s);
-    return from_hip(e, "kda_decode_step launch");
+    return decode_impl("kda_decode_step", q, k, v, g, beta, state, o, B, H, d_k, d_v, dtype, stream);
+}
+
+kda_status_t kda_decode_step_gated(const void* q, const void* k, const void* v, const void* z, const float* A,
+                                   float g_min, const void* beta, float* state, void* o, int B, int H, int d_k,
+                                   int d_v, kda_dtype_t dtype, void* stream)
+{
+    if (!std::isfinite(g_min) || !(g_min < 0.f))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_decode_step_gated: g_min must be finite and negative");
+    if (B > 0 && !A) return fail(KDA_ERR_INVALID_ARGUMENT, "kda_decode_step_gated: null A");
+    return decode_impl("kda_decode_step_gated", q, k, v, z, beta, state, o, B, H, d_k, d_v, dtype, stream, A,
+                       g_min);
 }
 
 // shared checks of kda_verify / kda_commit; returns KDA_OK with *noop set for B == 0

@@ -96,4 +96,25 @@ __device__ __forceinline__ void store8(typename DT::storage* p, const float (&x)
     }
 }
 
+// The gate g = g_min sigmoid(e^{A_h} z) ("NLP——技术报告解读-Kimi-K3", Model
+// Architecture / Kimi Delta Attention (KDA), lower-bounded decay), fused into
+// a kernel that consumes g: g = g_min / (1 + 2^{s2 z}) with
+// s2 = -e^{A_h} log2(e), in fp32 (hardware exp2 and reciprocal), so the decay
+// input never goes through HBM as g.  Off, it passes its argument through.
+struct GateZ {
+    bool on;
+    float s2, g_min;
+    __device__ __forceinline__ float operator()(float z) const
+    {
+        return on ? g_min * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(s2 * z)) : z;
+    }
+    // the gate of head h, or the identity when A is null
+    static __device__ __forceinline__ GateZ of_head(const float* A, int h, float g_min)
+    {
+        GateZ gz{A != nullptr, 0.f, g_min};
+        if (gz.on) gz.s2 = -__expf(A[h]) * 1.4426950408889634f;
+        return gz;
+    }
+};
+
 }  // namespace kda

@@ -32,7 +32,8 @@ __global__ void __launch_bounds__(256) decode_kernel(const typename DT::storage*
                                                      const typename DT::storage* __restrict__ g,
                                                      const typename DT::storage* __restrict__ beta,
                                                      float* __restrict__ state,
-                                                     typename DT::storage* __restrict__ o)
+                                                     typename DT::storage* __restrict__ o, int H,
+                                                     const float* __restrict__ gate_A, float g_min)
 {
     constexpr int CG = DV / 4;       // column groups of 4
     constexpr int RG = 256 / CG;     // row groups
@@ -49,6 +50,8 @@ __global__ void __launch_bounds__(256) decode_kernel(const typename DT::storage*
     const int rg = t / CG;
     const int c0 = rg * R;
 
+    // gate_A non-null: g holds the gate's input z, and the gate runs here
+    const GateZ gz = GateZ::of_head(gate_A, bh % H, g_min);
     float* S = state + int64_t(bh) * DK * DV;
     const auto* qb = q + int64_t(bh) * DK;
     const auto* kb = k + int64_t(bh) * DK;
@@ -64,7 +67,7 @@ __global__ void __launch_bounds__(256) decode_kernel(const typename DT::storage*
     float kr[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        const float a = __expf(load_elem<DT>(gb, c0 + r));
+        const float a = __expf(gz(load_elem<DT>(gb, c0 + r)));
         const float kc = load_elem<DT>(kb, c0 + r);
         const float qc = load_elem<DT>(qb, c0 + r);
         kr[r] = kc;
@@ -106,24 +109,25 @@ __global__ void __launch_bounds__(256) decode_kernel(const typename DT::storage*
 
 template <typename DT, int DK, int DV>
 hipError_t launch_decode_t(const void* q, const void* k, const void* v, const void* g,
-                           const void* beta, float* state, void* o, int BH, hipStream_t stream)
+                           const void* beta, float* state, void* o, int BH, int H, const float* gate_A,
+                           float g_min, hipStream_t stream)
 {
     using S = typename DT::storage;
     hipLaunchKernelGGL((decode_kernel<DT, DK, DV>), dim3(BH), dim3(256), 0, stream,
                        static_cast<const S*>(q), static_cast<const S*>(k), static_cast<const S*>(v),
                        static_cast<const S*>(g), static_cast<const S*>(beta), state,
-                       static_cast<S*>(o));
+                       static_cast<S*>(o), H, gate_A, g_min);
     return hipGetLastError();
 }
 
 template <typename DT>
 hipError_t launch_decode(const void* q, const void* k, const void* v, const void* g,
                          const void* beta, float* state, void* o, int BH, int dk, int dv,
-                         hipStream_t stream)
+                         hipStream_t stream, int H = 1, const float* gate_A = nullptr, float g_min = -5.f)
 {
 #define KDA_DEC(DKV, DVV)                                                                      \
     if (dk == DKV && dv == DVV)                                                                \
-        return launch_decode_t<DT, DKV, DVV>(q, k, v, g, beta, state, o, BH, stream);
+        return launch_decode_t<DT, DKV, DVV>(q, k, v, g, beta, state, o, BH, H, gate_A, g_min, stream);
     KDA_DEC(32, 32) KDA_DEC(32, 64) KDA_DEC(32, 128)
     KDA_DEC(64, 32) KDA_DEC(64, 64) KDA_DEC(64, 128)
     KDA_DEC(128, 32) KDA_DEC(128, 64) KDA_DEC(128, 128)

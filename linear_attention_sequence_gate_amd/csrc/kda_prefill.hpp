@@ -167,20 +167,6 @@ struct PrefillDev {
     float g_min;
 };
 
-// The gate fused into the decay stage ("NLP——技术报告解读-Kimi-K3", Model
-// Architecture / Kimi Delta Attention (KDA), lower-bounded decay):
-// g = g_min sigmoid(e^{A_h} z) = g_min / (1 + 2^{s2 z}) with
-// s2 = -e^{A_h} log2(e), in fp32, so the decay input never goes through HBM
-// as g.  Both passes over a segment apply it to the same z and get the same g.
-struct GateZ {
-    bool on;
-    float s2, g_min;
-    __device__ __forceinline__ float operator()(float z) const
-    {
-        return on ? g_min * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(s2 * z)) : z;
-    }
-};
-
 // Table entries (cu_seqlens clamped, segment, pass-1 and checkpoint offsets)
 __device__ __forceinline__ int32_t tab_cu(const PrefillDev& p, int n)
 {
@@ -706,6 +692,10 @@ __device__ __forceinline__ void prep_tiles(const PrepRegs<C, DT>& r, unsigned ch
     // or past the valid length add nothing)
     float c0[C::TPT], c1[C::TPT];
     float s0 = 0.f, s1 = 0.f;
+#ifdef KDA_PHASE_TIMING
+    asm volatile("" ::"v"(r.g[C::TPT - 1]));  // the raw loads have landed
+    pclk.mark(11);
+#endif
 #pragma unroll
     for (int i = 0; i < C::TPT; ++i) {
         const bool ok = tok0 + i < len;
@@ -964,8 +954,9 @@ prefill_block_kernel(PrefillDev p)
         const int part = lane / C::CPW;
         const int cpair = pw * C::CPW + lane % C::CPW;
         const int tok0 = part * C::TPT;
-        GateZ gz{p.gate_A != nullptr, 0.f, p.g_min};
-        if (gz.on) gz.s2 = -__expf(p.gate_A[h]) * 1.4426950408889634f;
+        // with the fused gate, g comes from z here; both passes apply it to
+        // the same z and get the same g
+        const GateZ gz = GateZ::of_head(p.gate_A, h, p.g_min);
         PrepRegs<C, DT> pr;
         if (nblk > 0) {
             prep_load<C, DT, SUMMARY>(pr, p, t_begin, blen(0), h, ptid, cpair, tok0);

@@ -75,14 +75,15 @@ __device__ __forceinline__ void load_run(const typename DT::storage* p, float (&
 // the d_v / 32 waves of one state (one slice each): they share nothing and
 // never synchronise, but run side by side, so each 512-byte state row is read
 // (and written) by the four waves at about the same time.
-template <typename DT, int DK, int DV, bool EMIT_O, bool WRITE_S>
+template <typename DT, int DK, int DV, bool EMIT_O, bool WRITE_S, bool GATED>
 __global__ void __launch_bounds__(64 * (DV / 32)) step_wave_kernel(const typename DT::storage* __restrict__ q,
                                                        const typename DT::storage* __restrict__ k,
                                                        const typename DT::storage* __restrict__ v,
                                                        const typename DT::storage* __restrict__ g,
                                                        const typename DT::storage* __restrict__ beta,
                                                        const int32_t* __restrict__ n_accept, float* state,
-                                                       typename DT::storage* __restrict__ o, int K, int H)
+                                                       typename DT::storage* __restrict__ o, int K, int H,
+                                                       const float* __restrict__ gate_A, float g_min)
 {
     constexpr int R = DK / 8;  // rows per lane
     static_assert(DV % 32 == 0 && (R == 4 || R == 8 || R == 16), "unsupported shape");
@@ -101,6 +102,9 @@ __global__ void __launch_bounds__(64 * (DV / 32)) step_wave_kernel(const typenam
         if (steps == 0) return;  // nothing accepted: the state is left untouched
     }
 
+    // GATED: g holds the gate's input z, and the gate runs here (a separate
+    // instantiation, so the plain kernel keeps its register budget)
+    const GateZ gz = GateZ::of_head(GATED ? gate_A : nullptr, h, g_min);
     float* S = state + int64_t(bh) * DK * DV + col;
     f32x4 s[R];
 #pragma unroll
@@ -116,7 +120,7 @@ __global__ void __launch_bounds__(64 * (DV / 32)) step_wave_kernel(const typenam
         float kq = 0.f;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            s[r] *= __expf(a[r]);
+            s[r] *= __expf(GATED ? gz(a[r]) : a[r]);
             pk += kk[r] * s[r];
             if (EMIT_O) {
                 pq += qq[r] * s[r];
@@ -164,16 +168,16 @@ inline bool step_wave_aligned(const void* q, const void* k, const void* v, const
     return al(q) && al(k) && al(v) && al(g) && al(o);
 }
 
-template <typename DT, int DK, int DV, bool EMIT_O, bool WRITE_S>
+template <typename DT, int DK, int DV, bool EMIT_O, bool WRITE_S, bool GATED = false>
 hipError_t launch_step_wave_t(const void* q, const void* k, const void* v, const void* g, const void* beta,
                               const int32_t* n_accept, float* state, void* o, int B, int K, int H,
-                              hipStream_t stream)
+                              const float* gate_A, float g_min, hipStream_t stream)
 {
     using S = typename DT::storage;
-    hipLaunchKernelGGL((step_wave_kernel<DT, DK, DV, EMIT_O, WRITE_S>), dim3(unsigned(B * H)),
+    hipLaunchKernelGGL((step_wave_kernel<DT, DK, DV, EMIT_O, WRITE_S, GATED>), dim3(unsigned(B * H)),
                        dim3(64 * (DV / 32)), 0, stream, static_cast<const S*>(q), static_cast<const S*>(k),
                        static_cast<const S*>(v), static_cast<const S*>(g), static_cast<const S*>(beta), n_accept,
-                       state, static_cast<S*>(o), K, H);
+                       state, static_cast<S*>(o), K, H, gate_A, g_min);
     return hipGetLastError();
 }
 
@@ -181,23 +185,31 @@ hipError_t launch_step_wave_t(const void* q, const void* k, const void* v, const
 template <typename DT, int DKV, int DVV>
 hipError_t launch_step_wave_shape(int mode, const void* q, const void* k, const void* v, const void* g,
                                   const void* beta, const int32_t* n_accept, float* state, void* o, int B, int K,
-                                  int H, hipStream_t stream)
+                                  int H, const float* gate_A, float g_min, hipStream_t stream)
 {
+    if (mode == 0 && gate_A)  // decode with the gate fused
+        return launch_step_wave_t<DT, DKV, DVV, true, true, true>(q, k, v, g, beta, n_accept, state, o, B, K, H,
+                                                                  gate_A, g_min, stream);
     if (mode == 0)
-        return launch_step_wave_t<DT, DKV, DVV, true, true>(q, k, v, g, beta, n_accept, state, o, B, K, H, stream);
+        return launch_step_wave_t<DT, DKV, DVV, true, true>(q, k, v, g, beta, n_accept, state, o, B, K, H, gate_A,
+                                                            g_min, stream);
     if (mode == 1)
-        return launch_step_wave_t<DT, DKV, DVV, true, false>(q, k, v, g, beta, n_accept, state, o, B, K, H, stream);
-    return launch_step_wave_t<DT, DKV, DVV, false, true>(q, k, v, g, beta, n_accept, state, o, B, K, H, stream);
+        return launch_step_wave_t<DT, DKV, DVV, true, false>(q, k, v, g, beta, n_accept, state, o, B, K, H,
+                                                             gate_A, g_min, stream);
+    return launch_step_wave_t<DT, DKV, DVV, false, true>(q, k, v, g, beta, n_accept, state, o, B, K, H, gate_A,
+                                                         g_min, stream);
 }
 
 template <typename DT>
 hipError_t launch_step_wave(int mode, const void* q, const void* k, const void* v, const void* g,
                             const void* beta, const int32_t* n_accept, float* state, void* o, int B, int K,
-                            int H, int dk, int dv, hipStream_t stream)
+                            int H, int dk, int dv, hipStream_t stream, const float* gate_A = nullptr,
+                            float g_min = -5.f)
 {
 #define KDA_STEP(DKV, DVV)                                                                                       \
     if (dk == DKV && dv == DVV)                                                                                  \
-        return launch_step_wave_shape<DT, DKV, DVV>(mode, q, k, v, g, beta, n_accept, state, o, B, K, H, stream);
+        return launch_step_wave_shape<DT, DKV, DVV>(mode, q, k, v, g, beta, n_accept, state, o, B, K, H, gate_A, \
+                                                    g_min, stream);
     KDA_STEP(32, 32) KDA_STEP(32, 64) KDA_STEP(32, 128)
     KDA_STEP(64, 32) KDA_STEP(64, 64) KDA_STEP(64, 128)
     KDA_STEP(128, 32) KDA_STEP(128, 64) KDA_STEP(128, 128)

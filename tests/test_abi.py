@@ -242,3 +242,26 @@ def test_prefill_gated_validation(L):
     assert b"kda_prefill_gated" in L.kda_last_error()
     # no tokens and no final state: nothing to do, A may be NULL
     assert call(T=0, A=None, fin=None, q=None, k=None, v=None, z=None, beta=None, o=None) == 0
+
+
+def test_decode_gated_validation(L):
+    B, H, dk, dv = 4, 2, 64, 64
+
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE + (1 << 20), v=FAKE + (2 << 20), z=FAKE + (3 << 20), A=FAKE + (5 << 20),
+                 gmin=-5.0, beta=FAKE + (4 << 20), S=FAKE + (8 << 20), o=FAKE + (16 << 20), B=B, H=H,
+                 dk=dk, dv=dv, dt=BF16)
+        a.update(kw)
+        return L.kda_decode_step_gated(a["q"], a["k"], a["v"], a["z"], a["A"], a["gmin"], a["beta"], a["S"],
+                                       a["o"], a["B"], a["H"], a["dk"], a["dv"], a["dt"], None)
+
+    assert call(A=None) == 1
+    assert call(gmin=0.0) == 1
+    assert call(gmin=float("inf")) == 1
+    assert call(A=FAKE + (16 << 20)) == 1                     # A inside o
+    assert call(A=FAKE + (8 << 20) + 64) == 1                 # A inside the state
+    assert call(z=None) == 1
+    assert call(dk=96) == 2
+    assert call(S=FAKE + (8 << 20) + 4) == 1                  # state not 16-byte aligned
+    assert b"kda_decode_step_gated" in L.kda_last_error()
+    assert call(B=0, A=None) == 0                             # nothing to do

@@ -32,21 +32,32 @@ def kda():
     return m
 
 
-def oracle_rows(wl, t0, t1, heads):
+def oracle_rows(wl, t0, t1, heads, gated=False):
+    """Oracle inputs for rows [t0, t1) of `heads`.  The separate gate returns g
+    rounded to bf16; the gate fused into kda_prefill_gated keeps it in fp32."""
     x = {n: synth.token_rows(wl, n, t0, t1)[:, heads] for n in ("q", "k", "v", "z", "beta")}
-    g = oracle.gate(x["z"], synth.gate_A(wl)[heads], round_bf16=True)
+    g = oracle.gate(x["z"], synth.gate_A(wl)[heads], round_bf16=not gated)
     return x, g
 
 
-def test_prefill_1m_windows(kda):
+def gpu_prefill(kda, xs, A, gated, **kw):
+    """kda_gate + kda_prefill, or the fused kda_prefill_gated, on device tensors."""
+    if gated:
+        return kda.kda_prefill_gated(xs["q"], xs["k"], xs["v"], xs["z"], A, xs["beta"], **kw)
+    g = kda.kda_gate(xs["z"], A)
+    del xs["z"]
+    return kda.kda_prefill(xs["q"], xs["k"], xs["v"], g, xs["beta"], **kw)
+
+
+@pytest.mark.parametrize("gated", [False, True])
+def test_prefill_1m_windows(kda, gated):
     import torch
     wl = synth.PREFILL_1M
     T = wl.T_total
-    announce(f"prefill_1m full size: H={wl.H} T={T}")
+    announce(f"prefill_1m full size: H={wl.H} T={T} gated={gated}")
     xs = {n: dev_stream(wl, n) for n in ("q", "k", "v", "z", "beta")}
-    g = kda.kda_gate(xs["z"], dev(synth.gate_A(wl)))
-    del xs["z"]
-    o, S = kda.kda_prefill(xs["q"], xs["k"], xs["v"], g, xs["beta"])
+    o, S = gpu_prefill(kda, xs, dev(synth.gate_A(wl)), gated)
+    del xs
     torch.cuda.synchronize()
     seg = 256 * 64  # the planner's segment length for this shape (tokens)
     heads = [2, 6]
@@ -54,7 +65,7 @@ def test_prefill_1m_windows(kda):
     windows = [(0, 256), (3 * T // 4 + 5000, 3 * T // 4 + 5256), (32 * seg - 37, 32 * seg + 219), (T - 256, T)]
     for a, b in windows:
         s0 = max(0, a - W)
-        x, gw = oracle_rows(wl, s0, b, heads)
+        x, gw = oracle_rows(wl, s0, b, heads, gated)
         if s0 > 0:  # damping of the state the window starts without
             damp = float(np.max(np.sum(np.max(gw[: a - s0], axis=2), axis=0)))
             assert damp < -60.0, f"warm-up too short: log damping {damp:.1f}"
@@ -70,25 +81,25 @@ def test_prefill_1m_windows(kda):
     assert torch.isfinite(o).all() and torch.isfinite(S).all()
 
 
-def test_varlen_64_sampled_sequences(kda):
+@pytest.mark.parametrize("gated", [False, True])
+def test_varlen_64_sampled_sequences(kda, gated):
     import torch
     wl = synth.VARLEN_64
     T = wl.T_total
     cu = wl.cu_seqlens
     lens = np.asarray(wl.seqlens)
-    announce(f"varlen_64 full size: N={wl.N} H={wl.H} T={T}")
+    announce(f"varlen_64 full size: N={wl.N} H={wl.H} T={T} gated={gated}")
     xs = {n: dev_stream(wl, n, rows=1 << 14) for n in ("q", "k", "v", "z", "beta")}
-    g = kda.kda_gate(xs["z"], dev(synth.gate_A(wl)))
-    del xs["z"]
     S0 = synth.initial_state(wl)
-    o, S = kda.kda_prefill(xs["q"], xs["k"], xs["v"], g, xs["beta"],
-                           cu_seqlens=torch.from_numpy(cu).cuda(), initial_state=dev(S0))
+    o, S = gpu_prefill(kda, xs, dev(synth.gate_A(wl)), gated, cu_seqlens=torch.from_numpy(cu).cuda(),
+                       initial_state=dev(S0))
+    del xs
     torch.cuda.synchronize()
     order = np.argsort(lens)
     cases = [(int(n), list(range(wl.H))) for n in order[:3]] + [(int(order[-1]), [5, 21])]
     for n, heads in cases:
         a, b = int(cu[n]), int(cu[n + 1])
-        x, gw = oracle_rows(wl, a, b, heads)
+        x, gw = oracle_rows(wl, a, b, heads, gated)
         o_ref, S_ref = oracle.prefill(x["q"], x["k"], x["v"], gw, x["beta"], S0=S0[n:n + 1][:, heads])
         eo = relerr(host(o[a:b, heads]), o_ref)
         es = relerr(host(S[n, heads]), S_ref[0])

@@ -68,50 +68,65 @@ def _decode_inputs(wl, set_index, B):
     return d
 
 
+def _decode(kda, gated, q, k, v, z, A, beta, St, o=None):
+    """kda_gate + kda_decode_step, or the fused kda_decode_step_gated."""
+    if gated:
+        return kda.kda_decode_step_gated(q, k, v, z, A, beta, St, o=o)
+    return kda.kda_decode_step(q, k, v, kda.kda_gate(z, A), beta, St, o=o)
+
+
+def _oracle_g(x, A, gated, dtype="bf16"):
+    """The oracle's g: rounded to the storage dtype for the separate gate, fp32
+    (unrounded) for the fused one."""
+    return oracle.gate(x["z"], A, round_bf16=(dtype == "bf16" and not gated))
+
+
+@pytest.mark.parametrize("gated", [False, True])
 @pytest.mark.parametrize("unaligned", [False, True])  # one-wave slice kernel / workgroup-per-state kernel
 @pytest.mark.parametrize("dk,dv,dtype", [(128, 128, "bf16"), (64, 32, "bf16"), (32, 128, "bf16"),
                                          (32, 32, "f32"), (128, 64, "f32")])
-def test_decode_small(kda, dk, dv, dtype, unaligned):
+def test_decode_small(kda, dk, dv, dtype, unaligned, gated):
     import torch
     wl = synth.DECODE_B256.with_(H=3, dk=dk, dv=dv, dtype=dtype, seqlens=(1,) * 5)
-    announce(f"decode small dk={dk} dv={dv} {dtype} unaligned={unaligned}")
+    announce(f"decode small dk={dk} dv={dv} {dtype} unaligned={unaligned} gated={gated}")
     B = 5
     x = _decode_inputs(wl, 0, B)
     A = synth.gate_A(wl)
     S0 = synth.initial_state(wl)
     St = dev(S0)
-    g = kda.kda_gate(dev(x["z"], dtype), dev(A))
     q = dev(x["q"], dtype)
     if unaligned:
         q = dev_unaligned(q)
-    o = kda.kda_decode_step(q, dev(x["k"], dtype), dev(x["v"], dtype), g, dev(x["beta"], dtype), St)
-    gr = oracle.gate(x["z"], A, round_bf16=(dtype == "bf16"))
+    o = _decode(kda, gated, q, dev(x["k"], dtype), dev(x["v"], dtype), dev(x["z"], dtype), dev(A),
+                dev(x["beta"], dtype), St)
+    gr = _oracle_g(x, A, gated, dtype)
     o_ref, S_ref = oracle.decode_step(x["q"], x["k"], x["v"], gr, x["beta"], S0)
     tol = TOL[dtype]
     assert relerr(host(o), o_ref) < tol
     assert relerr(host(St), S_ref) < tol
 
 
-def test_decode_full_one_step(kda):
+@pytest.mark.parametrize("gated", [False, True])
+def test_decode_full_one_step(kda, gated):
     """B=256, H=32, d=128: one step, every output and every state entry."""
     wl = synth.DECODE_B256
     B = wl.N
-    announce("decode B=256 H=32 one step")
+    announce(f"decode B=256 H=32 one step gated={gated}")
     x = _decode_inputs(wl, 0, B)
     A = synth.gate_A(wl)
     S0 = synth.initial_state(wl)
     St = dev(S0)
-    g = kda.kda_gate(dev(x["z"], "bf16"), dev(A))
-    o = kda.kda_decode_step(dev(x["q"], "bf16"), dev(x["k"], "bf16"), dev(x["v"], "bf16"), g,
-                            dev(x["beta"], "bf16"), St)
-    gr = oracle.gate(x["z"], A, round_bf16=True)
+    o = _decode(kda, gated, dev(x["q"], "bf16"), dev(x["k"], "bf16"), dev(x["v"], "bf16"), dev(x["z"], "bf16"),
+                dev(A), dev(x["beta"], "bf16"), St)
+    gr = _oracle_g(x, A, gated)
     o_ref, S_ref = oracle.decode_step(x["q"], x["k"], x["v"], gr, x["beta"], S0)
     e_o, e_s = relerr(host(o), o_ref), relerr(host(St), S_ref)
     print(f"decode 1 step: o err {e_o:.2e}, state err {e_s:.2e}")
     assert e_o < TOL["bf16"] and e_s < TOL["bf16"]
 
 
-def test_decode_full_1000_steps_sampled(kda):
+@pytest.mark.parametrize("gated", [False, True])
+def test_decode_full_1000_steps_sampled(kda, gated):
     """1000 consecutive in-place steps at B=256, H=32 (inputs cycle through 8
     seeded sets); 64 sampled (b, h) states and their last outputs are replayed
     by the oracle over all 1000 steps."""
@@ -119,26 +134,30 @@ def test_decode_full_1000_steps_sampled(kda):
     wl = synth.DECODE_B256
     B, H = wl.N, wl.H
     steps, nsets = 1000, 8
-    announce("decode B=256 H=32 1000 steps")
+    announce(f"decode B=256 H=32 1000 steps gated={gated}")
     A = synth.gate_A(wl)
     S0 = synth.initial_state(wl)
     sets = [_decode_inputs(wl, s, B) for s in range(nsets)]
     dsets = []
     for x in sets:
-        d = {n: dev(x[n], "bf16") for n in ("q", "k", "v", "beta")}
-        d["g"] = kda.kda_gate(dev(x["z"], "bf16"), dev(A))
+        d = {n: dev(x[n], "bf16") for n in ("q", "k", "v", "z", "beta")}
+        d["g"] = kda.kda_gate(d["z"], dev(A))
         dsets.append(d)
     St = dev(S0)
+    Ad = dev(A)
     o = torch.empty((B, H, wl.dv), dtype=torch.bfloat16, device="cuda")
     for t in range(steps):
         d = dsets[t % nsets]
-        kda.kda_decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], St, o=o)
+        if gated:
+            kda.kda_decode_step_gated(d["q"], d["k"], d["v"], d["z"], Ad, d["beta"], St, o=o)
+        else:
+            kda.kda_decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], St, o=o)
     torch.cuda.synchronize()
     rng = np.random.default_rng(7)
     units = rng.choice(B * H, size=64, replace=False)
     bs, hs = units // H, units % H
     S = S0[bs, hs][None].astype(np.float64)  # [1, 64, dk, dv] as 64 "heads" of one batch row
-    gr = [oracle.gate(x["z"], A, round_bf16=True) for x in sets]
+    gr = [_oracle_g(x, A, gated) for x in sets]
     for t in range(steps):
         x = sets[t % nsets]
         pick = lambda a: a[bs, hs][None]
