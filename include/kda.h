@@ -125,7 +125,8 @@ size_t kda_prefill_workspace_size(int64_t T_total, int N, int H, int d_k, int d_
  * composed exactly through S_end = S~ + M S_in.
  * Errors: KDA_ERR_INVALID_ARGUMENT (null required pointer, N < 1, T_total < 0,
  * N != 1 without cu_seqlens, forbidden aliasing), KDA_ERR_UNSUPPORTED (d_k,
- * d_v, chunk, H or dtype outside the supported set),
+ * d_v, chunk, H or dtype outside the supported set, T_total > 2^31 - 1:
+ * token offsets are int32 like cu_seqlens),
  * KDA_ERR_WORKSPACE_TOO_SMALL, KDA_ERR_HIP.
  */
 kda_status_t kda_prefill(const void* q, const void* k, const void* v, const void* g,

@@ -253,7 +253,8 @@ kda_status_t kda_commit(const void* k, const void* v, const void* g, const void*
 size_t kda_prefill_workspace_size(int64_t T_total, int N, int H, int d_k, int d_v, int chunk,
                                   kda_dtype_t dtype)
 {
-    if (T_total < 0 || N < 1 || H < 1 || H > KDA_MAX_HEADS || !dim_ok(d_k) || !dim_ok(d_v) || chunk != 64 ||
+    if (T_total < 0 || T_total > int64_t(0x7fffffff) || N < 1 || H < 1 || H > KDA_MAX_HEADS || !dim_ok(d_k) ||
+        !dim_ok(d_v) || chunk != 64 ||
         !dtype_ok(dtype) || (dtype == KDA_F32 && (d_k != 32 || d_v > 64)))
         return 0;
     return kda::prefill_plan(T_total, N, H, d_k, d_v).workspace_bytes;
@@ -279,8 +280,8 @@ static kda_status_t prefill_impl(const char* who, const void* q, const void* k, 
     if (chunk != 64) return fail(KDA_ERR_UNSUPPORTED, "%s: chunk=%d (only 64)", who, chunk);
     if (dtype == KDA_F32 && (d_k != 32 || d_v > 64))
         return fail(KDA_ERR_UNSUPPORTED, "%s: fp32 tensors need d_k = 32, d_v <= 64", who);
-    if (T_total > (int64_t(1) << 40))
-        return fail(KDA_ERR_UNSUPPORTED, "%s: T_total too large", who);
+    if (T_total > int64_t(0x7fffffff))  // token offsets are int32, as cu_seqlens
+        return fail(KDA_ERR_UNSUPPORTED, "%s: T_total > 2^31 - 1", who);
     if (T_total > 0 && (!q || !k || !v || !g || !beta || !o))
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: null token tensor", who);
     if (gate_A) {

@@ -92,6 +92,8 @@ def test_prefill_workspace_size(L):
     assert ws(256, 1, 2, 32, 32, dtype=F32) > 0
     assert ws(256, 1, 16384, 32, 32) > 0
     assert ws(256, 1, 16385, 32, 32) == 0                 # H above KDA_MAX_HEADS
+    assert ws((1 << 31) - 1, 1, 1, 32, 32) > 0
+    assert ws(1 << 31, 1, 1, 32, 32) == 0                 # token offsets are int32
     # a sequence too short to split needs no segment buffers
     small = ws(64 * 16, 1, 32, 128, 128)
     assert small < 4096
@@ -122,6 +124,7 @@ def test_prefill_validation(L):
     assert call(dt=F32, dk=128, dv=128) == 2
     assert call(dt=9) == 2
     assert call(H=16385) == 2                               # H above KDA_MAX_HEADS
+    assert call(T=1 << 31) == 2                             # token offsets are int32
     assert call(q=None) == 1
     assert call(o=None) == 1
     if need > 0:
