@@ -114,3 +114,60 @@ def test_prefill_weak_decay_long(kda):
     wl = synth.PREFILL_8K.with_(H=4, seqlens=(4096,), z_shift=-3.0, state_std=0.1)
     check(kda, wl)
     check(kda, wl, seg=4, tag="seg4")
+
+
+@pytest.mark.parametrize("case", ["beta0", "alpha1", "gmin", "alpha1_beta1_orthonormal"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_prefill_special_values(kda, case, dtype):
+    """Exact edge values of the decay and the write strength, given to
+    kda_prefill directly: beta = 0 (pure per-channel decay), g = 0 (alpha = 1,
+    no forgetting), g = -5 everywhere (the strongest decay the gate allows),
+    and alpha = beta = 1 with orthonormal keys (exact recall of every value).
+    Segments of 2 chunks, so the summary pass and the scan see them too."""
+    import torch
+    dk = dv = 32
+    # weak decay for beta = 0 (z shifted by -4), so the decayed state stays far
+    # above the fp32 underflow over 300 tokens and the relative error means something
+    wl = synth.VARLEN_64.with_(H=2, dk=dk, dv=dv, dtype=dtype, seqlens=(300, 130), state_std=0.1,
+                               z_shift=-4.0 if case == "beta0" else 0.0)
+    announce(f"prefill special values {case} {dtype}")
+    x = synth.prefill_inputs(wl)
+    T = wl.T_total
+    S0 = synth.initial_state(wl)
+    g = np.zeros((T, wl.H, dk), dtype=np.float32)
+    if case == "beta0":
+        x["beta"] = np.zeros_like(x["beta"])
+        g = oracle.gate(x["z"], x["A"], round_bf16=(dtype == "bf16")).astype(np.float32)
+    elif case == "gmin":
+        g[:] = -5.0
+    elif case == "alpha1_beta1_orthonormal":
+        # per sequence and head, keys = rows of an orthogonal matrix (<= d_k of them)
+        rng = np.random.default_rng(5)
+        wl = wl.with_(seqlens=(dk, 17))
+        T = wl.T_total
+        x = {n: a[:T] for n, a in x.items() if n != "A"} | {"A": x["A"]}
+        g = np.zeros((T, wl.H, dk), dtype=np.float32)
+        x["beta"] = np.ones((T, wl.H), dtype=np.float32)
+        for a, b in zip(wl.cu_seqlens[:-1], wl.cu_seqlens[1:]):
+            for h in range(wl.H):
+                qm, _ = np.linalg.qr(rng.standard_normal((dk, dk)))
+                x["k"][a:b, h] = qm[: b - a]
+                x["q"][a:b, h] = qm[: b - a]  # query each key back
+        if dtype == "bf16":  # keys must be exact in the storage dtype
+            for n in ("q", "k"):
+                x[n] = oracle.round_bf16(x[n]).astype(np.float32)
+        S0 = np.zeros_like(synth.initial_state(wl))
+    cu = torch.from_numpy(wl.cu_seqlens).to("cuda")
+    with SegEnv(2):
+        o, S = kda.kda_prefill(dev(x["q"], dtype), dev(x["k"], dtype), dev(x["v"], dtype), dev(g, dtype),
+                               dev(x["beta"], dtype), cu_seqlens=cu, initial_state=dev(S0))
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.prefill(x["q"], x["k"], x["v"], g, x["beta"], cu=wl.cu_seqlens, S0=S0)
+    tol = TOL[dtype]
+    assert relerr(host(o), o_ref) < tol and relerr(host(S), S_ref) < tol
+    if case == "beta0":  # closed form: the state only decays, channel by channel
+        for n, (a, b) in enumerate(zip(wl.cu_seqlens[:-1], wl.cu_seqlens[1:])):
+            decay = np.exp(np.sum(g[a:b].astype(np.float64), axis=0))  # [H, dk]
+            assert relerr(host(S[n]), decay[:, :, None] * S0[n]) < tol
+    if case == "alpha1_beta1_orthonormal" and dtype == "f32":  # exact recall: o_t = v_t
+        assert relerr(host(o), x["v"]) < tol
