@@ -14,7 +14,8 @@ kda_gate + kda_decode_step), and verify/commit (B=256, K=4) under
 by two HIP events on the stream the library launches on (an event between
 calls would serialise them).  `roofline` covers the prefill call (algorithmic
 bytes per call); each roofline also carries the fraction of a plain 1 GiB
-device copy measured on the same device.  `cpu_baseline` is the fp64 oracle
+device copy measured on the same device, and the prefill's matrix-core rate
+is also given against a plain bf16 GEMM measured there.  `cpu_baseline` is the fp64 oracle
 timed on this host on a bounded sample; `verified` compares the timed run's
 output with that oracle pass (whole workload, normwise max relative error).
 
@@ -367,6 +368,19 @@ def main():
     for r in (roofline, decode["roofline"], spec["verify"]["roofline"], spec["commit"]["roofline"]):
         r["measured_copy_gbs"] = round(copy_gbs, 1)
         r["frac_of_measured_copy"] = round(r["achieved"] / copy_gbs, 4)
+    # achievable bf16 matrix-core rate on this device: a plain 8192^3 bf16 GEMM
+    # (the vendor library), for the prefill's MFMA fraction against a measured
+    # rate as well as the published peak
+    ga = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+    gb = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+    gc = torch.empty(8192, 8192, device=dev, dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.mm(ga, gb, out=gc)
+    gemm_ms = timed_loop(lambda i: torch.mm(ga, gb, out=gc), 10)
+    gemm_tflops = 2.0 * 8192 ** 3 / (gemm_ms * 1e-3) / 1e12
+    del ga, gb, gc
+    roofline["measured_gemm_tflops"] = round(gemm_tflops, 1)
+    roofline["mfma_frac_of_measured_gemm"] = round(roofline["mfma_tflops"] / gemm_tflops, 4)
 
     if args.copy_calib:  # plain copy of known size, for the HBM counter calibration
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
