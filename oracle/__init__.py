@@ -41,8 +41,9 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_decode_step.argtypes = [P, P, P, P, P, P, P, I, I, I, I]
     lib.oracle_wy_T.argtypes = [P, P, P, I, I, P]
     lib.oracle_round_bf16.argtypes = [P, L]
+    lib.oracle_backward.argtypes = [P, P, P, P, P, P, I, I, I, I, P, P, P, P, P, P, P, P, P, I]
     for f in ("oracle_gate", "oracle_prefill", "oracle_prefill_chunked",
-              "oracle_decode_step", "oracle_wy_T", "oracle_round_bf16"):
+              "oracle_decode_step", "oracle_wy_T", "oracle_round_bf16", "oracle_backward"):
         getattr(lib, f).restype = None
     return lib
 
@@ -135,6 +136,28 @@ def decode_step(q, k, v, g, beta, S, lib=None):
     o = np.empty((B, H, dv))
     lib.oracle_decode_step(_p(q), _p(k), _p(v), _p(g), _p(beta), _p(S), _p(o), B, H, dk, dv)
     return o, S
+
+
+def backward(q, k, v, g, beta, dO=None, dS_fin=None, cu=None, S0=None, threads: int | None = None,
+             lib=None) -> dict:
+    """Gradients of L = sum_t <dO_t, o_t> + <dS_fin, S_T> for the token-serial
+    recurrence (every state of a sequence is kept: small cases).  Returns a dict
+    with dq, dk, dg [T, H, dk], dv [T, H, dv], dbeta [T, H], dS0 [N, H, dk, dv]."""
+    lib = lib or load()
+    q, k, v, g, beta = _d(q), _d(k), _d(v), _d(g), _d(beta)
+    T, H, dk = k.shape
+    dv = v.shape[2]
+    cu = _cu(cu, T)
+    N = cu.shape[0] - 1
+    S0 = None if S0 is None else _d(S0)
+    dO = None if dO is None else _d(dO)
+    dS_fin = None if dS_fin is None else _d(dS_fin)
+    out = {"dq": np.empty((T, H, dk)), "dk": np.empty((T, H, dk)), "dv": np.empty((T, H, dv)),
+           "dg": np.empty((T, H, dk)), "dbeta": np.empty((T, H)), "dS0": np.empty((N, H, dk, dv))}
+    lib.oracle_backward(_p(q), _p(k), _p(v), _p(g), _p(beta), _p(cu), N, H, dk, dv, _p(S0), _p(dO), _p(dS_fin),
+                        _p(out["dq"]), _p(out["dk"]), _p(out["dv"]), _p(out["dg"]), _p(out["dbeta"]),
+                        _p(out["dS0"]), threads or default_threads())
+    return out
 
 
 def wy_T(k, g, beta, lib=None) -> np.ndarray:

@@ -28,6 +28,8 @@
  *                          in fp64 with every e^{G_r - G_i} taken directly; used
  *                          only to check that chunking changes nothing.
  *   oracle_wy_T            the per-chunk triangular solve alone, for its pin.
+ *   oracle_backward        reverse-mode gradients of the token-serial recurrence
+ *                          (every state of a sequence is kept: small cases).
  *   oracle_round_bf16      round doubles to the nearest bf16 (ties to even).
  */
 #include <math.h>
@@ -250,6 +252,115 @@ void oracle_prefill_chunked(const double* q, const double* k, const double* v,
         }
         if (S_final) memcpy(S_final + w * ssz, S, sizeof(double) * (size_t)ssz);
         free(S); free(G); free(A); free(T); free(W); free(U); free(P);
+    }
+}
+
+/* Gradients of L = sum_t <dO_t, o_t> + <dS_fin, S_T> through the recurrence
+ * of token_step, taken backwards token by token (reverse-mode, the chain rule
+ * applied to each line of the step).  With Sp = Diag(a) S_prev, a = exp(g),
+ * w = Sp^T k, r = v - w, u = beta r, S = Sp + k u^T, o = S^T q:
+ *   dS += q dO^T            dq = S dO
+ *   du = dS^T k             dk = dS u
+ *   dv = beta du            dbeta = <du, r>
+ *   dw = -beta du           dk += Sp dw      dSp = dS + k dw^T
+ *   dg_c = a_c <dSp[c,:], S_prev[c,:]>        dS_prev = Diag(a) dSp
+ * S0, dO and dS_fin may be NULL (zero).  Every state of a sequence is kept,
+ * so memory grows as T dk dv per unit: for small cases. */
+void oracle_backward(const double* q, const double* k, const double* v, const double* g,
+                     const double* beta, const int64_t* cu, int N, int H, int dk, int dv,
+                     const double* S0, const double* dO, const double* dS_fin, double* dq,
+                     double* dk_out, double* dv_out, double* dg, double* dbeta, double* dS0,
+                     int nthreads)
+{
+    const int64_t units = (int64_t)N * H;
+    const int64_t ssz = (int64_t)dk * dv;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(pick_threads(nthreads))
+    for (int64_t w = 0; w < units; ++w) {
+        const int n = (int)(w / H), h = (int)(w % H);
+        const int64_t T0 = cu[n], L = cu[n + 1] - cu[n];
+        /* states[i] = S before token T0 + i, for i = 0 .. L (states[L] = S_T) */
+        double* states = (double*)malloc(sizeof(double) * (size_t)((L + 1) * ssz));
+        double* dS = (double*)malloc(sizeof(double) * (size_t)(3 * ssz + 4 * dv + dk));
+        double* Sp = dS + ssz;
+        double* Sc = Sp + ssz;
+        double* u = Sc + ssz;
+        double* r = u + dv;
+        double* du = r + dv;
+        double* dw = du + dv;
+        double* a = dw + dv;
+        if (S0) memcpy(states, S0 + w * ssz, sizeof(double) * (size_t)ssz);
+        else memset(states, 0, sizeof(double) * (size_t)ssz);
+        for (int64_t i = 0; i < L; ++i) {
+            const int64_t th = (T0 + i) * H + h;
+            memcpy(states + (i + 1) * ssz, states + i * ssz, sizeof(double) * (size_t)ssz);
+            token_step(dk, dv, states + (i + 1) * ssz, q + th * dk, k + th * dk, v + th * dv, g + th * dk,
+                       beta[th], NULL, u);
+        }
+        if (dS_fin) memcpy(dS, dS_fin + w * ssz, sizeof(double) * (size_t)ssz);
+        else memset(dS, 0, sizeof(double) * (size_t)ssz);
+        for (int64_t i = L - 1; i >= 0; --i) {
+            const int64_t th = (T0 + i) * H + h;
+            const double* Sprev = states + i * ssz;
+            const double *qt = q + th * dk, *kt = k + th * dk, *vt = v + th * dv, *gt = g + th * dk;
+            const double bt = beta[th];
+            /* forward quantities of this token */
+            for (int c = 0; c < dk; ++c) a[c] = exp(gt[c]);
+            for (int c = 0; c < dk; ++c)
+                for (int j = 0; j < dv; ++j) Sp[c * dv + j] = a[c] * Sprev[c * dv + j];
+            for (int j = 0; j < dv; ++j) {
+                double wj = 0.0;
+                for (int c = 0; c < dk; ++c) wj += kt[c] * Sp[c * dv + j];
+                r[j] = vt[j] - wj;
+                u[j] = bt * r[j];
+            }
+            for (int c = 0; c < dk; ++c)
+                for (int j = 0; j < dv; ++j) Sc[c * dv + j] = Sp[c * dv + j] + kt[c] * u[j];
+            /* o = S^T q */
+            if (dO) {
+                const double* dOt = dO + th * dv;
+                for (int c = 0; c < dk; ++c) {
+                    double s = 0.0;
+                    for (int j = 0; j < dv; ++j) {
+                        dS[c * dv + j] += qt[c] * dOt[j];
+                        s += Sc[c * dv + j] * dOt[j];
+                    }
+                    dq[th * dk + c] = s;
+                }
+            } else {
+                for (int c = 0; c < dk; ++c) dq[th * dk + c] = 0.0;
+            }
+            /* S = Sp + k u^T */
+            for (int j = 0; j < dv; ++j) {
+                double s = 0.0;
+                for (int c = 0; c < dk; ++c) s += kt[c] * dS[c * dv + j];
+                du[j] = s;
+            }
+            double db = 0.0;
+            for (int j = 0; j < dv; ++j) {
+                dv_out[th * dv + j] = bt * du[j];
+                db += du[j] * r[j];
+                dw[j] = -bt * du[j];
+            }
+            dbeta[th] = db;
+            for (int c = 0; c < dk; ++c) {
+                double s = 0.0;
+                for (int j = 0; j < dv; ++j) s += dS[c * dv + j] * u[j] + Sp[c * dv + j] * dw[j];
+                dk_out[th * dk + c] = s;
+            }
+            /* dSp = dS + k dw^T; then through Sp = Diag(a) S_prev */
+            for (int c = 0; c < dk; ++c) {
+                double s = 0.0;
+                for (int j = 0; j < dv; ++j) {
+                    const double dsp = dS[c * dv + j] + kt[c] * dw[j];
+                    s += dsp * Sprev[c * dv + j];
+                    dS[c * dv + j] = a[c] * dsp;
+                }
+                dg[th * dk + c] = a[c] * s;
+            }
+        }
+        memcpy(dS0 + w * ssz, dS, sizeof(double) * (size_t)ssz);
+        free(dS);
+        free(states);
     }
 }
 

@@ -22,6 +22,10 @@ deliberately broken copies of the oracle (tests/test_oracle_mutants.py).
   decode_equals_prefill  T decode steps = a T-token prefill.
   varlen_independent     packed sequences = separate runs; empty sequences pass
                          their state through.
+  backward_vs_finite_differences
+                         every gradient of the reverse-mode oracle (dq, dk, dv,
+                         dg, dbeta, dS0) against central differences of the
+                         forward recurrence, on two packed sequences.
 """
 from __future__ import annotations
 
@@ -286,6 +290,37 @@ def varlen_independent(lib):
         _close(S[n], S1[0], 1e-14, f"varlen S, seq {n}")
 
 
+def backward_vs_finite_differences(lib):
+    """L = sum_t <dO_t, o_t> + <dS_fin, S_T>: each input perturbed by +-h in
+    the forward oracle, (L(x + h) - L(x - h)) / 2h, against the backward."""
+    rng = np.random.default_rng(111)
+    lens = [3, 0, 4]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    T, H, dk, dv = int(cu[-1]), 2, 3, 4
+    q, k, v, g, beta = _inputs(rng, T, H, dk, dv, gmax=1.5)
+    S0 = rng.standard_normal((len(lens), H, dk, dv))
+    dO = rng.standard_normal((T, H, dv))
+    dS = rng.standard_normal((len(lens), H, dk, dv))
+    x = {"q": q, "k": k, "v": v, "g": g, "beta": beta, "S0": S0}
+
+    def loss(x):
+        o, S = oracle.prefill(x["q"], x["k"], x["v"], x["g"], x["beta"], cu=cu, S0=x["S0"], lib=lib)
+        return float(np.sum(o * dO) + np.sum(S * dS))
+
+    grads = oracle.backward(q, k, v, g, beta, dO=dO, dS_fin=dS, cu=cu, S0=S0, lib=lib)
+    names = {"q": "dq", "k": "dk", "v": "dv", "g": "dg", "beta": "dbeta", "S0": "dS0"}
+    h = 1e-6
+    for name, gname in names.items():
+        num = np.zeros_like(x[name])
+        for idx in np.ndindex(x[name].shape):
+            xp = {n: a.copy() for n, a in x.items()}
+            xm = {n: a.copy() for n, a in x.items()}
+            xp[name][idx] += h
+            xm[name][idx] -= h
+            num[idx] = (loss(xp) - loss(xm)) / (2 * h)
+        _close(grads[gname], num, 1e-7, f"backward {gname} vs finite differences")
+
+
 ALL_PINS = [gate_closed_forms, bf16_rounding, brute_force_T_le_4, beta_zero_pure_decay,
             exact_recall, delta_overwrite, linearity_kcp, chunked_equals_serial,
-            wy_solve_vs_scipy, decode_equals_prefill, varlen_independent]
+            wy_solve_vs_scipy, decode_equals_prefill, varlen_independent, backward_vs_finite_differences]

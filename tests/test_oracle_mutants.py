@@ -1,7 +1,7 @@
 """Plausible mistakes planted in copies of the oracle (on the CPU) must each be
 caught by at least one pin.  This shows the pins constrain every part of the
 oracle: the gate, the decay, the delta correction, the read-out, the head and
-sequence indexing, the chunkwise solve and the bf16 rounding."""
+sequence indexing, the chunkwise solve, the bf16 rounding and the backward."""
 import os
 import shutil
 
@@ -31,6 +31,13 @@ MUTANTS = {
                         "for (int i = 0; i < r; ++i) s += P[r * L + i] * U[i * dv + jv];"),
     "chunk_state_no_decay": ("double s = exp(gl) * S[c * dv + jv];", "double s = S[c * dv + jv];"),
     "bf16_one_bit_short": ("int sc = e - 8;", "int sc = e - 7;"),
+    "bwd_dk_no_erase_term": ("s += dS[c * dv + j] * u[j] + Sp[c * dv + j] * dw[j];",
+                             "s += dS[c * dv + j] * u[j];"),
+    "bwd_dw_sign": ("dw[j] = -bt * du[j];", "dw[j] = bt * du[j];"),
+    "bwd_dbeta_uses_u": ("db += du[j] * r[j];", "db += du[j] * u[j];"),
+    "bwd_no_decay_of_dS": ("dS[c * dv + j] = a[c] * dsp;", "dS[c * dv + j] = dsp;"),
+    "bwd_dg_without_a": ("dg[th * dk + c] = a[c] * s;", "dg[th * dk + c] = s;"),
+    "bwd_dq_before_update": ("s += Sc[c * dv + j] * dOt[j];", "s += Sp[c * dv + j] * dOt[j];"),
 }
 
 
