@@ -185,6 +185,41 @@ kda_status_t kda_prefill_gated(const void* q, const void* k, const void* v, cons
                                int ckpt_interval, float* ckpt_states, int64_t ckpt_capacity, void* stream);
 
 /*
+ * kda_backward — gradients for training ([K3-notes] Model Architecture / KDA:
+ * the state update and read-out, differentiated; Infrastructure / KDA
+ * algorithm-system co-design: FlashKDA serves training as well as inference).
+ * For the loss L = sum_t <d_o[t], o[t]> + <d_final_state, S_T> of the prefill
+ * with the same arguments (kda_prefill), returns, all fp32:
+ *   dq, dk, dg : [T_total, H, d_k]   dv : [T_total, H, d_v]   dbeta : [T_total, H]
+ *   d_initial_state : [N, H, d_k, d_v]
+ * Inputs as kda_prefill (q, k, v, g, beta in `dtype`; g is the log-decay), plus:
+ *   d_o            : [T_total, H, d_v] (dtype) or NULL (no output gradient).
+ *   d_final_state  : fp32 [N, H, d_k, d_v] or NULL (zero).
+ *   initial_state  : the forward's, or NULL (zero).
+ *   ckpt_states    : the forward's checkpoints at interval 64 (kda_prefill_ckpt
+ *                    or kda_prefill_gated with ckpt_interval = 64, same inputs
+ *                    and initial state), ckpt_capacity rows; may be NULL.  A
+ *                    64-token chunk without its checkpoint row is recomputed
+ *                    from the initial state (correct, but quadratic in the
+ *                    sequence length).
+ *   workspace      : at least kda_backward_workspace_size(N, H, d_k, d_v)
+ *                    bytes (one 64-token scratch of states per workgroup slot).
+ * State buffers, dv and the workspace must be 16-byte aligned; no output may
+ * overlap an input or another output.  d_k, d_v each one of 32, 64, 128.
+ * The gradient with respect to z and A of the gate follows from dg by the
+ * chain rule of kda_gate's formula and is left to the caller.
+ * Errors: KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED,
+ * KDA_ERR_WORKSPACE_TOO_SMALL, KDA_ERR_HIP.
+ */
+size_t kda_backward_workspace_size(int N, int H, int d_k, int d_v);
+kda_status_t kda_backward(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                          const int32_t* cu_seqlens, int N, int64_t T_total, int H, int d_k, int d_v,
+                          const float* initial_state, const float* ckpt_states, int64_t ckpt_capacity,
+                          const void* d_o, const float* d_final_state, float* dq, float* dk, float* dv, float* dg,
+                          float* dbeta, float* d_initial_state, kda_dtype_t dtype, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
  * Number of checkpoints kda_prefill_ckpt writes for these HOST cu_seqlens
  * (NULL: one sequence of T_total tokens), with the planner's clamping; -1 on
  * invalid arguments (N < 1, T_total < 0, ckpt_interval <= 0).  Host only.

@@ -19,7 +19,8 @@ _STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARGUMENT", 2: "KDA_ERR_UNSUPPORTED",
            3: "KDA_ERR_WORKSPACE_TOO_SMALL", 4: "KDA_ERR_HIP"}
 EXPORTED = ("kda_status_string", "kda_last_error", "kda_version", "kda_gate",
             "kda_prefill_workspace_size", "kda_prefill", "kda_decode_step", "kda_verify", "kda_commit",
-            "kda_prefill_ckpt", "kda_checkpoint_count", "kda_prefill_gated", "kda_decode_step_gated")
+            "kda_prefill_ckpt", "kda_checkpoint_count", "kda_prefill_gated", "kda_decode_step_gated",
+            "kda_backward_workspace_size", "kda_backward")
 
 _lib = None
 
@@ -64,6 +65,11 @@ def lib() -> ctypes.CDLL:
         L.kda_prefill_gated.restype = I
         L.kda_decode_step_gated.argtypes = [P, P, P, P, P, F, P, P, P, I, I, I, I, I, P]
         L.kda_decode_step_gated.restype = I
+        L.kda_backward_workspace_size.argtypes = [I, I, I, I]
+        L.kda_backward_workspace_size.restype = SZ
+        L.kda_backward.argtypes = [P, P, P, P, P, P, I, I64, I, I, I, P, P, I64, P, P, P, P, P, P, P, P, I, P, SZ,
+                                   P]
+        L.kda_backward.restype = I
         L.kda_checkpoint_count.argtypes = [P, I, I64, I]
         L.kda_checkpoint_count.restype = I64
         _lib = L
@@ -277,3 +283,31 @@ def kda_decode_step_gated(q, k, v, z, A, beta, state, o=None, g_min: float = -5.
     _check(lib().kda_decode_step_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(A), float(g_min), _ptr(beta),
                                        _ptr(state), _ptr(o), B, H, dk, dv, _dtype_code(k), _stream(stream)))
     return o
+
+
+def kda_backward(q, k, v, g, beta, d_o=None, d_final_state=None, cu_seqlens=None, initial_state=None,
+                 ckpt=None, workspace=None, stream=None):
+    """Gradients of L = sum_t <d_o[t], o[t]> + <d_final_state, S_T> for kda_prefill on the
+    same inputs.  ckpt: the forward's checkpoints at interval 64 (or None: recomputed).
+    Returns a dict of fp32 tensors dq, dk, dg [T, H, d_k], dv [T, H, d_v], dbeta [T, H],
+    d_initial_state [N, H, d_k, d_v]."""
+    import torch
+    _dense(q, k, v, g, beta, d_o, d_final_state, cu_seqlens, initial_state, ckpt, workspace)
+    T, H, dk = k.shape
+    dv = v.shape[2]
+    N = 1 if cu_seqlens is None else cu_seqlens.shape[0] - 1
+    dev = k.device
+    f = lambda *shape: torch.empty(shape, dtype=torch.float32, device=dev)
+    out = {"dq": f(T, H, dk), "dk": f(T, H, dk), "dv": f(T, H, dv), "dg": f(T, H, dk), "dbeta": f(T, H),
+           "d_initial_state": f(N, H, dk, dv)}
+    need = int(lib().kda_backward_workspace_size(N, H, dk, dv))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wbytes = workspace.numel() * workspace.element_size()
+    cap = 0 if ckpt is None else ckpt.shape[0]
+    _check(lib().kda_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N, T, H, dk, dv,
+                              _ptr(initial_state), _ptr(ckpt) if cap else None, cap, _ptr(d_o),
+                              _ptr(d_final_state), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                              _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out["d_initial_state"]), _dtype_code(k),
+                              _ptr(workspace), wbytes, _stream(stream)))
+    return out

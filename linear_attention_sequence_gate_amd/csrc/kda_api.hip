@@ -14,6 +14,7 @@
 #include "kda_prefill.hpp"
 #include "kda_spec.hpp"
 #include "kda_step.hpp"
+#include "kda_backward.hpp"
 
 namespace {
 
@@ -397,6 +398,66 @@ kda_status_t kda_prefill_gated(const void* q, const void* k, const void* v, cons
     return prefill_impl("kda_prefill_gated", q, k, v, z, beta, cu_seqlens, N, T_total, H, d_k, d_v, chunk,
                         initial_state, final_state, o, dtype, workspace, workspace_bytes, ckpt_interval,
                         ckpt_states, ckpt_capacity, stream, T_total > 0 ? A : nullptr, g_min);
+}
+
+size_t kda_backward_workspace_size(int N, int H, int d_k, int d_v)
+{
+    if (N < 1 || H < 1 || H > KDA_MAX_HEADS || !dim_ok(d_k) || !dim_ok(d_v)) return 0;
+    return kda::backward_scratch_bytes(N, H, d_k, d_v);
+}
+
+kda_status_t kda_backward(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                          const int32_t* cu_seqlens, int N, int64_t T_total, int H, int d_k, int d_v,
+                          const float* initial_state, const float* ckpt_states, int64_t ckpt_capacity,
+                          const void* d_o, const float* d_final_state, float* dq, float* dk, float* dv, float* dg,
+                          float* dbeta, float* d_initial_state, kda_dtype_t dtype, void* workspace,
+                          size_t workspace_bytes, void* stream)
+{
+    const char* who = "kda_backward";
+    if (N < 1 || T_total < 0 || H < 1)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: bad sizes N=%d T_total=%lld H=%d", who, N, (long long)T_total, H);
+    if (H > KDA_MAX_HEADS) return fail(KDA_ERR_UNSUPPORTED, "%s: H=%d > %d", who, H, KDA_MAX_HEADS);
+    if (T_total > int64_t(0x7fffffff)) return fail(KDA_ERR_UNSUPPORTED, "%s: T_total > 2^31 - 1", who);
+    if (!cu_seqlens && N != 1)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: cu_seqlens is NULL but N=%d", who, N);
+    if (!dtype_ok(dtype)) return fail(KDA_ERR_UNSUPPORTED, "%s: unknown dtype %d", who, (int)dtype);
+    if (!dim_ok(d_k) || !dim_ok(d_v))
+        return fail(KDA_ERR_UNSUPPORTED, "%s: d_k=%d d_v=%d not in {32,64,128}", who, d_k, d_v);
+    if (T_total > 0 && (!q || !k || !v || !g || !beta || !dq || !dk || !dv || !dg || !dbeta))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: null token tensor", who);
+    if (!d_initial_state) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: null d_initial_state", who);
+    if (ckpt_capacity < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: negative checkpoint capacity", who);
+    const size_t need = kda::backward_scratch_bytes(N, H, d_k, d_v);
+    if (!workspace || workspace_bytes < need)
+        return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes < %zu needed", who, workspace_bytes, need);
+    auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+    if (!al16(initial_state) || !al16(ckpt_states) || !al16(d_final_state) || !al16(d_initial_state) ||
+        !al16(dv) || !al16(workspace))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: states, dv and the workspace must be 16-byte aligned", who);
+    const size_t es = dsize(dtype), T = size_t(T_total);
+    const size_t nk = T * H * d_k * es, nv = T * H * d_v * es, nb = T * H * es;
+    const size_t ns = size_t(N) * H * d_k * d_v * sizeof(float);
+    const size_t nck = ckpt_states ? size_t(ckpt_capacity) * H * d_k * d_v * sizeof(float) : 0;
+    const void* ins[9] = {q, k, v, g, beta, initial_state, ckpt_states, d_o, d_final_state};
+    const size_t insz[9] = {nk, nk, nv, nk, nb, initial_state ? ns : 0, nck, d_o ? nv : 0, d_final_state ? ns : 0};
+    void* outs[7] = {dq, dk, dv, dg, dbeta, d_initial_state, workspace};
+    const size_t fk = T * H * d_k * sizeof(float);
+    const size_t outsz[7] = {fk, fk, T * H * d_v * sizeof(float), fk, T * H * sizeof(float), ns, need};
+    for (int i = 0; i < 7; ++i) {
+        for (int j = 0; j < 9; ++j)
+            if (overlap(outs[i], outsz[i], ins[j], insz[j]))
+                return fail(KDA_ERR_INVALID_ARGUMENT, "%s: an output overlaps an input", who);
+        for (int j = i + 1; j < 7; ++j)
+            if (overlap(outs[i], outsz[i], outs[j], outsz[j]))
+                return fail(KDA_ERR_INVALID_ARGUMENT, "%s: two outputs overlap", who);
+    }
+    kda::BackwardArgs a{q, k, v, g, beta, cu_seqlens, N, T_total, H, initial_state,
+                        ckpt_capacity > 0 ? ckpt_states : nullptr, ckpt_capacity, d_o, d_final_state,
+                        dq, dk, dv, dg, dbeta, d_initial_state, static_cast<float*>(workspace)};
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t e = dtype == KDA_BF16 ? kda::launch_backward<kda::BF16>(a, d_k, d_v, s)
+                                           : kda::launch_backward<kda::F32>(a, d_k, d_v, s);
+    return from_hip(e, "kda_backward launch");
 }
 
 int64_t kda_checkpoint_count(const int32_t* cu_seqlens_host, int N, int64_t T_total, int ckpt_interval)

@@ -268,3 +268,39 @@ def test_decode_gated_validation(L):
     assert call(S=FAKE + (8 << 20) + 4) == 1                  # state not 16-byte aligned
     assert b"kda_decode_step_gated" in L.kda_last_error()
     assert call(B=0, A=None) == 0                             # nothing to do
+
+
+def test_backward_validation(L):
+    T, N, H, dk, dv = 256, 1, 2, 64, 64
+    need = L.kda_backward_workspace_size(N, H, dk, dv)
+    assert need > 0
+    assert L.kda_backward_workspace_size(N, H, 96, dv) == 0
+    assert L.kda_backward_workspace_size(0, H, dk, dv) == 0
+
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE + (1 << 20), v=FAKE + (2 << 20), g=FAKE + (3 << 20), beta=FAKE + (4 << 20),
+                 cu=None, N=N, T=T, H=H, dk=dk, dv=dv, init=None, ck=None, cap=0, do=FAKE + (5 << 20),
+                 dfin=None, dq=FAKE + (8 << 20), dkk=FAKE + (9 << 20), dvv=FAKE + (10 << 20),
+                 dg=FAKE + (11 << 20), db=FAKE + (12 << 20), dinit=FAKE + (13 << 20), dt=BF16,
+                 ws=FAKE + (64 << 20), wsb=need)
+        a.update(kw)
+        return L.kda_backward(a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu"], a["N"], a["T"], a["H"],
+                              a["dk"], a["dv"], a["init"], a["ck"], a["cap"], a["do"], a["dfin"], a["dq"],
+                              a["dkk"], a["dvv"], a["dg"], a["db"], a["dinit"], a["dt"], a["ws"], a["wsb"], None)
+
+    assert call(N=0) == 1
+    assert call(N=3) == 1                                   # N > 1 needs cu_seqlens
+    assert call(dk=96) == 2
+    assert call(dt=7) == 2
+    assert call(T=1 << 31) == 2
+    assert call(q=None) == 1
+    assert call(dq=None) == 1
+    assert call(dinit=None) == 1
+    assert call(cap=-1) == 1
+    assert call(wsb=need - 1) == 3
+    assert call(ws=None) == 3
+    assert call(dvv=FAKE + (10 << 20) + 4) == 1             # dv not 16-byte aligned
+    assert call(dq=FAKE + (1 << 20)) == 1                   # dq overlaps k
+    assert call(dg=FAKE + (8 << 20) + 64) == 1              # dg overlaps dq
+    assert call(ws=FAKE + (13 << 20)) == 1                  # workspace overlaps d_initial_state
+    assert b"kda_backward" in L.kda_last_error()

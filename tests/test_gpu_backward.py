@@ -1,0 +1,90 @@
+"""GPU parity of kda_backward against the fp64 reverse-mode oracle (itself
+pinned by finite differences of the forward recurrence).
+
+The backward runs in fp32 from the given inputs.  With the forward's
+checkpoints (computed by the prefill on bf16 operands) the states it starts
+each 64-token chunk from carry the forward's bf16-operand error, so those
+cases are held to the bf16 tolerance; without checkpoints every state is
+recomputed in fp32 from the initial state and the fp32 tolerance applies."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_common import TOL, announce, dev, host, relerr
+
+pytestmark = pytest.mark.gpu
+
+GRADS = (("dq", "dq"), ("dk", "dk"), ("dv", "dv"), ("dg", "dg"), ("dbeta", "dbeta"), ("d_initial_state", "dS0"))
+
+
+@pytest.fixture(scope="module")
+def kda():
+    import torch
+    import linear_attention_sequence_gate_amd as m
+    assert torch.cuda.is_available()
+    m.lib()
+    return m
+
+
+def run_case(kda, wl, with_ckpt, heads=None, seed=5):
+    """GPU backward of the prefill on wl's inputs (gate applied on the host by
+    the oracle, so both sides take the same g), against the oracle on `heads`."""
+    import torch
+    dt = wl.dtype
+    x = synth.prefill_inputs(wl)
+    g = oracle.gate(x["z"], x["A"])
+    if dt == "bf16":
+        g = oracle.round_bf16(g)
+    rng = np.random.default_rng(seed)
+    S0 = synth.initial_state(wl) if wl.state_std > 0 else None
+    dO = rng.standard_normal((wl.T_total, wl.H, wl.dv)).astype(np.float32)
+    if dt == "bf16":
+        dO = oracle.round_bf16(dO).astype(np.float32)
+    dS = rng.standard_normal((wl.N, wl.H, wl.dk, wl.dv)).astype(np.float32)
+    cu = torch.from_numpy(wl.cu_seqlens).cuda() if wl.N > 1 else None
+    d = {n: dev(x[n], dt) for n in ("q", "k", "v", "beta")}
+    d["g"] = dev(g, dt)
+    S0d = None if S0 is None else dev(S0)
+    ck = None
+    if with_ckpt:
+        _, _, ck = kda.kda_prefill_ckpt(d["q"], d["k"], d["v"], d["g"], d["beta"], 64, cu_seqlens=cu,
+                                        cu_seqlens_host=wl.cu_seqlens if wl.N > 1 else None,
+                                        initial_state=S0d)
+    out = kda.kda_backward(d["q"], d["k"], d["v"], d["g"], d["beta"], d_o=dev(dO, dt), d_final_state=dev(dS),
+                           cu_seqlens=cu, initial_state=S0d, ckpt=ck)
+    torch.cuda.synchronize()
+    hs = list(range(wl.H)) if heads is None else heads
+    sel = lambda a: a[:, hs]
+    ref = oracle.backward(sel(x["q"]), sel(x["k"]), sel(x["v"]), sel(g), sel(x["beta"]), dO=sel(dO),
+                          dS_fin=dS[:, hs], cu=wl.cu_seqlens, S0=None if S0 is None else S0[:, hs])
+    tol = TOL["bf16"] if (with_ckpt and dt == "bf16") else TOL["f32"]
+    for gname, rname in GRADS:
+        got = host(out[gname])[:, hs]
+        e = relerr(got, ref[rname])
+        print(f"  {gname}: {e:.3e}")
+        assert e < tol, f"{gname}: {e:.3e} >= {tol}"
+
+
+@pytest.mark.parametrize("with_ckpt", [False, True])
+@pytest.mark.parametrize("dk,dv,dtype", [(32, 32, "f32"), (32, 64, "f32"), (64, 64, "bf16"),
+                                         (128, 128, "bf16"), (128, 32, "bf16"), (32, 128, "bf16")])
+def test_backward_varlen(kda, dk, dv, dtype, with_ckpt):
+    wl = synth.VARLEN_64.with_(H=2, dk=dk, dv=dv, dtype=dtype, seqlens=(0, 1, 63, 64, 65, 200),
+                               state_std=0.1, z_shift=-2.0)
+    announce(f"backward dk={dk} dv={dv} {dtype} ckpt={with_ckpt} lens={wl.seqlens}")
+    run_case(kda, wl, with_ckpt)
+
+
+def test_backward_no_initial_state(kda):
+    wl = synth.TINY_F32.with_(H=3, seqlens=(150,))
+    announce("backward, zero initial state, one sequence")
+    run_case(kda, wl, with_ckpt=True)
+
+
+def test_backward_8k_sampled_heads(kda):
+    """The 8K workload's shape (H=32, d=128, bf16) with the forward's checkpoints;
+    two heads against the oracle."""
+    wl = synth.PREFILL_8K.with_(state_std=0.1)
+    announce("backward 8K, heads 3 and 29")
+    run_case(kda, wl, with_ckpt=True, heads=[3, 29])
