@@ -94,6 +94,15 @@ def spec_algo(B: int, K: int, H: int, dk: int, dv: int, commit: bool):
     return state + tok
 
 
+def backward_algo(T: int, H: int, dk: int, dv: int, interval: int = 64):
+    """q, k, g, v, beta and dO read (bf16), dq, dk, dg, dv, dbeta written (fp32),
+    the forward's checkpoints read once (one state per 64 tokens), the final
+    state's gradient read and the initial state's written (fp32)."""
+    tok = T * H
+    return (tok * (3 * dk + 2 * dv + 1) * 2 + tok * (3 * dk + dv + 1) * 4 + (T // interval) * H * dk * dv * 4
+            + 2 * H * dk * dv * 4)
+
+
 def cpu_baseline(wl, seconds: float = 12.0):
     """The fp64 oracle on this host over the whole 8K workload (every head,
     every token), repeated until at least `seconds` of CPU time have passed;
@@ -356,6 +365,34 @@ def main():
                                     "traffic": load_traffic("commit_b256_k4"), "kernel": "step_wave_kernel (commit)",
                                     "algorithmic_bytes_per_call": cb}}}
 
+    # ------------------------------------------- backward leg (8K workload)
+    # the forward's interval-64 checkpoints and g come from untimed calls; one
+    # kda_backward call is timed per step (it is slow: sequential per head)
+    bsets = sets[0]
+    bg = torch.empty_like(bsets["z"])
+    kda.kda_gate(bsets["z"], A, g=bg)
+    _, _, bck = kda.kda_prefill_ckpt(bsets["q"], bsets["k"], bsets["v"], bg, bsets["beta"], 64)
+    gen = torch.Generator(device=dev).manual_seed(7)
+    bdo = torch.randn((T, H, dv), device=dev, generator=gen).to(torch.bfloat16)
+    bdfin = torch.randn((1, H, dk, dv), device=dev, generator=gen)
+    bws = torch.empty(kda.lib().kda_backward_workspace_size(1, H, dk, dv), dtype=torch.uint8, device=dev)
+
+    def bcall(i):
+        kda.kda_backward(bsets["q"], bsets["k"], bsets["v"], bg, bsets["beta"], d_o=bdo, d_final_state=bdfin,
+                         ckpt=bck, workspace=bws)
+
+    bcall(0)
+    b_ms = timed_loop(bcall, 3)
+    b_bytes = backward_algo(T, H, dk, dv)
+    backward = {"value": round(T / (b_ms * 1e-3), 1), "unit": "tokens/s", "ms_per_call": round(b_ms, 3),
+                "config": {"workload": "prefill_8k backward (dq, dk, dv, dg, dbeta, dS0) from interval-64 "
+                                       "checkpoints", "H": H, "T": T, "d_k": dk, "d_v": dv},
+                "roofline": {"bound": "latency (token-serial per head)", "achieved": round(b_bytes / (b_ms * 1e-3) / 1e9, 1),
+                             "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": round(b_bytes / (b_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 5),
+                             "kernel": "backward_kernel", "algorithmic_bytes_per_call": b_bytes}}
+    del bws, bck
+
     # achievable HBM bandwidth on this device: a plain 1 GiB device-to-device
     # copy (2 GiB moved per copy), for fractions against a measured roof too
     csrc = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -406,7 +443,7 @@ def main():
            "roofline": roofline, "cpu_baseline": cpu, "verified": verified, "unfused": unfused,
            "checkpoints": ckpt_leg,
            "decode": decode,
-           "speculative": spec,
+           "speculative": spec, "backward": backward,
            "wall_s": round(wall, 3), "source_hash": kernel_source_hash()}
     print(json.dumps(out), flush=True)
 
