@@ -375,7 +375,7 @@ def main():
     gen = torch.Generator(device=dev).manual_seed(7)
     bdo = torch.randn((T, H, dv), device=dev, generator=gen).to(torch.bfloat16)
     bdfin = torch.randn((1, H, dk, dv), device=dev, generator=gen)
-    bws = torch.empty(kda.lib().kda_backward_workspace_size(1, H, dk, dv), dtype=torch.uint8, device=dev)
+    bws = torch.empty(kda.lib().kda_backward_workspace_size(T, 1, H, dk, dv), dtype=torch.uint8, device=dev)
 
     def bcall(i):
         kda.kda_backward(bsets["q"], bsets["k"], bsets["v"], bg, bsets["beta"], d_o=bdo, d_final_state=bdfin,

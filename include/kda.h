@@ -202,8 +202,11 @@ kda_status_t kda_prefill_gated(const void* q, const void* k, const void* v, cons
  *                    64-token chunk without its checkpoint row is recomputed
  *                    from the initial state (correct, but quadratic in the
  *                    sequence length).
- *   workspace      : at least kda_backward_workspace_size(N, H, d_k, d_v)
- *                    bytes (one 64-token scratch of states per workgroup slot).
+ *   workspace      : at least kda_backward_workspace_size(T_total, N, H, d_k,
+ *                    d_v) bytes: a 64-token scratch of states per workgroup
+ *                    slot, and per (segment, head) the segment's gradient
+ *                    summary and its incoming state gradient (segments of a
+ *                    sequence run in parallel).
  * State buffers, dv and the workspace must be 16-byte aligned; no output may
  * overlap an input or another output.  d_k, d_v each one of 32, 64, 128.
  * The gradient with respect to z and A of the gate follows from dg by the
@@ -211,7 +214,7 @@ kda_status_t kda_prefill_gated(const void* q, const void* k, const void* v, cons
  * Errors: KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED,
  * KDA_ERR_WORKSPACE_TOO_SMALL, KDA_ERR_HIP.
  */
-size_t kda_backward_workspace_size(int N, int H, int d_k, int d_v);
+size_t kda_backward_workspace_size(int64_t T_total, int N, int H, int d_k, int d_v);
 kda_status_t kda_backward(const void* q, const void* k, const void* v, const void* g, const void* beta,
                           const int32_t* cu_seqlens, int N, int64_t T_total, int H, int d_k, int d_v,
                           const float* initial_state, const float* ckpt_states, int64_t ckpt_capacity,

@@ -65,7 +65,7 @@ def lib() -> ctypes.CDLL:
         L.kda_prefill_gated.restype = I
         L.kda_decode_step_gated.argtypes = [P, P, P, P, P, F, P, P, P, I, I, I, I, I, P]
         L.kda_decode_step_gated.restype = I
-        L.kda_backward_workspace_size.argtypes = [I, I, I, I]
+        L.kda_backward_workspace_size.argtypes = [I64, I, I, I, I]
         L.kda_backward_workspace_size.restype = SZ
         L.kda_backward.argtypes = [P, P, P, P, P, P, I, I64, I, I, I, P, P, I64, P, P, P, P, P, P, P, P, I, P, SZ,
                                    P]
@@ -300,7 +300,7 @@ def kda_backward(q, k, v, g, beta, d_o=None, d_final_state=None, cu_seqlens=None
     f = lambda *shape: torch.empty(shape, dtype=torch.float32, device=dev)
     out = {"dq": f(T, H, dk), "dk": f(T, H, dk), "dv": f(T, H, dv), "dg": f(T, H, dk), "dbeta": f(T, H),
            "d_initial_state": f(N, H, dk, dv)}
-    need = int(lib().kda_backward_workspace_size(N, H, dk, dv))
+    need = int(lib().kda_backward_workspace_size(T, N, H, dk, dv))
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     wbytes = workspace.numel() * workspace.element_size()

@@ -400,10 +400,12 @@ kda_status_t kda_prefill_gated(const void* q, const void* k, const void* v, cons
                         ckpt_states, ckpt_capacity, stream, T_total > 0 ? A : nullptr, g_min);
 }
 
-size_t kda_backward_workspace_size(int N, int H, int d_k, int d_v)
+size_t kda_backward_workspace_size(int64_t T_total, int N, int H, int d_k, int d_v)
 {
-    if (N < 1 || H < 1 || H > KDA_MAX_HEADS || !dim_ok(d_k) || !dim_ok(d_v)) return 0;
-    return kda::backward_scratch_bytes(N, H, d_k, d_v);
+    if (T_total < 0 || T_total > int64_t(0x7fffffff) || N < 1 || H < 1 || H > KDA_MAX_HEADS || !dim_ok(d_k) ||
+        !dim_ok(d_v))
+        return 0;
+    return kda::backward_plan(T_total, N, H, d_k, d_v).bytes;
 }
 
 kda_status_t kda_backward(const void* q, const void* k, const void* v, const void* g, const void* beta,
@@ -427,7 +429,8 @@ kda_status_t kda_backward(const void* q, const void* k, const void* v, const voi
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: null token tensor", who);
     if (!d_initial_state) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: null d_initial_state", who);
     if (ckpt_capacity < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: negative checkpoint capacity", who);
-    const size_t need = kda::backward_scratch_bytes(N, H, d_k, d_v);
+    const kda::BwdPlan plan = kda::backward_plan(T_total, N, H, d_k, d_v);
+    const size_t need = plan.bytes;
     if (!workspace || workspace_bytes < need)
         return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes < %zu needed", who, workspace_bytes, need);
     auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
@@ -453,10 +456,11 @@ kda_status_t kda_backward(const void* q, const void* k, const void* v, const voi
     }
     kda::BackwardArgs a{q, k, v, g, beta, cu_seqlens, N, T_total, H, initial_state,
                         ckpt_capacity > 0 ? ckpt_states : nullptr, ckpt_capacity, d_o, d_final_state,
-                        dq, dk, dv, dg, dbeta, d_initial_state, static_cast<float*>(workspace)};
+                        dq, dk, dv, dg, dbeta, d_initial_state, static_cast<float*>(workspace), 0, nullptr,
+                        nullptr};
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const hipError_t e = dtype == KDA_BF16 ? kda::launch_backward<kda::BF16>(a, d_k, d_v, s)
-                                           : kda::launch_backward<kda::F32>(a, d_k, d_v, s);
+    const hipError_t e = dtype == KDA_BF16 ? kda::launch_backward<kda::BF16>(a, plan, d_k, d_v, s)
+                                           : kda::launch_backward<kda::F32>(a, plan, d_k, d_v, s);
     return from_hip(e, "kda_backward launch");
 }
 

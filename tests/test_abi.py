@@ -272,10 +272,11 @@ def test_decode_gated_validation(L):
 
 def test_backward_validation(L):
     T, N, H, dk, dv = 256, 1, 2, 64, 64
-    need = L.kda_backward_workspace_size(N, H, dk, dv)
+    need = L.kda_backward_workspace_size(T, N, H, dk, dv)
     assert need > 0
-    assert L.kda_backward_workspace_size(N, H, 96, dv) == 0
-    assert L.kda_backward_workspace_size(0, H, dk, dv) == 0
+    assert L.kda_backward_workspace_size(T, N, H, 96, dv) == 0
+    assert L.kda_backward_workspace_size(T, 0, H, dk, dv) == 0
+    assert L.kda_backward_workspace_size(-1, N, H, dk, dv) == 0
 
     def call(**kw):
         a = dict(q=FAKE, k=FAKE + (1 << 20), v=FAKE + (2 << 20), g=FAKE + (3 << 20), beta=FAKE + (4 << 20),

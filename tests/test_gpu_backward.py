@@ -88,3 +88,40 @@ def test_backward_8k_sampled_heads(kda):
     wl = synth.PREFILL_8K.with_(state_std=0.1)
     announce("backward 8K, heads 3 and 29")
     run_case(kda, wl, with_ckpt=True, heads=[3, 29])
+
+
+class BwdSegEnv:
+    """Force the backward's segment length (tokens) for the library's planner."""
+
+    def __init__(self, tokens):
+        self.tokens = tokens
+
+    def __enter__(self):
+        import os
+        self.old = os.environ.get("KDA_BWD_SEG_TOKENS")
+        os.environ["KDA_BWD_SEG_TOKENS"] = str(self.tokens)
+
+    def __exit__(self, *a):
+        import os
+        if self.old is None:
+            os.environ.pop("KDA_BWD_SEG_TOKENS", None)
+        else:
+            os.environ["KDA_BWD_SEG_TOKENS"] = self.old
+
+
+@pytest.mark.parametrize("seg_tokens", [64, 192, 100000])
+def test_backward_segment_lengths(kda, seg_tokens):
+    """Segments of 1 and 3 chunks (summary, scan, full pass per segment) and one
+    segment per sequence (no scan step)."""
+    wl = synth.VARLEN_64.with_(H=2, dk=64, dv=32, dtype="f32", seqlens=(500, 0, 64, 129),
+                               state_std=0.1, z_shift=-2.0)
+    announce(f"backward segments of {seg_tokens} tokens")
+    with BwdSegEnv(seg_tokens):
+        run_case(kda, wl, with_ckpt=False)
+
+
+def test_backward_many_heads(kda):
+    """N * H >= 128: the planner's one-segment-per-sequence path."""
+    wl = synth.VARLEN_64.with_(H=64, dk=32, dv=32, dtype="f32", seqlens=(70, 130), state_std=0.1)
+    announce("backward, 2 sequences x 64 heads")
+    run_case(kda, wl, with_ckpt=True, heads=[0, 33, 63])
