@@ -203,10 +203,13 @@ kda_status_t kda_prefill_gated(const void* q, const void* k, const void* v, cons
  *                    from the initial state (correct, but quadratic in the
  *                    sequence length).
  *   workspace      : at least kda_backward_workspace_size(T_total, N, H, d_k,
- *                    d_v) bytes: a 64-token scratch of states per workgroup
- *                    slot, and per (segment, head) the segment's gradient
- *                    summary and its incoming state gradient (segments of a
- *                    sequence run in parallel).
+ *                    d_v) bytes: per workgroup slot, the states at the four
+ *                    16-token sub-chunk starts of a 64-token chunk and one
+ *                    staging state; per (segment, head) the segment's
+ *                    gradient summary and its incoming state gradient
+ *                    (segments of a sequence run in parallel).
+ * The products run on the matrix cores with operands in `dtype` (bf16
+ * operands and fp32 accumulation for KDA_BF16, as in the prefill).
  * State buffers, dv and the workspace must be 16-byte aligned; no output may
  * overlap an input or another output.  d_k, d_v each one of 32, 64, 128.
  * The gradient with respect to z and A of the gate follows from dg by the

@@ -15,6 +15,7 @@
 #include "kda_spec.hpp"
 #include "kda_step.hpp"
 #include "kda_backward.hpp"
+#include "kda_bwd_chunk.hpp"
 
 namespace {
 
