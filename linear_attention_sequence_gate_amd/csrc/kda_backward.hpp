@@ -86,20 +86,36 @@ __device__ inline SegLoc bwd_locate(const BackwardArgs& a, int seg)
     return L;
 }
 
-// Scan: one workgroup of 256 threads per (sequence, head, 32 columns of dS).
+// Scan: one workgroup of 256 threads per (sequence, head, 16 columns of dS).
 // Backwards over the sequence's segments: dS_end of segment s is dS_start of
-// segment s + 1, and dS_start(s) = M_s^T dS_end(s) + C_s, in fp32.  Writes
-// every segment's dS_end for the full pass and the initial state's gradient.
+// segment s + 1, and dS_start(s) = M_s^T dS_end(s) + C_s, in fp32.  M_s^T is
+// staged in LDS (the next one is loaded into registers while the current
+// product runs); each thread owns DK/16 rows of one column.  Writes every
+// segment's dS_end for the full pass and the initial state's gradient.
+constexpr int BWD_SCAN_COLS = 16;
+template <int DK>
+struct BwdScanCfg {
+    static constexpr int RG = 256 / BWD_SCAN_COLS;  // row groups
+    static constexpr int RPT = DK / RG;             // rows per thread
+    static constexpr int SM = DK + 4;               // padded row stride of M^T in LDS
+    static constexpr int NV = DK * DK / 4 / 256;    // float4 of M^T per thread
+    static constexpr int LDS = (DK * SM + DK * (BWD_SCAN_COLS + 1)) * 4;
+};
+
 template <int DK, int DV>
 __global__ void __launch_bounds__(256) bwd_scan_kernel(BackwardArgs a)
 {
-    constexpr int RPT = DK / 8;  // rows per thread (8 row groups x 32 columns)
-    __shared__ float sd[DK][33];
+    using C = BwdScanCfg<DK>;
+    constexpr int NSL = DV / BWD_SCAN_COLS;
+    extern __shared__ __attribute__((aligned(16))) float ssm[];
+    float* sM = ssm;                 // [DK][SM]
+    float* sd = ssm + DK * C::SM;    // [DK][BWD_SCAN_COLS + 1]
+    constexpr int SD = BWD_SCAN_COLS + 1;
     const int H = a.H;
-    const int slice = blockIdx.x % (DV / 32), unit = blockIdx.x / (DV / 32);
+    const int slice = blockIdx.x % NSL, unit = blockIdx.x / NSL;
     const int n = unit / H, h = unit % H;
-    const int t = threadIdx.x, jj = t & 31, rgp = t >> 5;
-    const int col = slice * 32 + jj;
+    const int t = threadIdx.x, jj = t % BWD_SCAN_COLS, rgp = t / BWD_SCAN_COLS;
+    const int col = slice * BWD_SCAN_COLS + jj;
     // this sequence's segments: the first segment of sequence n is the sum of
     // the earlier sequences' counts
     int seg0 = 0, nseg = 1;
@@ -118,29 +134,46 @@ __global__ void __launch_bounds__(256) bwd_scan_kernel(BackwardArgs a)
     auto cm_of = [&](int s) { return a.cm + (int64_t(seg0 + s) * H + h) * (DK * DV + DK * DK); };
     auto dsend_of = [&](int s) { return a.dsend + (int64_t(seg0 + s) * H + h) * DK * DV; };
     // the last segment ends at the final state: its dS_end is the final state's gradient
-    for (int r = rgp; r < DK; r += 8) {
+    for (int r = rgp; r < DK; r += C::RG) {
         dsend_of(nseg - 1)[r * DV + col] = a.d_fin ? a.d_fin[unit * int64_t(DK) * DV + r * DV + col] : 0.f;
-        sd[r][jj] = cm_of(nseg - 1)[r * DV + col];  // dS_start of the last segment
+        sd[r * SD + jj] = cm_of(nseg - 1)[r * DV + col];  // dS_start of the last segment
     }
+    f32x4 pre[C::NV];
+    auto load_m = [&](int s) {
+        const f32x4* src = reinterpret_cast<const f32x4*>(cm_of(s) + DK * DV);
+#pragma unroll
+        for (int i = 0; i < C::NV; ++i) pre[i] = src[t + 256 * i];
+    };
+    if (nseg >= 2) load_m(nseg - 2);
     __syncthreads();
     for (int s = nseg - 2; s >= 0; --s) {
-        const float* C = cm_of(s);
-        const float* MT = C + DK * DV;
-        float acc[RPT];
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) {
-            const int r = rgp * RPT + i;
-            float x = C[r * DV + col];
-            for (int c = 0; c < DK; ++c) x += MT[r * DK + c] * sd[c][jj];
-            acc[i] = x;
+        for (int i = 0; i < C::NV; ++i) {
+            const int e = 4 * (t + 256 * i), r = e / DK, c = e % DK;
+            *reinterpret_cast<f32x4*>(sM + r * C::SM + c) = pre[i];
         }
-        for (int r = rgp; r < DK; r += 8) dsend_of(s)[r * DV + col] = sd[r][jj];
-        __syncthreads();  // every thread has read dS_end(s)
+        const float* Cs = cm_of(s);
+        float acc[C::RPT];
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) sd[rgp * RPT + i][jj] = acc[i];
+        for (int i = 0; i < C::RPT; ++i) acc[i] = Cs[(rgp * C::RPT + i) * DV + col];
+        __syncthreads();  // M_s^T staged
+        if (s >= 1) load_m(s - 1);
+        for (int c = 0; c < DK; c += 4) {
+            const float d0 = sd[c * SD + jj], d1 = sd[(c + 1) * SD + jj];
+            const float d2 = sd[(c + 2) * SD + jj], d3 = sd[(c + 3) * SD + jj];
+#pragma unroll
+            for (int i = 0; i < C::RPT; ++i) {
+                const f32x4 m = *reinterpret_cast<const f32x4*>(sM + (rgp * C::RPT + i) * C::SM + c);
+                acc[i] += m[0] * d0 + m[1] * d1 + m[2] * d2 + m[3] * d3;
+            }
+        }
+        for (int r = rgp; r < DK; r += C::RG) dsend_of(s)[r * DV + col] = sd[r * SD + jj];
+        __syncthreads();  // every thread has read dS_end(s) and M_s^T
+#pragma unroll
+        for (int i = 0; i < C::RPT; ++i) sd[(rgp * C::RPT + i) * SD + jj] = acc[i];
         __syncthreads();
     }
-    for (int r = rgp; r < DK; r += 8) a.d_init[unit * int64_t(DK) * DV + r * DV + col] = sd[r][jj];
+    for (int r = rgp; r < DK; r += C::RG) a.d_init[unit * int64_t(DK) * DV + r * DV + col] = sd[r * SD + jj];
 }
 
 struct BwdPlan {

@@ -771,7 +771,11 @@ hipError_t launch_bwd_chunk(const BackwardArgs& a, const BwdPlan& plan, hipStrea
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k1, dim3(unsigned(plan.segs_max * a.H)), dim3(C1::NT), C1::LDS, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_scan_kernel<DK, DV>), dim3(unsigned(a.N * a.H * (DV / 32))), dim3(256), 0, stream, a);
+    auto ks = bwd_scan_kernel<DK, DV>;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(ks), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            BwdScanCfg<DK>::LDS);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(ks, dim3(unsigned(a.N * a.H * (DV / BWD_SCAN_COLS))), dim3(256), BwdScanCfg<DK>::LDS, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     auto k3 = bwd_chunk_full_kernel<DT, DK, DV>;
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(k3), hipFuncAttributeMaxDynamicSharedMemorySize, C3::LDS);
