@@ -259,7 +259,37 @@ size_t kda_prefill_workspace_size(int64_t T_total, int N, int H, int d_k, int d_
         !dim_ok(d_v) || chunk != 64 ||
         !dtype_ok(dtype) || (dtype == KDA_F32 && (d_k != 32 || d_v > 64)))
         return 0;
-    return kda::prefill_plan(T_total, N, H, d_k, d_v).workspace_bytes;
+    return kda::prefill_workspace(T_total, N, H, d_k, d_v);
+}
+
+// The second stream and the two events of the prefill's head split, one set
+// per host thread and device, created on first use and kept until the process
+// ends (default priority, non-blocking).
+struct SideStream {
+    hipStream_t st = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+static SideStream* side_stream()
+{
+    thread_local SideStream cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    SideStream& c = cache[dev];
+    if (!c.st) {
+        hipStream_t st = nullptr;
+        hipEvent_t e0 = nullptr, e1 = nullptr;
+        if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) return nullptr;
+        if (hipEventCreateWithFlags(&e0, hipEventDisableTiming) != hipSuccess ||
+            hipEventCreateWithFlags(&e1, hipEventDisableTiming) != hipSuccess) {
+            if (e0) (void)hipEventDestroy(e0);
+            (void)hipStreamDestroy(st);
+            return nullptr;
+        }
+        c.st = st;
+        c.fork = e0;
+        c.join = e1;
+    }
+    return &c;
 }
 
 static kda_status_t prefill_impl(const char* who, const void* q, const void* k, const void* v, const void* g,
@@ -293,13 +323,14 @@ static kda_status_t prefill_impl(const char* who, const void* q, const void* k, 
         const size_t na = size_t(H) * sizeof(float);
         if (overlap(o, size_t(T_total) * H * d_v * dsize(dtype), gate_A, na) ||
             overlap(final_state, final_state ? size_t(N) * H * d_k * d_v * sizeof(float) : 0, gate_A, na) ||
-            overlap(workspace, kda::prefill_plan(T_total, N, H, d_k, d_v).workspace_bytes, gate_A, na))
+            overlap(workspace, kda::prefill_workspace(T_total, N, H, d_k, d_v), gate_A, na))
             return fail(KDA_ERR_INVALID_ARGUMENT, "%s: A overlaps an output buffer", who);
     }
     const kda::PrefillPlan plan = kda::prefill_plan(T_total, N, H, d_k, d_v);
-    if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
+    const size_t ws_need = kda::prefill_workspace(T_total, N, H, d_k, d_v);
+    if (ws_need > 0 && (!workspace || workspace_bytes < ws_need))
         return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes < %zu needed", who,
-                    workspace_bytes, plan.workspace_bytes);
+                    workspace_bytes, ws_need);
     const size_t es = dsize(dtype);
     const size_t nk = size_t(T_total) * H * d_k * es, nv = size_t(T_total) * H * d_v * es;
     const size_t nb = size_t(T_total) * H * es;
@@ -311,15 +342,15 @@ static kda_status_t prefill_impl(const char* who, const void* q, const void* k, 
             return fail(KDA_ERR_INVALID_ARGUMENT, "%s: o aliases an input", who);
         if (i < 5 && overlap(final_state, final_state ? ns : 0, ins[i], insz[i]))
             return fail(KDA_ERR_INVALID_ARGUMENT, "%s: final_state aliases a token input", who);
-        if (overlap(workspace, plan.workspace_bytes, ins[i], insz[i]))
+        if (overlap(workspace, ws_need, ins[i], insz[i]))
             return fail(KDA_ERR_INVALID_ARGUMENT, "%s: workspace aliases an input", who);
     }
     if (final_state && initial_state && final_state != initial_state &&
         overlap(final_state, ns, initial_state, ns))
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: final_state partially overlaps initial_state", who);
     if (overlap(o, nv, final_state, final_state ? ns : 0) ||
-        overlap(workspace, plan.workspace_bytes, o, nv) ||
-        overlap(workspace, plan.workspace_bytes, final_state, final_state ? ns : 0))
+        overlap(workspace, ws_need, o, nv) ||
+        overlap(workspace, ws_need, final_state, final_state ? ns : 0))
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: output buffers overlap", who);
     if (ckpt_interval < 0 || (ckpt_interval > 0 && ckpt_interval % kda::CH != 0))
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: checkpoint interval %d is not a positive multiple of %d", who,
@@ -337,7 +368,7 @@ static kda_status_t prefill_impl(const char* who, const void* q, const void* k, 
                                  size_t(T_total) * H * dsize(dtype),
                                  initial_state ? size_t(N) * H * d_k * d_v * sizeof(float) : 0,
                                  final_state ? size_t(N) * H * d_k * d_v * sizeof(float) : 0,
-                                 size_t(T_total) * H * d_v * dsize(dtype), plan.workspace_bytes};
+                                 size_t(T_total) * H * d_v * dsize(dtype), ws_need};
         for (int i = 0; i < 9; ++i)
             if (overlap(ckpt_states, nc, all[i], allsz[i]))
                 return fail(KDA_ERR_INVALID_ARGUMENT, "%s: checkpoint buffer overlaps another buffer", who);
@@ -353,8 +384,45 @@ static kda_status_t prefill_impl(const char* who, const void* q, const void* k, 
     }
     a.gate_A = gate_A;
     a.g_min = g_min;
-    hipError_t e = dtype == KDA_BF16 ? kda::launch_prefill<kda::BF16>(a, plan, s)
-                                     : kda::launch_prefill<kda::F32>(a, plan, s);
+    auto launch = [&](const kda::PrefillArgs& x, const kda::PrefillPlan& p, hipStream_t st) {
+        return dtype == KDA_BF16 ? kda::launch_prefill<kda::BF16>(x, p, st) : kda::launch_prefill<kda::F32>(x, p, st);
+    };
+    // the head split (one sequence given without cu_seqlens; checkpoints, if
+    // any, must fall on the head's end)
+    const kda::PrefillSplit sp = kda::prefill_split(T_total, N, H, d_k, d_v);
+    SideStream* ss = nullptr;
+    if (sp.on && !cu_seqlens && (a.ckpt_interval == 0 || sp.head % a.ckpt_interval == 0)) ss = side_stream();
+    if (!ss) return from_hip(launch(a, plan, s), "kda_prefill launch");
+
+    const kda::PrefillPlan tplan = kda::prefill_plan(T_total - sp.head, 1, H, d_k, d_v, sp.tail_L);
+    float* head_fin = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) +
+                                               kda::align256(tplan.workspace_bytes));
+    kda::PrefillArgs hd = a;  // the head: its output pass only, state in -> head_fin
+    hd.T_total = sp.head;
+    hd.fin = head_fin;
+    const kda::PrefillPlan hplan = kda::prefill_plan(sp.head, 1, H, d_k, d_v);
+    kda::PrefillArgs tl = a;  // the rest, from the head's final state
+    const size_t ek = size_t(sp.head) * H * d_k * es, ev = size_t(sp.head) * H * d_v * es;
+    tl.q = static_cast<const char*>(q) + ek;
+    tl.k = static_cast<const char*>(k) + ek;
+    tl.g = static_cast<const char*>(g) + ek;
+    tl.v = static_cast<const char*>(v) + ev;
+    tl.beta = static_cast<const char*>(beta) + size_t(sp.head) * H * es;
+    tl.o = static_cast<char*>(o) + ev;
+    tl.T_total = T_total - sp.head;
+    tl.init = head_fin;
+    tl.join = ss->join;
+    if (a.ckpt) {
+        const int64_t hrows = sp.head / a.ckpt_interval;
+        tl.ckpt = a.ckpt_cap > hrows ? a.ckpt + hrows * int64_t(H) * d_k * d_v : nullptr;
+        tl.ckpt_cap = a.ckpt_cap > hrows ? a.ckpt_cap - hrows : 0;
+        if (!tl.ckpt) tl.ckpt_interval = 0;
+    }
+    hipError_t e = hipEventRecord(ss->fork, s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(ss->st, ss->fork, 0);
+    if (e == hipSuccess) e = launch(hd, hplan, ss->st);
+    if (e == hipSuccess) e = hipEventRecord(ss->join, ss->st);
+    if (e == hipSuccess) e = launch(tl, tplan, s);
     return from_hip(e, "kda_prefill launch");
 }
 

@@ -44,6 +44,9 @@
 //     segment from its true incoming state and writes the outputs.
 #pragma once
 
+#include <cmath>
+#include <cstdlib>
+
 #include "kda_common.hpp"
 
 namespace kda {
@@ -95,7 +98,8 @@ struct PrefillPlan {
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-inline PrefillPlan prefill_plan(int64_t T_total, int N, int H, int dk, int dv)
+// force_L > 0 fixes the segment length (in chunks) instead of choosing it.
+inline PrefillPlan prefill_plan(int64_t T_total, int N, int H, int dk, int dv, int force_L = 0)
 {
     PrefillPlan p;
     const int64_t chunks_bound = (T_total + CH - 1) / CH + N;  // >= total chunks over sequences
@@ -106,6 +110,7 @@ inline PrefillPlan prefill_plan(int64_t T_total, int N, int H, int dk, int dv)
         const long v = atol(e);
         if (v > 0) L = v;
     }
+    if (force_L > 0) L = force_L;
     const int64_t max_seq_chunks = (T_total + CH - 1) / CH;
     if (L >= max_seq_chunks) L = max_seq_chunks > 0 ? max_seq_chunks : 1;  // nothing splits
     p.seg_chunks = int(L);
@@ -124,6 +129,52 @@ inline PrefillPlan prefill_plan(int64_t T_total, int N, int H, int dk, int dv)
     return p;
 }
 
+// Head split of one long sequence.  Pass 1 leaves the compute units of the
+// final segments' heads idle, and the first segment's incoming state is
+// known before anything runs.  So the first `head` tokens run as a prefill of
+// their own (its output pass only) on a second stream while pass 1 of the
+// rest runs, and the rest's scan starts from the head's final state.  The
+// rest is cut into the same number of segments, each a little shorter; the
+// head is at most 0.84 of a segment, about the ratio of a summary pass's
+// time per block to an output pass's, so it ends before pass 1 does.  Used
+// when the rest's (segment, head) items still fit the compute units once.
+struct PrefillSplit {
+    bool on = false;
+    int64_t head = 0;  // tokens of the head (whole chunks)
+    int tail_L = 0;    // chunks per segment of the rest
+};
+
+inline PrefillSplit prefill_split(int64_t T_total, int N, int H, int dk, int dv)
+{
+    PrefillSplit sp;
+    if (N != 1 || getenv("KDA_SEG_CHUNKS")) return sp;
+    const PrefillPlan p = prefill_plan(T_total, 1, H, dk, dv);
+    const int64_t chunks = (T_total + CH - 1) / CH;
+    const int64_t nseg = (chunks + p.seg_chunks - 1) / p.seg_chunks;
+    if (nseg < 2 || nseg * H > NCU_TARGET) return sp;
+    const int64_t Lt = int64_t(std::ceil(double(chunks) / (double(nseg) + 0.84)));
+    const int64_t L0 = chunks - nseg * Lt;
+    if (L0 < 1 || L0 > Lt) return sp;
+    sp.on = true;
+    sp.head = L0 * CH;
+    sp.tail_L = int(Lt);
+    return sp;
+}
+
+// Workspace for a prefill call: its plan's, or, with the head split, the
+// rest's plan and the head's final state (fp32 [H][dk][dv]).
+inline size_t prefill_workspace(int64_t T_total, int N, int H, int dk, int dv)
+{
+    size_t ws = prefill_plan(T_total, N, H, dk, dv).workspace_bytes;
+    const PrefillSplit sp = prefill_split(T_total, N, H, dk, dv);
+    if (sp.on) {
+        const size_t t = align256(prefill_plan(T_total - sp.head, 1, H, dk, dv, sp.tail_L).workspace_bytes) +
+                         align256(size_t(H) * dk * dv * sizeof(float));
+        ws = ws > t ? ws : t;
+    }
+    return ws;
+}
+
 struct PrefillArgs {
     const void *q, *k, *v, *g, *beta;
     const int32_t* cu;
@@ -139,6 +190,7 @@ struct PrefillArgs {
     int64_t ckpt_cap = 0;   // checkpoints the buffer holds
     const float* gate_A = nullptr;  // non-null: g holds the gate's input z, and g = g_min sigmoid(e^{A_h} z)
     float g_min = -5.f;
+    hipEvent_t join = nullptr;  // non-null: the launches that read the incoming state wait for it
 };
 
 // Device-side view shared by the prefill kernels.
@@ -1440,6 +1492,7 @@ hipError_t launch_prefill_t(const PrefillArgs& a, const PrefillPlan& plan, hipSt
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(k1, dim3(unsigned(plan.np1_max * a.H)), dim3(C1::NT), C1::LDS, stream, d);
         if ((e = hipGetLastError()) != hipSuccess) return e;
+        if (a.join && (e = hipStreamWaitEvent(stream, a.join, 0)) != hipSuccess) return e;
         auto ks = scan_kernel<DK, DV>;
         constexpr int scan_lds = ScanCfg<DK, DV>::LDS;
         e = hipFuncSetAttribute(reinterpret_cast<const void*>(ks), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -1448,6 +1501,7 @@ hipError_t launch_prefill_t(const PrefillArgs& a, const PrefillPlan& plan, hipSt
         hipLaunchKernelGGL(ks, dim3(unsigned(a.N * a.H * (DV / SCAN_COLS))), dim3(256), scan_lds, stream, d);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
+    if (plan.np1_max == 0 && a.join && (e = hipStreamWaitEvent(stream, a.join, 0)) != hipSuccess) return e;
     using C3 = BlockCfg<DT, DK, DV, false>;
     auto k3 = prefill_block_kernel<DT, DK, DV, false>;
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(k3),
