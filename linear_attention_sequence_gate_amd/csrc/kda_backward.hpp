@@ -203,8 +203,9 @@ inline BwdPlan backward_plan(int64_t T_total, int N, int H, int dk, int dv)
     p.grid = int(items < BWD_MAX_WG ? items : BWD_MAX_WG);
     size_t off = 0;
     p.off_scratch = off;
-    // per workgroup: the states at the four 16-token sub-chunk starts of a chunk, and one more for dS'
-    off = align256(off + size_t(p.grid) * (BWD_CHUNK / 16 + 1) * size_t(dk) * dv * sizeof(float));
+    // per workgroup: the states at the four 16-token sub-chunk starts of a chunk
+    // (in two layouts), and one more for dS'
+    off = align256(off + size_t(p.grid) * (2 * (BWD_CHUNK / 16) + 1) * size_t(dk) * dv * sizeof(float));
     p.off_cm = off;
     off = align256(off + size_t(items) * (size_t(dk) * dv + size_t(dk) * dk) * sizeof(float));
     p.off_dsend = off;

@@ -52,7 +52,7 @@ namespace kda {
 constexpr int BSUB = 16;                 // tokens per sub-chunk
 constexpr int BNSUB = BWD_CHUNK / BSUB;  // sub-chunks per checkpoint chunk
 
-template <typename DT, int DKV, int DVV, bool FULL, bool DSN_LDS_>
+template <typename DT, int DKV, int DVV, bool FULL, bool DSN_LDS_, bool S_LDS_ = false>
 struct BwdLayout {
     static constexpr int DK = DKV, DV = DVV;
     static constexpr int NCOL = FULL ? DV : DV + DK;  // dS columns (extended in the summary)
@@ -61,6 +61,7 @@ struct BwdLayout {
     static constexpr int NW = FULL ? (NCW > NSL ? NCW : NSL) : NCW;
     static constexpr int NT = 64 * NW;
     static constexpr bool DSN_LDS = DSN_LDS_;
+    static constexpr bool S_LDS = FULL && S_LDS_;  // the sub-chunk's incoming state staged in LDS for the slices
     using OT = typename Op<DT>::T;
     static constexpr int ES = sizeof(OT);
     static constexpr int PAD = 16 / ES;
@@ -84,7 +85,8 @@ struct BwdLayout {
     static constexpr int O_U = O_DO + (FULL ? TV : 0);          // U
     static constexpr int O_DOT = O_U + (FULL ? TV : 0);         // dO^T [DV][S16]
     static constexpr int O_DSN = O_DOT + DV * S16 * ES;         // dS' [DK][SV]
-    static constexpr int O_QA = O_DSN + ((FULL && DSN_LDS) ? DK * SV * ES : 0);  // -Diag(beta) A'
+    static constexpr int O_SS = O_DSN + ((FULL && DSN_LDS) ? DK * SV * ES : 0);  // S [DK][SV]
+    static constexpr int O_QA = O_SS + (S_LDS ? DK * SV * ES : 0);  // -Diag(beta) A'
     static constexpr int O_T = O_QA + T16;                      // T
     static constexpr int O_P = O_T + T16;                       // P
     static constexpr int O_F32 = (O_P + T16 + 15) / 16 * 16;
@@ -100,17 +102,24 @@ struct BwdLayout {
 
 template <typename DT, int DK, int DV, bool FULL>
 struct BwdCfgSel {
-    // dS' goes through LDS when it fits; otherwise (fp32 at d_k = d_v = 128) through a scratch slot
+    // dS', then the incoming state, go through LDS where they fit; otherwise
+    // (fp32 at the larger heads) through scratch slots
     static constexpr bool FIT = BwdLayout<DT, DK, DV, FULL, true>::LDS <= 160 * 1024;
-    using type = BwdLayout<DT, DK, DV, FULL, FIT>;
+    static constexpr bool FIT_S = BwdLayout<DT, DK, DV, FULL, FIT, true>::LDS <= 160 * 1024;
+    using type = BwdLayout<DT, DK, DV, FULL, FIT, FIT_S>;
 };
 template <typename DT, int DK, int DV, bool FULL>
 using BwdCfg = typename BwdCfgSel<DT, DK, DV, FULL>::type;
 
-// state slots per workgroup in the scratch: one per sub-chunk start, and dS'
-// when it does not fit in LDS
+// state slots per workgroup in the scratch: per sub-chunk start the state as
+// the chain waves' accumulator tiles, and row-major too when the slices cannot
+// read it from LDS; then dS' when it does not fit in LDS
 template <typename DT, int DK, int DV>
-constexpr int bwd_slots() { return BNSUB + (BwdCfg<DT, DK, DV, true>::DSN_LDS ? 0 : 1); }
+constexpr int bwd_slots()
+{
+    using C = BwdCfg<DT, DK, DV, true>;
+    return BNSUB * (C::S_LDS ? 1 : 2) + (C::DSN_LDS ? 0 : 1);
+}
 
 // A 16x16x16 operand whose lane (l16 + 16 q4) holds p[l16][4 q4 .. 4 q4 + 3]:
 // as A it is the matrix p, as B its transpose.
@@ -466,7 +475,9 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
     // this workgroup's scratch: the state at each sub-chunk start of the
     // current chunk (row-major [DK][DV] fp32), then dS' when it is not in LDS
     float* slots = a.scratch + int64_t(blockIdx.x) * bwd_slots<DT, DK, DV>() * DK * DV;
-    float* gdsn = slots + BNSUB * DK * DV;
+    float* slotsB = slots + BNSUB * DK * DV;  // row-major copies (when the state is not staged in LDS)
+    float* gdsn = slots + BNSUB * (C::S_LDS ? 1 : 2) * DK * DV;
+    OT* sS = reinterpret_cast<OT*>(sm + C::O_SS);
 
     // X = V - K^ S and U = T Diag(beta) X for this wave's columns; S tiles from st(kt, ct)
     auto fwd_xu = [&](auto&& st, f32x4 (&X)[2], f32x4 (&U)[2]) {
@@ -558,14 +569,22 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
                 for (int s = 0; s < nsub; ++s) {
                     if (chain) {
                         const int lane = fresh_lane(), l16 = lane & 15, q4 = lane >> 4;
-                        float* dst = slots + s * DK * DV;
+                        float* dst = slots + s * DK * DV;  // accumulator tiles, one 16-byte vector per tile
 #pragma unroll
                         for (int rt = 0; rt < NCT; ++rt)
 #pragma unroll
                             for (int ct = 0; ct < 2; ++ct)
+                                *reinterpret_cast<f32x4*>(dst + acc_tile_off<DV>(rt, 2 * wave + ct, lane)) = S[rt][ct];
+                        if constexpr (!C::S_LDS) {
+                            float* dstB = slotsB + s * DK * DV;
 #pragma unroll
-                                for (int jj = 0; jj < 4; ++jj)
-                                    dst[uint32_t((16 * rt + 4 * q4 + jj) * DV + col0 + 16 * ct + l16)] = S[rt][ct][jj];
+                            for (int rt = 0; rt < NCT; ++rt)
+#pragma unroll
+                                for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                                    for (int jj = 0; jj < 4; ++jj)
+                                        dstB[uint32_t((16 * rt + 4 * q4 + jj) * DV + col0 + 16 * ct + l16)] = S[rt][ct][jj];
+                        }
                     }
                     if (s + 1 < nsub) fwd_sub(S, t0 + s * BSUB, BSUB, h);
                 }
@@ -574,7 +593,8 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
             for (int s = nsub - 1; s >= 0; --s) {
                 const int64_t t_s = t0 + s * BSUB;
                 const int n = clen - s * BSUB < BSUB ? clen - s * BSUB : BSUB;
-                const float* Sslot = slots + s * DK * DV;
+                const float* SslotA = slots + s * DK * DV;
+                const float* Sslot = slotsB + s * DK * DV;  // row-major (when not staged in LDS)
                 const int64_t row0 = t_s * H + h;
                 const uint32_t rsk = uint32_t(H) * DK, rsv = uint32_t(H) * DV;
                 float* dqb = a.dq + row0 * DK;
@@ -588,13 +608,23 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
                 if (chain) {
                     const int lane = fresh_lane(), l16 = lane & 15, q4 = lane >> 4;
                     f32x4 X[2], U[2], dY[2], dX[2];
-                    fwd_xu([&](int kt, int ct) {
-                        f32x4 x;
+                    f32x4 Sf[NCT][2];
 #pragma unroll
-                        for (int jj = 0; jj < 4; ++jj)
-                            x[jj] = Sslot[uint32_t((16 * kt + 4 * q4 + jj) * DV + col0 + 16 * ct + l16)];
-                        return x;
-                    }, X, U);
+                    for (int kt = 0; kt < NCT; ++kt)
+#pragma unroll
+                        for (int ct = 0; ct < 2; ++ct)
+                            Sf[kt][ct] = *reinterpret_cast<const f32x4*>(SslotA + acc_tile_off<DV>(kt, 2 * wave + ct, lane));
+                    fwd_xu([&](int kt, int ct) { return Sf[kt][ct]; }, X, U);
+                    if constexpr (C::S_LDS) {
+                        // the state for the slices' products (row-major, operand precision)
+#pragma unroll
+                        for (int kt = 0; kt < NCT; ++kt)
+#pragma unroll
+                            for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                                for (int jj = 0; jj < 4; ++jj)
+                                    sS[(16 * kt + 4 * q4 + jj) * C::SV + col0 + 16 * ct + l16] = O::to_op(Sf[kt][ct][jj]);
+                    }
                     bwd_dstep<C, DT, true>(sm, dS, col0, lane, dY, dX, [&] {
                         // dS' for the per-slice products, before dS moves on
 #pragma unroll
@@ -691,7 +721,15 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
                             for (int k4 = 0; k4 < DV / 16; k4 += 4) {
 #pragma unroll
                                 for (int kt = k4; kt < k4 + 4 && kt < DV / 16; ++kt) {
-                                    const f32x4 sv = *reinterpret_cast<const f32x4*>(Sslot + uint32_t(c * DV + 16 * kt + 4 * q4));
+                                    f32x4 sv;
+                                    typename O::Frag4 bs;  // B = S^T
+                                    if constexpr (C::S_LDS) {
+                                        bs = O::load4(sS + c * C::SV + 16 * kt + 4 * q4);
+                                        sv = unpack4<O>(bs);
+                                    } else {
+                                        sv = *reinterpret_cast<const f32x4*>(Sslot + uint32_t(c * DV + 16 * kt + 4 * q4));
+                                        bs = O::make4(sv);
+                                    }
                                     typename O::Frag4 bd;
                                     f32x4 dv;
                                     if constexpr (C::DSN_LDS) {
@@ -702,7 +740,6 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
                                         bd = O::make4(dv);
                                     }
                                     dot += sv[0] * dv[0] + sv[1] * dv[1] + sv[2] * dv[2] + sv[3] * dv[3];
-                                    const auto bs = O::make4(sv);  // B = S^T
                                     O::mma4(aQ, frag_rows<O>(sDO + 16 * kt, C::SV, lane), bs);
                                     O::mma4(aK, frag_rows<O>(sVY + 16 * kt, C::SV, lane), bs);
                                     O::mma4(aT, frag_rows<O>(sU + 16 * kt, C::SV, lane), bd);
