@@ -175,6 +175,15 @@ __device__ __forceinline__ float sum16(float x)
     return x;
 }
 
+// Lanes per channel in the prep: the largest power of two up to NT / DK,
+// at most the sub-chunk's 16 tokens.
+constexpr int bwd_prep_parts(int nt, int dk)
+{
+    int p = 1;
+    while (p * 2 <= nt / dk && p * 2 <= BSUB) p *= 2;
+    return p;
+}
+
 // Every state-independent operand of one sub-chunk (tokens t_s .. t_s + n - 1
 // of head h), by the whole workgroup.  FWD: a forward sub-chunk (K~^T in the
 // shared slot, no dO or Q^ tiles); otherwise a backward one (K-^T, dO).
@@ -203,35 +212,49 @@ __device__ __forceinline__ void bwd_prep(const BackwardArgs& a, unsigned char* s
     // uniform bases at the sub-chunk's first row; lanes add 32-bit offsets
     const int64_t row0 = t_s * H + h;
     const uint32_t rsk = uint32_t(H) * DK, rsv = uint32_t(H) * DV;
-    if (tid < DK) {
-        // one thread per channel over the sub-chunk; rows past the end re-read
-        // the last valid row (so every load is issued up front) and count as 0
-        const int c = tid;
+    // PARTS adjacent lanes per channel, each over a run of TPT tokens: the
+    // running sum of g crosses the runs as a lane scan.  Rows past the end
+    // re-read the last valid row (so every load is issued up front) and count as 0.
+    constexpr int PARTS = bwd_prep_parts(C::NT, DK), TPT = BSUB / PARTS;
+    if (tid < DK * PARTS) {
+        const int c = tid / PARTS, part = tid % PARTS, r0 = part * TPT;
         const STG* gb = g + row0 * DK;
         const STG* kb = k + row0 * DK;
         const STG* qb = q + row0 * DK;
-        float gr[BSUB], kr[BSUB], qr[BSUB];
+        float gr[TPT], kr[TPT], qr[TPT];
 #pragma unroll
-        for (int r = 0; r < BSUB; ++r) {
+        for (int i = 0; i < TPT; ++i) {
+            const int r = r0 + i;
             const uint32_t off = uint32_t(r < n ? r : n - 1) * rsk + uint32_t(c);
-            gr[r] = load_elem<DT>(gb, off);
-            kr[r] = load_elem<DT>(kb, off);
-            if (!fwd) qr[r] = load_elem<DT>(qb, off);
+            gr[i] = load_elem<DT>(gb, off);
+            kr[i] = load_elem<DT>(kb, off);
+            if (!fwd) qr[i] = load_elem<DT>(qb, off);
         }
-        float G[BSUB];
+        float G[TPT];
         float run = 0.f;
 #pragma unroll
-        for (int r = 0; r < BSUB; ++r) {
-            run += r < n ? gr[r] : 0.f;
-            G[r] = run;
-            if (FULL) sG[r * DK + c] = run;
+        for (int i = 0; i < TPT; ++i) {
+            run += r0 + i < n ? gr[i] : 0.f;
+            G[i] = run;
         }
-        sGam[c] = __expf(run);
+        // exclusive prefix over the runs before this one, and the sub-chunk's total
+        float incl = run;
 #pragma unroll
-        for (int r = 0; r < BSUB; ++r) {
+        for (int d = 1; d < PARTS; d *= 2) {
+            const float y = __shfl_up(incl, d, PARTS);
+            if (part >= d) incl += y;
+        }
+        const float total = __shfl(incl, PARTS - 1, PARTS);
+        const float excl = incl - run;
+        if (part == PARTS - 1) sGam[c] = __expf(total);
+#pragma unroll
+        for (int i = 0; i < TPT; ++i) {
+            const int r = r0 + i;
             const bool ok = r < n;
-            const float kv = ok ? kr[r] : 0.f;
-            const float eG = __expf(G[r]), eM = __expf(-G[r]), eT = __expf(run - G[r]);
+            const float Gr = excl + G[i];
+            if (FULL) sG[r * DK + c] = Gr;
+            const float kv = ok ? kr[i] : 0.f;
+            const float eG = __expf(Gr), eM = __expf(-Gr), eT = __expf(total - Gr);
             const OT kh = O::to_op(kv * eG), km = O::to_op(kv * eM), kt = O::to_op(kv * eT);
             sKH[r * C::SK + c] = kh;
             sKHT[c * C::S16 + r] = kh;
@@ -239,7 +262,7 @@ __device__ __forceinline__ void bwd_prep(const BackwardArgs& a, unsigned char* s
             sKT[r * C::SK + c] = kt;
             if (FULL) sKMT[c * C::S16 + r] = fwd ? kt : km;
             if (!fwd) {
-                const OT qh = O::to_op((ok ? qr[r] : 0.f) * eG);
+                const OT qh = O::to_op((ok ? qr[i] : 0.f) * eG);
                 sQH[r * C::SK + c] = qh;
                 sQHT[c * C::S16 + r] = qh;
             }
