@@ -38,10 +38,10 @@
 //     keeping the state at each 16-token sub-chunk start in a per-workgroup
 //     scratch slot (4 states, not one per token), then takes the sub-chunks in
 //     reverse.
-// dS (and, in the forward, S) lives in registers as 16x16 accumulator tiles,
-// 32 columns per wave.  Products that contract over d_v (dQ^, dK^, dK~, dP)
-// run per 32-channel slice of d_k, with S read back row-major from the slot
-// and dS' staged in LDS.
+// dS (and, in the forward, S) lives in registers as 16x16 accumulator tiles:
+// 16 columns per wave in the full pass, 32 in the summary.  Products that
+// contract over d_v (dQ^, dK^, dK~, dP) run per 16-channel unit of d_k, one
+// unit per wave, with S and dS' staged in LDS.
 #pragma once
 
 #include "kda_prefill.hpp"
@@ -56,9 +56,10 @@ template <typename DT, int DKV, int DVV, bool FULL, bool DSN_LDS_, bool S_LDS_ =
 struct BwdLayout {
     static constexpr int DK = DKV, DV = DVV;
     static constexpr int NCOL = FULL ? DV : DV + DK;  // dS columns (extended in the summary)
-    static constexpr int NCW = NCOL / 32;             // waves holding dS columns
-    static constexpr int NSL = DK / 32;               // 32-channel slices of d_k
-    static constexpr int NW = FULL ? (NCW > NSL ? NCW : NSL) : NCW;
+    static constexpr int CT = FULL ? 1 : 2;           // 16-column tiles of dS per chain wave
+    static constexpr int NCW = NCOL / (16 * CT);      // waves holding dS columns
+    static constexpr int NU = DK / 16;                // 16-channel units of d_k (per-slice products)
+    static constexpr int NW = FULL ? (NCW > NU ? NCW : NU) : NCW;
     static constexpr int NT = 64 * NW;
     static constexpr bool DSN_LDS = DSN_LDS_;
     static constexpr bool S_LDS = FULL && S_LDS_;  // the sub-chunk's incoming state staged in LDS for the slices
@@ -95,9 +96,9 @@ struct BwdLayout {
     static constexpr int O_GAM = O_G + (FULL ? BSUB * DK * 4 : 0);  // gamma [DK]
     static constexpr int O_BETA = O_GAM + DK * 4;               // beta [16]
     static constexpr int O_RB = O_BETA + BSUB * 4;              // dbeta partials [NW][16]
-    static constexpr int O_DG = O_RB + (FULL ? NW * BSUB * 4 : 0);  // dG per wave [16][33]
-    static constexpr int O_GL = O_DG + (FULL ? NW * BSUB * 33 * 4 : 0);  // dG_last per wave [32]
-    static constexpr int LDS = O_GL + (FULL ? NW * 32 * 4 : 0);
+    static constexpr int O_DG = O_RB + (FULL ? NW * BSUB * 4 : 0);  // dG per wave [16][17]
+    static constexpr int O_GL = O_DG + (FULL ? NW * BSUB * 17 * 4 : 0);  // dG_last per wave [16]
+    static constexpr int LDS = O_GL + (FULL ? NW * 16 * 4 : 0);
 };
 
 template <typename DT, int DK, int DV, bool FULL>
@@ -349,8 +350,8 @@ __device__ __forceinline__ void bwd_small(unsigned char* sm, int lane, bool need
 // (HASDO: the columns see dO).  Returns dY and, through dS, the gradient at
 // the sub-chunk's start.  Before the update, hook(dS') sees the incoming dS.
 template <typename C, typename DT, bool HASDO, typename Hook>
-__device__ __forceinline__ void bwd_dstep(unsigned char* sm, f32x4 (&dS)[C::DK / 16][2], int col0, int lane,
-                                          f32x4 (&dY)[2], f32x4 (&dX)[2], Hook&& hook)
+__device__ __forceinline__ void bwd_dstep(unsigned char* sm, f32x4 (&dS)[C::DK / 16][C::CT], int col0, int lane,
+                                          f32x4 (&dY)[C::CT], f32x4 (&dX)[C::CT], Hook&& hook)
 {
     using O = Op<DT>;
     using OT = typename O::T;
@@ -363,14 +364,14 @@ __device__ __forceinline__ void bwd_dstep(unsigned char* sm, f32x4 (&dS)[C::DK /
     const OT* sP = reinterpret_cast<const OT*>(sm + C::O_P);
     const float* sB = reinterpret_cast<const float*>(sm + C::O_BETA);
     const float* sGam = reinterpret_cast<const float*>(sm + C::O_GAM);
-    typename O::Frag4 bdo[2];
+    typename O::Frag4 bdo[C::CT];
     if constexpr (HASDO) {
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) bdo[ct] = frag_rows<O>(sDOT + (col0 + 16 * ct) * C::S16, C::S16, lane);  // B = dO
+        for (int ct = 0; ct < C::CT; ++ct) bdo[ct] = frag_rows<O>(sDOT + (col0 + 16 * ct) * C::S16, C::S16, lane);  // B = dO
     }
     const auto aTt = frag_cols<O>(sT, C::S16, lane);  // A = T^T
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
+    for (int ct = 0; ct < C::CT; ++ct) {
         f32x4 du = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kt = 0; kt < C::DK / 16; ++kt)
@@ -383,9 +384,9 @@ __device__ __forceinline__ void bwd_dstep(unsigned char* sm, f32x4 (&dS)[C::DK /
         for (int j = 0; j < 4; ++j) dX[ct][j] = sB[4 * q4 + j] * y[j];
     }
     hook();
-    typename O::Frag4 ndx[2];
+    typename O::Frag4 ndx[C::CT];
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) ndx[ct] = O::make4(-dX[ct]);
+    for (int ct = 0; ct < C::CT; ++ct) ndx[ct] = O::make4(-dX[ct]);
 #pragma unroll
     for (int rt = 0; rt < C::DK / 16; ++rt) {
         const auto aq = frag_rows<O>(sQHT + 16 * rt * C::S16, C::S16, lane);  // A = Q^^T
@@ -394,7 +395,7 @@ __device__ __forceinline__ void bwd_dstep(unsigned char* sm, f32x4 (&dS)[C::DK /
 #pragma unroll
         for (int j = 0; j < 4; ++j) gm[j] = sGam[16 * rt + 4 * q4 + j];
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
+        for (int ct = 0; ct < C::CT; ++ct) {
             f32x4 s = gm * dS[rt][ct];
             if constexpr (HASDO) O::mma4(s, aq, bdo[ct]);
             O::mma4(s, ak, ndx[ct]);
@@ -420,6 +421,7 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, false>::NT)) bwd_chunk_sum
     const bool mcols = wave >= DV / 32;  // a wave of the N (identity) columns
     const bool active = !(mcols && last);
     const int col0 = (mcols ? wave - DV / 32 : wave) * 32;
+    static_assert(C::CT == 2, "summary waves hold 32 columns");
     f32x4 dS[DK / 16][2];
 #pragma unroll
     for (int rt = 0; rt < DK / 16; ++rt)
@@ -472,10 +474,11 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
     using OT = typename O::T;
     using STG = typename DT::storage;
     constexpr int NCT = DK / 16;
+    constexpr int CT = C::CT;  // 16-column tiles per chain wave
     extern __shared__ __attribute__((aligned(16))) unsigned char sm[];
     const int wave = threadIdx.x >> 6;
     const bool chain = wave < C::NCW;  // holds 32 columns of dS
-    const int col0 = wave * 32;
+    const int col0 = wave * 16 * CT;
     const int H = a.H;
     const STG* q = static_cast<const STG*>(a.q);
     const STG* k = static_cast<const STG*>(a.k);
@@ -493,8 +496,8 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
     const float* sGam = reinterpret_cast<const float*>(sm + C::O_GAM);
     const float* sB = reinterpret_cast<const float*>(sm + C::O_BETA);
     float* sRB = reinterpret_cast<float*>(sm + C::O_RB);
-    float* sDG = reinterpret_cast<float*>(sm + C::O_DG) + wave * BSUB * 33;
-    float* sGL = reinterpret_cast<float*>(sm + C::O_GL) + wave * 32;
+    float* sDG = reinterpret_cast<float*>(sm + C::O_DG) + wave * BSUB * 17;
+    float* sGL = reinterpret_cast<float*>(sm + C::O_GL) + wave * 16;
     // this workgroup's scratch: the state at each sub-chunk start of the
     // current chunk (row-major [DK][DV] fp32), then dS' when it is not in LDS
     float* slots = a.scratch + int64_t(blockIdx.x) * bwd_slots<DT, DK, DV>() * DK * DV;
@@ -503,11 +506,11 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
     OT* sS = reinterpret_cast<OT*>(sm + C::O_SS);
 
     // X = V - K^ S and U = T Diag(beta) X for this wave's columns; S tiles from st(kt, ct)
-    auto fwd_xu = [&](auto&& st, f32x4 (&X)[2], f32x4 (&U)[2]) {
+    auto fwd_xu = [&](auto&& st, f32x4 (&X)[CT], f32x4 (&U)[CT]) {
         const int lane = fresh_lane(), l16 = lane & 15, q4 = lane >> 4;
         const auto aT = frag_rows<O>(sT, C::S16, lane);
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
+        for (int ct = 0; ct < CT; ++ct) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int k4 = 0; k4 < NCT; k4 += 4) {
@@ -529,16 +532,18 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
         }
     };
     // one forward sub-chunk on the register state S (prep and small already done)
-    auto fwd_update = [&](f32x4 (&S)[NCT][2]) {
-        f32x4 X[2], U[2];
+    auto fwd_update = [&](f32x4 (&S)[NCT][CT]) {
+        f32x4 X[CT], U[CT];
         fwd_xu([&](int kt, int ct) { return S[kt][ct]; }, X, U);
         const int lane = fresh_lane(), q4 = lane >> 4;
-        typename O::Frag4 bu[2] = {O::make4(U[0]), O::make4(U[1])};
+        typename O::Frag4 bu[CT];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) bu[ct] = O::make4(U[ct]);
 #pragma unroll
         for (int rt = 0; rt < NCT; ++rt) {
             const auto ak = frag_rows<O>(sKMT + 16 * rt * C::S16, C::S16, lane);  // A = K~^T
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
+            for (int ct = 0; ct < CT; ++ct) {
                 f32x4 s;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) s[j] = sGam[16 * rt + 4 * q4 + j] * S[rt][ct][j];
@@ -547,7 +552,7 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
             }
         }
     };
-    auto fwd_sub = [&](f32x4 (&S)[NCT][2], int64_t t_s, int n, int h) {
+    auto fwd_sub = [&](f32x4 (&S)[NCT][CT], int64_t t_s, int n, int h) {
         bwd_prep<C, DT, true>(a, sm, t_s, n, h, true);
         __syncthreads();
         if (wave == 0) bwd_small<C, DT, true>(sm, fresh_lane(), false);
@@ -555,12 +560,12 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
         if (chain) fwd_update(S);
         __syncthreads();
     };
-    auto load_tiles = [&](f32x4 (&S)[NCT][2], const float* src) {
+    auto load_tiles = [&](f32x4 (&S)[NCT][CT], const float* src) {
         const int lane = fresh_lane(), l16 = lane & 15, q4 = lane >> 4;
 #pragma unroll
         for (int rt = 0; rt < NCT; ++rt)
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
+            for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     S[rt][ct][j] = src ? src[uint32_t((16 * rt + 4 * q4 + j) * DV + col0 + 16 * ct + l16)] : 0.f;
@@ -572,7 +577,7 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
         if (L.n < 0) break;
         const int64_t c0 = L.c0, ck0 = L.ck0;
         const int64_t unit = int64_t(L.n) * H + h;
-        f32x4 dS[NCT][2];
+        f32x4 dS[NCT][CT];
         if (chain) load_tiles(dS, a.dsend + int64_t(item) * DK * DV);
         const int64_t j0 = (L.t0 - c0) / BWD_CHUNK, j1 = (L.t1 - c0 + BWD_CHUNK - 1) / BWD_CHUNK;
         for (int64_t j = j1 - 1; j >= j0; --j) {
@@ -581,7 +586,7 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
             const int nsub = (clen + BSUB - 1) / BSUB;
             // the state before token t0: the checkpoint, or recomputed from the initial state
             {
-                f32x4 S[NCT][2];
+                f32x4 S[NCT][CT];
                 const float* init = a.init ? a.init + unit * DK * DV : nullptr;
                 const int64_t ckrow = ck0 + j - 1;
                 const bool have_ck = j > 0 && a.ckpt && ckrow < a.ckpt_cap;
@@ -596,14 +601,14 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
 #pragma unroll
                         for (int rt = 0; rt < NCT; ++rt)
 #pragma unroll
-                            for (int ct = 0; ct < 2; ++ct)
-                                *reinterpret_cast<f32x4*>(dst + acc_tile_off<DV>(rt, 2 * wave + ct, lane)) = S[rt][ct];
+                            for (int ct = 0; ct < CT; ++ct)
+                                *reinterpret_cast<f32x4*>(dst + acc_tile_off<DV>(rt, CT * wave + ct, lane)) = S[rt][ct];
                         if constexpr (!C::S_LDS) {
                             float* dstB = slotsB + s * DK * DV;
 #pragma unroll
                             for (int rt = 0; rt < NCT; ++rt)
 #pragma unroll
-                                for (int ct = 0; ct < 2; ++ct)
+                                for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
                                     for (int jj = 0; jj < 4; ++jj)
                                         dstB[uint32_t((16 * rt + 4 * q4 + jj) * DV + col0 + 16 * ct + l16)] = S[rt][ct][jj];
@@ -630,20 +635,20 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
                 __syncthreads();
                 if (chain) {
                     const int lane = fresh_lane(), l16 = lane & 15, q4 = lane >> 4;
-                    f32x4 X[2], U[2], dY[2], dX[2];
-                    f32x4 Sf[NCT][2];
+                    f32x4 X[CT], U[CT], dY[CT], dX[CT];
+                    f32x4 Sf[NCT][CT];
 #pragma unroll
                     for (int kt = 0; kt < NCT; ++kt)
 #pragma unroll
-                        for (int ct = 0; ct < 2; ++ct)
-                            Sf[kt][ct] = *reinterpret_cast<const f32x4*>(SslotA + acc_tile_off<DV>(kt, 2 * wave + ct, lane));
+                        for (int ct = 0; ct < CT; ++ct)
+                            Sf[kt][ct] = *reinterpret_cast<const f32x4*>(SslotA + acc_tile_off<DV>(kt, CT * wave + ct, lane));
                     fwd_xu([&](int kt, int ct) { return Sf[kt][ct]; }, X, U);
                     if constexpr (C::S_LDS) {
                         // the state for the slices' products (row-major, operand precision)
 #pragma unroll
                         for (int kt = 0; kt < NCT; ++kt)
 #pragma unroll
-                            for (int ct = 0; ct < 2; ++ct)
+                            for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
                                 for (int jj = 0; jj < 4; ++jj)
                                     sS[(16 * kt + 4 * q4 + jj) * C::SV + col0 + 16 * ct + l16] = O::to_op(Sf[kt][ct][jj]);
@@ -653,7 +658,7 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
 #pragma unroll
                         for (int rt = 0; rt < NCT; ++rt)
 #pragma unroll
-                            for (int ct = 0; ct < 2; ++ct)
+                            for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
                                 for (int jj = 0; jj < 4; ++jj) {
                                     const int row = 16 * rt + 4 * q4 + jj, col = col0 + 16 * ct + l16;
@@ -664,7 +669,7 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
                     // dv = dX; dbeta's <dY, X> part; U and dY for the slices
                     float pb[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int ct = 0; ct < 2; ++ct)
+                    for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
                         for (int jj = 0; jj < 4; ++jj) {
                             const int r = 4 * q4 + jj, col = col0 + 16 * ct + l16;
@@ -680,8 +685,18 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
                     }
                 }
                 __syncthreads();
-                if (wave < C::NSL) {
+                if (wave < C::NU) {
                     const int lane = fresh_lane(), l16 = lane & 15, q4 = lane >> 4;
+                    const int ch0 = 16 * wave, c = ch0 + l16;  // this wave's 16 channels
+                    // raw k and q of this lane's elements (rows past the end re-read the last one)
+                    float kq[4][2];
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const int r = 4 * q4 + jj;
+                        const uint32_t off = uint32_t(r < n ? r : n - 1) * rsk + uint32_t(c);
+                        kq[jj][0] = load_elem<DT>(k + row0 * DK, off);
+                        kq[jj][1] = load_elem<DT>(q + row0 * DK, off);
+                    }
                     // dP = incl(dO U^T), dA' = -Diag(beta) strict(dY U^T), each with its transpose
                     f32x4 dP = {0.f, 0.f, 0.f, 0.f}, dPT = dP, M1 = dP, M1T = dP;
 #pragma unroll
@@ -721,96 +736,73 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
                     const auto fdPT = O::make4(dP);   // A = dP^T
                     const auto fdA = O::make4(M1T);   // A = dA'
                     const auto fdAT = O::make4(M1);   // A = dA'^T
-                    for (int sl = wave; sl < C::NSL; sl += C::NW) {
-                        // raw k and q of this lane's elements (rows past the end re-read the last one)
-                        float kq[2][4][2];
+                    f32x4 aQ = {0.f, 0.f, 0.f, 0.f}, aK = aQ, aT = aQ;
+                    float dot = 0.f;
 #pragma unroll
-                        for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-                            for (int jj = 0; jj < 4; ++jj) {
-                                const int r = 4 * q4 + jj;
-                                const uint32_t off = uint32_t(r < n ? r : n - 1) * rsk + uint32_t(32 * sl + 16 * nt + l16);
-                                kq[nt][jj][0] = load_elem<DT>(k + row0 * DK, off);
-                                kq[nt][jj][1] = load_elem<DT>(q + row0 * DK, off);
-                            }
-#pragma unroll
-                        for (int nt = 0; nt < 2; ++nt) {
-                            const int ch0 = 32 * sl + 16 * nt;
-                            const int c = ch0 + l16;
-                            f32x4 aQ = {0.f, 0.f, 0.f, 0.f}, aK = aQ, aT = aQ;
-                            float dot = 0.f;
-                            // four k-steps at a time, so the row loads of S stay few
-#pragma unroll
-                            for (int k4 = 0; k4 < DV / 16; k4 += 4) {
-#pragma unroll
-                                for (int kt = k4; kt < k4 + 4 && kt < DV / 16; ++kt) {
-                                    f32x4 sv;
-                                    typename O::Frag4 bs;  // B = S^T
-                                    if constexpr (C::S_LDS) {
-                                        bs = O::load4(sS + c * C::SV + 16 * kt + 4 * q4);
-                                        sv = unpack4<O>(bs);
-                                    } else {
-                                        sv = *reinterpret_cast<const f32x4*>(Sslot + uint32_t(c * DV + 16 * kt + 4 * q4));
-                                        bs = O::make4(sv);
-                                    }
-                                    typename O::Frag4 bd;
-                                    f32x4 dv;
-                                    if constexpr (C::DSN_LDS) {
-                                        bd = O::load4(sDSN + c * C::SV + 16 * kt + 4 * q4);
-                                        dv = unpack4<O>(bd);
-                                    } else {
-                                        dv = *reinterpret_cast<const f32x4*>(gdsn + uint32_t(c * DV + 16 * kt + 4 * q4));
-                                        bd = O::make4(dv);
-                                    }
-                                    dot += sv[0] * dv[0] + sv[1] * dv[1] + sv[2] * dv[2] + sv[3] * dv[3];
-                                    O::mma4(aQ, frag_rows<O>(sDO + 16 * kt, C::SV, lane), bs);
-                                    O::mma4(aK, frag_rows<O>(sVY + 16 * kt, C::SV, lane), bs);
-                                    O::mma4(aT, frag_rows<O>(sU + 16 * kt, C::SV, lane), bd);
-                                }
-                                __builtin_amdgcn_sched_barrier(0);
-                            }
-#pragma unroll
-                            for (int jj = 0; jj < 4; ++jj) aK[jj] *= -sB[4 * q4 + jj];
-                            const auto bkm = frag_rows<O>(sKMT + ch0 * C::S16, C::S16, lane);  // B = K-
-                            O::mma4(aQ, fdP, bkm);
-                            O::mma4(aK, fdA, bkm);
-                            f32x4 aM = {0.f, 0.f, 0.f, 0.f};
-                            O::mma4(aM, fdAT, frag_rows<O>(sKHT + ch0 * C::S16, C::S16, lane));  // dA'^T K^
-                            O::mma4(aM, fdPT, frag_rows<O>(sQHT + ch0 * C::S16, C::S16, lane));  // + dP^T Q^
-                            const float Gl = sG[(BSUB - 1) * DK + c];
-                            float gl = 0.f;
-#pragma unroll
-                            for (int jj = 0; jj < 4; ++jj) {
-                                const int r = 4 * q4 + jj;
-                                const bool ok = r < n;
-                                const uint32_t off = uint32_t(r) * rsk + uint32_t(c);
-                                const float kv = ok ? kq[nt][jj][0] : 0.f;
-                                const float qv = ok ? kq[nt][jj][1] : 0.f;
-                                const float G = sG[r * DK + c];
-                                const float eG = __expf(G), eM = __expf(-G), eT = __expf(Gl - G);
-                                const float Qh = qv * eG, Kh = kv * eG, Km = kv * eM, Kt = kv * eT;
-                                const float dq = aQ[jj] * eG;
-                                const float dk = aK[jj] * eG + aM[jj] * eM + aT[jj] * eT;
-                                const float dG = aQ[jj] * Qh + aK[jj] * Kh - aM[jj] * Km - aT[jj] * Kt;
-                                gl += aT[jj] * Kt;
-                                if (ok) {
-                                    dqb[off] = dq;
-                                    dkb[off] = dk;
-                                }
-                                sDG[r * 33 + 16 * nt + l16] = dG;
-                            }
-                            float tot = gl + sGam[c] * dot;
-                            tot += xor_lanes(tot, 16, lane);
-                            tot += xor_lanes(tot, 32, lane);
-                            if (q4 == 0) sGL[16 * nt + l16] = tot;
+                    for (int kt = 0; kt < DV / 16; ++kt) {
+                        f32x4 sv;
+                        typename O::Frag4 bs;  // B = S^T
+                        if constexpr (C::S_LDS) {
+                            bs = O::load4(sS + c * C::SV + 16 * kt + 4 * q4);
+                            sv = unpack4<O>(bs);
+                        } else {
+                            sv = *reinterpret_cast<const f32x4*>(Sslot + uint32_t(c * DV + 16 * kt + 4 * q4));
+                            bs = O::make4(sv);
                         }
-                        // dg: reverse running sum over the sub-chunk, one lane per channel
-                        if (lane < 32) {
-                            float acc = sGL[lane];
-                            for (int r = BSUB - 1; r >= 0; --r) {
-                                acc += sDG[r * 33 + lane];
-                                if (r < n) dgb[uint32_t(r) * rsk + uint32_t(32 * sl + lane)] = acc;
-                            }
+                        typename O::Frag4 bd;  // B = dS'^T
+                        f32x4 dv;
+                        if constexpr (C::DSN_LDS) {
+                            bd = O::load4(sDSN + c * C::SV + 16 * kt + 4 * q4);
+                            dv = unpack4<O>(bd);
+                        } else {
+                            dv = *reinterpret_cast<const f32x4*>(gdsn + uint32_t(c * DV + 16 * kt + 4 * q4));
+                            bd = O::make4(dv);
+                        }
+                        dot += sv[0] * dv[0] + sv[1] * dv[1] + sv[2] * dv[2] + sv[3] * dv[3];
+                        O::mma4(aQ, frag_rows<O>(sDO + 16 * kt, C::SV, lane), bs);
+                        O::mma4(aK, frag_rows<O>(sVY + 16 * kt, C::SV, lane), bs);
+                        O::mma4(aT, frag_rows<O>(sU + 16 * kt, C::SV, lane), bd);
+                    }
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) aK[jj] *= -sB[4 * q4 + jj];
+                    const auto bkm = frag_rows<O>(sKMT + ch0 * C::S16, C::S16, lane);  // B = K-
+                    O::mma4(aQ, fdP, bkm);
+                    O::mma4(aK, fdA, bkm);
+                    f32x4 aM = {0.f, 0.f, 0.f, 0.f};
+                    O::mma4(aM, fdAT, frag_rows<O>(sKHT + ch0 * C::S16, C::S16, lane));  // dA'^T K^
+                    O::mma4(aM, fdPT, frag_rows<O>(sQHT + ch0 * C::S16, C::S16, lane));  // + dP^T Q^
+                    const float Gl = sG[(BSUB - 1) * DK + c];
+                    float gl = 0.f;
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const int r = 4 * q4 + jj;
+                        const bool ok = r < n;
+                        const uint32_t off = uint32_t(r) * rsk + uint32_t(c);
+                        const float kv = ok ? kq[jj][0] : 0.f;
+                        const float qv = ok ? kq[jj][1] : 0.f;
+                        const float G = sG[r * DK + c];
+                        const float eG = __expf(G), eM = __expf(-G), eT = __expf(Gl - G);
+                        const float Qh = qv * eG, Kh = kv * eG, Km = kv * eM, Kt = kv * eT;
+                        const float dq = aQ[jj] * eG;
+                        const float dk = aK[jj] * eG + aM[jj] * eM + aT[jj] * eT;
+                        const float dG = aQ[jj] * Qh + aK[jj] * Kh - aM[jj] * Km - aT[jj] * Kt;
+                        gl += aT[jj] * Kt;
+                        if (ok) {
+                            dqb[off] = dq;
+                            dkb[off] = dk;
+                        }
+                        sDG[r * 17 + l16] = dG;
+                    }
+                    float tot = gl + sGam[c] * dot;
+                    tot += xor_lanes(tot, 16, lane);
+                    tot += xor_lanes(tot, 32, lane);
+                    if (q4 == 0) sGL[l16] = tot;
+                    // dg: reverse running sum over the sub-chunk, one lane per channel
+                    if (lane < 16) {
+                        float acc = sGL[lane];
+                        for (int r = BSUB - 1; r >= 0; --r) {
+                            acc += sDG[r * 17 + lane];
+                            if (r < n) dgb[uint32_t(r) * rsk + uint32_t(ch0 + lane)] = acc;
                         }
                     }
                 }
