@@ -56,7 +56,9 @@ template <typename DT, int DKV, int DVV, bool FULL, bool DSN_LDS_, bool S_LDS_ =
 struct BwdLayout {
     static constexpr int DK = DKV, DV = DVV;
     static constexpr int NCOL = FULL ? DV : DV + DK;  // dS columns (extended in the summary)
-    static constexpr int CT = FULL ? 1 : 2;           // 16-column tiles of dS per chain wave
+    // 16-column tiles of dS per chain wave: one in the full pass (eight waves,
+    // two per SIMD); two in the summary (its 16-wave variant was slower)
+    static constexpr int CT = FULL ? 1 : 2;
     static constexpr int NCW = NCOL / (16 * CT);      // waves holding dS columns
     static constexpr int NU = DK / 16;                // 16-channel units of d_k (per-slice products)
     static constexpr int NW = FULL ? (NCW > NU ? NCW : NU) : NCW;
@@ -96,9 +98,7 @@ struct BwdLayout {
     static constexpr int O_GAM = O_G + (FULL ? BSUB * DK * 4 : 0);  // gamma [DK]
     static constexpr int O_BETA = O_GAM + DK * 4;               // beta [16]
     static constexpr int O_RB = O_BETA + BSUB * 4;              // dbeta partials [NW][16]
-    static constexpr int O_DG = O_RB + (FULL ? NW * BSUB * 4 : 0);  // dG per wave [16][17]
-    static constexpr int O_GL = O_DG + (FULL ? NW * BSUB * 17 * 4 : 0);  // dG_last per wave [16]
-    static constexpr int LDS = O_GL + (FULL ? NW * 16 * 4 : 0);
+    static constexpr int LDS = O_RB + (FULL ? NW * BSUB * 4 : 0);
 };
 
 template <typename DT, int DK, int DV, bool FULL>
@@ -418,15 +418,15 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, false>::NT)) bwd_chunk_sum
     const SegLoc L = bwd_locate(a, item / H);
     if (L.n < 0) return;
     const bool last = L.s == L.nseg - 1;
-    const bool mcols = wave >= DV / 32;  // a wave of the N (identity) columns
+    constexpr int CT = C::CT, CW = 16 * CT;  // columns per wave
+    const bool mcols = wave >= DV / CW;  // a wave of the N (identity) columns
     const bool active = !(mcols && last);
-    const int col0 = (mcols ? wave - DV / 32 : wave) * 32;
-    static_assert(C::CT == 2, "summary waves hold 32 columns");
-    f32x4 dS[DK / 16][2];
+    const int col0 = (mcols ? wave - DV / CW : wave) * CW;
+    f32x4 dS[DK / 16][CT];
 #pragma unroll
     for (int rt = 0; rt < DK / 16; ++rt)
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
+        for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int row = 16 * rt + 4 * q4 + j, col = col0 + 16 * ct + l16;
@@ -445,7 +445,7 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, false>::NT)) bwd_chunk_sum
             if (wave == 0) bwd_small<C, DT, false>(sm, fresh_lane(), true);
             __syncthreads();
             if (active) {
-                f32x4 dY[2], dX[2];
+                f32x4 dY[CT], dX[CT];
                 if (mcols) bwd_dstep<C, DT, false>(sm, dS, col0, fresh_lane(), dY, dX, [] {});
                 else bwd_dstep<C, DT, true>(sm, dS, col0, fresh_lane(), dY, dX, [] {});
             }
@@ -459,7 +459,7 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, false>::NT)) bwd_chunk_sum
 #pragma unroll
     for (int rt = 0; rt < DK / 16; ++rt)
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
+        for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 out[(16 * rt + 4 * oq4 + j) * ld + col0 + 16 * ct + ol16] = dS[rt][ct][j];
@@ -496,8 +496,6 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
     const float* sGam = reinterpret_cast<const float*>(sm + C::O_GAM);
     const float* sB = reinterpret_cast<const float*>(sm + C::O_BETA);
     float* sRB = reinterpret_cast<float*>(sm + C::O_RB);
-    float* sDG = reinterpret_cast<float*>(sm + C::O_DG) + wave * BSUB * 17;
-    float* sGL = reinterpret_cast<float*>(sm + C::O_GL) + wave * 16;
     // this workgroup's scratch: the state at each sub-chunk start of the
     // current chunk (row-major [DK][DV] fp32), then dS' when it is not in LDS
     float* slots = a.scratch + int64_t(blockIdx.x) * bwd_slots<DT, DK, DV>() * DK * DV;
@@ -772,7 +770,7 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
                     O::mma4(aM, fdAT, frag_rows<O>(sKHT + ch0 * C::S16, C::S16, lane));  // dA'^T K^
                     O::mma4(aM, fdPT, frag_rows<O>(sQHT + ch0 * C::S16, C::S16, lane));  // + dP^T Q^
                     const float Gl = sG[(BSUB - 1) * DK + c];
-                    float gl = 0.f;
+                    float gl = 0.f, dGr[4];
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj) {
                         const int r = 4 * q4 + jj;
@@ -791,19 +789,27 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
                             dqb[off] = dq;
                             dkb[off] = dk;
                         }
-                        sDG[r * 17 + l16] = dG;
+                        dGr[jj] = dG;
                     }
                     float tot = gl + sGam[c] * dot;
                     tot += xor_lanes(tot, 16, lane);
                     tot += xor_lanes(tot, 32, lane);
-                    if (q4 == 0) sGL[l16] = tot;
-                    // dg: reverse running sum over the sub-chunk, one lane per channel
-                    if (lane < 16) {
-                        float acc = sGL[lane];
-                        for (int r = BSUB - 1; r >= 0; --r) {
-                            acc += sDG[r * 17 + lane];
-                            if (r < n) dgb[uint32_t(r) * rsk + uint32_t(ch0 + lane)] = acc;
-                        }
+                    // dg: reverse running sum over the sub-chunk's rows (this lane's
+                    // four, then the row groups after it), plus dG_last
+                    float suf[4];
+                    suf[3] = dGr[3];
+#pragma unroll
+                    for (int jj = 2; jj >= 0; --jj) suf[jj] = suf[jj + 1] + dGr[jj];
+                    float after = 0.f;
+#pragma unroll
+                    for (int qq = 1; qq < 4; ++qq) {
+                        const float b = __shfl(suf[0], l16 + 16 * qq, 64);
+                        after += qq > q4 ? b : 0.f;
+                    }
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const int r = 4 * q4 + jj;
+                        if (r < n) dgb[uint32_t(r) * rsk + uint32_t(c)] = tot + after + suf[jj];
                     }
                 }
                 __syncthreads();
