@@ -81,6 +81,20 @@ def test_decode_validation(L):
     assert call(B=0, q=None, o=None) == 0                  # empty batch: no-op
 
 
+def test_prefill_workspace_head_split(L, monkeypatch):
+    """One long sequence whose segments leave compute units idle takes the head
+    split: its workspace also holds the head's final state (fp32 [H][d_k][d_v]),
+    and is never smaller than the unsplit plan's (a forced segment length turns
+    the split off)."""
+    ws = kda.kda_prefill_workspace_size
+    split = ws(8192, 1, 32, 128, 128)
+    monkeypatch.setenv("KDA_SEG_CHUNKS", "16")
+    plain = ws(8192, 1, 32, 128, 128)
+    monkeypatch.delenv("KDA_SEG_CHUNKS")
+    assert split >= 32 * 128 * 128 * 4 and split >= plain
+    assert ws(8192, 2, 32, 128, 128) > 0  # packed sequences: no split
+
+
 def test_prefill_workspace_size(L):
     ws = kda.kda_prefill_workspace_size
     assert ws(8192, 1, 32, 128, 128) > 0

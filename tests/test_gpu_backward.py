@@ -67,7 +67,7 @@ def run_case(kda, wl, with_ckpt, heads=None, seed=5):
 @pytest.mark.parametrize("with_ckpt", [False, True])
 @pytest.mark.parametrize("dk,dv,dtype", [(32, 32, "f32"), (32, 64, "f32"), (64, 64, "bf16"),
                                          (128, 128, "bf16"), (128, 32, "bf16"), (32, 128, "bf16"),
-                                         (128, 128, "f32"), (64, 128, "f32")])
+                                         (128, 128, "f32"), (64, 128, "f32"), (128, 64, "f32")])
 def test_backward_varlen(kda, dk, dv, dtype, with_ckpt):
     if with_ckpt and dtype == "f32" and not (dk == 32 and dv <= 64):
         pytest.skip("the prefill has no fp32 path for this head shape, so there are no checkpoints to start from")
