@@ -253,14 +253,16 @@ __device__ __forceinline__ void bwd_prep(const BackwardArgs& a, unsigned char* s
             const int r = r0 + i;
             const bool ok = r < n;
             const float Gr = excl + G[i];
-            if (FULL) sG[r * DK + c] = Gr;
+            if (FULL && !fwd) sG[r * DK + c] = Gr;
             const float kv = ok ? kr[i] : 0.f;
             const float eG = __expf(Gr), eM = __expf(-Gr), eT = __expf(total - Gr);
             const OT kh = O::to_op(kv * eG), km = O::to_op(kv * eM), kt = O::to_op(kv * eT);
             sKH[r * C::SK + c] = kh;
-            sKHT[c * C::S16 + r] = kh;
             sKM[r * C::SK + c] = km;
-            sKT[r * C::SK + c] = kt;
+            if (!fwd) {  // the forward sub-chunks read K^ (rows), K- and K~^T only
+                sKHT[c * C::S16 + r] = kh;
+                sKT[r * C::SK + c] = kt;
+            }
             if (FULL) sKMT[c * C::S16 + r] = fwd ? kt : km;
             if (!fwd) {
                 const OT qh = O::to_op((ok ? qr[i] : 0.f) * eG);
@@ -312,7 +314,28 @@ __device__ __forceinline__ void bwd_prep(const BackwardArgs& a, unsigned char* s
     }
 }
 
-// A' (strictly lower), P (lower with the diagonal) and T = (I + Diag(beta) A')^{-1},
+// P (lower with the diagonal), by one wave on the matrix cores.
+template <typename C, typename DT>
+__device__ __forceinline__ void bwd_small_p(unsigned char* sm, int lane)
+{
+    using O = Op<DT>;
+    using OT = typename O::T;
+    const int l16 = lane & 15, q4 = lane >> 4;
+    const OT* sKM = reinterpret_cast<const OT*>(sm + C::O_KM);
+    const OT* sQH = reinterpret_cast<const OT*>(sm + C::O_QH);
+    OT* sP = reinterpret_cast<OT*>(sm + C::O_P);
+    f32x4 aP = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kt = 0; kt < C::DK / 16; ++kt)
+        O::mma4(aP, frag_rows<O>(sQH + 16 * kt, C::SK, lane), frag_rows<O>(sKM + 16 * kt, C::SK, lane));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = 4 * q4 + j;
+        sP[r * C::S16 + l16] = O::to_op(l16 <= r ? aP[j] : 0.f);
+    }
+}
+
+// A' (strictly lower), T = (I + Diag(beta) A')^{-1} and, with need_p, P,
 // by one wave on the matrix cores.
 template <typename C, typename DT, bool FULL>
 __device__ __forceinline__ void bwd_small(unsigned char* sm, int lane, bool need_p)
@@ -442,7 +465,8 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, false>::NT)) bwd_chunk_sum
             const int n = int(L.t1 - t_s < BSUB ? L.t1 - t_s : BSUB);
             bwd_prep<C, DT, false>(a, sm, t_s, n, h, false);
             __syncthreads();
-            if (wave == 0) bwd_small<C, DT, false>(sm, fresh_lane(), true);
+            if (wave == 0) bwd_small<C, DT, false>(sm, fresh_lane(), false);
+            else if (wave == 1) bwd_small_p<C, DT>(sm, fresh_lane());
             __syncthreads();
             if (active) {
                 f32x4 dY[CT], dX[CT];
@@ -629,7 +653,8 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
                 float* dvb = a.dv + row0 * DV;
                 bwd_prep<C, DT, true>(a, sm, t_s, n, h, false);
                 __syncthreads();
-                if (wave == 0) bwd_small<C, DT, true>(sm, fresh_lane(), true);
+                if (wave == 0) bwd_small<C, DT, true>(sm, fresh_lane(), false);
+                else if (wave == 1) bwd_small_p<C, DT>(sm, fresh_lane());
                 __syncthreads();
                 if (chain) {
                     const int lane = fresh_lane(), l16 = lane & 15, q4 = lane >> 4;
