@@ -23,7 +23,11 @@
  * Conventions for every call:
  *   - All tensor arguments are DEVICE pointers (memory of the current HIP
  *     device), row-major, densely packed, owned by the caller.  The library
- *     allocates nothing and keeps no state between calls.
+ *     allocates no device memory.  It keeps one thing between calls: for a
+ *     long single-sequence prefill it runs the first segment on a second
+ *     stream beside the rest (the head split, kda_prefill), and that stream
+ *     and its two events are created once per host thread and device on
+ *     first use and kept until the process ends.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Calls only enqueue work and return; completion and asynchronous HIP
  *     faults are observed by the caller synchronising the stream.
@@ -122,7 +126,12 @@ size_t kda_prefill_workspace_size(int64_t T_total, int N, int H, int d_k, int d_
  *               not matter and are clobbered.
  * Chunks restart at every sequence start; the last chunk of a sequence may be
  * short.  Long sequences are split into segments that run in parallel and are
- * composed exactly through S_end = S~ + M S_in.
+ * composed exactly through S_end = S~ + M S_in.  One sequence without
+ * cu_seqlens whose segments leave compute units idle also runs its first
+ * tokens (the head) on a second stream, whose fork from and join back to
+ * `stream` are recorded with events; the call stays ordered on `stream`
+ * like any other (checkpoints, if any, must fall on the head's end, else the
+ * head is not split off).
  * Errors: KDA_ERR_INVALID_ARGUMENT (null required pointer, N < 1, T_total < 0,
  * N != 1 without cu_seqlens, forbidden aliasing), KDA_ERR_UNSUPPORTED (d_k,
  * d_v, chunk, H or dtype outside the supported set, T_total > 2^31 - 1:
