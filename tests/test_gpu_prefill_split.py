@@ -106,3 +106,61 @@ def test_split_in_place_state_and_gate(kda):
     g = oracle.gate(x["z"], x["A"])  # the fused gate keeps g in fp32
     o_ref, S_ref = reference(wl, x, g, S0)
     assert relerr(host(o), o_ref) < TOL["bf16"] and relerr(host(st), S_ref) < TOL["bf16"]
+
+
+def test_split_two_streams(kda):
+    """Two calls in flight on two user streams share the library's second
+    stream and events: each result equals the same call run alone."""
+    import torch
+    wl = synth.PREFILL_8K.with_(H=4, seqlens=(2048,), state_std=0.1)
+    announce("head split, two calls on two streams")
+    x, g, S0 = inputs(wl)
+    d = {n: dev(x[n], wl.dtype) for n in ("q", "k", "v", "beta")}
+    gd = dev(g, wl.dtype)
+    o_ref, S_ref = kda.kda_prefill(d["q"], d["k"], d["v"], gd, d["beta"], initial_state=dev(S0))
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for st in (s1, s2):
+        with torch.cuda.stream(st):
+            outs.append(kda.kda_prefill(d["q"], d["k"], d["v"], gd, d["beta"], initial_state=dev(S0),
+                                        stream=st))
+    torch.cuda.synchronize()
+    for o, S in outs:
+        assert torch.equal(o, o_ref) and torch.equal(S, S_ref)
+
+
+def test_split_graph_replay(kda):
+    """The split call captured into a HIP graph (the second stream joins the
+    capture through the fork and join events) and replayed three times, with
+    eager work and synchronisation between replays: every replay equals the
+    eager call."""
+    import torch
+    wl = synth.PREFILL_8K.with_(H=4, seqlens=(2048,), state_std=0.1)
+    announce("head split, graph capture and replay")
+    x, g, S0 = inputs(wl)
+    d = {n: dev(x[n], wl.dtype) for n in ("q", "k", "v", "beta")}
+    gd = dev(g, wl.dtype)
+    T, H = wl.T_total, wl.H
+    init = dev(S0)
+    o_ref, S_ref = kda.kda_prefill(d["q"], d["k"], d["v"], gd, d["beta"], initial_state=init)
+    o = torch.empty_like(o_ref)
+    S = torch.empty_like(S_ref)
+    ws = torch.empty(kda.lib().kda_prefill_workspace_size(T, 1, H, wl.dk, wl.dv, 64, 1), dtype=torch.uint8,
+                     device="cuda")
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):  # warm up on the capture stream (creates the library's second stream)
+        kda.kda_prefill(d["q"], d["k"], d["v"], gd, d["beta"], initial_state=init, final_state=S, o=o,
+                        workspace=ws, stream=st)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=st):
+        kda.kda_prefill(d["q"], d["k"], d["v"], gd, d["beta"], initial_state=init, final_state=S, o=o,
+                        workspace=ws, stream=st)
+    for _ in range(3):
+        o.zero_()
+        S.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref) and torch.equal(S, S_ref)
