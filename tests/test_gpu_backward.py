@@ -126,3 +126,64 @@ def test_backward_many_heads(kda):
     wl = synth.VARLEN_64.with_(H=64, dk=32, dv=32, dtype="f32", seqlens=(70, 130), state_std=0.1)
     announce("backward, 2 sequences x 64 heads")
     run_case(kda, wl, with_ckpt=True, heads=[0, 33, 63])
+
+
+def test_backward_varlen_64_full_size(kda):
+    """The ~1M-token varlen workload (64 sequences, H=32, bf16) through the
+    forward's interval-64 checkpoints and the backward: N*H = 2048 items, one
+    segment per sequence, every workgroup looping over items.  dO and the final
+    state's gradient are nonzero on the three shortest sequences only (the
+    oracle keeps every state of a sequence, so it takes short ones): their
+    gradients on three heads against the oracle, and another sequence's
+    gradients exactly zero (nothing leaks across sequences)."""
+    import torch
+    from tests.gpu_common import dev_stream
+    wl = synth.VARLEN_64
+    T, H, dk, dv = wl.T_total, wl.H, wl.dk, wl.dv
+    cu = wl.cu_seqlens
+    lens = np.asarray(wl.seqlens)
+    announce(f"backward varlen_64 full size: N={wl.N} H={H} T={T}")
+    xs = {n: dev_stream(wl, n, rows=1 << 14) for n in ("q", "k", "v", "z", "beta")}
+    g = kda.kda_gate(xs["z"], dev(synth.gate_A(wl)))
+    del xs["z"]
+    S0 = synth.initial_state(wl)
+    cud = torch.from_numpy(cu).cuda()
+    S0d = dev(S0)
+    _, _, ck = kda.kda_prefill_ckpt(xs["q"], xs["k"], xs["v"], g, xs["beta"], 64, cu_seqlens=cud,
+                                    cu_seqlens_host=cu, initial_state=S0d)
+    order = np.argsort(lens)
+    picked = [int(n) for n in order[:3]]
+    rng = np.random.default_rng(17)
+    dO = torch.zeros((T, H, dv), dtype=torch.bfloat16, device="cuda")
+    dS = torch.zeros((wl.N, H, dk, dv), dtype=torch.float32, device="cuda")
+    up = {}
+    for n in picked:
+        a, b = int(cu[n]), int(cu[n + 1])
+        do_n = oracle.round_bf16(rng.standard_normal((b - a, H, dv)).astype(np.float32)).astype(np.float32)
+        ds_n = rng.standard_normal((H, dk, dv)).astype(np.float32)
+        dO[a:b] = dev(do_n, "bf16")
+        dS[n] = dev(ds_n)
+        up[n] = (do_n, ds_n)
+    out = kda.kda_backward(xs["q"], xs["k"], xs["v"], g, xs["beta"], d_o=dO, d_final_state=dS, cu_seqlens=cud,
+                           initial_state=S0d, ckpt=ck)
+    torch.cuda.synchronize()
+    del ck
+    heads = [0, 13, 31]
+    for n in picked:
+        a, b = int(cu[n]), int(cu[n + 1])
+        x = {nm: synth.token_rows(wl, nm, a, b)[:, heads] for nm in ("q", "k", "v", "z", "beta")}
+        gh = oracle.gate(x["z"], synth.gate_A(wl)[heads], round_bf16=True)
+        do_n, ds_n = up[n]
+        ref = oracle.backward(x["q"], x["k"], x["v"], gh, x["beta"], dO=do_n[:, heads], dS_fin=ds_n[None, heads],
+                              S0=S0[n:n + 1][:, heads])
+        for gname, rname in GRADS:
+            got = host(out[gname][n:n + 1] if gname == "d_initial_state" else out[gname][a:b])[:, heads]
+            e = relerr(got, ref[rname])
+            print(f"  sequence {n} (len {b - a}) {gname}: {e:.3e}")
+            assert e < TOL["bf16"], f"sequence {n} {gname}: {e:.3e}"
+    quiet = int(order[-1])  # the longest sequence, whose upstream gradients are zero
+    a, b = int(cu[quiet]), int(cu[quiet + 1])
+    for gname, _ in GRADS:
+        t = out[gname][quiet] if gname == "d_initial_state" else out[gname][a:b]
+        assert torch.count_nonzero(t).item() == 0, f"{gname} leaks into sequence {quiet}"
+        assert torch.isfinite(out[gname]).all()
