@@ -91,7 +91,7 @@ __device__ inline SegLoc bwd_locate(const BackwardArgs& a, int seg)
 // segment s + 1, and dS_start(s) = M_s^T dS_end(s) + C_s, in fp32.  M_s^T is
 // staged in LDS (the next one is loaded into registers while the current
 // product runs); each thread owns DK/16 rows of one column.  Writes every
-// segment's dS_end for the full pass and the initial state's gradient.
+// segment's dS_end for the full pass.
 constexpr int BWD_SCAN_COLS = 16;
 template <int DK>
 struct BwdScanCfg {
@@ -136,7 +136,7 @@ __global__ void __launch_bounds__(256) bwd_scan_kernel(BackwardArgs a)
     // the last segment ends at the final state: its dS_end is the final state's gradient
     for (int r = rgp; r < DK; r += C::RG) {
         dsend_of(nseg - 1)[r * DV + col] = a.d_fin ? a.d_fin[unit * int64_t(DK) * DV + r * DV + col] : 0.f;
-        sd[r * SD + jj] = cm_of(nseg - 1)[r * DV + col];  // dS_start of the last segment
+        if (nseg > 1) sd[r * SD + jj] = cm_of(nseg - 1)[r * DV + col];  // dS_start of the last segment
     }
     f32x4 pre[C::NV];
     auto load_m = [&](int s) {
@@ -173,7 +173,7 @@ __global__ void __launch_bounds__(256) bwd_scan_kernel(BackwardArgs a)
         for (int i = 0; i < C::RPT; ++i) sd[(rgp * C::RPT + i) * SD + jj] = acc[i];
         __syncthreads();
     }
-    for (int r = rgp; r < DK; r += C::RG) a.d_init[unit * int64_t(DK) * DV + r * DV + col] = sd[r * SD + jj];
+    // (the initial state's gradient is the full pass's: its first segment ends there)
 }
 
 struct BwdPlan {

@@ -439,7 +439,9 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, false>::NT)) bwd_chunk_sum
     const int H = a.H;
     const int item = blockIdx.x, h = item % H;
     const SegLoc L = bwd_locate(a, item / H);
-    if (L.n < 0) return;
+    // a sequence of one segment needs no summary: the full pass gives its
+    // initial state's gradient directly
+    if (L.n < 0 || L.nseg == 1) return;
     const bool last = L.s == L.nseg - 1;
     constexpr int CT = C::CT, CW = 16 * CT;  // columns per wave
     const bool mcols = wave >= DV / CW;  // a wave of the N (identity) columns
@@ -581,6 +583,16 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
         __syncthreads();
         if (chain) fwd_update(S);
         __syncthreads();
+    };
+    auto store_tiles = [&](const f32x4 (&S)[NCT][CT], float* dst) {
+        const int lane = fresh_lane(), l16 = lane & 15, q4 = lane >> 4;
+#pragma unroll
+        for (int rt = 0; rt < NCT; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    dst[uint32_t((16 * rt + 4 * q4 + j) * DV + col0 + 16 * ct + l16)] = S[rt][ct][j];
     };
     auto load_tiles = [&](f32x4 (&S)[NCT][CT], const float* src) {
         const int lane = fresh_lane(), l16 = lane & 15, q4 = lane >> 4;
@@ -840,6 +852,8 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
                 __syncthreads();
             }
         }
+        // the first segment of a sequence ends at the initial state's gradient
+        if (L.s == 0 && chain) store_tiles(dS, a.d_init + unit * DK * DV);
     }
 }
 
