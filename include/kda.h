@@ -213,8 +213,8 @@ kda_status_t kda_prefill_gated(const void* q, const void* k, const void* v, cons
  *                    sequence length).
  *   workspace      : at least kda_backward_workspace_size(T_total, N, H, d_k,
  *                    d_v) bytes: per workgroup slot, the states at the four
- *                    16-token sub-chunk starts of a 64-token chunk and one
- *                    staging state; per (segment, head) the segment's
+ *                    16-token sub-chunk starts of a 64-token chunk (in up to
+ *                    two layouts) and one staging state; per (segment, head) the segment's
  *                    gradient summary and its incoming state gradient
  *                    (segments of a sequence run in parallel).
  * The products run on the matrix cores with operands in `dtype` (bf16
