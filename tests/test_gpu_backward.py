@@ -187,3 +187,36 @@ def test_backward_varlen_64_full_size(kda):
         t = out[gname][quiet] if gname == "d_initial_state" else out[gname][a:b]
         assert torch.count_nonzero(t).item() == 0, f"{gname} leaks into sequence {quiet}"
         assert torch.isfinite(out[gname]).all()
+
+
+@pytest.mark.parametrize("which", ["none", "final_only", "output_only"])
+def test_backward_optional_gradients(kda, which):
+    """d_o and d_final_state may be omitted (zero): with neither, every gradient
+    is exactly zero; with one, the result matches the oracle given zeros for
+    the other."""
+    import torch
+    wl = synth.VARLEN_64.with_(H=2, dk=64, dv=64, dtype="bf16", seqlens=(150, 300), state_std=0.1,
+                               z_shift=-2.0)
+    announce(f"backward with optional upstream gradients: {which}")
+    x = synth.prefill_inputs(wl)
+    g = oracle.round_bf16(oracle.gate(x["z"], x["A"]))
+    S0 = synth.initial_state(wl)
+    rng = np.random.default_rng(23)
+    dO = oracle.round_bf16(rng.standard_normal((wl.T_total, wl.H, wl.dv)).astype(np.float32)).astype(np.float32)
+    dS = rng.standard_normal((wl.N, wl.H, wl.dk, wl.dv)).astype(np.float32)
+    use_o, use_s = which == "output_only", which == "final_only"
+    d = {n: dev(x[n], "bf16") for n in ("q", "k", "v", "beta")}
+    out = kda.kda_backward(d["q"], d["k"], d["v"], dev(g, "bf16"), d["beta"],
+                           d_o=dev(dO, "bf16") if use_o else None, d_final_state=dev(dS) if use_s else None,
+                           cu_seqlens=torch.from_numpy(wl.cu_seqlens).cuda(), initial_state=dev(S0))
+    torch.cuda.synchronize()
+    if which == "none":
+        for gname, _ in GRADS:
+            assert torch.count_nonzero(out[gname]).item() == 0, gname
+        return
+    ref = oracle.backward(x["q"], x["k"], x["v"], g, x["beta"], dO=dO if use_o else np.zeros_like(dO),
+                          dS_fin=dS if use_s else np.zeros_like(dS), cu=wl.cu_seqlens, S0=S0)
+    for gname, rname in GRADS:
+        e = relerr(host(out[gname]), ref[rname])
+        print(f"  {gname}: {e:.3e}")
+        assert e < TOL["bf16"], f"{gname}: {e:.3e}"

@@ -49,6 +49,21 @@ def test_split_outputs(kda, T):
     assert eo < TOL["bf16"] and es < TOL["bf16"]
 
 
+def test_split_f32(kda):
+    """The fp32 prefill (d_k = 32) takes the split too."""
+    wl = synth.TINY_F32.with_(H=2, seqlens=(2048,), state_std=0.1)
+    announce("head split, fp32, d_k = d_v = 32")
+    x = synth.prefill_inputs(wl)
+    g = oracle.gate(x["z"], x["A"])
+    S0 = synth.initial_state(wl)
+    d = {n: dev(x[n], "f32") for n in ("q", "k", "v", "beta")}
+    o, S = kda.kda_prefill(d["q"], d["k"], d["v"], dev(g), d["beta"], initial_state=dev(S0))
+    o_ref, S_ref = reference(wl, x, g, S0)
+    eo, es = relerr(host(o), o_ref), relerr(host(S), S_ref)
+    print(f"  o {eo:.3e}  S {es:.3e}")
+    assert eo < TOL["f32"] and es < TOL["f32"]
+
+
 def test_split_matches_unsplit_run(kda):
     """The same call with the split switched off (a forced segment length)
     lands on the oracle too, and both agree to the bf16 bar."""
