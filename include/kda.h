@@ -23,11 +23,9 @@
  * Conventions for every call:
  *   - All tensor arguments are DEVICE pointers (memory of the current HIP
  *     device), row-major, densely packed, owned by the caller.  The library
- *     allocates no device memory.  It keeps one thing between calls: for a
- *     long single-sequence prefill it runs the first segment on a second
- *     stream beside the rest (the head split, kda_prefill), and that stream
- *     and its two events are created once per host thread and device on
- *     first use and kept until the process ends.
+ *     allocates no device memory, creates no streams or events and keeps no
+ *     state between calls: everything a call needs is in its arguments.
+ *     Everything a call enqueues goes onto `stream`, in order.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Calls only enqueue work and return; completion and asynchronous HIP
  *     faults are observed by the caller synchronising the stream.
@@ -78,7 +76,10 @@ int kda_version(void);
  *     g[t,h,c] = g_min * sigmoid(exp(A[h]) * z[t,h,c])
  * z, g : [n_tokens, H, d_k] in `dtype` (g may alias z: in-place is allowed).
  * A    : [H] fp32 device pointer.
- * g_min: the lower bound (the pages use -5); must be finite and < 0.
+ * g_min: the lower bound, in [-5, 0) (the pages use -5).  kda_prefill and
+ *        kda_backward need every g >= -5 (they factor decay ratios per
+ *        16-token sub-tile and keep each factor inside the fp32 range), so a
+ *        lower bound below -5 is refused.
  * Computed in fp32 and rounded once to dtype.  n_tokens == 0 is a no-op.
  * Errors: KDA_ERR_INVALID_ARGUMENT for null pointers / negative sizes / bad
  * g_min, KDA_ERR_UNSUPPORTED for an unknown dtype, KDA_ERR_HIP on launch failure.
@@ -125,13 +126,15 @@ size_t kda_prefill_workspace_size(int64_t T_total, int N, int H, int d_k, int d_
  *               (may be NULL when that size is 0); its contents on entry do
  *               not matter and are clobbered.
  * Chunks restart at every sequence start; the last chunk of a sequence may be
- * short.  Long sequences are split into segments that run in parallel and are
- * composed exactly through S_end = S~ + M S_in.  One sequence without
- * cu_seqlens whose segments leave compute units idle also runs its first
- * tokens (the head) on a second stream, whose fork from and join back to
- * `stream` are recorded with events; the call stays ordered on `stream`
- * like any other (checkpoints, if any, must fall on the head's end, else the
- * head is not split off).
+ * short.  Long sequences are split into segments that run in parallel.  For
+ * d_k <= d_v each segment takes its incoming state from the 128 tokens before
+ * it, run from a zero state beside their transition M: once the computed M is
+ * exactly zero (all its entries underflow, as they do within about a hundred
+ * tokens under the bounded decay) the incoming state is the window's state.
+ * Chains (sequence, head) where M is not zero, and every chain when d_k > d_v,
+ * are composed exactly through S_end = S~ + M S_in (summary pass, scan,
+ * output pass).  Both routes enqueue the same launches on `stream`; the second
+ * route's kernels end at once for chains that do not need them.
  * Errors: KDA_ERR_INVALID_ARGUMENT (null required pointer, N < 1, T_total < 0,
  * N != 1 without cu_seqlens, forbidden aliasing), KDA_ERR_UNSUPPORTED (d_k,
  * d_v, chunk, H or dtype outside the supported set, T_total > 2^31 - 1:
@@ -192,6 +195,34 @@ kda_status_t kda_prefill_gated(const void* q, const void* k, const void* v, cons
                                int H, int d_k, int d_v, int chunk, const float* initial_state, float* final_state,
                                void* o, kda_dtype_t dtype, void* workspace, size_t workspace_bytes,
                                int ckpt_interval, float* ckpt_states, int64_t ckpt_capacity, void* stream);
+
+/*
+ * TEST ONLY — the prefill with the planner's two choices given as arguments,
+ * so tests can force segment boundaries and either route (kda_prefill).
+ *   g_or_z, A   : with A NULL, g_or_z is the log-decay g (as kda_prefill);
+ *                 else it is the gate's input z (as kda_prefill_gated, with
+ *                 g_min in [-5, 0)).
+ *   seg_chunks  : segment length in 64-token chunks, or 0 for the planner's.
+ *   warm_tokens : the warm-up window before each segment, a positive multiple
+ *                 of 32 tokens; 0 = no warm-up (every chain through the
+ *                 summary pass, scan and output pass); -1 = the planner's.
+ * Other arguments as kda_prefill_gated; chunk is 64.  The workspace size for
+ * the same choices is kda_test_prefill_workspace_size (0 on bad arguments).
+ * kda_test_prefill_flags returns how many int32 warm-up flags ([segments][H],
+ * 1 = that segment's window left M non-zero, so its chain went through the
+ * exact passes) the workspace holds, and at *offset_bytes where; 0 without a
+ * warm-up pass, -1 on bad arguments.  Only rows of real segments are written.
+ */
+kda_status_t kda_test_prefill(const void* q, const void* k, const void* v, const void* g_or_z, const float* A,
+                              float g_min, const void* beta, const int32_t* cu_seqlens, int N, int64_t T_total,
+                              int H, int d_k, int d_v, const float* initial_state, float* final_state, void* o,
+                              kda_dtype_t dtype, void* workspace, size_t workspace_bytes, int ckpt_interval,
+                              float* ckpt_states, int64_t ckpt_capacity, int seg_chunks, int warm_tokens,
+                              void* stream);
+size_t kda_test_prefill_workspace_size(int64_t T_total, int N, int H, int d_k, int d_v, kda_dtype_t dtype,
+                                       int seg_chunks, int warm_tokens);
+int64_t kda_test_prefill_flags(int64_t T_total, int N, int H, int d_k, int d_v, kda_dtype_t dtype, int seg_chunks,
+                               int warm_tokens, size_t* offset_bytes);
 
 /*
  * kda_backward — gradients for training ([K3-notes] Model Architecture / KDA:

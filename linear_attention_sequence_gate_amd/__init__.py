@@ -20,7 +20,8 @@ _STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARGUMENT", 2: "KDA_ERR_UNSUPPORTED",
 EXPORTED = ("kda_status_string", "kda_last_error", "kda_version", "kda_gate",
             "kda_prefill_workspace_size", "kda_prefill", "kda_decode_step", "kda_verify", "kda_commit",
             "kda_prefill_ckpt", "kda_checkpoint_count", "kda_prefill_gated", "kda_decode_step_gated",
-            "kda_backward_workspace_size", "kda_backward")
+            "kda_backward_workspace_size", "kda_backward", "kda_test_prefill", "kda_test_prefill_workspace_size",
+            "kda_test_prefill_flags")
 
 _lib = None
 
@@ -70,6 +71,13 @@ def lib() -> ctypes.CDLL:
         L.kda_backward.argtypes = [P, P, P, P, P, P, I, I64, I, I, I, P, P, I64, P, P, P, P, P, P, P, P, I, P, SZ,
                                    P]
         L.kda_backward.restype = I
+        L.kda_test_prefill.argtypes = [P, P, P, P, P, F, P, P, I, I64, I, I, I, P, P, P, I, P, SZ, I, P, I64, I, I,
+                                       P]
+        L.kda_test_prefill.restype = I
+        L.kda_test_prefill_workspace_size.argtypes = [I64, I, I, I, I, I, I, I]
+        L.kda_test_prefill_workspace_size.restype = SZ
+        L.kda_test_prefill_flags.argtypes = [I64, I, I, I, I, I, I, I, ctypes.POINTER(SZ)]
+        L.kda_test_prefill_flags.restype = I64
         L.kda_checkpoint_count.argtypes = [P, I, I64, I]
         L.kda_checkpoint_count.restype = I64
         _lib = L
@@ -311,3 +319,57 @@ def kda_backward(q, k, v, g, beta, d_o=None, d_final_state=None, cu_seqlens=None
                               _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out["d_initial_state"]), _dtype_code(k),
                               _ptr(workspace), wbytes, _stream(stream)))
     return out
+
+
+def kda_test_prefill(q, k, v, g_or_z, beta, A=None, g_min: float = -5.0, cu_seqlens=None, initial_state=None,
+                     final_state=None, o=None, workspace=None, interval: int = 0, ckpt=None, cu_seqlens_host=None,
+                     seg_chunks: int = 0, warm_tokens: int = -1, stream=None):
+    """TEST ONLY: the prefill with the planner's choices made explicit (segment
+    length in chunks, 0 = the planner's; warm-up tokens, -1 = the planner's, 0 =
+    the exact summary / scan / output passes only).  With A, g_or_z holds the
+    gate's input z (as kda_prefill_gated); without, the log-decay g.  Returns
+    (o, final_state, ckpt or None, workspace)."""
+    import torch
+    _dense(q, k, v, g_or_z, A, beta, cu_seqlens, initial_state, final_state, o, ckpt, workspace)
+    T, H, dk = k.shape
+    dv = v.shape[2]
+    N = 1 if cu_seqlens is None else cu_seqlens.shape[0] - 1
+    code = _dtype_code(k)
+    if o is None:
+        o = torch.empty((T, H, dv), dtype=v.dtype, device=v.device)
+    if final_state is None:
+        final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=k.device)
+    if interval > 0 and ckpt is None:
+        if cu_seqlens is not None and cu_seqlens_host is None:
+            cu_seqlens_host = cu_seqlens.cpu().numpy()
+        n = kda_checkpoint_count(cu_seqlens_host, T, interval)
+        ckpt = torch.empty((max(n, 0), H, dk, dv), dtype=torch.float32, device=k.device)
+    need = int(lib().kda_test_prefill_workspace_size(T, N, H, dk, dv, code, seg_chunks, warm_tokens))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=k.device)
+    wbytes = workspace.numel() * workspace.element_size()
+    cap = 0 if ckpt is None else ckpt.shape[0]
+    _check(lib().kda_test_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(g_or_z), _ptr(A), float(g_min), _ptr(beta),
+                                  _ptr(cu_seqlens), N, T, H, dk, dv, _ptr(initial_state), _ptr(final_state),
+                                  _ptr(o), code, _ptr(workspace), wbytes, int(interval),
+                                  _ptr(ckpt) if cap else None, cap, int(seg_chunks), int(warm_tokens),
+                                  _stream(stream)))
+    return o, final_state, ckpt, workspace
+
+
+def test_prefill_flags(workspace, T_total: int, N: int, H: int, d_k: int, d_v: int, dtype: int = KDA_BF16,
+                       seg_chunks: int = 0, warm_tokens: int = -1):
+    """TEST ONLY: the warm-up flags [nseg_max, H] (int32, 1 = the segment's
+    warm-up left M non-zero) that a kda_test_prefill call with these choices left
+    in its workspace; rows past the real segment count are unspecified.  None
+    when the plan has no warm-up pass."""
+    import torch
+    off = ctypes.c_size_t(0)
+    n = int(lib().kda_test_prefill_flags(T_total, N, H, d_k, d_v, dtype, seg_chunks, warm_tokens,
+                                         ctypes.byref(off)))
+    if n < 0:
+        raise ValueError("bad arguments")
+    if n == 0:
+        return None
+    raw = workspace[off.value:off.value + 4 * n]
+    return raw.view(torch.int32).view(n // H, H)

@@ -81,8 +81,10 @@ kda_status_t kda_gate(const void* z, const float* A, void* g, int64_t n_tokens, 
         return fail(KDA_ERR_INVALID_ARGUMENT, "kda_gate: bad sizes n_tokens=%lld H=%d d_k=%d",
                     (long long)n_tokens, H, d_k);
     if (!dtype_ok(dtype)) return fail(KDA_ERR_UNSUPPORTED, "kda_gate: unknown dtype %d", (int)dtype);
-    if (!std::isfinite(g_min) || !(g_min < 0.f))
-        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_gate: g_min must be finite and negative");
+    // the prefill and the backward factor decay ratios per 16-token sub-tile
+    // and need g >= -5 to keep every factor inside the fp32 range
+    if (!std::isfinite(g_min) || !(g_min < 0.f) || g_min < -5.f)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_gate: g_min must lie in [-5, 0)");
     if (n_tokens == 0) return ok();
     if (!z || !A || !g) return fail(KDA_ERR_INVALID_ARGUMENT, "kda_gate: null pointer");
     const size_t bytes = size_t(n_tokens) * H * d_k * dsize(dtype);
@@ -252,52 +254,31 @@ kda_status_t kda_commit(const void* k, const void* v, const void* g, const void*
     return from_hip(e, "kda_commit launch");
 }
 
+// the shapes the block kernels are built for
+static bool prefill_shape_ok(int64_t T_total, int N, int H, int d_k, int d_v, int chunk, kda_dtype_t dtype)
+{
+    return T_total >= 0 && T_total <= int64_t(0x7fffffff) && N >= 1 && H >= 1 && H <= KDA_MAX_HEADS &&
+           dim_ok(d_k) && dim_ok(d_v) && chunk == 64 && dtype_ok(dtype) &&
+           !(dtype == KDA_F32 && (d_k != 32 || d_v > 64));
+}
+
 size_t kda_prefill_workspace_size(int64_t T_total, int N, int H, int d_k, int d_v, int chunk,
                                   kda_dtype_t dtype)
 {
-    if (T_total < 0 || T_total > int64_t(0x7fffffff) || N < 1 || H < 1 || H > KDA_MAX_HEADS || !dim_ok(d_k) ||
-        !dim_ok(d_v) || chunk != 64 ||
-        !dtype_ok(dtype) || (dtype == KDA_F32 && (d_k != 32 || d_v > 64)))
-        return 0;
-    return kda::prefill_workspace(T_total, N, H, d_k, d_v);
+    if (!prefill_shape_ok(T_total, N, H, d_k, d_v, chunk, dtype)) return 0;
+    return kda::prefill_plan(T_total, N, H, d_k, d_v).workspace_bytes;
 }
 
-// The second stream and the two events of the prefill's head split, one set
-// per host thread and device, created on first use and kept until the process
-// ends (default priority, non-blocking).
-struct SideStream {
-    hipStream_t st = nullptr;
-    hipEvent_t fork = nullptr, join = nullptr;
-};
-static SideStream* side_stream()
-{
-    thread_local SideStream cache[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
-    SideStream& c = cache[dev];
-    if (!c.st) {
-        hipStream_t st = nullptr;
-        hipEvent_t e0 = nullptr, e1 = nullptr;
-        if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) return nullptr;
-        if (hipEventCreateWithFlags(&e0, hipEventDisableTiming) != hipSuccess ||
-            hipEventCreateWithFlags(&e1, hipEventDisableTiming) != hipSuccess) {
-            if (e0) (void)hipEventDestroy(e0);
-            (void)hipStreamDestroy(st);
-            return nullptr;
-        }
-        c.st = st;
-        c.fork = e0;
-        c.join = e1;
-    }
-    return &c;
-}
-
+// force_L > 0 fixes the segment length in chunks; warm_req < 0 takes the
+// planner's warm-up, 0 turns it off, > 0 sets it (both only from the test
+// entry point)
 static kda_status_t prefill_impl(const char* who, const void* q, const void* k, const void* v, const void* g,
                                  const void* beta, const int32_t* cu_seqlens, int N, int64_t T_total, int H,
                                  int d_k, int d_v, int chunk, const float* initial_state, float* final_state,
                                  void* o, kda_dtype_t dtype, void* workspace, size_t workspace_bytes,
                                  int ckpt_interval, float* ckpt_states, int64_t ckpt_capacity, void* stream,
-                                 const float* gate_A = nullptr, float g_min = -5.f)
+                                 const float* gate_A = nullptr, float g_min = -5.f, int force_L = 0,
+                                 int warm_req = -1)
 {
     if (N < 1 || T_total < 0 || H < 1)
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: bad sizes N=%d T_total=%lld H=%d", who, N,
@@ -323,11 +304,12 @@ static kda_status_t prefill_impl(const char* who, const void* q, const void* k, 
         const size_t na = size_t(H) * sizeof(float);
         if (overlap(o, size_t(T_total) * H * d_v * dsize(dtype), gate_A, na) ||
             overlap(final_state, final_state ? size_t(N) * H * d_k * d_v * sizeof(float) : 0, gate_A, na) ||
-            overlap(workspace, kda::prefill_workspace(T_total, N, H, d_k, d_v), gate_A, na))
+            overlap(workspace, kda::prefill_plan(T_total, N, H, d_k, d_v, force_L, warm_req).workspace_bytes,
+                    gate_A, na))
             return fail(KDA_ERR_INVALID_ARGUMENT, "%s: A overlaps an output buffer", who);
     }
-    const kda::PrefillPlan plan = kda::prefill_plan(T_total, N, H, d_k, d_v);
-    const size_t ws_need = kda::prefill_workspace(T_total, N, H, d_k, d_v);
+    const kda::PrefillPlan plan = kda::prefill_plan(T_total, N, H, d_k, d_v, force_L, warm_req);
+    const size_t ws_need = plan.workspace_bytes;
     if (ws_need > 0 && (!workspace || workspace_bytes < ws_need))
         return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes < %zu needed", who,
                     workspace_bytes, ws_need);
@@ -384,45 +366,8 @@ static kda_status_t prefill_impl(const char* who, const void* q, const void* k, 
     }
     a.gate_A = gate_A;
     a.g_min = g_min;
-    auto launch = [&](const kda::PrefillArgs& x, const kda::PrefillPlan& p, hipStream_t st) {
-        return dtype == KDA_BF16 ? kda::launch_prefill<kda::BF16>(x, p, st) : kda::launch_prefill<kda::F32>(x, p, st);
-    };
-    // the head split (one sequence given without cu_seqlens; checkpoints, if
-    // any, must fall on the head's end)
-    const kda::PrefillSplit sp = kda::prefill_split(T_total, N, H, d_k, d_v);
-    SideStream* ss = nullptr;
-    if (sp.on && !cu_seqlens && (a.ckpt_interval == 0 || sp.head % a.ckpt_interval == 0)) ss = side_stream();
-    if (!ss) return from_hip(launch(a, plan, s), "kda_prefill launch");
-
-    const kda::PrefillPlan tplan = kda::prefill_plan(T_total - sp.head, 1, H, d_k, d_v, sp.tail_L);
-    float* head_fin = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) +
-                                               kda::align256(tplan.workspace_bytes));
-    kda::PrefillArgs hd = a;  // the head: its output pass only, state in -> head_fin
-    hd.T_total = sp.head;
-    hd.fin = head_fin;
-    const kda::PrefillPlan hplan = kda::prefill_plan(sp.head, 1, H, d_k, d_v);
-    kda::PrefillArgs tl = a;  // the rest, from the head's final state
-    const size_t ek = size_t(sp.head) * H * d_k * es, ev = size_t(sp.head) * H * d_v * es;
-    tl.q = static_cast<const char*>(q) + ek;
-    tl.k = static_cast<const char*>(k) + ek;
-    tl.g = static_cast<const char*>(g) + ek;
-    tl.v = static_cast<const char*>(v) + ev;
-    tl.beta = static_cast<const char*>(beta) + size_t(sp.head) * H * es;
-    tl.o = static_cast<char*>(o) + ev;
-    tl.T_total = T_total - sp.head;
-    tl.init = head_fin;
-    tl.join = ss->join;
-    if (a.ckpt) {
-        const int64_t hrows = sp.head / a.ckpt_interval;
-        tl.ckpt = a.ckpt_cap > hrows ? a.ckpt + hrows * int64_t(H) * d_k * d_v : nullptr;
-        tl.ckpt_cap = a.ckpt_cap > hrows ? a.ckpt_cap - hrows : 0;
-        if (!tl.ckpt) tl.ckpt_interval = 0;
-    }
-    hipError_t e = hipEventRecord(ss->fork, s);
-    if (e == hipSuccess) e = hipStreamWaitEvent(ss->st, ss->fork, 0);
-    if (e == hipSuccess) e = launch(hd, hplan, ss->st);
-    if (e == hipSuccess) e = hipEventRecord(ss->join, ss->st);
-    if (e == hipSuccess) e = launch(tl, tplan, s);
+    const hipError_t e = dtype == KDA_BF16 ? kda::launch_prefill<kda::BF16>(a, plan, s)
+                                           : kda::launch_prefill<kda::F32>(a, plan, s);
     return from_hip(e, "kda_prefill launch");
 }
 
@@ -467,6 +412,49 @@ kda_status_t kda_prefill_gated(const void* q, const void* k, const void* v, cons
     return prefill_impl("kda_prefill_gated", q, k, v, z, beta, cu_seqlens, N, T_total, H, d_k, d_v, chunk,
                         initial_state, final_state, o, dtype, workspace, workspace_bytes, ckpt_interval,
                         ckpt_states, ckpt_capacity, stream, T_total > 0 ? A : nullptr, g_min);
+}
+
+// ---- test-only entry points: the planner's choices made explicit
+static bool test_plan_ok(int seg_chunks, int warm_tokens)
+{
+    return seg_chunks >= 0 && (warm_tokens == -1 || (warm_tokens >= 0 && warm_tokens % kda::BC == 0));
+}
+
+size_t kda_test_prefill_workspace_size(int64_t T_total, int N, int H, int d_k, int d_v, kda_dtype_t dtype,
+                                       int seg_chunks, int warm_tokens)
+{
+    if (!prefill_shape_ok(T_total, N, H, d_k, d_v, 64, dtype) || !test_plan_ok(seg_chunks, warm_tokens)) return 0;
+    return kda::prefill_plan(T_total, N, H, d_k, d_v, seg_chunks, warm_tokens).workspace_bytes;
+}
+
+int64_t kda_test_prefill_flags(int64_t T_total, int N, int H, int d_k, int d_v, kda_dtype_t dtype, int seg_chunks,
+                               int warm_tokens, size_t* offset_bytes)
+{
+    if (!prefill_shape_ok(T_total, N, H, d_k, d_v, 64, dtype) || !test_plan_ok(seg_chunks, warm_tokens) ||
+        !offset_bytes)
+        return -1;
+    const kda::PrefillPlan p = kda::prefill_plan(T_total, N, H, d_k, d_v, seg_chunks, warm_tokens);
+    *offset_bytes = p.off_flags;
+    return p.warm > 0 ? p.nseg_max * H : 0;
+}
+
+kda_status_t kda_test_prefill(const void* q, const void* k, const void* v, const void* g_or_z, const float* A,
+                              float g_min, const void* beta, const int32_t* cu_seqlens, int N, int64_t T_total,
+                              int H, int d_k, int d_v, const float* initial_state, float* final_state, void* o,
+                              kda_dtype_t dtype, void* workspace, size_t workspace_bytes, int ckpt_interval,
+                              float* ckpt_states, int64_t ckpt_capacity, int seg_chunks, int warm_tokens,
+                              void* stream)
+{
+    if (!test_plan_ok(seg_chunks, warm_tokens))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_test_prefill: seg_chunks=%d warm_tokens=%d", seg_chunks,
+                    warm_tokens);
+    if (ckpt_interval < 0 || ckpt_capacity < 0)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_test_prefill: negative checkpoint interval or capacity");
+    if (A && (!std::isfinite(g_min) || !(g_min < 0.f) || g_min < -5.f))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_test_prefill: g_min must lie in [-5, 0)");
+    return prefill_impl("kda_test_prefill", q, k, v, g_or_z, beta, cu_seqlens, N, T_total, H, d_k, d_v, 64,
+                        initial_state, final_state, o, dtype, workspace, workspace_bytes, ckpt_interval, ckpt_states,
+                        ckpt_capacity, stream, T_total > 0 ? A : nullptr, g_min, seg_chunks, warm_tokens);
 }
 
 size_t kda_backward_workspace_size(int64_t T_total, int N, int H, int d_k, int d_v)

@@ -45,7 +45,7 @@
 #pragma once
 
 #include <cmath>
-#include <cstdlib>
+#include <type_traits>
 
 #include "kda_common.hpp"
 
@@ -88,30 +88,62 @@ constexpr int CH = 64;  // tokens per chunk
 constexpr int NCU_TARGET = 256;
 
 // ---------------------------------------------------------------- host plan
+// A long sequence is cut into segments of L chunks that run in parallel.  Two
+// ways give each segment its incoming state:
+//   warm-up (the default where d_k <= d_v): the workgroup of segment s > 0
+//     first runs the `warm` tokens before the segment from a zero state,
+//     carrying the window's transition M beside the state ([S~ | M], M's
+//     columns start at I and see no v).  The incoming state is M S(window
+//     start) + S~; when the computed M is exactly zero (every entry has
+//     underflowed, as it does within about a hundred tokens of the decay the
+//     gate's bound produces) it is S~, and the segment runs on.  A window that
+//     reaches the sequence start begins from the initial state instead and
+//     needs no check.  A segment whose M is not zero flags its (sequence,
+//     head), and the exact passes below then run for every flagged chain.
+//   exact passes: a summary pass computes every non-final segment's [S~ | M]
+//     over the whole segment, a scan composes S_in(s+1) = M_s S_in(s) + S~_s,
+//     and an output pass reruns every segment from its true incoming state.
 struct PrefillPlan {
     int seg_chunks = 1;        // chunks per segment (L)
+    int warm = 0;              // warm-up tokens (a multiple of the 32-token block); 0: exact passes only
     int64_t nseg_max = 0;      // upper bound on the number of segments
     int64_t np1_max = 0;       // upper bound on the number of non-final segments
-    size_t off_table = 0, off_ms = 0, off_sin = 0;
+    size_t off_table = 0, off_flags = 0, off_ms = 0, off_sin = 0;
     size_t workspace_bytes = 0;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// force_L > 0 fixes the segment length (in chunks) instead of choosing it.
-inline PrefillPlan prefill_plan(int64_t T_total, int N, int H, int dk, int dv, int force_L = 0)
+constexpr int WARM_DEFAULT = 128;  // tokens
+
+// Whether the warm-up kernel exists for this head shape: its chain waves own
+// 16 state columns each and, during the warm-up, one 16-column tile of M
+// beside them, so M's d_k columns must fit in d_v / 16 tiles.
+constexpr bool warm_shape(int dk, int dv) { return dk <= dv; }
+
+// force_L > 0 fixes the segment length (in chunks); warm_req < 0 takes the
+// default warm-up, 0 turns it off, > 0 sets it (a multiple of 32 tokens).
+inline PrefillPlan prefill_plan(int64_t T_total, int N, int H, int dk, int dv, int force_L = 0, int warm_req = -1)
 {
     PrefillPlan p;
+    p.warm = warm_req < 0 ? WARM_DEFAULT : warm_req;
+    if (!warm_shape(dk, dv)) p.warm = 0;
     const int64_t chunks_bound = (T_total + CH - 1) / CH + N;  // >= total chunks over sequences
-    int64_t per_cu = (int64_t(H) * chunks_bound + NCU_TARGET - 1) / NCU_TARGET;
-    int64_t L = per_cu / 2;
-    if (L < 16) L = 16;
-    if (const char* e = getenv("KDA_SEG_CHUNKS")) {
-        const long v = atol(e);
-        if (v > 0) L = v;
-    }
-    if (force_L > 0) L = force_L;
     const int64_t max_seq_chunks = (T_total + CH - 1) / CH;
+    const int64_t per_cu = (int64_t(H) * chunks_bound + NCU_TARGET - 1) / NCU_TARGET;
+    int64_t L;
+    if (p.warm > 0 && N == 1) {
+        // one (segment, head) item per compute unit: a segment costs its own
+        // blocks plus a short warm-up, so fewer, longer segments waste least
+        const int64_t nseg = NCU_TARGET / H > 1 ? NCU_TARGET / H : 1;
+        L = (max_seq_chunks + nseg - 1) / nseg;
+    } else if (p.warm > 0) {
+        L = per_cu / 4;  // several items per unit: long sequences do not end last
+    } else {
+        L = per_cu / 2;  // the summary and output passes each fill the units once
+    }
+    if (L < 16) L = 16;
+    if (force_L > 0) L = force_L;
     if (L >= max_seq_chunks) L = max_seq_chunks > 0 ? max_seq_chunks : 1;  // nothing splits
     p.seg_chunks = int(L);
     p.nseg_max = chunks_bound / L + N + 1;
@@ -119,6 +151,10 @@ inline PrefillPlan prefill_plan(int64_t T_total, int N, int H, int dk, int dv, i
     size_t off = 0;
     p.off_table = off;
     off = align256(off + sizeof(int32_t) * 4 * size_t(N + 1));
+    if (p.warm > 0) {
+        p.off_flags = off;
+        off = align256(off + sizeof(int32_t) * size_t(p.nseg_max) * H);
+    }
     if (p.np1_max > 0) {
         p.off_ms = off;
         off = align256(off + sizeof(float) * size_t(p.np1_max) * H * dk * (dk + dv));
@@ -127,52 +163,6 @@ inline PrefillPlan prefill_plan(int64_t T_total, int N, int H, int dk, int dv, i
     }
     p.workspace_bytes = off;
     return p;
-}
-
-// Head split of one long sequence.  Pass 1 leaves the compute units of the
-// final segments' heads idle, and the first segment's incoming state is
-// known before anything runs.  So the first `head` tokens run as a prefill of
-// their own (its output pass only) on a second stream while pass 1 of the
-// rest runs, and the rest's scan starts from the head's final state.  The
-// rest is cut into the same number of segments, each a little shorter; the
-// head is at most 0.84 of a segment, about the ratio of a summary pass's
-// time per block to an output pass's, so it ends before pass 1 does.  Used
-// when the rest's (segment, head) items still fit the compute units once.
-struct PrefillSplit {
-    bool on = false;
-    int64_t head = 0;  // tokens of the head (whole chunks)
-    int tail_L = 0;    // chunks per segment of the rest
-};
-
-inline PrefillSplit prefill_split(int64_t T_total, int N, int H, int dk, int dv)
-{
-    PrefillSplit sp;
-    if (N != 1 || getenv("KDA_SEG_CHUNKS")) return sp;
-    const PrefillPlan p = prefill_plan(T_total, 1, H, dk, dv);
-    const int64_t chunks = (T_total + CH - 1) / CH;
-    const int64_t nseg = (chunks + p.seg_chunks - 1) / p.seg_chunks;
-    if (nseg < 2 || nseg * H > NCU_TARGET) return sp;
-    const int64_t Lt = int64_t(std::ceil(double(chunks) / (double(nseg) + 0.84)));
-    const int64_t L0 = chunks - nseg * Lt;
-    if (L0 < 1 || L0 > Lt) return sp;
-    sp.on = true;
-    sp.head = L0 * CH;
-    sp.tail_L = int(Lt);
-    return sp;
-}
-
-// Workspace for a prefill call: its plan's, or, with the head split, the
-// rest's plan and the head's final state (fp32 [H][dk][dv]).
-inline size_t prefill_workspace(int64_t T_total, int N, int H, int dk, int dv)
-{
-    size_t ws = prefill_plan(T_total, N, H, dk, dv).workspace_bytes;
-    const PrefillSplit sp = prefill_split(T_total, N, H, dk, dv);
-    if (sp.on) {
-        const size_t t = align256(prefill_plan(T_total - sp.head, 1, H, dk, dv, sp.tail_L).workspace_bytes) +
-                         align256(size_t(H) * dk * dv * sizeof(float));
-        ws = ws > t ? ws : t;
-    }
-    return ws;
 }
 
 struct PrefillArgs {
@@ -190,7 +180,6 @@ struct PrefillArgs {
     int64_t ckpt_cap = 0;   // checkpoints the buffer holds
     const float* gate_A = nullptr;  // non-null: g holds the gate's input z, and g = g_min sigmoid(e^{A_h} z)
     float g_min = -5.f;
-    hipEvent_t join = nullptr;  // non-null: the launches that read the incoming state wait for it
 };
 
 // Device-side view shared by the prefill kernels.
@@ -217,6 +206,8 @@ struct PrefillDev {
     int single_nck;
     const float* gate_A;  // non-null: the gate is applied to g (which holds z) in the decay stage
     float g_min;
+    int32_t* flags;  // [nseg_max][H]: 1 where a segment's warm-up left M non-zero; null: no warm-up pass
+    int warm;        // warm-up tokens
 };
 
 // Table entries (cu_seqlens clamped, segment, pass-1 and checkpoint offsets)
@@ -521,13 +512,22 @@ __device__ __forceinline__ typename Op<DT>::Frag acc_frag(const f32x4& lo, const
 // buffered (q.e^G, K-hat^T, e^{G_last}, beta).
 constexpr int BC = 32;
 
-template <typename DT, int DKV, int DVV, bool SUMMARY>
+// The three passes of the block kernel: the output pass (from a known
+// incoming state), the summary pass ([S~ | M] of a segment) and the warm-up
+// output pass (incoming state from a warm-up window, see the plan above).
+enum { MODE_OUT = 0, MODE_SUMMARY = 1, MODE_WARM = 2 };
+
+template <typename DT, int DKV, int DVV, int MODE>
 struct BlockCfg {
+    static constexpr bool SUMMARY = MODE == MODE_SUMMARY;
+    static constexpr bool WARM = MODE == MODE_WARM;
     static constexpr int DK = DKV, DV = DVV;
     static constexpr int NCOL = SUMMARY ? DV + DK : DV;  // extended state columns
     // state columns per chain wave (64 was measured slower for the summary
-    // pass: the chain's vector work, not its LDS reads, competes with the prep)
-    static constexpr int CW = 32;
+    // pass: the chain's vector work, not its LDS reads, competes with the
+    // prep).  The warm-up pass holds 16 state columns per wave, plus one
+    // 16-column tile of M during the warm-up: 16 waves fit at four per SIMD.
+    static constexpr int CW = WARM ? 16 : 32;
     static constexpr int NCT = CW / 16;                   // 16-wide column tiles per chain wave
     static constexpr int NCW = NCOL / CW;                 // chain waves
     // prep waves: two per SIMD for heads with d_k >= 64 (their vector work,
@@ -565,7 +565,8 @@ struct BlockCfg {
     static constexpr int O_D = O_P + (SUMMARY ? 0 : TILE_S);        // (I + A_aa)^{-1}, 2 blocks
     static constexpr int O_VEC = O_D + 2 * TILE_D;                  // fp32 channel vectors
     static constexpr int O_B = O_VEC + 3 * DK * 4;                  // beta, 2 buffers
-    static constexpr int LDS_TILES = O_B + 2 * BC * 4;
+    static constexpr int O_FLAG = O_B + 2 * BC * 4;                 // warm-up: one word per chain wave (M non-zero)
+    static constexpr int LDS_TILES = O_FLAG + (WARM ? 4 * ((NCW + 3) / 4 * 4) : 0);
     // summary pass, after the last block: each M-column wave stages its 32
     // columns (fp32, rows padded to 36) to write M split and permuted
     static constexpr int MSTAGE = 36;
@@ -576,7 +577,8 @@ struct BlockCfg {
     static constexpr int UPR_V = DV / EPU;
     static constexpr int U_V = BC * UPR_V;
     static constexpr int UPT_V = (U_V + NPT - 1) / NPT;
-    static_assert(NCOL % 32 == 0 && NCW >= 1, "state columns come in blocks of 32");
+    static_assert(NCOL % CW == 0 && NCW >= 1, "state columns come in whole chain-wave blocks");
+    static_assert(!WARM || DK <= DV, "the warm-up holds one tile of M per chain wave");
     static_assert(LDS <= 160 * 1024, "LDS budget exceeded");
     static_assert(PARTS >= 2 && BC % PARTS == 0 && CP * PARTS == NPT, "bad elementwise split");
     static_assert(16 % TPT == 0, "a token run stays inside one sub-tile");
@@ -936,11 +938,82 @@ __device__ __forceinline__ void prep_products(unsigned char* smem, int buf, int 
     }
 }
 
+// Whether any segment of the chain (sequence n, head h) left its warm-up's M
+// non-zero: the exact passes that follow a warm-up pass run only for those
+// chains.  Every thread reads the same words, so the answer is uniform.
+__device__ __forceinline__ bool chain_flagged(const PrefillDev& p, int seg0, int nseg, int h)
+{
+    for (int j = 0; j < nseg; ++j)
+        if (p.flags[int64_t(seg0 + j) * p.H + h] != 0) return true;
+    return false;
+}
+
+// The warm-up decision of a workgroup: the chain waves' words in LDS (written
+// before the barrier that ends the last warm-up block).
+template <typename C>
+__device__ __forceinline__ bool warm_failed(const unsigned char* smem)
+{
+    const int32_t* f = reinterpret_cast<const int32_t*>(smem + C::O_FLAG);
+    int32_t any = 0;
+#pragma unroll
+    for (int w = 0; w < C::NCW; ++w) any |= f[w];
+    return any != 0;
+}
+
+// The prep waves' loop: one barrier after the prologue, two per block (see
+// above).  Block bi covers tokens [blk0 + bi BC, ...) clipped at t_end.  After
+// the second barrier of block check_bi (when >= 0) the role ends early if the
+// warm-up flags are set; the chain waves take the same decision there.
+template <typename C, typename DT>
+__device__ __forceinline__ void prep_role(const PrefillDev& p, unsigned char* smem, int64_t blk0, int64_t t_end,
+                                          int64_t nblk, int h, int tid, int wave, int lane, int64_t check_bi,
+                                          PhaseClock& pclk)
+{
+    constexpr bool SUMMARY = C::SUMMARY;
+    const int pw = wave - C::NCW;
+    const int ptid = tid - 64 * C::NCW;
+    const int part = lane / C::CPW;
+    const int cpair = pw * C::CPW + lane % C::CPW;
+    const int tok0 = part * C::TPT;
+    auto blen = [&](int64_t bi) {
+        const int64_t b0 = blk0 + bi * BC;
+        return int(t_end - b0 < BC ? t_end - b0 : BC);
+    };
+    // with the fused gate, g comes from z here; every pass applies it to the
+    // same z and gets the same g
+    const GateZ gz = GateZ::of_head(p.gate_A, h, p.g_min);
+    PrepRegs<C, DT> pr;
+    if (nblk > 0) {
+        prep_load<C, DT, SUMMARY>(pr, p, blk0, blen(0), h, ptid, cpair, tok0);
+        prep_tiles<C, DT, SUMMARY>(pr, smem, 0, blen(0), lane, ptid, cpair, part, tok0, gz, pclk);
+        if (nblk > 1) prep_load<C, DT, SUMMARY>(pr, p, blk0 + BC, blen(1), h, ptid, cpair, tok0);
+    }
+    __syncthreads();
+    KDA_PHASE(4);
+    for (int64_t bi = 0; bi < nblk; ++bi) {
+        const int buf = int(bi & 1);
+        prep_products<C, DT, SUMMARY>(smem, buf, pw, lane);  // alpha: block bi
+        KDA_PHASE(0);
+        __syncthreads();
+        KDA_PHASE(1);
+        if (bi + 1 < nblk) {  // beta: tiles of block bi+1, loads of block bi+2
+            prep_tiles<C, DT, SUMMARY>(pr, smem, buf ^ 1, blen(bi + 1), lane, ptid, cpair, part, tok0, gz, pclk);
+            KDA_PHASE(10);
+            if (bi + 2 < nblk)
+                prep_load<C, DT, SUMMARY>(pr, p, blk0 + (bi + 2) * BC, blen(bi + 2), h, ptid, cpair, tok0);
+        }
+        KDA_PHASE(2);
+        __syncthreads();
+        KDA_PHASE(3);
+        if (bi == check_bi && warm_failed<C>(smem)) return;
+    }
+}
+
 template <typename DT, int DK, int DV, bool SUMMARY>
-__global__ void __launch_bounds__((BlockCfg<DT, DK, DV, SUMMARY>::NT))
+__global__ void __launch_bounds__((BlockCfg<DT, DK, DV, SUMMARY ? MODE_SUMMARY : MODE_OUT>::NT))
 prefill_block_kernel(PrefillDev p)
 {
-    using C = BlockCfg<DT, DK, DV, SUMMARY>;
+    using C = BlockCfg<DT, DK, DV, SUMMARY ? MODE_SUMMARY : MODE_OUT>;
     using O = Op<DT>;
     using OT = typename O::T;
     using Frag = typename O::Frag;
@@ -975,6 +1048,8 @@ prefill_block_kernel(PrefillDev p)
     const int s = item - off(n);
     const int seg0 = tab_seg(p, n);
     const int nseg = tab_seg(p, n + 1) - seg0;
+    // after a warm-up pass only the chains it flagged run again
+    if (p.flags && !chain_flagged(p, seg0, nseg, h)) return;
     const int64_t seq0 = tab_cu(p, n), seq1 = tab_cu(p, n + 1);
     const int64_t t_begin = seq0 + int64_t(s) * p.L * CH;
     int64_t t_end = t_begin + int64_t(p.L) * CH;
@@ -1000,40 +1075,7 @@ prefill_block_kernel(PrefillDev p)
     // The two roles run separate loops with the same barrier sequence (one
     // after the prologue, two per block), so their registers never overlap.
     if (wave >= C::NCW) {
-        // ================= prep waves
-        const int pw = wave - C::NCW;
-        const int ptid = tid - 64 * C::NCW;
-        const int part = lane / C::CPW;
-        const int cpair = pw * C::CPW + lane % C::CPW;
-        const int tok0 = part * C::TPT;
-        // with the fused gate, g comes from z here; both passes apply it to
-        // the same z and get the same g
-        const GateZ gz = GateZ::of_head(p.gate_A, h, p.g_min);
-        PrepRegs<C, DT> pr;
-        if (nblk > 0) {
-            prep_load<C, DT, SUMMARY>(pr, p, t_begin, blen(0), h, ptid, cpair, tok0);
-            prep_tiles<C, DT, SUMMARY>(pr, smem, 0, blen(0), lane, ptid, cpair, part, tok0, gz, pclk);
-            if (nblk > 1) prep_load<C, DT, SUMMARY>(pr, p, t_begin + BC, blen(1), h, ptid, cpair, tok0);
-        }
-        __syncthreads();
-        KDA_PHASE(4);
-        for (int64_t bi = 0; bi < nblk; ++bi) {
-            const int buf = int(bi & 1);
-            prep_products<C, DT, SUMMARY>(smem, buf, pw, lane);  // alpha: block bi
-            KDA_PHASE(0);
-            __syncthreads();
-            KDA_PHASE(1);
-            if (bi + 1 < nblk) {  // beta: tiles of block bi+1, loads of block bi+2
-                prep_tiles<C, DT, SUMMARY>(pr, smem, buf ^ 1, blen(bi + 1), lane, ptid, cpair, part, tok0, gz,
-                                           pclk);
-                KDA_PHASE(10);
-                if (bi + 2 < nblk)
-                    prep_load<C, DT, SUMMARY>(pr, p, t_begin + (bi + 2) * BC, blen(bi + 2), h, ptid, cpair, tok0);
-            }
-            KDA_PHASE(2);
-            __syncthreads();
-            KDA_PHASE(3);
-        }
+        prep_role<C, DT>(p, smem, t_begin, t_end, nblk, h, tid, wave, lane, -1, pclk);
         pclk.save(SUMMARY ? 8192 : 0);
         return;
     }
@@ -1339,6 +1381,7 @@ __global__ void __launch_bounds__(256) scan_kernel(PrefillDev p)
     const int n = unit / H;
     const int nseg = tab_seg(p, n + 1) - tab_seg(p, n);
     if (nseg <= 1) return;
+    if (p.flags && !chain_flagged(p, tab_seg(p, n), nseg, h)) return;  // after a warm-up pass: flagged chains only
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, q4 = lane >> 4;
     const int col0 = jb * SCAN_COLS;
@@ -1457,6 +1500,269 @@ __global__ void __launch_bounds__(256) scan_kernel(PrefillDev p)
     pclk.save(12288);
 }
 
+// ------------------------------------------------------- warm-up kernel
+// One workgroup per (segment, head), as the output pass, but segment s > 0
+// first runs the `warm` tokens before it (the plan above): chain wave w owns
+// state columns 16w..16w+15 and, during the warm-up, columns 16w..16w+15 of
+// the window's transition M as a second tile (M's columns start at I and see
+// no v, so X = -(K.e^G) M for them).  A wave whose M tile has become exactly
+// zero stops updating it (a zero tile stays zero).  After the window each
+// wave writes whether its M tile is still non-zero; the next barrier makes the
+// decision uniform: on zero the state is the warm-up's S~ and the segment runs
+// on, else the workgroup flags its (segment, head) and ends, and the exact
+// passes redo that chain.  A window that reaches the sequence start runs from
+// the initial state and needs no check.  Warm-up blocks write no outputs and
+// no checkpoints: those tokens belong to the previous segment.
+template <typename DT, int DK, int DV>
+__global__ void __launch_bounds__((BlockCfg<DT, DK, DV, MODE_WARM>::NT))
+prefill_warm_kernel(PrefillDev p)
+{
+    using C = BlockCfg<DT, DK, DV, MODE_WARM>;
+    using O = Op<DT>;
+    using OT = typename O::T;
+    using Frag = typename O::Frag;
+    using Frag4 = typename O::Frag4;
+    using ST = typename DT::storage;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    const OT* sKG = reinterpret_cast<const OT*>(smem + C::O_KG);
+    const OT* sV = reinterpret_cast<const OT*>(smem + C::O_V);
+    const OT* sA = reinterpret_cast<const OT*>(smem + C::O_A);
+    OT* sP = reinterpret_cast<OT*>(smem + C::O_P);
+    const OT* sD = reinterpret_cast<const OT*>(smem + C::O_D);
+    const float* sVec = reinterpret_cast<const float*>(smem + C::O_VEC);
+    int32_t* sFlag = reinterpret_cast<int32_t*>(smem + C::O_FLAG);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int l16 = lane & 15;
+    const int q4 = lane >> 4;
+    PhaseClock pclk;
+#ifdef KDA_PHASE_TIMING
+    pclk.on = tid == KDA_PHASE_TID;
+    pclk.last = clock64();
+#endif
+
+    // ---- work item
+    const int H = p.H;
+    const int item = blockIdx.x / H;
+    const int h = blockIdx.x % H;
+    if (item >= tab_seg(p, p.N)) return;
+    const int n = p.single ? 0 : find_seq(p.tab + (p.N + 1), p.N, item);
+    const int seg0 = tab_seg(p, n);
+    const int s = item - seg0;
+    const int nseg = tab_seg(p, n + 1) - seg0;
+    const int64_t seq0 = tab_cu(p, n), seq1 = tab_cu(p, n + 1);
+    const int64_t t_begin = seq0 + int64_t(s) * p.L * CH;
+    int64_t t_end = t_begin + int64_t(p.L) * CH;
+    if (t_end > seq1) t_end = seq1;
+    const bool last_seg = (s == nseg - 1);
+    // the warm-up window [ws, t_begin): whole 32-token blocks (segments start
+    // on chunk boundaries and the window is a multiple of 32 tokens)
+    int64_t ws = t_begin;
+    if (s > 0) ws = t_begin - p.warm > seq0 ? t_begin - p.warm : seq0;
+    const bool from_zero = ws > seq0;  // else the window starts at the sequence start
+    const int64_t nwarm = (t_begin - ws) / BC;
+    const int64_t nblk = nwarm + (t_end - t_begin + BC - 1) / BC;
+    ST* go = static_cast<ST*>(p.o);
+    const int64_t ck_first = p.ckpt ? int64_t(tab_ck(p, n)) : 0;
+    int32_t* gflag = p.flags + int64_t(item) * H + h;
+    if (tid == 0) *gflag = 0;
+
+    // strictly-upper 16x16 block of P: read by the P U product, never written
+    for (int e = tid; e < BC * BC; e += C::NT) {
+        const int r = e / BC, c = e % BC;
+        if ((c >> 4) > (r >> 4)) sP[r * C::ST + pcol(c)] = O::to_op(0.f);
+    }
+    auto blen = [&](int64_t bi) {
+        const int64_t b0 = ws + bi * BC;
+        return int(t_end - b0 < BC ? t_end - b0 : BC);
+    };
+
+    if (wave >= C::NCW) {
+        prep_role<C, DT>(p, smem, ws, t_end, nblk, h, tid, wave, lane, from_zero ? nwarm - 1 : -1, pclk);
+        pclk.save(0);
+        return;
+    }
+
+    // ================= chain waves
+    constexpr int RT = DK / 16;  // state row tiles
+    const int colbase = 16 * wave;
+    const bool hasM = from_zero && colbase < DK;
+    f32x4 S[RT][2];  // [.][0]: state columns colbase.., [.][1]: M columns colbase.. (warm-up only)
+    {
+        const float* src = (!from_zero && p.init) ? p.init + (int64_t(n) * H + h) * DK * DV : nullptr;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = rt * 16 + 4 * q4 + j;
+                const int col = colbase + l16;
+                S[rt][0][j] = src ? src[row * DV + col] : 0.f;
+                S[rt][1][j] = (hasM && row == col) ? 1.f : 0.f;
+            }
+    }
+    bool mlive = hasM;  // wave-uniform: the M tile is still non-zero
+    __syncthreads();
+    KDA_PHASE(4);
+
+    // one block: EXT carries the M tile beside the state, EMIT writes outputs
+    // and checkpoints
+    auto step = [&](const int64_t bi, auto ext_t, auto emit_t) {
+        constexpr bool EXT = decltype(ext_t)::value;
+        constexpr bool EMIT = decltype(emit_t)::value;
+        const int64_t b0 = ws + bi * BC;
+        const int len = blen(bi);
+        const int buf = int(bi & 1);
+        const bool act1 = EXT && mlive;
+        // ---- alpha: X = V - (K . e^G) S;  X_M = -(K . e^G) M
+        f32x4 Xt[2][2];
+        Frag iden;  // picks this wave's 16 columns of a v row (16*(wave&1) + l16 of block wave/2)
+        {
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = (kperm(q4, e) == (wave & 1) * 16 + l16) ? 1.f : 0.f;
+            iden = O::make(x);
+        }
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            Xt[rt][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+            Xt[rt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+            O::mma(Xt[rt][0], O::load(sV + (rt * 16 + l16) * C::SV + 32 * (wave >> 1) + 8 * q4), iden);
+        }
+#pragma unroll
+        for (int kb = 0; kb < DK / 32; ++kb) {
+            const Frag a0 = O::load(sKG + l16 * C::SK + kb * 32 + 8 * q4);
+            const Frag a1 = O::load(sKG + (16 + l16) * C::SK + kb * 32 + 8 * q4);
+            const Frag sb = acc_frag<DT>(S[2 * kb][0], S[2 * kb + 1][0]);
+            O::mma(Xt[0][0], a0, sb);
+            O::mma(Xt[1][0], a1, sb);
+            if (act1) {
+                const Frag sm = acc_frag<DT>(S[2 * kb][1], S[2 * kb + 1][1]);
+                O::mma(Xt[0][1], a0, sm);
+                O::mma(Xt[1][1], a1, sm);
+            }
+        }
+        KDA_PHASE(0);
+        __syncthreads();
+        KDA_PHASE(1);
+        // ---- beta: U = (I + A)^{-1} Diag(beta) X by block substitution
+        const float* sBb = reinterpret_cast<const float*>(smem + C::O_B) + buf * BC;
+        f32x4 U0[2], U1[2];
+        Frag Ub[2];
+        {
+            const f32x4 bv0 = *reinterpret_cast<const f32x4*>(sBb + 4 * q4);
+            const f32x4 bv1 = *reinterpret_cast<const f32x4*>(sBb + 16 + 4 * q4);
+            const Frag4 d0 = O::load4(sD + l16 * C::SD + 4 * q4);
+            const Frag4 d1 = O::load4(sD + (16 + l16) * C::SD + 4 * q4);
+            const Frag4 a10 = O::load4(sA + (16 + l16) * C::ST + 4 * q4);
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                if (ct == 1 && !act1) break;
+                U0[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+                O::mma4(U0[ct], d0, O::make4(bv0 * Xt[0][ct]));
+                f32x4 R = bv1 * Xt[1][ct];
+                O::mma4(R, a10, O::make4(U0[ct]));
+                U1[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+                O::mma4(U1[ct], d1, O::make4(R));
+                Ub[ct] = acc_frag<DT>(U0[ct], U1[ct]);
+            }
+        }
+        KDA_PHASE(5);
+        if constexpr (EMIT) {
+            // O^T = S^T (Q . e^G)^T + U^T P^T: four consecutive value columns per lane
+            const OT* sQG = reinterpret_cast<const OT*>(smem + C::O_QG + buf * C::TILE_K);
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+                f32x4 Ot = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < DK / 32; ++kb) {
+                    const Frag bf = O::load(sQG + (rt * 16 + l16) * C::SK + kb * 32 + 8 * q4);
+                    O::mma(Ot, acc_frag<DT>(S[2 * kb][0], S[2 * kb + 1][0]), bf);
+                }
+                const Frag pf = O::load(sP + (rt * 16 + l16) * C::ST + 8 * q4);
+                O::mma(Ot, Ub[0], pf);
+                const int row = rt * 16 + l16;
+                if (row < len) store4<DT>(go + ((b0 + row) * H + h) * DV + colbase + 4 * q4, Ot);
+            }
+        }
+        KDA_PHASE(6);
+        // S <- Diag(e^{G_last}) S + (K . e^{G_last - G})^T U
+        const OT* sKH = reinterpret_cast<const OT*>(smem + C::O_KH + buf * C::TILE_H);
+        const float* gcv = sVec + (V_GC + buf) * DK;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const f32x4 gc = *reinterpret_cast<const f32x4*>(gcv + pcol(rt * 16 + 4 * q4));
+            const Frag kf = O::load(sKH + (rt * 16 + l16) * C::ST + 8 * q4);
+            S[rt][0] *= gc;
+            O::mma(S[rt][0], kf, Ub[0]);
+            if (act1) {
+                S[rt][1] *= gc;
+                O::mma(S[rt][1], kf, Ub[1]);
+            }
+        }
+        if constexpr (EMIT) {
+            // state checkpoint when this block ends on a multiple of the interval
+            if (p.ckpt) {
+                const int64_t pos = b0 + len - seq0;  // tokens of the sequence consumed
+                if (pos % p.ckpt_interval == 0) {
+                    const int64_t idx = ck_first + pos / p.ckpt_interval - 1;
+                    if (idx < p.ckpt_cap) {
+                        // one lane pointer, formed here (see the output pass)
+                        uint32_t eo = uint32_t(4 * q4 * DV + colbase + l16);
+                        asm volatile("" : "+v"(eo));
+                        float* dst = p.ckpt + (idx * H + h) * DK * DV + eo;
+#pragma unroll
+                        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                            for (int j = 0; j < 4; ++j)
+                                __builtin_nontemporal_store(S[rt][0][j], dst + (rt * 16 + j) * DV);
+                    }
+                }
+            }
+        }
+        if constexpr (EXT) {
+            if (act1) {
+                bool nz = false;
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) nz = nz || (S[rt][1][j] != 0.f);
+                mlive = __ballot(nz) != 0;
+            }
+            if (bi == nwarm - 1 && lane == 0) sFlag[wave] = mlive ? 1 : 0;
+        }
+        KDA_PHASE(2);
+        __syncthreads();
+        KDA_PHASE(3);
+    };
+
+    int64_t bi = 0;
+    if (from_zero) {
+        for (; bi < nwarm; ++bi) step(bi, std::true_type{}, std::false_type{});
+        if (warm_failed<C>(smem)) {  // the incoming state still matters: the exact passes take over
+            if (tid == 0) *gflag = 1;
+            return;
+        }
+    } else {
+        for (; bi < nwarm; ++bi) step(bi, std::false_type{}, std::false_type{});
+    }
+    for (; bi < nblk; ++bi) step(bi, std::false_type{}, std::true_type{});
+    pclk.save(0);
+
+    if (last_seg && p.fin) {
+        // one lane offset, formed here: formed before the block loop, the
+        // compiler keeps the element addresses live across it
+        uint32_t eo = uint32_t(4 * q4 * DV + colbase + l16);
+        asm volatile("" : "+v"(eo));
+        float* dst = p.fin + (int64_t(n) * H + h) * DK * DV + eo;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) dst[(rt * 16 + j) * DV] = S[rt][0][j];
+    }
+}
+
 // ------------------------------------------------------------------ launch
 template <typename DT, int DK, int DV>
 hipError_t launch_prefill_t(const PrefillArgs& a, const PrefillPlan& plan, hipStream_t stream)
@@ -1472,27 +1778,42 @@ hipError_t launch_prefill_t(const PrefillArgs& a, const PrefillPlan& plan, hipSt
         single_nseg = int(ns < 1 ? 1 : ns);
         single_nck = (a.ckpt && a.ckpt_interval > 0) ? int(len / a.ckpt_interval) : 0;
     }
+    const bool warm = plan.warm > 0 && warm_shape(DK, DV);
     PrefillDev d{a.q, a.k, a.v, a.g, a.beta, tab, a.N, a.T_total, a.H, plan.seg_chunks,
                  a.init, a.fin, a.o,
                  plan.np1_max > 0 ? reinterpret_cast<float*>(ws + plan.off_ms) : nullptr,
                  plan.np1_max > 0 ? reinterpret_cast<float*>(ws + plan.off_sin) : nullptr,
                  a.ckpt, a.ckpt_interval, a.ckpt_cap, single ? 1 : 0, single_nseg, single_nck,
-                 a.gate_A, a.g_min};
+                 a.gate_A, a.g_min,
+                 warm ? reinterpret_cast<int32_t*>(ws + plan.off_flags) : nullptr, plan.warm};
     hipError_t e = hipSuccess;
     if (!single) {
         hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, stream, a.cu, a.N, a.T_total,
                            plan.seg_chunks, a.ckpt ? a.ckpt_interval : 0, tab);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
+    if constexpr (warm_shape(DK, DV)) {
+        if (warm) {
+            using CW_ = BlockCfg<DT, DK, DV, MODE_WARM>;
+            auto kw = prefill_warm_kernel<DT, DK, DV>;
+            e = hipFuncSetAttribute(reinterpret_cast<const void*>(kw), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    CW_::LDS);
+            if (e != hipSuccess) return e;
+            hipLaunchKernelGGL(kw, dim3(unsigned(plan.nseg_max * a.H)), dim3(CW_::NT), CW_::LDS, stream, d);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+            // every sequence is one segment: no warm-up can fail
+            if (plan.np1_max == 0) return hipSuccess;
+        }
+    }
+    // the exact passes (after a warm-up pass: only for the chains it flagged)
     if (plan.np1_max > 0) {
-        using C1 = BlockCfg<DT, DK, DV, true>;
+        using C1 = BlockCfg<DT, DK, DV, MODE_SUMMARY>;
         auto k1 = prefill_block_kernel<DT, DK, DV, true>;
         e = hipFuncSetAttribute(reinterpret_cast<const void*>(k1),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, C1::LDS);
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(k1, dim3(unsigned(plan.np1_max * a.H)), dim3(C1::NT), C1::LDS, stream, d);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        if (a.join && (e = hipStreamWaitEvent(stream, a.join, 0)) != hipSuccess) return e;
         auto ks = scan_kernel<DK, DV>;
         constexpr int scan_lds = ScanCfg<DK, DV>::LDS;
         e = hipFuncSetAttribute(reinterpret_cast<const void*>(ks), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -1501,8 +1822,7 @@ hipError_t launch_prefill_t(const PrefillArgs& a, const PrefillPlan& plan, hipSt
         hipLaunchKernelGGL(ks, dim3(unsigned(a.N * a.H * (DV / SCAN_COLS))), dim3(256), scan_lds, stream, d);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    if (plan.np1_max == 0 && a.join && (e = hipStreamWaitEvent(stream, a.join, 0)) != hipSuccess) return e;
-    using C3 = BlockCfg<DT, DK, DV, false>;
+    using C3 = BlockCfg<DT, DK, DV, MODE_OUT>;
     auto k3 = prefill_block_kernel<DT, DK, DV, false>;
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(k3),
                             hipFuncAttributeMaxDynamicSharedMemorySize, C3::LDS);

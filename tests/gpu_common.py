@@ -64,3 +64,16 @@ def dev_stream(wl, name: str, set_index: int = 0, rows: int = 1 << 16):
         x = torch.from_numpy(synth.token_rows(wl, name, t0, t1, set_index))
         out[t0:t1].copy_(x.to(torch_dtype(wl.dtype)))
     return out
+
+
+def gated_prefill(kda, q, k, v, z, A, beta, seg=None, warm=-1, interval=0, **kw):
+    """kda_prefill_gated; with a forced segment length (chunks) or warm-up
+    window (tokens; 0 = the exact passes only) through the test entry point
+    that takes the planner's choices as arguments.  Returns (o, S) or, with a
+    checkpoint interval, (o, S, ckpt)."""
+    if seg is None and warm == -1:
+        return kda.kda_prefill_gated(q, k, v, z, A, beta, interval=interval, **kw)
+    kw.pop("want_final_state", None)
+    o, S, ck, _ = kda.kda_test_prefill(q, k, v, z, beta, A=A, interval=interval, seg_chunks=seg or 0,
+                                       warm_tokens=warm, **kw)
+    return (o, S, ck) if interval > 0 else (o, S)

@@ -50,10 +50,15 @@ def test_gate_validation(L):
     assert L.kda_gate(FAKE, FAKE, FAKE, 4, 2, 32, 7, -5.0, None) == 2
     assert L.kda_gate(FAKE, FAKE, FAKE, 4, 2, 32, BF16, 1.0, None) == 1
     assert L.kda_gate(FAKE, FAKE, FAKE, 4, 2, 32, BF16, float("nan"), None) == 1
+    # g >= -5 is what the prefill and the backward need (their per-sub-tile
+    # decay factors stay inside the fp32 range): a lower bound below it is refused
+    assert L.kda_gate(FAKE, FAKE, FAKE, 4, 2, 32, BF16, -5.5, None) == 1
+    assert b"[-5, 0)" in L.kda_last_error()
     assert L.kda_gate(None, FAKE, FAKE, 4, 2, 32, BF16, -5.0, None) == 1
     assert b"null" in L.kda_last_error()
-    # partial overlap of g with z (exact aliasing is allowed)
-    assert L.kda_gate(FAKE, FAKE + 1 << 20, FAKE + 64, 4, 2, 32, BF16, -5.0, None) == 1
+    # partial overlap of g with z (exact aliasing is allowed); A far away
+    assert L.kda_gate(FAKE, FAKE + (1 << 20), FAKE + 64, 4, 2, 32, BF16, -5.0, None) == 1
+    assert b"partially overlaps" in L.kda_last_error()
     # n_tokens == 0 is a no-op that succeeds without touching the device
     assert L.kda_gate(None, None, None, 0, 2, 32, BF16, -5.0, None) == 0
 
@@ -81,18 +86,33 @@ def test_decode_validation(L):
     assert call(B=0, q=None, o=None) == 0                  # empty batch: no-op
 
 
-def test_prefill_workspace_head_split(L, monkeypatch):
-    """One long sequence whose segments leave compute units idle takes the head
-    split: its workspace also holds the head's final state (fp32 [H][d_k][d_v]),
-    and is never smaller than the unsplit plan's (a forced segment length turns
-    the split off)."""
+def test_prefill_plan_is_explicit(L, monkeypatch):
+    """The planner reads nothing from the environment: the workspace size
+    depends only on the arguments, and forced choices go through the test entry
+    point.  Its warm-up flags (int32 per segment and head) sit in the workspace
+    only when the plan has a warm-up pass."""
     ws = kda.kda_prefill_workspace_size
-    split = ws(8192, 1, 32, 128, 128)
-    monkeypatch.setenv("KDA_SEG_CHUNKS", "16")
-    plain = ws(8192, 1, 32, 128, 128)
-    monkeypatch.delenv("KDA_SEG_CHUNKS")
-    assert split >= 32 * 128 * 128 * 4 and split >= plain
-    assert ws(8192, 2, 32, 128, 128) > 0  # packed sequences: no split
+    tws = L.kda_test_prefill_workspace_size
+    base = ws(8192, 1, 32, 128, 128)
+    for var in ("KDA_SEG_CHUNKS", "KDA_BWD_SEG_TOKENS", "KDA_LOG"):
+        monkeypatch.setenv(var, "3")
+    assert ws(8192, 1, 32, 128, 128) == base
+    assert tws(8192, 1, 32, 128, 128, BF16, 0, -1) == base
+    assert tws(8192, 1, 32, 128, 128, BF16, 3, -1) > base      # more segments, more summaries
+    assert tws(8192, 1, 32, 128, 128, BF16, 0, 0) > 0          # exact passes only
+    assert tws(8192, 1, 32, 128, 128, BF16, -1, -1) == 0       # bad segment length
+    assert tws(8192, 1, 32, 128, 128, BF16, 0, 48) == 0        # warm-up not a multiple of 32
+    off = ctypes.c_size_t(0)
+    n = L.kda_test_prefill_flags(8192, 1, 32, 128, 128, BF16, 0, -1, ctypes.byref(off))
+    assert n >= 8 * 32 and off.value % 256 == 0 and off.value + 4 * n <= base
+    assert L.kda_test_prefill_flags(8192, 1, 32, 128, 128, BF16, 0, 0, ctypes.byref(off)) == 0
+    # no warm-up kernel for d_k > d_v: the exact passes are the plan
+    assert L.kda_test_prefill_flags(8192, 1, 32, 128, 64, BF16, 0, -1, ctypes.byref(off)) == 0
+    # the test entry point validates its own arguments before the prefill's
+    assert L.kda_test_prefill(FAKE, FAKE, FAKE, FAKE, None, -5.0, FAKE, None, 1, 256, 2, 64, 64, None, None,
+                              FAKE, BF16, FAKE, 1 << 20, 0, None, 0, 0, 40, None) == 1
+    assert L.kda_test_prefill(FAKE, FAKE, FAKE, FAKE, FAKE + (64 << 20), -6.0, FAKE, None, 1, 256, 2, 64, 64,
+                              None, None, FAKE, BF16, FAKE, 1 << 20, 0, None, 0, 0, -1, None) == 1
 
 
 def test_prefill_workspace_size(L):

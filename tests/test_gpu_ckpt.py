@@ -8,7 +8,6 @@ import pytest
 import oracle
 import synth
 from tests.gpu_common import TOL, announce, dev, host, relerr
-from tests.test_gpu_prefill import SegEnv
 
 pytestmark = pytest.mark.gpu
 
@@ -35,21 +34,27 @@ def oracle_ckpts(wl, x, g, S0, interval):
     return np.array(out) if out else np.zeros((0, wl.H, wl.dk, wl.dv))
 
 
-def check(kda, wl, interval, seg=None):
+def check(kda, wl, interval, seg=None, warm=-1):
     import torch
     announce(f"ckpt {wl.name} H={wl.H} dk={wl.dk} dv={wl.dv} {wl.dtype} lens={list(wl.seqlens)[:10]} "
-             f"interval={interval} seg={seg}")
+             f"interval={interval} seg={seg} warm={warm}")
     dt = wl.dtype
     x = synth.prefill_inputs(wl)
     S0 = synth.initial_state(wl) if wl.state_std > 0 else None
     g_dev = kda.kda_gate(dev(x["z"], dt), dev(x["A"]))
     cu = torch.from_numpy(wl.cu_seqlens).cuda() if wl.N > 1 else None
     args = [dev(x[n], dt) for n in ("q", "k", "v")] + [g_dev, dev(x["beta"], dt)]
-    with SegEnv(seg):
+    init = None if S0 is None else dev(S0)
+    if seg is None:
         o, S, ck = kda.kda_prefill_ckpt(*args, interval=interval, cu_seqlens=cu,
-                                        cu_seqlens_host=wl.cu_seqlens if wl.N > 1 else None,
-                                        initial_state=None if S0 is None else dev(S0))
-        o2, S2 = kda.kda_prefill(*args, cu_seqlens=cu, initial_state=None if S0 is None else dev(S0))
+                                        cu_seqlens_host=wl.cu_seqlens if wl.N > 1 else None, initial_state=init)
+        o2, S2 = kda.kda_prefill(*args, cu_seqlens=cu, initial_state=init)
+    else:  # a forced segment length, through the test entry point
+        hcu = wl.cu_seqlens if wl.N > 1 else None
+        o, S, ck, _ = kda.kda_test_prefill(*args, interval=interval, cu_seqlens=cu, cu_seqlens_host=hcu,
+                                           initial_state=init, seg_chunks=seg, warm_tokens=warm)
+        o2, S2, _, _ = kda.kda_test_prefill(*args, cu_seqlens=cu, initial_state=init, seg_chunks=seg,
+                                            warm_tokens=warm)
     torch.cuda.synchronize()
     assert torch.equal(o, o2) and torch.equal(S, S2), "checkpointing changed the outputs"
     g = oracle.gate(x["z"], x["A"], round_bf16=(dt == "bf16"))
@@ -68,10 +73,13 @@ def test_ckpt_varlen(kda, interval):
     check(kda, wl, interval)
 
 
-def test_ckpt_segmented(kda):
-    """checkpoints written by the output pass of every segment of a long sequence"""
-    wl = synth.VARLEN_64.with_(H=2, seqlens=(3000, 700), state_std=0.1)
-    check(kda, wl, 128, seg=3)
+@pytest.mark.parametrize("warm", [-1, 0])
+@pytest.mark.parametrize("zshift", [0.0, -3.0])
+def test_ckpt_segmented(kda, warm, zshift):
+    """checkpoints written by every segment of long sequences, after a warm-up
+    window (weak decay: the exact passes write them) or the exact passes alone"""
+    wl = synth.VARLEN_64.with_(H=2, seqlens=(3000, 700), state_std=0.1, z_shift=zshift)
+    check(kda, wl, 128, seg=3, warm=warm)
 
 
 def test_ckpt_f32(kda):

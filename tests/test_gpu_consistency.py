@@ -9,8 +9,7 @@ import pytest
 
 import oracle
 import synth
-from tests.gpu_common import TOL, announce, dev, host, relerr
-from tests.test_gpu_prefill import SegEnv
+from tests.gpu_common import TOL, announce, dev, gated_prefill, host, relerr
 
 pytestmark = pytest.mark.gpu
 
@@ -34,9 +33,8 @@ def _inputs(wl):
 def _gated(kda, d, rows=None, cu=None, S0=None, seg=None):
     import torch
     sl = (lambda t: t) if rows is None else (lambda t: t[rows[0]:rows[1]].contiguous())
-    with SegEnv(seg):
-        o, S = kda.kda_prefill_gated(sl(d["q"]), sl(d["k"]), sl(d["v"]), sl(d["z"]), d["A"], sl(d["beta"]),
-                                     cu_seqlens=cu, initial_state=S0)
+    o, S = gated_prefill(kda, sl(d["q"]), sl(d["k"]), sl(d["v"]), sl(d["z"]), d["A"], sl(d["beta"]), seg=seg,
+                         cu_seqlens=cu, initial_state=S0)
     torch.cuda.synchronize()
     return o, S
 

@@ -1,8 +1,6 @@
 """GPU parity: kda_gate + kda_prefill against the fp64 oracle (token-serial
 recurrence).  The GPU path applies its own gate to z and A; the oracle applies
 its gate and rounds g to the storage dtype, as the gate's output contract says."""
-import os
-
 import numpy as np
 import pytest
 
@@ -22,33 +20,21 @@ def kda():
     return m
 
 
-class SegEnv:
-    """Force a segment length (chunks) for the library's planner."""
-
-    def __init__(self, chunks):
-        self.chunks = chunks
-
-    def __enter__(self):
-        self.old = os.environ.get("KDA_SEG_CHUNKS")
-        if self.chunks is not None:
-            os.environ["KDA_SEG_CHUNKS"] = str(self.chunks)
-
-    def __exit__(self, *a):
-        if self.old is None:
-            os.environ.pop("KDA_SEG_CHUNKS", None)
-        else:
-            os.environ["KDA_SEG_CHUNKS"] = self.old
-
-
-def run_gpu(kda, wl, x, S0, seg=None):
+def run_gpu(kda, wl, x, S0, seg=None, warm=-1):
+    """kda_gate + kda_prefill; with a forced segment length (chunks) or warm-up
+    (tokens; 0 = the exact summary / scan / output passes only) through the
+    test entry point that takes the planner's choices as arguments."""
     import torch
     dt = wl.dtype
     cu = torch.from_numpy(wl.cu_seqlens).to("cuda") if wl.N > 1 else None
     g = kda.kda_gate(dev(x["z"], dt), dev(x["A"]))
-    with SegEnv(seg):
-        o, S = kda.kda_prefill(dev(x["q"], dt), dev(x["k"], dt), dev(x["v"], dt), g,
-                               dev(x["beta"], dt), cu_seqlens=cu,
-                               initial_state=None if S0 is None else dev(S0))
+    args = (dev(x["q"], dt), dev(x["k"], dt), dev(x["v"], dt), g, dev(x["beta"], dt))
+    init = None if S0 is None else dev(S0)
+    if seg is None and warm == -1:
+        o, S = kda.kda_prefill(*args, cu_seqlens=cu, initial_state=init)
+    else:
+        o, S, _, _ = kda.kda_test_prefill(*args, cu_seqlens=cu, initial_state=init, seg_chunks=seg or 0,
+                                          warm_tokens=warm)
     torch.cuda.synchronize()
     return host(o), host(S)
 
@@ -58,12 +44,12 @@ def run_oracle(wl, x, S0):
     return oracle.prefill(x["q"], x["k"], x["v"], g, x["beta"], cu=wl.cu_seqlens, S0=S0)
 
 
-def check(kda, wl, seg=None, tag=""):
+def check(kda, wl, seg=None, tag="", warm=-1):
     announce(f"prefill {wl.name} {tag} H={wl.H} dk={wl.dk} dv={wl.dv} {wl.dtype} "
-             f"lens={list(wl.seqlens)[:8]} seg={seg}")
+             f"lens={list(wl.seqlens)[:8]} seg={seg} warm={warm}")
     x = synth.prefill_inputs(wl)
     S0 = synth.initial_state(wl) if wl.state_std > 0 else None
-    o, S = run_gpu(kda, wl, x, S0, seg)
+    o, S = run_gpu(kda, wl, x, S0, seg, warm)
     o_ref, S_ref = run_oracle(wl, x, S0)
     e_o, e_s = relerr(o, o_ref), relerr(S, S_ref)
     print(f"  o err {e_o:.3e}  state err {e_s:.3e}")
@@ -92,20 +78,26 @@ def test_prefill_varlen_dims(kda, dk, dv, dtype):
     check(kda, wl)
 
 
+@pytest.mark.parametrize("warm", [-1, 0, 64])
 @pytest.mark.parametrize("seg", [1, 2, 3])
 @pytest.mark.parametrize("zshift", [0.0, -3.0])
-def test_prefill_segmented(kda, seg, zshift):
-    """Segments of `seg` chunks: transition/zero-state summary, scan, rerun."""
+def test_prefill_segmented(kda, seg, zshift, warm):
+    """Segments of `seg` chunks, each given its incoming state by a warm-up
+    window (default 128 tokens, or 64: windows that reach the sequence start run
+    from the initial state, the others check their transition; with the weak
+    decay of z - 3 the exact passes take over) or by the exact passes alone
+    (warm = 0: transition/zero-state summary, scan, rerun)."""
     wl = synth.VARLEN_64.with_(H=4, seqlens=(700, 0, 64, 129, 1000, 5), state_std=0.1,
                                z_shift=zshift)
-    check(kda, wl, seg=seg, tag=f"zshift={zshift}")
+    check(kda, wl, seg=seg, tag=f"zshift={zshift}", warm=warm)
 
 
+@pytest.mark.parametrize("warm", [-1, 0])
 @pytest.mark.parametrize("dv", [32, 64])
-def test_prefill_segmented_f32(kda, dv):
-    """fp32 storage through the segment summary and scan (fp32 tolerance)."""
+def test_prefill_segmented_f32(kda, dv, warm):
+    """fp32 storage through the segment passes (fp32 tolerance)."""
     wl = synth.TINY_F32.with_(H=3, dv=dv, seqlens=(700, 3, 450), state_std=0.1, z_shift=-2.0)
-    check(kda, wl, seg=2)
+    check(kda, wl, seg=2, warm=warm)
 
 
 def test_prefill_weak_decay_long(kda):
@@ -114,16 +106,20 @@ def test_prefill_weak_decay_long(kda):
     wl = synth.PREFILL_8K.with_(H=4, seqlens=(4096,), z_shift=-3.0, state_std=0.1)
     check(kda, wl)
     check(kda, wl, seg=4, tag="seg4")
+    check(kda, wl, seg=4, tag="seg4 exact passes", warm=0)
 
 
+@pytest.mark.parametrize("warm", [-1, 0])
 @pytest.mark.parametrize("case", ["beta0", "alpha1", "gmin", "alpha1_beta1_orthonormal"])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_prefill_special_values(kda, case, dtype):
+def test_prefill_special_values(kda, case, dtype, warm):
     """Exact edge values of the decay and the write strength, given to
     kda_prefill directly: beta = 0 (pure per-channel decay), g = 0 (alpha = 1,
     no forgetting), g = -5 everywhere (the strongest decay the gate allows),
     and alpha = beta = 1 with orthonormal keys (exact recall of every value).
-    Segments of 2 chunks, so the summary pass and the scan see them too."""
+    Segments of 2 chunks, so the warm-up windows (the transition of g = -5
+    vanishes; without decay it never does and the exact passes take over) and
+    the summary pass and scan (warm = 0) see them too."""
     import torch
     dk = dv = 32
     # weak decay for beta = 0 (z shifted by -4), so the decayed state stays far
@@ -158,9 +154,9 @@ def test_prefill_special_values(kda, case, dtype):
                 x[n] = oracle.round_bf16(x[n]).astype(np.float32)
         S0 = np.zeros_like(synth.initial_state(wl))
     cu = torch.from_numpy(wl.cu_seqlens).to("cuda")
-    with SegEnv(2):
-        o, S = kda.kda_prefill(dev(x["q"], dtype), dev(x["k"], dtype), dev(x["v"], dtype), dev(g, dtype),
-                               dev(x["beta"], dtype), cu_seqlens=cu, initial_state=dev(S0))
+    o, S, _, _ = kda.kda_test_prefill(dev(x["q"], dtype), dev(x["k"], dtype), dev(x["v"], dtype), dev(g, dtype),
+                                      dev(x["beta"], dtype), cu_seqlens=cu, initial_state=dev(S0), seg_chunks=2,
+                                      warm_tokens=warm)
     torch.cuda.synchronize()
     o_ref, S_ref = oracle.prefill(x["q"], x["k"], x["v"], g, x["beta"], cu=wl.cu_seqlens, S0=S0)
     tol = TOL[dtype]

@@ -7,8 +7,7 @@ import pytest
 
 import oracle
 import synth
-from tests.gpu_common import TOL, announce, dev, host, relerr
-from tests.test_gpu_prefill import SegEnv
+from tests.gpu_common import TOL, announce, dev, gated_prefill, host, relerr
 
 pytestmark = pytest.mark.gpu
 
@@ -26,11 +25,10 @@ def run_gated(kda, wl, x, S0, seg=None, g_min=-5.0, interval=0):
     import torch
     dt = wl.dtype
     cu = torch.from_numpy(wl.cu_seqlens).to("cuda") if wl.N > 1 else None
-    with SegEnv(seg):
-        res = kda.kda_prefill_gated(dev(x["q"], dt), dev(x["k"], dt), dev(x["v"], dt), dev(x["z"], dt),
-                                    dev(x["A"]), dev(x["beta"], dt), g_min=g_min, cu_seqlens=cu,
-                                    initial_state=None if S0 is None else dev(S0), interval=interval,
-                                    cu_seqlens_host=wl.cu_seqlens if wl.N > 1 else None)
+    res = gated_prefill(kda, dev(x["q"], dt), dev(x["k"], dt), dev(x["v"], dt), dev(x["z"], dt),
+                        dev(x["A"]), dev(x["beta"], dt), seg=seg, g_min=g_min, cu_seqlens=cu,
+                        initial_state=None if S0 is None else dev(S0), interval=interval,
+                        cu_seqlens_host=wl.cu_seqlens if wl.N > 1 else None)
     torch.cuda.synchronize()
     return tuple(host(t) for t in res)
 
