@@ -196,6 +196,31 @@ kda_status_t kda_prefill_gated(const void* q, const void* k, const void* v, cons
                                void* o, kda_dtype_t dtype, void* workspace, size_t workspace_bytes,
                                int ckpt_interval, float* ckpt_states, int64_t ckpt_capacity, void* stream);
 
+/* Bytes of the static scratch kda_prefill_gated_noalloc takes its workspace from. */
+#define KDA_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * kda_prefill_gated_noalloc — kda_prefill_gated without a workspace argument,
+ * for callers that cannot allocate device memory (code under stream capture,
+ * tight serving loops, harnesses that forbid allocation).  It takes its
+ * workspace from a static device array of KDA_NOALLOC_SCRATCH_BYTES that the
+ * library holds on each GPU it runs on until the process ends (its device
+ * address is looked up on the first call on each device), and calls no
+ * allocating routine.  Arguments, results and errors are those of
+ * kda_prefill_gated, plus KDA_ERR_UNSUPPORTED when the call would need more
+ * workspace than the scratch holds (kda_prefill_workspace_size gives the
+ * amount; a single sequence at d_k = d_v = 128 needs about 50 MB at most).
+ * Every call on a GPU shares that GPU's scratch, which keeps the last call's
+ * contents (nothing in it must start at zero): calls that overlap in time on
+ * one GPU, on different streams or threads, race and give wrong results;
+ * serialize them.
+ */
+kda_status_t kda_prefill_gated_noalloc(const void* q, const void* k, const void* v, const void* z, const float* A,
+                                       float g_min, const void* beta, const int32_t* cu_seqlens, int N,
+                                       int64_t T_total, int H, int d_k, int d_v, int chunk,
+                                       const float* initial_state, float* final_state, void* o, kda_dtype_t dtype,
+                                       int ckpt_interval, float* ckpt_states, int64_t ckpt_capacity, void* stream);
+
 /*
  * TEST ONLY — the prefill with the planner's two choices given as arguments,
  * so tests can force segment boundaries and either route (kda_prefill).

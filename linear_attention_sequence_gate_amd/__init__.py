@@ -21,7 +21,7 @@ EXPORTED = ("kda_status_string", "kda_last_error", "kda_version", "kda_gate",
             "kda_prefill_workspace_size", "kda_prefill", "kda_decode_step", "kda_verify", "kda_commit",
             "kda_prefill_ckpt", "kda_checkpoint_count", "kda_prefill_gated", "kda_decode_step_gated",
             "kda_backward_workspace_size", "kda_backward", "kda_test_prefill", "kda_test_prefill_workspace_size",
-            "kda_test_prefill_flags")
+            "kda_test_prefill_flags", "kda_prefill_gated_noalloc")
 
 _lib = None
 
@@ -78,6 +78,9 @@ def lib() -> ctypes.CDLL:
         L.kda_test_prefill_workspace_size.restype = SZ
         L.kda_test_prefill_flags.argtypes = [I64, I, I, I, I, I, I, I, ctypes.POINTER(SZ)]
         L.kda_test_prefill_flags.restype = I64
+        L.kda_prefill_gated_noalloc.argtypes = [P, P, P, P, P, F, P, P, I, I64, I, I, I, I, P, P, P, I, I, P, I64,
+                                                P]
+        L.kda_prefill_gated_noalloc.restype = I
         L.kda_checkpoint_count.argtypes = [P, I, I64, I]
         L.kda_checkpoint_count.restype = I64
         _lib = L
@@ -275,6 +278,24 @@ def kda_prefill_gated(q, k, v, z, A, beta, g_min: float = -5.0, cu_seqlens=None,
                                    _ptr(ckpt) if cap else None, cap, _stream(stream)))
     if interval > 0:
         return o, final_state, ckpt
+    return o, final_state
+
+
+def kda_prefill_gated_noalloc(q, k, v, z, A, beta, o, final_state=None, g_min: float = -5.0, cu_seqlens=None,
+                              initial_state=None, interval: int = 0, ckpt=None, chunk: int = 64, stream=None):
+    """kda_prefill_gated without a workspace: the library's static scratch is
+    used instead (calls on one GPU must not overlap).  The caller passes the
+    outputs (o [T, H, d_v], final_state or None, ckpt when interval > 0).
+    Returns (o, final_state)."""
+    _dense(q, k, v, z, A, beta, o, final_state, cu_seqlens, initial_state, ckpt)
+    T, H, dk = k.shape
+    dv = v.shape[2]
+    N = 1 if cu_seqlens is None else cu_seqlens.shape[0] - 1
+    cap = 0 if ckpt is None else ckpt.shape[0]
+    _check(lib().kda_prefill_gated_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(A), float(g_min), _ptr(beta),
+                                           _ptr(cu_seqlens), N, T, H, dk, dv, chunk, _ptr(initial_state),
+                                           _ptr(final_state), _ptr(o), _dtype_code(k), int(interval),
+                                           _ptr(ckpt) if cap else None, cap, _stream(stream)))
     return o, final_state
 
 

@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
+#include <mutex>
 
 #include "kda.h"
 #include "kda_decode.hpp"
@@ -412,6 +413,58 @@ kda_status_t kda_prefill_gated(const void* q, const void* k, const void* v, cons
     return prefill_impl("kda_prefill_gated", q, k, v, z, beta, cu_seqlens, N, T_total, H, d_k, d_v, chunk,
                         initial_state, final_state, o, dtype, workspace, workspace_bytes, ckpt_interval,
                         ckpt_states, ckpt_capacity, stream, T_total > 0 ? A : nullptr, g_min);
+}
+
+// ---- the prefill without a workspace argument, for callers that cannot
+// allocate.  Its workspace is this array: each GPU the library runs on holds
+// one copy until the process ends.  Host code must use the address that
+// hipGetSymbolAddress returns for the current device, never the array's name
+// (on the host that is a stand-in, not a device address).
+static __device__ __align__(256) unsigned char scratch[KDA_NOALLOC_SCRATCH_BYTES];
+
+// The device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept; null with *err set on failure.
+static void* scratch_address(hipError_t* err)
+{
+    constexpr int MAX_DEV = 64;
+    static std::mutex mu;
+    static void* addr[MAX_DEV] = {};
+    int dev = -1;
+    *err = hipGetDevice(&dev);
+    if (*err != hipSuccess) return nullptr;
+    if (dev < 0 || dev >= MAX_DEV) {
+        *err = hipErrorInvalidDevice;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (*err != hipSuccess) return nullptr;
+        addr[dev] = p;
+    }
+    return addr[dev];
+}
+
+kda_status_t kda_prefill_gated_noalloc(const void* q, const void* k, const void* v, const void* z, const float* A,
+                                       float g_min, const void* beta, const int32_t* cu_seqlens, int N,
+                                       int64_t T_total, int H, int d_k, int d_v, int chunk,
+                                       const float* initial_state, float* final_state, void* o, kda_dtype_t dtype,
+                                       int ckpt_interval, float* ckpt_states, int64_t ckpt_capacity, void* stream)
+{
+    const char* who = "kda_prefill_gated_noalloc";
+    if (!prefill_shape_ok(T_total, N, H, d_k, d_v, chunk, dtype))
+        return fail(KDA_ERR_UNSUPPORTED, "%s: shape outside the supported set (see kda_prefill)", who);
+    const size_t need = kda::prefill_plan(T_total, N, H, d_k, d_v).workspace_bytes;
+    if (need > KDA_NOALLOC_SCRATCH_BYTES)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: this call needs %zu bytes of workspace, more than the %zu-byte "
+                    "static scratch; use kda_prefill_gated with a workspace", who, need,
+                    size_t(KDA_NOALLOC_SCRATCH_BYTES));
+    hipError_t e = hipSuccess;
+    void* ws = need > 0 ? scratch_address(&e) : nullptr;
+    if (need > 0 && !ws) return from_hip(e, "kda_prefill_gated_noalloc: scratch address");
+    return kda_prefill_gated(q, k, v, z, A, g_min, beta, cu_seqlens, N, T_total, H, d_k, d_v, chunk, initial_state,
+                             final_state, o, dtype, ws, need, ckpt_interval, ckpt_states, ckpt_capacity, stream);
 }
 
 // ---- test-only entry points: the planner's choices made explicit

@@ -339,3 +339,21 @@ def test_backward_validation(L):
     assert call(dg=FAKE + (8 << 20) + 64) == 1              # dg overlaps dq
     assert call(ws=FAKE + (13 << 20)) == 1                  # workspace overlaps d_initial_state
     assert b"kda_backward" in L.kda_last_error()
+
+
+def test_noalloc_limits(L):
+    """kda_prefill_gated_noalloc checks its workspace against the static
+    scratch on the host, before touching the device: a packed batch whose
+    segment buffers exceed it is refused with a message naming both sizes;
+    the 8K workload fits."""
+    assert kda.kda_prefill_workspace_size(8192, 1, 32, 128, 128) <= (64 << 20)
+    big = kda.kda_prefill_workspace_size(1 << 20, 64, 32, 128, 128)
+    assert big > (64 << 20)
+    st = L.kda_prefill_gated_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, -5.0, FAKE, FAKE, 64, 1 << 20, 32, 128, 128, 64,
+                                     None, None, FAKE, BF16, 0, None, 0, None)
+    assert st == 2
+    msg = L.kda_last_error().decode()
+    assert "static scratch" in msg and str(big) in msg
+    # unsupported shapes are refused as by kda_prefill_gated
+    assert L.kda_prefill_gated_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, -5.0, FAKE, None, 1, 256, 2, 96, 64, 64,
+                                       None, None, FAKE, BF16, 0, None, 0, None) == 2
