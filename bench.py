@@ -379,7 +379,7 @@ def main():
 
     def bcall(i):
         kda.kda_backward(bsets["q"], bsets["k"], bsets["v"], bg, bsets["beta"], d_o=bdo, d_final_state=bdfin,
-                         ckpt=bck, workspace=bws)
+                         ckpt=bck, interval=64, workspace=bws)
 
     bcall(0)
     b_ms = timed_loop(bcall, 3)

@@ -261,12 +261,18 @@ int64_t kda_test_prefill_flags(int64_t T_total, int N, int H, int d_k, int d_v, 
  *   d_o            : [T_total, H, d_v] (dtype) or NULL (no output gradient).
  *   d_final_state  : fp32 [N, H, d_k, d_v] or NULL (zero).
  *   initial_state  : the forward's, or NULL (zero).
- *   ckpt_states    : the forward's checkpoints at interval 64 (kda_prefill_ckpt
- *                    or kda_prefill_gated with ckpt_interval = 64, same inputs
- *                    and initial state), ckpt_capacity rows; may be NULL.  A
- *                    64-token chunk without its checkpoint row is recomputed
- *                    from the initial state (correct, but quadratic in the
- *                    sequence length).
+ *   ckpt_states    : the forward's checkpoints (kda_prefill_ckpt or
+ *                    kda_prefill_gated with the same inputs and initial state)
+ *                    at ckpt_interval tokens, ckpt_capacity rows, laid out as
+ *                    kda_prefill_ckpt writes them; may be NULL.  Each 64-token
+ *                    chunk rebuilds its forward state from the nearest
+ *                    checkpoint at or before its start that the buffer holds
+ *                    (interval 64: the chunk's own row, nothing to rebuild),
+ *                    else from the initial state.  Without checkpoints that
+ *                    rebuild is quadratic in the sequence length, so T_total
+ *                    is then limited to KDA_BWD_MAX_TOKENS_WITHOUT_CKPT.
+ *   ckpt_interval  : a positive multiple of 64 when ckpt_states is given
+ *                    (ignored otherwise).
  *   workspace      : at least kda_backward_workspace_size(T_total, N, H, d_k,
  *                    d_v) bytes: per workgroup slot, the states at the four
  *                    16-token sub-chunk starts of a 64-token chunk (in up to
@@ -279,16 +285,33 @@ int64_t kda_test_prefill_flags(int64_t T_total, int N, int H, int d_k, int d_v, 
  * overlap an input or another output.  d_k, d_v each one of 32, 64, 128.
  * The gradient with respect to z and A of the gate follows from dg by the
  * chain rule of kda_gate's formula and is left to the caller.
- * Errors: KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED,
+ * Errors: KDA_ERR_INVALID_ARGUMENT (also a bad ckpt_interval with
+ * checkpoints), KDA_ERR_UNSUPPORTED (also T_total above
+ * KDA_BWD_MAX_TOKENS_WITHOUT_CKPT without checkpoints),
  * KDA_ERR_WORKSPACE_TOO_SMALL, KDA_ERR_HIP.
  */
+#define KDA_BWD_MAX_TOKENS_WITHOUT_CKPT 4096
 size_t kda_backward_workspace_size(int64_t T_total, int N, int H, int d_k, int d_v);
 kda_status_t kda_backward(const void* q, const void* k, const void* v, const void* g, const void* beta,
                           const int32_t* cu_seqlens, int N, int64_t T_total, int H, int d_k, int d_v,
                           const float* initial_state, const float* ckpt_states, int64_t ckpt_capacity,
-                          const void* d_o, const float* d_final_state, float* dq, float* dk, float* dv, float* dg,
-                          float* dbeta, float* d_initial_state, kda_dtype_t dtype, void* workspace,
-                          size_t workspace_bytes, void* stream);
+                          int ckpt_interval, const void* d_o, const float* d_final_state, float* dq, float* dk,
+                          float* dv, float* dg, float* dbeta, float* d_initial_state, kda_dtype_t dtype,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * TEST ONLY — kda_backward with its segment length given: seg_tokens > 0 cuts
+ * every sequence into segments of that many tokens (rounded up to whole
+ * 64-token chunks), 0 takes the planner's.  kda_test_backward_workspace_size
+ * is the workspace for the same choice.
+ */
+kda_status_t kda_test_backward(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                               const int32_t* cu_seqlens, int N, int64_t T_total, int H, int d_k, int d_v,
+                               const float* initial_state, const float* ckpt_states, int64_t ckpt_capacity,
+                               int ckpt_interval, const void* d_o, const float* d_final_state, float* dq, float* dk,
+                               float* dv, float* dg, float* dbeta, float* d_initial_state, kda_dtype_t dtype,
+                               void* workspace, size_t workspace_bytes, int64_t seg_tokens, void* stream);
+size_t kda_test_backward_workspace_size(int64_t T_total, int N, int H, int d_k, int d_v, int64_t seg_tokens);
 
 /*
  * Number of checkpoints kda_prefill_ckpt writes for these HOST cu_seqlens

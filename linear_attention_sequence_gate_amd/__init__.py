@@ -21,7 +21,8 @@ EXPORTED = ("kda_status_string", "kda_last_error", "kda_version", "kda_gate",
             "kda_prefill_workspace_size", "kda_prefill", "kda_decode_step", "kda_verify", "kda_commit",
             "kda_prefill_ckpt", "kda_checkpoint_count", "kda_prefill_gated", "kda_decode_step_gated",
             "kda_backward_workspace_size", "kda_backward", "kda_test_prefill", "kda_test_prefill_workspace_size",
-            "kda_test_prefill_flags", "kda_prefill_gated_noalloc")
+            "kda_test_prefill_flags", "kda_prefill_gated_noalloc", "kda_test_backward",
+            "kda_test_backward_workspace_size")
 
 _lib = None
 
@@ -68,8 +69,8 @@ def lib() -> ctypes.CDLL:
         L.kda_decode_step_gated.restype = I
         L.kda_backward_workspace_size.argtypes = [I64, I, I, I, I]
         L.kda_backward_workspace_size.restype = SZ
-        L.kda_backward.argtypes = [P, P, P, P, P, P, I, I64, I, I, I, P, P, I64, P, P, P, P, P, P, P, P, I, P, SZ,
-                                   P]
+        L.kda_backward.argtypes = [P, P, P, P, P, P, I, I64, I, I, I, P, P, I64, I, P, P, P, P, P, P, P, P, I, P,
+                                   SZ, P]
         L.kda_backward.restype = I
         L.kda_test_prefill.argtypes = [P, P, P, P, P, F, P, P, I, I64, I, I, I, P, P, P, I, P, SZ, I, P, I64, I, I,
                                        P]
@@ -81,6 +82,11 @@ def lib() -> ctypes.CDLL:
         L.kda_prefill_gated_noalloc.argtypes = [P, P, P, P, P, F, P, P, I, I64, I, I, I, I, P, P, P, I, I, P, I64,
                                                 P]
         L.kda_prefill_gated_noalloc.restype = I
+        L.kda_test_backward.argtypes = [P, P, P, P, P, P, I, I64, I, I, I, P, P, I64, I, P, P, P, P, P, P, P, P, I,
+                                        P, SZ, I64, P]
+        L.kda_test_backward.restype = I
+        L.kda_test_backward_workspace_size.argtypes = [I64, I, I, I, I, I64]
+        L.kda_test_backward_workspace_size.restype = SZ
         L.kda_checkpoint_count.argtypes = [P, I, I64, I]
         L.kda_checkpoint_count.restype = I64
         _lib = L
@@ -315,11 +321,13 @@ def kda_decode_step_gated(q, k, v, z, A, beta, state, o=None, g_min: float = -5.
 
 
 def kda_backward(q, k, v, g, beta, d_o=None, d_final_state=None, cu_seqlens=None, initial_state=None,
-                 ckpt=None, workspace=None, stream=None):
+                 ckpt=None, interval: int = 64, workspace=None, stream=None, seg_tokens: int | None = None):
     """Gradients of L = sum_t <d_o[t], o[t]> + <d_final_state, S_T> for kda_prefill on the
-    same inputs.  ckpt: the forward's checkpoints at interval 64 (or None: recomputed).
-    Returns a dict of fp32 tensors dq, dk, dg [T, H, d_k], dv [T, H, d_v], dbeta [T, H],
-    d_initial_state [N, H, d_k, d_v]."""
+    same inputs.  ckpt: the forward's checkpoints every `interval` tokens (64 is
+    the fast path; None: every chunk's state is rebuilt from the initial state,
+    for short inputs only).  seg_tokens (tests only) forces the segment length
+    through kda_test_backward.  Returns a dict of fp32 tensors dq, dk, dg
+    [T, H, d_k], dv [T, H, d_v], dbeta [T, H], d_initial_state [N, H, d_k, d_v]."""
     import torch
     _dense(q, k, v, g, beta, d_o, d_final_state, cu_seqlens, initial_state, ckpt, workspace)
     T, H, dk = k.shape
@@ -329,16 +337,22 @@ def kda_backward(q, k, v, g, beta, d_o=None, d_final_state=None, cu_seqlens=None
     f = lambda *shape: torch.empty(shape, dtype=torch.float32, device=dev)
     out = {"dq": f(T, H, dk), "dk": f(T, H, dk), "dv": f(T, H, dv), "dg": f(T, H, dk), "dbeta": f(T, H),
            "d_initial_state": f(N, H, dk, dv)}
-    need = int(lib().kda_backward_workspace_size(T, N, H, dk, dv))
+    if seg_tokens is None:
+        need = int(lib().kda_backward_workspace_size(T, N, H, dk, dv))
+    else:
+        need = int(lib().kda_test_backward_workspace_size(T, N, H, dk, dv, int(seg_tokens)))
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     wbytes = workspace.numel() * workspace.element_size()
     cap = 0 if ckpt is None else ckpt.shape[0]
-    _check(lib().kda_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N, T, H, dk, dv,
-                              _ptr(initial_state), _ptr(ckpt) if cap else None, cap, _ptr(d_o),
-                              _ptr(d_final_state), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
-                              _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out["d_initial_state"]), _dtype_code(k),
-                              _ptr(workspace), wbytes, _stream(stream)))
+    args = [_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N, T, H, dk, dv,
+            _ptr(initial_state), _ptr(ckpt) if cap else None, cap, int(interval), _ptr(d_o), _ptr(d_final_state),
+            _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]), _ptr(out["dbeta"]),
+            _ptr(out["d_initial_state"]), _dtype_code(k), _ptr(workspace), wbytes]
+    if seg_tokens is None:
+        _check(lib().kda_backward(*args, _stream(stream)))
+    else:
+        _check(lib().kda_test_backward(*args, int(seg_tokens), _stream(stream)))
     return out
 
 

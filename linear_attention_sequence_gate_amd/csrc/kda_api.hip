@@ -518,14 +518,15 @@ size_t kda_backward_workspace_size(int64_t T_total, int N, int H, int d_k, int d
     return kda::backward_plan(T_total, N, H, d_k, d_v).bytes;
 }
 
-kda_status_t kda_backward(const void* q, const void* k, const void* v, const void* g, const void* beta,
-                          const int32_t* cu_seqlens, int N, int64_t T_total, int H, int d_k, int d_v,
-                          const float* initial_state, const float* ckpt_states, int64_t ckpt_capacity,
-                          const void* d_o, const float* d_final_state, float* dq, float* dk, float* dv, float* dg,
-                          float* dbeta, float* d_initial_state, kda_dtype_t dtype, void* workspace,
-                          size_t workspace_bytes, void* stream)
+// seg_tokens > 0 fixes the segment length (the test entry point only)
+static kda_status_t backward_impl(const char* who, const void* q, const void* k, const void* v, const void* g,
+                                  const void* beta, const int32_t* cu_seqlens, int N, int64_t T_total, int H,
+                                  int d_k, int d_v, const float* initial_state, const float* ckpt_states,
+                                  int64_t ckpt_capacity, int ckpt_interval, const void* d_o,
+                                  const float* d_final_state, float* dq, float* dk, float* dv, float* dg,
+                                  float* dbeta, float* d_initial_state, kda_dtype_t dtype, void* workspace,
+                                  size_t workspace_bytes, void* stream, int64_t seg_tokens)
 {
-    const char* who = "kda_backward";
     if (N < 1 || T_total < 0 || H < 1)
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: bad sizes N=%d T_total=%lld H=%d", who, N, (long long)T_total, H);
     if (H > KDA_MAX_HEADS) return fail(KDA_ERR_UNSUPPORTED, "%s: H=%d > %d", who, H, KDA_MAX_HEADS);
@@ -539,7 +540,17 @@ kda_status_t kda_backward(const void* q, const void* k, const void* v, const voi
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: null token tensor", who);
     if (!d_initial_state) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: null d_initial_state", who);
     if (ckpt_capacity < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: negative checkpoint capacity", who);
-    const kda::BwdPlan plan = kda::backward_plan(T_total, N, H, d_k, d_v);
+    const bool have_ck = ckpt_states && ckpt_capacity > 0;
+    if (have_ck && (ckpt_interval <= 0 || ckpt_interval % kda::BWD_CHUNK != 0))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s: checkpoint interval %d is not a positive multiple of %d", who,
+                    ckpt_interval, kda::BWD_CHUNK);
+    // without checkpoints every 64-token chunk rebuilds its state from the
+    // sequence start: quadratic in the length, so long inputs are refused
+    if (!have_ck && T_total > KDA_BWD_MAX_TOKENS_WITHOUT_CKPT)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: %lld tokens without checkpoints (at most %d); pass the forward's "
+                    "checkpoints (kda_prefill_ckpt or kda_prefill_gated, interval 64 for the fast path)", who,
+                    (long long)T_total, KDA_BWD_MAX_TOKENS_WITHOUT_CKPT);
+    const kda::BwdPlan plan = kda::backward_plan(T_total, N, H, d_k, d_v, seg_tokens);
     const size_t need = plan.bytes;
     if (!workspace || workspace_bytes < need)
         return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes < %zu needed", who, workspace_bytes, need);
@@ -565,13 +576,48 @@ kda_status_t kda_backward(const void* q, const void* k, const void* v, const voi
                 return fail(KDA_ERR_INVALID_ARGUMENT, "%s: two outputs overlap", who);
     }
     kda::BackwardArgs a{q, k, v, g, beta, cu_seqlens, N, T_total, H, initial_state,
-                        ckpt_capacity > 0 ? ckpt_states : nullptr, ckpt_capacity, d_o, d_final_state,
+                        have_ck ? ckpt_states : nullptr, have_ck ? ckpt_capacity : 0,
+                        have_ck ? int64_t(ckpt_interval) : int64_t(kda::BWD_CHUNK), d_o, d_final_state,
                         dq, dk, dv, dg, dbeta, d_initial_state, static_cast<float*>(workspace), 0, nullptr,
                         nullptr};
     hipStream_t s = static_cast<hipStream_t>(stream);
     const hipError_t e = dtype == KDA_BF16 ? kda::launch_backward<kda::BF16>(a, plan, d_k, d_v, s)
                                            : kda::launch_backward<kda::F32>(a, plan, d_k, d_v, s);
     return from_hip(e, "kda_backward launch");
+}
+
+kda_status_t kda_backward(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                          const int32_t* cu_seqlens, int N, int64_t T_total, int H, int d_k, int d_v,
+                          const float* initial_state, const float* ckpt_states, int64_t ckpt_capacity,
+                          int ckpt_interval, const void* d_o, const float* d_final_state, float* dq, float* dk,
+                          float* dv, float* dg, float* dbeta, float* d_initial_state, kda_dtype_t dtype,
+                          void* workspace, size_t workspace_bytes, void* stream)
+{
+    return backward_impl("kda_backward", q, k, v, g, beta, cu_seqlens, N, T_total, H, d_k, d_v, initial_state,
+                         ckpt_states, ckpt_capacity, ckpt_interval, d_o, d_final_state, dq, dk, dv, dg, dbeta,
+                         d_initial_state, dtype, workspace, workspace_bytes, stream, 0);
+}
+
+size_t kda_test_backward_workspace_size(int64_t T_total, int N, int H, int d_k, int d_v, int64_t seg_tokens)
+{
+    if (seg_tokens < 0 || T_total < 0 || T_total > int64_t(0x7fffffff) || N < 1 || H < 1 || H > KDA_MAX_HEADS ||
+        !dim_ok(d_k) || !dim_ok(d_v))
+        return 0;
+    return kda::backward_plan(T_total, N, H, d_k, d_v, seg_tokens).bytes;
+}
+
+kda_status_t kda_test_backward(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                               const int32_t* cu_seqlens, int N, int64_t T_total, int H, int d_k, int d_v,
+                               const float* initial_state, const float* ckpt_states, int64_t ckpt_capacity,
+                               int ckpt_interval, const void* d_o, const float* d_final_state, float* dq, float* dk,
+                               float* dv, float* dg, float* dbeta, float* d_initial_state, kda_dtype_t dtype,
+                               void* workspace, size_t workspace_bytes, int64_t seg_tokens, void* stream)
+{
+    if (seg_tokens < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "kda_test_backward: seg_tokens=%lld",
+                                    (long long)seg_tokens);
+    return backward_impl("kda_test_backward", q, k, v, g, beta, cu_seqlens, N, T_total, H, d_k, d_v, initial_state,
+                         ckpt_states, ckpt_capacity, ckpt_interval, d_o, d_final_state, dq, dk, dv, dg, dbeta,
+                         d_initial_state, dtype, workspace, workspace_bytes, stream, seg_tokens);
 }
 
 int64_t kda_checkpoint_count(const int32_t* cu_seqlens_host, int N, int64_t T_total, int ckpt_interval)

@@ -33,8 +33,9 @@ struct BackwardArgs {
     int64_t T_total;
     int H;
     const float* init;      // [N, H, dk, dv] or null
-    const float* ckpt;      // checkpoints every 64 tokens, or null
+    const float* ckpt;      // the forward's checkpoints every ckpt_interval tokens, or null
     int64_t ckpt_cap;
+    int64_t ckpt_interval;  // a positive multiple of BWD_CHUNK
     const void* d_o;        // [T, H, dv] or null
     const float* d_fin;     // [N, H, dk, dv] or null
     float *dq, *dk, *dv, *dg, *dbeta, *d_init;
@@ -80,7 +81,7 @@ __device__ inline SegLoc bwd_locate(const BackwardArgs& a, int seg)
             return L;
         }
         acc += ns;
-        ck += (x - prev) / BWD_CHUNK;
+        ck += (x - prev) / a.ckpt_interval;
         prev = x;
     }
     return L;
@@ -184,7 +185,8 @@ struct BwdPlan {
 
 // Segment length: enough (segment, head) items to cover the compute units
 // about once (each runs its chunks in series), at least one 64-token chunk.
-inline BwdPlan backward_plan(int64_t T_total, int N, int H, int dk, int dv)
+// force_tokens > 0 fixes it instead (rounded up to whole chunks).
+inline BwdPlan backward_plan(int64_t T_total, int N, int H, int dk, int dv, int64_t force_tokens = 0)
 {
     BwdPlan p;
     const int64_t T = T_total > 0 ? T_total : 1;
@@ -194,10 +196,7 @@ inline BwdPlan backward_plan(int64_t T_total, int N, int H, int dk, int dv)
         const int64_t per = (T * H + int64_t(BWD_MAX_WG) * BWD_CHUNK - 1) / (int64_t(BWD_MAX_WG) * BWD_CHUNK);
         p.Lseg = BWD_CHUNK * (per > 0 ? per : 1);
     }
-    if (const char* e = getenv("KDA_BWD_SEG_TOKENS")) {  // tests: force a segment length
-        const long v = atol(e);
-        if (v > 0) p.Lseg = (v + BWD_CHUNK - 1) / BWD_CHUNK * BWD_CHUNK;
-    }
+    if (force_tokens > 0) p.Lseg = (force_tokens + BWD_CHUNK - 1) / BWD_CHUNK * BWD_CHUNK;
     p.segs_max = T / p.Lseg + 1 + N;  // >= the sum over sequences of max(1, ceil(len / Lseg))
     const int64_t items = p.segs_max * H;
     p.grid = int(items < BWD_MAX_WG ? items : BWD_MAX_WG);

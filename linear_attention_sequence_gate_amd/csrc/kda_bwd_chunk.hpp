@@ -618,15 +618,18 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
             const int64_t t0 = c0 + j * BWD_CHUNK;
             const int clen = int((L.t1 - t0) < BWD_CHUNK ? (L.t1 - t0) : BWD_CHUNK);
             const int nsub = (clen + BSUB - 1) / BSUB;
-            // the state before token t0: the checkpoint, or recomputed from the initial state
+            // the state before token t0: rebuilt from the nearest checkpoint at
+            // or before t0 that the buffer holds (with interval 64, the
+            // checkpoint at t0 itself), else from the initial state
             {
                 f32x4 S[NCT][CT];
                 const float* init = a.init ? a.init + unit * DK * DV : nullptr;
-                const int64_t ckrow = ck0 + j - 1;
-                const bool have_ck = j > 0 && a.ckpt && ckrow < a.ckpt_cap;
-                if (chain) load_tiles(S, have_ck ? a.ckpt + (ckrow * H + h) * DK * DV : init);
-                if (!have_ck)
-                    for (int64_t t = c0; t < t0; t += BSUB) fwd_sub(S, t, BSUB, h);
+                int64_t m = j * BWD_CHUNK / a.ckpt_interval;  // checkpoints of the sequence before t0
+                if (m > a.ckpt_cap - ck0) m = a.ckpt_cap - ck0;
+                const bool have_ck = a.ckpt && m >= 1;
+                const int64_t from = have_ck ? c0 + m * a.ckpt_interval : c0;
+                if (chain) load_tiles(S, have_ck ? a.ckpt + ((ck0 + m - 1) * H + h) * DK * DV : init);
+                for (int64_t t = from; t < t0; t += BSUB) fwd_sub(S, t, BSUB, h);
                 // forward through the chunk, keeping the state at each sub-chunk start
                 for (int s = 0; s < nsub; ++s) {
                     if (chain) {

@@ -314,13 +314,13 @@ def test_backward_validation(L):
 
     def call(**kw):
         a = dict(q=FAKE, k=FAKE + (1 << 20), v=FAKE + (2 << 20), g=FAKE + (3 << 20), beta=FAKE + (4 << 20),
-                 cu=None, N=N, T=T, H=H, dk=dk, dv=dv, init=None, ck=None, cap=0, do=FAKE + (5 << 20),
+                 cu=None, N=N, T=T, H=H, dk=dk, dv=dv, init=None, ck=None, cap=0, iv=64, do=FAKE + (5 << 20),
                  dfin=None, dq=FAKE + (8 << 20), dkk=FAKE + (9 << 20), dvv=FAKE + (10 << 20),
                  dg=FAKE + (11 << 20), db=FAKE + (12 << 20), dinit=FAKE + (13 << 20), dt=BF16,
                  ws=FAKE + (64 << 20), wsb=need)
         a.update(kw)
         return L.kda_backward(a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu"], a["N"], a["T"], a["H"],
-                              a["dk"], a["dv"], a["init"], a["ck"], a["cap"], a["do"], a["dfin"], a["dq"],
+                              a["dk"], a["dv"], a["init"], a["ck"], a["cap"], a["iv"], a["do"], a["dfin"], a["dq"],
                               a["dkk"], a["dvv"], a["dg"], a["db"], a["dinit"], a["dt"], a["ws"], a["wsb"], None)
 
     assert call(N=0) == 1
@@ -339,6 +339,28 @@ def test_backward_validation(L):
     assert call(dg=FAKE + (8 << 20) + 64) == 1              # dg overlaps dq
     assert call(ws=FAKE + (13 << 20)) == 1                  # workspace overlaps d_initial_state
     assert b"kda_backward" in L.kda_last_error()
+    # checkpoints come with a positive interval that is a multiple of 64
+    ck = dict(ck=FAKE + (32 << 20), cap=4)
+    assert call(iv=0, **ck) == 1
+    assert call(iv=96, **ck) == 1
+    assert b"interval" in L.kda_last_error()
+    # without checkpoints every chunk rebuilds its state from the sequence
+    # start (quadratic), so long inputs are refused; the interval is then ignored
+    T2 = 4097
+    big = L.kda_backward_workspace_size(T2, N, H, dk, dv)
+    far = dict(T=T2, wsb=big, q=FAKE, k=FAKE + (4 << 20), v=FAKE + (8 << 20), g=FAKE + (12 << 20),
+               beta=FAKE + (16 << 20), do=FAKE + (20 << 20), dq=FAKE + (32 << 20), dkk=FAKE + (40 << 20),
+               dvv=FAKE + (48 << 20), dg=FAKE + (56 << 20), db=FAKE + (64 << 20), dinit=FAKE + (68 << 20),
+               ws=FAKE + (72 << 20))
+    assert call(iv=0, **far) == 2
+    assert b"without checkpoints" in L.kda_last_error()
+    # the test entry point validates its segment length first
+    assert L.kda_test_backward(FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 256, 2, 64, 64, None, None, 0, 64, None, None,
+                               FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, BF16, FAKE, 1 << 30, -1, None) == 1
+    # 128 heads: the planner gives the sequence one segment; forced 64-token
+    # segments need a summary and an incoming gradient each
+    assert L.kda_test_backward_workspace_size(4096, 1, 128, 64, 64, 64) > L.kda_test_backward_workspace_size(
+        4096, 1, 128, 64, 64, 0) > 0
 
 
 def test_noalloc_limits(L):

@@ -25,7 +25,7 @@ def kda():
     return m
 
 
-def run_case(kda, wl, with_ckpt, heads=None, seed=5):
+def run_case(kda, wl, with_ckpt, heads=None, seed=5, interval=64, seg_tokens=None):
     """GPU backward of the prefill on wl's inputs (gate applied on the host by
     the oracle, so both sides take the same g), against the oracle on `heads`."""
     import torch
@@ -46,11 +46,11 @@ def run_case(kda, wl, with_ckpt, heads=None, seed=5):
     S0d = None if S0 is None else dev(S0)
     ck = None
     if with_ckpt:
-        _, _, ck = kda.kda_prefill_ckpt(d["q"], d["k"], d["v"], d["g"], d["beta"], 64, cu_seqlens=cu,
+        _, _, ck = kda.kda_prefill_ckpt(d["q"], d["k"], d["v"], d["g"], d["beta"], interval, cu_seqlens=cu,
                                         cu_seqlens_host=wl.cu_seqlens if wl.N > 1 else None,
                                         initial_state=S0d)
     out = kda.kda_backward(d["q"], d["k"], d["v"], d["g"], d["beta"], d_o=dev(dO, dt), d_final_state=dev(dS),
-                           cu_seqlens=cu, initial_state=S0d, ckpt=ck)
+                           cu_seqlens=cu, initial_state=S0d, ckpt=ck, interval=interval, seg_tokens=seg_tokens)
     torch.cuda.synchronize()
     hs = list(range(wl.H)) if heads is None else heads
     sel = lambda a: a[:, hs]
@@ -91,34 +91,54 @@ def test_backward_8k_sampled_heads(kda):
     run_case(kda, wl, with_ckpt=True, heads=[3, 29])
 
 
-class BwdSegEnv:
-    """Force the backward's segment length (tokens) for the library's planner."""
-
-    def __init__(self, tokens):
-        self.tokens = tokens
-
-    def __enter__(self):
-        import os
-        self.old = os.environ.get("KDA_BWD_SEG_TOKENS")
-        os.environ["KDA_BWD_SEG_TOKENS"] = str(self.tokens)
-
-    def __exit__(self, *a):
-        import os
-        if self.old is None:
-            os.environ.pop("KDA_BWD_SEG_TOKENS", None)
-        else:
-            os.environ["KDA_BWD_SEG_TOKENS"] = self.old
-
-
 @pytest.mark.parametrize("seg_tokens", [64, 192, 100000])
 def test_backward_segment_lengths(kda, seg_tokens):
     """Segments of 1 and 3 chunks (summary, scan, full pass per segment) and one
-    segment per sequence (no scan step)."""
+    segment per sequence (no scan step), through the test entry point."""
     wl = synth.VARLEN_64.with_(H=2, dk=64, dv=32, dtype="f32", seqlens=(500, 0, 64, 129),
                                state_std=0.1, z_shift=-2.0)
     announce(f"backward segments of {seg_tokens} tokens")
-    with BwdSegEnv(seg_tokens):
-        run_case(kda, wl, with_ckpt=False)
+    run_case(kda, wl, with_ckpt=False, seg_tokens=seg_tokens)
+
+
+@pytest.mark.parametrize("interval", [128, 512])
+def test_backward_sparse_checkpoints(kda, interval):
+    """Checkpoints every 128 or 512 tokens (the prefix cache's block): each
+    64-token chunk rebuilds its state from the nearest earlier row; varlen
+    lengths on both sides of the interval, segments of 3 chunks."""
+    wl = synth.VARLEN_64.with_(H=2, dk=64, dv=64, dtype="bf16", seqlens=(1500, 0, 511, 512, 700),
+                               state_std=0.1, z_shift=-2.0)
+    announce(f"backward from interval-{interval} checkpoints")
+    run_case(kda, wl, with_ckpt=True, interval=interval, seg_tokens=192)
+
+
+def test_backward_truncated_checkpoints(kda):
+    """A checkpoint buffer shorter than the forward wrote (rows past its end
+    are missing): the chunks past it rebuild from the last row it holds, or
+    from the initial state for sequences with no row in it."""
+    import torch
+    wl = synth.VARLEN_64.with_(H=2, dk=32, dv=32, dtype="f32", seqlens=(700, 300), state_std=0.1, z_shift=-2.0)
+    announce("backward, truncated checkpoint buffer")
+    x = synth.prefill_inputs(wl)
+    g = oracle.gate(x["z"], x["A"])
+    rng = np.random.default_rng(9)
+    S0 = synth.initial_state(wl)
+    dO = rng.standard_normal((wl.T_total, wl.H, wl.dv)).astype(np.float32)
+    dS = rng.standard_normal((wl.N, wl.H, wl.dk, wl.dv)).astype(np.float32)
+    cu = torch.from_numpy(wl.cu_seqlens).cuda()
+    d = {n: dev(x[n]) for n in ("q", "k", "v", "beta")}
+    d["g"] = dev(g)
+    _, _, ck = kda.kda_prefill_ckpt(d["q"], d["k"], d["v"], d["g"], d["beta"], 128, cu_seqlens=cu,
+                                    cu_seqlens_host=wl.cu_seqlens, initial_state=dev(S0))
+    assert ck.shape[0] == 5 + 2
+    out = kda.kda_backward(d["q"], d["k"], d["v"], d["g"], d["beta"], d_o=dev(dO), d_final_state=dev(dS),
+                           cu_seqlens=cu, initial_state=dev(S0), ckpt=ck[:3].contiguous(), interval=128)
+    torch.cuda.synchronize()
+    ref = oracle.backward(x["q"], x["k"], x["v"], g, x["beta"], dO=dO, dS_fin=dS, cu=wl.cu_seqlens, S0=S0)
+    for gname, rname in GRADS:
+        e = relerr(host(out[gname]), ref[rname])
+        print(f"  {gname}: {e:.3e}")
+        assert e < TOL["f32"]
 
 
 def test_backward_many_heads(kda):
