@@ -24,6 +24,15 @@ output with that oracle pass (whole workload, normwise max relative error).
 
 Before the W warmup steps the prefill step runs untimed for --spin-up seconds
 (0.5 by default) so that the timed steps see the GPU's steady clocks.
+
+Two more legs time the million-token workloads: `prefill_1m` (one sequence,
+H=8, T=2^20, z shifted by +3) and `varlen_64` (64 packed sequences, ~1.03M
+tokens, H=32, initial states N(0, 0.01)), each one kda_prefill_gated call on
+seeded inputs drawn on the device (the same distributions as the tests'), with
+its HBM roofline and an oracle check on sampled heads and sequences.
+`measured_roofs` holds the device's own streaming bandwidth (read, write and
+copy kernels) and bf16 matrix-core issue rate (libkda_roofs), against which
+every roofline also reports a fraction.
 """
 from __future__ import annotations
 
@@ -65,14 +74,16 @@ def load_traffic(kind: str):
     return d.get("bytes_per_call")
 
 
-def prefill_algo(T: int, H: int, dk: int, dv: int, chunk: int = 64):
+def prefill_algo(T: int, H: int, dk: int, dv: int, chunk: int = 64, N: int = 1, with_init: bool = False):
     """Algorithmic HBM bytes and flops of one prefill call (bf16 tokens, fp32 state).
 
-    bytes: q, k, g, v, beta read once, o written once, final state written.
+    bytes: q, k, g, v, beta read once, o written once, the N final states
+    written (and the N initial states read, with_init).
     flops: per token and head, C*(3*dk + 2*dv) + 6*dk*dv for the chunkwise form
     with triangular intra-chunk products (2 flops per multiply-add)."""
     tok = T * H
-    nbytes = tok * (3 * dk + dv + 1) * 2 + tok * dv * 2 + H * dk * dv * 4
+    states = N * H * dk * dv * 4
+    nbytes = tok * (3 * dk + dv + 1) * 2 + tok * dv * 2 + states * (2 if with_init else 1)
     flops = tok * (chunk * (3 * dk + 2 * dv) + 6 * dk * dv)
     return nbytes, flops
 
@@ -103,32 +114,62 @@ def backward_algo(T: int, H: int, dk: int, dv: int, interval: int = 64):
             + 2 * H * dk * dv * 4)
 
 
+CPU_SHARE = 16  # host threads a one-GPU machine gives a job, whatever the machine has
+
+
+def host_cpu() -> dict:
+    """What the CPU baseline ran on: the machine's logical CPUs, the ones this
+    process may use, and the model name."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        allowed = len(os.sched_getaffinity(0))
+    except AttributeError:
+        allowed = os.cpu_count()
+    return {"logical_cpus": os.cpu_count(), "allowed_cpus": allowed, "model": model}
+
+
 def cpu_baseline(wl, seconds: float = 12.0):
     """The fp64 oracle on this host over the whole 8K workload (every head,
-    every token), repeated until at least `seconds` of CPU time have passed;
-    tokens/s of the full problem.  Also returns the first pass's (o, S): the
-    oracle's result for input set 0 (bf16-rounded inputs, as the GPU holds
-    them; g from the gate in fp64, unrounded, as the fused gate keeps it),
-    against which the timed run's output is checked."""
+    every token), repeated until at least `seconds` have passed; tokens/s of
+    the full problem.  The oracle is compiled here for this host (gcc -O3
+    -march=native, OpenMP) and runs one thread per head, up to the host share
+    of CPUs.  Also returns the first pass's (o, S): the oracle's result for
+    input set 0 (bf16-rounded inputs, as the GPU holds them; g from the gate
+    in fp64, unrounded, as the fused gate keeps it), against which the timed
+    run's output is checked."""
+    import tempfile
     import oracle
     import synth
-    threads = oracle.default_threads()
+    cpu = host_cpu()
+    threads = max(1, min(wl.H, CPU_SHARE, cpu["allowed_cpus"] or 1))
+    out = os.path.join(tempfile.mkdtemp(prefix="kda_oracle_"), "liboracle_native.so")
+    oracle.build(out=out, native=True)
+    lib = oracle.load(out)
     x = synth.prefill_inputs(wl)
     for n in ("q", "k", "v", "z", "beta"):
-        x[n] = oracle.round_bf16(x[n])
-    g = oracle.gate(x["z"], x["A"])  # the fused gate keeps g in fp32
+        x[n] = oracle.round_bf16(x[n], lib=lib)
+    g = oracle.gate(x["z"], x["A"], lib=lib)  # the fused gate keeps g in fp32
     reps, first, t0 = 0, None, time.perf_counter()
     while True:
-        res = oracle.prefill(x["q"], x["k"], x["v"], g, x["beta"], threads=threads)
+        res = oracle.prefill(x["q"], x["k"], x["v"], g, x["beta"], threads=threads, lib=lib)
         first = first or res
         reps += 1
         dt = time.perf_counter() - t0
         if dt >= seconds:
             break
     return ({"value": round(reps * wl.T_total / dt, 1), "unit": "tokens/s", "cores": threads,
-             "kind": "oracle",
+             "threads": threads, "kind": "oracle", "build": "gcc -O3 -march=native -fopenmp, built on this host",
+             "host": cpu,
              "sample": f"fp64 token-serial oracle on the whole 8K workload ({wl.H} heads x "
-                       f"{wl.T_total} tokens), {reps} passes in {dt:.1f} s"}, first)
+                       f"{wl.T_total} tokens, one head per thread), {reps} passes in {dt:.1f} s"}, first)
 
 
 def max_rel_err(got, want) -> float:
@@ -137,6 +178,122 @@ def max_rel_err(got, want) -> float:
     got = np.asarray(got, dtype=np.float64)
     want = np.asarray(want, dtype=np.float64)
     return float(np.max(np.abs(got - want)) / max(float(np.max(np.abs(want))), 1e-300))
+
+
+def measured_roofs(torch, dev, stream) -> dict:
+    """Streaming read, write and copy bandwidth over 4 GiB and the bf16
+    matrix-core issue rate, measured with libkda_roofs on this device."""
+    import ctypes
+    from linear_attention_sequence_gate_amd import build as kbuild
+    L = ctypes.CDLL(kbuild.ROOFS_LIB)
+    P, I, I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+    L.kda_roof_stream.argtypes = [I, P, P, I64, P, I64, I, I, P, ctypes.POINTER(ctypes.c_float)]
+    L.kda_roof_mfma.argtypes = [I, I, P, P, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_double)]
+    nbytes = 4 << 30
+    wgs = 256 * 16
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    sink = torch.empty(wgs * 256, dtype=torch.int32, device=dev)
+    ms = ctypes.c_float(0.0)
+    out = {}
+    for mode, name, moved in ((0, "hbm_read_gbs", nbytes), (1, "hbm_write_gbs", nbytes), (2, "hbm_copy_gbs", 2 * nbytes)):
+        rc = L.kda_roof_stream(mode, src.data_ptr(), dst.data_ptr(), nbytes, sink.data_ptr(), sink.numel(), wgs, 5,
+                               stream.cuda_stream, ctypes.byref(ms))
+        if rc != 0:
+            raise RuntimeError(f"kda_roof_stream mode {mode}: {rc}")
+        out[name] = round(moved / (ms.value * 1e-3) / 1e9, 1)
+    del src, dst
+    fsink = torch.empty(256 * 8 * 256, dtype=torch.float32, device=dev)
+    fl = ctypes.c_double(0.0)
+    rc = L.kda_roof_mfma(256 * 8, 4096, fsink.data_ptr(), stream.cuda_stream, ctypes.byref(ms), ctypes.byref(fl))
+    if rc != 0:
+        raise RuntimeError(f"kda_roof_mfma: {rc}")
+    out["mfma_bf16_tflops"] = round(fl.value / (ms.value * 1e-3) / 1e12, 1)
+    out["how"] = ("libkda_roofs: 16-byte vector loads/stores over 4 GiB, 4096 workgroups of 256, streaming "
+                  "stores, mean of 5 launches (copy counts read + write bytes); 2048 workgroups of 4 waves, "
+                  "each issuing 4096 x 8 independent v_mfma_f32_16x16x32_bf16")
+    return out
+
+
+def device_inputs(torch, wl, dev, seed):
+    """The workload's token tensors drawn on the device (seeded torch
+    generator, the distributions of the seeded host generator): q, k ~ N(0,1)
+    L2-normalised per (token, head), v ~ N(0,1), z ~ N(shift, 1),
+    beta = sigmoid(N(0,1)), all rounded once to bf16; drawn in windows so the
+    fp32 temporaries stay small."""
+    gen = torch.Generator(device=dev).manual_seed(seed)
+    T, H = wl.T_total, wl.H
+    out = {n: torch.empty((T, H, wl.dv if n == "v" else wl.dk), dtype=torch.bfloat16, device=dev)
+           for n in ("q", "k", "v", "z")}
+    out["beta"] = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    step = 1 << 16
+    for t0 in range(0, T, step):
+        t1 = min(T, t0 + step)
+        for n in ("q", "k"):
+            x = torch.randn((t1 - t0, H, wl.dk), generator=gen, device=dev)
+            out[n][t0:t1] = (x / x.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+        out["v"][t0:t1] = torch.randn((t1 - t0, H, wl.dv), generator=gen, device=dev).to(torch.bfloat16)
+        out["z"][t0:t1] = (torch.randn((t1 - t0, H, wl.dk), generator=gen, device=dev) + wl.z_shift).to(
+            torch.bfloat16)
+        out["beta"][t0:t1] = torch.sigmoid(torch.randn((t1 - t0, H), generator=gen, device=dev)).to(torch.bfloat16)
+    return out
+
+
+def big_leg(kda, torch, synth, wl, dev, stream, timed_loop, copy_gbs, roof_ms, steps=5):
+    """One million-token workload: one kda_prefill_gated call per step, timed
+    over `steps` back-to-back calls, with its HBM roofline and an oracle check
+    of sampled outputs and final states the fp64 oracle computes exactly."""
+    import numpy as np
+    import oracle
+    T, H, dk, dv, N = wl.T_total, wl.H, wl.dk, wl.dv, wl.N
+    x = device_inputs(torch, wl, dev, wl.seed)
+    A = torch.from_numpy(synth.gate_A(wl)).to(dev)
+    cu = torch.from_numpy(wl.cu_seqlens).to(dev) if N > 1 else None
+    S0 = torch.from_numpy(synth.initial_state(wl)).to(dev) if wl.state_std > 0 else None
+    o = torch.empty((T, H, dv), dtype=torch.bfloat16, device=dev)
+    S = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(kda.kda_prefill_workspace_size(T, N, H, dk, dv), 1), dtype=torch.uint8, device=dev)
+
+    def call(i):
+        kda.kda_prefill_gated(x["q"], x["k"], x["v"], x["z"], A, x["beta"], cu_seqlens=cu, initial_state=S0,
+                              final_state=S, o=o, workspace=ws)
+
+    for i in range(2):
+        call(i)
+    ms = timed_loop(call, steps)
+    nbytes, flops = prefill_algo(T, H, dk, dv, N=N, with_init=S0 is not None)
+    ach = nbytes / (ms * 1e-3) / 1e9
+    # oracle check on samples: outputs from the sequence start (exact from the
+    # known initial state) and whole short sequences with their final states
+    hx = lambda t: t.float().cpu().numpy()
+    Ah = synth.gate_A(wl)
+    heads = [0, H // 2 + 1]
+    errs = {}
+    cuh = wl.cu_seqlens
+    picks = [0] if N == 1 else [int(n) for n in np.argsort(np.asarray(wl.seqlens))[:2]]
+    for n in picks:
+        a = int(cuh[n])
+        b = min(int(cuh[n + 1]), a + 8192)
+        xs = {k_: hx(x[k_][a:b][:, heads]) for k_ in ("q", "k", "v", "z")}
+        xs["beta"] = hx(x["beta"][a:b][:, heads])
+        g = oracle.gate(xs["z"], Ah[heads])
+        s0 = None if S0 is None else S0[n:n + 1][:, heads].cpu().numpy()
+        o_ref, S_ref = oracle.prefill(xs["q"], xs["k"], xs["v"], g, xs["beta"], S0=s0)
+        errs[f"seq{n}_heads{heads}_o_tokens_{b - a}"] = max_rel_err(hx(o[a:b][:, heads]), o_ref)
+        if b == int(cuh[n + 1]):
+            errs[f"seq{n}_heads{heads}_final_state"] = max_rel_err(S[n, heads].cpu().numpy(), S_ref[0])
+    del x, ws
+    return {"value": round(T / (ms * 1e-3), 1), "unit": "tokens/s", "ms_per_call": round(ms, 4), "steps": steps,
+            "config": {"workload": wl.name, "N": N, "H": H, "T": T, "d_k": dk, "d_v": dv, "z_shift": wl.z_shift,
+                       "initial_state": S0 is not None, "inputs": "drawn on the device, seeded"},
+            "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(ach / HBM_PEAK_GBS, 4), "frac_of_measured_copy": round(ach / copy_gbs, 4),
+                         "binding_roof_ms": roof_ms, "algorithmic_bytes_per_call": nbytes,
+                         "mfma_tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+                         "traffic": load_traffic(wl.name), "kernel": "kda_prefill_gated"},
+            "verified": {"against": "fp64 oracle on sampled heads and sequences (exact from their initial state)",
+                         "max_rel_err": errs, "tolerance": 2e-2}}
 
 
 def main():
@@ -148,6 +305,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--spin-up", type=float, default=SPIN_UP_S,
                     help="seconds of untimed steps before the warmup steps (clock ramp)")
+    ap.add_argument("--no-big", action="store_true", help="skip the million-token legs")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -251,7 +409,8 @@ def main():
     traffic = load_traffic("prefill_8k")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "kda_prefill_gated (segment summary + scan + chunk kernels, gate in the decay stage)",
+                "kernel": "kda_prefill_gated: prefill_warm_kernel (segments with warm-up windows, gate in the "
+                          "decay stage) + the flag-gated exact passes, which end at once here",
                 "algorithmic_bytes_per_call": p_bytes, "ms_per_call": round(ms_step, 4),
                 "mfma_tflops": round(p_flops / (ms_step * 1e-3) / 1e12, 1),
                 "mfma_frac": round(p_flops / (ms_step * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)}
@@ -391,24 +550,22 @@ def main():
                              "peak": HBM_PEAK_GBS, "unit": "GB/s",
                              "frac": round(b_bytes / (b_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 5),
                              "kernel": "bwd_chunk_summary_kernel + bwd_scan_kernel + bwd_chunk_full_kernel",
+                             "traffic": load_traffic("backward_8k"),
                              "algorithmic_bytes_per_call": b_bytes}}
     del bws, bck
 
-    # achievable HBM bandwidth on this device: a plain 1 GiB device-to-device
-    # copy (2 GiB moved per copy), for fractions against a measured roof too
-    csrc = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-    cdst = torch.empty_like(csrc)
-    for _ in range(3):
-        cdst.copy_(csrc)
-    copy_ms = timed_loop(lambda i: cdst.copy_(csrc), 10)
-    copy_gbs = 2.0 * (1 << 30) / (copy_ms * 1e-3) / 1e9
-    del csrc, cdst
-    for r in (roofline, decode["roofline"], spec["verify"]["roofline"], spec["commit"]["roofline"]):
+    # the device's own roofs: streaming read / write / copy kernels over 4 GiB
+    # (far past the 256 MB last-level cache) and back-to-back 16x16x32 bf16
+    # matrix-core instructions on every SIMD (libkda_roofs)
+    roofs = measured_roofs(torch, dev, stream)
+    copy_gbs = roofs["hbm_copy_gbs"]
+    for r in (roofline, decode["roofline"], spec["verify"]["roofline"], spec["commit"]["roofline"],
+              backward["roofline"]):
         r["measured_copy_gbs"] = round(copy_gbs, 1)
         r["frac_of_measured_copy"] = round(r["achieved"] / copy_gbs, 4)
-    # achievable bf16 matrix-core rate on this device: a plain 8192^3 bf16 GEMM
-    # (the vendor library), for the prefill's MFMA fraction against a measured
-    # rate as well as the published peak
+    roofline["measured_mfma_bf16_tflops"] = roofs["mfma_bf16_tflops"]
+    roofline["mfma_frac_of_measured_mfma"] = round(roofline["mfma_tflops"] / roofs["mfma_bf16_tflops"], 4)
+    # a plain 8192^3 bf16 GEMM through the vendor library, for reference
     ga = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
     gb = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
     gc = torch.empty(8192, 8192, device=dev, dtype=torch.bfloat16)
@@ -417,8 +574,13 @@ def main():
     gemm_ms = timed_loop(lambda i: torch.mm(ga, gb, out=gc), 10)
     gemm_tflops = 2.0 * 8192 ** 3 / (gemm_ms * 1e-3) / 1e12
     del ga, gb, gc
-    roofline["measured_gemm_tflops"] = round(gemm_tflops, 1)
-    roofline["mfma_frac_of_measured_gemm"] = round(roofline["mfma_tflops"] / gemm_tflops, 4)
+    roofs["vendor_gemm_bf16_tflops"] = round(gemm_tflops, 1)
+
+    # ------------------------------------------- million-token workloads
+    big = {}
+    if not args.no_big:
+        big["prefill_1m"] = big_leg(kda, torch, synth, synth.PREFILL_1M, dev, stream, timed_loop, copy_gbs, 1.34)
+        big["varlen_64"] = big_leg(kda, torch, synth, synth.VARLEN_64, dev, stream, timed_loop, copy_gbs, 5.1)
 
     if args.copy_calib:  # plain copy of known size, for the HBM counter calibration
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -444,7 +606,7 @@ def main():
            "roofline": roofline, "cpu_baseline": cpu, "verified": verified, "unfused": unfused,
            "checkpoints": ckpt_leg,
            "decode": decode,
-           "speculative": spec, "backward": backward,
+           "speculative": spec, "backward": backward, "million_token": big, "measured_roofs": roofs,
            "wall_s": round(wall, 3), "source_hash": kernel_source_hash()}
     print(json.dumps(out), flush=True)
 

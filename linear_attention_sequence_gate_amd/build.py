@@ -1,4 +1,5 @@
-"""Build libkda.so (hipcc, gfx950) in place, next to this file."""
+"""Build libkda.so (hipcc, gfx950) in place, next to this file, and the
+measurement library libkda_roofs.so (the benchmark's roofs)."""
 from __future__ import annotations
 
 import os
@@ -10,6 +11,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkda.so")
 SOURCES = [os.path.join(CSRC, "kda_api.hip")]
+ROOFS_LIB = os.path.join(HERE, "libkda_roofs.so")
+ROOFS_SOURCES = [os.path.join(CSRC, "kda_roofs.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -20,21 +23,28 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False, extra: list[str] | None = None) -> str:
+def _compile(sources: list[str], out: str, verbose: bool, extra: list[str] | None) -> str:
     cmd = [HIPCC, *FLAGS, *(extra or []), "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           *SOURCES, "-o", LIB + ".tmp"]
+           *sources, "-o", out + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)
+    dst = out
     r = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
                     if "packed-fp32-ops" not in l)
     if r.returncode != 0:
         sys.stderr.write(out + "\n")
-        raise RuntimeError("libkda build failed")
+        raise RuntimeError(f"{os.path.basename(dst)} build failed")
     if verbose and out.strip():
         print(out)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(dst + ".tmp", dst)
+    return dst
+
+
+def build(verbose: bool = False, extra: list[str] | None = None) -> str:
+    """Compile libkda.so and libkda_roofs.so; returns libkda's path."""
+    _compile(ROOFS_SOURCES, ROOFS_LIB, verbose, extra)
+    return _compile(SOURCES, LIB, verbose, extra)
 
 
 if __name__ == "__main__":

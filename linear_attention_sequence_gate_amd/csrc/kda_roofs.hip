@@ -1,0 +1,155 @@
+// libkda_roofs: measurement kernels for the rooflines the benchmark reports
+// against (not part of libkda's path).  Each entry point times its own
+// launches with HIP events on the given stream and returns the mean
+// milliseconds per launch; the caller turns that into GB/s or TFLOP/s.
+//   kda_roof_stream : read, write or copy of a device buffer with 16-byte
+//                     vector accesses, grid-stride, streaming (non-temporal)
+//                     stores, many workgroups per compute unit.
+//   kda_roof_mfma   : back-to-back independent 16x16x32 bf16 matrix-core
+//                     instructions on every SIMD (the issue ceiling of the
+//                     instruction the prefill's products use).
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "kda_roofs.h"
+
+namespace {
+
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+
+// mode 0: read (each thread folds what it reads into one word, written once
+// per thread so the loads cannot be dropped), 1: write, 2: copy
+template <int MODE>
+__global__ void __launch_bounds__(256) stream_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                     int64_t n, uint32_t* __restrict__ sink)
+{
+    const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+    int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    uint32_t acc = 0;
+    for (; i + 3 * stride < n; i += 4 * stride) {  // four independent vectors in flight per thread
+        if constexpr (MODE == 1) {
+            const u32x4 w = {uint32_t(i), 0u, 0u, 0u};
+            __builtin_nontemporal_store(w, dst + i);
+            __builtin_nontemporal_store(w, dst + i + stride);
+            __builtin_nontemporal_store(w, dst + i + 2 * stride);
+            __builtin_nontemporal_store(w, dst + i + 3 * stride);
+        } else {
+            const u32x4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+            if constexpr (MODE == 0) {
+                acc ^= a[0] ^ a[1] ^ a[2] ^ a[3] ^ b[0] ^ b[1] ^ b[2] ^ b[3];
+                acc ^= c[0] ^ c[1] ^ c[2] ^ c[3] ^ d[0] ^ d[1] ^ d[2] ^ d[3];
+            } else {
+                __builtin_nontemporal_store(a, dst + i);
+                __builtin_nontemporal_store(b, dst + i + stride);
+                __builtin_nontemporal_store(c, dst + i + 2 * stride);
+                __builtin_nontemporal_store(d, dst + i + 3 * stride);
+            }
+        }
+    }
+    for (; i < n; i += stride) {
+        if constexpr (MODE == 1) {
+            __builtin_nontemporal_store(u32x4{uint32_t(i), 0u, 0u, 0u}, dst + i);
+        } else {
+            const u32x4 a = src[i];
+            if constexpr (MODE == 0) acc ^= a[0] ^ a[1] ^ a[2] ^ a[3];
+            else __builtin_nontemporal_store(a, dst + i);
+        }
+    }
+    if constexpr (MODE == 0) sink[int64_t(blockIdx.x) * blockDim.x + threadIdx.x] = acc;
+}
+
+// Each wave keeps NACC independent accumulators and issues ITERS rounds of
+// NACC matrix instructions; the results are folded into one word per lane so
+// nothing is dead code.
+constexpr int NACC = 8;
+__global__ void __launch_bounds__(256) mfma_kernel(int iters, float* __restrict__ sink)
+{
+    const int lane = threadIdx.x & 63;
+    bf16x8 a, b;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        a[e] = (__bf16)(0.001f * float(lane + e));
+        b[e] = (__bf16)(0.002f * float(lane - e));
+    }
+    f32x4 acc[NACC];
+#pragma unroll
+    for (int j = 0; j < NACC; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int j = 0; j < NACC; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[j], 0, 0, 0);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < NACC; ++j) s += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
+    sink[int64_t(blockIdx.x) * blockDim.x + threadIdx.x] = s;
+}
+
+// Mean milliseconds per launch of `reps` back-to-back launches of `launch`
+// on stream s, between two events; 0 on success, 2 on a HIP error.
+template <typename F>
+int timed(F&& launch, int reps, hipStream_t s, float* ms_per_launch)
+{
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    hipError_t e = hipEventCreate(&e0);
+    if (e == hipSuccess) e = hipEventCreate(&e1);
+    if (e == hipSuccess) e = hipEventRecord(e0, s);
+    if (e == hipSuccess) {
+        for (int r = 0; r < reps; ++r) launch();
+        e = hipGetLastError();
+    }
+    if (e == hipSuccess) e = hipEventRecord(e1, s);
+    if (e == hipSuccess) e = hipEventSynchronize(e1);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+    if (e0) (void)hipEventDestroy(e0);
+    if (e1) (void)hipEventDestroy(e1);
+    if (e != hipSuccess) return 2;
+    *ms_per_launch = ms / float(reps);
+    return 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_roof_stream(int mode, const void* src, void* dst, int64_t bytes, void* sink, int64_t sink_words,
+                    int workgroups, int reps, void* stream, float* ms_per_launch)
+{
+    if (mode < 0 || mode > 2 || bytes < 16 || bytes % 16 != 0 || workgroups < 1 || reps < 1 || !ms_per_launch)
+        return 1;
+    if ((mode != 1 && !src) || (mode != 0 && !dst)) return 1;
+    if (mode == 0 && (!sink || sink_words < int64_t(workgroups) * 256)) return 1;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t n = bytes / 16;
+    const u32x4* in = static_cast<const u32x4*>(src);
+    u32x4* out = static_cast<u32x4*>(dst);
+    uint32_t* sk = static_cast<uint32_t*>(sink);
+    auto launch = [&]() {
+        if (mode == 0) hipLaunchKernelGGL(stream_kernel<0>, dim3(workgroups), dim3(256), 0, s, in, out, n, sk);
+        else if (mode == 1) hipLaunchKernelGGL(stream_kernel<1>, dim3(workgroups), dim3(256), 0, s, in, out, n, sk);
+        else hipLaunchKernelGGL(stream_kernel<2>, dim3(workgroups), dim3(256), 0, s, in, out, n, sk);
+    };
+    launch();  // first launch loads the code object
+    if (hipGetLastError() != hipSuccess) return 2;
+    return timed(launch, reps, s, ms_per_launch);
+}
+
+int kda_roof_mfma(int workgroups, int iters, void* sink, void* stream, float* ms_per_launch, double* flops_per_launch)
+{
+    if (workgroups < 1 || iters < 1 || !sink || !ms_per_launch || !flops_per_launch) return 1;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    float* sk = static_cast<float*>(sink);
+    auto launch = [&]() { hipLaunchKernelGGL(mfma_kernel, dim3(workgroups), dim3(256), 0, s, iters, sk); };
+    launch();
+    if (hipGetLastError() != hipSuccess) return 2;
+    const int r = timed(launch, 1, s, ms_per_launch);
+    if (r != 0) return r;
+    // 4 waves per workgroup, NACC instructions per round, 16*16*32 multiply-adds each
+    *flops_per_launch = double(workgroups) * 4.0 * double(iters) * NACC * 2.0 * 16 * 16 * 32;
+    return 0;
+}
+
+}  // extern "C"

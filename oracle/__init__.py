@@ -23,9 +23,13 @@ LIB = os.path.join(HERE, "liboracle.so")
 _lib = None
 
 
-def build(src: str = SRC, out: str = LIB) -> str:
-    """Compile the oracle (gcc, -O2, OpenMP, a portable x86-64-v3 target)."""
-    cmd = ["gcc", "-O2", "-march=x86-64-v3", "-fopenmp", "-fPIC", "-shared",
+def build(src: str = SRC, out: str = LIB, native: bool = False) -> str:
+    """Compile the oracle with gcc and OpenMP: -O2 for a portable x86-64-v3
+    target (the copy the tests load, which may run on another host than the
+    one it was built on), or -O3 -march=native for the host it is built on
+    (the benchmark's CPU baseline builds its own)."""
+    arch = ["-O3", "-march=native"] if native else ["-O2", "-march=x86-64-v3"]
+    cmd = ["gcc", *arch, "-fopenmp", "-fPIC", "-shared",
            "-std=c11", "-o", out + ".tmp", src, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(out + ".tmp", out)

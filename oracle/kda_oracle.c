@@ -44,6 +44,7 @@
 void oracle_gate(const double* z, const double* A, int64_t n_tok, int H, int dk,
                  double g_min, double* g)
 {
+#pragma omp parallel for schedule(static)
     for (int64_t t = 0; t < n_tok; ++t)
         for (int h = 0; h < H; ++h) {
             const double s = exp(A[h]);

@@ -77,3 +77,21 @@ def gated_prefill(kda, q, k, v, z, A, beta, seg=None, warm=-1, interval=0, **kw)
     o, S, ck, _ = kda.kda_test_prefill(q, k, v, z, beta, A=A, interval=interval, seg_chunks=seg or 0,
                                        warm_tokens=warm, **kw)
     return (o, S, ck) if interval > 0 else (o, S)
+
+
+_native = None
+
+
+def native_oracle():
+    """The oracle compiled for the host the tests run on (gcc -O3
+    -march=native, into a temporary directory): the same source as the
+    portable copy, faster on the full-size workloads."""
+    global _native
+    if _native is None:
+        import os
+        import tempfile
+        import oracle
+        out = os.path.join(tempfile.mkdtemp(prefix="kda_oracle_"), "liboracle_native.so")
+        oracle.build(out=out, native=True)
+        _native = oracle.load(out)
+    return _native

@@ -7,6 +7,10 @@ deliberately broken copies of the oracle (tests/test_oracle_mutants.py).
   gate_closed_forms      g(0) = g_min/2; g(z) + g(-z) = g_min; saturation at g_min
                          and 0; agreement with scipy's expit; the printed
                          "at most 99.33% forgotten per step" (tests/golden).
+  gate_metamorphic       the per-head scale enters only as e^{A_h} z: g(z, A) =
+                         g(e^{A} z, 0) with e^{A} from numpy; g(z, ln 2) =
+                         g(2z, 0); g(z, -1) = g(z/e, 0); g(+-ln 3, 0) =
+                         -5 * (3/4, 1/4) exactly.
   bf16_rounding          nearest-bf16 rounding against a brute-force search.
   brute_force_T_le_4     the recurrence as a Kronecker-vectorised affine map
                          (dense (dk*dv+1)^2 matrices), T <= 4.
@@ -88,6 +92,29 @@ def gate_closed_forms(lib):
     alpha_min = float(np.min(np.exp(oracle.gate(np.full((1, 3, 1), 1000.0), A, lib=lib))))
     forget = round(100.0 * (1.0 - alpha_min), gold["printed_decimals"])
     assert forget == gold["max_forget_percent_printed"], f"max forgetting {forget}%"
+
+
+def gate_metamorphic(lib):
+    """The head's parameter only rescales the pre-activation: with e^{A_h}
+    computed independently (numpy), g(z, A) = g(e^{A} z, 0), so a gate that
+    drops the exponential, flips its sign or applies A elsewhere fails."""
+    rng = np.random.default_rng(17)
+    A = np.array([-1.0, -0.3, 0.0, 0.5, 1.0])
+    z = rng.uniform(-4, 4, (50, 5, 6))
+    g = oracle.gate(z, A, lib=lib)
+    scaled = np.exp(A)[None, :, None] * z
+    g0 = oracle.gate(scaled, np.zeros(5), lib=lib)
+    _close(g, g0, 1e-14, "g(z, A) = g(e^A z, 0)")
+    # exact special scales: A = ln 2 doubles z, A = -1 divides it by e
+    g2 = oracle.gate(z[:, :1], np.array([np.log(2.0)]), lib=lib)
+    _close(g2, oracle.gate(2.0 * z[:, :1], np.zeros(1), lib=lib), 1e-14, "g(z, ln 2) = g(2z, 0)")
+    gm = oracle.gate(z[:, :1], np.array([-1.0]), lib=lib)
+    _close(gm, oracle.gate(z[:, :1] / np.e, np.zeros(1), lib=lib), 1e-14, "g(z, -1) = g(z/e, 0)")
+    # and A = 0 is the plain sigmoid scaled by g_min, at a few exact points:
+    # sigmoid(ln 3) = 3/4, sigmoid(-ln 3) = 1/4
+    pts = np.array([np.log(3.0), -np.log(3.0)]).reshape(2, 1, 1)
+    _close(oracle.gate(pts, np.zeros(1), lib=lib).ravel(), np.array([-3.75, -1.25]), 1e-15,
+           "g(+-ln 3, 0) = -5 * (3/4, 1/4)")
 
 
 def _bf16_brute(x: float) -> float:
@@ -321,6 +348,6 @@ def backward_vs_finite_differences(lib):
         _close(grads[gname], num, 1e-7, f"backward {gname} vs finite differences")
 
 
-ALL_PINS = [gate_closed_forms, bf16_rounding, brute_force_T_le_4, beta_zero_pure_decay,
+ALL_PINS = [gate_closed_forms, gate_metamorphic, bf16_rounding, brute_force_T_le_4, beta_zero_pure_decay,
             exact_recall, delta_overwrite, linearity_kcp, chunked_equals_serial,
             wy_solve_vs_scipy, decode_equals_prefill, varlen_independent, backward_vs_finite_differences]

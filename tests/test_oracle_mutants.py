@@ -13,6 +13,8 @@ from tests import oracle_pins
 MUTANTS = {
     "gate_sign": ("g_min / (1.0 + exp(-x))", "g_min / (1.0 + exp(x))"),
     "gate_no_exp_A": ("const double s = exp(A[h]);", "const double s = A[h];"),
+    "gate_exp_neg_A": ("const double s = exp(A[h]);", "const double s = exp(-A[h]);"),
+    "gate_A_of_head_0": ("const double s = exp(A[h]);", "const double s = exp(A[0]);"),
     "decay_sign": ("const double a = exp(g[c]);", "const double a = exp(-g[c]);"),
     "decay_dropped": ("for (int j = 0; j < dv; ++j) row[j] *= a;",
                       "for (int j = 0; j < dv; ++j) row[j] *= 1.0;"),
