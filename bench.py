@@ -288,7 +288,7 @@ def big_leg(kda, torch, synth, wl, dev, stream, timed_loop, copy_gbs, roof_ms, s
             "config": {"workload": wl.name, "N": N, "H": H, "T": T, "d_k": dk, "d_v": dv, "z_shift": wl.z_shift,
                        "initial_state": S0 is not None, "inputs": "drawn on the device, seeded"},
             "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(ach / HBM_PEAK_GBS, 4), "frac_of_measured_copy": round(ach / copy_gbs, 4),
+                         "frac": round(ach / HBM_PEAK_GBS, 4), "frac_of_measured_copy": round(ach / copy_gbs, 4) if copy_gbs else None,
                          "binding_roof_ms": roof_ms, "algorithmic_bytes_per_call": nbytes,
                          "mfma_tflops": round(flops / (ms * 1e-3) / 1e12, 1),
                          "traffic": load_traffic(wl.name), "kernel": "kda_prefill_gated"},
@@ -306,9 +306,14 @@ def main():
     ap.add_argument("--spin-up", type=float, default=SPIN_UP_S,
                     help="seconds of untimed steps before the warmup steps (clock ramp)")
     ap.add_argument("--no-big", action="store_true", help="skip the million-token legs")
+    ap.add_argument("--legs", default="decode,speculative,backward,roofs,big",
+                    help="comma-separated legs to run beside the 8K prefill (default: all)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
+    legs = set(x for x in args.legs.split(",") if x)
+    if args.no_big:
+        legs.discard("big")
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(the KDA path here is built and measured on a single MI355X)", file=sys.stderr)
@@ -430,155 +435,163 @@ def main():
                 "overhead_vs_plain": round(ck_ms / ms_step - 1.0, 4),
                 "checkpoint_bytes_per_call": n_ck * H * dk * dv * 4}
 
-    # ------------------------------------------------------------- decode leg
-    dwl = synth.DECODE_B256
-    B = dwl.N
-    dA = torch.from_numpy(synth.gate_A(dwl)).to(dev)
-    dsets = []
-    for si in range(8):
-        x = {n: synth.token_rows(dwl, n, 0, B, set_index=si) for n in ("q", "k", "v", "z", "beta")}
-        d = {n: torch.from_numpy(x[n]).to(dev).to(torch.bfloat16) for n in x}
-        d["g"] = torch.empty_like(d["z"])
-        dsets.append(d)
-    state = torch.from_numpy(synth.initial_state(dwl)).to(dev)
-    dout = torch.empty((B, dwl.H, dwl.dv), dtype=torch.bfloat16, device=dev)
+    decode = spec = backward = None
+    roofs, big = {}, {}
+    copy_gbs = None
+    if "decode" in legs:
+        # ------------------------------------------------------------- decode leg
+        dwl = synth.DECODE_B256
+        B = dwl.N
+        dA = torch.from_numpy(synth.gate_A(dwl)).to(dev)
+        dsets = []
+        for si in range(8):
+            x = {n: synth.token_rows(dwl, n, 0, B, set_index=si) for n in ("q", "k", "v", "z", "beta")}
+            d = {n: torch.from_numpy(x[n]).to(dev).to(torch.bfloat16) for n in x}
+            d["g"] = torch.empty_like(d["z"])
+            dsets.append(d)
+        state = torch.from_numpy(synth.initial_state(dwl)).to(dev)
+        dout = torch.empty((B, dwl.H, dwl.dv), dtype=torch.bfloat16, device=dev)
 
-    def dstep(i):  # one call: the gate fused into the decode step
-        d = dsets[i % 8]
-        kda.kda_decode_step_gated(d["q"], d["k"], d["v"], d["z"], dA, d["beta"], state, o=dout)
+        def dstep(i):  # one call: the gate fused into the decode step
+            d = dsets[i % 8]
+            kda.kda_decode_step_gated(d["q"], d["k"], d["v"], d["z"], dA, d["beta"], state, o=dout)
 
-    def dstep_unfused(i):
-        d = dsets[i % 8]
-        kda.kda_gate(d["z"], dA, g=d["g"])
-        kda.kda_decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], state, o=dout)
+        def dstep_unfused(i):
+            d = dsets[i % 8]
+            kda.kda_gate(d["z"], dA, g=d["g"])
+            kda.kda_decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], state, o=dout)
 
-    for i in range(16):
-        dstep(i)
-    d_total_ms = timed_loop(dstep, args.decode_steps) * args.decode_steps
-    d_kernel_ms = d_total_ms / args.decode_steps  # the step is the one launch
-    for i in range(16):
-        dstep_unfused(i)
-    d_unfused_ms = timed_loop(dstep_unfused, args.decode_steps)
-    d_bytes, d_flops = decode_algo(B, dwl.H, dwl.dk, dwl.dv)
-    d_ach = d_bytes / (d_kernel_ms * 1e-3) / 1e9
-    decode = {"value": round(B * args.decode_steps / (d_total_ms * 1e-3), 1), "unit": "tokens/s",
-              "steps": args.decode_steps, "ms_per_step": round(d_total_ms / args.decode_steps, 4),
-              "config": {"workload": "decode_b256", "B": B, "H": dwl.H, "d_k": dwl.dk,
-                         "d_v": dwl.dv, "input_sets": 8},
-              "roofline": {"bound": "hbm", "achieved": round(d_ach, 1), "peak": HBM_PEAK_GBS,
-                           "unit": "GB/s", "frac": round(d_ach / HBM_PEAK_GBS, 4),
-                           "traffic": load_traffic("decode_b256"),
-                           "kernel": "step_wave_kernel (kda_decode_step_gated)",
-                           "algorithmic_bytes_per_call": d_bytes,
-                           "ms_per_call": round(d_kernel_ms, 4)},
-              "unfused": {"ms_per_step": round(d_unfused_ms, 4),
-                          "value": round(B / (d_unfused_ms * 1e-3), 1)}}
+        for i in range(16):
+            dstep(i)
+        d_total_ms = timed_loop(dstep, args.decode_steps) * args.decode_steps
+        d_kernel_ms = d_total_ms / args.decode_steps  # the step is the one launch
+        for i in range(16):
+            dstep_unfused(i)
+        d_unfused_ms = timed_loop(dstep_unfused, args.decode_steps)
+        d_bytes, d_flops = decode_algo(B, dwl.H, dwl.dk, dwl.dv)
+        d_ach = d_bytes / (d_kernel_ms * 1e-3) / 1e9
+        decode = {"value": round(B * args.decode_steps / (d_total_ms * 1e-3), 1), "unit": "tokens/s",
+                  "steps": args.decode_steps, "ms_per_step": round(d_total_ms / args.decode_steps, 4),
+                  "config": {"workload": "decode_b256", "B": B, "H": dwl.H, "d_k": dwl.dk,
+                             "d_v": dwl.dv, "input_sets": 8},
+                  "roofline": {"bound": "hbm", "achieved": round(d_ach, 1), "peak": HBM_PEAK_GBS,
+                               "unit": "GB/s", "frac": round(d_ach / HBM_PEAK_GBS, 4),
+                               "traffic": load_traffic("decode_b256"),
+                               "kernel": "step_wave_kernel (kda_decode_step_gated)",
+                               "algorithmic_bytes_per_call": d_bytes,
+                               "ms_per_call": round(d_kernel_ms, 4)},
+                  "unfused": {"ms_per_step": round(d_unfused_ms, 4),
+                              "value": round(B / (d_unfused_ms * 1e-3), 1)}}
 
-    # ------------------------------------------- speculative decode leg (K = 4)
-    swl = synth.VERIFY_B256_K4
-    K = swl.seqlens[0]
-    SB = swl.N
-    sA = torch.from_numpy(synth.gate_A(swl)).to(dev)
-    ssets = []
-    for si in range(4):
-        x = {n: synth.token_rows(swl, n, 0, SB * K, set_index=si) for n in ("q", "k", "v", "z", "beta")}
-        d = {n: torch.from_numpy(x[n]).to(dev).to(torch.bfloat16) for n in x}
-        d["g"] = kda.kda_gate(d["z"], sA)
-        d = {n: t.reshape((SB, K) + tuple(t.shape[1:])) for n, t in d.items()}
-        ssets.append(d)
-    sstate = torch.from_numpy(synth.initial_state(swl.with_(seqlens=(1,) * SB))).to(dev)
-    sout = torch.empty((SB, K, swl.H, swl.dv), dtype=torch.bfloat16, device=dev)
-    n_all = torch.full((SB,), K, dtype=torch.int32, device=dev)
-    spec_iters = 200
-    for i in range(5):
-        d = ssets[i % 4]
-        kda.kda_verify(d["q"], d["k"], d["v"], d["g"], d["beta"], sstate, o=sout)
-        kda.kda_commit(d["k"], d["v"], d["g"], d["beta"], n_all, sstate)
-    torch.cuda.synchronize()
+    if "speculative" in legs:
+        # ------------------------------------------- speculative decode leg (K = 4)
+        swl = synth.VERIFY_B256_K4
+        K = swl.seqlens[0]
+        SB = swl.N
+        sA = torch.from_numpy(synth.gate_A(swl)).to(dev)
+        ssets = []
+        for si in range(4):
+            x = {n: synth.token_rows(swl, n, 0, SB * K, set_index=si) for n in ("q", "k", "v", "z", "beta")}
+            d = {n: torch.from_numpy(x[n]).to(dev).to(torch.bfloat16) for n in x}
+            d["g"] = kda.kda_gate(d["z"], sA)
+            d = {n: t.reshape((SB, K) + tuple(t.shape[1:])) for n, t in d.items()}
+            ssets.append(d)
+        sstate = torch.from_numpy(synth.initial_state(swl.with_(seqlens=(1,) * SB))).to(dev)
+        sout = torch.empty((SB, K, swl.H, swl.dv), dtype=torch.bfloat16, device=dev)
+        n_all = torch.full((SB,), K, dtype=torch.int32, device=dev)
+        spec_iters = 200
+        for i in range(5):
+            d = ssets[i % 4]
+            kda.kda_verify(d["q"], d["k"], d["v"], d["g"], d["beta"], sstate, o=sout)
+            kda.kda_commit(d["k"], d["v"], d["g"], d["beta"], n_all, sstate)
+        torch.cuda.synchronize()
 
-    def vcall(i):
-        d = ssets[i % 4]
-        kda.kda_verify(d["q"], d["k"], d["v"], d["g"], d["beta"], sstate, o=sout)
+        def vcall(i):
+            d = ssets[i % 4]
+            kda.kda_verify(d["q"], d["k"], d["v"], d["g"], d["beta"], sstate, o=sout)
 
-    def ccall(i):
-        d = ssets[i % 4]
-        kda.kda_commit(d["k"], d["v"], d["g"], d["beta"], n_all, sstate)
+        def ccall(i):
+            d = ssets[i % 4]
+            kda.kda_commit(d["k"], d["v"], d["g"], d["beta"], n_all, sstate)
 
-    v_ms = timed_loop(vcall, spec_iters)
-    c_ms = timed_loop(ccall, spec_iters)
-    vb = spec_algo(SB, K, swl.H, swl.dk, swl.dv, False)
-    cb = spec_algo(SB, K, swl.H, swl.dk, swl.dv, True)
-    spec = {"value": round(SB * K / ((v_ms + c_ms) * 1e-3), 1), "unit": "draft tokens/s (verify + commit)",
-            "config": {"workload": "verify_b256_k4", "B": SB, "K": K, "H": swl.H, "d_k": swl.dk,
-                       "d_v": swl.dv, "n_accept": K, "input_sets": 4},
-            "verify": {"ms_per_call": round(v_ms, 4),
-                       "roofline": {"bound": "hbm", "achieved": round(vb / (v_ms * 1e-3) / 1e9, 1),
-                                    "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                    "frac": round(vb / (v_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                                    "traffic": load_traffic("verify_b256_k4"), "kernel": "step_wave_kernel (verify)",
-                                    "algorithmic_bytes_per_call": vb}},
-            "commit": {"ms_per_call": round(c_ms, 4),
-                       "roofline": {"bound": "hbm", "achieved": round(cb / (c_ms * 1e-3) / 1e9, 1),
-                                    "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                    "frac": round(cb / (c_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                                    "traffic": load_traffic("commit_b256_k4"), "kernel": "step_wave_kernel (commit)",
-                                    "algorithmic_bytes_per_call": cb}}}
+        v_ms = timed_loop(vcall, spec_iters)
+        c_ms = timed_loop(ccall, spec_iters)
+        vb = spec_algo(SB, K, swl.H, swl.dk, swl.dv, False)
+        cb = spec_algo(SB, K, swl.H, swl.dk, swl.dv, True)
+        spec = {"value": round(SB * K / ((v_ms + c_ms) * 1e-3), 1), "unit": "draft tokens/s (verify + commit)",
+                "config": {"workload": "verify_b256_k4", "B": SB, "K": K, "H": swl.H, "d_k": swl.dk,
+                           "d_v": swl.dv, "n_accept": K, "input_sets": 4},
+                "verify": {"ms_per_call": round(v_ms, 4),
+                           "roofline": {"bound": "hbm", "achieved": round(vb / (v_ms * 1e-3) / 1e9, 1),
+                                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                        "frac": round(vb / (v_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                        "traffic": load_traffic("verify_b256_k4"), "kernel": "step_wave_kernel (verify)",
+                                        "algorithmic_bytes_per_call": vb}},
+                "commit": {"ms_per_call": round(c_ms, 4),
+                           "roofline": {"bound": "hbm", "achieved": round(cb / (c_ms * 1e-3) / 1e9, 1),
+                                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                        "frac": round(cb / (c_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                        "traffic": load_traffic("commit_b256_k4"), "kernel": "step_wave_kernel (commit)",
+                                        "algorithmic_bytes_per_call": cb}}}
 
-    # ------------------------------------------- backward leg (8K workload)
-    # the forward's interval-64 checkpoints and g come from untimed calls; one
-    # kda_backward call (summary, scan and full pass) is timed per step
-    bsets = sets[0]
-    bg = torch.empty_like(bsets["z"])
-    kda.kda_gate(bsets["z"], A, g=bg)
-    _, _, bck = kda.kda_prefill_ckpt(bsets["q"], bsets["k"], bsets["v"], bg, bsets["beta"], 64)
-    gen = torch.Generator(device=dev).manual_seed(7)
-    bdo = torch.randn((T, H, dv), device=dev, generator=gen).to(torch.bfloat16)
-    bdfin = torch.randn((1, H, dk, dv), device=dev, generator=gen)
-    bws = torch.empty(kda.lib().kda_backward_workspace_size(T, 1, H, dk, dv), dtype=torch.uint8, device=dev)
+    if "backward" in legs:
+        # ------------------------------------------- backward leg (8K workload)
+        # the forward's interval-64 checkpoints and g come from untimed calls; one
+        # kda_backward call (summary, scan and full pass) is timed per step
+        bsets = sets[0]
+        bg = torch.empty_like(bsets["z"])
+        kda.kda_gate(bsets["z"], A, g=bg)
+        _, _, bck = kda.kda_prefill_ckpt(bsets["q"], bsets["k"], bsets["v"], bg, bsets["beta"], 64)
+        gen = torch.Generator(device=dev).manual_seed(7)
+        bdo = torch.randn((T, H, dv), device=dev, generator=gen).to(torch.bfloat16)
+        bdfin = torch.randn((1, H, dk, dv), device=dev, generator=gen)
+        bws = torch.empty(kda.lib().kda_backward_workspace_size(T, 1, H, dk, dv), dtype=torch.uint8, device=dev)
 
-    def bcall(i):
-        kda.kda_backward(bsets["q"], bsets["k"], bsets["v"], bg, bsets["beta"], d_o=bdo, d_final_state=bdfin,
-                         ckpt=bck, interval=64, workspace=bws)
+        def bcall(i):
+            kda.kda_backward(bsets["q"], bsets["k"], bsets["v"], bg, bsets["beta"], d_o=bdo, d_final_state=bdfin,
+                             ckpt=bck, interval=64, workspace=bws)
 
-    bcall(0)
-    b_ms = timed_loop(bcall, 3)
-    b_bytes = backward_algo(T, H, dk, dv)
-    backward = {"value": round(T / (b_ms * 1e-3), 1), "unit": "tokens/s", "ms_per_call": round(b_ms, 3),
-                "config": {"workload": "prefill_8k backward (dq, dk, dv, dg, dbeta, dS0) from interval-64 "
-                                       "checkpoints", "H": H, "T": T, "d_k": dk, "d_v": dv},
-                "roofline": {"bound": "hbm", "achieved": round(b_bytes / (b_ms * 1e-3) / 1e9, 1),
-                             "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                             "frac": round(b_bytes / (b_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 5),
-                             "kernel": "bwd_chunk_summary_kernel + bwd_scan_kernel + bwd_chunk_full_kernel",
-                             "traffic": load_traffic("backward_8k"),
-                             "algorithmic_bytes_per_call": b_bytes}}
-    del bws, bck
+        bcall(0)
+        b_ms = timed_loop(bcall, 3)
+        b_bytes = backward_algo(T, H, dk, dv)
+        backward = {"value": round(T / (b_ms * 1e-3), 1), "unit": "tokens/s", "ms_per_call": round(b_ms, 3),
+                    "config": {"workload": "prefill_8k backward (dq, dk, dv, dg, dbeta, dS0) from interval-64 "
+                                           "checkpoints", "H": H, "T": T, "d_k": dk, "d_v": dv},
+                    "roofline": {"bound": "hbm", "achieved": round(b_bytes / (b_ms * 1e-3) / 1e9, 1),
+                                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                 "frac": round(b_bytes / (b_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 5),
+                                 "kernel": "bwd_chunk_summary_kernel + bwd_scan_kernel + bwd_chunk_full_kernel",
+                                 "traffic": load_traffic("backward_8k"),
+                                 "algorithmic_bytes_per_call": b_bytes}}
+        del bws, bck
 
-    # the device's own roofs: streaming read / write / copy kernels over 4 GiB
-    # (far past the 256 MB last-level cache) and back-to-back 16x16x32 bf16
-    # matrix-core instructions on every SIMD (libkda_roofs)
-    roofs = measured_roofs(torch, dev, stream)
-    copy_gbs = roofs["hbm_copy_gbs"]
-    for r in (roofline, decode["roofline"], spec["verify"]["roofline"], spec["commit"]["roofline"],
-              backward["roofline"]):
-        r["measured_copy_gbs"] = round(copy_gbs, 1)
-        r["frac_of_measured_copy"] = round(r["achieved"] / copy_gbs, 4)
-    roofline["measured_mfma_bf16_tflops"] = roofs["mfma_bf16_tflops"]
-    roofline["mfma_frac_of_measured_mfma"] = round(roofline["mfma_tflops"] / roofs["mfma_bf16_tflops"], 4)
-    # a plain 8192^3 bf16 GEMM through the vendor library, for reference
-    ga = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
-    gb = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
-    gc = torch.empty(8192, 8192, device=dev, dtype=torch.bfloat16)
-    for _ in range(3):
-        torch.mm(ga, gb, out=gc)
-    gemm_ms = timed_loop(lambda i: torch.mm(ga, gb, out=gc), 10)
-    gemm_tflops = 2.0 * 8192 ** 3 / (gemm_ms * 1e-3) / 1e12
-    del ga, gb, gc
-    roofs["vendor_gemm_bf16_tflops"] = round(gemm_tflops, 1)
+    if "roofs" in legs:
+        # the device's own roofs: streaming read / write / copy kernels over 4 GiB
+        # (far past the 256 MB last-level cache) and back-to-back 16x16x32 bf16
+        # matrix-core instructions on every SIMD (libkda_roofs)
+        roofs = measured_roofs(torch, dev, stream)
+        copy_gbs = roofs["hbm_copy_gbs"]
+        for r in (roofline, decode and decode["roofline"], spec and spec["verify"]["roofline"],
+                  spec and spec["commit"]["roofline"], backward and backward["roofline"]):
+            if r is None:
+                continue
+            r["measured_copy_gbs"] = round(copy_gbs, 1)
+            r["frac_of_measured_copy"] = round(r["achieved"] / copy_gbs, 4)
+        roofline["measured_mfma_bf16_tflops"] = roofs["mfma_bf16_tflops"]
+        roofline["mfma_frac_of_measured_mfma"] = round(roofline["mfma_tflops"] / roofs["mfma_bf16_tflops"], 4)
+        # a plain 8192^3 bf16 GEMM through the vendor library, for reference
+        ga = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+        gb = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+        gc = torch.empty(8192, 8192, device=dev, dtype=torch.bfloat16)
+        for _ in range(3):
+            torch.mm(ga, gb, out=gc)
+        gemm_ms = timed_loop(lambda i: torch.mm(ga, gb, out=gc), 10)
+        gemm_tflops = 2.0 * 8192 ** 3 / (gemm_ms * 1e-3) / 1e12
+        del ga, gb, gc
+        roofs["vendor_gemm_bf16_tflops"] = round(gemm_tflops, 1)
 
     # ------------------------------------------- million-token workloads
-    big = {}
-    if not args.no_big:
+    if "big" in legs:
         big["prefill_1m"] = big_leg(kda, torch, synth, synth.PREFILL_1M, dev, stream, timed_loop, copy_gbs, 1.34)
         big["varlen_64"] = big_leg(kda, torch, synth, synth.VARLEN_64, dev, stream, timed_loop, copy_gbs, 5.1)
 
