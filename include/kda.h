@@ -277,8 +277,13 @@ int64_t kda_test_prefill_flags(int64_t T_total, int N, int H, int d_k, int d_v, 
  *                    d_v) bytes: per workgroup slot, the states at the four
  *                    16-token sub-chunk starts of a 64-token chunk (in up to
  *                    two layouts) and one staging state; per (segment, head) the segment's
- *                    gradient summary and its incoming state gradient
- *                    (segments of a sequence run in parallel).
+ *                    gradient summary, its end-of-segment state gradient and
+ *                    a flag (segments of a sequence run in parallel).
+ * Segments of one sequence run in parallel.  Each takes the state gradient at
+ * its end from the 128 tokens after it, run backwards from zero beside the
+ * window's transposed transition; where that transition is not exactly zero
+ * (slow decay), the chain's segments are composed exactly through a summary
+ * pass and a scan instead, whose launches end at once for the other chains.
  * The products run on the matrix cores with operands in `dtype` (bf16
  * operands and fp32 accumulation for KDA_BF16, as in the prefill).
  * State buffers, dv and the workspace must be 16-byte aligned; no output may
@@ -300,17 +305,21 @@ kda_status_t kda_backward(const void* q, const void* k, const void* v, const voi
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * TEST ONLY — kda_backward with its segment length given: seg_tokens > 0 cuts
- * every sequence into segments of that many tokens (rounded up to whole
- * 64-token chunks), 0 takes the planner's.  kda_test_backward_workspace_size
- * is the workspace for the same choice.
+ * TEST ONLY — kda_backward with the planner's two choices given: seg_tokens >
+ * 0 cuts every sequence into segments of that many tokens (rounded up to whole
+ * 64-token chunks), 0 takes the planner's; warm_tokens is the window after each
+ * segment that gives its end-of-segment state gradient (a positive multiple of
+ * 16), 0 sends every chain through the summary pass and the scan, -1 takes the
+ * planner's.  kda_test_backward_workspace_size is the workspace for the same
+ * segment length (it does not depend on the window).
  */
 kda_status_t kda_test_backward(const void* q, const void* k, const void* v, const void* g, const void* beta,
                                const int32_t* cu_seqlens, int N, int64_t T_total, int H, int d_k, int d_v,
                                const float* initial_state, const float* ckpt_states, int64_t ckpt_capacity,
                                int ckpt_interval, const void* d_o, const float* d_final_state, float* dq, float* dk,
                                float* dv, float* dg, float* dbeta, float* d_initial_state, kda_dtype_t dtype,
-                               void* workspace, size_t workspace_bytes, int64_t seg_tokens, void* stream);
+                               void* workspace, size_t workspace_bytes, int64_t seg_tokens, int64_t warm_tokens,
+                               void* stream);
 size_t kda_test_backward_workspace_size(int64_t T_total, int N, int H, int d_k, int d_v, int64_t seg_tokens);
 
 /*

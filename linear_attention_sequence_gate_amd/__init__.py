@@ -83,7 +83,7 @@ def lib() -> ctypes.CDLL:
                                                 P]
         L.kda_prefill_gated_noalloc.restype = I
         L.kda_test_backward.argtypes = [P, P, P, P, P, P, I, I64, I, I, I, P, P, I64, I, P, P, P, P, P, P, P, P, I,
-                                        P, SZ, I64, P]
+                                        P, SZ, I64, I64, P]
         L.kda_test_backward.restype = I
         L.kda_test_backward_workspace_size.argtypes = [I64, I, I, I, I, I64]
         L.kda_test_backward_workspace_size.restype = SZ
@@ -321,12 +321,13 @@ def kda_decode_step_gated(q, k, v, z, A, beta, state, o=None, g_min: float = -5.
 
 
 def kda_backward(q, k, v, g, beta, d_o=None, d_final_state=None, cu_seqlens=None, initial_state=None,
-                 ckpt=None, interval: int = 64, workspace=None, stream=None, seg_tokens: int | None = None):
+                 ckpt=None, interval: int = 64, workspace=None, stream=None, seg_tokens: int | None = None,
+                 warm_tokens: int = -1):
     """Gradients of L = sum_t <d_o[t], o[t]> + <d_final_state, S_T> for kda_prefill on the
     same inputs.  ckpt: the forward's checkpoints every `interval` tokens (64 is
     the fast path; None: every chunk's state is rebuilt from the initial state,
-    for short inputs only).  seg_tokens (tests only) forces the segment length
-    through kda_test_backward.  Returns a dict of fp32 tensors dq, dk, dg
+    for short inputs only).  seg_tokens and warm_tokens (tests only) force the
+    segment length and the end-of-segment window through kda_test_backward.  Returns a dict of fp32 tensors dq, dk, dg
     [T, H, d_k], dv [T, H, d_v], dbeta [T, H], d_initial_state [N, H, d_k, d_v]."""
     import torch
     _dense(q, k, v, g, beta, d_o, d_final_state, cu_seqlens, initial_state, ckpt, workspace)
@@ -337,10 +338,11 @@ def kda_backward(q, k, v, g, beta, d_o=None, d_final_state=None, cu_seqlens=None
     f = lambda *shape: torch.empty(shape, dtype=torch.float32, device=dev)
     out = {"dq": f(T, H, dk), "dk": f(T, H, dk), "dv": f(T, H, dv), "dg": f(T, H, dk), "dbeta": f(T, H),
            "d_initial_state": f(N, H, dk, dv)}
-    if seg_tokens is None:
+    test = seg_tokens is not None or warm_tokens != -1
+    if not test:
         need = int(lib().kda_backward_workspace_size(T, N, H, dk, dv))
     else:
-        need = int(lib().kda_test_backward_workspace_size(T, N, H, dk, dv, int(seg_tokens)))
+        need = int(lib().kda_test_backward_workspace_size(T, N, H, dk, dv, int(seg_tokens or 0)))
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     wbytes = workspace.numel() * workspace.element_size()
@@ -349,10 +351,10 @@ def kda_backward(q, k, v, g, beta, d_o=None, d_final_state=None, cu_seqlens=None
             _ptr(initial_state), _ptr(ckpt) if cap else None, cap, int(interval), _ptr(d_o), _ptr(d_final_state),
             _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]), _ptr(out["dbeta"]),
             _ptr(out["d_initial_state"]), _dtype_code(k), _ptr(workspace), wbytes]
-    if seg_tokens is None:
+    if not test:
         _check(lib().kda_backward(*args, _stream(stream)))
     else:
-        _check(lib().kda_test_backward(*args, int(seg_tokens), _stream(stream)))
+        _check(lib().kda_test_backward(*args, int(seg_tokens or 0), int(warm_tokens), _stream(stream)))
     return out
 
 

@@ -525,7 +525,8 @@ static kda_status_t backward_impl(const char* who, const void* q, const void* k,
                                   int64_t ckpt_capacity, int ckpt_interval, const void* d_o,
                                   const float* d_final_state, float* dq, float* dk, float* dv, float* dg,
                                   float* dbeta, float* d_initial_state, kda_dtype_t dtype, void* workspace,
-                                  size_t workspace_bytes, void* stream, int64_t seg_tokens)
+                                  size_t workspace_bytes, void* stream, int64_t seg_tokens,
+                                  int64_t warm_tokens = -1)
 {
     if (N < 1 || T_total < 0 || H < 1)
         return fail(KDA_ERR_INVALID_ARGUMENT, "%s: bad sizes N=%d T_total=%lld H=%d", who, N, (long long)T_total, H);
@@ -550,7 +551,7 @@ static kda_status_t backward_impl(const char* who, const void* q, const void* k,
         return fail(KDA_ERR_UNSUPPORTED, "%s: %lld tokens without checkpoints (at most %d); pass the forward's "
                     "checkpoints (kda_prefill_ckpt or kda_prefill_gated, interval 64 for the fast path)", who,
                     (long long)T_total, KDA_BWD_MAX_TOKENS_WITHOUT_CKPT);
-    const kda::BwdPlan plan = kda::backward_plan(T_total, N, H, d_k, d_v, seg_tokens);
+    const kda::BwdPlan plan = kda::backward_plan(T_total, N, H, d_k, d_v, seg_tokens, warm_tokens);
     const size_t need = plan.bytes;
     if (!workspace || workspace_bytes < need)
         return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes < %zu needed", who, workspace_bytes, need);
@@ -611,13 +612,15 @@ kda_status_t kda_test_backward(const void* q, const void* k, const void* v, cons
                                const float* initial_state, const float* ckpt_states, int64_t ckpt_capacity,
                                int ckpt_interval, const void* d_o, const float* d_final_state, float* dq, float* dk,
                                float* dv, float* dg, float* dbeta, float* d_initial_state, kda_dtype_t dtype,
-                               void* workspace, size_t workspace_bytes, int64_t seg_tokens, void* stream)
+                               void* workspace, size_t workspace_bytes, int64_t seg_tokens, int64_t warm_tokens,
+                               void* stream)
 {
-    if (seg_tokens < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "kda_test_backward: seg_tokens=%lld",
-                                    (long long)seg_tokens);
+    if (seg_tokens < 0 || warm_tokens < -1 || (warm_tokens > 0 && warm_tokens % 16 != 0))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_test_backward: seg_tokens=%lld warm_tokens=%lld",
+                    (long long)seg_tokens, (long long)warm_tokens);
     return backward_impl("kda_test_backward", q, k, v, g, beta, cu_seqlens, N, T_total, H, d_k, d_v, initial_state,
                          ckpt_states, ckpt_capacity, ckpt_interval, d_o, d_final_state, dq, dk, dv, dg, dbeta,
-                         d_initial_state, dtype, workspace, workspace_bytes, stream, seg_tokens);
+                         d_initial_state, dtype, workspace, workspace_bytes, stream, seg_tokens, warm_tokens);
 }
 
 int64_t kda_checkpoint_count(const int32_t* cu_seqlens_host, int N, int64_t T_total, int ckpt_interval)

@@ -13,10 +13,17 @@
 // dS_prev = F^T (dS + q dO^T), F = (I - beta k k^T) Diag(e^g) the forward
 // transition: affine in dS and free of the forward state.  So a segment maps
 // dS_start = M^T dS_end + C, with M the segment's forward transition and C
-// the segment's own contribution (dS_end = 0).  A summary pass computes
-// [C | M^T] per (segment, head); a scan takes dS_start = M^T dS_end + C
-// backwards over each sequence's segments; the full pass then runs every
-// segment from its true dS_end, in parallel.
+// the segment's own contribution (dS_end = 0).  Every segment but a
+// sequence's last first takes its dS_end from a window of `warm` tokens after
+// it: the state-free step run backwards from dS = 0 at the window's far end
+// beside the window's M^T (columns starting at I).  When the computed M^T is
+// exactly zero (its entries underflow within about a hundred tokens of the
+// gate's bounded decay) dS_end is the window's C; a window that reaches the
+// sequence end starts from the final state's gradient and is exact.  Chains
+// where a window's M^T is not zero are flagged, and for them a summary pass
+// computes [C | M^T] per (segment, head) and a scan takes dS_start = M^T
+// dS_end + C backwards over the segments.  The full pass then runs every
+// segment from its dS_end, in parallel.
 #pragma once
 
 #include "kda_common.hpp"
@@ -43,7 +50,20 @@ struct BackwardArgs {
     int64_t Lseg;           // tokens per segment (a multiple of BWD_CHUNK)
     float* cm;              // per (segment, head): C [dk][dv] then M^T [dk][dk], fp32
     float* dsend;           // per (segment, head): dS at the segment's end [dk][dv], fp32
+    int32_t* flags = nullptr;  // per (segment, head): 1 where the window's M^T was not zero
+    int64_t warm = 0;          // window tokens (a multiple of 16); 0: summary pass and scan for every chain
 };
+
+// Whether the chain (sequence of segments seg0 .. seg0+nseg-1, head h) goes
+// through the summary pass and the scan: always without windows (no flags),
+// else when any of its segments was flagged; uniform across the workgroup.
+__device__ __forceinline__ bool bwd_chain_flagged(const BackwardArgs& a, int seg0, int nseg, int h)
+{
+    if (a.flags == nullptr) return true;
+    for (int j = 0; j < nseg; ++j)
+        if (a.flags[int64_t(seg0 + j) * a.H + h] != 0) return true;
+    return false;
+}
 
 // Where segment `seg` (0 .. total) of the packed sequences lies.  Offsets are
 // clamped into [0, T_total] and made non-decreasing, as the prefill's planner
@@ -132,6 +152,7 @@ __global__ void __launch_bounds__(256) bwd_scan_kernel(BackwardArgs a)
             prev = x;
         }
     }
+    if (!bwd_chain_flagged(a, seg0, nseg, h)) return;  // the windows gave every dS_end
     auto cm_of = [&](int s) { return a.cm + (int64_t(seg0 + s) * H + h) * (DK * DV + DK * DK); };
     auto dsend_of = [&](int s) { return a.dsend + (int64_t(seg0 + s) * H + h) * DK * DV; };
     // the last segment ends at the final state: its dS_end is the final state's gradient
@@ -145,9 +166,11 @@ __global__ void __launch_bounds__(256) bwd_scan_kernel(BackwardArgs a)
 #pragma unroll
         for (int i = 0; i < C::NV; ++i) pre[i] = src[t + 256 * i];
     };
-    if (nseg >= 2) load_m(nseg - 2);
+    if (nseg >= 3) load_m(nseg - 2);
     __syncthreads();
-    for (int s = nseg - 2; s >= 0; --s) {
+    // dS_start of segment 0 is the full pass's (the initial state's gradient),
+    // so the composition stops at segment 1 and segment 0's summary is not read
+    for (int s = nseg - 2; s >= 1; --s) {
 #pragma unroll
         for (int i = 0; i < C::NV; ++i) {
             const int e = 4 * (t + 256 * i), r = e / DK, c = e % DK;
@@ -158,7 +181,7 @@ __global__ void __launch_bounds__(256) bwd_scan_kernel(BackwardArgs a)
 #pragma unroll
         for (int i = 0; i < C::RPT; ++i) acc[i] = Cs[(rgp * C::RPT + i) * DV + col];
         __syncthreads();  // M_s^T staged
-        if (s >= 1) load_m(s - 1);
+        if (s >= 2) load_m(s - 1);
         for (int c = 0; c < DK; c += 4) {
             const float d0 = sd[c * SD + jj], d1 = sd[(c + 1) * SD + jj];
             const float d2 = sd[(c + 2) * SD + jj], d3 = sd[(c + 3) * SD + jj];
@@ -174,21 +197,28 @@ __global__ void __launch_bounds__(256) bwd_scan_kernel(BackwardArgs a)
         for (int i = 0; i < C::RPT; ++i) sd[(rgp * C::RPT + i) * SD + jj] = acc[i];
         __syncthreads();
     }
-    // (the initial state's gradient is the full pass's: its first segment ends there)
+    if (nseg >= 2)
+        for (int r = rgp; r < DK; r += C::RG) dsend_of(0)[r * DV + col] = sd[r * SD + jj];
 }
 
 struct BwdPlan {
-    int64_t Lseg = 0, segs_max = 0;
+    int64_t Lseg = 0, segs_max = 0, warm = 0;
     int grid = 0;
-    size_t off_scratch = 0, off_cm = 0, off_dsend = 0, bytes = 0;
+    size_t off_scratch = 0, off_cm = 0, off_dsend = 0, off_flags = 0, bytes = 0;
 };
+
+constexpr int64_t BWD_WARM_DEFAULT = 128;  // tokens
 
 // Segment length: enough (segment, head) items to cover the compute units
 // about once (each runs its chunks in series), at least one 64-token chunk.
-// force_tokens > 0 fixes it instead (rounded up to whole chunks).
-inline BwdPlan backward_plan(int64_t T_total, int N, int H, int dk, int dv, int64_t force_tokens = 0)
+// force_tokens > 0 fixes it instead (rounded up to whole chunks); warm_req
+// < 0 takes the default window, 0 turns the windows off, > 0 sets them (a
+// multiple of 16 tokens).
+inline BwdPlan backward_plan(int64_t T_total, int N, int H, int dk, int dv, int64_t force_tokens = 0,
+                             int64_t warm_req = -1)
 {
     BwdPlan p;
+    p.warm = warm_req < 0 ? BWD_WARM_DEFAULT : warm_req;
     const int64_t T = T_total > 0 ? T_total : 1;
     if (int64_t(N) * H >= BWD_MAX_WG / 2) {
         p.Lseg = (T + BWD_CHUNK - 1) / BWD_CHUNK * BWD_CHUNK;  // one segment per sequence
@@ -209,6 +239,8 @@ inline BwdPlan backward_plan(int64_t T_total, int N, int H, int dk, int dv, int6
     off = align256(off + size_t(items) * (size_t(dk) * dv + size_t(dk) * dk) * sizeof(float));
     p.off_dsend = off;
     off = align256(off + size_t(items) * dk * dv * sizeof(float));
+    p.off_flags = off;
+    off = align256(off + size_t(items) * sizeof(int32_t));
     p.bytes = off;
     return p;
 }

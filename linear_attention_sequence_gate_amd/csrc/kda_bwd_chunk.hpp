@@ -429,23 +429,52 @@ __device__ __forceinline__ void bwd_dstep(unsigned char* sm, f32x4 (&dS)[C::DK /
 }
 
 // Summary pass: [C | M^T] of dS_start = M^T dS_end + C per (segment, head).
-template <typename DT, int DK, int DV>
+// WINDOW: per (segment, head), dS at the segment's end from the window of
+// a.warm tokens after it (see kda_backward.hpp): written to dsend when the
+// window's M^T is exactly zero or the window reaches the sequence end (then it
+// starts from d_fin and is exact); otherwise the (segment, head) is flagged.
+// A sequence's last segment takes d_fin itself.  Without WINDOW: the
+// segment's [C | M^T] for the scan, for the chains a window flagged.
+template <typename DT, int DK, int DV, bool WINDOW>
 __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, false>::NT)) bwd_chunk_summary_kernel(BackwardArgs a)
 {
     using C = BwdCfg<DT, DK, DV, false>;
     extern __shared__ __attribute__((aligned(16))) unsigned char sm[];
+    __shared__ int s_live;  // WINDOW: some wave's M^T columns are still non-zero
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int l16 = lane & 15, q4 = lane >> 4;
     const int H = a.H;
     const int item = blockIdx.x, h = item % H;
     const SegLoc L = bwd_locate(a, item / H);
-    // a sequence of one segment needs no summary: the full pass gives its
-    // initial state's gradient directly
-    if (L.n < 0 || L.nseg == 1) return;
+    if (L.n < 0) return;
     const bool last = L.s == L.nseg - 1;
+    const int64_t unit = int64_t(L.n) * H + h;
+    // the tokens this workgroup runs backwards over, and where dS starts
+    int64_t r0 = L.t0, r1 = L.t1;
+    bool from_fin = last;  // dS starts at d_fin (else at 0)
+    if constexpr (WINDOW) {
+        float* dst = a.dsend + int64_t(item) * DK * DV;
+        if (last) {  // the sequence's last segment ends at the final state
+            const float* src = a.d_fin ? a.d_fin + unit * DK * DV : nullptr;
+            for (int e = threadIdx.x; e < DK * DV; e += C::NT) dst[e] = src ? src[e] : 0.f;
+            if (threadIdx.x == 0) a.flags[item] = 0;
+            return;
+        }
+        r0 = L.t1;
+        r1 = L.t1 + a.warm < L.c1 ? L.t1 + a.warm : L.c1;
+        from_fin = r1 == L.c1;
+        if (threadIdx.x == 0) s_live = 0;
+        __syncthreads();
+    } else {
+        // a sequence of one segment needs no summary (the full pass gives its
+        // initial state's gradient directly), nor does its first segment (the
+        // scan stops at the second), nor a chain every window served
+        if (L.nseg == 1 || L.s == 0) return;
+        if (!bwd_chain_flagged(a, L.seg0, L.nseg, h)) return;
+    }
     constexpr int CT = C::CT, CW = 16 * CT;  // columns per wave
     const bool mcols = wave >= DV / CW;  // a wave of the N (identity) columns
-    const bool active = !(mcols && last);
+    const bool active = !(mcols && from_fin);
     const int col0 = (mcols ? wave - DV / CW : wave) * CW;
     f32x4 dS[DK / 16][CT];
 #pragma unroll
@@ -457,14 +486,14 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, false>::NT)) bwd_chunk_sum
                 const int row = 16 * rt + 4 * q4 + j, col = col0 + 16 * ct + l16;
                 float x = 0.f;
                 if (mcols) x = row == col ? 1.f : 0.f;
-                else if (last && a.d_fin) x = a.d_fin[(int64_t(L.n) * H + h) * DK * DV + row * DV + col];
+                else if (from_fin && a.d_fin) x = a.d_fin[unit * DK * DV + row * DV + col];
                 dS[rt][ct][j] = x;
             }
-    if (L.t1 > L.t0) {
-        const int64_t m0 = (L.t0 - L.c0) / BSUB, m1 = (L.t1 - 1 - L.c0) / BSUB;
+    if (r1 > r0) {
+        const int64_t m0 = (r0 - L.c0) / BSUB, m1 = (r1 - 1 - L.c0) / BSUB;
         for (int64_t m = m1; m >= m0; --m) {
             const int64_t t_s = L.c0 + m * BSUB;
-            const int n = int(L.t1 - t_s < BSUB ? L.t1 - t_s : BSUB);
+            const int n = int(r1 - t_s < BSUB ? r1 - t_s : BSUB);
             bwd_prep<C, DT, false>(a, sm, t_s, n, h, false);
             __syncthreads();
             if (wave == 0) bwd_small<C, DT, false>(sm, fresh_lane(), false);
@@ -477,6 +506,35 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, false>::NT)) bwd_chunk_sum
             }
             __syncthreads();
         }
+    }
+    if constexpr (WINDOW) {
+        // the window's M^T: exactly zero, or the chain goes through the scan
+        if (!from_fin) {
+            if (mcols) {
+                bool nz = false;
+#pragma unroll
+                for (int rt = 0; rt < DK / 16; ++rt)
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) nz = nz || (dS[rt][ct][j] != 0.f);
+                if (__ballot(nz) != 0 && fresh_lane() == 0) atomicOr(&s_live, 1);
+            }
+            __syncthreads();
+        }
+        const bool fail = !from_fin && s_live != 0;
+        if (threadIdx.x == 0) a.flags[item] = fail ? 1 : 0;
+        if (fail || mcols) return;
+        const int ln = fresh_lane(), ol16 = ln & 15, oq4 = ln >> 4;
+        float* out = a.dsend + int64_t(item) * DK * DV;
+#pragma unroll
+        for (int rt = 0; rt < DK / 16; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    out[(16 * rt + 4 * oq4 + j) * DV + col0 + 16 * ct + ol16] = dS[rt][ct][j];
+        return;
     }
     if (!active) return;
     const int ln = fresh_lane(), ol16 = ln & 15, oq4 = ln >> 4;
@@ -865,22 +923,40 @@ hipError_t launch_bwd_chunk(const BackwardArgs& a, const BwdPlan& plan, hipStrea
 {
     using C1 = BwdCfg<DT, DK, DV, false>;
     using C3 = BwdCfg<DT, DK, DV, true>;
-    auto k1 = bwd_chunk_summary_kernel<DT, DK, DV>;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k1),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, C1::LDS);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k1, dim3(unsigned(plan.segs_max * a.H)), dim3(C1::NT), C1::LDS, stream, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    auto ks = bwd_scan_kernel<DK, DV>;
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(ks), hipFuncAttributeMaxDynamicSharedMemorySize,
-                            BwdScanCfg<DK>::LDS);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(ks, dim3(unsigned(a.N * a.H * (DV / BWD_SCAN_COLS))), dim3(256), BwdScanCfg<DK>::LDS, stream, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipError_t e = hipSuccess;
+    BackwardArgs b = a;
+    if (plan.warm > 0) {  // the windows: dS_end of every segment, flags where M^T did not vanish
+        auto kw = bwd_chunk_summary_kernel<DT, DK, DV, true>;
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(kw), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                C1::LDS);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(kw, dim3(unsigned(plan.segs_max * a.H)), dim3(C1::NT), C1::LDS, stream, b);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    } else {
+        b.flags = nullptr;  // every chain through the summary and the scan
+    }
+    // the summary pass and the scan: flagged chains only (all of them without
+    // windows, where the scan also hands each sequence's last segment d_fin);
+    // with windows and one segment per sequence there is nothing to compose
+    if (b.flags == nullptr || plan.Lseg < a.T_total) {
+        auto k1 = bwd_chunk_summary_kernel<DT, DK, DV, false>;
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(k1), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                C1::LDS);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(k1, dim3(unsigned(plan.segs_max * a.H)), dim3(C1::NT), C1::LDS, stream, b);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        auto ks = bwd_scan_kernel<DK, DV>;
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(ks), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                BwdScanCfg<DK>::LDS);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(ks, dim3(unsigned(a.N * a.H * (DV / BWD_SCAN_COLS))), dim3(256), BwdScanCfg<DK>::LDS,
+                           stream, b);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     auto k3 = bwd_chunk_full_kernel<DT, DK, DV>;
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(k3), hipFuncAttributeMaxDynamicSharedMemorySize, C3::LDS);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k3, dim3(unsigned(plan.grid)), dim3(C3::NT), C3::LDS, stream, a);
+    hipLaunchKernelGGL(k3, dim3(unsigned(plan.grid)), dim3(C3::NT), C3::LDS, stream, b);
     return hipGetLastError();
 }
 
@@ -893,6 +969,8 @@ hipError_t launch_backward(const BackwardArgs& a, const BwdPlan& plan, int dk, i
     b.scratch = reinterpret_cast<float*>(ws + plan.off_scratch);
     b.cm = reinterpret_cast<float*>(ws + plan.off_cm);
     b.dsend = reinterpret_cast<float*>(ws + plan.off_dsend);
+    b.flags = reinterpret_cast<int32_t*>(ws + plan.off_flags);
+    b.warm = plan.warm;
 #define KDA_BWD(DKV, DVV) \
     if (dk == DKV && dv == DVV) return launch_bwd_chunk<DT, DKV, DVV>(b, plan, stream);
     KDA_BWD(32, 32) KDA_BWD(32, 64) KDA_BWD(32, 128)

@@ -356,7 +356,9 @@ def test_backward_validation(L):
     assert b"without checkpoints" in L.kda_last_error()
     # the test entry point validates its segment length first
     assert L.kda_test_backward(FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 256, 2, 64, 64, None, None, 0, 64, None, None,
-                               FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, BF16, FAKE, 1 << 30, -1, None) == 1
+                               FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, BF16, FAKE, 1 << 30, -1, -1, None) == 1
+    assert L.kda_test_backward(FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 256, 2, 64, 64, None, None, 0, 64, None, None,
+                               FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, BF16, FAKE, 1 << 30, 0, 40, None) == 1
     # 128 heads: the planner gives the sequence one segment; forced 64-token
     # segments need a summary and an incoming gradient each
     assert L.kda_test_backward_workspace_size(4096, 1, 128, 64, 64, 64) > L.kda_test_backward_workspace_size(

@@ -25,7 +25,7 @@ def kda():
     return m
 
 
-def run_case(kda, wl, with_ckpt, heads=None, seed=5, interval=64, seg_tokens=None):
+def run_case(kda, wl, with_ckpt, heads=None, seed=5, interval=64, seg_tokens=None, warm_tokens=-1):
     """GPU backward of the prefill on wl's inputs (gate applied on the host by
     the oracle, so both sides take the same g), against the oracle on `heads`."""
     import torch
@@ -50,7 +50,8 @@ def run_case(kda, wl, with_ckpt, heads=None, seed=5, interval=64, seg_tokens=Non
                                         cu_seqlens_host=wl.cu_seqlens if wl.N > 1 else None,
                                         initial_state=S0d)
     out = kda.kda_backward(d["q"], d["k"], d["v"], d["g"], d["beta"], d_o=dev(dO, dt), d_final_state=dev(dS),
-                           cu_seqlens=cu, initial_state=S0d, ckpt=ck, interval=interval, seg_tokens=seg_tokens)
+                           cu_seqlens=cu, initial_state=S0d, ckpt=ck, interval=interval, seg_tokens=seg_tokens,
+                           warm_tokens=warm_tokens)
     torch.cuda.synchronize()
     hs = list(range(wl.H)) if heads is None else heads
     sel = lambda a: a[:, hs]
@@ -83,22 +84,29 @@ def test_backward_no_initial_state(kda):
     run_case(kda, wl, with_ckpt=True)
 
 
-def test_backward_8k_sampled_heads(kda):
+@pytest.mark.parametrize("warm", [-1, 0])
+def test_backward_8k_sampled_heads(kda, warm):
     """The 8K workload's shape (H=32, d=128, bf16) with the forward's checkpoints;
-    two heads against the oracle."""
+    two heads against the oracle; segment end gradients from the windows (the
+    default) or from the summary pass and scan."""
     wl = synth.PREFILL_8K.with_(state_std=0.1)
-    announce("backward 8K, heads 3 and 29")
-    run_case(kda, wl, with_ckpt=True, heads=[3, 29])
+    announce(f"backward 8K, heads 3 and 29, window {warm}")
+    run_case(kda, wl, with_ckpt=True, heads=[3, 29], warm_tokens=warm)
 
 
+@pytest.mark.parametrize("warm", [-1, 0, 32])
+@pytest.mark.parametrize("zshift", [0.0, -2.0])
 @pytest.mark.parametrize("seg_tokens", [64, 192, 100000])
-def test_backward_segment_lengths(kda, seg_tokens):
-    """Segments of 1 and 3 chunks (summary, scan, full pass per segment) and one
-    segment per sequence (no scan step), through the test entry point."""
+def test_backward_segment_lengths(kda, seg_tokens, zshift, warm):
+    """Segments of 1 and 3 chunks and one segment per sequence, through the
+    test entry point; each segment's end gradient from a window after it (128
+    or 32 tokens; windows that reach a sequence's end start from the final
+    state's gradient; with the slower decay of z - 2 the summary pass and scan
+    take over) or from the summary pass and scan alone (warm = 0)."""
     wl = synth.VARLEN_64.with_(H=2, dk=64, dv=32, dtype="f32", seqlens=(500, 0, 64, 129),
-                               state_std=0.1, z_shift=-2.0)
-    announce(f"backward segments of {seg_tokens} tokens")
-    run_case(kda, wl, with_ckpt=False, seg_tokens=seg_tokens)
+                               state_std=0.1, z_shift=zshift)
+    announce(f"backward segments of {seg_tokens} tokens, z shift {zshift}, window {warm}")
+    run_case(kda, wl, with_ckpt=False, seg_tokens=seg_tokens, warm_tokens=warm)
 
 
 @pytest.mark.parametrize("interval", [128, 512])
