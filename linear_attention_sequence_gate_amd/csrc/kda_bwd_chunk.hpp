@@ -185,19 +185,87 @@ constexpr int bwd_prep_parts(int nt, int dk)
     return p;
 }
 
-// Every state-independent operand of one sub-chunk (tokens t_s .. t_s + n - 1
-// of head h), by the whole workgroup.  FWD: a forward sub-chunk (K~^T in the
-// shared slot, no dO or Q^ tiles); otherwise a backward one (K-^T, dO).
+// One sub-chunk's raw inputs in a prep thread's registers, loaded ahead of
+// their use (the loads stay in flight across the barriers of the sub-chunk
+// before).  PARTS adjacent lanes per channel, each over a run of TPT tokens of
+// g, k and q; 16-byte units of the v and dO rows; one beta per thread of the
+// first BSUB.
+template <typename C, typename DT>
+struct BwdRaw {
+    using STG = typename DT::storage;
+    static constexpr int PARTS = bwd_prep_parts(C::NT, C::DK), TPT = BSUB / PARTS;
+    static constexpr int EPU = 16 / int(sizeof(STG));           // elements per 16-byte unit
+    static constexpr int UPR = C::DV / EPU, NUV = BSUB * UPR;   // units per row, per sub-chunk
+    static constexpr int UPT = (NUV + C::NT - 1) / C::NT;       // units per thread
+    STG g[TPT], k[TPT], q[TPT];
+    u32x4 v[UPT], d[UPT];
+    STG b;
+};
+
+// Issue the loads of sub-chunk (tokens t_s .. t_s + n - 1 of head h).  FWD
+// sub-chunks need no q or dO.  Rows past the end re-read the last valid row,
+// so every load stays inside the sequence.
 template <typename C, typename DT, bool FULL>
-__device__ __forceinline__ void bwd_prep(const BackwardArgs& a, unsigned char* sm, int64_t t_s, int n, int h,
-                                         bool fwd)
+__device__ __forceinline__ void bwd_prep_load(BwdRaw<C, DT>& R, const BackwardArgs& a, int64_t t_s, int n, int h,
+                                              bool fwd)
 {
-    using O = Op<DT>;
-    using OT = typename O::T;
+    using RW = BwdRaw<C, DT>;
     using STG = typename DT::storage;
     constexpr int DK = C::DK, DV = C::DV;
     const int tid = fresh_tid();
     const int64_t H = a.H;
+    const int64_t row0 = t_s * H + h;
+    const uint32_t rsk = uint32_t(H) * DK, rsv = uint32_t(H) * DV;
+    if (tid < DK * RW::PARTS) {
+        const int c = tid / RW::PARTS, part = tid % RW::PARTS, r0 = part * RW::TPT;
+        const STG* gb = static_cast<const STG*>(a.g) + row0 * DK;
+        const STG* kb = static_cast<const STG*>(a.k) + row0 * DK;
+        const STG* qb = static_cast<const STG*>(a.q) + row0 * DK;
+#pragma unroll
+        for (int i = 0; i < RW::TPT; ++i) {
+            const int r = r0 + i;
+            const uint32_t off = uint32_t(r < n ? r : n - 1) * rsk + uint32_t(c);
+            R.g[i] = gb[off];
+            R.k[i] = kb[off];
+            if (!fwd) R.q[i] = qb[off];
+        }
+    }
+    if (FULL || !fwd) {
+        const STG* v = static_cast<const STG*>(a.v) + row0 * DV;
+        const STG* dO = static_cast<const STG*>(a.d_o);
+#pragma unroll
+        for (int i = 0; i < RW::UPT; ++i) {
+            const int u = tid + i * C::NT;
+            if (RW::NUV % C::NT == 0 || u < RW::NUV) {
+                const int r = u / RW::UPR, col = (u % RW::UPR) * RW::EPU;
+                const uint32_t off = uint32_t(r < n ? r : n - 1) * rsv + uint32_t(col);
+                if (FULL) R.v[i] = *reinterpret_cast<const u32x4*>(v + off);
+                if (!fwd && dO) R.d[i] = *reinterpret_cast<const u32x4*>(dO + row0 * DV + off);
+            }
+        }
+    }
+    if (tid < BSUB && tid < n) R.b = static_cast<const STG*>(a.beta)[row0 + int64_t(tid) * H];
+}
+
+template <typename DT>
+__device__ __forceinline__ float raw_elem(const u32x4& w, int e)
+{
+    if constexpr (DT::is_bf16) return (e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1]);
+    else return __uint_as_float(w[e]);
+}
+
+// Every state-independent operand of one sub-chunk from its raw inputs, into
+// LDS, by the whole workgroup.  FWD: a forward sub-chunk (K~^T in the shared
+// slot, no dO or Q^ tiles); otherwise a backward one (K-^T, dO).
+template <typename C, typename DT, bool FULL>
+__device__ __forceinline__ void bwd_prep_store(const BwdRaw<C, DT>& R, const BackwardArgs& a, unsigned char* sm,
+                                               int n, bool fwd)
+{
+    using O = Op<DT>;
+    using OT = typename O::T;
+    using RW = BwdRaw<C, DT>;
+    constexpr int DK = C::DK;
+    const int tid = fresh_tid();
     OT* sKH = reinterpret_cast<OT*>(sm + C::O_KH);
     OT* sKM = reinterpret_cast<OT*>(sm + C::O_KM);
     OT* sQH = reinterpret_cast<OT*>(sm + C::O_QH);
@@ -207,35 +275,20 @@ __device__ __forceinline__ void bwd_prep(const BackwardArgs& a, unsigned char* s
     OT* sQHT = reinterpret_cast<OT*>(sm + C::O_QHT);
     float* sG = reinterpret_cast<float*>(sm + C::O_G);
     float* sGam = reinterpret_cast<float*>(sm + C::O_GAM);
-    const STG* g = static_cast<const STG*>(a.g);
-    const STG* k = static_cast<const STG*>(a.k);
-    const STG* q = static_cast<const STG*>(a.q);
-    // uniform bases at the sub-chunk's first row; lanes add 32-bit offsets
-    const int64_t row0 = t_s * H + h;
-    const uint32_t rsk = uint32_t(H) * DK, rsv = uint32_t(H) * DV;
-    // PARTS adjacent lanes per channel, each over a run of TPT tokens: the
-    // running sum of g crosses the runs as a lane scan.  Rows past the end
-    // re-read the last valid row (so every load is issued up front) and count as 0.
-    constexpr int PARTS = bwd_prep_parts(C::NT, DK), TPT = BSUB / PARTS;
+    auto cvt = [](typename DT::storage x) {
+        if constexpr (DT::is_bf16) return bf16_to_f32(x);
+        else return float(x);
+    };
+    // the running sum of g crosses the runs as a lane scan; rows past the end
+    // count as 0
+    constexpr int PARTS = RW::PARTS, TPT = RW::TPT;
     if (tid < DK * PARTS) {
         const int c = tid / PARTS, part = tid % PARTS, r0 = part * TPT;
-        const STG* gb = g + row0 * DK;
-        const STG* kb = k + row0 * DK;
-        const STG* qb = q + row0 * DK;
-        float gr[TPT], kr[TPT], qr[TPT];
-#pragma unroll
-        for (int i = 0; i < TPT; ++i) {
-            const int r = r0 + i;
-            const uint32_t off = uint32_t(r < n ? r : n - 1) * rsk + uint32_t(c);
-            gr[i] = load_elem<DT>(gb, off);
-            kr[i] = load_elem<DT>(kb, off);
-            if (!fwd) qr[i] = load_elem<DT>(qb, off);
-        }
         float G[TPT];
         float run = 0.f;
 #pragma unroll
         for (int i = 0; i < TPT; ++i) {
-            run += r0 + i < n ? gr[i] : 0.f;
+            run += r0 + i < n ? cvt(R.g[i]) : 0.f;
             G[i] = run;
         }
         // exclusive prefix over the runs before this one, and the sub-chunk's total
@@ -254,7 +307,7 @@ __device__ __forceinline__ void bwd_prep(const BackwardArgs& a, unsigned char* s
             const bool ok = r < n;
             const float Gr = excl + G[i];
             if (FULL && !fwd) sG[r * DK + c] = Gr;
-            const float kv = ok ? kr[i] : 0.f;
+            const float kv = ok ? cvt(R.k[i]) : 0.f;
             const float eG = __expf(Gr), eM = __expf(-Gr), eT = __expf(total - Gr);
             const OT kh = O::to_op(kv * eG), km = O::to_op(kv * eM), kt = O::to_op(kv * eT);
             sKH[r * C::SK + c] = kh;
@@ -265,42 +318,29 @@ __device__ __forceinline__ void bwd_prep(const BackwardArgs& a, unsigned char* s
             }
             if (FULL) sKMT[c * C::S16 + r] = fwd ? kt : km;
             if (!fwd) {
-                const OT qh = O::to_op((ok ? qr[i] : 0.f) * eG);
+                const OT qh = O::to_op((ok ? cvt(R.q[i]) : 0.f) * eG);
                 sQH[r * C::SK + c] = qh;
                 sQHT[c * C::S16 + r] = qh;
             }
         }
     }
     if (FULL || !fwd) {
-        // v and dO rows in 8-element units, all loads first
+        // v and dO rows, 16-byte units
         OT* sV = reinterpret_cast<OT*>(sm + C::O_VY);
         OT* sDO = reinterpret_cast<OT*>(sm + C::O_DO);
         OT* sDOT = reinterpret_cast<OT*>(sm + C::O_DOT);
-        const STG* v = static_cast<const STG*>(a.v);
-        const STG* dO = static_cast<const STG*>(a.d_o);
-        constexpr int UPR = DV / 8, NU = BSUB * UPR, UPT = (NU + C::NT - 1) / C::NT;
-        float xv[UPT][8], xd[UPT][8];
+        const bool has_do = a.d_o != nullptr;
 #pragma unroll
-        for (int i = 0; i < UPT; ++i) {
+        for (int i = 0; i < RW::UPT; ++i) {
             const int u = tid + i * C::NT;
-            if (NU % C::NT == 0 || u < NU) {
-                const int r = u / UPR, col = (u % UPR) * 8;
-                const uint32_t off = uint32_t(r < n ? r : n - 1) * rsv + uint32_t(col);
-                if (FULL) load8<DT>(v + row0 * DV + off, xv[i]);
-                if (!fwd && dO) load8<DT>(dO + row0 * DV + off, xd[i]);
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < UPT; ++i) {
-            const int u = tid + i * C::NT;
-            if (NU % C::NT == 0 || u < NU) {
-                const int r = u / UPR, col = (u % UPR) * 8;
+            if (RW::NUV % C::NT == 0 || u < RW::NUV) {
+                const int r = u / RW::UPR, col = (u % RW::UPR) * RW::EPU;
                 const bool ok = r < n;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    if (FULL) sV[r * C::SV + col + e] = O::to_op(ok ? xv[i][e] : 0.f);
+                for (int e = 0; e < RW::EPU; ++e) {
+                    if (FULL) sV[r * C::SV + col + e] = O::to_op(ok ? raw_elem<DT>(R.v[i], e) : 0.f);
                     if (!fwd) {
-                        const OT d = O::to_op((ok && dO) ? xd[i][e] : 0.f);
+                        const OT d = O::to_op((ok && has_do) ? raw_elem<DT>(R.d[i], e) : 0.f);
                         if (FULL) sDO[r * C::SV + col + e] = d;
                         sDOT[(col + e) * C::S16 + r] = d;
                     }
@@ -310,8 +350,25 @@ __device__ __forceinline__ void bwd_prep(const BackwardArgs& a, unsigned char* s
     }
     if (tid < BSUB) {
         float* sB = reinterpret_cast<float*>(sm + C::O_BETA);
-        sB[tid] = tid < n ? load_elem<DT>(static_cast<const STG*>(a.beta) + row0, uint32_t(tid) * uint32_t(H)) : 0.f;
+        sB[tid] = tid < n ? cvt(R.b) : 0.f;
     }
+}
+
+// Where a prep reads: tokens t .. t + n - 1, forward or backward sub-chunk.
+struct BwdPrepAt {
+    int64_t t;
+    int n;
+    bool fwd, valid;
+};
+
+// Both halves at once (the summary pass, which does not prefetch).
+template <typename C, typename DT, bool FULL>
+__device__ __forceinline__ void bwd_prep(const BackwardArgs& a, unsigned char* sm, int64_t t_s, int n, int h,
+                                         bool fwd)
+{
+    BwdRaw<C, DT> R;
+    bwd_prep_load<C, DT, FULL>(R, a, t_s, n, h, fwd);
+    bwd_prep_store<C, DT, FULL>(R, a, sm, n, fwd);
 }
 
 // P (lower with the diagonal), by one wave on the matrix cores.
@@ -586,6 +643,14 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
     float* slotsB = slots + BNSUB * DK * DV;  // row-major copies (when the state is not staged in LDS)
     float* gdsn = slots + BNSUB * (C::S_LDS ? 1 : 2) * DK * DV;
     OT* sS = reinterpret_cast<OT*>(sm + C::O_SS);
+    // phases (timing build): 0-2 forward sub-chunk prep / small / update,
+    // 3 checkpoint load and state slots, 4-7 backward prep / small / chain
+    // waves / slices, 8 the item's end
+    PhaseClock pclk;
+#ifdef KDA_PHASE_TIMING
+    pclk.on = threadIdx.x == KDA_PHASE_TID;
+    pclk.last = clock64();
+#endif
 
     // X = V - K^ S and U = T Diag(beta) X for this wave's columns; S tiles from st(kt, ct)
     auto fwd_xu = [&](auto&& st, f32x4 (&X)[CT], f32x4 (&U)[CT]) {
@@ -634,13 +699,17 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
             }
         }
     };
-    auto fwd_sub = [&](f32x4 (&S)[NCT][CT], int64_t t_s, int n, int h) {
-        bwd_prep<C, DT, true>(a, sm, t_s, n, h, true);
+    // one forward sub-chunk; prep() puts its operands into LDS
+    auto fwd_sub = [&](f32x4 (&S)[NCT][CT], auto&& prep) {
+        prep();
         __syncthreads();
+        KDA_PHASE(0);
         if (wave == 0) bwd_small<C, DT, true>(sm, fresh_lane(), false);
         __syncthreads();
+        KDA_PHASE(1);
         if (chain) fwd_update(S);
         __syncthreads();
+        KDA_PHASE(2);
     };
     auto store_tiles = [&](const f32x4 (&S)[NCT][CT], float* dst) {
         const int lane = fresh_lane(), l16 = lane & 15, q4 = lane >> 4;
@@ -672,22 +741,67 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
         f32x4 dS[NCT][CT];
         if (chain) load_tiles(dS, a.dsend + int64_t(item) * DK * DV);
         const int64_t j0 = (L.t0 - c0) / BWD_CHUNK, j1 = (L.t1 - c0 + BWD_CHUNK - 1) / BWD_CHUNK;
+        // Chunk j: its first token, length, sub-chunks, and the checkpoint the
+        // state before it is rebuilt from: the nearest one at or before its
+        // start that the buffer holds (with interval 64, the one at its start),
+        // else the initial state, m = the sequence's checkpoints used.
+        auto chunk_t0 = [&](int64_t j) { return c0 + j * BWD_CHUNK; };
+        auto chunk_len = [&](int64_t j) {
+            const int64_t r = L.t1 - chunk_t0(j);
+            return int(r < BWD_CHUNK ? r : BWD_CHUNK);
+        };
+        auto chunk_ck = [&](int64_t j) {
+            int64_t m = j * BWD_CHUNK / a.ckpt_interval;
+            if (m > a.ckpt_cap - ck0) m = a.ckpt_cap - ck0;
+            return a.ckpt ? m : int64_t(0);
+        };
+        // The item's sub-chunk preps in order: per chunk (last to first) the
+        // forward sub-chunks from the rebuild point up to the chunk's last
+        // sub-chunk start, then the chunk's sub-chunks in reverse.  Each prep's
+        // loads are issued as soon as the one before has gone into LDS.
+        auto first_prep = [&](int64_t j) -> BwdPrepAt {
+            const int64_t t0 = chunk_t0(j);
+            const int clen = chunk_len(j), nsub = (clen + BSUB - 1) / BSUB;
+            const int64_t fend = t0 + int64_t(nsub - 1) * BSUB, m = chunk_ck(j);
+            const int64_t from = m >= 1 ? c0 + m * a.ckpt_interval : c0;
+            if (from < fend) return {from, BSUB, true, true};
+            return {fend, clen - (nsub - 1) * BSUB, false, true};
+        };
+        auto next_prep = [&](const BwdPrepAt& c, int64_t j) -> BwdPrepAt {
+            const int64_t t0 = chunk_t0(j);
+            const int clen = chunk_len(j), nsub = (clen + BSUB - 1) / BSUB;
+            const int64_t fend = t0 + int64_t(nsub - 1) * BSUB;
+            if (c.fwd) {
+                if (c.t + BSUB < fend) return {c.t + BSUB, BSUB, true, true};
+                return {fend, clen - (nsub - 1) * BSUB, false, true};
+            }
+            if (c.t > t0) return {c.t - BSUB, BSUB, false, true};
+            if (j - 1 >= j0) return first_prep(j - 1);
+            return {0, 0, false, false};
+        };
+        BwdRaw<C, DT> R;
+        BwdPrepAt cur = {0, 0, false, false};
+        if (j1 > j0) {
+            cur = first_prep(j1 - 1);
+            bwd_prep_load<C, DT, true>(R, a, cur.t, cur.n, h, cur.fwd);
+        }
+        auto consume = [&](int64_t j) {
+            bwd_prep_store<C, DT, true>(R, a, sm, cur.n, cur.fwd);
+            const BwdPrepAt nx = next_prep(cur, j);
+            if (nx.valid) bwd_prep_load<C, DT, true>(R, a, nx.t, nx.n, h, nx.fwd);
+            cur = nx;
+        };
         for (int64_t j = j1 - 1; j >= j0; --j) {
-            const int64_t t0 = c0 + j * BWD_CHUNK;
-            const int clen = int((L.t1 - t0) < BWD_CHUNK ? (L.t1 - t0) : BWD_CHUNK);
+            const int64_t t0 = chunk_t0(j);
+            const int clen = chunk_len(j);
             const int nsub = (clen + BSUB - 1) / BSUB;
-            // the state before token t0: rebuilt from the nearest checkpoint at
-            // or before t0 that the buffer holds (with interval 64, the
-            // checkpoint at t0 itself), else from the initial state
             {
                 f32x4 S[NCT][CT];
                 const float* init = a.init ? a.init + unit * DK * DV : nullptr;
-                int64_t m = j * BWD_CHUNK / a.ckpt_interval;  // checkpoints of the sequence before t0
-                if (m > a.ckpt_cap - ck0) m = a.ckpt_cap - ck0;
-                const bool have_ck = a.ckpt && m >= 1;
-                const int64_t from = have_ck ? c0 + m * a.ckpt_interval : c0;
-                if (chain) load_tiles(S, have_ck ? a.ckpt + ((ck0 + m - 1) * H + h) * DK * DV : init);
-                for (int64_t t = from; t < t0; t += BSUB) fwd_sub(S, t, BSUB, h);
+                const int64_t m = chunk_ck(j);
+                const int64_t from = m >= 1 ? c0 + m * a.ckpt_interval : c0;
+                if (chain) load_tiles(S, m >= 1 ? a.ckpt + ((ck0 + m - 1) * H + h) * DK * DV : init);
+                for (int64_t t = from; t < t0; t += BSUB) fwd_sub(S, [&] { consume(j); });
                 // forward through the chunk, keeping the state at each sub-chunk start
                 for (int s = 0; s < nsub; ++s) {
                     if (chain) {
@@ -709,10 +823,12 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
                                         dstB[uint32_t((16 * rt + 4 * q4 + jj) * DV + col0 + 16 * ct + l16)] = S[rt][ct][jj];
                         }
                     }
-                    if (s + 1 < nsub) fwd_sub(S, t0 + s * BSUB, BSUB, h);
+                    KDA_PHASE(3);
+                    if (s + 1 < nsub) fwd_sub(S, [&] { consume(j); });
                 }
             }
             __syncthreads();  // every slot is written
+            KDA_PHASE(3);
             for (int s = nsub - 1; s >= 0; --s) {
                 const int64_t t_s = t0 + s * BSUB;
                 const int n = clen - s * BSUB < BSUB ? clen - s * BSUB : BSUB;
@@ -724,11 +840,13 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
                 float* dkb = a.dk + row0 * DK;
                 float* dgb = a.dg + row0 * DK;
                 float* dvb = a.dv + row0 * DV;
-                bwd_prep<C, DT, true>(a, sm, t_s, n, h, false);
+                consume(j);
                 __syncthreads();
+                KDA_PHASE(4);
                 if (wave == 0) bwd_small<C, DT, true>(sm, fresh_lane(), false);
                 else if (wave == 1) bwd_small_p<C, DT>(sm, fresh_lane());
                 __syncthreads();
+                KDA_PHASE(5);
                 if (chain) {
                     const int lane = fresh_lane(), l16 = lane & 15, q4 = lane >> 4;
                     f32x4 X[CT], U[CT], dY[CT], dX[CT];
@@ -781,6 +899,7 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
                     }
                 }
                 __syncthreads();
+                KDA_PHASE(6);
                 if (wave < C::NU) {
                     const int lane = fresh_lane(), l16 = lane & 15, q4 = lane >> 4;
                     const int ch0 = 16 * wave, c = ch0 + l16;  // this wave's 16 channels
@@ -911,11 +1030,14 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
                     }
                 }
                 __syncthreads();
+                KDA_PHASE(7);
             }
         }
         // the first segment of a sequence ends at the initial state's gradient
         if (L.s == 0 && chain) store_tiles(dS, a.d_init + unit * DK * DV);
+        KDA_PHASE(8);
     }
+    pclk.save();
 }
 
 template <typename DT, int DK, int DV>
