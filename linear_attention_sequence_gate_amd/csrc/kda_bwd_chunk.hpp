@@ -85,9 +85,8 @@ struct BwdLayout {
     static constexpr int O_QHT = O_KMT + (FULL ? TT : 0);       // Q^^T
     static constexpr int O_VY = O_QHT + TT;                     // v, then dY (column by column)
     static constexpr int O_DO = O_VY + (FULL ? TV : 0);         // dO
-    static constexpr int O_U = O_DO + (FULL ? TV : 0);          // U
-    static constexpr int O_DOT = O_U + (FULL ? TV : 0);         // dO^T [DV][S16]
-    static constexpr int O_DSN = O_DOT + DV * S16 * ES;         // dS' [DK][SV]
+    static constexpr int O_U = O_DO + TV;                       // U
+    static constexpr int O_DSN = O_U + (FULL ? TV : 0);         // dS' [DK][SV]
     static constexpr int O_SS = O_DSN + ((FULL && DSN_LDS) ? DK * SV * ES : 0);  // S [DK][SV]
     static constexpr int O_QA = O_SS + (S_LDS ? DK * SV * ES : 0);  // -Diag(beta) A'
     static constexpr int O_T = O_QA + T16;                      // T
@@ -183,6 +182,37 @@ constexpr int bwd_prep_parts(int nt, int dk)
     int p = 1;
     while (p * 2 <= nt / dk && p * 2 <= BSUB) p *= 2;
     return p;
+}
+
+// N consecutive LDS elements from registers in 16-byte (or smaller) vector
+// writes; p is aligned to the write size (N * sizeof(T), or 16 beyond it).
+template <int B>
+struct LdsVec;
+template <>
+struct LdsVec<2> { using T = uint16_t; };
+template <>
+struct LdsVec<4> { using T = uint32_t; };
+template <>
+struct LdsVec<8> { using T = u32x2; };
+template <>
+struct LdsVec<16> { using T = u32x4; };
+template <typename T, int N>
+__device__ __forceinline__ void st_run(T* p, const T (&x)[N])
+{
+    constexpr int B = N * int(sizeof(T));
+    if constexpr (B <= 16) {
+        typename LdsVec<B>::T w;
+        __builtin_memcpy(&w, x, B);
+        *reinterpret_cast<typename LdsVec<B>::T*>(p) = w;
+    } else {
+        constexpr int M = 16 / int(sizeof(T));
+#pragma unroll
+        for (int h = 0; h < N / M; ++h) {
+            u32x4 w;
+            __builtin_memcpy(&w, x + h * M, 16);
+            *reinterpret_cast<u32x4*>(p + h * M) = w;
+        }
+    }
 }
 
 // One sub-chunk's raw inputs in a prep thread's registers, loaded ahead of
@@ -301,6 +331,9 @@ __device__ __forceinline__ void bwd_prep_store(const BwdRaw<C, DT>& R, const Bac
         const float total = __shfl(incl, PARTS - 1, PARTS);
         const float excl = incl - run;
         if (part == PARTS - 1) sGam[c] = __expf(total);
+        // token-major tiles element by element; this thread's run of tokens
+        // of a channel-major tile in one vector write
+        OT khr[TPT], kmtr[TPT], qhr[TPT];
 #pragma unroll
         for (int i = 0; i < TPT; ++i) {
             const int r = r0 + i;
@@ -312,39 +345,34 @@ __device__ __forceinline__ void bwd_prep_store(const BwdRaw<C, DT>& R, const Bac
             const OT kh = O::to_op(kv * eG), km = O::to_op(kv * eM), kt = O::to_op(kv * eT);
             sKH[r * C::SK + c] = kh;
             sKM[r * C::SK + c] = km;
-            if (!fwd) {  // the forward sub-chunks read K^ (rows), K- and K~^T only
-                sKHT[c * C::S16 + r] = kh;
-                sKT[r * C::SK + c] = kt;
-            }
-            if (FULL) sKMT[c * C::S16 + r] = fwd ? kt : km;
+            if (!fwd) sKT[r * C::SK + c] = kt;  // the forward sub-chunks read K^ (rows), K- and K~^T only
+            khr[i] = kh;
+            kmtr[i] = fwd ? kt : km;
             if (!fwd) {
                 const OT qh = O::to_op((ok ? cvt(R.q[i]) : 0.f) * eG);
                 sQH[r * C::SK + c] = qh;
-                sQHT[c * C::S16 + r] = qh;
+                qhr[i] = qh;
             }
         }
+        if (!fwd) st_run(sKHT + c * C::S16 + r0, khr);
+        if (FULL) st_run(sKMT + c * C::S16 + r0, kmtr);
+        if (!fwd) st_run(sQHT + c * C::S16 + r0, qhr);
     }
     if (FULL || !fwd) {
-        // v and dO rows, 16-byte units
+        // v and dO rows: the 16-byte units as loaded (the operand type is the
+        // storage type), zero past the end
         OT* sV = reinterpret_cast<OT*>(sm + C::O_VY);
         OT* sDO = reinterpret_cast<OT*>(sm + C::O_DO);
-        OT* sDOT = reinterpret_cast<OT*>(sm + C::O_DOT);
         const bool has_do = a.d_o != nullptr;
+        const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int i = 0; i < RW::UPT; ++i) {
             const int u = tid + i * C::NT;
             if (RW::NUV % C::NT == 0 || u < RW::NUV) {
                 const int r = u / RW::UPR, col = (u % RW::UPR) * RW::EPU;
                 const bool ok = r < n;
-#pragma unroll
-                for (int e = 0; e < RW::EPU; ++e) {
-                    if (FULL) sV[r * C::SV + col + e] = O::to_op(ok ? raw_elem<DT>(R.v[i], e) : 0.f);
-                    if (!fwd) {
-                        const OT d = O::to_op((ok && has_do) ? raw_elem<DT>(R.d[i], e) : 0.f);
-                        if (FULL) sDO[r * C::SV + col + e] = d;
-                        sDOT[(col + e) * C::S16 + r] = d;
-                    }
-                }
+                if (FULL) *reinterpret_cast<u32x4*>(sV + r * C::SV + col) = ok ? R.v[i] : zero;
+                if (!fwd) *reinterpret_cast<u32x4*>(sDO + r * C::SV + col) = (ok && has_do) ? R.d[i] : zero;
             }
         }
     }
@@ -439,7 +467,7 @@ __device__ __forceinline__ void bwd_dstep(unsigned char* sm, f32x4 (&dS)[C::DK /
     const OT* sKT = reinterpret_cast<const OT*>(sm + C::O_KT);
     const OT* sKHT = reinterpret_cast<const OT*>(sm + C::O_KHT);
     const OT* sQHT = reinterpret_cast<const OT*>(sm + C::O_QHT);
-    const OT* sDOT = reinterpret_cast<const OT*>(sm + C::O_DOT);
+    const OT* sDO = reinterpret_cast<const OT*>(sm + C::O_DO);
     const OT* sT = reinterpret_cast<const OT*>(sm + C::O_T);
     const OT* sP = reinterpret_cast<const OT*>(sm + C::O_P);
     const float* sB = reinterpret_cast<const float*>(sm + C::O_BETA);
@@ -447,7 +475,7 @@ __device__ __forceinline__ void bwd_dstep(unsigned char* sm, f32x4 (&dS)[C::DK /
     typename O::Frag4 bdo[C::CT];
     if constexpr (HASDO) {
 #pragma unroll
-        for (int ct = 0; ct < C::CT; ++ct) bdo[ct] = frag_rows<O>(sDOT + (col0 + 16 * ct) * C::S16, C::S16, lane);  // B = dO
+        for (int ct = 0; ct < C::CT; ++ct) bdo[ct] = frag_cols<O>(sDO + col0 + 16 * ct, C::SV, lane);  // B = dO
     }
     const auto aTt = frag_cols<O>(sT, C::S16, lane);  // A = T^T
 #pragma unroll
