@@ -166,12 +166,18 @@ __device__ __forceinline__ int fresh_tid()
 }
 
 // sum over the 16 lanes of a row of 16 (lane bits 0..3)
+// (DPP rotations inside each row of 16 lanes, on the VALU: no LDS round trip)
+template <int CTRL>
+__device__ __forceinline__ float dpp_row(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
 __device__ __forceinline__ float sum16(float x)
 {
-    x += __shfl_xor(x, 1, 64);
-    x += __shfl_xor(x, 2, 64);
-    x += __shfl_xor(x, 4, 64);
-    x += __shfl_xor(x, 8, 64);
+    x += dpp_row<0x128>(x);  // row_ror:8
+    x += dpp_row<0x124>(x);  // row_ror:4
+    x += dpp_row<0x122>(x);  // row_ror:2
+    x += dpp_row<0x121>(x);  // row_ror:1
     return x;
 }
 
@@ -230,14 +236,24 @@ struct BwdRaw {
     STG g[TPT], k[TPT], q[TPT];
     u32x4 v[UPT], d[UPT];
     STG b;
+    // Wait for these loads here: called before a thread's next global store.
+    // A later wait on them (after stores issued since) is counted in one
+    // in-order counter with those stores, and would wait for them too.
+    __device__ __forceinline__ void settle() const
+    {
+#pragma unroll
+        for (int i = 0; i < TPT; ++i) asm volatile("" ::"v"(g[i]), "v"(k[i]), "v"(q[i]));
+#pragma unroll
+        for (int i = 0; i < UPT; ++i) asm volatile("" ::"v"(v[i]), "v"(d[i]));
+        asm volatile("" ::"v"(b));
+    }
 };
 
 // Issue the loads of sub-chunk (tokens t_s .. t_s + n - 1 of head h).  FWD
 // sub-chunks need no q or dO.  Rows past the end re-read the last valid row,
 // so every load stays inside the sequence.
-template <typename C, typename DT, bool FULL>
-__device__ __forceinline__ void bwd_prep_load(BwdRaw<C, DT>& R, const BackwardArgs& a, int64_t t_s, int n, int h,
-                                              bool fwd)
+template <typename C, typename DT, bool FULL, bool fwd>
+__device__ __forceinline__ void bwd_prep_load(BwdRaw<C, DT>& R, const BackwardArgs& a, int64_t t_s, int n, int h)
 {
     using RW = BwdRaw<C, DT>;
     using STG = typename DT::storage;
@@ -246,7 +262,7 @@ __device__ __forceinline__ void bwd_prep_load(BwdRaw<C, DT>& R, const BackwardAr
     const int64_t H = a.H;
     const int64_t row0 = t_s * H + h;
     const uint32_t rsk = uint32_t(H) * DK, rsv = uint32_t(H) * DV;
-    if (tid < DK * RW::PARTS) {
+    if (DK * RW::PARTS >= C::NT || tid < DK * RW::PARTS) {
         const int c = tid / RW::PARTS, part = tid % RW::PARTS, r0 = part * RW::TPT;
         const STG* gb = static_cast<const STG*>(a.g) + row0 * DK;
         const STG* kb = static_cast<const STG*>(a.k) + row0 * DK;
@@ -287,9 +303,8 @@ __device__ __forceinline__ float raw_elem(const u32x4& w, int e)
 // Every state-independent operand of one sub-chunk from its raw inputs, into
 // LDS, by the whole workgroup.  FWD: a forward sub-chunk (K~^T in the shared
 // slot, no dO or Q^ tiles); otherwise a backward one (K-^T, dO).
-template <typename C, typename DT, bool FULL>
-__device__ __forceinline__ void bwd_prep_store(const BwdRaw<C, DT>& R, const BackwardArgs& a, unsigned char* sm,
-                                               int n, bool fwd)
+template <typename C, typename DT, bool FULL, bool fwd>
+__device__ __forceinline__ void bwd_prep_store(const BwdRaw<C, DT>& R, const BackwardArgs& a, unsigned char* sm, int n)
 {
     using O = Op<DT>;
     using OT = typename O::T;
@@ -312,7 +327,7 @@ __device__ __forceinline__ void bwd_prep_store(const BwdRaw<C, DT>& R, const Bac
     // the running sum of g crosses the runs as a lane scan; rows past the end
     // count as 0
     constexpr int PARTS = RW::PARTS, TPT = RW::TPT;
-    if (tid < DK * PARTS) {
+    if (DK * PARTS >= C::NT || tid < DK * PARTS) {
         const int c = tid / PARTS, part = tid % PARTS, r0 = part * TPT;
         float G[TPT];
         float run = 0.f;
@@ -321,14 +336,27 @@ __device__ __forceinline__ void bwd_prep_store(const BwdRaw<C, DT>& R, const Bac
             run += r0 + i < n ? cvt(R.g[i]) : 0.f;
             G[i] = run;
         }
-        // exclusive prefix over the runs before this one, and the sub-chunk's total
-        float incl = run;
+        // exclusive prefix over the runs before this one, and the sub-chunk's
+        // total: within a quad of lanes by DPP quad permutes, else by shuffles
+        float incl = run, total;
+        if constexpr (PARTS == 4) {
+            const float y1 = dpp_row<0x90>(incl);  // quad_perm [0,0,1,2]
+            incl += part >= 1 ? y1 : 0.f;
+            const float y2 = dpp_row<0x40>(incl);  // quad_perm [0,0,0,1]
+            incl += part >= 2 ? y2 : 0.f;
+            total = dpp_row<0xFF>(incl);           // quad_perm [3,3,3,3]
+        } else if constexpr (PARTS == 2) {
+            const float y1 = dpp_row<0xA0>(incl);  // quad_perm [0,0,2,2]
+            incl += part >= 1 ? y1 : 0.f;
+            total = dpp_row<0xF5>(incl);           // quad_perm [1,1,3,3]
+        } else {
 #pragma unroll
-        for (int d = 1; d < PARTS; d *= 2) {
-            const float y = __shfl_up(incl, d, PARTS);
-            if (part >= d) incl += y;
+            for (int d = 1; d < PARTS; d *= 2) {
+                const float y = __shfl_up(incl, d, PARTS);
+                if (part >= d) incl += y;
+            }
+            total = __shfl(incl, PARTS - 1, PARTS);
         }
-        const float total = __shfl(incl, PARTS - 1, PARTS);
         const float excl = incl - run;
         if (part == PARTS - 1) sGam[c] = __expf(total);
         // token-major tiles element by element; this thread's run of tokens
@@ -395,8 +423,13 @@ __device__ __forceinline__ void bwd_prep(const BackwardArgs& a, unsigned char* s
                                          bool fwd)
 {
     BwdRaw<C, DT> R;
-    bwd_prep_load<C, DT, FULL>(R, a, t_s, n, h, fwd);
-    bwd_prep_store<C, DT, FULL>(R, a, sm, n, fwd);
+    if (fwd) {
+        bwd_prep_load<C, DT, FULL, true>(R, a, t_s, n, h);
+        bwd_prep_store<C, DT, FULL, true>(R, a, sm, n);
+    } else {
+        bwd_prep_load<C, DT, FULL, false>(R, a, t_s, n, h);
+        bwd_prep_store<C, DT, FULL, false>(R, a, sm, n);
+    }
 }
 
 // P (lower with the diagonal), by one wave on the matrix cores.
@@ -808,15 +841,20 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
             return {0, 0, false, false};
         };
         BwdRaw<C, DT> R;
+        auto load_prep = [&](const BwdPrepAt& p) {
+            if (p.fwd) bwd_prep_load<C, DT, true, true>(R, a, p.t, p.n, h);
+            else bwd_prep_load<C, DT, true, false>(R, a, p.t, p.n, h);
+        };
         BwdPrepAt cur = {0, 0, false, false};
         if (j1 > j0) {
             cur = first_prep(j1 - 1);
-            bwd_prep_load<C, DT, true>(R, a, cur.t, cur.n, h, cur.fwd);
+            load_prep(cur);
         }
         auto consume = [&](int64_t j) {
-            bwd_prep_store<C, DT, true>(R, a, sm, cur.n, cur.fwd);
+            if (cur.fwd) bwd_prep_store<C, DT, true, true>(R, a, sm, cur.n);
+            else bwd_prep_store<C, DT, true, false>(R, a, sm, cur.n);
             const BwdPrepAt nx = next_prep(cur, j);
-            if (nx.valid) bwd_prep_load<C, DT, true>(R, a, nx.t, nx.n, h, nx.fwd);
+            if (nx.valid) load_prep(nx);
             cur = nx;
         };
         for (int64_t j = j1 - 1; j >= j0; --j) {
@@ -833,6 +871,7 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
                 // forward through the chunk, keeping the state at each sub-chunk start
                 for (int s = 0; s < nsub; ++s) {
                     if (chain) {
+                        R.settle();
                         const int lane = fresh_lane(), l16 = lane & 15, q4 = lane >> 4;
                         float* dst = slots + s * DK * DV;  // accumulator tiles, one 16-byte vector per tile
 #pragma unroll
@@ -895,6 +934,7 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
                                 for (int jj = 0; jj < 4; ++jj)
                                     sS[(16 * kt + 4 * q4 + jj) * C::SV + col0 + 16 * ct + l16] = O::to_op(Sf[kt][ct][jj]);
                     }
+                    KDA_PHASE(9);
                     bwd_dstep<C, DT, true>(sm, dS, col0, lane, dY, dX, [&] {
                         // dS' for the per-slice products, before dS moves on
 #pragma unroll
@@ -908,6 +948,8 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
                                     else gdsn[uint32_t(row * DV + col)] = dS[rt][ct][jj];
                                 }
                     });
+                    KDA_PHASE(10);
+                    R.settle();
                     // dv = dX; dbeta's <dY, X> part; U and dY for the slices
                     float pb[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -929,6 +971,7 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
                 __syncthreads();
                 KDA_PHASE(6);
                 if (wave < C::NU) {
+                    if (!chain) R.settle();
                     const int lane = fresh_lane(), l16 = lane & 15, q4 = lane >> 4;
                     const int ch0 = 16 * wave, c = ch0 + l16;  // this wave's 16 channels
                     // raw k and q of this lane's elements (rows past the end re-read the last one)
@@ -952,29 +995,33 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
                         O::mma4(M1, fy, fu);
                         O::mma4(M1T, fu, fy);
                     }
+                    // every lane reads (all indices are in range), then masks
                     float tb[4];
+                    const float bl = sB[l16];
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj) {
                         const int r4 = 4 * q4 + jj;
                         const float m1 = M1[jj];
-                        tb[jj] = l16 < r4 ? -m1 * sAP[r4 * 17 + l16] : 0.f;
+                        const float ap = sAP[r4 * 17 + l16], br = sB[r4];
+                        tb[jj] = l16 < r4 ? -m1 * ap : 0.f;
                         dP[jj] = l16 <= r4 ? dP[jj] : 0.f;
                         dPT[jj] = r4 <= l16 ? dPT[jj] : 0.f;
-                        M1[jj] = l16 < r4 ? -sB[r4] * m1 : 0.f;
-                        M1T[jj] = r4 < l16 ? -sB[l16] * M1T[jj] : 0.f;
+                        M1[jj] = l16 < r4 ? -br * m1 : 0.f;
+                        M1T[jj] = r4 < l16 ? -bl * M1T[jj] : 0.f;
                     }
                     if (wave == 0) {
+                        // dbeta_r: this row's sum of tb plus the chain waves'
+                        // <dY_r, X_r> partials, lane l16 < NCW adding wave l16's
+                        static_assert(C::NCW <= 16, "one partial per lane of a row");
 #pragma unroll
                         for (int jj = 0; jj < 4; ++jj) {
-                            const float s = sum16(tb[jj]);
                             const int r = 4 * q4 + jj;
-                            if (l16 == 0 && r < n) {
-                                float t = s;
-                                for (int w2 = 0; w2 < C::NCW; ++w2) t += sRB[w2 * BSUB + r];
-                                a.dbeta[row0 + uint32_t(r) * uint32_t(H)] = t;
-                            }
+                            const float pr = sRB[(l16 < C::NCW ? l16 : 0) * BSUB + r];
+                            const float s = sum16(tb[jj] + (l16 < C::NCW ? pr : 0.f));
+                            if (l16 == 0 && r < n) a.dbeta[row0 + uint32_t(r) * uint32_t(H)] = s;
                         }
                     }
+                    KDA_PHASE(12);
                     const auto fdP = O::make4(dPT);   // A = dP
                     const auto fdPT = O::make4(dP);   // A = dP^T
                     const auto fdA = O::make4(M1T);   // A = dA'
@@ -1008,6 +1055,7 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
                     }
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj) aK[jj] *= -sB[4 * q4 + jj];
+                    KDA_PHASE(13);
                     const auto bkm = frag_rows<O>(sKMT + ch0 * C::S16, C::S16, lane);  // B = K-
                     O::mma4(aQ, fdP, bkm);
                     O::mma4(aK, fdA, bkm);
@@ -1036,6 +1084,7 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
                         }
                         dGr[jj] = dG;
                     }
+                    KDA_PHASE(14);
                     float tot = gl + sGam[c] * dot;
                     tot += xor_lanes(tot, 16, lane);
                     tot += xor_lanes(tot, 32, lane);

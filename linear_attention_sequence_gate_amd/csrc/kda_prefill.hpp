@@ -59,7 +59,7 @@ namespace kda {
 #endif
 __device__ unsigned long long kda_phase_cycles[16384 * 16];
 struct PhaseClock {
-    long long acc[12] = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+    long long acc[16] = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
     long long last = 0;
     bool on = false;
     __device__ void mark(int i)
@@ -73,7 +73,7 @@ struct PhaseClock {
     __device__ void save(int base = 0)
     {
         if (on && base + blockIdx.x < 16384)
-            for (int i = 0; i < 12; ++i) kda_phase_cycles[(base + blockIdx.x) * 16 + i] = acc[i];
+            for (int i = 0; i < 16; ++i) kda_phase_cycles[(base + blockIdx.x) * 16 + i] = acc[i];
     }
 };
 #else
