@@ -190,19 +190,24 @@ def measured_roofs(torch, dev, stream) -> dict:
     L.kda_roof_stream.argtypes = [I, P, P, I64, P, I64, I, I, P, ctypes.POINTER(ctypes.c_float)]
     L.kda_roof_mfma.argtypes = [I, I, P, P, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_double)]
     nbytes = 4 << 30
-    wgs = 256 * 16
     src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
     src.fill_(1)
-    sink = torch.empty(wgs * 256, dtype=torch.int32, device=dev)
+    dst.fill_(0)
+    sink = torch.empty(32768 * 256, dtype=torch.int32, device=dev)
     ms = ctypes.c_float(0.0)
     out = {}
-    for mode, name, moved in ((0, "hbm_read_gbs", nbytes), (1, "hbm_write_gbs", nbytes), (2, "hbm_copy_gbs", 2 * nbytes)):
+    # (mode, name, bytes moved per launch, workgroups: 0 = one vector per thread);
+    # the shapes are the fastest of a sweep of grid-stride widths, one to sixteen
+    # vectors per thread and streaming or plain stores on MI355X
+    for mode, name, moved, wgs in ((0, "hbm_read_gbs", nbytes, 8192), (1, "hbm_write_gbs", nbytes, 32768),
+                                   (2, "hbm_copy_gbs", 2 * nbytes, 0), (3, "hbm_inplace_gbs", 2 * nbytes, 0)):
         rc = L.kda_roof_stream(mode, src.data_ptr(), dst.data_ptr(), nbytes, sink.data_ptr(), sink.numel(), wgs, 5,
                                stream.cuda_stream, ctypes.byref(ms))
         if rc != 0:
             raise RuntimeError(f"kda_roof_stream mode {mode}: {rc}")
         out[name] = round(moved / (ms.value * 1e-3) / 1e9, 1)
+    out["hbm_rw_gbs"] = max(out["hbm_copy_gbs"], out["hbm_inplace_gbs"])
     del src, dst
     fsink = torch.empty(256 * 8 * 256, dtype=torch.float32, device=dev)
     fl = ctypes.c_double(0.0)
@@ -210,9 +215,10 @@ def measured_roofs(torch, dev, stream) -> dict:
     if rc != 0:
         raise RuntimeError(f"kda_roof_mfma: {rc}")
     out["mfma_bf16_tflops"] = round(fl.value / (ms.value * 1e-3) / 1e12, 1)
-    out["how"] = ("libkda_roofs: 16-byte vector loads/stores over 4 GiB, 4096 workgroups of 256, streaming "
-                  "stores, mean of 5 launches (copy counts read + write bytes); 2048 workgroups of 4 waves, "
-                  "each issuing 4096 x 8 independent v_mfma_f32_16x16x32_bf16")
+    out["how"] = ("libkda_roofs over 4 GiB, 16-byte vectors, mean of 5 launches: read grid-stride over 8192 "
+                  "workgroups of 256, write grid-stride over 32768, copy and in-place update one vector per "
+                  "thread (both count read + write bytes; hbm_rw_gbs is the larger); 2048 workgroups of 4 "
+                  "waves, each issuing 4096 x 8 independent v_mfma_f32_16x16x32_bf16")
     return out
 
 
@@ -240,7 +246,7 @@ def device_inputs(torch, wl, dev, seed):
     return out
 
 
-def big_leg(kda, torch, synth, wl, dev, stream, timed_loop, copy_gbs, roof_ms, steps=5):
+def big_leg(kda, torch, synth, wl, dev, stream, timed_loop, rw_gbs, roof_ms, steps=5):
     """One million-token workload: one kda_prefill_gated call per step, timed
     over `steps` back-to-back calls, with its HBM roofline and an oracle check
     of sampled outputs and final states the fp64 oracle computes exactly."""
@@ -288,7 +294,7 @@ def big_leg(kda, torch, synth, wl, dev, stream, timed_loop, copy_gbs, roof_ms, s
             "config": {"workload": wl.name, "N": N, "H": H, "T": T, "d_k": dk, "d_v": dv, "z_shift": wl.z_shift,
                        "initial_state": S0 is not None, "inputs": "drawn on the device, seeded"},
             "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(ach / HBM_PEAK_GBS, 4), "frac_of_measured_copy": round(ach / copy_gbs, 4) if copy_gbs else None,
+                         "frac": round(ach / HBM_PEAK_GBS, 4), "frac_of_measured_rw": round(ach / rw_gbs, 4) if rw_gbs else None,
                          "binding_roof_ms": roof_ms, "algorithmic_bytes_per_call": nbytes,
                          "mfma_tflops": round(flops / (ms * 1e-3) / 1e12, 1),
                          "traffic": load_traffic(wl.name), "kernel": "kda_prefill_gated"},
@@ -437,7 +443,7 @@ def main():
 
     decode = spec = backward = None
     roofs, big = {}, {}
-    copy_gbs = None
+    rw_gbs = None
     if "decode" in legs:
         # ------------------------------------------------------------- decode leg
         dwl = synth.DECODE_B256
@@ -566,17 +572,17 @@ def main():
         del bws, bck
 
     if "roofs" in legs:
-        # the device's own roofs: streaming read / write / copy kernels over 4 GiB
+        # the device's own roofs: streaming read / write / copy / in-place kernels over 4 GiB
         # (far past the 256 MB last-level cache) and back-to-back 16x16x32 bf16
         # matrix-core instructions on every SIMD (libkda_roofs)
         roofs = measured_roofs(torch, dev, stream)
-        copy_gbs = roofs["hbm_copy_gbs"]
+        rw_gbs = roofs["hbm_rw_gbs"]
         for r in (roofline, decode and decode["roofline"], spec and spec["verify"]["roofline"],
                   spec and spec["commit"]["roofline"], backward and backward["roofline"]):
             if r is None:
                 continue
-            r["measured_copy_gbs"] = round(copy_gbs, 1)
-            r["frac_of_measured_copy"] = round(r["achieved"] / copy_gbs, 4)
+            r["measured_rw_gbs"] = round(rw_gbs, 1)
+            r["frac_of_measured_rw"] = round(r["achieved"] / rw_gbs, 4)
         roofline["measured_mfma_bf16_tflops"] = roofs["mfma_bf16_tflops"]
         roofline["mfma_frac_of_measured_mfma"] = round(roofline["mfma_tflops"] / roofs["mfma_bf16_tflops"], 4)
         # a plain 8192^3 bf16 GEMM through the vendor library, for reference
@@ -592,8 +598,8 @@ def main():
 
     # ------------------------------------------- million-token workloads
     if "big" in legs:
-        big["prefill_1m"] = big_leg(kda, torch, synth, synth.PREFILL_1M, dev, stream, timed_loop, copy_gbs, 1.34)
-        big["varlen_64"] = big_leg(kda, torch, synth, synth.VARLEN_64, dev, stream, timed_loop, copy_gbs, 5.1)
+        big["prefill_1m"] = big_leg(kda, torch, synth, synth.PREFILL_1M, dev, stream, timed_loop, rw_gbs, 1.34)
+        big["varlen_64"] = big_leg(kda, torch, synth, synth.VARLEN_64, dev, stream, timed_loop, rw_gbs, 5.1)
 
     if args.copy_calib:  # plain copy of known size, for the HBM counter calibration
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)

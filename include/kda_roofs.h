@@ -18,12 +18,15 @@ extern "C" {
 
 /*
  * kda_roof_stream — mode 0 reads `bytes` of src, 1 writes `bytes` of dst,
- * 2 copies src to dst; 16-byte vector accesses, grid-stride over
- * `workgroups` workgroups of 256 threads, streaming stores.  bytes is a
- * positive multiple of 16; src and dst are 16-byte aligned device buffers of
- * at least `bytes`.  Mode 0 writes one uint32 per thread to `sink` (device,
- * at least workgroups * 256 words).  One untimed launch, then `reps` timed
- * back to back: *ms_per_launch is their mean.
+ * 2 copies src to dst, 3 updates dst in place (reads each 16-byte vector and
+ * writes it back, each word + 1); 16-byte vector accesses.  workgroups > 0:
+ * grid-stride over that many workgroups of 256 threads, four vectors in
+ * flight per thread; workgroups == 0 (modes 1-3): one vector per thread, the
+ * grid covering the buffer.  bytes is a positive multiple of 16; src and dst
+ * are 16-byte aligned device buffers of at least `bytes`.  Mode 0 writes one
+ * uint32 per thread to `sink` (device, at least workgroups * 256 words).
+ * One untimed launch, then `reps` timed back to back: *ms_per_launch is
+ * their mean.
  */
 int kda_roof_stream(int mode, const void* src, void* dst, int64_t bytes, void* sink, int64_t sink_words,
                     int workgroups, int reps, void* stream, float* ms_per_launch);

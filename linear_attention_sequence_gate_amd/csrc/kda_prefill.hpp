@@ -647,6 +647,25 @@ __device__ __forceinline__ void diag_inverse(const typename O::T* sA, typename O
     for (int j = 0; j < 4; ++j) sD[(a * 16 + 4 * q4 + j) * C::SD + l16] = O::to_op(d[j]);
 }
 
+// One product of the block substitution, acc += a b: a is a 16x16 tile of
+// the operand type, b the fp32 right-hand side as computed.  bf16: b goes in
+// as two bf16 parts, hi = bf16(b) and lo = bf16(b - hi), two matrix
+// instructions, so the right-hand side keeps about 16 bits (fp32 accumulation
+// throughout).  fp32 operands: the ordinary product.
+template <typename O>
+__device__ __forceinline__ void sub_mma(f32x4& acc, const typename O::Frag4& a, const f32x4& b)
+{
+    if constexpr (std::is_same<O, Op<BF16>>::value) {
+        const typename O::Frag4 hi = O::make4(b);
+        const u32x2 w = __builtin_bit_cast(u32x2, hi);
+        const f32x4 hf = {bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1])};
+        O::mma4(acc, a, hi);
+        O::mma4(acc, a, O::make4(b - hf));
+    } else {
+        O::mma4(acc, a, O::make4(b));
+    }
+}
+
 // The value held by lane `lane ^ dist` (dist a power of two): rows of 16 lanes
 // swap with v_permlane16_swap / v_permlane32_swap, half rows with a DPP
 // rotate, and smaller distances go through ds_bpermute.
@@ -1156,7 +1175,8 @@ prefill_block_kernel(PrefillDev p)
         KDA_PHASE(0);
         __syncthreads();
         KDA_PHASE(1);
-        // ---- beta: U = (I + A)^{-1} Diag(beta) X by block substitution:
+        // ---- beta: U = (I + A)^{-1} Diag(beta) X by block substitution, the
+        // right-hand sides in two bf16 parts (sub_mma):
         //   U_0 = D_0 beta_0 X_0,  U_1 = D_1 (beta_1 X_1 - A_10 U_0)
         const float* sBb = reinterpret_cast<const float*>(smem + C::O_B) + buf * BC;
         f32x4 U0[NCT], U1[NCT];
@@ -1169,11 +1189,11 @@ prefill_block_kernel(PrefillDev p)
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
                 U0[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-                O::mma4(U0[ct], d0, O::make4(bv0 * Xt[0][ct]));
+                sub_mma<O>(U0[ct], d0, bv0 * Xt[0][ct]);
                 f32x4 R = bv1 * Xt[1][ct];
-                O::mma4(R, a10, O::make4(U0[ct]));
+                sub_mma<O>(R, a10, U0[ct]);
                 U1[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-                O::mma4(U1[ct], d1, O::make4(R));
+                sub_mma<O>(U1[ct], d1, R);
             }
         }
         Frag Ub[NCT];
@@ -1660,11 +1680,11 @@ prefill_warm_kernel(PrefillDev p)
             for (int ct = 0; ct < 2; ++ct) {
                 if (ct == 1 && !act1) break;
                 U0[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-                O::mma4(U0[ct], d0, O::make4(bv0 * Xt[0][ct]));
+                sub_mma<O>(U0[ct], d0, bv0 * Xt[0][ct]);
                 f32x4 R = bv1 * Xt[1][ct];
-                O::mma4(R, a10, O::make4(U0[ct]));
+                sub_mma<O>(R, a10, U0[ct]);
                 U1[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-                O::mma4(U1[ct], d1, O::make4(R));
+                sub_mma<O>(U1[ct], d1, R);
                 Ub[ct] = acc_frag<DT>(U0[ct], U1[ct]);
             }
         }

@@ -2,9 +2,9 @@
 // against (not part of libkda's path).  Each entry point times its own
 // launches with HIP events on the given stream and returns the mean
 // milliseconds per launch; the caller turns that into GB/s or TFLOP/s.
-//   kda_roof_stream : read, write or copy of a device buffer with 16-byte
-//                     vector accesses, grid-stride, streaming (non-temporal)
-//                     stores, many workgroups per compute unit.
+//   kda_roof_stream : read, write, copy or in-place update of a device
+//                     buffer with 16-byte vector accesses: grid-stride over a
+//                     given number of workgroups, or one vector per thread.
 //   kda_roof_mfma   : back-to-back independent 16x16x32 bf16 matrix-core
 //                     instructions on every SIMD (the issue ceiling of the
 //                     instruction the prefill's products use).
@@ -20,8 +20,10 @@ typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 
-// mode 0: read (each thread folds what it reads into one word, written once
-// per thread so the loads cannot be dropped), 1: write, 2: copy
+// Grid-stride over `n` 16-byte vectors, four in flight per thread.  Mode 0:
+// read (each thread folds what it reads into one word, written once per
+// thread so the loads cannot be dropped), 1: write, 2: copy, 3: in place
+// (each word + 1, written back where it was read).
 template <int MODE>
 __global__ void __launch_bounds__(256) stream_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
                                                      int64_t n, uint32_t* __restrict__ sink)
@@ -32,33 +34,47 @@ __global__ void __launch_bounds__(256) stream_kernel(const u32x4* __restrict__ s
     for (; i + 3 * stride < n; i += 4 * stride) {  // four independent vectors in flight per thread
         if constexpr (MODE == 1) {
             const u32x4 w = {uint32_t(i), 0u, 0u, 0u};
-            __builtin_nontemporal_store(w, dst + i);
-            __builtin_nontemporal_store(w, dst + i + stride);
-            __builtin_nontemporal_store(w, dst + i + 2 * stride);
-            __builtin_nontemporal_store(w, dst + i + 3 * stride);
+            dst[i] = w;
+            dst[i + stride] = w;
+            dst[i + 2 * stride] = w;
+            dst[i + 3 * stride] = w;
         } else {
-            const u32x4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+            const u32x4* in = MODE == 3 ? dst : src;
+            const u32x4 a = in[i], b = in[i + stride], c = in[i + 2 * stride], d = in[i + 3 * stride];
             if constexpr (MODE == 0) {
                 acc ^= a[0] ^ a[1] ^ a[2] ^ a[3] ^ b[0] ^ b[1] ^ b[2] ^ b[3];
                 acc ^= c[0] ^ c[1] ^ c[2] ^ c[3] ^ d[0] ^ d[1] ^ d[2] ^ d[3];
             } else {
-                __builtin_nontemporal_store(a, dst + i);
-                __builtin_nontemporal_store(b, dst + i + stride);
-                __builtin_nontemporal_store(c, dst + i + 2 * stride);
-                __builtin_nontemporal_store(d, dst + i + 3 * stride);
+                const uint32_t inc = MODE == 3 ? 1u : 0u;
+                dst[i] = a + inc;
+                dst[i + stride] = b + inc;
+                dst[i + 2 * stride] = c + inc;
+                dst[i + 3 * stride] = d + inc;
             }
         }
     }
     for (; i < n; i += stride) {
         if constexpr (MODE == 1) {
-            __builtin_nontemporal_store(u32x4{uint32_t(i), 0u, 0u, 0u}, dst + i);
+            dst[i] = u32x4{uint32_t(i), 0u, 0u, 0u};
         } else {
-            const u32x4 a = src[i];
+            const u32x4 a = (MODE == 3 ? dst : src)[i];
             if constexpr (MODE == 0) acc ^= a[0] ^ a[1] ^ a[2] ^ a[3];
-            else __builtin_nontemporal_store(a, dst + i);
+            else dst[i] = MODE == 3 ? a + 1u : a;
         }
     }
     if constexpr (MODE == 0) sink[int64_t(blockIdx.x) * blockDim.x + threadIdx.x] = acc;
+}
+
+// One 16-byte vector per thread, the grid covering all `n` (modes 1-3 as
+// above): every load of a workgroup is in flight at once.
+template <int MODE>
+__global__ void __launch_bounds__(256) tile_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst, int64_t n)
+{
+    const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= n) return;
+    if constexpr (MODE == 1) dst[i] = u32x4{uint32_t(i), 0u, 0u, 0u};
+    else if constexpr (MODE == 2) dst[i] = src[i];
+    else dst[i] = dst[i] + 1u;
 }
 
 // Each wave keeps NACC independent accumulators and issues ITERS rounds of
@@ -118,19 +134,32 @@ extern "C" {
 int kda_roof_stream(int mode, const void* src, void* dst, int64_t bytes, void* sink, int64_t sink_words,
                     int workgroups, int reps, void* stream, float* ms_per_launch)
 {
-    if (mode < 0 || mode > 2 || bytes < 16 || bytes % 16 != 0 || workgroups < 1 || reps < 1 || !ms_per_launch)
+    if (mode < 0 || mode > 3 || bytes < 16 || bytes % 16 != 0 || workgroups < 0 || reps < 1 || !ms_per_launch)
         return 1;
-    if ((mode != 1 && !src) || (mode != 0 && !dst)) return 1;
+    if (workgroups == 0 && (mode == 0 || bytes / 16 > int64_t(0x7fffffff) * 256)) return 1;
+    if ((mode == 0 || mode == 2) && !src) return 1;
+    if (mode != 0 && !dst) return 1;
     if (mode == 0 && (!sink || sink_words < int64_t(workgroups) * 256)) return 1;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int64_t n = bytes / 16;
     const u32x4* in = static_cast<const u32x4*>(src);
     u32x4* out = static_cast<u32x4*>(dst);
     uint32_t* sk = static_cast<uint32_t*>(sink);
+    const unsigned tiles = unsigned((n + 255) / 256);
     auto launch = [&]() {
-        if (mode == 0) hipLaunchKernelGGL(stream_kernel<0>, dim3(workgroups), dim3(256), 0, s, in, out, n, sk);
-        else if (mode == 1) hipLaunchKernelGGL(stream_kernel<1>, dim3(workgroups), dim3(256), 0, s, in, out, n, sk);
-        else hipLaunchKernelGGL(stream_kernel<2>, dim3(workgroups), dim3(256), 0, s, in, out, n, sk);
+        if (workgroups == 0) {
+            if (mode == 1) hipLaunchKernelGGL(tile_kernel<1>, dim3(tiles), dim3(256), 0, s, in, out, n);
+            else if (mode == 2) hipLaunchKernelGGL(tile_kernel<2>, dim3(tiles), dim3(256), 0, s, in, out, n);
+            else hipLaunchKernelGGL(tile_kernel<3>, dim3(tiles), dim3(256), 0, s, in, out, n);
+        } else if (mode == 0) {
+            hipLaunchKernelGGL(stream_kernel<0>, dim3(workgroups), dim3(256), 0, s, in, out, n, sk);
+        } else if (mode == 1) {
+            hipLaunchKernelGGL(stream_kernel<1>, dim3(workgroups), dim3(256), 0, s, in, out, n, sk);
+        } else if (mode == 2) {
+            hipLaunchKernelGGL(stream_kernel<2>, dim3(workgroups), dim3(256), 0, s, in, out, n, sk);
+        } else {
+            hipLaunchKernelGGL(stream_kernel<3>, dim3(workgroups), dim3(256), 0, s, in, out, n, sk);
+        }
     };
     launch();  // first launch loads the code object
     if (hipGetLastError() != hipSuccess) return 2;

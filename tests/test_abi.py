@@ -381,3 +381,45 @@ def test_noalloc_limits(L):
     # unsupported shapes are refused as by kda_prefill_gated
     assert L.kda_prefill_gated_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, -5.0, FAKE, None, 1, 256, 2, 96, 64, 64,
                                        None, None, FAKE, BF16, 0, None, 0, None) == 2
+
+
+def test_roofs_library_exports_and_validation():
+    """libkda_roofs (the benchmark's measurement kernels) loads, exports what
+    include/kda_roofs.h declares, and rejects bad arguments with 1 before it
+    launches anything."""
+    from linear_attention_sequence_gate_amd import build as kbuild
+    header = os.path.join(os.path.dirname(HEADER), "kda_roofs.h")
+    text = re.sub(r"/\*.*?\*/", "", open(header).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(kda_\w+)\s*\(", text)))
+    assert names == ["kda_roof_mfma", "kda_roof_stream"]
+    R = ctypes.CDLL(kbuild.ROOFS_LIB)
+    for n in names:
+        assert hasattr(R, n)
+    P, I, I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+    R.kda_roof_stream.argtypes = [I, P, P, I64, P, I64, I, I, P, ctypes.POINTER(ctypes.c_float)]
+    R.kda_roof_stream.restype = I
+    R.kda_roof_mfma.argtypes = [I, I, P, P, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_double)]
+    R.kda_roof_mfma.restype = I
+    ms, fl = ctypes.c_float(0.0), ctypes.c_double(0.0)
+    msp = ctypes.byref(ms)
+    bad = [
+        (4, FAKE, FAKE, 1 << 20, FAKE, 1 << 20, 16, 1),    # unknown mode
+        (-1, FAKE, FAKE, 1 << 20, FAKE, 1 << 20, 16, 1),
+        (2, FAKE, FAKE, 0, None, 0, 16, 1),                # no bytes
+        (2, FAKE, FAKE, 100, None, 0, 16, 1),              # not a multiple of 16
+        (2, FAKE, FAKE, 1 << 20, None, 0, -1, 1),          # negative width
+        (2, FAKE, FAKE, 1 << 20, None, 0, 16, 0),          # no repetitions
+        (0, FAKE, None, 1 << 20, FAKE, 1 << 20, 0, 1),     # read needs a grid-stride width
+        (0, FAKE, None, 1 << 20, None, 0, 16, 1),          # read needs a sink
+        (0, FAKE, None, 1 << 20, FAKE, 16 * 256 - 1, 16, 1),  # sink too small
+        (0, None, None, 1 << 20, FAKE, 1 << 20, 16, 1),    # read needs src
+        (2, None, FAKE, 1 << 20, None, 0, 0, 1),           # copy needs src
+        (1, None, None, 1 << 20, None, 0, 0, 1),           # write needs dst
+        (3, FAKE, None, 1 << 20, None, 0, 0, 1),           # in place needs dst
+    ]
+    for mode, src, dst, nbytes, sink, words, wgs, reps in bad:
+        assert R.kda_roof_stream(mode, src, dst, nbytes, sink, words, wgs, reps, None, msp) == 1, (mode, nbytes, wgs)
+    assert R.kda_roof_stream(2, FAKE, FAKE, 1 << 20, None, 0, 16, 1, None, None) == 1  # no result pointer
+    assert R.kda_roof_mfma(0, 16, FAKE, None, msp, ctypes.byref(fl)) == 1
+    assert R.kda_roof_mfma(16, 0, FAKE, None, msp, ctypes.byref(fl)) == 1
+    assert R.kda_roof_mfma(16, 16, None, None, msp, ctypes.byref(fl)) == 1
