@@ -48,15 +48,25 @@
 extern "C" {
 #endif
 
+/* Both enums are int-sized with every int value representable (the two
+ * range enumerators are never returned or accepted), so a caller may pass any
+ * int: the library rejects the ones it does not know. */
 typedef enum {
     KDA_OK = 0,
     KDA_ERR_INVALID_ARGUMENT = 1,    /* null pointer, negative size, bad cu_seqlens ... */
     KDA_ERR_UNSUPPORTED = 2,         /* a dimension / dtype / chunk outside the built set */
     KDA_ERR_WORKSPACE_TOO_SMALL = 3, /* prefill workspace smaller than the queried size */
-    KDA_ERR_HIP = 4                  /* a HIP runtime call or launch failed */
+    KDA_ERR_HIP = 4,                 /* a HIP runtime call or launch failed */
+    KDA_STATUS_RANGE_MIN_ = -0x7fffffff - 1,
+    KDA_STATUS_RANGE_MAX_ = 0x7fffffff
 } kda_status_t;
 
-typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype_t;
+typedef enum {
+    KDA_F32 = 0,
+    KDA_BF16 = 1,
+    KDA_DTYPE_RANGE_MIN_ = -0x7fffffff - 1,
+    KDA_DTYPE_RANGE_MAX_ = 0x7fffffff
+} kda_dtype_t;
 
 /* Largest head count kda_prefill accepts (token rows stay below 2^24 bytes). */
 #define KDA_MAX_HEADS 16384
@@ -220,6 +230,22 @@ kda_status_t kda_prefill_gated_noalloc(const void* q, const void* k, const void*
                                        int64_t T_total, int H, int d_k, int d_v, int chunk,
                                        const float* initial_state, float* final_state, void* o, kda_dtype_t dtype,
                                        int ckpt_interval, float* ckpt_states, int64_t ckpt_capacity, void* stream);
+
+/*
+ * Plan descriptions — what kda_prefill (and its gated and checkpointing
+ * forms, which plan alike) and kda_backward would launch for these sizes, as
+ * text: the segment length, the warm-up window, the workspace bytes and one
+ * line per kernel launch with its grid, workgroup size, LDS bytes and role.
+ * Host only: no device call, no state; the plan depends only on the
+ * arguments.  packed: cu_seqlens will be given (it must be when N > 1).
+ * Writes at most cap bytes including the terminating NUL into buf (buf may
+ * be NULL when cap is 0) and returns the length of the whole description,
+ * as snprintf does; -1 for a shape the call would reject.
+ */
+int64_t kda_describe_prefill_plan(int64_t T_total, int N, int H, int d_k, int d_v, kda_dtype_t dtype, int packed,
+                                  char* buf, size_t cap);
+int64_t kda_describe_backward_plan(int64_t T_total, int N, int H, int d_k, int d_v, kda_dtype_t dtype, char* buf,
+                                   size_t cap);
 
 /*
  * TEST ONLY — the prefill with the planner's two choices given as arguments,

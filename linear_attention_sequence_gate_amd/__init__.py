@@ -22,7 +22,7 @@ EXPORTED = ("kda_status_string", "kda_last_error", "kda_version", "kda_gate",
             "kda_prefill_ckpt", "kda_checkpoint_count", "kda_prefill_gated", "kda_decode_step_gated",
             "kda_backward_workspace_size", "kda_backward", "kda_test_prefill", "kda_test_prefill_workspace_size",
             "kda_test_prefill_flags", "kda_prefill_gated_noalloc", "kda_test_backward",
-            "kda_test_backward_workspace_size")
+            "kda_test_backward_workspace_size", "kda_describe_prefill_plan", "kda_describe_backward_plan")
 
 _lib = None
 
@@ -89,6 +89,10 @@ def lib() -> ctypes.CDLL:
         L.kda_test_backward_workspace_size.restype = SZ
         L.kda_checkpoint_count.argtypes = [P, I, I64, I]
         L.kda_checkpoint_count.restype = I64
+        L.kda_describe_prefill_plan.argtypes = [I64, I, I, I, I, I, I, ctypes.c_char_p, SZ]
+        L.kda_describe_prefill_plan.restype = I64
+        L.kda_describe_backward_plan.argtypes = [I64, I, I, I, I, I, ctypes.c_char_p, SZ]
+        L.kda_describe_backward_plan.restype = I64
         _lib = L
     return _lib
 
@@ -209,6 +213,29 @@ def kda_commit(k, v, g, beta, n_accept, state, stream=None):
     _check(lib().kda_commit(_ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(n_accept), _ptr(state),
                             B, K, H, dk, dv, _dtype_code(k), _stream(stream)))
     return state
+
+
+def _describe(fn, *args) -> str:
+    n = int(fn(*args, None, 0))
+    if n < 0:
+        raise KDAError(1, "shape outside the supported set")
+    buf = ctypes.create_string_buffer(n + 1)
+    fn(*args, buf, n + 1)
+    return buf.value.decode()
+
+
+def describe_prefill_plan(T_total: int, H: int, d_k: int, d_v: int, N: int = 1, packed: bool | None = None,
+                          dtype: int = None) -> str:
+    """The launch plan kda_prefill would use for these sizes (host only)."""
+    dtype = KDA_BF16 if dtype is None else dtype
+    packed = N > 1 if packed is None else packed
+    return _describe(lib().kda_describe_prefill_plan, T_total, N, H, d_k, d_v, dtype, int(packed))
+
+
+def describe_backward_plan(T_total: int, H: int, d_k: int, d_v: int, N: int = 1, dtype: int = None) -> str:
+    """The launch plan kda_backward would use for these sizes (host only)."""
+    dtype = KDA_BF16 if dtype is None else dtype
+    return _describe(lib().kda_describe_backward_plan, T_total, N, H, d_k, d_v, dtype)
 
 
 def kda_checkpoint_count(cu_seqlens_host, T_total: int, interval: int) -> int:

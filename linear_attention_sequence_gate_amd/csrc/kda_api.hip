@@ -7,6 +7,8 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
+#include <cstring>
+#include <string>
 #include <mutex>
 
 #include "kda.h"
@@ -516,6 +518,59 @@ size_t kda_backward_workspace_size(int64_t T_total, int N, int H, int d_k, int d
         !dim_ok(d_v))
         return 0;
     return kda::backward_plan(T_total, N, H, d_k, d_v).bytes;
+}
+
+// ---- plan descriptions (host only)
+static int64_t emit_text(const std::string& text, char* buf, size_t cap)
+{
+    if (buf && cap > 0) {
+        const size_t n = text.size() < cap - 1 ? text.size() : cap - 1;
+        memcpy(buf, text.data(), n);
+        buf[n] = '\0';
+    }
+    return int64_t(text.size());
+}
+
+int64_t kda_describe_prefill_plan(int64_t T_total, int N, int H, int d_k, int d_v, kda_dtype_t dtype, int packed,
+                                  char* buf, size_t cap)
+{
+    if (!prefill_shape_ok(T_total, N, H, d_k, d_v, 64, dtype) || (!packed && N != 1) || (!buf && cap > 0)) return -1;
+    const kda::PrefillPlan p = kda::prefill_plan(T_total, N, H, d_k, d_v);
+    char head[512];
+    snprintf(head, sizeof(head),
+             "kda_prefill plan: T_total=%lld N=%d H=%d d_k=%d d_v=%d dtype=%s%s\n"
+             "segments: %d chunks of 64 tokens (%lld tokens) each; at most %lld segments, %lld of them "
+             "non-final\nwarm-up window: %d tokens%s\nworkspace: %zu bytes\n",
+             (long long)T_total, N, H, d_k, d_v, dtype == KDA_BF16 ? "bf16" : "f32",
+             packed ? " (packed, cu_seqlens given)" : "", p.seg_chunks, (long long)p.seg_chunks * 64,
+             (long long)p.nseg_max, (long long)p.np1_max, p.warm,
+             p.warm > 0 ? "" : " (none: the exact passes run for every chain)", p.workspace_bytes);
+    std::string text = head;
+    const bool ok = dtype == KDA_BF16 ? kda::describe_prefill<kda::BF16>(p, N, H, d_k, d_v, packed != 0, text)
+                                      : kda::describe_prefill<kda::F32>(p, N, H, d_k, d_v, packed != 0, text);
+    if (!ok) return -1;
+    return emit_text(text, buf, cap);
+}
+
+int64_t kda_describe_backward_plan(int64_t T_total, int N, int H, int d_k, int d_v, kda_dtype_t dtype, char* buf,
+                                   size_t cap)
+{
+    if (T_total < 0 || T_total > int64_t(0x7fffffff) || N < 1 || H < 1 || H > KDA_MAX_HEADS || !dim_ok(d_k) ||
+        !dim_ok(d_v) || !dtype_ok(dtype) || (!buf && cap > 0))
+        return -1;
+    const kda::BwdPlan p = kda::backward_plan(T_total, N, H, d_k, d_v);
+    char head[512];
+    snprintf(head, sizeof(head),
+             "kda_backward plan: T_total=%lld N=%d H=%d d_k=%d d_v=%d dtype=%s\n"
+             "segments: %lld tokens each; at most %lld segments; window %lld tokens; full pass %d workgroups\n"
+             "workspace: %zu bytes\n",
+             (long long)T_total, N, H, d_k, d_v, dtype == KDA_BF16 ? "bf16" : "f32", (long long)p.Lseg,
+             (long long)p.segs_max, (long long)p.warm, p.grid, p.bytes);
+    std::string text = head;
+    const bool ok = dtype == KDA_BF16 ? kda::describe_backward<kda::BF16>(p, T_total, N, H, d_k, d_v, text)
+                                      : kda::describe_backward<kda::F32>(p, T_total, N, H, d_k, d_v, text);
+    if (!ok) return -1;
+    return emit_text(text, buf, cap);
 }
 
 // seg_tokens > 0 fixes the segment length (the test entry point only)

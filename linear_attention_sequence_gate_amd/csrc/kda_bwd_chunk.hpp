@@ -1159,6 +1159,50 @@ hipError_t launch_bwd_chunk(const BackwardArgs& a, const BwdPlan& plan, hipStrea
     return hipGetLastError();
 }
 
+// The launches launch_bwd_chunk makes for this plan, as text (host only).
+template <typename DT, int DK, int DV>
+void describe_backward_t(const BwdPlan& plan, int64_t T_total, int N, int H, std::string& out)
+{
+    using C1 = BwdCfg<DT, DK, DV, false>;
+    using C3 = BwdCfg<DT, DK, DV, true>;
+    char line[256];
+    int n = 0;
+    auto add = [&](const char* kernel, int64_t grid, int threads, int lds, const char* what) {
+        snprintf(line, sizeof(line), "launch %d: %s grid %lld x %d threads, %d B LDS; %s\n", ++n, kernel,
+                 (long long)grid, threads, lds, what);
+        out += line;
+    };
+    if (plan.warm > 0)
+        add("bwd_chunk_summary_kernel (window)", plan.segs_max * H, C1::NT, C1::LDS,
+            "every segment's end-of-segment state gradient from the window after it; flags the chains where the "
+            "window's transposed transition is not zero");
+    if (plan.warm == 0 || plan.Lseg < T_total) {
+        add("bwd_chunk_summary_kernel", plan.segs_max * H, C1::NT, C1::LDS,
+            plan.warm > 0 ? "[C | M^T] of the flagged chains' segments 1.. (returns at once elsewhere)"
+                          : "[C | M^T] of every segment but a sequence's first");
+        add("bwd_scan_kernel", int64_t(N) * H * (DV / BWD_SCAN_COLS), 256, BwdScanCfg<DK>::LDS,
+            plan.warm > 0 ? "end-of-segment gradients of the flagged chains" : "every end-of-segment gradient");
+    }
+    add("bwd_chunk_full_kernel", plan.grid, C3::NT, C3::LDS,
+        "every (segment, head) from its end-of-segment gradient: dq, dk, dv, dg, dbeta, the initial state's "
+        "gradient; the states rebuilt from the checkpoints");
+}
+
+template <typename DT>
+bool describe_backward(const BwdPlan& plan, int64_t T_total, int N, int H, int dk, int dv, std::string& out)
+{
+#define KDA_BWD(DKV, DVV)                                                                                  \
+    if (dk == DKV && dv == DVV) {                                                                          \
+        describe_backward_t<DT, DKV, DVV>(plan, T_total, N, H, out);                                       \
+        return true;                                                                                       \
+    }
+    KDA_BWD(32, 32) KDA_BWD(32, 64) KDA_BWD(32, 128)
+    KDA_BWD(64, 32) KDA_BWD(64, 64) KDA_BWD(64, 128)
+    KDA_BWD(128, 32) KDA_BWD(128, 64) KDA_BWD(128, 128)
+#undef KDA_BWD
+    return false;
+}
+
 template <typename DT>
 hipError_t launch_backward(const BackwardArgs& a, const BwdPlan& plan, int dk, int dv, hipStream_t stream)
 {

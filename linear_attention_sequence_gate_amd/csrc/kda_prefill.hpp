@@ -45,6 +45,8 @@
 #pragma once
 
 #include <cmath>
+#include <cstdio>
+#include <string>
 #include <type_traits>
 
 #include "kda_common.hpp"
@@ -1849,6 +1851,63 @@ hipError_t launch_prefill_t(const PrefillArgs& a, const PrefillPlan& plan, hipSt
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k3, dim3(unsigned(plan.nseg_max * a.H)), dim3(C3::NT), C3::LDS, stream, d);
     return hipGetLastError();
+}
+
+// The launches launch_prefill_t makes for this plan, as text (host only): one
+// line per kernel with its grid, block and LDS bytes.  packed: cu_seqlens is
+// given (the plan kernel runs first).
+template <typename DT, int DK, int DV>
+void describe_prefill_t(const PrefillPlan& plan, int N, int H, bool packed, std::string& out)
+{
+    char line[256];
+    int n = 0;
+    auto add = [&](const char* kernel, int64_t grid, int threads, int lds, const char* what) {
+        snprintf(line, sizeof(line), "launch %d: %s grid %lld x %d threads, %d B LDS; %s\n", ++n, kernel,
+                 (long long)grid, threads, lds, what);
+        out += line;
+    };
+    if (packed) add("plan_kernel", 1, 256, 0, "segment table of the packed sequences");
+    const bool warm = plan.warm > 0 && warm_shape(DK, DV);
+    if constexpr (warm_shape(DK, DV)) {
+        if (warm) {
+            using CW_ = BlockCfg<DT, DK, DV, MODE_WARM>;
+            add("prefill_warm_kernel", plan.nseg_max * H, CW_::NT, CW_::LDS,
+                "every (segment, head): its incoming state from the warm-up window, outputs and final states; "
+                "flags the chains where the window's transition is not zero");
+            if (plan.np1_max == 0) return;
+        }
+    }
+    if (plan.np1_max > 0) {
+        using C1 = BlockCfg<DT, DK, DV, MODE_SUMMARY>;
+        add("prefill_block_kernel (summary)", plan.np1_max * H, C1::NT, C1::LDS,
+            warm ? "[S~ | M] of the flagged chains' non-final segments (returns at once elsewhere)"
+                 : "[S~ | M] of every non-final segment");
+        add("scan_kernel", int64_t(N) * H * (DV / SCAN_COLS), 256, ScanCfg<DK, DV>::LDS,
+            warm ? "incoming states of the flagged chains' segments" : "incoming state of every segment");
+    }
+    using C3 = BlockCfg<DT, DK, DV, MODE_OUT>;
+    add("prefill_block_kernel (output)", plan.nseg_max * H, C3::NT, C3::LDS,
+        warm ? "outputs and final states of the flagged chains (returns at once elsewhere)"
+             : "outputs and final states of every segment");
+}
+
+template <typename DT>
+bool describe_prefill(const PrefillPlan& plan, int N, int H, int dk, int dv, bool packed, std::string& out)
+{
+#define KDA_PF(DKV, DVV)                                                                                   \
+    if (dk == DKV && dv == DVV) {                                                                          \
+        describe_prefill_t<DT, DKV, DVV>(plan, N, H, packed, out);                                         \
+        return true;                                                                                       \
+    }
+    if constexpr (DT::is_bf16) {
+        KDA_PF(32, 32) KDA_PF(32, 64) KDA_PF(32, 128)
+        KDA_PF(64, 32) KDA_PF(64, 64) KDA_PF(64, 128)
+        KDA_PF(128, 32) KDA_PF(128, 64) KDA_PF(128, 128)
+    } else {
+        KDA_PF(32, 32) KDA_PF(32, 64)
+    }
+#undef KDA_PF
+    return false;
 }
 
 template <typename DT>

@@ -423,3 +423,35 @@ def test_roofs_library_exports_and_validation():
     assert R.kda_roof_mfma(0, 16, FAKE, None, msp, ctypes.byref(fl)) == 1
     assert R.kda_roof_mfma(16, 0, FAKE, None, msp, ctypes.byref(fl)) == 1
     assert R.kda_roof_mfma(16, 16, None, None, msp, ctypes.byref(fl)) == 1
+
+
+def test_plan_descriptions(L):
+    """The plan descriptions are host-only text: the planner's numbers and one
+    line per launch, truncated like snprintf, -1 for rejected shapes."""
+    txt = kda.describe_prefill_plan(8192, 32, 128, 128)
+    assert "T_total=8192 N=1 H=32 d_k=128 d_v=128 dtype=bf16" in txt
+    assert "warm-up window: 128 tokens" in txt
+    assert f"workspace: {kda.lib().kda_prefill_workspace_size(8192, 1, 32, 128, 128, 64, BF16)} bytes" in txt
+    lines = [l for l in txt.splitlines() if l.startswith("launch ")]
+    assert lines[0].startswith("launch 1: prefill_warm_kernel grid ")
+    assert [l.split(":")[1].split(" grid")[0].strip() for l in lines] == [
+        "prefill_warm_kernel", "prefill_block_kernel (summary)", "scan_kernel", "prefill_block_kernel (output)"]
+    # packed sequences: the plan kernel first; no warm-up for d_k > d_v
+    txt = kda.describe_prefill_plan(10000, 4, 128, 32, N=3)
+    assert "launch 1: plan_kernel grid 1 x 256" in txt and "prefill_warm_kernel" not in txt
+    assert "warm-up window: 0 tokens" in txt
+    # the backward
+    txt = kda.describe_backward_plan(8192, 32, 128, 128)
+    assert f"workspace: {kda.lib().kda_backward_workspace_size(8192, 1, 32, 128, 128)} bytes" in txt
+    assert "window 128 tokens" in txt and "bwd_chunk_full_kernel grid 256 x 512" in txt
+    # snprintf semantics and rejections
+    full = L.kda_describe_prefill_plan(8192, 1, 32, 128, 128, BF16, 0, None, 0)
+    buf = ctypes.create_string_buffer(16)
+    assert L.kda_describe_prefill_plan(8192, 1, 32, 128, 128, BF16, 0, buf, 16) == full
+    assert len(buf.value) == 15
+    assert L.kda_describe_prefill_plan(8192, 1, 32, 128, 128, BF16, 0, None, 16) == -1
+    assert L.kda_describe_prefill_plan(8192, 2, 32, 128, 128, BF16, 0, None, 0) == -1  # N > 1 needs cu_seqlens
+    assert L.kda_describe_prefill_plan(8192, 1, 32, 96, 128, BF16, 0, None, 0) == -1
+    assert L.kda_describe_prefill_plan(8192, 1, 32, 128, 128, F32, 0, None, 0) == -1  # fp32 d_k > 32
+    assert L.kda_describe_backward_plan(-1, 1, 32, 128, 128, BF16, None, 0) == -1
+    assert L.kda_describe_backward_plan(64, 1, 32, 128, 128, 7, None, 0) == -1
