@@ -566,7 +566,7 @@ def main():
                     "roofline": {"bound": "hbm", "achieved": round(b_bytes / (b_ms * 1e-3) / 1e9, 1),
                                  "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                  "frac": round(b_bytes / (b_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 5),
-                                 "kernel": "bwd_chunk_summary_kernel + bwd_scan_kernel + bwd_chunk_full_kernel",
+                                 "kernel": "bwd_chunk_summary_kernel (windows) + flag-gated summary and scan + bwd_chunk_full_kernel",
                                  "traffic": load_traffic("backward_8k"),
                                  "algorithmic_bytes_per_call": b_bytes}}
         del bws, bck
