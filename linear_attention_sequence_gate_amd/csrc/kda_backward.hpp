@@ -60,9 +60,15 @@ struct BackwardArgs {
 __device__ __forceinline__ bool bwd_chain_flagged(const BackwardArgs& a, int seg0, int nseg, int h)
 {
     if (a.flags == nullptr) return true;
-    for (int j = 0; j < nseg; ++j)
-        if (a.flags[int64_t(seg0 + j) * a.H + h] != 0) return true;
-    return false;
+    // lane j reads segment j's flag, all at once (see the prefill's chain_flagged)
+    const int lane = threadIdx.x & 63;
+    bool any = false;
+    for (int j0 = 0; j0 < nseg; j0 += 64) {
+        const int j = j0 + lane;
+        const bool f = j < nseg && a.flags[int64_t(seg0 + j) * a.H + h] != 0;
+        any = any || __ballot(f) != 0;
+    }
+    return any;
 }
 
 // Where segment `seg` (0 .. total) of the packed sequences lies.  Offsets are

@@ -964,9 +964,17 @@ __device__ __forceinline__ void prep_products(unsigned char* smem, int buf, int 
 // chains.  Every thread reads the same words, so the answer is uniform.
 __device__ __forceinline__ bool chain_flagged(const PrefillDev& p, int seg0, int nseg, int h)
 {
-    for (int j = 0; j < nseg; ++j)
-        if (p.flags[int64_t(seg0 + j) * p.H + h] != 0) return true;
-    return false;
+    // lane j reads segment j's flag, all at once, and the wave's ballot
+    // combines them (one memory round trip, not one per segment); every wave
+    // reads the same words, so the result is uniform across the workgroup
+    const int lane = threadIdx.x & 63;
+    bool any = false;
+    for (int j0 = 0; j0 < nseg; j0 += 64) {
+        const int j = j0 + lane;
+        const bool f = j < nseg && p.flags[int64_t(seg0 + j) * p.H + h] != 0;
+        any = any || __ballot(f) != 0;
+    }
+    return any;
 }
 
 // The warm-up decision of a workgroup: the chain waves' words in LDS (written
