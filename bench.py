@@ -114,7 +114,7 @@ def backward_algo(T: int, H: int, dk: int, dv: int, interval: int = 64):
             + 2 * H * dk * dv * 4)
 
 
-CPU_SHARE = 16  # host threads a one-GPU machine gives a job, whatever the machine has
+CPU_SHARE = 16  # CPU threads the baseline uses at most: one GPU's share of the host
 
 
 def host_cpu() -> dict:
