@@ -134,17 +134,20 @@ inline PrefillPlan prefill_plan(int64_t T_total, int N, int H, int dk, int dv, i
     const int64_t max_seq_chunks = (T_total + CH - 1) / CH;
     const int64_t per_cu = (int64_t(H) * chunks_bound + NCU_TARGET - 1) / NCU_TARGET;
     int64_t L;
+    int64_t L_min = 16;  // the exact passes: a segment's summary and scan step must pay off
     if (p.warm > 0 && N == 1) {
         // one (segment, head) item per compute unit: a segment costs its own
-        // blocks plus a short warm-up, so fewer, longer segments waste least
+        // blocks plus a short warm-up, so fewer, longer segments waste least;
+        // with few heads segments may be as short as twice the default window
         const int64_t nseg = NCU_TARGET / H > 1 ? NCU_TARGET / H : 1;
         L = (max_seq_chunks + nseg - 1) / nseg;
+        L_min = 4;
     } else if (p.warm > 0) {
         L = per_cu / 4;  // several items per unit: long sequences do not end last
     } else {
         L = per_cu / 2;  // the summary and output passes each fill the units once
     }
-    if (L < 16) L = 16;
+    if (L < L_min) L = L_min;
     if (force_L > 0) L = force_L;
     if (L >= max_seq_chunks) L = max_seq_chunks > 0 ? max_seq_chunks : 1;  // nothing splits
     p.seg_chunks = int(L);

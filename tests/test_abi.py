@@ -128,9 +128,11 @@ def test_prefill_workspace_size(L):
     assert ws(256, 1, 16385, 32, 32) == 0                 # H above KDA_MAX_HEADS
     assert ws((1 << 31) - 1, 1, 1, 32, 32) > 0
     assert ws(1 << 31, 1, 1, 32, 32) == 0                 # token offsets are int32
-    # a sequence too short to split needs no segment buffers
-    small = ws(64 * 16, 1, 32, 128, 128)
+    # a sequence too short to split (at most the shortest segment the planner
+    # makes, 4 chunks) needs no segment buffers
+    small = ws(64 * 4, 1, 32, 128, 128)
     assert small < 4096
+    assert ws(64 * 16, 1, 32, 128, 128) > small  # 16 chunks at H=32: four segments
     # a long one does (transition + incoming state per segment)
     big = ws(1 << 20, 1, 8, 128, 128)
     assert big > 8 * 128 * 256 * 4
