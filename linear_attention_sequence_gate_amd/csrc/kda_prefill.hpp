@@ -143,7 +143,8 @@ inline PrefillPlan prefill_plan(int64_t T_total, int N, int H, int dk, int dv, i
         L = (max_seq_chunks + nseg - 1) / nseg;
         L_min = 4;
     } else if (p.warm > 0) {
-        L = per_cu / 4;  // several items per unit: long sequences do not end last
+        L = per_cu / 8;  // several items per unit, so long sequences do not end last (1.03M tokens
+                         // in 64 sequences: 14.4 ms per call, against 15.7 with per_cu / 4)
     } else {
         L = per_cu / 2;  // the summary and output passes each fill the units once
     }
