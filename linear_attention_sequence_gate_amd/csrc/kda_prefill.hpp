@@ -156,7 +156,7 @@ inline PrefillPlan prefill_plan(int64_t T_total, int N, int H, int dk, int dv, i
     p.np1_max = (max_seq_chunks > L) ? chunks_bound / L + 1 : 0;
     size_t off = 0;
     p.off_table = off;
-    off = align256(off + sizeof(int32_t) * 4 * size_t(N + 1));
+    off = align256(off + sizeof(int32_t) * 5 * size_t(N + 1));
     if (p.warm > 0) {
         p.off_flags = off;
         off = align256(off + sizeof(int32_t) * size_t(p.nseg_max) * H);
@@ -237,7 +237,11 @@ __device__ __forceinline__ int32_t tab_ck(const PrefillDev& p, int n)
 // ------------------------------------------------------------- plan kernel
 // One workgroup: clamps cu_seqlens into a non-decreasing sequence inside
 // [0, T_total] and writes the per-sequence segment, pass-1 and checkpoint
-// offsets (a sequence of length len holds len / ckpt_interval checkpoints).
+// offsets (a sequence of length len holds len / ckpt_interval checkpoints),
+// then the warm-up kernel's dispatch order of the sequences' final segments:
+// longest first (a counting sort on the chunk count, PERM_BUCKETS buckets,
+// the longest sharing the last), so no long item starts last.
+constexpr int PERM_BUCKETS = 1024;
 __global__ void __launch_bounds__(256) plan_kernel(const int32_t* __restrict__ cu, int N,
                                                    int64_t T_total, int L, int ckpt_interval,
                                                    int32_t* __restrict__ tab)
@@ -322,6 +326,47 @@ __global__ void __launch_bounds__(256) plan_kernel(const int32_t* __restrict__ c
         }
         __syncthreads();
     }
+    // ---- final segments, longest first (the barrier above makes this
+    // workgroup's table writes visible to all of it)
+    __shared__ int32_t s_hist[PERM_BUCKETS];
+    int32_t* perm = tab + 4 * (N + 1);
+    auto bucket_of = [&](int n) {  // reversed chunk count of n's final segment: 0 = longest
+        const int64_t len = int64_t(cuc[n + 1]) - cuc[n];
+        const int64_t ch = (len + CH - 1) / CH;
+        int64_t ns = (ch + L - 1) / L;
+        if (ns < 1) ns = 1;
+        int64_t f = ch - (ns - 1) * L;  // in [0, L]
+        if (f > PERM_BUCKETS - 1) f = PERM_BUCKETS - 1;
+        return PERM_BUCKETS - 1 - int(f);
+    };
+    for (int b = t; b < PERM_BUCKETS; b += 256) s_hist[b] = 0;
+    __syncthreads();
+    for (int n = t; n < N; n += 256) atomicAdd(&s_hist[bucket_of(n)], 1);
+    __syncthreads();
+    // exclusive scan of the buckets: each thread sums its four, the 256 sums
+    // are scanned, then each thread writes its four starts
+    constexpr int BPT = PERM_BUCKETS / 256;
+    int32_t own = 0;
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) own += s_hist[BPT * t + i];
+    s_seg[t] = own;
+    __syncthreads();
+    for (int d = 1; d < 256; d <<= 1) {
+        const int32_t a = (t >= d) ? s_seg[t - d] : 0;
+        __syncthreads();
+        s_seg[t] += a;
+        __syncthreads();
+    }
+    int32_t start = s_seg[t] - own;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+        const int32_t c = s_hist[BPT * t + i];
+        s_hist[BPT * t + i] = start;
+        start += c;
+    }
+    __syncthreads();
+    for (int n = t; n < N; n += 256) perm[atomicAdd(&s_hist[bucket_of(n)], 1)] = n;
 }
 
 // index n with off[n] <= item < off[n+1] (off non-decreasing, off[0] = 0)
@@ -1577,14 +1622,29 @@ prefill_warm_kernel(PrefillDev p)
     pclk.last = clock64();
 #endif
 
-    // ---- work item
+    // ---- work item.  Packed sequences: every non-final segment first (all
+    // of full length, in sequence order), then the sequences' final segments
+    // longest first (the plan kernel's order), so long items start early.
     const int H = p.H;
-    const int item = blockIdx.x / H;
+    const int rank = blockIdx.x / H;
     const int h = blockIdx.x % H;
-    if (item >= tab_seg(p, p.N)) return;
-    const int n = p.single ? 0 : find_seq(p.tab + (p.N + 1), p.N, item);
+    if (rank >= tab_seg(p, p.N)) return;
+    int n, s;
+    if (p.single) {
+        n = 0;
+        s = rank;
+    } else {
+        const int np1 = tab_p1(p, p.N);
+        if (rank < np1) {
+            n = find_seq(p.tab + 2 * (p.N + 1), p.N, rank);
+            s = rank - tab_p1(p, n);
+        } else {
+            n = p.tab[4 * (p.N + 1) + (rank - np1)];
+            s = tab_seg(p, n + 1) - tab_seg(p, n) - 1;
+        }
+    }
     const int seg0 = tab_seg(p, n);
-    const int s = item - seg0;
+    const int item = seg0 + s;  // the segment's index in sequence order (its flag)
     const int nseg = tab_seg(p, n + 1) - seg0;
     const int64_t seq0 = tab_cu(p, n), seq1 = tab_cu(p, n + 1);
     const int64_t t_begin = seq0 + int64_t(s) * p.L * CH;
