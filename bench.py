@@ -531,7 +531,7 @@ def main():
                            "roofline": {"bound": "hbm", "achieved": round(vb / (v_ms * 1e-3) / 1e9, 1),
                                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                         "frac": round(vb / (v_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                                        "traffic": load_traffic("verify_b256_k4"), "kernel": "step_wave_kernel (verify)",
+                                        "traffic": load_traffic("verify_b256_k4"), "kernel": "verify_wave_kernel",
                                         "algorithmic_bytes_per_call": vb}},
                 "commit": {"ms_per_call": round(c_ms, 4),
                            "roofline": {"bound": "hbm", "achieved": round(cb / (c_ms * 1e-3) / 1e9, 1),

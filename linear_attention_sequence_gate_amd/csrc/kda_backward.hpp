@@ -233,7 +233,8 @@ inline BwdPlan backward_plan(int64_t T_total, int N, int H, int dk, int dv, int6
         p.Lseg = BWD_CHUNK * (per > 0 ? per : 1);
     }
     if (force_tokens > 0) p.Lseg = (force_tokens + BWD_CHUNK - 1) / BWD_CHUNK * BWD_CHUNK;
-    p.segs_max = T / p.Lseg + 1 + N;  // >= the sum over sequences of max(1, ceil(len / Lseg))
+    // >= the sum over sequences of max(1, ceil(len / Lseg)); exact for one sequence
+    p.segs_max = N == 1 ? (T + p.Lseg - 1) / p.Lseg : T / p.Lseg + 1 + N;
     const int64_t items = p.segs_max * H;
     p.grid = int(items < BWD_MAX_WG ? items : BWD_MAX_WG);
     size_t off = 0;

@@ -152,8 +152,16 @@ inline PrefillPlan prefill_plan(int64_t T_total, int N, int H, int dk, int dv, i
     if (force_L > 0) L = force_L;
     if (L >= max_seq_chunks) L = max_seq_chunks > 0 ? max_seq_chunks : 1;  // nothing splits
     p.seg_chunks = int(L);
-    p.nseg_max = chunks_bound / L + N + 1;
-    p.np1_max = (max_seq_chunks > L) ? chunks_bound / L + 1 : 0;
+    if (N == 1) {
+        // one sequence of at most max_seq_chunks chunks: the count is exact,
+        // so no launch carries workgroups that only return (at one workgroup
+        // per compute unit they would take a dispatch round of their own)
+        p.nseg_max = max_seq_chunks > L ? (max_seq_chunks + L - 1) / L : 1;
+        p.np1_max = p.nseg_max - 1;
+    } else {
+        p.nseg_max = chunks_bound / L + N + 1;
+        p.np1_max = (max_seq_chunks > L) ? chunks_bound / L + 1 : 0;
+    }
     size_t off = 0;
     p.off_table = off;
     off = align256(off + sizeof(int32_t) * 5 * size_t(N + 1));

@@ -17,8 +17,8 @@
 // of one (b, h) state, all d_k rows of it, in registers: lane = 8 * rg + cgl
 // holds 4 consecutive columns (cgl) of d_k / 8 consecutive rows (rg).  The
 // sums over d_k are three lane exchanges inside the wave (row groups differ in
-// lane bits 3..5): no LDS and no barrier.  Each row of the slice is 128
-// contiguous bytes, read by the 8 lanes of one row group.
+// lane bits 3..5): no LDS and no barrier in the arithmetic.  Each row of the
+// slice is 128 contiguous bytes, read by the 8 lanes of one row group.
 #pragma once
 
 #include "kda_common.hpp"
@@ -69,12 +69,12 @@ __device__ __forceinline__ void load_run(const typename DT::storage* p, float (&
     }
 }
 
-// EMIT_O: write o per token (decode, verify).  WRITE_S: write the state back
-// (decode, commit).  Decode runs K = 1 token; verify K; commit the first
-// n_accept[b] (clamped to [0, K]) of K and emits nothing.  The workgroup is
-// the d_v / 32 waves of one state (one slice each): they share nothing and
-// never synchronise, but run side by side, so each 512-byte state row is read
-// (and written) by the four waves at about the same time.
+// EMIT_O: write o per token (decode).  WRITE_S: write the state back (decode,
+// commit).  Decode runs K = 1 token; commit the first n_accept[b] (clamped to
+// [0, K]) of K and emits nothing; verify has a kernel of its own below.  The
+// workgroup is the d_v / 32 waves of one state (one slice each): they share
+// nothing and never synchronise, but run side by side, so each 512-byte state
+// row is read (and written) by the four waves at about the same time.
 template <typename DT, int DK, int DV, bool EMIT_O, bool WRITE_S, bool GATED>
 __global__ void __launch_bounds__(64 * (DV / 32)) step_wave_kernel(const typename DT::storage* __restrict__ q,
                                                        const typename DT::storage* __restrict__ k,
@@ -161,6 +161,152 @@ __global__ void __launch_bounds__(64 * (DV / 32)) step_wave_kernel(const typenam
     }
 }
 
+// Verify: K draft tokens scored from the resident state, which is read once
+// and never written.  Same lane layout and per-token arithmetic as
+// step_wave_kernel, but the tokens' inputs are staged through LDS, G tokens
+// at a time: the workgroup reads each token's g, k, q, v rows once, as
+// 16-byte pieces spread over its threads (where every lane would otherwise
+// read its d_k / 8 rows of them from the caches, token after token), and the
+// first group's loads are issued before the state's, so they arrive while
+// the state streams in.  In the kernels that write the state (decode,
+// commit) the staging measured slower, so they keep the direct form.
+template <typename DT, int DK, int DV>
+__global__ void __launch_bounds__(64 * (DV / 32)) verify_wave_kernel(const typename DT::storage* __restrict__ q,
+                                                         const typename DT::storage* __restrict__ k,
+                                                         const typename DT::storage* __restrict__ v,
+                                                         const typename DT::storage* __restrict__ g,
+                                                         const typename DT::storage* __restrict__ beta,
+                                                         const float* __restrict__ state,
+                                                         typename DT::storage* __restrict__ o, int K, int H)
+{
+    using ST = typename DT::storage;
+    constexpr int R = DK / 8;                     // rows per lane
+    constexpr int RH = 4;                         // rows per run of LDS reads
+    constexpr int NT = 64 * (DV / 32);            // threads of the workgroup
+    constexpr int E = 16 / int(sizeof(ST));       // elements per 16-byte piece
+    constexpr int OQ = 2 * DK;                    // staged token: g, k, q, v
+    constexpr int OV = 3 * DK;
+    constexpr int TS = OV + DV;                   // elements per staged token
+    constexpr int PT = TS / E;                    // pieces per token
+    constexpr int G = (2 * NT) / PT < 1 ? 1 : (2 * NT) / PT > 8 ? 8 : (2 * NT) / PT;  // tokens per group
+    constexpr int NP = (G * PT + NT - 1) / NT;    // pieces per thread per group (at most 2)
+    static_assert(DV % 32 == 0 && (R == 4 || R == 8 || R == 16), "unsupported shape");
+    __shared__ __align__(16) ST tok[G * TS];
+    __shared__ float tbeta[G];
+
+    const int bh = blockIdx.x;
+    const int slice = threadIdx.x >> 6;  // waves of one workgroup: the slices of one state
+    const int b = bh / H, h = bh % H;
+    const int lane = threadIdx.x & 63;
+    const int cgl = lane & 7, rg = lane >> 3;
+    const int c0 = rg * R;
+    const int col = slice * 32 + 4 * cgl;
+
+    // piece p of the group starting at token i0: token p / PT of the group,
+    // elements [E (p % PT), E (p % PT) + E) of its staged row, which sits at
+    // tok + E p in LDS
+    u32x4 buf[NP];
+    ST bbuf = 0;  // raw: converted once staged, so no wait falls before the state's loads
+    auto fetch = [&](int i0) {
+        const int n = min(G, K - i0);
+#pragma unroll
+        for (int j = 0; j < NP; ++j) {
+            const int p = int(threadIdx.x) + j * NT;
+            if (p < n * PT) {
+                const int t = p / PT, c = (p - t * PT) * E;
+                const int64_t row = (int64_t(b) * K + i0 + t) * H + h;  // token tensors are [B, K, H, d]
+                const ST* src = c < DK   ? g + row * DK + c
+                                : c < OQ ? k + row * DK + (c - DK)
+                                : c < OV ? q + row * DK + (c - OQ)
+                                         : v + row * DV + (c - OV);
+                buf[j] = *reinterpret_cast<const u32x4*>(src);
+            }
+        }
+        if (int(threadIdx.x) < n) bbuf = beta[(int64_t(b) * K + i0 + threadIdx.x) * H + h];
+    };
+    auto stage = [&](int i0) {
+        const int n = min(G, K - i0);
+#pragma unroll
+        for (int j = 0; j < NP; ++j) {
+            const int p = int(threadIdx.x) + j * NT;
+            if (p < n * PT) *reinterpret_cast<u32x4*>(tok + p * E) = buf[j];
+        }
+        if (int(threadIdx.x) < n) tbeta[threadIdx.x] = load_elem<DT>(&bbuf, 0);
+    };
+
+    fetch(0);
+    const float* S = state + int64_t(bh) * DK * DV + col;
+    f32x4 s[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) s[r] = *reinterpret_cast<const f32x4*>(S + (c0 + r) * DV);
+
+    for (int i0 = 0; i0 < K; i0 += G) {
+        stage(i0);
+        __syncthreads();
+        const int n = min(G, K - i0);
+#pragma unroll 1
+        for (int t = 0; t < n; ++t) {
+            const ST* tk = tok + t * TS;
+            f32x4 pk = {0.f, 0.f, 0.f, 0.f}, pq = {0.f, 0.f, 0.f, 0.f};
+            float kq = 0.f;
+            // the rows in runs of RH, read from LDS as they are needed (LDS
+            // reads are cheap to repeat; registers for all of them are not)
+#pragma unroll
+            for (int r0 = 0; r0 < R; r0 += RH) {
+                float a[RH], kk[RH], qq[RH];
+                load_run<DT, RH>(tk + c0 + r0, a);
+                load_run<DT, RH>(tk + DK + c0 + r0, kk);
+                load_run<DT, RH>(tk + OQ + c0 + r0, qq);
+#pragma unroll
+                for (int r = 0; r < RH; ++r) {
+                    s[r0 + r] *= __expf(a[r]);
+                    pk += kk[r] * s[r0 + r];
+                    pq += qq[r] * s[r0 + r];
+                    kq += kk[r] * qq[r];
+                }
+                asm volatile("" ::: "memory");  // keep the next run's LDS reads here
+            }
+            // column sums over all d_k rows: the 8 row groups of the wave
+#pragma unroll
+            for (int d = 8; d < 64; d <<= 1) {
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    pk[m] += lane_xor_8_16_32(pk[m], d, lane);
+                    pq[m] += lane_xor_8_16_32(pq[m], d, lane);
+                }
+                kq += lane_xor_8_16_32(kq, d, lane);
+            }
+            float vv[4];
+            load_run<DT, 4>(tk + OV + col, vv);
+            const float bt = tbeta[t];
+            f32x4 u;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) u[m] = bt * (vv[m] - pk[m]);
+            if (rg == 0) {
+                const f32x4 ov = pq + kq * u;
+                auto* ob = o + ((int64_t(b) * K + i0 + t) * H + h) * DV + col;
+                if constexpr (DT::is_bf16) {
+                    *reinterpret_cast<u32x2*>(ob) = u32x2{pack_bf16x2(ov[0], ov[1]), pack_bf16x2(ov[2], ov[3])};
+                } else {
+                    *reinterpret_cast<f32x4*>(ob) = ov;
+                }
+            }
+#pragma unroll
+            for (int r0 = 0; r0 < R; r0 += RH) {
+                float kk[RH];
+                load_run<DT, RH>(tk + DK + c0 + r0, kk);
+#pragma unroll
+                for (int r = 0; r < RH; ++r) s[r0 + r] += kk[r] * u;
+                asm volatile("" ::: "memory");
+            }
+        }
+        if (i0 + G < K) {
+            __syncthreads();  // the group is read before the next one is staged
+            fetch(i0 + G);
+        }
+    }
+}
+
 // 16-byte alignment of every token tensor (the kernel's vector loads and stores)
 inline bool step_wave_aligned(const void* q, const void* k, const void* v, const void* g, const void* o)
 {
@@ -193,9 +339,13 @@ hipError_t launch_step_wave_shape(int mode, const void* q, const void* k, const 
     if (mode == 0)
         return launch_step_wave_t<DT, DKV, DVV, true, true>(q, k, v, g, beta, n_accept, state, o, B, K, H, gate_A,
                                                             g_min, stream);
-    if (mode == 1)
-        return launch_step_wave_t<DT, DKV, DVV, true, false>(q, k, v, g, beta, n_accept, state, o, B, K, H,
-                                                             gate_A, g_min, stream);
+    if (mode == 1) {
+        using S = typename DT::storage;
+        hipLaunchKernelGGL((verify_wave_kernel<DT, DKV, DVV>), dim3(unsigned(B * H)), dim3(64 * (DVV / 32)), 0,
+                           stream, static_cast<const S*>(q), static_cast<const S*>(k), static_cast<const S*>(v),
+                           static_cast<const S*>(g), static_cast<const S*>(beta), state, static_cast<S*>(o), K, H);
+        return hipGetLastError();
+    }
     return launch_step_wave_t<DT, DKV, DVV, false, true>(q, k, v, g, beta, n_accept, state, o, B, K, H, gate_A,
                                                          g_min, stream);
 }

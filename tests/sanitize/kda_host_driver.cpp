@@ -91,10 +91,11 @@ int main()
     if (need > 0) EXPECT(prefill(1, 256, 64, BF, at(16), need - 1) == KDA_ERR_WORKSPACE_TOO_SMALL);
     EXPECT(prefill(1, 256, 64, BF, (char*)at(0) + 8, need) == KDA_ERR_INVALID_ARGUMENT);  // o aliases q
 
-    // the no-allocation form refuses what its static scratch cannot hold
-    EXPECT(kda_prefill_gated_noalloc(at(0), at(1), at(2), at(3), (const float*)at(4), -5.f, at(5), nullptr, 1,
-                                     int64_t(1) << 30, 64, 128, 128, 64, nullptr, (float*)at(8), at(16), BF, 0,
-                                     nullptr, 0, nullptr) == KDA_ERR_UNSUPPORTED);
+    // the no-allocation form refuses what its static scratch cannot hold (64
+    // packed sequences over 2^30 tokens: hundreds of MB of workspace)
+    EXPECT(kda_prefill_gated_noalloc(at(0), at(1), at(2), at(3), (const float*)at(4), -5.f, at(5),
+                                     (const int32_t*)at(6), 64, int64_t(1) << 30, 64, 128, 128, 64, nullptr,
+                                     (float*)at(8), at(16), BF, 0, nullptr, 0, nullptr) == KDA_ERR_UNSUPPORTED);
 
     // backward rejections
     const size_t bneed = kda_backward_workspace_size(256, 1, 2, 64, 64);

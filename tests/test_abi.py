@@ -427,6 +427,18 @@ def test_roofs_library_exports_and_validation():
     assert R.kda_roof_mfma(16, 16, None, None, msp, ctypes.byref(fl)) == 1
 
 
+def test_single_sequence_workspace_fits_the_noalloc_scratch():
+    """One sequence at d_k = d_v = 128 needs about 50 MB of workspace at most,
+    whatever its length and head count (the planner cuts it into about
+    256 / H segments), so it always fits the 64 MiB static scratch of
+    kda_prefill_gated_noalloc; packed sequences can need more."""
+    for H in (1, 2, 4, 8, 16, 32, 64, 128, 256, 512):
+        for T in (1, 255, 4096, 8192, 1 << 20, 1 << 30, (1 << 31) - 1):
+            need = kda.kda_prefill_workspace_size(T, 1, H, 128, 128)
+            assert 0 < need <= 50_500_000, (H, T, need)
+    assert kda.kda_prefill_workspace_size(1 << 30, 64, 64, 128, 128) > (64 << 20)
+
+
 def test_plan_descriptions(L):
     """The plan descriptions are host-only text: the planner's numbers and one
     line per launch, truncated like snprintf, -1 for rejected shapes."""
@@ -438,6 +450,11 @@ def test_plan_descriptions(L):
     assert lines[0].startswith("launch 1: prefill_warm_kernel grid ")
     assert [l.split(":")[1].split(" grid")[0].strip() for l in lines] == [
         "prefill_warm_kernel", "prefill_block_kernel (summary)", "scan_kernel", "prefill_block_kernel (output)"]
+    # one sequence: the segment count is exact (8 of 1024 tokens), so the
+    # segment launches carry no workgroups that only return
+    assert "at most 8 segments, 7 of them non-final" in txt
+    assert "prefill_warm_kernel grid 256 x " in txt and "prefill_block_kernel (summary) grid 224 x " in txt
+    assert "bwd_chunk_summary_kernel (window) grid 256 x " in kda.describe_backward_plan(8192, 32, 128, 128)
     # packed sequences: the plan kernel first; no warm-up for d_k > d_v
     txt = kda.describe_prefill_plan(10000, 4, 128, 32, N=3)
     assert "launch 1: plan_kernel grid 1 x 256" in txt and "prefill_warm_kernel" not in txt

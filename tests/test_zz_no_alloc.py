@@ -53,7 +53,7 @@ def test_noalloc_two_calls(kda):
     wl1 = synth.PREFILL_8K.with_(H=16, seqlens=(4096,), state_std=0.1)
     announce("noalloc call 1: H=16 T=4096")
     need1 = kda.kda_prefill_workspace_size(wl1.T_total, 1, wl1.H, 128, 128)
-    assert 0 < need1 <= kda.lib().kda_prefill_workspace_size(8192, 1, 32, 128, 128, 64, 1)
+    assert 0 < need1 <= (64 << 20)  # within the static scratch (KDA_NOALLOC_SCRATCH_BYTES)
     one_call(kda, wl1)
     wl2 = synth.VARLEN_64.with_(H=4, seqlens=(1500, 700, 33), state_std=0.1)
     announce("noalloc call 2: smaller, varlen, weak decay on heads 1 and 3")
