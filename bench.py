@@ -30,9 +30,13 @@ H=8, T=2^20, z shifted by +3) and `varlen_64` (64 packed sequences, ~1.03M
 tokens, H=32, initial states N(0, 0.01)), each one kda_prefill_gated call on
 seeded inputs drawn on the device (the same distributions as the tests'), with
 its HBM roofline and an oracle check on sampled heads and sequences.
-`measured_roofs` holds the device's own streaming bandwidth (read, write and
-copy kernels) and bf16 matrix-core issue rate (libkda_roofs), against which
-every roofline also reports a fraction.
+`measured_roofs` holds the device's own streaming bandwidth (read, write, copy
+and in-place kernels) and bf16 matrix-core issue rate (libkda_roofs), against
+which every roofline also reports a fraction.  Decode and commit also report
+against the same in-place update over their own 512 MiB working set, part of
+which the 256 MB last-level cache keeps between launches; the decode leg times
+one more step over a 4 GiB state (B=2048), past that cache, for comparison
+with the 4 GiB roof.
 """
 from __future__ import annotations
 
@@ -207,7 +211,25 @@ def measured_roofs(torch, dev, stream) -> dict:
         if rc != 0:
             raise RuntimeError(f"kda_roof_stream mode {mode}: {rc}")
         out[name] = round(moved / (ms.value * 1e-3) / 1e9, 1)
-    out["hbm_rw_gbs"] = max(out["hbm_copy_gbs"], out["hbm_inplace_gbs"])
+    # in place in the decode step's access pattern (64 KB fp32 states, all 16
+    # loads of a lane in flight, streaming stores), the delay between each
+    # workgroup's loads and stores swept (it spreads their read and write
+    # bursts apart): over 4 GiB, and over 512 MiB, the size of the decode
+    # workload's state, which the 256 MB last-level cache partly holds from
+    # one launch to the next
+    L.kda_roof_state_inplace.argtypes = [P, I64, I, I, P, ctypes.POINTER(ctypes.c_float)]
+    for size, name, reps in ((nbytes, "hbm_inplace_state_gbs", 5), (512 << 20, "inplace_state_512mib_gbs", 50)):
+        best, best_delay = 0.0, 0
+        for delay in (0, 16, 20, 24, 28, 32):
+            rc = L.kda_roof_state_inplace(dst.data_ptr(), size, delay, reps, stream.cuda_stream, ctypes.byref(ms))
+            if rc != 0:
+                raise RuntimeError(f"kda_roof_state_inplace: {rc}")
+            gbs = 2 * size / (ms.value * 1e-3) / 1e9
+            if gbs > best:
+                best, best_delay = gbs, delay
+        out[name] = round(best, 1)
+        out[name.replace("_gbs", "_delay")] = best_delay
+    out["hbm_rw_gbs"] = max(out["hbm_copy_gbs"], out["hbm_inplace_gbs"], out["hbm_inplace_state_gbs"])
     del src, dst
     fsink = torch.empty(256 * 8 * 256, dtype=torch.float32, device=dev)
     fl = ctypes.c_double(0.0)
@@ -217,8 +239,11 @@ def measured_roofs(torch, dev, stream) -> dict:
     out["mfma_bf16_tflops"] = round(fl.value / (ms.value * 1e-3) / 1e12, 1)
     out["how"] = ("libkda_roofs over 4 GiB, 16-byte vectors, mean of 5 launches: read grid-stride over 8192 "
                   "workgroups of 256, write grid-stride over 32768, copy and in-place update one vector per "
-                  "thread (both count read + write bytes; hbm_rw_gbs is the larger); 2048 workgroups of 4 "
-                  "waves, each issuing 4096 x 8 independent v_mfma_f32_16x16x32_bf16")
+                  "thread, in-place update of 64 KB fp32 states in the decode step's access pattern with "
+                  "streaming stores, best over a 0-32 round delay between loads and stores (read + write "
+                  "bytes; hbm_rw_gbs is the largest of the three); the same state update over 512 MiB, the "
+                  "decode workload's own working set (inplace_state_512mib_gbs, mean of 50); 2048 "
+                  "workgroups of 4 waves, each issuing 4096 x 8 independent v_mfma_f32_16x16x32_bf16")
     return out
 
 
@@ -474,6 +499,28 @@ def main():
         for i in range(16):
             dstep_unfused(i)
         d_unfused_ms = timed_loop(dstep_unfused, args.decode_steps)
+        # the same step over a 4 GiB state (B = 2048), far past the 256 MB
+        # last-level cache, which holds part of the 512 MiB state above from
+        # one step to the next: its rate is compared with the 4 GiB
+        # state-update roof
+        B4 = 2048
+        g4 = torch.Generator(device=dev).manual_seed(dwl.seed + 1)
+        x4 = {}
+        for n in ("q", "k", "v", "z"):
+            t = torch.randn((B4, dwl.H, dwl.dk), generator=g4, device=dev)
+            x4[n] = (t / t.norm(dim=-1, keepdim=True) if n in ("q", "k") else t).to(torch.bfloat16)
+        b4 = torch.sigmoid(torch.randn((B4, dwl.H), generator=g4, device=dev)).to(torch.bfloat16)
+        s4 = torch.randn((B4, dwl.H, dwl.dk, dwl.dv), generator=g4, device=dev) * 0.05
+        o4 = torch.empty((B4, dwl.H, dwl.dv), dtype=torch.bfloat16, device=dev)
+
+        def dstep4(i):
+            kda.kda_decode_step_gated(x4["q"], x4["k"], x4["v"], x4["z"], dA, b4, s4, o=o4)
+
+        for i in range(3):
+            dstep4(i)
+        d4_ms = timed_loop(dstep4, 20)
+        d4_bytes, _ = decode_algo(B4, dwl.H, dwl.dk, dwl.dv)
+        del x4, b4, s4, o4
         d_bytes, d_flops = decode_algo(B, dwl.H, dwl.dk, dwl.dv)
         d_ach = d_bytes / (d_kernel_ms * 1e-3) / 1e9
         decode = {"value": round(B * args.decode_steps / (d_total_ms * 1e-3), 1), "unit": "tokens/s",
@@ -487,7 +534,9 @@ def main():
                                "algorithmic_bytes_per_call": d_bytes,
                                "ms_per_call": round(d_kernel_ms, 4)},
                   "unfused": {"ms_per_step": round(d_unfused_ms, 4),
-                              "value": round(B / (d_unfused_ms * 1e-3), 1)}}
+                              "value": round(B / (d_unfused_ms * 1e-3), 1)},
+                  "state_4gib": {"B": B4, "ms_per_call": round(d4_ms, 4), "algorithmic_bytes_per_call": d4_bytes,
+                                 "achieved_gbs": round(d4_bytes / (d4_ms * 1e-3) / 1e9, 1)}}
 
     if "speculative" in legs:
         # ------------------------------------------- speculative decode leg (K = 4)
@@ -583,6 +632,19 @@ def main():
                 continue
             r["measured_rw_gbs"] = round(rw_gbs, 1)
             r["frac_of_measured_rw"] = round(r["achieved"] / rw_gbs, 4)
+        # decode and commit update a 512 MiB state in place: against the same
+        # update over the same working set (part of it cache-resident), and
+        # decode over 4 GiB against the 4 GiB state update
+        same = roofs["inplace_state_512mib_gbs"]
+        for r in (decode and decode["roofline"], spec and spec["commit"]["roofline"]):
+            if r is not None:
+                r["measured_rw_same_working_set_gbs"] = same
+                r["frac_of_measured_rw_same_working_set"] = round(r["achieved"] / same, 4)
+        if decode is not None:
+            d4 = decode["state_4gib"]
+            d4["measured_state_rw_gbs"] = roofs["hbm_inplace_state_gbs"]
+            d4["frac_of_measured_state_rw"] = round(d4["achieved_gbs"] / roofs["hbm_inplace_state_gbs"], 4)
+            d4["frac"] = round(d4["achieved_gbs"] / HBM_PEAK_GBS, 4)
         roofline["measured_mfma_bf16_tflops"] = roofs["mfma_bf16_tflops"]
         roofline["mfma_frac_of_measured_mfma"] = round(roofline["mfma_tflops"] / roofs["mfma_bf16_tflops"], 4)
         # a plain 8192^3 bf16 GEMM through the vendor library, for reference

@@ -3,9 +3,9 @@
  * rates against (HBM streaming bandwidth and the bf16 matrix-core issue rate
  * of one MI355X).  Not part of the KDA path; libkda does not use it.
  *
- * Both calls launch on `stream` (a hipStream_t, NULL = the null stream), time
- * their own launches with two HIP events, wait for them, and return 0 on
- * success, 1 on bad arguments (nothing launched), 2 on a HIP error.
+ * Every call launches on `stream` (a hipStream_t, NULL = the null stream),
+ * times its own launches with two HIP events, waits for them, and returns 0
+ * on success, 1 on bad arguments (nothing launched), 2 on a HIP error.
  */
 #ifndef KDA_ROOFS_H
 #define KDA_ROOFS_H
@@ -30,6 +30,18 @@ extern "C" {
  */
 int kda_roof_stream(int mode, const void* src, void* dst, int64_t bytes, void* sink, int64_t sink_words,
                     int workgroups, int reps, void* stream, float* ms_per_launch);
+
+/*
+ * kda_roof_state_inplace — updates `bytes` of buf in place as 64 KB blocks of
+ * 128 x 128 fp32 (each word + 1 after `delay` rounds of dependent arithmetic
+ * on it, 0 <= delay <= 4096), one workgroup of 256 threads per block, in the
+ * access pattern of kda_decode_step on a d_k = d_v = 128 state: 16-byte loads
+ * all in flight, then streaming 16-byte stores.  bytes is a positive
+ * multiple of 65536; buf a 16-byte aligned device buffer of at least that.
+ * One untimed launch, then `reps` timed back to back: *ms_per_launch is
+ * their mean (each launch reads and writes `bytes`).
+ */
+int kda_roof_state_inplace(void* buf, int64_t bytes, int delay, int reps, void* stream, float* ms_per_launch);
 
 /*
  * kda_roof_mfma — `workgroups` workgroups of four waves, each wave issuing

@@ -5,6 +5,9 @@
 //   kda_roof_stream : read, write, copy or in-place update of a device
 //                     buffer with 16-byte vector accesses: grid-stride over a
 //                     given number of workgroups, or one vector per thread.
+//   kda_roof_state_inplace : in-place update of 64 KB fp32 states in the
+//                     decode step's access pattern (the read + write roof of
+//                     a working set of the decode step's size).
 //   kda_roof_mfma   : back-to-back independent 16x16x32 bf16 matrix-core
 //                     instructions on every SIMD (the issue ceiling of the
 //                     instruction the prefill's products use).
@@ -75,6 +78,29 @@ __global__ void __launch_bounds__(256) tile_kernel(const u32x4* __restrict__ src
     if constexpr (MODE == 1) dst[i] = u32x4{uint32_t(i), 0u, 0u, 0u};
     else if constexpr (MODE == 2) dst[i] = src[i];
     else dst[i] = dst[i] + 1u;
+}
+
+// In place over 64 KB blocks laid out as 128 x 128 fp32 states, in the
+// decode step's access pattern: a workgroup per block, wave w = 32 columns,
+// lane = (row group of 16 rows, 4 columns); all 16 loads of a
+// lane in flight, then `delay` rounds of dependent arithmetic on the values,
+// then 16 streaming stores.  The delay spreads the workgroups' write bursts
+// apart from their read bursts (it is what the decode step's own arithmetic
+// does); the caller sweeps it.
+__global__ void __launch_bounds__(256) state_inplace_kernel(float* __restrict__ x, int delay)
+{
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int cgl = lane & 7, rg = lane >> 3;
+    float* S = x + int64_t(blockIdx.x) * 128 * 128 + w * 32 + 4 * cgl;
+    f32x4 v[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) v[r] = *reinterpret_cast<const f32x4*>(S + (rg * 16 + r) * 128);
+    for (int d = 0; d < delay; ++d) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v[r] = v[r] * 0.999f + 0.001f;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) __builtin_nontemporal_store(v[r] + 1.f, reinterpret_cast<f32x4*>(S + (rg * 16 + r) * 128));
 }
 
 // Each wave keeps NACC independent accumulators and issues ITERS rounds of
@@ -162,6 +188,20 @@ int kda_roof_stream(int mode, const void* src, void* dst, int64_t bytes, void* s
         }
     };
     launch();  // first launch loads the code object
+    if (hipGetLastError() != hipSuccess) return 2;
+    return timed(launch, reps, s, ms_per_launch);
+}
+
+int kda_roof_state_inplace(void* buf, int64_t bytes, int delay, int reps, void* stream, float* ms_per_launch)
+{
+    if (!buf || bytes < 65536 || bytes % 65536 != 0 || bytes / 65536 > int64_t(0x7fffffff) || delay < 0 ||
+        delay > 4096 || reps < 1 || !ms_per_launch)
+        return 1;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    float* x = static_cast<float*>(buf);
+    const unsigned blocks = unsigned(bytes / 65536);
+    auto launch = [&]() { hipLaunchKernelGGL(state_inplace_kernel, dim3(blocks), dim3(256), 0, s, x, delay); };
+    launch();
     if (hipGetLastError() != hipSuccess) return 2;
     return timed(launch, reps, s, ms_per_launch);
 }

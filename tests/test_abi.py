@@ -393,7 +393,7 @@ def test_roofs_library_exports_and_validation():
     header = os.path.join(os.path.dirname(HEADER), "kda_roofs.h")
     text = re.sub(r"/\*.*?\*/", "", open(header).read(), flags=re.S)
     names = sorted(set(re.findall(r"\b(kda_\w+)\s*\(", text)))
-    assert names == ["kda_roof_mfma", "kda_roof_stream"]
+    assert names == ["kda_roof_mfma", "kda_roof_state_inplace", "kda_roof_stream"]
     R = ctypes.CDLL(kbuild.ROOFS_LIB)
     for n in names:
         assert hasattr(R, n)
@@ -425,6 +425,13 @@ def test_roofs_library_exports_and_validation():
     assert R.kda_roof_mfma(0, 16, FAKE, None, msp, ctypes.byref(fl)) == 1
     assert R.kda_roof_mfma(16, 0, FAKE, None, msp, ctypes.byref(fl)) == 1
     assert R.kda_roof_mfma(16, 16, None, None, msp, ctypes.byref(fl)) == 1
+    R.kda_roof_state_inplace.argtypes = [P, I64, I, I, P, ctypes.POINTER(ctypes.c_float)]
+    R.kda_roof_state_inplace.restype = I
+    for buf, nbytes, delay, reps, res in ((None, 1 << 20, 0, 1, msp), (FAKE, 0, 0, 1, msp),
+                                          (FAKE, (1 << 20) + 16, 0, 1, msp), (FAKE, 1 << 20, -1, 1, msp),
+                                          (FAKE, 1 << 20, 4097, 1, msp), (FAKE, 1 << 20, 0, 0, msp),
+                                          (FAKE, 1 << 20, 0, 1, None)):
+        assert R.kda_roof_state_inplace(buf, nbytes, delay, reps, None, res) == 1, (nbytes, delay, reps)
 
 
 def test_single_sequence_workspace_fits_the_noalloc_scratch():
