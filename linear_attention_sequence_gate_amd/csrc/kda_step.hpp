@@ -41,6 +41,31 @@ __device__ __forceinline__ float lane_xor_8_16_32(float x, int dist, int lane)
     return __int_as_float(__builtin_amdgcn_update_dpp(0, int(u), 0x128, 0xf, 0xf, false));  // row_ror:8
 }
 
+// a and b each summed over lane bit 4 in one exchange: lanes with bit 4 clear
+// get a + a', the others b' + b (x' the value of lane ^ 16)
+__device__ __forceinline__ float fold16(float a, float b)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// the same over lane bit 5: lanes below 32 get a + a', the others b' + b
+__device__ __forceinline__ float fold32(float a, float b)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// x holds value Q in the lanes of quarter Q (lanes 16 Q .. 16 Q + 15): every
+// lane gets the four values, each from the lane of its quarter at its own
+// position in the quarter
+__device__ __forceinline__ f32x4 gather_quarters(float x)
+{
+    const unsigned w = __float_as_uint(x);
+    const auto h = __builtin_amdgcn_permlane32_swap(w, w, false, false);  // [0]: values 0 | 1, [1]: 2 | 3
+    const auto a = __builtin_amdgcn_permlane16_swap(h[0], h[0], false, false);
+    const auto c = __builtin_amdgcn_permlane16_swap(h[1], h[1], false, false);
+    return f32x4{__uint_as_float(a[0]), __uint_as_float(a[1]), __uint_as_float(c[0]), __uint_as_float(c[1])};
+}
+
 // R consecutive elements (R = 4, 8 or 16) from an address aligned to their size
 template <typename DT, int R>
 __device__ __forceinline__ void load_run(const typename DT::storage* p, float (&x)[R])
@@ -168,7 +193,9 @@ __global__ void __launch_bounds__(64 * (DV / 32)) step_wave_kernel(const typenam
 // 16-byte pieces spread over its threads (where every lane would otherwise
 // read its d_k / 8 rows of them from the caches, token after token), and the
 // first group's loads are issued before the state's, so they arrive while
-// the state streams in.  In the kernels that write the state (decode,
+// the state streams in.  The staging also does, once per workgroup, the work
+// every lane would repeat on its rows: the rows go to LDS as fp32, and g as
+// the decay alpha = exp(g).  In the kernels that write the state (decode,
 // commit) the staging measured slower, so they keep the direct form.
 template <typename DT, int DK, int DV>
 __global__ void __launch_bounds__(64 * (DV / 32)) verify_wave_kernel(const typename DT::storage* __restrict__ q,
@@ -184,14 +211,14 @@ __global__ void __launch_bounds__(64 * (DV / 32)) verify_wave_kernel(const typen
     constexpr int RH = 4;                         // rows per run of LDS reads
     constexpr int NT = 64 * (DV / 32);            // threads of the workgroup
     constexpr int E = 16 / int(sizeof(ST));       // elements per 16-byte piece
-    constexpr int OQ = 2 * DK;                    // staged token: g, k, q, v
+    constexpr int OQ = 2 * DK;                    // staged token: alpha, k, q, v (fp32)
     constexpr int OV = 3 * DK;
     constexpr int TS = OV + DV;                   // elements per staged token
     constexpr int PT = TS / E;                    // pieces per token
     constexpr int G = (2 * NT) / PT < 1 ? 1 : (2 * NT) / PT > 8 ? 8 : (2 * NT) / PT;  // tokens per group
     constexpr int NP = (G * PT + NT - 1) / NT;    // pieces per thread per group (at most 2)
     static_assert(DV % 32 == 0 && (R == 4 || R == 8 || R == 16), "unsupported shape");
-    __shared__ __align__(16) ST tok[G * TS];
+    __shared__ __align__(16) float tok[G * TS];
     __shared__ float tbeta[G];
 
     const int bh = blockIdx.x;
@@ -229,7 +256,27 @@ __global__ void __launch_bounds__(64 * (DV / 32)) verify_wave_kernel(const typen
 #pragma unroll
         for (int j = 0; j < NP; ++j) {
             const int p = int(threadIdx.x) + j * NT;
-            if (p < n * PT) *reinterpret_cast<u32x4*>(tok + p * E) = buf[j];
+            if (p < n * PT) {
+                const bool is_g = (p - p / PT * PT) * E < DK;
+                float x[E];
+                if constexpr (DT::is_bf16) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        x[2 * e] = bf16_lo(buf[j][e]);
+                        x[2 * e + 1] = bf16_hi(buf[j][e]);
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) x[e] = __uint_as_float(buf[j][e]);
+                }
+                if (is_g) {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) x[e] = __expf(x[e]);
+                }
+#pragma unroll
+                for (int e = 0; e < E; e += 4)
+                    *reinterpret_cast<f32x4*>(tok + p * E + e) = f32x4{x[e], x[e + 1], x[e + 2], x[e + 3]};
+            }
         }
         if (int(threadIdx.x) < n) tbeta[threadIdx.x] = load_elem<DT>(&bbuf, 0);
     };
@@ -246,55 +293,51 @@ __global__ void __launch_bounds__(64 * (DV / 32)) verify_wave_kernel(const typen
         const int n = min(G, K - i0);
 #pragma unroll 1
         for (int t = 0; t < n; ++t) {
-            const ST* tk = tok + t * TS;
+            const float* tk = tok + t * TS;
             f32x4 pk = {0.f, 0.f, 0.f, 0.f}, pq = {0.f, 0.f, 0.f, 0.f};
             float kq = 0.f;
             // the rows in runs of RH, read from LDS as they are needed (LDS
             // reads are cheap to repeat; registers for all of them are not)
 #pragma unroll
             for (int r0 = 0; r0 < R; r0 += RH) {
-                float a[RH], kk[RH], qq[RH];
-                load_run<DT, RH>(tk + c0 + r0, a);
-                load_run<DT, RH>(tk + DK + c0 + r0, kk);
-                load_run<DT, RH>(tk + OQ + c0 + r0, qq);
+                const f32x4 a = *reinterpret_cast<const f32x4*>(tk + c0 + r0);
+                const f32x4 kk = *reinterpret_cast<const f32x4*>(tk + DK + c0 + r0);
+                const f32x4 qq = *reinterpret_cast<const f32x4*>(tk + OQ + c0 + r0);
 #pragma unroll
                 for (int r = 0; r < RH; ++r) {
-                    s[r0 + r] *= __expf(a[r]);
+                    s[r0 + r] *= a[r];
                     pk += kk[r] * s[r0 + r];
                     pq += qq[r] * s[r0 + r];
                     kq += kk[r] * qq[r];
                 }
                 asm volatile("" ::: "memory");  // keep the next run's LDS reads here
             }
-            // column sums over all d_k rows: the 8 row groups of the wave
+            // column sums over all d_k rows (the 8 row groups, lane bits 3..5),
+            // pairing the addends as step_wave_kernel's butterfly does (bit 3,
+            // then 4, then 5), but as a reduce-scatter: afterwards the lane in
+            // quarter Q = lane / 16 holds column 4 cgl + Q of pk and pq
 #pragma unroll
-            for (int d = 8; d < 64; d <<= 1) {
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    pk[m] += lane_xor_8_16_32(pk[m], d, lane);
-                    pq[m] += lane_xor_8_16_32(pq[m], d, lane);
-                }
-                kq += lane_xor_8_16_32(kq, d, lane);
+            for (int m = 0; m < 4; ++m) {
+                pk[m] += lane_xor_8_16_32(pk[m], 8, lane);
+                pq[m] += lane_xor_8_16_32(pq[m], 8, lane);
             }
-            float vv[4];
-            load_run<DT, 4>(tk + OV + col, vv);
-            const float bt = tbeta[t];
-            f32x4 u;
-#pragma unroll
-            for (int m = 0; m < 4; ++m) u[m] = bt * (vv[m] - pk[m]);
-            if (rg == 0) {
-                const f32x4 ov = pq + kq * u;
-                auto* ob = o + ((int64_t(b) * K + i0 + t) * H + h) * DV + col;
-                if constexpr (DT::is_bf16) {
-                    *reinterpret_cast<u32x2*>(ob) = u32x2{pack_bf16x2(ov[0], ov[1]), pack_bf16x2(ov[2], ov[3])};
-                } else {
-                    *reinterpret_cast<f32x4*>(ob) = ov;
-                }
+            kq += lane_xor_8_16_32(kq, 8, lane);
+            kq += lane_xor_8_16_32(kq, 16, lane);
+            kq += lane_xor_8_16_32(kq, 32, lane);
+            const float pkq = fold32(fold16(pk[0], pk[1]), fold16(pk[2], pk[3]));
+            const float pqq = fold32(fold16(pq[0], pq[1]), fold16(pq[2], pq[3]));
+            const int cq = col + (lane >> 4);  // this lane's column
+            const float uq = tbeta[t] * (tk[OV + cq] - pkq);
+            if ((lane & 8) == 0) {  // one lane per column
+                const float ov = pqq + kq * uq;
+                auto* ob = o + ((int64_t(b) * K + i0 + t) * H + h) * DV + cq;
+                if constexpr (DT::is_bf16) *ob = uint16_t(pack_bf16x2(ov, 0.f));
+                else *ob = ov;
             }
+            const f32x4 u = gather_quarters(uq);
 #pragma unroll
             for (int r0 = 0; r0 < R; r0 += RH) {
-                float kk[RH];
-                load_run<DT, RH>(tk + DK + c0 + r0, kk);
+                const f32x4 kk = *reinterpret_cast<const f32x4*>(tk + DK + c0 + r0);
 #pragma unroll
                 for (int r = 0; r < RH; ++r) s[r0 + r] += kk[r] * u;
                 asm volatile("" ::: "memory");
