@@ -107,6 +107,35 @@ def test_verify_commit_match_decode_steps(kda):
     assert relerr(host(state), host(s2)) < 1e-6
 
 
+@pytest.mark.parametrize("K", [17, 64])
+def test_long_drafts_match_decode_steps_and_oracle(kda, K):
+    """Drafts of several LDS token groups (up to the K = 64 maximum; 17 ends in
+    a one-token group): verify's outputs and commit's state equal K decode
+    steps and meet the oracle's bar."""
+    import torch
+    B = 3
+    wl = synth.VERIFY_B256_K4.with_(H=4)
+    announce(f"verify/commit B={B} K={K} H=4 d=128 bf16 against decode steps")
+    x, g, S0 = inputs(wl, B, K)
+    t = to_dev(kda, wl, x, B, K)
+    state = dev(S0)
+    o = kda.kda_verify(t["q"], t["k"], t["v"], t["g"], t["beta"], state)
+    s2 = dev(S0)
+    outs = []
+    for i in range(K):
+        sl = lambda a: a[:, i].contiguous()
+        outs.append(kda.kda_decode_step(sl(t["q"]), sl(t["k"]), sl(t["v"]), sl(t["g"]), sl(t["beta"]), s2))
+    n = torch.full((B,), K, dtype=torch.int32, device="cuda")
+    kda.kda_commit(t["k"], t["v"], t["g"], t["beta"], n, state)
+    torch.cuda.synchronize()
+    assert torch.equal(o, torch.stack(outs, dim=1)), "verify differs from the decode steps"
+    assert torch.equal(state, s2), "commit differs from the decode steps"
+    o_ref, S_ref = oracle_run(x, g, S0, [K] * B, K)
+    eo, es = relerr(host(o).reshape(B * K, 4, wl.dv), o_ref), relerr(host(state), S_ref)
+    print(f"  o {eo:.3e}  state {es:.3e}")
+    assert eo < TOL["bf16"] and es < TOL["bf16"]
+
+
 def test_verify_commit_full_sampled(kda):
     """The decode workload's shape (B=256, H=32, d=128) with K=4 draft tokens;
     sampled sequences against the oracle."""
