@@ -84,6 +84,33 @@ def test_verify_and_commit_small(kda, dk, dv, dtype, K, unaligned):
     assert es < TOL[dtype]
 
 
+OTHER_SHAPES = [(dk, dv, dt) for dt in ("bf16", "f32") for dk in (32, 64, 128) for dv in (32, 64, 128)
+                if (dk, dv, dt) not in CASES]
+
+
+@pytest.mark.parametrize("dk,dv,dtype", OTHER_SHAPES)
+def test_verify_and_commit_other_shapes(kda, dk, dv, dtype):
+    """The remaining head shapes and dtypes the step kernels are built for (the
+    verify kernel stages 1 to 8 tokens per group, over 64 to 256 threads,
+    depending on the shape), with K = 9 drafts."""
+    import torch
+    B, K, H = 4, 9, 2
+    wl = synth.VERIFY_B256_K4.with_(H=H, dk=dk, dv=dv, dtype=dtype)
+    announce(f"verify/commit B={B} K={K} H={H} dk={dk} dv={dv} {dtype}")
+    x, g, S0 = inputs(wl, B, K)
+    t = to_dev(kda, wl, x, B, K)
+    state = dev(S0)
+    o = kda.kda_verify(t["q"], t["k"], t["v"], t["g"], t["beta"], state)
+    n = np.array([K, 0, 5, 1], dtype=np.int32)
+    kda.kda_commit(t["k"], t["v"], t["g"], t["beta"], torch.from_numpy(n).cuda(), state)
+    torch.cuda.synchronize()
+    o_ref, _ = oracle_run(x, g, S0, [K] * B, K)
+    _, S_ref = oracle_run(x, g, S0, list(n), K)
+    eo, es = relerr(host(o).reshape(B * K, H, dv), o_ref), relerr(host(state), S_ref)
+    print(f"  verify o {eo:.3e}  commit state {es:.3e}")
+    assert eo < TOL[dtype] and es < TOL[dtype]
+
+
 def test_verify_commit_match_decode_steps(kda):
     """verify's outputs and commit's state equal the same tokens fed one by one
     to kda_decode_step (the same arithmetic per token)."""
