@@ -187,13 +187,14 @@ __global__ void __launch_bounds__(64 * (DV / 32)) step_wave_kernel(const typenam
 }
 
 // Verify: K draft tokens scored from the resident state, which is read once
-// and never written.  Same lane layout and per-token arithmetic as
-// step_wave_kernel, but the tokens' inputs are staged through LDS, G tokens
-// at a time: the workgroup reads each token's g, k, q, v rows once, as
-// 16-byte pieces spread over its threads (where every lane would otherwise
-// read its d_k / 8 rows of them from the caches, token after token), and the
-// first group's loads are issued before the state's, so they arrive while
-// the state streams in.  The staging also does, once per workgroup, the work
+// and never written.  Same lane layout as step_wave_kernel and the same
+// arithmetic per token (every sum pairs the same addends), so its outputs
+// equal K decode steps bit for bit; but the tokens' inputs are staged
+// through LDS, G tokens at a time: the workgroup reads each token's g, k, q,
+// v rows once, as 16-byte pieces spread over its threads (where every lane
+// would otherwise read its d_k / 8 rows of them from the caches, token after
+// token), and the first group's loads are issued before the state's, so
+// they arrive while the state streams in.  The staging also does, once per workgroup, the work
 // every lane would repeat on its rows: the rows go to LDS as fp32, and g as
 // the decay alpha = exp(g).  In the kernels that write the state (decode,
 // commit) the staging measured slower, so they keep the direct form.
@@ -218,6 +219,7 @@ __global__ void __launch_bounds__(64 * (DV / 32)) verify_wave_kernel(const typen
     constexpr int G = (2 * NT) / PT < 1 ? 1 : (2 * NT) / PT > 8 ? 8 : (2 * NT) / PT;  // tokens per group
     constexpr int NP = (G * PT + NT - 1) / NT;    // pieces per thread per group (at most 2)
     static_assert(DV % 32 == 0 && (R == 4 || R == 8 || R == 16), "unsupported shape");
+    static_assert(NP <= 2, "at most two pieces per thread");
     __shared__ __align__(16) float tok[G * TS];
     __shared__ float tbeta[G];
 
