@@ -772,14 +772,12 @@ __device__ __forceinline__ void prep_load(PrepRegs<C, DT>& r, const PrefillDev& 
     const char* gv = static_cast<const char*>(p.v) + rv0;
     const uint32_t rsk = uint32_t(H) * uint32_t(C::DK * sizeof(ST)), rsv = uint32_t(H) * uint32_t(C::DV * sizeof(ST));
     const uint32_t cb = uint32_t(2 * cpair * sizeof(ST));
-#pragma unroll
-    for (int i = 0; i < C::TPT; ++i) {
-        const int row = tok0 + i < len ? tok0 + i : len - 1;
-        const uint32_t off = __umul24(uint32_t(row), rsk) + cb;
-        if (!SUMMARY) r.q[i] = *reinterpret_cast<const Pair*>(gq + off);
-        r.k[i] = *reinterpret_cast<const Pair*>(gk + off);
-        r.g[i] = *reinterpret_cast<const Pair*>(gg + off);
-    }
+    // beta and v first: the running sums wait for g, issued last, and loads
+    // complete in issue order, so that one wait covers every load here (beta
+    // and v issued last were still being waited for in the middle of the tile
+    // pass)
+    const char* gb = static_cast<const char*>(p.beta) + (b0 * H + h) * int64_t(sizeof(ST));
+    r.b = *reinterpret_cast<const ST*>(gb + __umul24(uint32_t(ptid < len ? ptid : len - 1), uint32_t(H * sizeof(ST))));
 #pragma unroll
     for (int j = 0; j < C::UPT_V; ++j) {
         const int u = ptid + j * C::NPT;
@@ -790,8 +788,14 @@ __device__ __forceinline__ void prep_load(PrepRegs<C, DT>& r, const PrefillDev& 
             r.v[j] = *reinterpret_cast<const u32x4*>(gv + off);
         }
     }
-    const char* gb = static_cast<const char*>(p.beta) + (b0 * H + h) * int64_t(sizeof(ST));
-    r.b = *reinterpret_cast<const ST*>(gb + __umul24(uint32_t(ptid < len ? ptid : len - 1), uint32_t(H * sizeof(ST))));
+#pragma unroll
+    for (int i = 0; i < C::TPT; ++i) {
+        const int row = tok0 + i < len ? tok0 + i : len - 1;
+        const uint32_t off = __umul24(uint32_t(row), rsk) + cb;
+        if (!SUMMARY) r.q[i] = *reinterpret_cast<const Pair*>(gq + off);
+        r.k[i] = *reinterpret_cast<const Pair*>(gk + off);
+        r.g[i] = *reinterpret_cast<const Pair*>(gg + off);
+    }
 }
 
 // Prep stage of the beta step: every state-independent tile of one block from
