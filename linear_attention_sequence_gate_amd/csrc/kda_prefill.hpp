@@ -756,7 +756,11 @@ struct PrepRegs {
     typename DT::storage b;  // raw bits: converted where used, so the load is not waited on here
 };
 
-template <typename C, typename DT, bool SUMMARY>
+// Parts of a block's raw inputs, loaded separately as each one's registers
+// become free in the tile pass of the block before
+enum PrepPart { PP_ALL, PP_G, PP_KQ, PP_B, PP_V };
+
+template <typename C, typename DT, bool SUMMARY, int PART = PP_ALL>
 __device__ __forceinline__ void prep_load(PrepRegs<C, DT>& r, const PrefillDev& p, int64_t b0, int len, int h,
                                           int ptid, int cpair, int tok0)
 {
@@ -772,29 +776,35 @@ __device__ __forceinline__ void prep_load(PrepRegs<C, DT>& r, const PrefillDev& 
     const char* gv = static_cast<const char*>(p.v) + rv0;
     const uint32_t rsk = uint32_t(H) * uint32_t(C::DK * sizeof(ST)), rsv = uint32_t(H) * uint32_t(C::DV * sizeof(ST));
     const uint32_t cb = uint32_t(2 * cpair * sizeof(ST));
-    // beta and v first: the running sums wait for g, issued last, and loads
-    // complete in issue order, so that one wait covers every load here (beta
-    // and v issued last were still being waited for in the middle of the tile
-    // pass)
-    const char* gb = static_cast<const char*>(p.beta) + (b0 * H + h) * int64_t(sizeof(ST));
-    r.b = *reinterpret_cast<const ST*>(gb + __umul24(uint32_t(ptid < len ? ptid : len - 1), uint32_t(H * sizeof(ST))));
+    // all parts at once (the first block): beta and v first, since the running
+    // sums wait for g, issued last, and loads complete in issue order, so that
+    // one wait covers every load here
+    if constexpr (PART == PP_ALL || PART == PP_B) {
+        const char* gb = static_cast<const char*>(p.beta) + (b0 * H + h) * int64_t(sizeof(ST));
+        r.b = *reinterpret_cast<const ST*>(gb + __umul24(uint32_t(ptid < len ? ptid : len - 1),
+                                                         uint32_t(H * sizeof(ST))));
+    }
+    if constexpr (PART == PP_ALL || PART == PP_V) {
 #pragma unroll
-    for (int j = 0; j < C::UPT_V; ++j) {
-        const int u = ptid + j * C::NPT;
-        if (C::U_V % C::NPT == 0 || u < C::U_V) {
-            int row = u / C::UPR_V;
-            row = row < len ? row : len - 1;
-            const uint32_t off = __umul24(uint32_t(row), rsv) + uint32_t((u % C::UPR_V) * 16);
-            r.v[j] = *reinterpret_cast<const u32x4*>(gv + off);
+        for (int j = 0; j < C::UPT_V; ++j) {
+            const int u = ptid + j * C::NPT;
+            if (C::U_V % C::NPT == 0 || u < C::U_V) {
+                int row = u / C::UPR_V;
+                row = row < len ? row : len - 1;
+                const uint32_t off = __umul24(uint32_t(row), rsv) + uint32_t((u % C::UPR_V) * 16);
+                r.v[j] = *reinterpret_cast<const u32x4*>(gv + off);
+            }
         }
     }
 #pragma unroll
     for (int i = 0; i < C::TPT; ++i) {
         const int row = tok0 + i < len ? tok0 + i : len - 1;
         const uint32_t off = __umul24(uint32_t(row), rsk) + cb;
-        if (!SUMMARY) r.q[i] = *reinterpret_cast<const Pair*>(gq + off);
-        r.k[i] = *reinterpret_cast<const Pair*>(gk + off);
-        r.g[i] = *reinterpret_cast<const Pair*>(gg + off);
+        if constexpr (PART == PP_ALL || PART == PP_KQ) {
+            if (!SUMMARY) r.q[i] = *reinterpret_cast<const Pair*>(gq + off);
+            r.k[i] = *reinterpret_cast<const Pair*>(gk + off);
+        }
+        if constexpr (PART == PP_ALL || PART == PP_G) r.g[i] = *reinterpret_cast<const Pair*>(gg + off);
     }
 }
 
@@ -804,10 +814,15 @@ __device__ __forceinline__ void prep_load(PrepRegs<C, DT>& r, const PrefillDev& 
 // running sum of g across runs is a lane scan.  Sums are kept in natural-log
 // units and scaled to log2 once, inside the exponent's FMA; R_a is G before
 // sub-tile a (R_0 = 0).
-template <typename C, typename DT, bool SUMMARY>
-__device__ __forceinline__ void prep_tiles(const PrepRegs<C, DT>& r, unsigned char* smem, int buf, int len,
+// `next(r, part)` loads that part of the next block's raw inputs into r; it is
+// called as soon as the pass has read the part's registers for the last time
+// (g after the running sums, k and q after the tile loop, beta and v after
+// their stores), which gives g the most time to land: the running sums of the
+// next pass wait for it first.
+template <typename C, typename DT, bool SUMMARY, typename Next>
+__device__ __forceinline__ void prep_tiles(PrepRegs<C, DT>& r, unsigned char* smem, int buf, int len,
                                            int lane, int ptid, int cpair, int part, int tok0, const GateZ& gz,
-                                           PhaseClock& pclk)
+                                           PhaseClock& pclk, Next&& next)
 {
     using O = Op<DT>;
     using OT = typename O::T;
@@ -840,6 +855,8 @@ __device__ __forceinline__ void prep_tiles(const PrepRegs<C, DT>& r, unsigned ch
         c0[i] = s0;
         c1[i] = s1;
     }
+    next(r, std::integral_constant<int, PP_G>{});
+    asm volatile("" ::: "memory");  // issue them here, not with the k and q loads below
     pclk.mark(7);
     // running sums across the runs of this channel pair (lanes cpl + CPW * part):
     // an exchange butterfly over the part index.  At level d every lane adds its
@@ -896,6 +913,7 @@ __device__ __forceinline__ void prep_tiles(const PrepRegs<C, DT>& r, unsigned ch
             O::stp(sQG + t * C::SK + pc, q0 * ga, q1 * gb);
         }
     }
+    next(r, std::integral_constant<int, PP_KQ>{});
     pclk.mark(9);
     // K-hat^T rows 2c, 2c+1 (tokens 4m..4m+3 stay contiguous under pcol)
     if constexpr (C::TPT >= 4) {
@@ -924,6 +942,7 @@ __device__ __forceinline__ void prep_tiles(const PrepRegs<C, DT>& r, unsigned ch
         else bv = r.b;
         sB[ptid] = ptid < len ? bv : 0.f;
     }
+    next(r, std::integral_constant<int, PP_B>{});
     // v rows at their permuted column positions
 #pragma unroll
     for (int j = 0; j < C::UPT_V; ++j) {
@@ -940,6 +959,7 @@ __device__ __forceinline__ void prep_tiles(const PrepRegs<C, DT>& r, unsigned ch
             }
         }
     }
+    next(r, std::integral_constant<int, PP_V>{});
 }
 
 // Prep stage of the alpha step: per 16x16 block (a, b), b <= a, of the block
@@ -1073,10 +1093,17 @@ __device__ __forceinline__ void prep_role(const PrefillDev& p, unsigned char* sm
     // same z and gets the same g
     const GateZ gz = GateZ::of_head(p.gate_A, h, p.g_min);
     PrepRegs<C, DT> pr;
+    // the loads of block nb, part by part (past the last block they re-read
+    // it: unconditional loads keep the wait counts exact)
+    auto loads_of = [&](int64_t nb) {
+        const int64_t b = nb < nblk ? nb : nblk - 1;
+        return [&, b](PrepRegs<C, DT>& r, auto part_t) {
+            prep_load<C, DT, SUMMARY, decltype(part_t)::value>(r, p, blk0 + b * BC, blen(b), h, ptid, cpair, tok0);
+        };
+    };
     if (nblk > 0) {
         prep_load<C, DT, SUMMARY>(pr, p, blk0, blen(0), h, ptid, cpair, tok0);
-        prep_tiles<C, DT, SUMMARY>(pr, smem, 0, blen(0), lane, ptid, cpair, part, tok0, gz, pclk);
-        if (nblk > 1) prep_load<C, DT, SUMMARY>(pr, p, blk0 + BC, blen(1), h, ptid, cpair, tok0);
+        prep_tiles<C, DT, SUMMARY>(pr, smem, 0, blen(0), lane, ptid, cpair, part, tok0, gz, pclk, loads_of(1));
     }
     __syncthreads();
     KDA_PHASE(4);
@@ -1087,10 +1114,9 @@ __device__ __forceinline__ void prep_role(const PrefillDev& p, unsigned char* sm
         __syncthreads();
         KDA_PHASE(1);
         if (bi + 1 < nblk) {  // beta: tiles of block bi+1, loads of block bi+2
-            prep_tiles<C, DT, SUMMARY>(pr, smem, buf ^ 1, blen(bi + 1), lane, ptid, cpair, part, tok0, gz, pclk);
+            prep_tiles<C, DT, SUMMARY>(pr, smem, buf ^ 1, blen(bi + 1), lane, ptid, cpair, part, tok0, gz, pclk,
+                                       loads_of(bi + 2));
             KDA_PHASE(10);
-            if (bi + 2 < nblk)
-                prep_load<C, DT, SUMMARY>(pr, p, blk0 + (bi + 2) * BC, blen(bi + 2), h, ptid, cpair, tok0);
         }
         KDA_PHASE(2);
         __syncthreads();
