@@ -15,6 +15,7 @@
 #include "kda_decode.hpp"
 #include "kda_gate.hpp"
 #include "kda_prefill.hpp"
+#include "kda_serial.hpp"
 #include "kda_spec.hpp"
 #include "kda_step.hpp"
 #include "kda_backward.hpp"
@@ -261,15 +262,27 @@ kda_status_t kda_commit(const void* k, const void* v, const void* g, const void*
 static bool prefill_shape_ok(int64_t T_total, int N, int H, int d_k, int d_v, int chunk, kda_dtype_t dtype)
 {
     return T_total >= 0 && T_total <= int64_t(0x7fffffff) && N >= 1 && H >= 1 && H <= KDA_MAX_HEADS &&
-           dim_ok(d_k) && dim_ok(d_v) && chunk == 64 && dtype_ok(dtype) &&
-           !(dtype == KDA_F32 && (d_k != 32 || d_v > 64));
+           dim_ok(d_k) && dim_ok(d_v) && chunk == 64 && dtype_ok(dtype);
+}
+
+// fp32 head shapes without a chunk kernel run token by token
+static bool serial_path(int d_k, int d_v, kda_dtype_t dtype)
+{
+    return dtype == KDA_F32 && kda::serial_shape_f32(d_k, d_v);
+}
+
+static kda::PrefillPlan plan_for(int64_t T_total, int N, int H, int d_k, int d_v, kda_dtype_t dtype,
+                                 int force_L = 0, int warm_req = -1)
+{
+    if (serial_path(d_k, d_v, dtype)) return kda::serial_plan(T_total, N);
+    return kda::prefill_plan(T_total, N, H, d_k, d_v, force_L, warm_req);
 }
 
 size_t kda_prefill_workspace_size(int64_t T_total, int N, int H, int d_k, int d_v, int chunk,
                                   kda_dtype_t dtype)
 {
     if (!prefill_shape_ok(T_total, N, H, d_k, d_v, chunk, dtype)) return 0;
-    return kda::prefill_plan(T_total, N, H, d_k, d_v).workspace_bytes;
+    return plan_for(T_total, N, H, d_k, d_v, dtype).workspace_bytes;
 }
 
 // force_L > 0 fixes the segment length in chunks; warm_req < 0 takes the
@@ -294,8 +307,6 @@ static kda_status_t prefill_impl(const char* who, const void* q, const void* k, 
     if (!dim_ok(d_k) || !dim_ok(d_v))
         return fail(KDA_ERR_UNSUPPORTED, "%s: d_k=%d d_v=%d not in {32,64,128}", who, d_k, d_v);
     if (chunk != 64) return fail(KDA_ERR_UNSUPPORTED, "%s: chunk=%d (only 64)", who, chunk);
-    if (dtype == KDA_F32 && (d_k != 32 || d_v > 64))
-        return fail(KDA_ERR_UNSUPPORTED, "%s: fp32 tensors need d_k = 32, d_v <= 64", who);
     if (T_total > int64_t(0x7fffffff))  // token offsets are int32, as cu_seqlens
         return fail(KDA_ERR_UNSUPPORTED, "%s: T_total > 2^31 - 1", who);
     if (T_total > 0 && (!q || !k || !v || !g || !beta || !o))
@@ -307,11 +318,11 @@ static kda_status_t prefill_impl(const char* who, const void* q, const void* k, 
         const size_t na = size_t(H) * sizeof(float);
         if (overlap(o, size_t(T_total) * H * d_v * dsize(dtype), gate_A, na) ||
             overlap(final_state, final_state ? size_t(N) * H * d_k * d_v * sizeof(float) : 0, gate_A, na) ||
-            overlap(workspace, kda::prefill_plan(T_total, N, H, d_k, d_v, force_L, warm_req).workspace_bytes,
+            overlap(workspace, plan_for(T_total, N, H, d_k, d_v, dtype, force_L, warm_req).workspace_bytes,
                     gate_A, na))
             return fail(KDA_ERR_INVALID_ARGUMENT, "%s: A overlaps an output buffer", who);
     }
-    const kda::PrefillPlan plan = kda::prefill_plan(T_total, N, H, d_k, d_v, force_L, warm_req);
+    const kda::PrefillPlan plan = plan_for(T_total, N, H, d_k, d_v, dtype, force_L, warm_req);
     const size_t ws_need = plan.workspace_bytes;
     if (ws_need > 0 && (!workspace || workspace_bytes < ws_need))
         return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes < %zu needed", who,
@@ -369,8 +380,9 @@ static kda_status_t prefill_impl(const char* who, const void* q, const void* k, 
     }
     a.gate_A = gate_A;
     a.g_min = g_min;
-    const hipError_t e = dtype == KDA_BF16 ? kda::launch_prefill<kda::BF16>(a, plan, s)
-                                           : kda::launch_prefill<kda::F32>(a, plan, s);
+    const hipError_t e = serial_path(d_k, d_v, dtype) ? kda::launch_serial(a, plan, s)
+                         : dtype == KDA_BF16         ? kda::launch_prefill<kda::BF16>(a, plan, s)
+                                                     : kda::launch_prefill<kda::F32>(a, plan, s);
     return from_hip(e, "kda_prefill launch");
 }
 
@@ -457,7 +469,7 @@ kda_status_t kda_prefill_gated_noalloc(const void* q, const void* k, const void*
     const char* who = "kda_prefill_gated_noalloc";
     if (!prefill_shape_ok(T_total, N, H, d_k, d_v, chunk, dtype))
         return fail(KDA_ERR_UNSUPPORTED, "%s: shape outside the supported set (see kda_prefill)", who);
-    const size_t need = kda::prefill_plan(T_total, N, H, d_k, d_v).workspace_bytes;
+    const size_t need = plan_for(T_total, N, H, d_k, d_v, dtype).workspace_bytes;
     if (need > KDA_NOALLOC_SCRATCH_BYTES)
         return fail(KDA_ERR_UNSUPPORTED, "%s: this call needs %zu bytes of workspace, more than the %zu-byte "
                     "static scratch; use kda_prefill_gated with a workspace", who, need,
@@ -479,7 +491,7 @@ size_t kda_test_prefill_workspace_size(int64_t T_total, int N, int H, int d_k, i
                                        int seg_chunks, int warm_tokens)
 {
     if (!prefill_shape_ok(T_total, N, H, d_k, d_v, 64, dtype) || !test_plan_ok(seg_chunks, warm_tokens)) return 0;
-    return kda::prefill_plan(T_total, N, H, d_k, d_v, seg_chunks, warm_tokens).workspace_bytes;
+    return plan_for(T_total, N, H, d_k, d_v, dtype, seg_chunks, warm_tokens).workspace_bytes;
 }
 
 int64_t kda_test_prefill_flags(int64_t T_total, int N, int H, int d_k, int d_v, kda_dtype_t dtype, int seg_chunks,
@@ -488,7 +500,7 @@ int64_t kda_test_prefill_flags(int64_t T_total, int N, int H, int d_k, int d_v, 
     if (!prefill_shape_ok(T_total, N, H, d_k, d_v, 64, dtype) || !test_plan_ok(seg_chunks, warm_tokens) ||
         !offset_bytes)
         return -1;
-    const kda::PrefillPlan p = kda::prefill_plan(T_total, N, H, d_k, d_v, seg_chunks, warm_tokens);
+    const kda::PrefillPlan p = plan_for(T_total, N, H, d_k, d_v, dtype, seg_chunks, warm_tokens);
     *offset_bytes = p.off_flags;
     return p.warm > 0 ? p.nseg_max * H : 0;
 }
@@ -535,6 +547,19 @@ int64_t kda_describe_prefill_plan(int64_t T_total, int N, int H, int d_k, int d_
                                   char* buf, size_t cap)
 {
     if (!prefill_shape_ok(T_total, N, H, d_k, d_v, 64, dtype) || (!packed && N != 1) || (!buf && cap > 0)) return -1;
+    if (serial_path(d_k, d_v, dtype)) {
+        const kda::PrefillPlan p = kda::serial_plan(T_total, N);
+        char head[512];
+        snprintf(head, sizeof(head),
+                 "kda_prefill plan: T_total=%lld N=%d H=%d d_k=%d d_v=%d dtype=f32%s\n"
+                 "token-serial fp32 path (no chunk kernel for this fp32 head shape): one segment per sequence\n"
+                 "workspace: %zu bytes\n",
+                 (long long)T_total, N, H, d_k, d_v, packed ? " (packed, cu_seqlens given)" : "",
+                 p.workspace_bytes);
+        std::string text = head;
+        kda::describe_serial(N, H, d_v, packed != 0, text);
+        return emit_text(text, buf, cap);
+    }
     const kda::PrefillPlan p = kda::prefill_plan(T_total, N, H, d_k, d_v);
     char head[512];
     snprintf(head, sizeof(head),

@@ -85,7 +85,7 @@ int main()
     EXPECT(prefill(0, 256, 64, BF, at(16), need) == KDA_ERR_INVALID_ARGUMENT);
     EXPECT(prefill(3, 256, 64, BF, at(16), need) == KDA_ERR_INVALID_ARGUMENT);
     EXPECT(prefill(1, 256, 96, BF, at(16), need) == KDA_ERR_UNSUPPORTED);
-    EXPECT(prefill(1, 256, 64, F, at(16), need) == KDA_ERR_UNSUPPORTED);
+    EXPECT(prefill(1, 256, 64, F, at(16), 0) == KDA_ERR_WORKSPACE_TOO_SMALL);  // the fp32 token-serial path
     EXPECT(prefill(1, int64_t(1) << 31, 64, BF, at(16), need) == KDA_ERR_UNSUPPORTED);
     EXPECT(prefill(1, 256, 64, BF, nullptr, need) == KDA_ERR_INVALID_ARGUMENT);
     if (need > 0) EXPECT(prefill(1, 256, 64, BF, at(16), need - 1) == KDA_ERR_WORKSPACE_TOO_SMALL);

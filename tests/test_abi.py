@@ -121,8 +121,10 @@ def test_prefill_workspace_size(L):
     assert ws(0, 1, 32, 128, 128) > 0
     assert ws(8192, 1, 32, 96, 128) == 0
     assert ws(8192, 1, 32, 128, 128, chunk=32) == 0
-    assert ws(8192, 1, 32, 128, 128, dtype=F32) == 0      # fp32 needs d_k = 32
-    assert ws(8192, 1, 32, 64, 64, dtype=F32) == 0
+    # fp32 shapes without a chunk kernel run token by token: only the table
+    assert 0 < ws(8192, 1, 32, 128, 128, dtype=F32) <= 256
+    assert 0 < ws(8192, 1, 32, 64, 64, dtype=F32) <= 256
+    assert 0 < ws(1 << 20, 3, 32, 32, 128, dtype=F32) <= 256
     assert ws(256, 1, 2, 32, 32, dtype=F32) > 0
     assert ws(256, 1, 16384, 32, 32) > 0
     assert ws(256, 1, 16385, 32, 32) == 0                 # H above KDA_MAX_HEADS
@@ -157,7 +159,7 @@ def test_prefill_validation(L):
     assert call(N=3) == 1                                   # N > 1 needs cu_seqlens
     assert call(dk=96) == 2
     assert call(chunk=32) == 2
-    assert call(dt=F32, dk=128, dv=128) == 2
+    assert call(dt=F32, dk=96, dv=128) == 2
     assert call(dt=9) == 2
     assert call(H=16385) == 2                               # H above KDA_MAX_HEADS
     assert call(T=1 << 31) == 2                             # token offsets are int32
@@ -478,6 +480,15 @@ def test_plan_descriptions(L):
     assert L.kda_describe_prefill_plan(8192, 1, 32, 128, 128, BF16, 0, None, 16) == -1
     assert L.kda_describe_prefill_plan(8192, 2, 32, 128, 128, BF16, 0, None, 0) == -1  # N > 1 needs cu_seqlens
     assert L.kda_describe_prefill_plan(8192, 1, 32, 96, 128, BF16, 0, None, 0) == -1
-    assert L.kda_describe_prefill_plan(8192, 1, 32, 128, 128, F32, 0, None, 0) == -1  # fp32 d_k > 32
+    # the token-serial fp32 path: its one launch (two when packed)
+    n32 = L.kda_describe_prefill_plan(8192, 1, 32, 128, 128, F32, 0, None, 0)
+    buf = ctypes.create_string_buffer(n32 + 1)
+    assert L.kda_describe_prefill_plan(8192, 1, 32, 128, 128, F32, 0, buf, n32 + 1) == n32
+    txt = buf.value.decode()
+    assert "token-serial" in txt and "prefill_serial_kernel grid 32 x 256" in txt and "plan_kernel" not in txt
+    n32p = L.kda_describe_prefill_plan(8192, 4, 8, 64, 32, F32, 1, None, 0)
+    buf = ctypes.create_string_buffer(n32p + 1)
+    L.kda_describe_prefill_plan(8192, 4, 8, 64, 32, F32, 1, buf, n32p + 1)
+    assert "plan_kernel" in buf.value.decode() and "prefill_serial_kernel grid 32 x 64" in buf.value.decode()
     assert L.kda_describe_backward_plan(-1, 1, 32, 128, 128, BF16, None, 0) == -1
     assert L.kda_describe_backward_plan(64, 1, 32, 128, 128, 7, None, 0) == -1

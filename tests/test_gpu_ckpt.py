@@ -86,5 +86,13 @@ def test_ckpt_f32(kda):
     check(kda, synth.TINY_F32.with_(seqlens=(256, 130), state_std=0.1), 64)
 
 
+@pytest.mark.parametrize("interval", [64, 192])
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 32)])
+def test_ckpt_f32_serial(kda, dk, dv, interval):
+    """checkpoints of the token-serial fp32 kernel over packed sequences"""
+    wl = synth.TINY_F32.with_(H=2, dk=dk, dv=dv, seqlens=(0, 63, 64, 65, 400, 130), state_std=0.1)
+    check(kda, wl, interval)
+
+
 def test_ckpt_8k(kda):
     check(kda, synth.PREFILL_8K, 512)

@@ -72,7 +72,10 @@ LENS = (0, 1, 63, 64, 65, 130, 300, 17)
 
 @pytest.mark.parametrize("dk,dv,dtype", [(128, 128, "bf16"), (64, 64, "bf16"), (32, 32, "bf16"),
                                          (128, 32, "bf16"), (32, 128, "bf16"), (64, 128, "bf16"),
-                                         (32, 32, "f32"), (32, 64, "f32")])
+                                         (32, 32, "f32"), (32, 64, "f32"),
+                                         # fp32 shapes of the token-serial kernel
+                                         (128, 128, "f32"), (64, 64, "f32"), (32, 128, "f32"), (64, 32, "f32"),
+                                         (64, 128, "f32"), (128, 32, "f32"), (128, 64, "f32")])
 def test_prefill_varlen_dims(kda, dk, dv, dtype):
     wl = synth.VARLEN_64.with_(H=3, dk=dk, dv=dv, dtype=dtype, seqlens=LENS, state_std=0.1)
     check(kda, wl)
@@ -167,3 +170,28 @@ def test_prefill_special_values(kda, case, dtype, warm):
             assert relerr(host(S[n]), decay[:, :, None] * S0[n]) < tol
     if case == "alpha1_beta1_orthonormal" and dtype == "f32":  # exact recall: o_t = v_t
         assert relerr(host(o), x["v"]) < tol
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 128)])
+def test_prefill_f32_serial_long(kda, dk, dv):
+    """The token-serial fp32 path over one 3000-token sequence with the weak
+    decay of z - 3 (the incoming state and early tokens still matter at the
+    end), and the same sequence split in two calls chained through the final
+    state, in place (initial_state is final_state)."""
+    import torch
+    wl = synth.TINY_F32.with_(H=2, dk=dk, dv=dv, seqlens=(3000,), z_shift=-3.0, state_std=0.1)
+    o, S = check(kda, wl, tag="serial long")
+    x = synth.prefill_inputs(wl)
+    S0 = synth.initial_state(wl)
+    g = kda.kda_gate(dev(x["z"]), dev(x["A"]))
+    St = dev(S0)
+    outs = []
+    for a, b in ((0, 1700), (1700, 3000)):
+        sl = lambda name: dev(x[name][a:b])
+        oo, _ = kda.kda_prefill(sl("q"), sl("k"), sl("v"), g[a:b].contiguous(), sl("beta"), initial_state=St,
+                                final_state=St)
+        outs.append(oo)
+    torch.cuda.synchronize()
+    # the same arithmetic token by token: split calls equal one call exactly
+    assert np.array_equal(host(torch.cat(outs)), o)
+    assert np.array_equal(host(St), S)

@@ -57,7 +57,7 @@ def test_gated_8k_bf16(kda):
 
 
 @pytest.mark.parametrize("dk,dv,dtype", [(128, 128, "bf16"), (64, 64, "bf16"), (32, 32, "bf16"),
-                                         (32, 32, "f32"), (32, 64, "f32")])
+                                         (32, 32, "f32"), (32, 64, "f32"), (128, 128, "f32"), (64, 32, "f32")])
 def test_gated_varlen_dims(kda, dk, dv, dtype):
     wl = synth.VARLEN_64.with_(H=3, dk=dk, dv=dv, dtype=dtype, seqlens=(0, 1, 63, 64, 65, 130, 300, 17),
                                state_std=0.1)
