@@ -432,6 +432,22 @@ kda_status_t kda_commit(const void* k, const void* v, const void* g, const void*
                         const int32_t* n_accept, float* state, int B, int K, int H, int d_k, int d_v,
                         kda_dtype_t dtype, void* stream);
 
+/*
+ * kda_debug_check_bits — exported only by the checked build of the library
+ * (libkda_checked.so, compiled with -DKDA_DEVICE_CHECKS; a debugging aid, not
+ * a method step).  In that build every kernel checks, where it sets up its
+ * work item, that the token ranges, sequence and state indices, workspace
+ * indices, checkpoint rows and block lengths its accesses are derived from
+ * lie inside the buffers' extents, and sets one bit per kind of failure in a
+ * device word (bit 0 token range, 1 sequence or state index, 2 workspace
+ * index, 3 checkpoint row, 4 block length); kernels carry on either way.
+ *   bits  : host pointer; receives the word of the current device.  The call
+ *           synchronises with the device (a blocking copy).
+ *   reset : non-zero clears the word after reading it.
+ * Errors: KDA_ERR_INVALID_ARGUMENT (null bits), KDA_ERR_HIP.
+ */
+kda_status_t kda_debug_check_bits(unsigned int* bits, int reset);
+
 #ifdef __cplusplus
 }
 #endif

@@ -8,11 +8,14 @@ been built, importing the binding functions raises: there is no fallback.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libkda.so")
+# the same library with device-side bounds checks (kda_debug_check_bits)
+CHECKED_LIB_PATH = os.path.join(HERE, "libkda_checked.so")
 
 KDA_F32, KDA_BF16 = 0, 1
 _STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARGUMENT", 2: "KDA_ERR_UNSUPPORTED",
@@ -37,64 +40,96 @@ def lib() -> ctypes.CDLL:
     """The loaded libkda (raises if it has not been built)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise ImportError(f"libkda.so not found at {LIB_PATH}; build it with "
-                              "`python -m linear_attention_sequence_gate_amd.build`")
-        L = ctypes.CDLL(LIB_PATH)
-        P, I, I64, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
-        L.kda_status_string.argtypes = [I]
-        L.kda_status_string.restype = ctypes.c_char_p
-        L.kda_last_error.argtypes = []
-        L.kda_last_error.restype = ctypes.c_char_p
-        L.kda_version.argtypes = []
-        L.kda_version.restype = I
-        L.kda_gate.argtypes = [P, P, P, I64, I, I, I, F, P]
-        L.kda_gate.restype = I
-        L.kda_prefill_workspace_size.argtypes = [I64, I, I, I, I, I, I]
-        L.kda_prefill_workspace_size.restype = SZ
-        L.kda_prefill.argtypes = [P, P, P, P, P, P, I, I64, I, I, I, I, P, P, P, I, P, SZ, P]
-        L.kda_prefill.restype = I
-        L.kda_decode_step.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, P]
-        L.kda_decode_step.restype = I
-        L.kda_verify.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, P]
-        L.kda_verify.restype = I
-        L.kda_commit.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, P]
-        L.kda_commit.restype = I
-        L.kda_prefill_ckpt.argtypes = [P, P, P, P, P, P, I, I64, I, I, I, I, P, P, P, I, P, SZ, I, P, I64, P]
-        L.kda_prefill_ckpt.restype = I
-        L.kda_prefill_gated.argtypes = [P, P, P, P, P, F, P, P, I, I64, I, I, I, I, P, P, P, I, P, SZ, I, P, I64,
-                                        P]
-        L.kda_prefill_gated.restype = I
-        L.kda_decode_step_gated.argtypes = [P, P, P, P, P, F, P, P, P, I, I, I, I, I, P]
-        L.kda_decode_step_gated.restype = I
-        L.kda_backward_workspace_size.argtypes = [I64, I, I, I, I]
-        L.kda_backward_workspace_size.restype = SZ
-        L.kda_backward.argtypes = [P, P, P, P, P, P, I, I64, I, I, I, P, P, I64, I, P, P, P, P, P, P, P, P, I, P,
-                                   SZ, P]
-        L.kda_backward.restype = I
-        L.kda_test_prefill.argtypes = [P, P, P, P, P, F, P, P, I, I64, I, I, I, P, P, P, I, P, SZ, I, P, I64, I, I,
-                                       P]
-        L.kda_test_prefill.restype = I
-        L.kda_test_prefill_workspace_size.argtypes = [I64, I, I, I, I, I, I, I]
-        L.kda_test_prefill_workspace_size.restype = SZ
-        L.kda_test_prefill_flags.argtypes = [I64, I, I, I, I, I, I, I, ctypes.POINTER(SZ)]
-        L.kda_test_prefill_flags.restype = I64
-        L.kda_prefill_gated_noalloc.argtypes = [P, P, P, P, P, F, P, P, I, I64, I, I, I, I, P, P, P, I, I, P, I64,
-                                                P]
-        L.kda_prefill_gated_noalloc.restype = I
-        L.kda_test_backward.argtypes = [P, P, P, P, P, P, I, I64, I, I, I, P, P, I64, I, P, P, P, P, P, P, P, P, I,
-                                        P, SZ, I64, I64, P]
-        L.kda_test_backward.restype = I
-        L.kda_test_backward_workspace_size.argtypes = [I64, I, I, I, I, I64]
-        L.kda_test_backward_workspace_size.restype = SZ
-        L.kda_checkpoint_count.argtypes = [P, I, I64, I]
-        L.kda_checkpoint_count.restype = I64
-        L.kda_describe_prefill_plan.argtypes = [I64, I, I, I, I, I, I, ctypes.c_char_p, SZ]
-        L.kda_describe_prefill_plan.restype = I64
-        L.kda_describe_backward_plan.argtypes = [I64, I, I, I, I, I, ctypes.c_char_p, SZ]
-        L.kda_describe_backward_plan.restype = I64
-        _lib = L
+        _lib = load(LIB_PATH)
     return _lib
+
+
+@contextlib.contextmanager
+def using_library(path: str):
+    """Route every binding call to the library at `path` (say the checked
+    build, CHECKED_LIB_PATH) inside the block."""
+    global _lib
+    prev = _lib
+    _lib = load(path)
+    try:
+        yield _lib
+    finally:
+        _lib = prev
+
+
+def device_check_bits(reset: bool = False) -> int:
+    """The checked build's device-side check bits (0: every check held);
+    synchronises with the device."""
+    L = lib()
+    if not hasattr(L, "kda_debug_check_bits"):
+        raise RuntimeError("the loaded library is not the checked build")
+    bits = ctypes.c_uint(0)
+    _check(L.kda_debug_check_bits(ctypes.byref(bits), int(reset)))
+    return bits.value
+
+
+def load(path: str) -> ctypes.CDLL:
+    """Load a build of libkda and declare its signatures."""
+    if not os.path.exists(path):
+        raise ImportError(f"{os.path.basename(path)} not found at {path}; build it with "
+                          "`python -m linear_attention_sequence_gate_amd.build`")
+    L = ctypes.CDLL(path)
+    P, I, I64, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    L.kda_status_string.argtypes = [I]
+    L.kda_status_string.restype = ctypes.c_char_p
+    L.kda_last_error.argtypes = []
+    L.kda_last_error.restype = ctypes.c_char_p
+    L.kda_version.argtypes = []
+    L.kda_version.restype = I
+    L.kda_gate.argtypes = [P, P, P, I64, I, I, I, F, P]
+    L.kda_gate.restype = I
+    L.kda_prefill_workspace_size.argtypes = [I64, I, I, I, I, I, I]
+    L.kda_prefill_workspace_size.restype = SZ
+    L.kda_prefill.argtypes = [P, P, P, P, P, P, I, I64, I, I, I, I, P, P, P, I, P, SZ, P]
+    L.kda_prefill.restype = I
+    L.kda_decode_step.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, P]
+    L.kda_decode_step.restype = I
+    L.kda_verify.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, P]
+    L.kda_verify.restype = I
+    L.kda_commit.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, P]
+    L.kda_commit.restype = I
+    L.kda_prefill_ckpt.argtypes = [P, P, P, P, P, P, I, I64, I, I, I, I, P, P, P, I, P, SZ, I, P, I64, P]
+    L.kda_prefill_ckpt.restype = I
+    L.kda_prefill_gated.argtypes = [P, P, P, P, P, F, P, P, I, I64, I, I, I, I, P, P, P, I, P, SZ, I, P, I64,
+                                    P]
+    L.kda_prefill_gated.restype = I
+    L.kda_decode_step_gated.argtypes = [P, P, P, P, P, F, P, P, P, I, I, I, I, I, P]
+    L.kda_decode_step_gated.restype = I
+    L.kda_backward_workspace_size.argtypes = [I64, I, I, I, I]
+    L.kda_backward_workspace_size.restype = SZ
+    L.kda_backward.argtypes = [P, P, P, P, P, P, I, I64, I, I, I, P, P, I64, I, P, P, P, P, P, P, P, P, I, P,
+                               SZ, P]
+    L.kda_backward.restype = I
+    L.kda_test_prefill.argtypes = [P, P, P, P, P, F, P, P, I, I64, I, I, I, P, P, P, I, P, SZ, I, P, I64, I, I,
+                                   P]
+    L.kda_test_prefill.restype = I
+    L.kda_test_prefill_workspace_size.argtypes = [I64, I, I, I, I, I, I, I]
+    L.kda_test_prefill_workspace_size.restype = SZ
+    L.kda_test_prefill_flags.argtypes = [I64, I, I, I, I, I, I, I, ctypes.POINTER(SZ)]
+    L.kda_test_prefill_flags.restype = I64
+    L.kda_prefill_gated_noalloc.argtypes = [P, P, P, P, P, F, P, P, I, I64, I, I, I, I, P, P, P, I, I, P, I64,
+                                            P]
+    L.kda_prefill_gated_noalloc.restype = I
+    L.kda_test_backward.argtypes = [P, P, P, P, P, P, I, I64, I, I, I, P, P, I64, I, P, P, P, P, P, P, P, P, I,
+                                    P, SZ, I64, I64, P]
+    L.kda_test_backward.restype = I
+    L.kda_test_backward_workspace_size.argtypes = [I64, I, I, I, I, I64]
+    L.kda_test_backward_workspace_size.restype = SZ
+    L.kda_checkpoint_count.argtypes = [P, I, I64, I]
+    L.kda_checkpoint_count.restype = I64
+    L.kda_describe_prefill_plan.argtypes = [I64, I, I, I, I, I, I, ctypes.c_char_p, SZ]
+    L.kda_describe_prefill_plan.restype = I64
+    L.kda_describe_backward_plan.argtypes = [I64, I, I, I, I, I, ctypes.c_char_p, SZ]
+    L.kda_describe_backward_plan.restype = I64
+    if hasattr(L, "kda_debug_check_bits"):
+        L.kda_debug_check_bits.argtypes = [ctypes.POINTER(ctypes.c_uint), I]
+        L.kda_debug_check_bits.restype = I
+    return L
 
 
 def _check(status: int):

@@ -1,5 +1,6 @@
-"""Build libkda.so (hipcc, gfx950) in place, next to this file, and the
-measurement library libkda_roofs.so (the benchmark's roofs)."""
+"""Build libkda.so (hipcc, gfx950) in place, next to this file, with its
+checked build libkda_checked.so (device-side bounds checks, -DKDA_DEVICE_CHECKS)
+and the measurement library libkda_roofs.so (the benchmark's roofs)."""
 from __future__ import annotations
 
 import os
@@ -10,6 +11,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkda.so")
+CHECKED_LIB = os.path.join(HERE, "libkda_checked.so")
 SOURCES = [os.path.join(CSRC, "kda_api.hip")]
 ROOFS_LIB = os.path.join(HERE, "libkda_roofs.so")
 ROOFS_SOURCES = [os.path.join(CSRC, "kda_roofs.hip")]
@@ -23,16 +25,19 @@ FLAGS = [
 ]
 
 
-def _compile(sources: list[str], out: str, verbose: bool, extra: list[str] | None) -> str:
+def _start(sources: list[str], out: str, verbose: bool, extra: list[str] | None):
     cmd = [HIPCC, *FLAGS, *(extra or []), "-I", os.path.join(ROOT, "include"), "-I", CSRC,
            *sources, "-o", out + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)
-    dst = out
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
-                    if "packed-fp32-ops" not in l)
-    if r.returncode != 0:
+    return out, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+
+
+def _finish(job, verbose: bool) -> str:
+    dst, proc = job
+    text, _ = proc.communicate()
+    out = "\n".join(l for l in text.splitlines() if "packed-fp32-ops" not in l)
+    if proc.returncode != 0:
         sys.stderr.write(out + "\n")
         raise RuntimeError(f"{os.path.basename(dst)} build failed")
     if verbose and out.strip():
@@ -42,9 +47,13 @@ def _compile(sources: list[str], out: str, verbose: bool, extra: list[str] | Non
 
 
 def build(verbose: bool = False, extra: list[str] | None = None) -> str:
-    """Compile libkda.so and libkda_roofs.so; returns libkda's path."""
-    _compile(ROOFS_SOURCES, ROOFS_LIB, verbose, extra)
-    return _compile(SOURCES, LIB, verbose, extra)
+    """Compile libkda.so, libkda_checked.so and libkda_roofs.so (side by
+    side); returns libkda's path."""
+    jobs = [_start(ROOFS_SOURCES, ROOFS_LIB, verbose, extra),
+            _start(SOURCES, CHECKED_LIB, verbose, [*(extra or []), "-DKDA_DEVICE_CHECKS"]),
+            _start(SOURCES, LIB, verbose, extra)]
+    done = [_finish(j, verbose) for j in jobs]
+    return done[-1]
 
 
 if __name__ == "__main__":

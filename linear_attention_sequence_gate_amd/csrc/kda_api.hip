@@ -719,6 +719,21 @@ int64_t kda_checkpoint_count(const int32_t* cu_seqlens_host, int N, int64_t T_to
 
 }  // extern "C"
 
+#ifdef KDA_DEVICE_CHECKS
+// The device-side check bits of the checked build (see include/kda.h).
+extern "C" kda_status_t kda_debug_check_bits(unsigned int* bits, int reset)
+{
+    if (!bits) return fail(KDA_ERR_INVALID_ARGUMENT, "kda_debug_check_bits: null pointer");
+    hipError_t e = hipMemcpyFromSymbol(bits, HIP_SYMBOL(kda::kda_check_bits), sizeof(unsigned int), 0,
+                                       hipMemcpyDeviceToHost);
+    if (e == hipSuccess && reset) {
+        const unsigned int zero = 0;
+        e = hipMemcpyToSymbol(HIP_SYMBOL(kda::kda_check_bits), &zero, sizeof(zero), 0, hipMemcpyHostToDevice);
+    }
+    return from_hip(e, "kda_debug_check_bits");
+}
+#endif
+
 #ifdef KDA_PHASE_TIMING
 // Copy the per-workgroup phase cycle counters of the last chunk-kernel launch.
 extern "C" int kda_phase_cycles_read(unsigned long long* host, int n)

@@ -52,6 +52,7 @@ struct BackwardArgs {
     float* dsend;           // per (segment, head): dS at the segment's end [dk][dv], fp32
     int32_t* flags = nullptr;  // per (segment, head): 1 where the window's M^T was not zero
     int64_t warm = 0;          // window tokens (a multiple of 16); 0: summary pass and scan for every chain
+    int64_t segs_cap = 0;      // the plan's segment count (bounds checks)
 };
 
 // Whether the chain (sequence of segments seg0 .. seg0+nseg-1, head h) goes
@@ -158,6 +159,8 @@ __global__ void __launch_bounds__(256) bwd_scan_kernel(BackwardArgs a)
             prev = x;
         }
     }
+    KDA_CHECK(n < a.N, CK_SEQ);
+    KDA_CHECK(seg0 + nseg <= a.segs_cap, CK_WS);
     if (!bwd_chain_flagged(a, seg0, nseg, h)) return;  // the windows gave every dS_end
     auto cm_of = [&](int s) { return a.cm + (int64_t(seg0 + s) * H + h) * (DK * DV + DK * DK); };
     auto dsend_of = [&](int s) { return a.dsend + (int64_t(seg0 + s) * H + h) * DK * DV; };

@@ -261,6 +261,8 @@ __device__ __forceinline__ void bwd_prep_load(BwdRaw<C, DT>& R, const BackwardAr
     const int tid = fresh_tid();
     const int64_t H = a.H;
     const int64_t row0 = t_s * H + h;
+    KDA_CHECK(t_s >= 0 && t_s + n <= a.T_total, CK_TOKENS);
+    KDA_CHECK(n >= 1 && n <= BSUB, CK_BLOCK);
     const uint32_t rsk = uint32_t(H) * DK, rsv = uint32_t(H) * DV;
     if (DK * RW::PARTS >= C::NT || tid < DK * RW::PARTS) {
         const int c = tid / RW::PARTS, part = tid % RW::PARTS, r0 = part * RW::TPT;
@@ -565,6 +567,9 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, false>::NT)) bwd_chunk_sum
     const int item = blockIdx.x, h = item % H;
     const SegLoc L = bwd_locate(a, item / H);
     if (L.n < 0) return;
+    KDA_CHECK(L.n < a.N, CK_SEQ);
+    KDA_CHECK(L.c0 >= 0 && L.c0 <= L.t0 && L.t0 <= L.t1 && L.t1 <= L.c1 && L.c1 <= a.T_total, CK_TOKENS);
+    KDA_CHECK(item < a.segs_cap * H, CK_WS);
     const bool last = L.s == L.nseg - 1;
     const int64_t unit = int64_t(L.n) * H + h;
     // the tokens this workgroup runs backwards over, and where dS starts
@@ -797,6 +802,9 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
         const int h = item % H;
         const SegLoc L = bwd_locate(a, item / H);
         if (L.n < 0) break;
+        KDA_CHECK(L.n < a.N, CK_SEQ);
+        KDA_CHECK(L.c0 >= 0 && L.c0 <= L.t0 && L.t0 <= L.t1 && L.t1 <= L.c1 && L.c1 <= a.T_total, CK_TOKENS);
+        KDA_CHECK(item < a.segs_cap * H, CK_WS);
         const int64_t c0 = L.c0, ck0 = L.ck0;
         const int64_t unit = int64_t(L.n) * H + h;
         f32x4 dS[NCT][CT];
@@ -866,6 +874,7 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
                 const float* init = a.init ? a.init + unit * DK * DV : nullptr;
                 const int64_t m = chunk_ck(j);
                 const int64_t from = m >= 1 ? c0 + m * a.ckpt_interval : c0;
+                KDA_CHECK(m < 1 || (ck0 + m - 1 >= 0 && ck0 + m - 1 < a.ckpt_cap), CK_CKPT);
                 if (chain) load_tiles(S, m >= 1 ? a.ckpt + ((ck0 + m - 1) * H + h) * DK * DV : init);
                 for (int64_t t = from; t < t0; t += BSUB) fwd_sub(S, [&] { consume(j); });
                 // forward through the chunk, keeping the state at each sub-chunk start
@@ -1214,6 +1223,7 @@ hipError_t launch_backward(const BackwardArgs& a, const BwdPlan& plan, int dk, i
     b.dsend = reinterpret_cast<float*>(ws + plan.off_dsend);
     b.flags = reinterpret_cast<int32_t*>(ws + plan.off_flags);
     b.warm = plan.warm;
+    b.segs_cap = plan.segs_max;
 #define KDA_BWD(DKV, DVV) \
     if (dk == DKV && dv == DVV) return launch_bwd_chunk<DT, DKV, DVV>(b, plan, stream);
     KDA_BWD(32, 32) KDA_BWD(32, 64) KDA_BWD(32, 128)

@@ -6,6 +6,31 @@
 
 namespace kda {
 
+// Device-side bounds checks, compiled only with -DKDA_DEVICE_CHECKS (the
+// library's checked build): each kernel checks, at its work item's set-up,
+// that the index ranges its accesses are derived from lie inside the
+// buffers' extents; a failed check sets its bit in kda_check_bits (read back
+// by kda_debug_check_bits) and the kernel carries on.  The release build
+// compiles every check away.
+enum CheckBit {
+    CK_TOKENS = 0,   // a token range outside [0, T_total)
+    CK_SEQ = 1,      // a sequence or state index outside [0, N)
+    CK_WS = 2,       // a workspace index (segment, summary, flag) outside its plan's count
+    CK_CKPT = 3,     // a checkpoint row read outside [0, capacity)
+    CK_BLOCK = 4,    // a block or sub-chunk length outside [1, its size]
+};
+#ifdef KDA_DEVICE_CHECKS
+__device__ unsigned int kda_check_bits;
+#define KDA_CHECK(cond, bit)                                                        \
+    do {                                                                            \
+        if (!(cond)) atomicOr(&::kda::kda_check_bits, 1u << (unsigned)(::kda::bit)); \
+    } while (0)
+#else
+#define KDA_CHECK(cond, bit) \
+    do {                     \
+    } while (0)
+#endif
+
 typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;

@@ -222,6 +222,7 @@ struct PrefillDev {
     float g_min;
     int32_t* flags;  // [nseg_max][H]: 1 where a segment's warm-up left M non-zero; null: no warm-up pass
     int warm;        // warm-up tokens
+    int64_t nseg_cap = 0, np1_cap = 0;  // the plan's segment and non-final segment counts (bounds checks)
 };
 
 // Table entries (cu_seqlens clamped, segment, pass-1 and checkpoint offsets)
@@ -767,6 +768,8 @@ __device__ __forceinline__ void prep_load(PrepRegs<C, DT>& r, const PrefillDev& 
     using ST = typename DT::storage;
     using Pair = typename Op<DT>::Pair;
     const int64_t H = p.H;
+    KDA_CHECK(b0 >= 0 && b0 + len <= p.T_total, CK_TOKENS);
+    KDA_CHECK(len >= 1 && len <= BC, CK_BLOCK);
     // uniform per-block byte bases + 32-bit lane byte offsets (a block spans 32
     // token rows, and the host caps H so that a row is below 2^24 bytes)
     const int64_t rk0 = (b0 * H + h) * C::DK * int64_t(sizeof(ST)), rv0 = (b0 * H + h) * C::DV * int64_t(sizeof(ST));
@@ -1172,6 +1175,9 @@ prefill_block_kernel(PrefillDev p)
     if (t_end > seq1) t_end = seq1;
     const bool last_seg = (s == nseg - 1);
     const int64_t nblk = (t_end - t_begin + BC - 1) / BC;
+    KDA_CHECK(n >= 0 && n < p.N, CK_SEQ);
+    KDA_CHECK(seq0 >= 0 && seq0 <= t_begin && t_begin <= t_end && t_end <= seq1 && seq1 <= p.T_total, CK_TOKENS);
+    KDA_CHECK(SUMMARY ? item < p.np1_cap : seg0 + s < p.nseg_cap, CK_WS);
     ST* go = static_cast<ST*>(p.o);
     // first checkpoint slot of this sequence, read before the block loop (a
     // table read inside it would wait for every store in flight)
@@ -1509,6 +1515,7 @@ __global__ void __launch_bounds__(256) scan_kernel(PrefillDev p)
 #endif
     // Table entries are read once, into registers: a re-read after the state
     // stores below would wait for every load in flight, the prefetch included.
+    KDA_CHECK(tab_p1(p, n) + nseg - 1 <= p.np1_cap && tab_seg(p, n) + nseg <= p.nseg_cap, CK_WS);
     const float* const ms0 = p.ms + (int64_t(tab_p1(p, n)) * H + h) * DK * (DK + DV);
     float* const sin0 = p.sin + (int64_t(tab_seg(p, n)) * H + h) * DK * DV;
     auto ms_of = [&](int st) { return ms0 + int64_t(st) * H * DK * (DK + DV); };
@@ -1696,6 +1703,10 @@ prefill_warm_kernel(PrefillDev p)
     const bool from_zero = ws > seq0;  // else the window starts at the sequence start
     const int64_t nwarm = (t_begin - ws) / BC;
     const int64_t nblk = nwarm + (t_end - t_begin + BC - 1) / BC;
+    KDA_CHECK(n >= 0 && n < p.N, CK_SEQ);
+    KDA_CHECK(seq0 >= 0 && seq0 <= ws && ws <= t_begin && t_begin <= t_end && t_end <= seq1 &&
+                  seq1 <= p.T_total, CK_TOKENS);
+    KDA_CHECK(item >= 0 && item < p.nseg_cap, CK_WS);
     ST* go = static_cast<ST*>(p.o);
     const int64_t ck_first = p.ckpt ? int64_t(tab_ck(p, n)) : 0;
     int32_t* gflag = p.flags + int64_t(item) * H + h;
@@ -1917,7 +1928,8 @@ hipError_t launch_prefill_t(const PrefillArgs& a, const PrefillPlan& plan, hipSt
                  plan.np1_max > 0 ? reinterpret_cast<float*>(ws + plan.off_sin) : nullptr,
                  a.ckpt, a.ckpt_interval, a.ckpt_cap, single ? 1 : 0, single_nseg, single_nck,
                  a.gate_A, a.g_min,
-                 warm ? reinterpret_cast<int32_t*>(ws + plan.off_flags) : nullptr, plan.warm};
+                 warm ? reinterpret_cast<int32_t*>(ws + plan.off_flags) : nullptr, plan.warm,
+                 plan.nseg_max, plan.np1_max};
     hipError_t e = hipSuccess;
     if (!single) {
         hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, stream, a.cu, a.N, a.T_total,

@@ -67,6 +67,8 @@ __global__ void __launch_bounds__(64 * (DV / 32)) prefill_serial_kernel(PrefillD
 
     const int32_t t0 = tab_cu(p, n);
     const int len = tab_cu(p, n + 1) - t0;
+    KDA_CHECK(n < p.N, CK_SEQ);
+    KDA_CHECK(t0 >= 0 && len >= 0 && int64_t(t0) + len <= p.T_total, CK_TOKENS);
     const GateZ gz = GateZ::of_head(GATED ? p.gate_A : nullptr, h, p.g_min);
 
     // piece j of this thread in the group starting at token i0: piece
@@ -229,7 +231,7 @@ hipError_t launch_serial_t(const PrefillArgs& a, const PrefillPlan& plan, hipStr
     PrefillDev d{a.q, a.k, a.v, a.g, a.beta, tab, a.N, a.T_total, a.H, plan.seg_chunks,
                  a.init, a.fin, a.o, nullptr, nullptr,
                  a.ckpt, a.ckpt_interval, a.ckpt_cap, single ? 1 : 0, 1, single_nck,
-                 a.gate_A, a.g_min, nullptr, 0};
+                 a.gate_A, a.g_min, nullptr, 0, plan.nseg_max, 0};
     hipError_t e = hipSuccess;
     if (!single) {
         hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, stream, a.cu, a.N, a.T_total, plan.seg_chunks,

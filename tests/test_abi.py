@@ -26,11 +26,25 @@ def L():
     return kda.lib()
 
 
+CHECKED_ONLY = {"kda_debug_check_bits"}  # exported by the checked build alone
+
+
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert set(names) == set(kda.EXPORTED), names
+    assert set(names) == set(kda.EXPORTED) | CHECKED_ONLY, names
     for n in names:
-        assert hasattr(L, n), f"libkda does not export {n}"
+        assert hasattr(L, n) == (n not in CHECKED_ONLY), f"libkda and {n}"
+
+
+def test_checked_build_exports(L):
+    """The checked build (device-side bounds checks) exports every declared
+    symbol, its check-bit reader included, and validates like the release
+    build on the host."""
+    C = kda.load(kda.CHECKED_LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(C, n), f"libkda_checked does not export {n}"
+    assert C.kda_debug_check_bits(None, 0) == 1  # null pointer, refused before any device call
+    assert C.kda_gate(FAKE, FAKE + (1 << 20), FAKE + (2 << 20), 4, 2, 32, BF16, -6.0, None) == 1
 
 
 def test_version_and_status_strings(L):
