@@ -274,7 +274,7 @@ static bool serial_path(int d_k, int d_v, kda_dtype_t dtype)
 static kda::PrefillPlan plan_for(int64_t T_total, int N, int H, int d_k, int d_v, kda_dtype_t dtype,
                                  int force_L = 0, int warm_req = -1)
 {
-    if (serial_path(d_k, d_v, dtype)) return kda::serial_plan(T_total, N);
+    if (serial_path(d_k, d_v, dtype)) return kda::serial_plan(T_total, N, H, force_L, warm_req);
     return kda::prefill_plan(T_total, N, H, d_k, d_v, force_L, warm_req);
 }
 
@@ -548,16 +548,17 @@ int64_t kda_describe_prefill_plan(int64_t T_total, int N, int H, int d_k, int d_
 {
     if (!prefill_shape_ok(T_total, N, H, d_k, d_v, 64, dtype) || (!packed && N != 1) || (!buf && cap > 0)) return -1;
     if (serial_path(d_k, d_v, dtype)) {
-        const kda::PrefillPlan p = kda::serial_plan(T_total, N);
+        const kda::PrefillPlan p = kda::serial_plan(T_total, N, H);
         char head[512];
         snprintf(head, sizeof(head),
                  "kda_prefill plan: T_total=%lld N=%d H=%d d_k=%d d_v=%d dtype=f32%s\n"
-                 "token-serial fp32 path (no chunk kernel for this fp32 head shape): one segment per sequence\n"
-                 "workspace: %zu bytes\n",
-                 (long long)T_total, N, H, d_k, d_v, packed ? " (packed, cu_seqlens given)" : "",
-                 p.workspace_bytes);
+                 "token-serial fp32 path (no chunk kernel for this fp32 head shape)\n"
+                 "segments: %d chunks of 64 tokens (%lld tokens) each; at most %lld segments\n"
+                 "warm-up window: %d tokens\nworkspace: %zu bytes\n",
+                 (long long)T_total, N, H, d_k, d_v, packed ? " (packed, cu_seqlens given)" : "", p.seg_chunks,
+                 (long long)p.seg_chunks * 64, (long long)p.nseg_max, p.warm, p.workspace_bytes);
         std::string text = head;
-        kda::describe_serial(N, H, d_v, packed != 0, text);
+        kda::describe_serial(p, N, H, d_k, d_v, packed != 0, text);
         return emit_text(text, buf, cap);
     }
     const kda::PrefillPlan p = kda::prefill_plan(T_total, N, H, d_k, d_v);

@@ -135,10 +135,10 @@ def test_prefill_workspace_size(L):
     assert ws(0, 1, 32, 128, 128) > 0
     assert ws(8192, 1, 32, 96, 128) == 0
     assert ws(8192, 1, 32, 128, 128, chunk=32) == 0
-    # fp32 shapes without a chunk kernel run token by token: only the table
-    assert 0 < ws(8192, 1, 32, 128, 128, dtype=F32) <= 256
-    assert 0 < ws(8192, 1, 32, 64, 64, dtype=F32) <= 256
-    assert 0 < ws(1 << 20, 3, 32, 32, 128, dtype=F32) <= 256
+    # fp32 shapes without a chunk kernel run token by token: the table and a flag per (segment, head)
+    assert 0 < ws(8192, 1, 32, 128, 128, dtype=F32) <= 256 + 256 * 4
+    assert 0 < ws(8192, 1, 32, 64, 64, dtype=F32) <= 256 + 256 * 4
+    assert 0 < ws(1 << 20, 3, 32, 32, 128, dtype=F32) < 1 << 20
     assert ws(256, 1, 2, 32, 32, dtype=F32) > 0
     assert ws(256, 1, 16384, 32, 32) > 0
     assert ws(256, 1, 16385, 32, 32) == 0                 # H above KDA_MAX_HEADS
@@ -499,10 +499,14 @@ def test_plan_descriptions(L):
     buf = ctypes.create_string_buffer(n32 + 1)
     assert L.kda_describe_prefill_plan(8192, 1, 32, 128, 128, F32, 0, buf, n32 + 1) == n32
     txt = buf.value.decode()
-    assert "token-serial" in txt and "prefill_serial_kernel grid 32 x 256" in txt and "plan_kernel" not in txt
+    assert "token-serial" in txt and "plan_kernel" not in txt
+    # eight segments of 1024 tokens per head: 256 windowed workgroups of 8 waves, then the flagged chains
+    assert "segments: 16 chunks" in txt and "prefill_serial_kernel (windowed) grid 256 x 512" in txt
+    assert "prefill_serial_kernel (chains) grid 32 x 256" in txt
     n32p = L.kda_describe_prefill_plan(8192, 4, 8, 64, 32, F32, 1, None, 0)
     buf = ctypes.create_string_buffer(n32p + 1)
     L.kda_describe_prefill_plan(8192, 4, 8, 64, 32, F32, 1, buf, n32p + 1)
-    assert "plan_kernel" in buf.value.decode() and "prefill_serial_kernel grid 32 x 64" in buf.value.decode()
+    txt = buf.value.decode()
+    assert "plan_kernel" in txt and "x 192 threads" in txt and "(chains) grid 32 x 64" in txt
     assert L.kda_describe_backward_plan(-1, 1, 32, 128, 128, BF16, None, 0) == -1
     assert L.kda_describe_backward_plan(64, 1, 32, 128, 128, 7, None, 0) == -1

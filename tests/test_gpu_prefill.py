@@ -195,3 +195,14 @@ def test_prefill_f32_serial_long(kda, dk, dv):
     # the same arithmetic token by token: split calls equal one call exactly
     assert np.array_equal(host(torch.cat(outs)), o)
     assert np.array_equal(host(St), S)
+
+
+@pytest.mark.parametrize("warm", [-1, 0])
+@pytest.mark.parametrize("zshift", [0.0, -3.0])
+def test_prefill_f32_serial_segments(kda, zshift, warm):
+    """The token-serial path over packed sequences cut into segments of 2
+    chunks: warm-up windows (flagged chains, which the weak decay of z - 3
+    makes, rerun whole) or none (warm = 0: every chain reruns whole)."""
+    wl = synth.TINY_F32.with_(H=3, dk=128, dv=64, seqlens=(700, 0, 129, 1000, 5), state_std=0.1,
+                              z_shift=zshift)
+    check(kda, wl, seg=2, tag=f"serial zshift={zshift}", warm=warm)

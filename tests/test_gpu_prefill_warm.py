@@ -235,3 +235,51 @@ def test_graph_replay(kda, weak):
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(o, o_ref) and torch.equal(S, S_ref)
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 32)])
+def test_serial_windows(kda, dk, dv):
+    """The fp32 token-serial path cut into segments of 4 chunks with the
+    default 128-token windows: under the workloads' gate no window is
+    flagged; heads 1 and 2 with g from z - 4 are flagged and rerun whole."""
+    wl = synth.TINY_F32.with_(H=3, dk=dk, dv=dv, seqlens=(2000,), state_std=0.1)
+    announce(f"serial windows dk={dk} dv={dv}")
+    x, g, S0 = inputs(wl)
+    o, S, _, flags = run(kda, wl, x, g, S0, seg=4)
+    n = nseg_of(2000, 4)
+    assert int(host(flags[:n]).sum()) == 0, f"a window fell back: {host(flags[:n])}"
+    check(o, S, wl, x, g, S0)
+    x, g, S0 = inputs(wl, g_shift_heads=[1, 2])
+    o, S, _, flags = run(kda, wl, x, g, S0, seg=4)
+    per_head = host(flags[:n]).sum(axis=0)
+    assert per_head[0] == 0 and per_head[1] > 0 and per_head[2] > 0, per_head
+    check(o, S, wl, x, g, S0)
+
+
+@pytest.mark.parametrize("warm", [0, 32])
+def test_serial_short_or_no_windows(kda, warm):
+    """warm = 0 flags every segment after the first (the chains rerun whole);
+    a 32-token window falls back on the slower decay of z - 2 somewhere."""
+    wl = synth.TINY_F32.with_(H=2, dk=64, dv=64, seqlens=(1100,), state_std=0.1, z_shift=-2.0)
+    announce(f"serial windows of {warm} tokens")
+    x, g, S0 = inputs(wl)
+    o, S, _, _ = run(kda, wl, x, g, S0, seg=4, warm=warm)
+    check(o, S, wl, x, g, S0)
+
+
+@pytest.mark.parametrize("interval", [64, 192])
+def test_serial_checkpoints_across_segments(kda, interval):
+    """checkpoints written by every segment of the windowed serial path, at
+    positions counted from the sequence start"""
+    wl = synth.TINY_F32.with_(H=2, dk=128, dv=64, seqlens=(1500,), state_std=0.1)
+    announce(f"serial checkpoints interval={interval}")
+    x, g, S0 = inputs(wl)
+    o, S, ck, flags = run(kda, wl, x, g, S0, seg=4, interval=interval)
+    assert int(host(flags[:nseg_of(1500, 4)]).sum()) == 0
+    check(o, S, wl, x, g, S0)
+    St = S0
+    for j in range(1500 // interval):
+        r = slice(j * interval, (j + 1) * interval)
+        _, St = oracle.prefill(x["q"][r], x["k"][r], x["v"][r], g[r], x["beta"][r], S0=St)
+        e = relerr(host(ck[j]), St[0])
+        assert e < TOL["f32"], f"checkpoint {j}: {e:.3e}"
