@@ -973,7 +973,7 @@ __device__ __forceinline__ void prep_tiles(PrepRegs<C, DT>& r, unsigned char* sm
 // diagonal A block then invert their block of (I + A) in place
 // (wave-private, no barrier).
 template <typename C, typename DT, bool SUMMARY>
-__device__ __forceinline__ void prep_products(unsigned char* smem, int buf, int pw, int lane)
+__device__ __forceinline__ void prep_products(unsigned char* smem, int buf, int pw, int lane, PhaseClock& pclk)
 {
     using O = Op<DT>;
     using OT = typename O::T;
@@ -1034,6 +1034,7 @@ __device__ __forceinline__ void prep_products(unsigned char* smem, int buf, int 
         for (int j = 0; j < 4; ++j) v4[j] = (i0 + j <= rr) ? accP[j] : 0.f;
         O::st4(sP + rr * C::ST + pcol(i0), v4);
     }
+    KDA_PHASE(12);
     if (doA && a == b) {
         // this wave's block is complete in LDS (in-order within the wave)
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -1112,7 +1113,7 @@ __device__ __forceinline__ void prep_role(const PrefillDev& p, unsigned char* sm
     KDA_PHASE(4);
     for (int64_t bi = 0; bi < nblk; ++bi) {
         const int buf = int(bi & 1);
-        prep_products<C, DT, SUMMARY>(smem, buf, pw, lane);  // alpha: block bi
+        prep_products<C, DT, SUMMARY>(smem, buf, pw, lane, pclk);  // alpha: block bi
         KDA_PHASE(0);
         __syncthreads();
         KDA_PHASE(1);
@@ -1760,18 +1761,17 @@ prefill_warm_kernel(PrefillDev p)
         const bool act1 = EXT && mlive;
         // ---- alpha: X = V - (K . e^G) S;  X_M = -(K . e^G) M
         f32x4 Xt[2][2];
-        Frag iden;  // picks this wave's 16 columns of a v row (16*(wave&1) + l16 of block wave/2)
         {
-            float x[8];
+            // v in the accumulator layout: lane (l16, q4) takes column
+            // 16 (wave & 1) + l16 of block wave / 2 (its permuted position in
+            // the tile) of rows 4 q4 .. 4 q4 + 3 of each sub-tile
+            const OT* vc = sV + 32 * (wave >> 1) + 8 * (l16 >> 2) + 4 * (wave & 1) + (l16 & 3);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = (kperm(q4, e) == (wave & 1) * 16 + l16) ? 1.f : 0.f;
-            iden = O::make(x);
-        }
+            for (int rt = 0; rt < 2; ++rt) {
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-            Xt[rt][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-            Xt[rt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-            O::mma(Xt[rt][0], O::load(sV + (rt * 16 + l16) * C::SV + 32 * (wave >> 1) + 8 * q4), iden);
+                for (int j = 0; j < 4; ++j) Xt[rt][0][j] = O::from_op(vc[(rt * 16 + 4 * q4 + j) * C::SV]);
+                Xt[rt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
         }
 #pragma unroll
         for (int kb = 0; kb < DK / 32; ++kb) {
