@@ -134,3 +134,12 @@ def test_checked_backward(kda, dk, dv, dtype, with_ckpt):
                                ckpt=ck, interval=64, seg_tokens=64)
         return [out[n] for n in sorted(out)]
     expect_same(kda, run)
+
+
+@pytest.mark.parametrize("zshift", [0.0, -4.0])
+def test_checked_serial_windows(kda, zshift):
+    """the fp32 token-serial path in segments of 4 chunks: windows that hold
+    (z) and windows that fall back to whole chains (z - 4), with checkpoints"""
+    wl = synth.TINY_F32.with_(H=2, dk=128, dv=64, seqlens=(2000,), state_std=0.1, z_shift=zshift)
+    announce(f"checked serial windows zshift={zshift}")
+    expect_same(kda, prefill_run(kda, wl, seg=4, interval=192))
