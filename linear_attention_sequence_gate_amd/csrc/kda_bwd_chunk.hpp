@@ -97,7 +97,13 @@ struct BwdLayout {
     static constexpr int O_GAM = O_G + (FULL ? BSUB * DK * 4 : 0);  // gamma [DK]
     static constexpr int O_BETA = O_GAM + DK * 4;               // beta [16]
     static constexpr int O_RB = O_BETA + BSUB * 4;              // dbeta partials [NW][16]
-    static constexpr int LDS = O_RB + (FULL ? NW * BSUB * 4 : 0);
+    static constexpr int LDS0 = O_RB + (FULL ? NW * BSUB * 4 : 0);
+    // the full pass keeps T and A' of a chunk's forward sub-chunks (all but the
+    // last) for the backward sub-chunks of the same tokens, where they fit
+    static constexpr int TC_ONE = (T16 + BSUB * 17 * 4 + 15) / 16 * 16;
+    static constexpr int O_TC = (LDS0 + 15) / 16 * 16;
+    static constexpr bool TCACHE = FULL && O_TC + (BNSUB - 1) * TC_ONE <= 160 * 1024;
+    static constexpr int LDS = TCACHE ? O_TC + (BNSUB - 1) * TC_ONE : LDS0;
 };
 
 template <typename DT, int DK, int DV, bool FULL>
@@ -489,6 +495,25 @@ __device__ __forceinline__ void bwd_small(unsigned char* sm, int lane, bool need
     diag_inverse<C, O>(sQA, sT, 0, lane);
 }
 
+// T and A' of one sub-chunk between their live tiles and cache slot `slot`
+// (put: live -> slot), as 16-byte pieces, by one wave after its own writes
+template <typename C>
+__device__ __forceinline__ void tcache_copy(unsigned char* sm, int slot, int lane, bool put)
+{
+    static_assert(C::T16 % 16 == 0 && (BSUB * 17 * 4) % 16 == 0, "16-byte pieces");
+    constexpr int NT16 = C::T16 / 16, NAP = BSUB * 17 * 4 / 16;
+    unsigned char* kept = sm + C::O_TC + slot * C::TC_ONE;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int i = lane; i < NT16 + NAP; i += 64) {
+        unsigned char* live = i < NT16 ? sm + C::O_T + 16 * i : sm + C::O_AP + 16 * (i - NT16);
+        u32x4* dst = reinterpret_cast<u32x4*>(put ? kept + 16 * i : live);
+        const u32x4* src = reinterpret_cast<const u32x4*>(put ? live : kept + 16 * i);
+        *dst = *src;
+    }
+}
+
 // The state-free backward step of one sub-chunk for a wave's 32 columns of dS
 // (HASDO: the columns see dO).  Returns dY and, through dS, the gradient at
 // the sub-chunk's start.  Before the update, hook(dS') sees the incoming dS.
@@ -765,12 +790,16 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
             }
         }
     };
-    // one forward sub-chunk; prep() puts its operands into LDS
-    auto fwd_sub = [&](f32x4 (&S)[NCT][CT], auto&& prep) {
+    // one forward sub-chunk; prep() puts its operands into LDS; T and A' go to
+    // cache slot cslot (when >= 0) for the backward sub-chunk of the same tokens
+    auto fwd_sub = [&](f32x4 (&S)[NCT][CT], auto&& prep, int cslot) {
         prep();
         __syncthreads();
         KDA_PHASE(0);
-        if (wave == 0) bwd_small<C, DT, true>(sm, fresh_lane(), false);
+        if (wave == 0) {
+            bwd_small<C, DT, true>(sm, fresh_lane(), false);
+            if (C::TCACHE && cslot >= 0) tcache_copy<C>(sm, cslot, fresh_lane(), true);
+        }
         __syncthreads();
         KDA_PHASE(1);
         if (chain) fwd_update(S);
@@ -876,7 +905,7 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
                 const int64_t from = m >= 1 ? c0 + m * a.ckpt_interval : c0;
                 KDA_CHECK(m < 1 || (ck0 + m - 1 >= 0 && ck0 + m - 1 < a.ckpt_cap), CK_CKPT);
                 if (chain) load_tiles(S, m >= 1 ? a.ckpt + ((ck0 + m - 1) * H + h) * DK * DV : init);
-                for (int64_t t = from; t < t0; t += BSUB) fwd_sub(S, [&] { consume(j); });
+                for (int64_t t = from; t < t0; t += BSUB) fwd_sub(S, [&] { consume(j); }, -1);
                 // forward through the chunk, keeping the state at each sub-chunk start
                 for (int s = 0; s < nsub; ++s) {
                     if (chain) {
@@ -900,7 +929,7 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
                         }
                     }
                     KDA_PHASE(3);
-                    if (s + 1 < nsub) fwd_sub(S, [&] { consume(j); });
+                    if (s + 1 < nsub) fwd_sub(S, [&] { consume(j); }, s);
                 }
             }
             __syncthreads();  // every slot is written
@@ -919,8 +948,14 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
                 consume(j);
                 __syncthreads();
                 KDA_PHASE(4);
-                if (wave == 0) bwd_small<C, DT, true>(sm, fresh_lane(), false);
-                else if (wave == 1) bwd_small_p<C, DT>(sm, fresh_lane());
+                // T and A' of the sub-chunks the forward pass ran were kept;
+                // the chunk's last sub-chunk computes them here
+                if (wave == 0) {
+                    if (C::TCACHE && s + 1 < nsub) tcache_copy<C>(sm, s, fresh_lane(), false);
+                    else bwd_small<C, DT, true>(sm, fresh_lane(), false);
+                } else if (wave == 1) {
+                    bwd_small_p<C, DT>(sm, fresh_lane());
+                }
                 __syncthreads();
                 KDA_PHASE(5);
                 if (chain) {
