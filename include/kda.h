@@ -121,7 +121,11 @@ size_t kda_prefill_workspace_size(int64_t T_total, int N, int H, int d_k, int d_
  *   initial_state : fp32 [N, H, d_k, d_v] or NULL (zero initial states).
  *   final_state   : fp32 [N, H, d_k, d_v] or NULL (not written).  May alias
  *                   initial_state exactly (in-place hand-off); no other
- *                   aliasing is allowed between any two buffers.
+ *                   aliasing is allowed between any two buffers.  In place,
+ *                   a segment whose warm-up holds may write the final state
+ *                   before the passes that compose other segments exactly have
+ *                   read the initial state, so the first pass keeps a copy of
+ *                   the initial states in the workspace for them.
  *   chunk   : 64, the granularity (in tokens) at which long sequences are
  *             cut into segments; inside a segment the recurrence advances
  *             in blocks of 32 tokens.

@@ -274,7 +274,7 @@ static bool serial_path(int d_k, int d_v, kda_dtype_t dtype)
 static kda::PrefillPlan plan_for(int64_t T_total, int N, int H, int d_k, int d_v, kda_dtype_t dtype,
                                  int force_L = 0, int warm_req = -1)
 {
-    if (serial_path(d_k, d_v, dtype)) return kda::serial_plan(T_total, N, H, force_L, warm_req);
+    if (serial_path(d_k, d_v, dtype)) return kda::serial_plan(T_total, N, H, d_k, d_v, force_L, warm_req);
     return kda::prefill_plan(T_total, N, H, d_k, d_v, force_L, warm_req);
 }
 
@@ -380,6 +380,7 @@ static kda_status_t prefill_impl(const char* who, const void* q, const void* k, 
     }
     a.gate_A = gate_A;
     a.g_min = g_min;
+    a.init_snap = (initial_state && initial_state == final_state) ? 1 : 0;
     const hipError_t e = serial_path(d_k, d_v, dtype) ? kda::launch_serial(a, plan, s)
                          : dtype == KDA_BF16         ? kda::launch_prefill<kda::BF16>(a, plan, s)
                                                      : kda::launch_prefill<kda::F32>(a, plan, s);
@@ -548,7 +549,7 @@ int64_t kda_describe_prefill_plan(int64_t T_total, int N, int H, int d_k, int d_
 {
     if (!prefill_shape_ok(T_total, N, H, d_k, d_v, 64, dtype) || (!packed && N != 1) || (!buf && cap > 0)) return -1;
     if (serial_path(d_k, d_v, dtype)) {
-        const kda::PrefillPlan p = kda::serial_plan(T_total, N, H);
+        const kda::PrefillPlan p = kda::serial_plan(T_total, N, H, d_k, d_v);
         char head[512];
         snprintf(head, sizeof(head),
                  "kda_prefill plan: T_total=%lld N=%d H=%d d_k=%d d_v=%d dtype=f32%s\n"

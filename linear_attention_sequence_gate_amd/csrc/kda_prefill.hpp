@@ -194,6 +194,7 @@ struct PrefillArgs {
     int64_t ckpt_cap = 0;   // checkpoints the buffer holds
     const float* gate_A = nullptr;  // non-null: g holds the gate's input z, and g = g_min sigmoid(e^{A_h} z)
     float g_min = -5.f;
+    int init_snap = 0;  // initial_state is final_state: passes after the first read a copy of it
 };
 
 // Device-side view shared by the prefill kernels.
@@ -223,6 +224,12 @@ struct PrefillDev {
     int32_t* flags;  // [nseg_max][H]: 1 where a segment's warm-up left M non-zero; null: no warm-up pass
     int warm;        // warm-up tokens
     int64_t nseg_cap = 0, np1_cap = 0;  // the plan's segment and non-final segment counts (bounds checks)
+    // 1: the initial state is also the final state, which a warm-up workgroup
+    // may write before a later pass reads the initial state; so the warm-up
+    // pass copies each sequence's initial state (row-major) into its segment
+    // 0 slot of `sin` (the scan writes slots 1..) and the later passes read it
+    // there
+    int init_snap = 0;
 };
 
 // Table entries (cu_seqlens clamped, segment, pass-1 and checkpoint offsets)
@@ -1211,7 +1218,8 @@ prefill_block_kernel(PrefillDev p)
     f32x4 S[RT][NCT];
     {
         const float* src = nullptr;
-        if (!SUMMARY && s == 0 && p.init) src = p.init + (int64_t(n) * H + h) * DK * DV;
+        if (!SUMMARY && s == 0 && p.init)
+            src = p.init_snap ? p.sin + (int64_t(seg0) * H + h) * DK * DV : p.init + (int64_t(n) * H + h) * DK * DV;
         if (!SUMMARY && s > 0) {
             // S_in from the scan, in accumulator tiles
             const float* tin = p.sin + (int64_t(seg0 + s) * H + h) * DK * DV;
@@ -1526,7 +1534,7 @@ __global__ void __launch_bounds__(256) scan_kernel(PrefillDev p)
         const int j = e / (DK / 4), k = (e % (DK / 4)) * 4;
         f32x4 x = {0.f, 0.f, 0.f, 0.f};
         if (p.init) {
-            const float* src = p.init + (int64_t(n) * H + h) * DK * DV + col0 + j;
+            const float* src = (p.init_snap ? sin0 : p.init + (int64_t(n) * H + h) * DK * DV) + col0 + j;
 #pragma unroll
             for (int m = 0; m < 4; ++m) x[m] = src[(k + m) * DV];
         }
@@ -1745,6 +1753,13 @@ prefill_warm_kernel(PrefillDev p)
                 S[rt][0][j] = src ? src[row * DV + col] : 0.f;
                 S[rt][1][j] = (hasM && row == col) ? 1.f : 0.f;
             }
+        if (p.init_snap && s == 0) {
+            float* snap = p.sin + (int64_t(seg0) * H + h) * DK * DV;
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) snap[(rt * 16 + 4 * q4 + j) * DV + colbase + l16] = S[rt][0][j];
+        }
     }
     bool mlive = hasM;  // wave-uniform: the M tile is still non-zero
     __syncthreads();
@@ -1930,6 +1945,7 @@ hipError_t launch_prefill_t(const PrefillArgs& a, const PrefillPlan& plan, hipSt
                  a.gate_A, a.g_min,
                  warm ? reinterpret_cast<int32_t*>(ws + plan.off_flags) : nullptr, plan.warm,
                  plan.nseg_max, plan.np1_max};
+    d.init_snap = (a.init_snap && warm && plan.np1_max > 0) ? 1 : 0;
     hipError_t e = hipSuccess;
     if (!single) {
         hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, stream, a.cu, a.N, a.T_total,

@@ -163,7 +163,8 @@ __global__ void __launch_bounds__(64 * ((DV + (WINDOWED ? DK : 0)) / 32)) prefil
 #pragma unroll
             for (int e = 0; e < 4; ++e) st[r][e] = (c0 + r == col + e) ? 1.f : 0.f;
         } else if (!from_zero && p.init) {
-            const float* src = p.init + soff + r * DV;
+            // the chains' rerun reads the copy segment 0 made (p.init_snap)
+            const float* src = (!WINDOWED && p.init_snap ? p.sin : p.init) + soff + r * DV;
             st[r] = f32x4{src[0], src[1], src[2], src[3]};
         } else {
             st[r] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -172,6 +173,14 @@ __global__ void __launch_bounds__(64 * ((DV + (WINDOWED ? DK : 0)) / 32)) prefil
     // checkpoints: the state after every multiple of the interval tokens of
     // the sequence, counted from the segment's first token
     const int64_t pos0 = t_begin - seq0;
+    // in place: segment 0 keeps a copy of the initial state for the chains'
+    // rerun, since a last segment may write the final state over it first
+    if (WINDOWED && p.init_snap && s == 0 && !mwave) {
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) p.sin[soff + r * DV + e] = st[r][e];
+    }
     int64_t ck_row = 0;
     int to_ck = 0;
     if (p.ckpt) {
@@ -288,16 +297,19 @@ __global__ void __launch_bounds__(64 * ((DV + (WINDOWED ? DK : 0)) / 32)) prefil
 // prefill_plan; a zero window flags every segment after the first, so the
 // chains run whole); the workspace holds the table
 // the plan kernel writes (clamped cu_seqlens, segment and checkpoint offsets)
-// and one flag per (segment, head).
-inline PrefillPlan serial_plan(int64_t T_total, int N, int H, int force_L = 0, int warm_req = -1)
+// and one flag per (segment, head), then room for a copy of the initial
+// states (read by the chains' rerun when the initial state is the final state).
+inline PrefillPlan serial_plan(int64_t T_total, int N, int H, int dk, int dv, int force_L = 0, int warm_req = -1)
 {
     PrefillPlan p = prefill_plan(T_total, N, H, 32, 32, force_L, warm_req);  // the warm-up planner's segments
     p.np1_max = 0;
-    p.off_ms = p.off_sin = 0;
+    p.off_ms = 0;
     size_t off = align256(sizeof(int32_t) * 5 * size_t(N + 1));
     p.off_table = 0;
     p.off_flags = off;
     off = align256(off + sizeof(int32_t) * size_t(p.nseg_max) * H);
+    p.off_sin = off;
+    off = align256(off + sizeof(float) * size_t(N) * H * dk * dv);
     p.workspace_bytes = off;
     return p;
 }
@@ -317,10 +329,11 @@ hipError_t launch_serial_t(const PrefillArgs& a, const PrefillPlan& plan, hipStr
         single_nck = (a.ckpt && a.ckpt_interval > 0) ? int(len / a.ckpt_interval) : 0;
     }
     PrefillDev d{a.q, a.k, a.v, a.g, a.beta, tab, a.N, a.T_total, a.H, plan.seg_chunks,
-                 a.init, a.fin, a.o, nullptr, nullptr,
+                 a.init, a.fin, a.o, nullptr, reinterpret_cast<float*>(ws + plan.off_sin),
                  a.ckpt, a.ckpt_interval, a.ckpt_cap, single ? 1 : 0, single_nseg, single_nck,
                  a.gate_A, a.g_min, reinterpret_cast<int32_t*>(ws + plan.off_flags), plan.warm,
                  plan.nseg_max, 0};
+    d.init_snap = a.init_snap;
     hipError_t e = hipSuccess;
     if (!single) {
         hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, stream, a.cu, a.N, a.T_total, plan.seg_chunks,

@@ -135,10 +135,11 @@ def test_prefill_workspace_size(L):
     assert ws(0, 1, 32, 128, 128) > 0
     assert ws(8192, 1, 32, 96, 128) == 0
     assert ws(8192, 1, 32, 128, 128, chunk=32) == 0
-    # fp32 shapes without a chunk kernel run token by token: the table and a flag per (segment, head)
-    assert 0 < ws(8192, 1, 32, 128, 128, dtype=F32) <= 256 + 256 * 4
-    assert 0 < ws(8192, 1, 32, 64, 64, dtype=F32) <= 256 + 256 * 4
-    assert 0 < ws(1 << 20, 3, 32, 32, 128, dtype=F32) < 1 << 20
+    # fp32 shapes without a chunk kernel run token by token: the table, a flag
+    # per (segment, head) and room for a copy of the initial states
+    assert 32 * 128 * 128 * 4 < ws(8192, 1, 32, 128, 128, dtype=F32) <= 32 * 128 * 128 * 4 + 256 + 256 * 4 + 512
+    assert 32 * 64 * 64 * 4 < ws(8192, 1, 32, 64, 64, dtype=F32) <= 32 * 64 * 64 * 4 + 256 + 256 * 4 + 512
+    assert 3 * 32 * 32 * 128 * 4 < ws(1 << 20, 3, 32, 32, 128, dtype=F32) < 3 * 32 * 32 * 128 * 4 + (1 << 20)
     assert ws(256, 1, 2, 32, 32, dtype=F32) > 0
     assert ws(256, 1, 16384, 32, 32) > 0
     assert ws(256, 1, 16385, 32, 32) == 0                 # H above KDA_MAX_HEADS

@@ -283,3 +283,32 @@ def test_serial_checkpoints_across_segments(kda, interval):
         _, St = oracle.prefill(x["q"][r], x["k"][r], x["v"][r], g[r], x["beta"][r], S0=St)
         e = relerr(host(ck[j]), St[0])
         assert e < TOL["f32"], f"checkpoint {j}: {e:.3e}"
+
+
+@pytest.mark.parametrize("dk,dv,dtype", [(128, 128, "bf16"), (64, 64, "bf16"), (128, 128, "f32")])
+def test_in_place_with_some_windows_failing(kda, dk, dv, dtype):
+    """initial_state is final_state with segments of 4 chunks, where tokens
+    256..767 decay weakly (g from z - 4): the windows inside them fail and the
+    chain is composed exactly, while the last segment's window holds and that
+    segment writes the final state early.  The exact composition must still
+    start from the initial state, not from the final state written over it."""
+    import torch
+    wl = synth.PREFILL_8K.with_(H=2, dk=dk, dv=dv, dtype=dtype, seqlens=(2048,), state_std=0.1)
+    announce(f"in place, windows failing in the middle, dk={dk} dv={dv} {dtype}")
+    x = synth.prefill_inputs(wl)
+    z = x["z"].copy()
+    z[256:768] -= 4.0
+    g = oracle.gate(z, x["A"], round_bf16=(dtype == "bf16"))
+    S0 = synth.initial_state(wl)
+    d = {n: dev(x[n], dtype) for n in ("q", "k", "v", "beta")}
+    st = dev(S0)
+    o, S, _, ws = kda.kda_test_prefill(d["q"], d["k"], d["v"], dev(g, dtype), d["beta"], initial_state=st,
+                                       final_state=st, seg_chunks=4)
+    torch.cuda.synchronize()
+    flags = kda.test_prefill_flags(ws, wl.T_total, 1, wl.H, dk, dv, 1 if dtype == "bf16" else 0, 4, -1)
+    per_seg = host(flags[:nseg_of(2048, 4)]).sum(axis=1)
+    assert per_seg[2] > 0 and per_seg[-1] == 0, per_seg  # windows fail inside the weak part, hold at the end
+    o_ref, S_ref = oracle.prefill(x["q"], x["k"], x["v"], g, x["beta"], S0=S0)
+    eo, es = relerr(host(o), o_ref), relerr(host(st), S_ref)
+    print(f"  o {eo:.3e}  S {es:.3e}")
+    assert eo < TOL[dtype] and es < TOL[dtype]
