@@ -96,3 +96,33 @@ def test_ckpt_f32_serial(kda, dk, dv, interval):
 
 def test_ckpt_8k(kda):
     check(kda, synth.PREFILL_8K, 512)
+
+
+@pytest.mark.parametrize("dk,dv,dtype,seg,warm", [(128, 128, "bf16", 0, -1), (64, 64, "bf16", 3, 0),
+                                                  (64, 64, "bf16", 3, -1), (128, 64, "f32", 4, -1)])
+def test_ckpt_capacity_short(kda, dk, dv, dtype, seg, warm):
+    """A checkpoint buffer three rows short of kda_checkpoint_count: the rows it
+    holds equal a full-capacity run's and nothing is written past it (the
+    buffer is a view into a larger sentinel-filled one); outputs unchanged."""
+    import torch
+    wl = synth.VARLEN_64.with_(H=2, dk=dk, dv=dv, dtype=dtype, seqlens=(700, 0, 1300, 65, 900), state_std=0.1)
+    announce(f"ckpt capacity short dk={dk} dv={dv} {dtype} seg={seg} warm={warm}")
+    x = synth.prefill_inputs(wl)
+    cu = torch.from_numpy(wl.cu_seqlens).cuda()
+    args = [dev(x[n], dtype) for n in ("q", "k", "v", "z", "beta")]
+    A = dev(x["A"])
+    init = dev(synth.initial_state(wl))
+    n_full = kda.kda_checkpoint_count(wl.cu_seqlens, wl.T_total, 128)
+    full = torch.empty((n_full, wl.H, dk, dv), dtype=torch.float32, device="cuda")
+    big = torch.full((n_full + 2, wl.H, dk, dv), float("nan"), dtype=torch.float32, device="cuda")
+    short = big[:n_full - 3]
+    outs = []
+    for ck in (full, short):
+        o, S, _, _ = kda.kda_test_prefill(*args[:4], args[4], A=A, cu_seqlens=cu, cu_seqlens_host=wl.cu_seqlens,
+                                          initial_state=init, interval=128, ckpt=ck, seg_chunks=seg,
+                                          warm_tokens=warm)
+        outs.append((o, S))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    assert torch.equal(short, full[:n_full - 3])
+    assert torch.isnan(big[n_full - 3:]).all(), "a checkpoint was written past the capacity"
