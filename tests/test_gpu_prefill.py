@@ -114,8 +114,8 @@ def test_prefill_weak_decay_long(kda):
 
 @pytest.mark.parametrize("warm", [-1, 0])
 @pytest.mark.parametrize("case", ["beta0", "alpha1", "gmin", "alpha1_beta1_orthonormal"])
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_prefill_special_values(kda, case, dtype, warm):
+@pytest.mark.parametrize("dtype,dk", [("bf16", 32), ("f32", 32), ("f32", 64)])  # fp32 at 64: the serial path
+def test_prefill_special_values(kda, case, dtype, dk, warm):
     """Exact edge values of the decay and the write strength, given to
     kda_prefill directly: beta = 0 (pure per-channel decay), g = 0 (alpha = 1,
     no forgetting), g = -5 everywhere (the strongest decay the gate allows),
@@ -124,7 +124,7 @@ def test_prefill_special_values(kda, case, dtype, warm):
     vanishes; without decay it never does and the exact passes take over) and
     the summary pass and scan (warm = 0) see them too."""
     import torch
-    dk = dv = 32
+    dv = dk
     # weak decay for beta = 0 (z shifted by -4), so the decayed state stays far
     # above the fp32 underflow over 300 tokens and the relative error means something
     wl = synth.VARLEN_64.with_(H=2, dk=dk, dv=dv, dtype=dtype, seqlens=(300, 130), state_std=0.1,
