@@ -30,6 +30,8 @@ H=8, T=2^20, z shifted by +3) and `varlen_64` (64 packed sequences, ~1.03M
 tokens, H=32, initial states N(0, 0.01)), each one kda_prefill_gated call on
 seeded inputs drawn on the device (the same distributions as the tests'), with
 its HBM roofline and an oracle check on sampled heads and sequences.
+`f32_prefill` times the 8K shape with fp32 tensors (the token-serial path,
+segments with warm-up windows) and checks two heads against the oracle.
 `measured_roofs` holds the device's own streaming bandwidth (read, write, copy
 and in-place kernels) and bf16 matrix-core issue rate (libkda_roofs), against
 which every roofline also reports a fraction.  Decode and commit also report
@@ -337,7 +339,7 @@ def main():
     ap.add_argument("--spin-up", type=float, default=SPIN_UP_S,
                     help="seconds of untimed steps before the warmup steps (clock ramp)")
     ap.add_argument("--no-big", action="store_true", help="skip the million-token legs")
-    ap.add_argument("--legs", default="decode,speculative,backward,roofs,big",
+    ap.add_argument("--legs", default="decode,speculative,backward,f32,roofs,big",
                     help="comma-separated legs to run beside the 8K prefill (default: all)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
@@ -658,6 +660,43 @@ def main():
         del ga, gb, gc
         roofs["vendor_gemm_bf16_tflops"] = round(gemm_tflops, 1)
 
+    f32 = None
+    if "f32" in legs:
+        # ------------------------------------------- fp32 tensors at the 8K shape
+        # (d_k = d_v = 128 in fp32: the token-serial path, segments with warm-up
+        # windows), one kda_prefill_gated call per step; two heads against the oracle
+        import numpy as np
+        import oracle
+        fw = synth.PREFILL_8K.with_(dtype="f32")
+        fx = {n: torch.from_numpy(synth.token_rows(fw, n, 0, T)).to(dev) for n in ("q", "k", "v", "z", "beta")}
+        fA = torch.from_numpy(synth.gate_A(fw)).to(dev)
+        fo = torch.empty((T, H, dv), dtype=torch.float32, device=dev)
+        fS = torch.empty((1, H, dk, dv), dtype=torch.float32, device=dev)
+        fws = torch.empty(kda.kda_prefill_workspace_size(T, 1, H, dk, dv, dtype=kda.KDA_F32), dtype=torch.uint8,
+                          device=dev)
+
+        def fcall(i):
+            kda.kda_prefill_gated(fx["q"], fx["k"], fx["v"], fx["z"], fA, fx["beta"], final_state=fS, o=fo,
+                                  workspace=fws)
+
+        for i in range(2):
+            fcall(i)
+        f_ms = timed_loop(fcall, 10)
+        heads = [1, H - 2]
+        hx = {n: fx[n][:, heads].cpu().numpy() for n in fx}
+        fo_ref, fS_ref = oracle.prefill(hx["q"], hx["k"], hx["v"], oracle.gate(hx["z"], synth.gate_A(fw)[heads]),
+                                        hx["beta"])
+        f_bytes = T * H * ((3 * dk + dv + 1) * 4 + dv * 4) + H * dk * dv * 4
+        f32 = {"value": round(T / (f_ms * 1e-3), 1), "unit": "tokens/s", "ms_per_call": round(f_ms, 4),
+               "config": {"workload": "prefill_8k shape with fp32 tensors (token-serial path)", "H": H, "T": T,
+                          "d_k": dk, "d_v": dv},
+               "achieved_gbs": round(f_bytes / (f_ms * 1e-3) / 1e9, 1), "bound": "latency (token-serial VALU chain)",
+               "verified": {"against": f"fp64 oracle, heads {heads}, whole sequence",
+                            "o_max_rel_err": max_rel_err(fo[:, heads].cpu().numpy(), fo_ref),
+                            "final_state_max_rel_err": max_rel_err(fS[0, heads].cpu().numpy(), fS_ref[0]),
+                            "tolerance": 1e-4}}
+        del fx, fo, fws
+
     # ------------------------------------------- million-token workloads
     if "big" in legs:
         big["prefill_1m"] = big_leg(kda, torch, synth, synth.PREFILL_1M, dev, stream, timed_loop, rw_gbs, 1.34)
@@ -687,7 +726,8 @@ def main():
            "roofline": roofline, "cpu_baseline": cpu, "verified": verified, "unfused": unfused,
            "checkpoints": ckpt_leg,
            "decode": decode,
-           "speculative": spec, "backward": backward, "million_token": big, "measured_roofs": roofs,
+           "speculative": spec, "backward": backward, "f32_prefill": f32, "million_token": big,
+           "measured_roofs": roofs,
            "wall_s": round(wall, 3), "source_hash": kernel_source_hash()}
     print(json.dumps(out), flush=True)
 
