@@ -312,3 +312,28 @@ def test_in_place_with_some_windows_failing(kda, dk, dv, dtype):
     eo, es = relerr(host(o), o_ref), relerr(host(st), S_ref)
     print(f"  o {eo:.3e}  S {es:.3e}")
     assert eo < TOL[dtype] and es < TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype,dk", [("bf16", 128), ("f32", 128)])
+def test_in_place_packed_with_some_windows_failing(kda, dtype, dk):
+    """The same over packed sequences (weak decay in the middle of the first
+    one only), through cu_seqlens: each sequence's initial state is copied
+    before any last segment writes its final state over it."""
+    import torch
+    wl = synth.VARLEN_64.with_(H=2, dk=dk, dv=dk, dtype=dtype, seqlens=(2048, 700, 0, 1300), state_std=0.1)
+    announce(f"in place, packed, windows failing in the first sequence, {dtype}")
+    x = synth.prefill_inputs(wl)
+    z = x["z"].copy()
+    z[256:768] -= 4.0
+    g = oracle.gate(z, x["A"], round_bf16=(dtype == "bf16"))
+    S0 = synth.initial_state(wl)
+    d = {n: dev(x[n], dtype) for n in ("q", "k", "v", "beta")}
+    st = dev(S0)
+    cu = torch.from_numpy(wl.cu_seqlens).cuda()
+    o, _, _, _ = kda.kda_test_prefill(d["q"], d["k"], d["v"], dev(g, dtype), d["beta"], cu_seqlens=cu,
+                                      initial_state=st, final_state=st, seg_chunks=4)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.prefill(x["q"], x["k"], x["v"], g, x["beta"], cu=wl.cu_seqlens, S0=S0)
+    eo, es = relerr(host(o), o_ref), relerr(host(st), S_ref)
+    print(f"  o {eo:.3e}  S {es:.3e}")
+    assert eo < TOL[dtype] and es < TOL[dtype]
