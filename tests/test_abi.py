@@ -32,8 +32,9 @@ CHECKED_ONLY = {"kda_debug_check_bits"}  # exported by the checked build alone
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
     assert set(names) == set(kda.EXPORTED) | CHECKED_ONLY, names
+    checked = kda.LIB_PATH == kda.CHECKED_LIB_PATH  # the suite run with --kda-checked
     for n in names:
-        assert hasattr(L, n) == (n not in CHECKED_ONLY), f"libkda and {n}"
+        assert hasattr(L, n) == (checked or n not in CHECKED_ONLY), f"{kda.LIB_PATH} and {n}"
 
 
 def test_checked_build_exports(L):
