@@ -136,10 +136,10 @@ size_t kda_prefill_workspace_size(int64_t T_total, int N, int H, int d_k, int d_
  *   d_k, d_v: each one of 32, 64, 128, for both dtypes.  fp32 heads with
  *             d_k = 32 and d_v <= 64 take the chunk kernels; the other fp32
  *             shapes (whose fp32 operand tiles do not fit one CU's LDS) run
- *             token by token in fp32 with the state in registers, one
- *             workgroup per (sequence, head): the same results, with no
- *             segment parallelism, so a long fp32 sequence takes time in
- *             proportion to its length.
+ *             token by token in fp32 with the state in registers, in the
+ *             same segments and warm-up windows as the chunk kernels (chains
+ *             whose windows fail are rerun from their start, token by
+ *             token); the same results, about ten times the bf16 time.
  *   workspace : device buffer of at least kda_prefill_workspace_size(...) bytes
  *               (may be NULL when that size is 0); its contents on entry do
  *               not matter and are clobbered.
