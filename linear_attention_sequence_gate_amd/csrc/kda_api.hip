@@ -70,6 +70,7 @@ const char* kda_status_string(kda_status_t s)
     case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
     case KDA_ERR_WORKSPACE_TOO_SMALL: return "KDA_ERR_WORKSPACE_TOO_SMALL";
     case KDA_ERR_HIP: return "KDA_ERR_HIP";
+    default: break;  // the int-range enumerators and unknown codes
     }
     return "KDA_ERR_UNKNOWN";
 }
