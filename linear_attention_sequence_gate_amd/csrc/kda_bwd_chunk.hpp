@@ -366,7 +366,8 @@ __device__ __forceinline__ void bwd_prep_store(const BwdRaw<C, DT>& R, const Bac
             total = __shfl(incl, PARTS - 1, PARTS);
         }
         const float excl = incl - run;
-        if (part == PARTS - 1) sGam[c] = __expf(total);
+        const float eTot = __expf(total);  // e^{G_last}, in [e^-80, 1]
+        if (part == PARTS - 1) sGam[c] = eTot;
         // token-major tiles element by element; this thread's run of tokens
         // of a channel-major tile in one vector write
         OT khr[TPT], kmtr[TPT], qhr[TPT];
@@ -377,7 +378,8 @@ __device__ __forceinline__ void bwd_prep_store(const BwdRaw<C, DT>& R, const Bac
             const float Gr = excl + G[i];
             if (FULL && !fwd) sG[r * DK + c] = Gr;
             const float kv = ok ? cvt(R.k[i]) : 0.f;
-            const float eG = __expf(Gr), eM = __expf(-Gr), eT = __expf(total - Gr);
+            // e^{G_last - G} = e^{G_last} e^{-G} (<= 1; one exponential less per element)
+            const float eG = __expf(Gr), eM = __expf(-Gr), eT = eTot * eM;
             const OT kh = O::to_op(kv * eG), km = O::to_op(kv * eM), kt = O::to_op(kv * eT);
             sKH[r * C::SK + c] = kh;
             sKM[r * C::SK + c] = km;
