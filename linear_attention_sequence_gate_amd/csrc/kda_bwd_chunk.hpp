@@ -1108,7 +1108,7 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
                     f32x4 aM = {0.f, 0.f, 0.f, 0.f};
                     O::mma4(aM, fdAT, frag_rows<O>(sKHT + ch0 * C::S16, C::S16, lane));  // dA'^T K^
                     O::mma4(aM, fdPT, frag_rows<O>(sQHT + ch0 * C::S16, C::S16, lane));  // + dP^T Q^
-                    const float Gl = sG[(BSUB - 1) * DK + c];
+                    const float eGl = sGam[c];  // e^{G_last}
                     float gl = 0.f, dGr[4];
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj) {
@@ -1118,7 +1118,7 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
                         const float kv = ok ? kq[jj][0] : 0.f;
                         const float qv = ok ? kq[jj][1] : 0.f;
                         const float G = sG[r * DK + c];
-                        const float eG = __expf(G), eM = __expf(-G), eT = __expf(Gl - G);
+                        const float eG = __expf(G), eM = __expf(-G), eT = eGl * eM;  // e^{G_last - G}
                         const float Qh = qv * eG, Kh = kv * eG, Km = kv * eM, Kt = kv * eT;
                         const float dq = aQ[jj] * eG;
                         const float dk = aK[jj] * eG + aM[jj] * eM + aT[jj] * eT;
