@@ -1029,21 +1029,18 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
                         kq[jj][0] = load_elem<DT>(k + row0 * DK, off);
                         kq[jj][1] = load_elem<DT>(q + row0 * DK, off);
                     }
-                    // dP = incl(dO U^T), dA' = -Diag(beta) strict(dY U^T), each with its transpose
-                    f32x4 dP = {0.f, 0.f, 0.f, 0.f}, dPT = dP, M1 = dP, M1T = dP;
+                    // dP = incl(dO U^T), dA' = -Diag(beta) strict(dY U^T)
+                    f32x4 dP = {0.f, 0.f, 0.f, 0.f}, M1 = dP;
 #pragma unroll
                     for (int kt = 0; kt < DV / 16; ++kt) {
                         const auto fo = frag_rows<O>(sDO + 16 * kt, C::SV, lane);
                         const auto fu = frag_rows<O>(sU + 16 * kt, C::SV, lane);
                         const auto fy = frag_rows<O>(sVY + 16 * kt, C::SV, lane);
                         O::mma4(dP, fo, fu);
-                        O::mma4(dPT, fu, fo);
                         O::mma4(M1, fy, fu);
-                        O::mma4(M1T, fu, fy);
                     }
                     // every lane reads (all indices are in range), then masks
                     float tb[4];
-                    const float bl = sB[l16];
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj) {
                         const int r4 = 4 * q4 + jj;
@@ -1051,9 +1048,19 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
                         const float ap = sAP[r4 * 17 + l16], br = sB[r4];
                         tb[jj] = l16 < r4 ? -m1 * ap : 0.f;
                         dP[jj] = l16 <= r4 ? dP[jj] : 0.f;
-                        dPT[jj] = r4 <= l16 ? dPT[jj] : 0.f;
                         M1[jj] = l16 < r4 ? -br * m1 : 0.f;
-                        M1T[jj] = r4 < l16 ? -bl * M1T[jj] : 0.f;
+                    }
+                    // their transposes: an accumulator tile as the A operand is its
+                    // matrix transposed, so X^T = (that operand) x I, one product
+                    // each (exact: the operand is what the products below use)
+                    f32x4 dPT = {0.f, 0.f, 0.f, 0.f}, M1T = dPT;
+                    {
+                        f32x4 x;
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj) x[jj] = (4 * q4 + jj == l16) ? 1.f : 0.f;
+                        const auto iden = O::make4(x);
+                        O::mma4(dPT, O::make4(dP), iden);
+                        O::mma4(M1T, O::make4(M1), iden);
                     }
                     if (wave == 0) {
                         // dbeta_r: this row's sum of tb plus the chain waves'
