@@ -1029,8 +1029,11 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
                         kq[jj][0] = load_elem<DT>(k + row0 * DK, off);
                         kq[jj][1] = load_elem<DT>(q + row0 * DK, off);
                     }
-                    // dP = incl(dO U^T), dA' = -Diag(beta) strict(dY U^T)
-                    f32x4 dP = {0.f, 0.f, 0.f, 0.f}, M1 = dP;
+                    // one pass over d_v: dP = incl(dO U^T) and dA' = -Diag(beta) strict(dY U^T)
+                    // (masked below), dO S^T, dY S^T and U dS'^T for the channel
+                    // products, and this lane's share of <S, dS'>
+                    f32x4 dP = {0.f, 0.f, 0.f, 0.f}, M1 = dP, aQ = dP, aK = dP, aT = dP;
+                    float dot = 0.f;
 #pragma unroll
                     for (int kt = 0; kt < DV / 16; ++kt) {
                         const auto fo = frag_rows<O>(sDO + 16 * kt, C::SV, lane);
@@ -1038,6 +1041,28 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
                         const auto fy = frag_rows<O>(sVY + 16 * kt, C::SV, lane);
                         O::mma4(dP, fo, fu);
                         O::mma4(M1, fy, fu);
+                        f32x4 sv;
+                        typename O::Frag4 bs;  // B = S^T
+                        if constexpr (C::S_LDS) {
+                            bs = O::load4(sS + c * C::SV + 16 * kt + 4 * q4);
+                            sv = unpack4<O>(bs);
+                        } else {
+                            sv = *reinterpret_cast<const f32x4*>(Sslot + uint32_t(c * DV + 16 * kt + 4 * q4));
+                            bs = O::make4(sv);
+                        }
+                        typename O::Frag4 bd;  // B = dS'^T
+                        f32x4 dv;
+                        if constexpr (C::DSN_LDS) {
+                            bd = O::load4(sDSN + c * C::SV + 16 * kt + 4 * q4);
+                            dv = unpack4<O>(bd);
+                        } else {
+                            dv = *reinterpret_cast<const f32x4*>(gdsn + uint32_t(c * DV + 16 * kt + 4 * q4));
+                            bd = O::make4(dv);
+                        }
+                        dot += sv[0] * dv[0] + sv[1] * dv[1] + sv[2] * dv[2] + sv[3] * dv[3];
+                        O::mma4(aQ, fo, bs);
+                        O::mma4(aK, fy, bs);
+                        O::mma4(aT, fu, bd);
                     }
                     // every lane reads (all indices are in range), then masks
                     float tb[4];
@@ -1079,33 +1104,6 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
                     const auto fdPT = O::make4(dP);   // A = dP^T
                     const auto fdA = O::make4(M1T);   // A = dA'
                     const auto fdAT = O::make4(M1);   // A = dA'^T
-                    f32x4 aQ = {0.f, 0.f, 0.f, 0.f}, aK = aQ, aT = aQ;
-                    float dot = 0.f;
-#pragma unroll
-                    for (int kt = 0; kt < DV / 16; ++kt) {
-                        f32x4 sv;
-                        typename O::Frag4 bs;  // B = S^T
-                        if constexpr (C::S_LDS) {
-                            bs = O::load4(sS + c * C::SV + 16 * kt + 4 * q4);
-                            sv = unpack4<O>(bs);
-                        } else {
-                            sv = *reinterpret_cast<const f32x4*>(Sslot + uint32_t(c * DV + 16 * kt + 4 * q4));
-                            bs = O::make4(sv);
-                        }
-                        typename O::Frag4 bd;  // B = dS'^T
-                        f32x4 dv;
-                        if constexpr (C::DSN_LDS) {
-                            bd = O::load4(sDSN + c * C::SV + 16 * kt + 4 * q4);
-                            dv = unpack4<O>(bd);
-                        } else {
-                            dv = *reinterpret_cast<const f32x4*>(gdsn + uint32_t(c * DV + 16 * kt + 4 * q4));
-                            bd = O::make4(dv);
-                        }
-                        dot += sv[0] * dv[0] + sv[1] * dv[1] + sv[2] * dv[2] + sv[3] * dv[3];
-                        O::mma4(aQ, frag_rows<O>(sDO + 16 * kt, C::SV, lane), bs);
-                        O::mma4(aK, frag_rows<O>(sVY + 16 * kt, C::SV, lane), bs);
-                        O::mma4(aT, frag_rows<O>(sU + 16 * kt, C::SV, lane), bd);
-                    }
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj) aK[jj] *= -sB[4 * q4 + jj];
                     KDA_PHASE(13);
