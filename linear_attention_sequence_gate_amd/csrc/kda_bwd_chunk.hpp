@@ -93,8 +93,11 @@ struct BwdLayout {
     static constexpr int O_P = O_T + T16;                       // P
     static constexpr int O_F32 = (O_P + T16 + 15) / 16 * 16;
     static constexpr int O_AP = O_F32;                          // A' fp32 [16][17]
-    static constexpr int O_G = O_AP + (FULL ? BSUB * 17 * 4 : 0);  // G fp32 [16][DK]
-    static constexpr int O_GAM = O_G + (FULL ? BSUB * DK * 4 : 0);  // gamma [DK]
+    // G fp32 [16][SG]: rows padded by 4 floats, so the rows four apart that one
+    // wave touches together start 16 banks apart
+    static constexpr int SG = DK + 4;
+    static constexpr int O_G = O_AP + (FULL ? BSUB * 17 * 4 : 0);
+    static constexpr int O_GAM = O_G + (FULL ? BSUB * SG * 4 : 0);  // gamma [DK]
     static constexpr int O_BETA = O_GAM + DK * 4;               // beta [16]
     static constexpr int O_RB = O_BETA + BSUB * 4;              // dbeta partials [NW][16]
     static constexpr int LDS0 = O_RB + (FULL ? NW * BSUB * 4 : 0);
@@ -376,7 +379,7 @@ __device__ __forceinline__ void bwd_prep_store(const BwdRaw<C, DT>& R, const Bac
             const int r = r0 + i;
             const bool ok = r < n;
             const float Gr = excl + G[i];
-            if (FULL && !fwd) sG[r * DK + c] = Gr;
+            if (FULL && !fwd) sG[r * C::SG + c] = Gr;
             const float kv = ok ? cvt(R.k[i]) : 0.f;
             // e^{G_last - G} = e^{G_last} e^{-G} (<= 1; one exponential less per element)
             const float eG = __expf(Gr), eM = __expf(-Gr), eT = eTot * eM;
@@ -1122,7 +1125,7 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
                         const uint32_t off = uint32_t(r) * rsk + uint32_t(c);
                         const float kv = ok ? kq[jj][0] : 0.f;
                         const float qv = ok ? kq[jj][1] : 0.f;
-                        const float G = sG[r * DK + c];
+                        const float G = sG[r * C::SG + c];
                         const float eG = __expf(G), eM = __expf(-G), eT = eGl * eM;  // e^{G_last - G}
                         const float Qh = qv * eG, Kh = kv * eG, Km = kv * eM, Kt = kv * eT;
                         const float dq = aQ[jj] * eG;
