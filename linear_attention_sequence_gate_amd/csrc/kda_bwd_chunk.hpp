@@ -903,17 +903,23 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
             const int64_t t0 = chunk_t0(j);
             const int clen = chunk_len(j);
             const int nsub = (clen + BSUB - 1) / BSUB;
+            // the chunk's start state where it already lies in memory, row-major
+            // (its checkpoint row, or the initial state): where the slices read
+            // S from LDS, sub-chunk 0 takes it from there and its slot is not written
+            const float* s0 = nullptr;
             {
                 f32x4 S[NCT][CT];
                 const float* init = a.init ? a.init + unit * DK * DV : nullptr;
                 const int64_t m = chunk_ck(j);
                 const int64_t from = m >= 1 ? c0 + m * a.ckpt_interval : c0;
                 KDA_CHECK(m < 1 || (ck0 + m - 1 >= 0 && ck0 + m - 1 < a.ckpt_cap), CK_CKPT);
-                if (chain) load_tiles(S, m >= 1 ? a.ckpt + ((ck0 + m - 1) * H + h) * DK * DV : init);
+                const float* src = m >= 1 ? a.ckpt + ((ck0 + m - 1) * H + h) * DK * DV : init;
+                if (C::S_LDS && from == t0) s0 = src;
+                if (chain) load_tiles(S, src);
                 for (int64_t t = from; t < t0; t += BSUB) fwd_sub(S, [&] { consume(j); }, -1);
                 // forward through the chunk, keeping the state at each sub-chunk start
                 for (int s = 0; s < nsub; ++s) {
-                    if (chain) {
+                    if (chain && (s > 0 || !s0)) {
                         R.settle();
                         const int lane = fresh_lane(), l16 = lane & 15, q4 = lane >> 4;
                         float* dst = slots + s * DK * DV;  // accumulator tiles, one 16-byte vector per tile
@@ -967,11 +973,22 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
                     const int lane = fresh_lane(), l16 = lane & 15, q4 = lane >> 4;
                     f32x4 X[CT], U[CT], dY[CT], dX[CT];
                     f32x4 Sf[NCT][CT];
+                    if (s == 0 && s0) {
 #pragma unroll
-                    for (int kt = 0; kt < NCT; ++kt)
+                        for (int kt = 0; kt < NCT; ++kt)
 #pragma unroll
-                        for (int ct = 0; ct < CT; ++ct)
-                            Sf[kt][ct] = *reinterpret_cast<const f32x4*>(SslotA + acc_tile_off<DV>(kt, CT * wave + ct, lane));
+                            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                                for (int jj = 0; jj < 4; ++jj)
+                                    Sf[kt][ct][jj] = s0[uint32_t((16 * kt + 4 * q4 + jj) * DV + col0 + 16 * ct + l16)];
+                    } else {
+#pragma unroll
+                        for (int kt = 0; kt < NCT; ++kt)
+#pragma unroll
+                            for (int ct = 0; ct < CT; ++ct)
+                                Sf[kt][ct] =
+                                    *reinterpret_cast<const f32x4*>(SslotA + acc_tile_off<DV>(kt, CT * wave + ct, lane));
+                    }
                     fwd_xu([&](int kt, int ct) { return Sf[kt][ct]; }, X, U);
                     if constexpr (C::S_LDS) {
                         // the state for the slices' products (row-major, operand precision)
