@@ -907,8 +907,10 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
             // (its checkpoint row, or the initial state): where the slices read
             // S from LDS, sub-chunk 0 takes it from there and its slot is not written
             const float* s0 = nullptr;
+            // the forward's state; after the loop below, the state before the
+            // chunk's last sub-chunk, which the backward takes first, from here
+            f32x4 S[NCT][CT];
             {
-                f32x4 S[NCT][CT];
                 const float* init = a.init ? a.init + unit * DK * DV : nullptr;
                 const int64_t m = chunk_ck(j);
                 const int64_t from = m >= 1 ? c0 + m * a.ckpt_interval : c0;
@@ -919,15 +921,21 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
                 for (int64_t t = from; t < t0; t += BSUB) fwd_sub(S, [&] { consume(j); }, -1);
                 // forward through the chunk, keeping the state at each sub-chunk start
                 for (int s = 0; s < nsub; ++s) {
-                    if (chain && (s > 0 || !s0)) {
+                    // accumulator-tile slots for all but the last sub-chunk, and
+                    // not for sub-chunk 0 where it reads s0
+                    const bool acc_slot = s + 1 < nsub && (s > 0 || !s0);
+                    if (chain && (acc_slot || !C::S_LDS)) {
                         R.settle();
                         const int lane = fresh_lane(), l16 = lane & 15, q4 = lane >> 4;
                         float* dst = slots + s * DK * DV;  // accumulator tiles, one 16-byte vector per tile
+                        if (acc_slot) {
 #pragma unroll
-                        for (int rt = 0; rt < NCT; ++rt)
+                            for (int rt = 0; rt < NCT; ++rt)
 #pragma unroll
-                            for (int ct = 0; ct < CT; ++ct)
-                                *reinterpret_cast<f32x4*>(dst + acc_tile_off<DV>(rt, CT * wave + ct, lane)) = S[rt][ct];
+                                for (int ct = 0; ct < CT; ++ct)
+                                    *reinterpret_cast<f32x4*>(dst + acc_tile_off<DV>(rt, CT * wave + ct, lane)) =
+                                        S[rt][ct];
+                        }
                         if constexpr (!C::S_LDS) {
                             float* dstB = slotsB + s * DK * DV;
 #pragma unroll
@@ -973,7 +981,12 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
                     const int lane = fresh_lane(), l16 = lane & 15, q4 = lane >> 4;
                     f32x4 X[CT], U[CT], dY[CT], dX[CT];
                     f32x4 Sf[NCT][CT];
-                    if (s == 0 && s0) {
+                    if (s == nsub - 1) {
+#pragma unroll
+                        for (int kt = 0; kt < NCT; ++kt)
+#pragma unroll
+                            for (int ct = 0; ct < CT; ++ct) Sf[kt][ct] = S[kt][ct];
+                    } else if (s == 0 && s0) {
 #pragma unroll
                         for (int kt = 0; kt < NCT; ++kt)
 #pragma unroll
