@@ -908,8 +908,11 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
             // S from LDS, sub-chunk 0 takes it from there and its slot is not written
             const float* s0 = nullptr;
             // the forward's state; after the loop below, the state before the
-            // chunk's last sub-chunk, which the backward takes first, from here
-            f32x4 S[NCT][CT];
+            // chunk's last sub-chunk, which the backward takes first, from here.
+            // With bf16 operands (registers to spare) the state before the one
+            // before it stays in registers too (S2).
+            constexpr bool KEEP2 = DT::is_bf16;
+            f32x4 S[NCT][CT], S2[NCT][CT];
             {
                 const float* init = a.init ? a.init + unit * DK * DV : nullptr;
                 const int64_t m = chunk_ck(j);
@@ -921,9 +924,17 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
                 for (int64_t t = from; t < t0; t += BSUB) fwd_sub(S, [&] { consume(j); }, -1);
                 // forward through the chunk, keeping the state at each sub-chunk start
                 for (int s = 0; s < nsub; ++s) {
-                    // accumulator-tile slots for all but the last sub-chunk, and
-                    // not for sub-chunk 0 where it reads s0
-                    const bool acc_slot = s + 1 < nsub && (s > 0 || !s0);
+                    // accumulator-tile slots for all but the last sub-chunk (and
+                    // with KEEP2 the one before), and not for sub-chunk 0 where it
+                    // reads s0
+                    const bool in_s0 = s == 0 && s0, in_s2 = KEEP2 && s == nsub - 2 && !in_s0;
+                    const bool acc_slot = s + 1 < nsub && !in_s0 && !in_s2;
+                    if (chain && in_s2) {
+#pragma unroll
+                        for (int rt = 0; rt < NCT; ++rt)
+#pragma unroll
+                            for (int ct = 0; ct < CT; ++ct) S2[rt][ct] = S[rt][ct];
+                    }
                     if (chain && (acc_slot || !C::S_LDS)) {
                         R.settle();
                         const int lane = fresh_lane(), l16 = lane & 15, q4 = lane >> 4;
@@ -986,6 +997,11 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, true>::NT)) bwd_chunk_full
                         for (int kt = 0; kt < NCT; ++kt)
 #pragma unroll
                             for (int ct = 0; ct < CT; ++ct) Sf[kt][ct] = S[kt][ct];
+                    } else if (KEEP2 && s == nsub - 2 && !(s == 0 && s0)) {
+#pragma unroll
+                        for (int kt = 0; kt < NCT; ++kt)
+#pragma unroll
+                            for (int ct = 0; ct < CT; ++ct) Sf[kt][ct] = S2[kt][ct];
                     } else if (s == 0 && s0) {
 #pragma unroll
                         for (int kt = 0; kt < NCT; ++kt)
