@@ -430,21 +430,6 @@ struct BwdPrepAt {
     bool fwd, valid;
 };
 
-// Both halves at once (the summary pass, which does not prefetch).
-template <typename C, typename DT, bool FULL>
-__device__ __forceinline__ void bwd_prep(const BackwardArgs& a, unsigned char* sm, int64_t t_s, int n, int h,
-                                         bool fwd)
-{
-    BwdRaw<C, DT> R;
-    if (fwd) {
-        bwd_prep_load<C, DT, FULL, true>(R, a, t_s, n, h);
-        bwd_prep_store<C, DT, FULL, true>(R, a, sm, n);
-    } else {
-        bwd_prep_load<C, DT, FULL, false>(R, a, t_s, n, h);
-        bwd_prep_store<C, DT, FULL, false>(R, a, sm, n);
-    }
-}
-
 // P (lower with the diagonal), by one wave on the matrix cores.
 template <typename C, typename DT>
 __device__ __forceinline__ void bwd_small_p(unsigned char* sm, int lane)
@@ -644,10 +629,17 @@ __global__ void __launch_bounds__((BwdCfg<DT, DK, DV, false>::NT)) bwd_chunk_sum
             }
     if (r1 > r0) {
         const int64_t m0 = (r0 - L.c0) / BSUB, m1 = (r1 - 1 - L.c0) / BSUB;
-        for (int64_t m = m1; m >= m0; --m) {
+        auto sub_len = [&](int64_t m) {
             const int64_t t_s = L.c0 + m * BSUB;
-            const int n = int(r1 - t_s < BSUB ? r1 - t_s : BSUB);
-            bwd_prep<C, DT, false>(a, sm, t_s, n, h, false);
+            return int(r1 - t_s < BSUB ? r1 - t_s : BSUB);
+        };
+        // each sub-chunk's inputs are loaded one sub-chunk ahead (no global
+        // stores happen inside the loop, so no wait on them is held up)
+        BwdRaw<C, DT> R;
+        bwd_prep_load<C, DT, false, false>(R, a, L.c0 + m1 * BSUB, sub_len(m1), h);
+        for (int64_t m = m1; m >= m0; --m) {
+            bwd_prep_store<C, DT, false, false>(R, a, sm, sub_len(m));
+            if (m > m0) bwd_prep_load<C, DT, false, false>(R, a, L.c0 + (m - 1) * BSUB, sub_len(m - 1), h);
             __syncthreads();
             if (wave == 0) bwd_small<C, DT, false>(sm, fresh_lane(), false);
             else if (wave == 1) bwd_small_p<C, DT>(sm, fresh_lane());
